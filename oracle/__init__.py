@@ -1,0 +1,12 @@
+"""CPU oracle (test infrastructure only): see gla_oracle.py."""
+
+from .gla_oracle import (  # noqa: F401
+    SCAN_B2T,
+    SCAN_L2R,
+    SCAN_R2L,
+    SCAN_ROTATE_BATCH,
+    SCAN_T2B,
+    batch_directions,
+    gla_forward,
+    scan_order,
+)
