@@ -1,0 +1,104 @@
+/*
+ * gla.h - C ABI of the chunkwise gated-linear-attention forward pass with
+ * key-only decay over an H x W patch grid, for AMD Instinct MI355X (gfx950).
+ *
+ * Operation (GTR news write-up, tokendh.com, section "What linear attention
+ * saves": a running d_k x d_v summary, a learnable forget gate, decay on the
+ * key side only with the value-side decay fixed at 1):
+ *
+ *     S_t = diag(alpha_t) S_{t-1} + k_t^T v_t ,   o_t = q_t S_t ,   S_{-1} = 0
+ *
+ * with alpha_t = exp(log_alpha_t) in (0,1]^{d_k}, per token, head and key dim.
+ * t runs over the H*W cells of the grid in the call's scan direction (same
+ * write-up, section "The flaw of one-way scanning and GTR's fix": left->right,
+ * right->left, top->bottom, bottom->top, cycled over the blocks); the state is
+ * carried across row / column ends, one sequence of H*W steps per
+ * (batch, head).  The computation is chunkwise (section "Where the speed comes
+ * from": fixed-size chunks computed in parallel inside, a boundary state handed
+ * between chunks, chunk summaries computed for all chunks at once and only the
+ * boundary hand-off done in order).  No 1/sqrt(d_k) scale and no normaliser are
+ * applied.
+ *
+ * Layout (all tensors dense, row-major, contiguous, 16-byte aligned):
+ *   q, k, log_alpha : [B][heads][H][W][d_k]
+ *   v, out          : [B][heads][H][W][d_v]      (out in grid order)
+ *   final_state     : [B][heads][d_k][d_v] float32, the state after the last
+ *                     scan step; may be NULL.
+ *
+ * Ownership and execution: the caller owns every buffer (device memory).  The
+ * call validates its arguments on the host, then enqueues its kernels on
+ * `stream` (a hipStream_t passed as void*, NULL = the default stream) and
+ * returns without waiting; errors raised while the kernels run surface at the
+ * caller's next synchronisation.  A temporary workspace, when the sequence is
+ * split into spans, is taken and released stream-ordered on `stream`.  The
+ * library keeps no pointer after returning and holds no global state besides a
+ * one-time read of tuning environment variables, so concurrent calls on
+ * different streams are independent.
+ *
+ * Errors: every argument check runs before any HIP call; on failure nothing is
+ * enqueued and a negative status is returned (see gla_status_str).  Nothing
+ * throws across this boundary.
+ */
+#ifndef GLA_H
+#define GLA_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* scan_dir values: the four directions, plus a batch rotation (batch element b
+ * uses direction b mod 4, so one call covers a batch whose elements take
+ * different directions). */
+enum {
+  GLA_SCAN_L2R = 0,           /* rows top to bottom, each left to right        */
+  GLA_SCAN_R2L = 1,           /* rows top to bottom, each right to left        */
+  GLA_SCAN_T2B = 2,           /* columns left to right, each top to bottom     */
+  GLA_SCAN_B2T = 3,           /* columns left to right, each bottom to top     */
+  GLA_SCAN_ROTATE_BATCH = 4
+};
+
+/* status codes */
+enum {
+  GLA_OK = 0,
+  GLA_ERR_NULL = -1,          /* a required pointer is NULL                     */
+  GLA_ERR_SHAPE = -2,         /* B, heads, H or W < 1, or a size overflows      */
+  GLA_ERR_UNSUPPORTED = -3,   /* d_k / d_v / chunk combination not built        */
+  GLA_ERR_ALIGN = -4,         /* a tensor pointer is not 16-byte aligned        */
+  GLA_ERR_SCAN_DIR = -5,      /* scan_dir outside 0..4                          */
+  GLA_ERR_ALIAS = -6,         /* out or final_state overlaps another tensor     */
+  GLA_ERR_HIP = -7            /* a HIP runtime call failed while enqueueing     */
+};
+
+/*
+ * Float16 entry: q, k, v, log_alpha and out are IEEE binary16; final_state is
+ * float32.  Arithmetic: per-chunk cumulative log-decay in float32, 16-bit MFMA
+ * tiles with float32 accumulation, float32 state; out is rounded to nearest
+ * even.  Supported: chunk = 64, d_k in {64, 128}, d_v in {64, 128}.
+ * Numerical domain: log_alpha finite and <= 0, with the decay summed over any
+ * 16 consecutive scan steps of one key dim >= -10 (so the 16-bit key factors
+ * of the diagonal sub-blocks stay finite).
+ */
+int gla_chunk_fwd(const void* q, const void* k, const void* v, const void* log_alpha,
+                  int scan_dir, int B, int heads, int H, int W, int d_k, int d_v, int chunk,
+                  void* out, float* final_state, void* stream);
+
+/*
+ * Float32 entry: every tensor float32, float32 MFMA tiles, float32 state.
+ * Same arguments and semantics.  Supported: chunk = 64, d_k = 64,
+ * d_v in {64, 128}.  Domain: log_alpha finite and <= 0, 16-step decay >= -80.
+ */
+int gla_chunk_fwd_f32(const float* q, const float* k, const float* v, const float* log_alpha,
+                      int scan_dir, int B, int heads, int H, int W, int d_k, int d_v, int chunk,
+                      float* out, float* final_state, void* stream);
+
+/* Static, human-readable text for a status code. */
+const char* gla_status_str(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int gla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GLA_H */

@@ -1,0 +1,15 @@
+"""Chunkwise gated linear attention with key-only decay over a patch grid,
+as hand-written HIP kernels for AMD Instinct MI355X (gfx950).
+
+    out, final_state = gla_chunk_fwd(q, k, v, log_alpha, scan_dir)
+
+The heavy lifting is in libgla.so (C ABI: include/gla.h); this package is a
+thin binding around it plus the seeded synthetic workloads.
+"""
+
+from ._lib import GlaError, gla_chunk_fwd, load, status_str  # noqa: F401
+
+SCAN_L2R, SCAN_R2L, SCAN_T2B, SCAN_B2T, SCAN_ROTATE_BATCH = 0, 1, 2, 3, 4
+
+__all__ = ["gla_chunk_fwd", "GlaError", "load", "status_str", "SCAN_L2R", "SCAN_R2L",
+           "SCAN_T2B", "SCAN_B2T", "SCAN_ROTATE_BATCH"]

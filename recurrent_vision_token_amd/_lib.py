@@ -1,0 +1,103 @@
+"""ctypes binding of libgla.so (argument marshalling only).
+
+Every step of the forward pass runs in the HIP kernels behind the C ABI of
+include/gla.h; this module only checks tensors, allocates outputs with torch,
+and passes raw device pointers and the current HIP stream.  There is no CPU
+fallback: when the library is missing or no GPU is present, calls raise.
+"""
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libgla.so")
+
+GLA_OK = 0
+STATUS = {
+    0: "GLA_OK", -1: "GLA_ERR_NULL", -2: "GLA_ERR_SHAPE", -3: "GLA_ERR_UNSUPPORTED",
+    -4: "GLA_ERR_ALIGN", -5: "GLA_ERR_SCAN_DIR", -6: "GLA_ERR_ALIAS", -7: "GLA_ERR_HIP",
+}
+EXPORTED = ("gla_chunk_fwd", "gla_chunk_fwd_f32", "gla_status_str", "gla_version")
+
+_lib = None
+
+
+class GlaError(RuntimeError):
+    def __init__(self, status, text):
+        super().__init__("%s (%d): %s" % (STATUS.get(status, "?"), status, text))
+        self.status = status
+
+
+def load():
+    """Load libgla.so (built in-tree by recurrent_vision_token_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libgla.so is not built; run __graft_entry__.build() "
+                           "or python recurrent_vision_token_amd/build.py")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    sig = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, vp, vp]
+    for name in ("gla_chunk_fwd", "gla_chunk_fwd_f32"):
+        fn = getattr(lib, name)
+        fn.argtypes = sig
+        fn.restype = ctypes.c_int
+    lib.gla_status_str.argtypes = [ctypes.c_int]
+    lib.gla_status_str.restype = ctypes.c_char_p
+    lib.gla_version.argtypes = []
+    lib.gla_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_str(status):
+    return load().gla_status_str(int(status)).decode()
+
+
+def raw_call(dtype, q, k, v, la, scan_dir, B, heads, H, W, d_k, d_v, chunk, out, final_state,
+             stream):
+    """Call the C entry point with integer pointers; returns the status code."""
+    lib = load()
+    fn = lib.gla_chunk_fwd if dtype == "fp16" else lib.gla_chunk_fwd_f32
+    return fn(q, k, v, la, scan_dir, B, heads, H, W, d_k, d_v, chunk, out, final_state, stream)
+
+
+def gla_chunk_fwd(q, k, v, log_alpha, scan_dir, chunk=64, out=None, final_state=None,
+                  want_final_state=True, stream=None):
+    """Chunkwise GLA forward on device tensors.
+
+    q, k, log_alpha: [B, heads, H, W, d_k]; v: [B, heads, H, W, d_v]; all float16
+    (or all float32), contiguous, on one HIP device.  Returns (out, final_state);
+    final_state is float32 [B, heads, d_k, d_v] or None.
+    """
+    import torch
+
+    tens = (q, k, v, log_alpha)
+    if not all(isinstance(t, torch.Tensor) and t.is_cuda for t in tens):
+        raise ValueError("q, k, v, log_alpha must be device tensors")
+    dt = q.dtype
+    if dt not in (torch.float16, torch.float32) or any(t.dtype != dt for t in tens):
+        raise ValueError("q, k, v, log_alpha must all be float16 or all float32")
+    if q.dim() != 5:
+        raise ValueError("expected [B, heads, H, W, d] tensors")
+    B, heads, H, W, d_k = q.shape
+    d_v = v.shape[-1]
+    if k.shape != q.shape or log_alpha.shape != q.shape or tuple(v.shape[:4]) != (B, heads, H, W):
+        raise ValueError("shape mismatch among q, k, v, log_alpha")
+    if not all(t.is_contiguous() for t in tens):
+        raise ValueError("tensors must be contiguous")
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, heads, H, W, d_v), dtype=dt, device=dev)
+    if final_state is None and want_final_state:
+        final_state = torch.empty((B, heads, d_k, d_v), dtype=torch.float32, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    fs_ptr = final_state.data_ptr() if final_state is not None else None
+    rc = raw_call("fp16" if dt == torch.float16 else "fp32", q.data_ptr(), k.data_ptr(),
+                  v.data_ptr(), log_alpha.data_ptr(), int(scan_dir), B, heads, H, W, d_k, d_v,
+                  int(chunk), out.data_ptr(), fs_ptr, stream)
+    if rc != GLA_OK:
+        raise GlaError(rc, status_str(rc))
+    return out, final_state

@@ -1,0 +1,58 @@
+"""Build the HIP library libgla.so in-tree for gfx950.
+
+The device code is compiled by hipcc with packed-fp32 instructions disabled;
+the host API layer is plain C++.  The result lands next to this file so that
+it travels with the source tree.
+"""
+
+import os
+import shutil
+import subprocess
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libgla.so")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+ARCH = "gfx950"
+
+HIP_FLAGS = [
+    "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
+    # packed fp32 VALU forms are kept out of the generated code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-command-line-argument",
+]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError("build step failed: %s\n%s" % (" ".join(cmd), out))
+    return out
+
+
+def build(verbose=False):
+    hipcc = shutil.which("hipcc") or os.path.join(ROCM, "bin", "hipcc")
+    os.makedirs(BUILD, exist_ok=True)
+    k_obj = os.path.join(BUILD, "gla_kernels.o")
+    a_obj = os.path.join(BUILD, "gla_api.o")
+    logs = []
+    logs.append(_run([hipcc] + HIP_FLAGS + ["-I", INCLUDE, "-I", CSRC, "-c",
+                                            os.path.join(CSRC, "gla_kernels.hip"), "-o", k_obj]))
+    logs.append(_run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-D__HIP_PLATFORM_AMD__",
+                      "-I", os.path.join(ROCM, "include"), "-I", INCLUDE, "-I", CSRC, "-c",
+                      os.path.join(CSRC, "gla_api.cpp"), "-o", a_obj]))
+    tmp = LIB + ".tmp"
+    logs.append(_run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", k_obj, a_obj,
+                      "-o", tmp]))
+    os.replace(tmp, LIB)
+    if verbose:
+        print("\n".join(x for x in logs if x.strip()))
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,176 @@
+// Host side of the C ABI declared in include/gla.h: argument validation (all
+// of it before any HIP call), span planning, stream-ordered workspace, launch.
+
+#include <hip/hip_runtime_api.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstdlib>
+#include <mutex>
+
+#include "gla.h"
+#include "gla_internal.h"
+
+namespace {
+
+constexpr int kChunk = 64;
+constexpr int kMaxDevices = 64;
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Multiprocessor count per device, read once per device.
+std::atomic<int> g_cu_count[kMaxDevices];
+
+int cu_count(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return 256;
+  int n = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  g_cu_count[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Optional override of the chunks handled per output workgroup (0 = automatic).
+int span_override() {
+  static std::once_flag once;
+  static int value = 0;
+  std::call_once(once, [] {
+    const char* s = std::getenv("GLA_SPAN_CHUNKS");
+    if (s != nullptr) {
+      const long v = std::strtol(s, nullptr, 10);
+      if (v > 0 && v < (1L << 20)) value = (int)v;
+    }
+  });
+  return value;
+}
+
+// Chunks per span: enough workgroups to cover every CU about twice, and no
+// span split at all when the (batch, head) sequences alone do that.
+int plan_span_chunks(long long bh, int n_chunks, int cus) {
+  const int forced = span_override();
+  if (forced > 0) return forced < n_chunks ? forced : n_chunks;
+  const long long target = 2LL * cus;
+  const long long total = bh * n_chunks;
+  long long m = (total + target - 1) / target;
+  if (m < 1) m = 1;
+  if (m > n_chunks) m = n_chunks;
+  return (int)m;
+}
+
+int forward(gla::Dtype dt, size_t esize, const void* q, const void* k, const void* v,
+            const void* la, int scan_dir, int B, int heads, int H, int W, int d_k, int d_v,
+            int chunk, void* out, float* final_state, void* stream) {
+  if (scan_dir < 0 || scan_dir > 4) return GLA_ERR_SCAN_DIR;
+  if (!q || !k || !v || !la || !out) return GLA_ERR_NULL;
+  if (B < 1 || heads < 1 || H < 1 || W < 1 || d_k < 1 || d_v < 1) return GLA_ERR_SHAPE;
+  const long long T = (long long)H * W;
+  const long long BH = (long long)B * heads;
+  if (T > (1LL << 30) || BH > (1LL << 30)) return GLA_ERR_SHAPE;
+  const long long dmax = d_k > d_v ? d_k : d_v;
+  if (BH * T > (1LL << 62) / (dmax * 8)) return GLA_ERR_SHAPE;
+  if (chunk != kChunk || !gla::has_variant(dt, d_k, d_v)) return GLA_ERR_UNSUPPORTED;
+  const void* tens[5] = {q, k, v, la, out};
+  for (const void* t : tens)
+    if (reinterpret_cast<uintptr_t>(t) % 16 != 0) return GLA_ERR_ALIGN;
+  if (final_state && reinterpret_cast<uintptr_t>(final_state) % 4 != 0) return GLA_ERR_ALIGN;
+
+  const uintptr_t nk = (uintptr_t)(BH * T * d_k) * esize;
+  const uintptr_t nv = (uintptr_t)(BH * T * d_v) * esize;
+  const Range rq{(uintptr_t)q, (uintptr_t)q + nk}, rk{(uintptr_t)k, (uintptr_t)k + nk};
+  const Range rv{(uintptr_t)v, (uintptr_t)v + nv}, rl{(uintptr_t)la, (uintptr_t)la + nk};
+  const Range ro{(uintptr_t)out, (uintptr_t)out + nv};
+  if (overlap(ro, rq) || overlap(ro, rk) || overlap(ro, rv) || overlap(ro, rl)) return GLA_ERR_ALIAS;
+  if (final_state) {
+    const Range rf{(uintptr_t)final_state,
+                   (uintptr_t)final_state + (uintptr_t)(BH * d_k * d_v) * sizeof(float)};
+    if (overlap(rf, rq) || overlap(rf, rk) || overlap(rf, rv) || overlap(rf, rl) || overlap(rf, ro))
+      return GLA_ERR_ALIAS;
+  }
+
+  const int n_chunks = (int)((T + kChunk - 1) / kChunk);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return GLA_ERR_HIP;
+  const int span_chunks = plan_span_chunks(BH, n_chunks, cu_count(dev));
+  const int n_spans = (n_chunks + span_chunks - 1) / span_chunks;
+  if (BH * n_spans > (1LL << 31) - 1) return GLA_ERR_SHAPE;
+
+  gla::FwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.la = la;
+  p.out = out;
+  p.final_state = final_state;
+  p.B = B;
+  p.heads = heads;
+  p.H = H;
+  p.W = W;
+  p.T = (int)T;
+  p.scan_dir = scan_dir;
+  p.n_chunks = n_chunks;
+  p.span_chunks = span_chunks;
+  p.n_spans = n_spans;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  if (n_spans > 1) {
+    const size_t state_elems = (size_t)BH * n_spans * d_k * d_v;
+    const size_t gate_elems = (size_t)BH * n_spans * d_k;
+    if (hipMallocAsync(&ws, (state_elems + gate_elems) * sizeof(float), st) != hipSuccess)
+      return GLA_ERR_HIP;
+    p.span_state = static_cast<float*>(ws);
+    p.span_gate = p.span_state + state_elems;
+  }
+  const hipError_t e = gla::launch_forward(dt, d_k, d_v, p, st);
+  if (ws != nullptr && hipFreeAsync(ws, st) != hipSuccess) return GLA_ERR_HIP;
+  return e == hipSuccess ? GLA_OK : GLA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gla_chunk_fwd(const void* q, const void* k, const void* v, const void* log_alpha,
+                  int scan_dir, int B, int heads, int H, int W, int d_k, int d_v, int chunk,
+                  void* out, float* final_state, void* stream) {
+  try {
+    return forward(gla::Dtype::kF16, 2, q, k, v, log_alpha, scan_dir, B, heads, H, W, d_k, d_v,
+                   chunk, out, final_state, stream);
+  } catch (...) {
+    return GLA_ERR_HIP;
+  }
+}
+
+int gla_chunk_fwd_f32(const float* q, const float* k, const float* v, const float* log_alpha,
+                      int scan_dir, int B, int heads, int H, int W, int d_k, int d_v, int chunk,
+                      float* out, float* final_state, void* stream) {
+  try {
+    return forward(gla::Dtype::kF32, 4, q, k, v, log_alpha, scan_dir, B, heads, H, W, d_k, d_v,
+                   chunk, out, final_state, stream);
+  } catch (...) {
+    return GLA_ERR_HIP;
+  }
+}
+
+const char* gla_status_str(int status) {
+  switch (status) {
+    case GLA_OK: return "ok";
+    case GLA_ERR_NULL: return "a required pointer is NULL";
+    case GLA_ERR_SHAPE: return "B, heads, H or W below 1, or a size too large";
+    case GLA_ERR_UNSUPPORTED: return "unsupported chunk / d_k / d_v combination";
+    case GLA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    case GLA_ERR_SCAN_DIR: return "scan_dir must be 0..4";
+    case GLA_ERR_ALIAS: return "out or final_state overlaps another tensor";
+    case GLA_ERR_HIP: return "a HIP runtime call failed";
+    default: return "unknown status";
+  }
+}
+
+int gla_version(void) { return 100; }
+
+}  // extern "C"

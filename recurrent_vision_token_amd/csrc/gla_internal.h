@@ -1,0 +1,36 @@
+// Internal interface between the host API layer (gla_api.cpp) and the HIP
+// kernels (gla_kernels.hip).  Not installed, not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+
+namespace gla {
+
+enum class Dtype { kF16, kF32 };
+
+// One call of the forward pass, already validated on the host.
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* la;
+  void* out;
+  float* final_state;   // may be null
+  float* span_state;    // [BH][n_spans][d_k][d_v] span summaries, then entry states
+  float* span_gate;     // [BH][n_spans][d_k] product of the span's gates
+  int B, heads, H, W, T;
+  int scan_dir;
+  int n_chunks;         // ceil(T / 64)
+  int span_chunks;      // chunks handled by one workgroup of the output kernel
+  int n_spans;          // ceil(n_chunks / span_chunks)
+};
+
+// True when a kernel family is compiled for this (dtype, d_k, d_v).
+bool has_variant(Dtype dt, int d_k, int d_v);
+
+// Enqueue the span-summary, span-scan and output kernels on `stream`.
+// The caller has validated p and supplied a workspace when n_spans > 1.
+hipError_t launch_forward(Dtype dt, int d_k, int d_v, const FwdParams& p, hipStream_t stream);
+
+}  // namespace gla

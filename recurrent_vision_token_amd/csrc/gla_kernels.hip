@@ -1,0 +1,713 @@
+// Chunkwise forward pass of gated linear attention with key-only decay over an
+// H x W patch grid, for gfx950 (CDNA4, MI355X).
+//
+// The recurrence S_t = diag(alpha_t) S_{t-1} + k_t^T v_t, o_t = q_t S_t is
+// evaluated chunkwise (GTR news write-up, tokendh.com, section "Where the speed
+// comes from"): the scan is cut into 64-token chunks; everything inside a chunk
+// is dense 16x16 MFMA tiles, and only a d_k x d_v boundary state is handed
+// along the scan.  The "summarise every chunk in parallel, hand off only the
+// boundary state in order" split of the same section becomes three kernels:
+//
+//   1. span_summary : one workgroup per (batch*head, span of chunks) runs the
+//                     span from a zero state and writes its summary
+//                     (prod alpha over the span, state reached) - fully parallel;
+//   2. span_scan    : per (batch*head) the short sequential scan over spans,
+//                     elementwise over the d_k*d_v state, turning summaries into
+//                     each span's entry state;
+//   3. chunk_output : one workgroup per (batch*head, span) replays its chunks
+//                     from the entry state and writes outputs in grid order.
+//
+// When batch*heads alone fills the chip there is one span per sequence and only
+// kernel 3 runs.
+//
+// Inside a chunk (scan steps cC .. cC+63, b_t = inclusive cumulative log decay):
+//   o_t = sum_{s<=t} (q_t . (k_s * exp(b_t - b_s))) v_s  +  (q_t * exp(b_t)) S_entry
+// The decay mask exp(b_t - b_s) is rank one per key dim, so it splits into a
+// row scaling of Q and a column scaling of K (the Hadamard-product identity of
+// the SAGA summary, gist.science, Methodology section B).  Scalings are anchored
+// per 16-token sub-block so every 16-bit factor stays in range: q_t*exp(c_t) and
+// k_s*exp(-c_s) with c the cumulative decay inside the sub-block, and between
+// sub-blocks J < I an extra per-dim factor exp(Bst_I - Bst_J) <= 1.
+//
+// The scan direction is an index remap applied to every 16-byte row load and
+// store (cell = pi(t)); no transposed copy of any tensor is made.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <type_traits>
+
+#include "gla_internal.h"
+
+namespace gla {
+namespace {
+
+typedef _Float16 f16;
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+typedef f16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kChunk = 64;     // tokens per chunk
+constexpr int kSub = 16;       // tokens per sub-block (one MFMA tile edge)
+constexpr int kThreads = 256;  // four wave64s
+
+template <class T>
+struct Elt;
+template <>
+struct Elt<f16> {
+  static constexpr int kPerPiece = 8;  // elements per 16-byte row piece
+  static constexpr int kPad = 8;       // LDS row padding (elements)
+  typedef f16x8 piece_t;               // one 16-byte piece as a vector
+};
+template <>
+struct Elt<float> {
+  static constexpr int kPerPiece = 4;
+  static constexpr int kPad = 4;
+  typedef f32x4 piece_t;
+};
+
+template <class T>
+__device__ __forceinline__ float fexp(float x) {
+  if constexpr (std::is_same<T, float>::value) {
+    return expf(x);
+  } else {
+    return __expf(x);
+  }
+}
+
+// Scan step t -> row-major grid cell for one of the four directions.
+__device__ __forceinline__ int cell_of(int t, int H, int W, int dir) {
+  if (dir == 0) return t;
+  if (dir == 1) {
+    const int r = t / W;
+    return r * W + (W - 1 - (t - r * W));
+  }
+  const int c = t / H;
+  const int r = t - c * H;
+  return (dir == 2 ? r : (H - 1 - r)) * W + c;
+}
+
+__device__ __forceinline__ f32x4 mma32(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16(f16x4 a, f16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Pair index of sub-block pair (I, J), J < I, in the factor table.
+__device__ __forceinline__ constexpr int pair_index(int I, int J) { return I * (I - 1) / 2 + J; }
+
+// ---------------------------------------------------------------------------
+// Shared-memory tiles of one chunk.
+template <class T, int DK, int DV>
+struct ChunkSmem {
+  static constexpr int P = Elt<T>::kPad;
+  static constexpr int QS = DK + P;      // row stride: [token][d_k] tiles
+  static constexpr int AS = kChunk + P;  // row stride: [*][token] tiles
+  static constexpr int OS = DV + P;      // row stride: [token][d_v] tile
+  static constexpr int LA_ELEMS = kChunk * QS;
+  static constexpr int A_ELEMS = kChunk * AS;
+  alignas(16) T q[kChunk * QS];    // raw q, then q_t*exp(c_t)
+  alignas(16) T k[kChunk * QS];    // raw k, then k_s*exp(-c_s)
+  alignas(16) T la[(LA_ELEMS > A_ELEMS) ? LA_ELEMS : A_ELEMS];  // raw log-alpha, then A[t][s]
+  alignas(16) T vt[DV * AS];       // V^T [d_v][token]
+  alignas(16) T klt[DK * AS];      // (k_s*exp(b_last-b_s))^T [d_k][token]
+  alignas(16) T o[kChunk * OS];    // output staging [token][d_v]
+  alignas(16) float e[4 * DK];     // exp(Bst_I): decay from chunk start to sub-block I
+  alignas(16) float f[6 * DK];     // exp(Bst_I - Bst_J), J < I
+  alignas(16) float g[DK];         // exp(b_last): decay over the whole chunk
+};
+
+template <class T, int DK, int DV>
+struct SummarySmem {
+  static constexpr int P = Elt<T>::kPad;
+  static constexpr int QS = DK + P;
+  static constexpr int AS = kChunk + P;
+  alignas(16) T k[kChunk * QS];
+  alignas(16) T la[kChunk * QS];
+  alignas(16) T vt[DV * AS];
+  alignas(16) T klt[DK * AS];
+  alignas(16) float g[DK];
+};
+
+// ---------------------------------------------------------------------------
+// Row-piece loader: q, k, log-alpha as [token][d_k], v as token pairs for the
+// transposed V tile.  Pieces beyond the sequence end read as zero.
+template <class T, int DK, int DV>
+struct Loader {
+  static constexpr int EPP = Elt<T>::kPerPiece;
+  static constexpr int PPT_K = DK / EPP;                 // pieces per token row (d_k)
+  static constexpr int PPT_V = DV / EPP;                 // pieces per token row (d_v)
+  static constexpr int NK = kChunk * PPT_K / kThreads;   // d_k pieces per thread
+  static constexpr int NVP = (kChunk / 2) * PPT_V / kThreads;  // v token pairs per thread
+  static_assert(NK >= 1 && NVP >= 1, "tile too small for the thread count");
+
+  uint4 rq[NK], rk[NK], rl[NK], rv[2 * NVP];
+
+  __device__ __forceinline__ static uint4 ld(const T* base, size_t off) {
+    return *reinterpret_cast<const uint4*>(base + off);
+  }
+
+  template <bool WITH_Q>
+  __device__ __forceinline__ void load(const T* q, const T* k, const T* la, const T* v,
+                                       size_t off_k, size_t off_v, int t0, int valid, int H,
+                                       int W, int dir) {
+    const int tid = threadIdx.x;
+    const uint4 zero = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < NK; ++j) {
+      const int id = tid + kThreads * j;
+      const int tok = id / PPT_K;
+      const int pc = id - tok * PPT_K;
+      if (tok < valid) {
+        const size_t o = off_k + (size_t)cell_of(t0 + tok, H, W, dir) * DK + pc * EPP;
+        if (WITH_Q) rq[j] = ld(q, o);
+        rk[j] = ld(k, o);
+        rl[j] = ld(la, o);
+      } else {
+        if (WITH_Q) rq[j] = zero;
+        rk[j] = zero;
+        rl[j] = zero;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NVP; ++j) {
+      const int id = tid + kThreads * j;
+      const int tp = id / PPT_V;
+      const int pc = id - tp * PPT_V;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int tok = 2 * tp + h;
+        rv[2 * j + h] = (tok < valid)
+                            ? ld(v, off_v + (size_t)cell_of(t0 + tok, H, W, dir) * DV + pc * EPP)
+                            : zero;
+      }
+    }
+  }
+
+  // Registers -> shared tiles: q, k, la row-major; v transposed to [d_v][token].
+  template <bool WITH_Q>
+  __device__ __forceinline__ void store(T* sq, T* sk, T* sla, T* svt, int QS, int AS) const {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < NK; ++j) {
+      const int id = tid + kThreads * j;
+      const int tok = id / PPT_K;
+      const int pc = id - tok * PPT_K;
+      const int o = tok * QS + pc * EPP;
+      if (WITH_Q) *reinterpret_cast<uint4*>(sq + o) = rq[j];
+      *reinterpret_cast<uint4*>(sk + o) = rk[j];
+      *reinterpret_cast<uint4*>(sla + o) = rl[j];
+    }
+#pragma unroll
+    for (int j = 0; j < NVP; ++j) {
+      const int id = tid + kThreads * j;
+      const int tp = id / PPT_V;
+      const int pc = id - tp * PPT_V;
+      typedef typename Elt<T>::piece_t piece_t;
+      const piece_t a = __builtin_bit_cast(piece_t, rv[2 * j]);
+      const piece_t b = __builtin_bit_cast(piece_t, rv[2 * j + 1]);
+#pragma unroll
+      for (int u = 0; u < EPP; ++u) {
+        typedef T pair_t __attribute__((ext_vector_type(2)));
+        pair_t pr;
+        pr[0] = a[u];
+        pr[1] = b[u];
+        *reinterpret_cast<pair_t*>(svt + (pc * EPP + u) * AS + 2 * tp) = pr;
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// d_k x d_v state held in MFMA accumulators.  Wave w owns value-column blocks
+// cb = w + 4*j; tile (r, j) holds S[16r + 4g + u][16cb + n] in lane (g, n).
+template <int DK, int DV>
+struct StateRegs {
+  static constexpr int NR = DK / 16;
+  static constexpr int NC = DV / 64;
+  f32x4 s[NR][NC];
+};
+
+// S <- diag(exp(b_last)) S + KL^T V for this wave's column blocks.
+template <class T, int DK, int DV>
+__device__ __forceinline__ void state_update(StateRegs<DK, DV>& st, const T* klt, const T* vt,
+                                             const float* gch, int AS) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < StateRegs<DK, DV>::NC; ++j) {
+    const int col = 16 * (wave + 4 * j) + n16;
+#pragma unroll
+    for (int r = 0; r < StateRegs<DK, DV>::NR; ++r) {
+      f32x4 acc = st.s[r][j];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[u] *= gch[16 * r + 4 * g + u];
+      const int dim = 16 * r + n16;
+      if constexpr (std::is_same<T, f16>::value) {
+#pragma unroll
+        for (int s0 = 0; s0 < kChunk; s0 += 32) {
+          const f16x8 a = *reinterpret_cast<const f16x8*>(klt + dim * AS + s0 + 8 * g);
+          const f16x8 b = *reinterpret_cast<const f16x8*>(vt + col * AS + s0 + 8 * g);
+          acc = mma32(a, b, acc);
+        }
+      } else {
+#pragma unroll
+        for (int s0 = 0; s0 < kChunk; s0 += 4)
+          acc = mma4(klt[dim * AS + s0 + g], vt[col * AS + s0 + g], acc);
+      }
+      st.s[r][j] = acc;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 1: span summaries.  Runs the span's chunks from a zero state and
+// writes the state reached and the product of the span's gates.
+template <class T, int DK, int DV>
+__global__ __launch_bounds__(kThreads) void span_summary_kernel(FwdParams p) {
+  using SM = SummarySmem<T, DK, DV>;
+  __shared__ SM sm;
+  constexpr int QS = SM::QS, AS = SM::AS;
+  const int tid = threadIdx.x, lane = tid & 63;
+
+  const int bh = blockIdx.x / p.n_spans;
+  const int span = blockIdx.x - bh * p.n_spans;
+  const int b = bh / p.heads;
+  const int dir = (p.scan_dir == 4) ? (b & 3) : p.scan_dir;
+  const size_t off_k = (size_t)bh * p.T * DK;
+  const size_t off_v = (size_t)bh * p.T * DV;
+  const int c_begin = span * p.span_chunks;
+  const int c_end = min(c_begin + p.span_chunks, p.n_chunks);
+
+  const T* k = static_cast<const T*>(p.k);
+  const T* la = static_cast<const T*>(p.la);
+  const T* v = static_cast<const T*>(p.v);
+
+  StateRegs<DK, DV> st;
+#pragma unroll
+  for (int r = 0; r < StateRegs<DK, DV>::NR; ++r)
+#pragma unroll
+    for (int j = 0; j < StateRegs<DK, DV>::NC; ++j) st.s[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  constexpr int NI = DK / 64;  // (key dim, sub-block) items per thread
+  float log_gate[NI];
+#pragma unroll
+  for (int it = 0; it < NI; ++it) log_gate[it] = 0.f;
+
+  Loader<T, DK, DV> ld;
+  {
+    const int t0 = c_begin * kChunk;
+    ld.template load<false>(nullptr, k, la, v, off_k, off_v, t0, min(kChunk, p.T - t0), p.H, p.W,
+                            dir);
+  }
+  for (int c = c_begin; c < c_end; ++c) {
+    __syncthreads();  // previous chunk's MFMA reads of vt / klt are done
+    ld.template store<false>(nullptr, sm.k, sm.la, sm.vt, QS, AS);
+    if (c + 1 < c_end) {
+      const int t0 = (c + 1) * kChunk;
+      ld.template load<false>(nullptr, k, la, v, off_k, off_v, t0, min(kChunk, p.T - t0), p.H,
+                              p.W, dir);
+    }
+    __syncthreads();
+    // Cumulative decay per (key dim, sub-block) and the decayed keys k_s*exp(b_last-b_s).
+#pragma unroll
+    for (int it = 0; it < NI; ++it) {
+      const int item = tid + kThreads * it;
+      const int i = item >> 2, J = item & 3;
+      float cs[kSub];
+      float c_run = 0.f;
+#pragma unroll
+      for (int r = 0; r < kSub; ++r) {
+        c_run += (float)sm.la[(kSub * J + r) * QS + i];
+        cs[r] = c_run;
+      }
+      const int base = lane & ~3;
+      const float D0 = __shfl(c_run, base + 0, 64);
+      const float D1 = __shfl(c_run, base + 1, 64);
+      const float D2 = __shfl(c_run, base + 2, 64);
+      const float D3 = __shfl(c_run, base + 3, 64);
+      const float bst = (J > 0 ? D0 : 0.f) + (J > 1 ? D1 : 0.f) + (J > 2 ? D2 : 0.f);
+      const float blast = D0 + D1 + D2 + D3;
+      constexpr int EPP = Elt<T>::kPerPiece;
+      typedef typename Elt<T>::piece_t piece_t;
+#pragma unroll
+      for (int r0 = 0; r0 < kSub; r0 += EPP) {
+        piece_t w;
+#pragma unroll
+        for (int u = 0; u < EPP; ++u) {
+          const float kv = (float)sm.k[(kSub * J + r0 + u) * QS + i];
+          w[u] = (T)(kv * fexp<T>(blast - bst - cs[r0 + u]));
+        }
+        *reinterpret_cast<piece_t*>(sm.klt + i * AS + kSub * J + r0) = w;
+      }
+      if (J == 0) {
+        sm.g[i] = fexp<T>(blast);
+        log_gate[it] += blast;
+      }
+    }
+    __syncthreads();
+    state_update<T, DK, DV>(st, sm.klt, sm.vt, sm.g, AS);
+  }
+
+  // Write the span summary.
+  const int wave = tid >> 6, n16 = lane & 15, g = lane >> 4;
+  float* dst = p.span_state + ((size_t)bh * p.n_spans + span) * DK * DV;
+#pragma unroll
+  for (int j = 0; j < StateRegs<DK, DV>::NC; ++j) {
+    const int col = 16 * (wave + 4 * j) + n16;
+#pragma unroll
+    for (int r = 0; r < StateRegs<DK, DV>::NR; ++r)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) dst[(16 * r + 4 * g + u) * DV + col] = st.s[r][j][u];
+  }
+#pragma unroll
+  for (int it = 0; it < NI; ++it) {
+    const int item = tid + kThreads * it;
+    const int i = item >> 2, J = item & 3;
+    if (J == 0)
+      p.span_gate[((size_t)bh * p.n_spans + span) * DK + i] = fexp<T>(log_gate[it]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 2: sequential scan over spans, elementwise over the state.  Replaces
+// each span summary by the state entering that span.
+template <int DK, int DV>
+__global__ __launch_bounds__(kThreads) void span_scan_kernel(FwdParams p) {
+  const int bh = blockIdx.x;
+  const int e = blockIdx.y * kThreads + threadIdx.x;  // element of the d_k x d_v state
+  const int dim = e / DV;
+  const size_t sbase = (size_t)bh * p.n_spans * DK * DV + e;
+  const size_t gbase = (size_t)bh * p.n_spans * DK + dim;
+  float s = 0.f;
+  int sp = 0;
+  constexpr int U = 8;
+  for (; sp + U <= p.n_spans; sp += U) {
+    float L[U], G[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      L[u] = p.span_state[sbase + (size_t)(sp + u) * DK * DV];
+      G[u] = p.span_gate[gbase + (size_t)(sp + u) * DK];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      p.span_state[sbase + (size_t)(sp + u) * DK * DV] = s;
+      s = G[u] * s + L[u];
+    }
+  }
+  for (; sp < p.n_spans; ++sp) {
+    const float L = p.span_state[sbase + (size_t)sp * DK * DV];
+    const float G = p.span_gate[gbase + (size_t)sp * DK];
+    p.span_state[sbase + (size_t)sp * DK * DV] = s;
+    s = G * s + L;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 3: outputs.  Replays the span's chunks from the span's entry state.
+template <class T, int DK, int DV>
+__global__ __launch_bounds__(kThreads) void chunk_output_kernel(FwdParams p) {
+  using SM = ChunkSmem<T, DK, DV>;
+  __shared__ SM sm;
+  constexpr int QS = SM::QS, AS = SM::AS, OS = SM::OS;
+  constexpr int EPP = Elt<T>::kPerPiece;
+  constexpr bool kF16 = std::is_same<T, f16>::value;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n16 = lane & 15, g = lane >> 4;
+
+  const int bh = blockIdx.x / p.n_spans;
+  const int span = blockIdx.x - bh * p.n_spans;
+  const int b = bh / p.heads;
+  const int dir = (p.scan_dir == 4) ? (b & 3) : p.scan_dir;
+  const size_t off_k = (size_t)bh * p.T * DK;
+  const size_t off_v = (size_t)bh * p.T * DV;
+  const int c_begin = span * p.span_chunks;
+  const int c_end = min(c_begin + p.span_chunks, p.n_chunks);
+
+  const T* q = static_cast<const T*>(p.q);
+  const T* k = static_cast<const T*>(p.k);
+  const T* la = static_cast<const T*>(p.la);
+  const T* v = static_cast<const T*>(p.v);
+  T* out = static_cast<T*>(p.out);
+
+  // Entry state of the span.
+  StateRegs<DK, DV> st;
+  {
+    const float* src =
+        (span > 0) ? p.span_state + ((size_t)bh * p.n_spans + span) * DK * DV : nullptr;
+#pragma unroll
+    for (int j = 0; j < StateRegs<DK, DV>::NC; ++j) {
+      const int col = 16 * (wave + 4 * j) + n16;
+#pragma unroll
+      for (int r = 0; r < StateRegs<DK, DV>::NR; ++r)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          st.s[r][j][u] = src ? src[(16 * r + 4 * g + u) * DV + col] : 0.f;
+    }
+  }
+
+  constexpr int NI = DK / 64;
+  // Sub-block tiles (I, J), J <= I, of the causal score matrix, spread over the
+  // four waves (3, 3, 2, 2 tiles); one byte (I << 4 | J) per tile.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t tile_codes = (wave_u == 0) ? 0x313000u
+                            : (wave_u == 1) ? 0x321110u
+                            : (wave_u == 2) ? 0x2120u
+                                            : 0x3322u;
+  const int n_tiles = (wave_u < 2) ? 3 : 2;
+
+  Loader<T, DK, DV> ld;
+  {
+    const int t0 = c_begin * kChunk;
+    ld.template load<true>(q, k, la, v, off_k, off_v, t0, min(kChunk, p.T - t0), p.H, p.W, dir);
+  }
+  for (int c = c_begin; c < c_end; ++c) {
+    const int t0 = c * kChunk;
+    const int valid = min(kChunk, p.T - t0);
+    ld.template store<true>(sm.q, sm.k, sm.la, sm.vt, QS, AS);
+    if (c + 1 < c_end) {
+      const int t1 = t0 + kChunk;
+      ld.template load<true>(q, k, la, v, off_k, off_v, t1, min(kChunk, p.T - t1), p.H, p.W,
+                             dir);
+    }
+    __syncthreads();
+
+    // Phase P: cumulative decay per (key dim i, sub-block J); anchored q, k,
+    // decayed keys for the state update, and the per-dim factor tables.
+#pragma unroll
+    for (int it = 0; it < NI; ++it) {
+      const int item = tid + kThreads * it;
+      const int i = item >> 2, J = item & 3;
+      float cs[kSub];
+      float c_run = 0.f;
+#pragma unroll
+      for (int r = 0; r < kSub; ++r) {
+        c_run += (float)sm.la[(kSub * J + r) * QS + i];
+        cs[r] = c_run;
+      }
+      const int base = lane & ~3;
+      float D[4];
+      D[0] = __shfl(c_run, base + 0, 64);
+      D[1] = __shfl(c_run, base + 1, 64);
+      D[2] = __shfl(c_run, base + 2, 64);
+      D[3] = __shfl(c_run, base + 3, 64);
+      float bst[4];
+      bst[0] = 0.f;
+      bst[1] = D[0];
+      bst[2] = D[0] + D[1];
+      bst[3] = D[0] + D[1] + D[2];
+      const float blast = bst[3] + D[3];
+      const float my_bst = bst[J];
+      const float fl = fexp<T>(blast - my_bst);
+      typedef typename Elt<T>::piece_t piece_t;
+#pragma unroll
+      for (int r0 = 0; r0 < kSub; r0 += EPP) {
+        piece_t w;
+#pragma unroll
+        for (int u = 0; u < EPP; ++u) {
+          const int row = (kSub * J + r0 + u) * QS + i;
+          const float eq = fexp<T>(cs[r0 + u]);
+          const float ek = fexp<T>(-cs[r0 + u]);
+          const float qv = (float)sm.q[row];
+          const float kv = (float)sm.k[row];
+          sm.q[row] = (T)(qv * eq);
+          sm.k[row] = (T)(kv * ek);
+          w[u] = (T)(kv * (ek * fl));
+        }
+        *reinterpret_cast<piece_t*>(sm.klt + i * AS + kSub * J + r0) = w;
+      }
+      sm.e[J * DK + i] = fexp<T>(my_bst);
+#pragma unroll
+      for (int I = 1; I < 4; ++I)
+        if (I > J) sm.f[pair_index(I, J) * DK + i] = fexp<T>(bst[I] - my_bst);
+      if (J == 0) sm.g[i] = fexp<T>(blast);
+    }
+    __syncthreads();
+
+    // Phase A: A[t][s] for s <= t as transposed 16x16 tiles (rows s, cols t).
+    T* sa = sm.la;
+    for (int ti = 0; ti < n_tiles; ++ti) {
+      const int code = (tile_codes >> (8 * ti)) & 0xff;
+      const int I = code >> 4, J = code & 0xf;
+      const int s_row = kSub * J + n16;  // key token supplying the A operand
+      const int t_row = kSub * I + n16;  // query token supplying the B operand
+      const float* F = (J < I) ? sm.f + pair_index(I, J) * DK : nullptr;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (kF16) {
+#pragma unroll
+        for (int d0 = 0; d0 < DK; d0 += 32) {
+          f16x8 a = *reinterpret_cast<const f16x8*>(sm.k + s_row * QS + d0 + 8 * g);
+          if (F) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) a[u] = (f16)((float)a[u] * F[d0 + 8 * g + u]);
+          }
+          const f16x8 bq = *reinterpret_cast<const f16x8*>(sm.q + t_row * QS + d0 + 8 * g);
+          acc = mma32(a, bq, acc);
+        }
+      } else {
+#pragma unroll 8
+        for (int d0 = 0; d0 < DK; d0 += 4) {
+          float a = sm.k[s_row * QS + d0 + g];
+          if (F) a *= F[d0 + g];
+          acc = mma4(a, sm.q[t_row * QS + d0 + g], acc);
+        }
+      }
+      // lane holds A^T[s = 16J + 4g + u][t = 16I + n16]
+      if (I == J) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (4 * g + u > n16) acc[u] = 0.f;
+      }
+      typedef T quad_t __attribute__((ext_vector_type(4)));
+      quad_t w;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) w[u] = (T)acc[u];
+      *reinterpret_cast<quad_t*>(sa + t_row * AS + kSub * J + 4 * g) = w;
+    }
+    __syncthreads();
+
+    // Phase O: O^T tiles (rows = value columns, cols = tokens) = V^T A^T + S^T (Q*exp(b))^T,
+    // then the state update.
+#pragma unroll
+    for (int j = 0; j < StateRegs<DK, DV>::NC; ++j) {
+      const int col0 = 16 * (wave + 4 * j);
+      const int col = col0 + n16;
+      f16x8 sh[DK / 32];
+      if constexpr (kF16) {
+#pragma unroll
+        for (int rho = 0; rho < DK / 32; ++rho)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            sh[rho][u] = (f16)st.s[2 * rho][j][u];
+            sh[rho][4 + u] = (f16)st.s[2 * rho + 1][j][u];
+          }
+      }
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        const int t = kSub * I + n16;
+        const int len = kSub * (I + 1);
+        const float* E = sm.e + I * DK;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (kF16) {
+#pragma unroll
+          for (int s0 = 0; s0 + 32 <= len; s0 += 32) {
+            const f16x8 a = *reinterpret_cast<const f16x8*>(sm.vt + col * AS + s0 + 8 * g);
+            const f16x8 bb = *reinterpret_cast<const f16x8*>(sa + t * AS + s0 + 8 * g);
+            acc = mma32(a, bb, acc);
+          }
+          if (len & 16) {
+            const int s0 = len - 16;
+            const f16x4 a = *reinterpret_cast<const f16x4*>(sm.vt + col * AS + s0 + 4 * g);
+            const f16x4 bb = *reinterpret_cast<const f16x4*>(sa + t * AS + s0 + 4 * g);
+            acc = mma16(a, bb, acc);
+          }
+#pragma unroll
+          for (int rho = 0; rho < DK / 32; ++rho) {
+            const int dlo = 32 * rho + 4 * g, dhi = dlo + 16;
+            const f16x4 qlo = *reinterpret_cast<const f16x4*>(sm.q + t * QS + dlo);
+            const f16x4 qhi = *reinterpret_cast<const f16x4*>(sm.q + t * QS + dhi);
+            f16x8 bq;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              bq[u] = (f16)((float)qlo[u] * E[dlo + u]);
+              bq[4 + u] = (f16)((float)qhi[u] * E[dhi + u]);
+            }
+            acc = mma32(sh[rho], bq, acc);
+          }
+        } else {
+#pragma unroll 4
+          for (int s0 = 0; s0 < len; s0 += 4)
+            acc = mma4(sm.vt[col * AS + s0 + g], sa[t * AS + s0 + g], acc);
+#pragma unroll
+          for (int r = 0; r < DK / 16; ++r)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const int d = 16 * r + 4 * g + u;
+              acc = mma4(st.s[r][j][u], sm.q[t * QS + d] * E[d], acc);
+            }
+        }
+        // lane holds O^T[col0 + 4g + u][t]
+        typedef T quad_t __attribute__((ext_vector_type(4)));
+        quad_t w;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) w[u] = (T)acc[u];
+        *reinterpret_cast<quad_t*>(sm.o + t * OS + col0 + 4 * g) = w;
+      }
+    }
+    state_update<T, DK, DV>(st, sm.klt, sm.vt, sm.g, AS);
+    __syncthreads();
+
+    // Phase W: output rows to their grid cells.
+    constexpr int PPT_O = DV / EPP;
+    constexpr int NO = kChunk * PPT_O / kThreads;
+#pragma unroll
+    for (int jj = 0; jj < NO; ++jj) {
+      const int id = tid + kThreads * jj;
+      const int tok = id / PPT_O;
+      const int pc = id - tok * PPT_O;
+      if (tok < valid) {
+        const size_t o = off_v + (size_t)cell_of(t0 + tok, p.H, p.W, dir) * DV + pc * EPP;
+        *reinterpret_cast<uint4*>(out + o) =
+            *reinterpret_cast<const uint4*>(sm.o + tok * OS + pc * EPP);
+      }
+    }
+  }
+
+  if (span == p.n_spans - 1 && p.final_state != nullptr) {
+    float* dst = p.final_state + (size_t)bh * DK * DV;
+#pragma unroll
+    for (int j = 0; j < StateRegs<DK, DV>::NC; ++j) {
+      const int col = 16 * (wave + 4 * j) + n16;
+#pragma unroll
+      for (int r = 0; r < StateRegs<DK, DV>::NR; ++r)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) dst[(16 * r + 4 * g + u) * DV + col] = st.s[r][j][u];
+    }
+  }
+}
+
+template <class T, int DK, int DV>
+hipError_t launch_variant(const FwdParams& p, hipStream_t stream) {
+  const int BH = p.B * p.heads;
+  if (p.n_spans > 1) {
+    hipLaunchKernelGGL((span_summary_kernel<T, DK, DV>), dim3(BH * p.n_spans), dim3(kThreads), 0,
+                       stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((span_scan_kernel<DK, DV>), dim3(BH, DK * DV / kThreads), dim3(kThreads),
+                       0, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((chunk_output_kernel<T, DK, DV>), dim3(BH * p.n_spans), dim3(kThreads), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool has_variant(Dtype dt, int d_k, int d_v) {
+  if (dt == Dtype::kF16)
+    return (d_k == 64 || d_k == 128) && (d_v == 64 || d_v == 128);
+  return d_k == 64 && (d_v == 64 || d_v == 128);
+}
+
+hipError_t launch_forward(Dtype dt, int d_k, int d_v, const FwdParams& p, hipStream_t stream) {
+  if (dt == Dtype::kF16) {
+    if (d_k == 64 && d_v == 64) return launch_variant<f16, 64, 64>(p, stream);
+    if (d_k == 64 && d_v == 128) return launch_variant<f16, 64, 128>(p, stream);
+    if (d_k == 128 && d_v == 64) return launch_variant<f16, 128, 64>(p, stream);
+    if (d_k == 128 && d_v == 128) return launch_variant<f16, 128, 128>(p, stream);
+  } else {
+    if (d_k == 64 && d_v == 64) return launch_variant<float, 64, 64>(p, stream);
+    if (d_k == 64 && d_v == 128) return launch_variant<float, 64, 128>(p, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gla

@@ -1,0 +1,71 @@
+"""The C ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before any HIP call (no GPU needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from recurrent_vision_token_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gla.h")
+
+# plausible-looking device addresses; validation never dereferences them
+P = [0x7F0000000000 + i * (1 << 32) for i in range(8)]
+Q, K, V, LA, OUT, FS = P[0], P[1], P[2], P[3], P[4], P[5]
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gla_\w+)\s*\(", text)))
+
+
+def call(dtype="fp16", q=Q, k=K, v=V, la=LA, scan_dir=0, B=1, heads=2, H=8, W=8, d_k=64,
+         d_v=64, chunk=64, out=OUT, fs=FS):
+    return _lib.raw_call(dtype, q, k, v, la, scan_dir, B, heads, H, W, d_k, d_v, chunk, out, fs,
+                         None)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+def test_status_strings_and_version():
+    for code in range(-7, 1):
+        s = _lib.status_str(code)
+        assert s and s != "unknown status"
+    assert _lib.status_str(-99) == "unknown status"
+    assert _lib.load().gla_version() >= 100
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "fp32"])
+def test_argument_errors(dtype):
+    assert call(dtype, scan_dir=5) == -5
+    assert call(dtype, scan_dir=-1) == -5
+    for kw in ("q", "k", "v", "la", "out"):
+        assert call(dtype, **{kw: None}) == -1, kw
+    for kw in ("B", "heads", "H", "W"):
+        assert call(dtype, **{kw: 0}) == -2, kw
+    assert call(dtype, H=1 << 16, W=1 << 16) == -2          # T beyond 2^30
+    assert call(dtype, chunk=32) == -3
+    assert call(dtype, d_k=96) == -3
+    assert call(dtype, d_v=32) == -3
+    assert call(dtype, q=Q + 8) == -4
+    assert call(dtype, out=OUT + 2) == -4
+    assert call(dtype, fs=FS + 2) == -4
+    assert call(dtype, out=Q) == -6                          # out aliases q
+    assert call(dtype, out=V + 64) == -6                     # out overlaps v
+    assert call(dtype, fs=OUT + 1024) == -6                  # final_state inside out
+
+
+def test_fp32_entry_rejects_unbuilt_key_dim():
+    assert call("fp32", d_k=128) == -3
+    assert call("fp16", d_k=128, scan_dir=9) == -5           # direction checked first

@@ -1,0 +1,162 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Acceptance per call, for out and final_state:
+  fp16 inputs: relative Frobenius error <= 5e-3 and max |err| <= 2e-2 * max |ref|
+  fp32 inputs: relative Frobenius error <= 1e-5
+Inputs are the seeded synthetic workloads; both sides read the same stored
+16- or 32-bit values, the oracle in float64.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import gla_forward
+from recurrent_vision_token_amd.workloads import WORKLOADS, make_inputs, workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+FP16_REL, FP16_MAX, FP32_REL = 5e-3, 2e-2, 1e-5
+
+
+def _torch():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    return torch
+
+
+def run_gpu(q, k, v, la, d, stream=None):
+    torch = _torch()
+    from recurrent_vision_token_amd import gla_chunk_fwd
+    dev = torch.device("cuda:0")
+    tq, tk, tv, tl = (torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in (q, k, v, la))
+    out, fs = gla_chunk_fwd(tq, tk, tv, tl, d, stream=stream)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), fs.cpu().numpy().astype(np.float64)
+
+
+def check(got, ref, fp16, what=""):
+    assert np.all(np.isfinite(got)), what + ": non-finite values"
+    err = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
+    if fp16:
+        mx = np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30)
+        assert err <= FP16_REL and mx <= FP16_MAX, "%s: rel %.3g max %.3g" % (what, err, mx)
+    else:
+        assert err <= FP32_REL, "%s: rel %.3g" % (what, err)
+    return err
+
+
+def parity(q, k, v, la, d, fp16, what=""):
+    o, s = run_gpu(q, k, v, la, d)
+    ro, rs = gla_forward(q, k, v, la, d)
+    check(o, ro, fp16, what + " out")
+    check(s, rs, fp16, what + " final_state")
+    return o, s
+
+
+# ---------------------------------------------------------------- small / edge
+
+@pytest.mark.parametrize("d", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("dtype", ["fp16", "fp32"])
+@pytest.mark.parametrize("H,W", [(1, 1), (7, 9), (13, 11), (1, 37), (29, 1), (16, 16)])
+def test_small_grids(dtype, H, W, d):
+    B = 4 if d == 4 else 1
+    q, k, v, la = make_inputs(B, 3, H, W, 64, 64, dtype, 1.0, seed=H * 31 + W + d)
+    parity(q, k, v, la, d, dtype == "fp16", "%s %dx%d dir %d" % (dtype, H, W, d))
+
+
+@pytest.mark.parametrize("dk,dv,dtype", [(64, 128, "fp16"), (128, 64, "fp16"),
+                                         (128, 128, "fp16"), (64, 128, "fp32")])
+@pytest.mark.parametrize("d", [0, 3])
+def test_head_dims(dk, dv, dtype, d):
+    q, k, v, la = make_inputs(1, 2, 24, 21, dk, dv, dtype, 1.0, seed=dk + dv + d)
+    parity(q, k, v, la, d, dtype == "fp16", "%s dk%d dv%d" % (dtype, dk, dv))
+
+
+def test_many_sequences_single_span():
+    # batch*heads large enough that each sequence is one workgroup, several chunks long
+    q, k, v, la = make_inputs(32, 16, 16, 16, 64, 64, "fp16", 1.0, seed=77)
+    parity(q, k, v, la, 4, True, "512 sequences")
+
+
+def test_strong_decay_and_no_decay():
+    q, k, v, la = make_inputs(1, 2, 20, 20, 64, 64, "fp16", 1.0, seed=5)
+    # gates at the edge of the fp16 domain: 16-step decay down to -9.6
+    la_strong = np.full_like(la, np.float16(-0.6))
+    parity(q, k, v, la_strong, 1, True, "strong decay")
+    parity(q, k, v, np.zeros_like(la), 2, True, "alpha = 1")
+
+
+# ---------------------------------------------------------------- workloads
+
+def test_tiny_config_fp32():
+    wl = WORKLOADS["tiny"]
+    for seed, d in wl.calls:
+        q, k, v, la = workload_inputs(wl, seed)
+        parity(q, k, v, la, d, False, "tiny")
+
+
+@pytest.mark.parametrize("name", ["gtr1.6k", "img768", "hires16.4k"])
+def test_workload_full(name):
+    wl = WORKLOADS[name]
+    for seed, d in wl.calls:
+        q, k, v, la = workload_inputs(wl, seed)
+        parity(q, k, v, la, d, True, "%s seed %d dir %d" % (name, seed, d))
+
+
+def test_batched_sampled_sequences():
+    # full-size run (the benchmark's launch shape); each (b, head) sequence is
+    # independent, so sampled sequences are checked exactly by the oracle
+    wl = WORKLOADS["batched"]
+    seed, d = wl.calls[0]
+    q, k, v, la = workload_inputs(wl, seed)
+    o, s = run_gpu(q, k, v, la, d)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(s))
+    rng = np.random.default_rng(0)
+    picks = [(b, int(rng.integers(wl.heads))) for b in (0, 1, 2, 3, 17, 30, 31)]
+    for b, h in picks:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        ro, rs = gla_forward(q[sl], k[sl], v[sl], la[sl], b % 4)
+        check(o[sl], ro, True, "batched b%d h%d out" % (b, h))
+        check(s[sl], rs, True, "batched b%d h%d state" % (b, h))
+
+
+# ---------------------------------------------------------------- properties
+
+def test_bitwise_determinism():
+    q, k, v, la = make_inputs(1, 12, 40, 40, 64, 64, "fp16", 1.0, seed=9)
+    o1, s1 = run_gpu(q, k, v, la, 2)
+    o2, s2 = run_gpu(q, k, v, la, 2)
+    assert np.array_equal(o1, o2) and np.array_equal(s1, s2)
+
+
+@pytest.mark.parametrize("d", [0, 1, 2, 3])
+def test_bitwise_causality(d):
+    H, W = 24, 24
+    q, k, v, la = make_inputs(1, 2, H, W, 64, 64, "fp16", 1.0, seed=40 + d)
+    perm = {0: np.arange(H * W).reshape(H, W), 1: np.arange(H * W).reshape(H, W)[:, ::-1],
+            2: np.arange(H * W).reshape(H, W).T, 3: np.arange(H * W).reshape(H, W)[::-1].T}[d]
+    perm = perm.reshape(-1)
+    t0 = 300
+    rng = np.random.default_rng(1)
+    q2, k2, v2, la2 = (x.copy() for x in (q, k, v, la))
+    for x in (q2, k2, v2):
+        f = x.reshape(1, 2, H * W, -1)
+        f[:, :, perm[t0 + 1:]] = rng.standard_normal(f[:, :, perm[t0 + 1:]].shape).astype(x.dtype)
+    f = la2.reshape(1, 2, H * W, -1)
+    f[:, :, perm[t0 + 1:]] = -rng.random(f[:, :, perm[t0 + 1:]].shape).astype(la.dtype) * 0.3
+    o1, _ = run_gpu(q, k, v, la, d)
+    o2, _ = run_gpu(q2, k2, v2, la2, d)
+    e1 = o1.reshape(1, 2, H * W, -1)[:, :, perm[:t0 + 1]]
+    e2 = o2.reshape(1, 2, H * W, -1)[:, :, perm[:t0 + 1]]
+    assert np.array_equal(e1, e2)
+
+
+def test_explicit_stream():
+    torch = _torch()
+    q, k, v, la = make_inputs(1, 2, 16, 24, 64, 64, "fp16", 1.0, seed=3)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o, st = run_gpu(q, k, v, la, 1, stream=s.cuda_stream)
+    ro, rs = gla_forward(q, k, v, la, 1)
+    check(o, ro, True, "stream out")
+    check(st, rs, True, "stream state")
