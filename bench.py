@@ -1,0 +1,287 @@
+#!/usr/bin/env python3
+"""Throughput of the chunkwise GLA forward pass (key-only decay, four scan
+directions) on one MI355X, against the HBM roofline, with the CPU oracle timed
+beside it.
+
+A step is one pass of the workload's call list through gla_chunk_fwd: for the
+16.4K-token grid (B=1, 12 heads, 128x128 tokens, d_k=d_v=64, fp16) the four scan
+directions.  Inputs sit in HBM before timing starts.  Each call reads its own
+device copy of the inputs and writes its own outputs, and the copies are cycled
+so that the bytes touched between two reuses of a copy exceed the 256 MB
+last-level (Infinity) cache: every call streams from HBM as a real layer
+stack would, instead of re-reading cache-resident data.
+
+Prints ONE JSON line on stdout; details go to stderr.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GLA chunkwise fwd tokens/s at 1.6K & 16.4K tokens; % of HBM/MFMA roofline"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 MFMA, published
+LLC_BYTES = 256 << 20           # Infinity Cache
+KERNEL_SRC = os.path.join(ROOT, "recurrent_vision_token_amd", "csrc", "gla_kernels.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic(wl):
+    """Per-call algorithmic bytes and flops of the method (per token-head unit)."""
+    es = 2 if wl.dtype == "fp16" else 4
+    th = wl.B * wl.heads * wl.T                         # token-heads per call
+    bh = wl.B * wl.heads
+    io_bytes = th * es * (3 * wl.d_k + 2 * wl.d_v)      # read q, k, log_alpha, v; write out
+    state_bytes = bh * wl.d_k * wl.d_v * 4              # final state
+    flops = th * ((wl.chunk + 1) * (wl.d_k + wl.d_v) + 4 * wl.d_k * wl.d_v)
+    return {"bytes": io_bytes + state_bytes, "io_bytes_per_token_head": es * (3 * wl.d_k + 2 * wl.d_v),
+            "flops": flops, "token_heads": th}
+
+
+def kernel_bytes(wl, n_spans):
+    """Algorithmic bytes each kernel of one call moves (its own reads and writes)."""
+    es = 2 if wl.dtype == "fp16" else 4
+    th = wl.B * wl.heads * wl.T
+    bh = wl.B * wl.heads
+    st = wl.d_k * wl.d_v * 4
+    out = {"chunk_output": th * es * (3 * wl.d_k + 2 * wl.d_v) + bh * st + (bh * n_spans * st if n_spans > 1 else 0)}
+    if n_spans > 1:
+        out["span_summary"] = th * es * (2 * wl.d_k + wl.d_v) + bh * n_spans * (st + 4 * wl.d_k)
+        out["span_scan"] = bh * n_spans * (2 * st + 4 * wl.d_k)
+    return out
+
+
+class Runner:
+    """Device copies of a workload's inputs, cycled across calls."""
+
+    def __init__(self, wl, torch, min_sets_bytes=2 * LLC_BYTES):
+        from recurrent_vision_token_amd.workloads import workload_inputs
+        self.torch = torch
+        self.wl = wl
+        self.dev = torch.device("cuda:0")
+        calls = wl.calls
+        host = {}
+        for seed, _ in calls:
+            if seed not in host:
+                host[seed] = workload_inputs(wl, seed)
+        self.host = host
+        per_call = algorithmic(wl)["bytes"]
+        reps = max(1, math.ceil(min_sets_bytes / (per_call * len(calls))))
+        self.sets = []
+        for _ in range(reps):
+            for seed, d in calls:
+                q, k, v, la = (torch.from_numpy(x).to(self.dev) for x in host[seed])
+                out = torch.empty(v.shape, dtype=v.dtype, device=self.dev)
+                fs = torch.empty((wl.B, wl.heads, wl.d_k, wl.d_v), dtype=torch.float32, device=self.dev)
+                self.sets.append((q, k, v, la, out, fs, d))
+        self.cursor = 0
+        torch.cuda.synchronize()
+
+    def step(self, events=None):
+        """One pass of the call list; events: list of 4-event lists, one per call."""
+        from recurrent_vision_token_amd import _lib
+        from recurrent_vision_token_amd import gla_chunk_fwd
+        for c in range(len(self.wl.calls)):
+            q, k, v, la, out, fs, d = self.sets[self.cursor]
+            self.cursor = (self.cursor + 1) % len(self.sets)
+            if events is not None:
+                rc = _lib.set_kernel_events([e.cuda_event for e in events[c]])
+                if rc != 0:
+                    raise RuntimeError("gla_set_kernel_events failed: %d" % rc)
+            gla_chunk_fwd(q, k, v, la, d, out=out, final_state=fs)
+
+
+def time_workload(wl, torch, steps, warmup):
+    r = Runner(wl, torch)
+    ncall = len(wl.calls)
+    log("[bench] %s: %d device input sets (%.0f MB), %d calls/step" %
+        (wl.name, len(r.sets), len(r.sets) * algorithmic(wl)["bytes"] / 1e6, ncall))
+    for _ in range(warmup):
+        r.step()
+    torch.cuda.synchronize()
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(ncall)]
+           for _ in range(steps)]
+    stream = torch.cuda.current_stream()
+    for per_step in evs:                      # materialise the HIP events
+        for per_call in per_step:
+            for e in per_call:
+                e.record(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        r.step(evs[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / steps
+    k_ms = {"span_summary": [], "span_scan": [], "chunk_output": [], "call": []}
+    for per_step in evs:
+        for e in per_step:
+            k_ms["span_summary"].append(e[0].elapsed_time(e[1]))
+            k_ms["span_scan"].append(e[1].elapsed_time(e[2]))
+            k_ms["chunk_output"].append(e[2].elapsed_time(e[3]))
+            k_ms["call"].append(e[0].elapsed_time(e[3]))
+    mean = {k: sum(v) / len(v) for k, v in k_ms.items()}
+    return r, ms_step, mean
+
+
+def n_spans_of(wl):
+    from recurrent_vision_token_amd import _lib
+    return _lib.plan_spans(wl.dtype, wl.B, wl.heads, wl.H, wl.W, wl.d_k, wl.d_v, wl.chunk)[1]
+
+
+def traffic_from_profiles(wl_name, kernel):
+    """HBM bytes per launch from committed counter runs, if they match this source."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % wl_name)
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+        src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+        if rec.get("kernel_source_sha256") != src_hash:
+            return None
+        return rec["kernels"][kernel]["hbm_bytes_per_launch"]
+    except Exception:
+        return None
+
+
+def cpu_baseline(wl, host, budget_s=12.0):
+    """The oracle as it stands, on a bounded sample of the same workload."""
+    from oracle import gla_forward
+    t0 = time.perf_counter()
+    c0 = time.process_time()
+    tokens = 0
+    done = 0
+    for seed, d in wl.calls:
+        q, k, v, la = host[seed]
+        gla_forward(q, k, v, la, d)
+        tokens += wl.B * wl.T
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    wall = time.perf_counter() - t0
+    cpu = time.process_time() - c0
+    cores = max(1, int(round(cpu / wall)))
+    return {"value": tokens / wall, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": "%d of the %d calls of one step (%s, full size, numpy float64 token loop), "
+                      "%.1f s wall" % (done, len(wl.calls), wl.name, wall)}
+
+
+def describe(wl):
+    dirs = sorted(set(d for _, d in wl.calls))
+    return ("%s: B=%d, heads=%d, %dx%d grid (%d tokens), d_k=%d, d_v=%d, chunk=%d, %s, "
+            "gate_std=%g, seeds %s, scan dirs %s, %d calls per step" %
+            (wl.name, wl.B, wl.heads, wl.H, wl.W, wl.T, wl.d_k, wl.d_v, wl.chunk, wl.dtype,
+             wl.gate_std, sorted(set(s for s, _ in wl.calls)), dirs, len(wl.calls)))
+
+
+def summarize(wl, ms_step, mean):
+    alg = algorithmic(wl)
+    ncall = len(wl.calls)
+    tokens_step = ncall * wl.B * wl.T
+    spans = n_spans_of(wl)
+    kb = kernel_bytes(wl, spans)
+    present = [k for k in kb if mean[k] > 0]
+    dom = max(present, key=lambda k: mean[k])
+    ach = kb[dom] / (mean[dom] * 1e-3) / 1e9
+    path_gbps = alg["bytes"] / (mean["call"] * 1e-3) / 1e9
+    return {
+        "tokens_per_step": tokens_step,
+        "value": tokens_step / (ms_step * 1e-3),
+        "dominant": dom,
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": traffic_from_profiles(wl.name, dom),
+                     "kernel": dom, "algorithmic_bytes_per_launch": kb[dom],
+                     "avg_launch_us": round(mean[dom] * 1e3, 2)},
+        "path": {"gpu_us_per_call": round(mean["call"] * 1e3, 2),
+                 "algorithmic_bytes_per_call": alg["bytes"],
+                 "achieved_GBps": round(path_gbps, 1),
+                 "hbm_frac": round(path_gbps / HBM_PEAK_GBPS, 4),
+                 "mfma_frac": round(alg["flops"] / (mean["call"] * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+                 "kernel_us": {k: round(mean[k] * 1e3, 2) for k in ("span_summary", "span_scan", "chunk_output")},
+                 "n_spans": spans},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="hires16.4k")
+    ap.add_argument("--secondary", default="gtr1.6k", help="'' to skip")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(sequences shard across GPUs with no communication; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if int(os.environ.get("RANK", "0")) != 0:
+        return
+
+    import torch
+    from recurrent_vision_token_amd import load
+    from recurrent_vision_token_amd.workloads import WORKLOADS
+
+    load()  # fails loudly if the HIP library is not built
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a HIP device")
+
+    wl = WORKLOADS[args.workload]
+    runner, ms_step, mean = time_workload(wl, torch, args.steps, args.warmup)
+    main_sum = summarize(wl, ms_step, mean)
+    log("[bench] %s: %.3f ms/step, %.3e tokens/s, GPU %.2f us/call, kernels %s" %
+        (wl.name, ms_step, main_sum["value"], main_sum["path"]["gpu_us_per_call"],
+         main_sum["path"]["kernel_us"]))
+
+    secondary = None
+    if args.secondary:
+        wl2 = WORKLOADS[args.secondary]
+        _, ms2, mean2 = time_workload(wl2, torch, max(20, args.steps), max(5, args.warmup))
+        s2 = summarize(wl2, ms2, mean2)
+        secondary = {"workload": describe(wl2), "value": s2["value"], "unit": "tokens/s",
+                     "ms_per_step": round(ms2, 4), "roofline": s2["roofline"], "path": s2["path"]}
+        log("[bench] %s: %.3f ms/step, %.3e tokens/s, GPU %.2f us/call" %
+            (wl2.name, ms2, s2["value"], s2["path"]["gpu_us_per_call"]))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, runner.host)
+        log("[bench] cpu oracle: %.3e tokens/s on %d core(s)" % (cpu["value"], cpu["cores"]))
+
+    line = {
+        "metric": METRIC,
+        "value": main_sum["value"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if wl.dtype == "fp16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": describe(wl), "tokens_per_step": main_sum["tokens_per_step"],
+                   "input_copies_cycled": len(runner.sets)},
+        "roofline": main_sum["roofline"],
+        "path": main_sum["path"],
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -91,6 +91,31 @@ int gla_chunk_fwd_f32(const float* q, const float* k, const float* v, const floa
                       int scan_dir, int B, int heads, int H, int W, int d_k, int d_v, int chunk,
                       float* out, float* final_state, void* stream);
 
+/*
+ * Work split the forward call would use on the current device: each sequence
+ * of ceil(H*W/64) chunks is cut into n_spans spans of span_chunks chunks (the
+ * last may be shorter), one output workgroup per (batch, head, span).  When
+ * n_spans > 1 the call also runs the span-summary and span-scan kernels and
+ * takes a stream-ordered workspace of B*heads*n_spans*(d_k*d_v + d_k) floats.
+ * use_f32 selects the float32 entry.  Reads device attributes (a HIP call);
+ * returns the same argument errors as the forward entry points.
+ */
+int gla_plan_spans(int use_f32, int B, int heads, int H, int W, int d_k, int d_v, int chunk,
+                   int* span_chunks, int* n_spans);
+
+/*
+ * Measurement hook (for benchmarks and profilers, not needed for computing).
+ * events: n = 4 hipEvent_t handles (as void*), or n = 0 to clear.  The next
+ * forward call made by the calling thread records events[0] before its first
+ * kernel, events[1] after the span-summary kernel, events[2] after the
+ * span-scan kernel (when a sequence is not split into spans, events[0..2] are
+ * recorded back to back) and events[3] after the output kernel, all on that
+ * call's stream; the hook then clears itself.  The caller owns the events.
+ * Returns GLA_ERR_NULL if n = 4 and a handle is NULL, GLA_ERR_SHAPE if n is
+ * neither 0 nor 4.
+ */
+int gla_set_kernel_events(void* const* events, int n);
+
 /* Static, human-readable text for a status code. */
 const char* gla_status_str(int status);
 

@@ -17,7 +17,8 @@ STATUS = {
     0: "GLA_OK", -1: "GLA_ERR_NULL", -2: "GLA_ERR_SHAPE", -3: "GLA_ERR_UNSUPPORTED",
     -4: "GLA_ERR_ALIGN", -5: "GLA_ERR_SCAN_DIR", -6: "GLA_ERR_ALIAS", -7: "GLA_ERR_HIP",
 }
-EXPORTED = ("gla_chunk_fwd", "gla_chunk_fwd_f32", "gla_status_str", "gla_version")
+EXPORTED = ("gla_chunk_fwd", "gla_chunk_fwd_f32", "gla_plan_spans", "gla_set_kernel_events",
+            "gla_status_str", "gla_version")
 
 _lib = None
 
@@ -45,6 +46,10 @@ def load():
         fn.restype = ctypes.c_int
     lib.gla_status_str.argtypes = [ctypes.c_int]
     lib.gla_status_str.restype = ctypes.c_char_p
+    lib.gla_plan_spans.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i)]
+    lib.gla_plan_spans.restype = ctypes.c_int
+    lib.gla_set_kernel_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
+    lib.gla_set_kernel_events.restype = ctypes.c_int
     lib.gla_version.argtypes = []
     lib.gla_version.restype = ctypes.c_int
     _lib = lib
@@ -101,3 +106,22 @@ def gla_chunk_fwd(q, k, v, log_alpha, scan_dir, chunk=64, out=None, final_state=
     if rc != GLA_OK:
         raise GlaError(rc, status_str(rc))
     return out, final_state
+
+
+def set_kernel_events(handles):
+    """Arm the measurement hook with four hipEvent_t handles (ints), or clear it."""
+    lib = load()
+    if not handles:
+        return lib.gla_set_kernel_events(None, 0)
+    arr = (ctypes.c_void_p * len(handles))(*handles)
+    return lib.gla_set_kernel_events(arr, len(handles))
+
+
+def plan_spans(dtype, B, heads, H, W, d_k, d_v, chunk=64):
+    """(span_chunks, n_spans) the forward call would use on the current device."""
+    a, b = ctypes.c_int(0), ctypes.c_int(0)
+    rc = load().gla_plan_spans(1 if dtype == "fp32" else 0, B, heads, H, W, d_k, d_v, chunk,
+                               ctypes.byref(a), ctypes.byref(b))
+    if rc != GLA_OK:
+        raise GlaError(rc, status_str(rc))
+    return a.value, b.value

@@ -22,16 +22,30 @@ struct Range {
 
 bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 
-// Multiprocessor count per device, read once per device.
-std::atomic<int> g_cu_count[kMaxDevices];
+// Events of the measurement hook, per calling thread (see gla_set_kernel_events).
+thread_local hipEvent_t t_events[4];
+thread_local bool t_events_set = false;
 
-int cu_count(int dev) {
+// Output-kernel workgroup slots per device (CUs x resident workgroups per CU),
+// read once per (device, variant).
+constexpr int kVariants = 8;
+std::atomic<int> g_slots[kMaxDevices][kVariants];
+
+int variant_index(gla::Dtype dt, int d_k, int d_v) {
+  return (dt == gla::Dtype::kF16 ? 0 : 4) + (d_k == 128 ? 2 : 0) + (d_v == 128 ? 1 : 0);
+}
+
+int output_slots(int dev, gla::Dtype dt, int d_k, int d_v) {
+  const int vi = variant_index(dt, d_k, d_v);
   if (dev < 0 || dev >= kMaxDevices) return 256;
-  int n = g_cu_count[dev].load(std::memory_order_relaxed);
+  int n = g_slots[dev][vi].load(std::memory_order_relaxed);
   if (n > 0) return n;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-    n = 256;
-  g_cu_count[dev].store(n, std::memory_order_relaxed);
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  n = cus * gla::output_blocks_per_cu(dt, d_k, d_v);
+  g_slots[dev][vi].store(n, std::memory_order_relaxed);
   return n;
 }
 
@@ -49,22 +63,34 @@ int span_override() {
   return value;
 }
 
-// Chunks per span: enough workgroups to cover every CU about twice, and no
-// span split at all when the (batch, head) sequences alone do that.
-int plan_span_chunks(long long bh, int n_chunks, int cus) {
+// Chunks per span.  The output kernel's time is the longest chain of chunks any
+// workgroup slot processes; with W = bh * ceil(n_chunks / m) workgroups over
+// `slots` resident slots that is ceil(W / slots) * m.  Take the smallest m that
+// minimises it (shorter spans also mean a cheaper span scan), and no split at
+// all when the sequences alone fill the slots.
+int plan_span_chunks(long long bh, int n_chunks, int slots) {
   const int forced = span_override();
   if (forced > 0) return forced < n_chunks ? forced : n_chunks;
-  const long long target = 2LL * cus;
-  const long long total = bh * n_chunks;
-  long long m = (total + target - 1) / target;
-  if (m < 1) m = 1;
-  if (m > n_chunks) m = n_chunks;
-  return (int)m;
+  if (bh >= slots) return n_chunks;
+  // one wave of workgroups at m1 chunks each bounds the optimum from above
+  const long long per_seq = slots / bh;
+  const int m1 = (int)((n_chunks + per_seq - 1) / per_seq);
+  long long best_cost = -1;
+  int best_m = n_chunks;
+  for (int m = 1; m <= m1; ++m) {
+    const long long wgs = bh * ((n_chunks + m - 1) / m);
+    const long long cost = ((wgs + slots - 1) / slots) * m;
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best_m = m;
+    }
+  }
+  return best_m;
 }
 
 int forward(gla::Dtype dt, size_t esize, const void* q, const void* k, const void* v,
             const void* la, int scan_dir, int B, int heads, int H, int W, int d_k, int d_v,
-            int chunk, void* out, float* final_state, void* stream) {
+            int chunk, void* out, float* final_state, void* stream, int* plan_only = nullptr) {
   if (scan_dir < 0 || scan_dir > 4) return GLA_ERR_SCAN_DIR;
   if (!q || !k || !v || !la || !out) return GLA_ERR_NULL;
   if (B < 1 || heads < 1 || H < 1 || W < 1 || d_k < 1 || d_v < 1) return GLA_ERR_SHAPE;
@@ -95,9 +121,14 @@ int forward(gla::Dtype dt, size_t esize, const void* q, const void* k, const voi
   const int n_chunks = (int)((T + kChunk - 1) / kChunk);
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return GLA_ERR_HIP;
-  const int span_chunks = plan_span_chunks(BH, n_chunks, cu_count(dev));
+  const int span_chunks = plan_span_chunks(BH, n_chunks, output_slots(dev, dt, d_k, d_v));
   const int n_spans = (n_chunks + span_chunks - 1) / span_chunks;
   if (BH * n_spans > (1LL << 31) - 1) return GLA_ERR_SHAPE;
+  if (plan_only != nullptr) {
+    plan_only[0] = span_chunks;
+    plan_only[1] = n_spans;
+    return GLA_OK;
+  }
 
   gla::FwdParams p{};
   p.q = q;
@@ -126,7 +157,9 @@ int forward(gla::Dtype dt, size_t esize, const void* q, const void* k, const voi
     p.span_state = static_cast<float*>(ws);
     p.span_gate = p.span_state + state_elems;
   }
-  const hipError_t e = gla::launch_forward(dt, d_k, d_v, p, st);
+  const hipEvent_t* ev = t_events_set ? t_events : nullptr;
+  t_events_set = false;
+  const hipError_t e = gla::launch_forward(dt, d_k, d_v, p, st, ev);
   if (ws != nullptr && hipFreeAsync(ws, st) != hipSuccess) return GLA_ERR_HIP;
   return e == hipSuccess ? GLA_OK : GLA_ERR_HIP;
 }
@@ -155,6 +188,43 @@ int gla_chunk_fwd_f32(const float* q, const float* k, const float* v, const floa
   } catch (...) {
     return GLA_ERR_HIP;
   }
+}
+
+int gla_plan_spans(int use_f32, int B, int heads, int H, int W, int d_k, int d_v, int chunk,
+                   int* span_chunks, int* n_spans) {
+  if (span_chunks == nullptr || n_spans == nullptr) return GLA_ERR_NULL;
+  // Validation only looks at pointer values; these placeholders are distinct,
+  // aligned and never dereferenced.
+  const uintptr_t base = (uintptr_t)1 << 40;
+  const uintptr_t gap = (uintptr_t)1 << 38;
+  int plan[2] = {0, 0};
+  int rc;
+  try {
+    rc = forward(use_f32 ? gla::Dtype::kF32 : gla::Dtype::kF16, use_f32 ? 4 : 2,
+                 (const void*)base, (const void*)(base + gap), (const void*)(base + 2 * gap),
+                 (const void*)(base + 3 * gap), 0, B, heads, H, W, d_k, d_v, chunk,
+                 (void*)(base + 4 * gap), nullptr, nullptr, plan);
+  } catch (...) {
+    return GLA_ERR_HIP;
+  }
+  if (rc != GLA_OK) return rc;
+  *span_chunks = plan[0];
+  *n_spans = plan[1];
+  return GLA_OK;
+}
+
+int gla_set_kernel_events(void* const* events, int n) {
+  if (n == 0) {
+    t_events_set = false;
+    return GLA_OK;
+  }
+  if (n != 4) return GLA_ERR_SHAPE;
+  if (events == nullptr) return GLA_ERR_NULL;
+  for (int i = 0; i < 4; ++i)
+    if (events[i] == nullptr) return GLA_ERR_NULL;
+  for (int i = 0; i < 4; ++i) t_events[i] = static_cast<hipEvent_t>(events[i]);
+  t_events_set = true;
+  return GLA_OK;
 }
 
 const char* gla_status_str(int status) {

@@ -26,11 +26,16 @@ struct FwdParams {
   int n_spans;          // ceil(n_chunks / span_chunks)
 };
 
+// Output-kernel workgroups resident per CU for this variant (occupancy).
+int output_blocks_per_cu(Dtype dt, int d_k, int d_v);
+
 // True when a kernel family is compiled for this (dtype, d_k, d_v).
 bool has_variant(Dtype dt, int d_k, int d_v);
 
 // Enqueue the span-summary, span-scan and output kernels on `stream`.
 // The caller has validated p and supplied a workspace when n_spans > 1.
-hipError_t launch_forward(Dtype dt, int d_k, int d_v, const FwdParams& p, hipStream_t stream);
+// events: null, or four hipEvent_t recorded around the kernels (see gla.h).
+hipError_t launch_forward(Dtype dt, int d_k, int d_v, const FwdParams& p, hipStream_t stream,
+                          hipEvent_t const* events);
 
 }  // namespace gla

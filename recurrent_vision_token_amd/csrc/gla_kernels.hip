@@ -386,7 +386,7 @@ __global__ __launch_bounds__(kThreads) void span_scan_kernel(FwdParams p) {
   const size_t gbase = (size_t)bh * p.n_spans * DK + dim;
   float s = 0.f;
   int sp = 0;
-  constexpr int U = 8;
+  constexpr int U = 32;  // summaries loaded ahead of the dependent chain
   for (; sp + U <= p.n_spans; sp += U) {
     float L[U], G[U];
 #pragma unroll
@@ -400,11 +400,23 @@ __global__ __launch_bounds__(kThreads) void span_scan_kernel(FwdParams p) {
       s = G[u] * s + L[u];
     }
   }
-  for (; sp < p.n_spans; ++sp) {
-    const float L = p.span_state[sbase + (size_t)sp * DK * DV];
-    const float G = p.span_gate[gbase + (size_t)sp * DK];
-    p.span_state[sbase + (size_t)sp * DK * DV] = s;
-    s = G * s + L;
+  const int rest = p.n_spans - sp;
+  if (rest > 0) {
+    float L[U], G[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (u < rest) {
+        L[u] = p.span_state[sbase + (size_t)(sp + u) * DK * DV];
+        G[u] = p.span_gate[gbase + (size_t)(sp + u) * DK];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (u < rest) {
+        p.span_state[sbase + (size_t)(sp + u) * DK * DV] = s;
+        s = G[u] * s + L[u];
+      }
+    }
   }
 }
 
@@ -671,25 +683,593 @@ __global__ __launch_bounds__(kThreads) void chunk_output_kernel(FwdParams p) {
   }
 }
 
+// ===========================================================================
+// Float16 kernels.  The per-chunk elementwise work (cumulative decay, anchored
+// q / k scalings, decayed keys) runs in MFMA-friendly register layouts so that
+// every LDS access is a 64- or 128-bit vector op:
+//  * log-alpha is staged transposed ([d_k][token]); cumulative sums over tokens
+//    are 16x16x16 MFMAs against constant triangular matrices (log2(e) folded
+//    in as an exact hi + lo pair), landing either as "4 key dims of one token
+//    per lane" (output kernel) or "4 tokens of one key dim per lane" (summary);
+//  * the decay over each 16-token sub-block is broadcast along each 16-lane
+//    row with DPP, so the per-(dim, sub-block) factors need no exp and no LDS;
+//  * keys are pre-scaled into the variants the causal score tiles need, so the
+//    score MFMAs read unscaled operands;
+//  * the decayed keys for the state update are transposed with an identity
+//    MFMA (exact: one non-zero product per output).
+
+__device__ __forceinline__ float row_bcast15(float x) {
+  // every lane of a 16-lane row receives the row's lane 15 value
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                0x15F, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// log2(e) split into two binary16 values whose sum is log2(e) to ~1e-7.
+constexpr float kLog2eHi = 1.4423828125f;          // fp16(log2 e)
+constexpr float kLog2eLo = 1.4426950408889634f - 1.4423828125f;
+
+template <int DK, int DV>
+struct OutSmemH {
+  static constexpr int QS = DK + 8;      // [token][d_k] rows
+  static constexpr int AS = kChunk + 8;  // [*][token] rows
+  static constexpr int OS = DV + 8;      // [token][d_v] rows
+  static constexpr int KV_ROWS = 48 + 32 + 16;
+  static constexpr int KV_ELEMS = (KV_ROWS * QS > kChunk * OS) ? KV_ROWS * QS : kChunk * OS;
+  static constexpr int LAT_ELEMS = (DK * AS > kChunk * AS) ? DK * AS : kChunk * AS;
+  alignas(16) f16 q[kChunk * QS];    // raw q, then q_t*exp(c_t)   (c: decay inside the sub-block)
+  alignas(16) f16 qt[kChunk * QS];   // q_t*exp(b_t)               (b: decay from the chunk start)
+  alignas(16) f16 k[kChunk * QS];    // raw k, then k_s*exp(-c_s)
+  alignas(16) f16 kv[KV_ELEMS];      // k decayed to the end of its sub-block (rows 0..47), of the
+                                     // next one (48..79), of the one after (80..95); then O staging
+  alignas(16) f16 lat[LAT_ELEMS];    // log-alpha^T [d_k][token], then A[t][s]
+  alignas(16) f16 vt[DV * AS];       // V^T [d_v][token]
+  alignas(16) f16 klt[DK * AS];      // (k_s*exp(b_last-b_s))^T [d_k][token]
+  alignas(16) float g[DK];           // exp(b_last)
+};
+
+// Row pieces of q and k, token-pair pieces of log-alpha and v (for the
+// transposed tiles).  Pieces past the sequence end read as zero.
+template <int DK, int DV, bool WITH_Q, bool K_ROWS>
+struct LoaderH {
+  static constexpr int PK = DK / 8, PV = DV / 8;   // 16-byte pieces per token row
+  static constexpr int NK = kChunk * PK / kThreads;          // row pieces per thread
+  static constexpr int NKP = (kChunk / 2) * PK / kThreads;   // d_k token pairs per thread
+  static constexpr int NVP = (kChunk / 2) * PV / kThreads;   // d_v token pairs per thread
+  static_assert(NK >= 1 && NKP >= 1 && NVP >= 1, "tile too small");
+  uint4 rq[WITH_Q ? NK : 1];
+  uint4 rk[K_ROWS ? NK : 2 * NKP];
+  uint4 rl[2 * NKP];
+  uint4 rv[2 * NVP];
+
+  __device__ __forceinline__ static uint4 ld(const f16* p) {
+    return *reinterpret_cast<const uint4*>(p);
+  }
+
+  __device__ __forceinline__ void load(const f16* q, const f16* k, const f16* la, const f16* v,
+                                       size_t off_k, size_t off_v, int t0, int valid, int H,
+                                       int W, int dir) {
+    const int tid = threadIdx.x;
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    if (WITH_Q || K_ROWS) {
+#pragma unroll
+      for (int j = 0; j < NK; ++j) {
+        const int id = tid + kThreads * j;
+        const int tok = id / PK, pc = id - tok * PK;
+        const bool in = tok < valid;
+        const size_t o = in ? off_k + (size_t)cell_of(t0 + tok, H, W, dir) * DK + pc * 8 : 0;
+        if (WITH_Q) rq[j] = in ? ld(q + o) : z;
+        if (K_ROWS) rk[j] = in ? ld(k + o) : z;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NKP; ++j) {
+      const int id = tid + kThreads * j;
+      const int tp = id / PK, pc = id - tp * PK;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int tok = 2 * tp + h;
+        const bool in = tok < valid;
+        const size_t o = in ? off_k + (size_t)cell_of(t0 + tok, H, W, dir) * DK + pc * 8 : 0;
+        rl[2 * j + h] = in ? ld(la + o) : z;
+        if (!K_ROWS) rk[2 * j + h] = in ? ld(k + o) : z;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NVP; ++j) {
+      const int id = tid + kThreads * j;
+      const int tp = id / PV, pc = id - tp * PV;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int tok = 2 * tp + h;
+        const bool in = tok < valid;
+        rv[2 * j + h] =
+            in ? ld(v + off_v + (size_t)cell_of(t0 + tok, H, W, dir) * DV + pc * 8) : z;
+      }
+    }
+  }
+
+  // Write a token pair (a, b) of 8-element pieces transposed: dst[(8pc+u)*AS + 2tp].
+  __device__ __forceinline__ static void put_pair_t(f16* dst, int AS, int pc, int tp, uint4 a,
+                                                    uint4 b) {
+    const f16x8 x = __builtin_bit_cast(f16x8, a);
+    const f16x8 y = __builtin_bit_cast(f16x8, b);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      f16x2 pr;
+      pr[0] = x[u];
+      pr[1] = y[u];
+      *reinterpret_cast<f16x2*>(dst + (8 * pc + u) * AS + 2 * tp) = pr;
+    }
+  }
+
+  __device__ __forceinline__ void store(f16* sq, f16* sk, int QS, f16* skt, f16* slat, f16* svt,
+                                        int AS) const {
+    const int tid = threadIdx.x;
+    if (WITH_Q || K_ROWS) {
+#pragma unroll
+      for (int j = 0; j < NK; ++j) {
+        const int id = tid + kThreads * j;
+        const int tok = id / PK, pc = id - tok * PK;
+        if (WITH_Q) *reinterpret_cast<uint4*>(sq + tok * QS + pc * 8) = rq[j];
+        if (K_ROWS) *reinterpret_cast<uint4*>(sk + tok * QS + pc * 8) = rk[j];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NKP; ++j) {
+      const int id = tid + kThreads * j;
+      const int tp = id / PK, pc = id - tp * PK;
+      put_pair_t(slat, AS, pc, tp, rl[2 * j], rl[2 * j + 1]);
+      if (!K_ROWS) put_pair_t(skt, AS, pc, tp, rk[2 * j], rk[2 * j + 1]);
+    }
+#pragma unroll
+    for (int j = 0; j < NVP; ++j) {
+      const int id = tid + kThreads * j;
+      const int tp = id / PV, pc = id - tp * PV;
+      put_pair_t(svt, AS, pc, tp, rv[2 * j], rv[2 * j + 1]);
+    }
+  }
+};
+
+// Constant 16x16x16 MFMA B operands, lane (n, g) holding rows 4g..4g+3 of column n:
+// U[s][t] = (s <= t) * v, and the identity.
+__device__ __forceinline__ f16x4 upper_incl(float v) {
+  const int lane = threadIdx.x & 63, n16 = lane & 15, g = lane >> 4;
+  f16x4 r;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) r[u] = (f16)((4 * g + u <= n16) ? v : 0.f);
+  return r;
+}
+__device__ __forceinline__ f16x4 identity16() {
+  const int lane = threadIdx.x & 63, n16 = lane & 15, g = lane >> 4;
+  f16x4 r;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) r[u] = (f16)((4 * g + u == n16) ? 1.f : 0.f);
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// Output kernel, float16.
+template <int DK, int DV>
+__global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 2 : 1) void chunk_output_f16_kernel(
+    FwdParams p) {
+  using SM = OutSmemH<DK, DV>;
+  __shared__ SM sm;
+  constexpr int QS = SM::QS, AS = SM::AS, OS = SM::OS;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n16 = lane & 15, g = lane >> 4;
+
+  const int bh = blockIdx.x / p.n_spans;
+  const int span = blockIdx.x - bh * p.n_spans;
+  const int b = bh / p.heads;
+  const int dir = (p.scan_dir == 4) ? (b & 3) : p.scan_dir;
+  const size_t off_k = (size_t)bh * p.T * DK;
+  const size_t off_v = (size_t)bh * p.T * DV;
+  const int c_begin = span * p.span_chunks;
+  const int c_end = min(c_begin + p.span_chunks, p.n_chunks);
+
+  const f16* q = static_cast<const f16*>(p.q);
+  const f16* k = static_cast<const f16*>(p.k);
+  const f16* la = static_cast<const f16*>(p.la);
+  const f16* v = static_cast<const f16*>(p.v);
+  f16* out = static_cast<f16*>(p.out);
+
+  StateRegs<DK, DV> st;
+  {
+    const float* src =
+        (span > 0) ? p.span_state + ((size_t)bh * p.n_spans + span) * DK * DV : nullptr;
+#pragma unroll
+    for (int j = 0; j < StateRegs<DK, DV>::NC; ++j) {
+      const int col = 16 * (wave + 4 * j) + n16;
+#pragma unroll
+      for (int r = 0; r < StateRegs<DK, DV>::NR; ++r)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          st.s[r][j][u] = src ? src[(16 * r + 4 * g + u) * DV + col] : 0.f;
+    }
+  }
+
+  const f16x4 u_hi = upper_incl(kLog2eHi), u_lo = upper_incl(kLog2eLo);
+  const f16x4 ident = identity16();
+  const uint32_t tile_codes = (wave == 0) ? 0x313000u
+                            : (wave == 1) ? 0x321110u
+                            : (wave == 2) ? 0x2120u
+                                          : 0x3322u;
+  const int n_tiles = (wave < 2) ? 3 : 2;
+  f16* const kv1 = sm.kv;
+  f16* const kv2 = sm.kv + 48 * QS;
+  f16* const kv3 = sm.kv + 80 * QS;
+  f16* const so = sm.kv;   // output staging reuses the key-variant region
+  f16* const sa = sm.lat;  // score tile reuses the log-alpha^T region
+
+  LoaderH<DK, DV, true, true> ld;
+  ld.load(q, k, la, v, off_k, off_v, c_begin * kChunk, min(kChunk, p.T - c_begin * kChunk), p.H,
+          p.W, dir);
+  for (int c = c_begin; c < c_end; ++c) {
+    const int t0 = c * kChunk;
+    const int valid = min(kChunk, p.T - t0);
+    ld.store(sm.q, sm.k, QS, nullptr, sm.lat, sm.vt, AS);
+    if (c + 1 < c_end) {
+      const int t1 = t0 + kChunk;
+      ld.load(q, k, la, v, off_k, off_v, t1, min(kChunk, p.T - t1), p.H, p.W, dir);
+    }
+    __syncthreads();
+
+    // ---- Phase P: wave w owns key dims 16*db .. 16*db+15, db = w (+4).
+#pragma unroll
+    for (int dbi = 0; dbi < DK / 64; ++dbi) {
+      const int db = wave + 4 * dbi;
+      const int dim0 = 16 * db + 4 * g;  // this lane's 4 key dims in the row layout
+      f32x4 eq[4], ek[4], ed[4];
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        // c*log2(e) at token 16I+n16, dims dim0..dim0+3
+        const f16x4 a = *reinterpret_cast<const f16x4*>(sm.lat + (16 * db + n16) * AS + 16 * I + 4 * g);
+        f32x4 c2 = {0.f, 0.f, 0.f, 0.f};
+        c2 = mma16(a, u_hi, c2);
+        c2 = mma16(a, u_lo, c2);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          eq[I][u] = exp2_fast(c2[u]);
+          ek[I][u] = exp2_fast(-c2[u]);
+          ed[I][u] = row_bcast15(eq[I][u]);  // exp(decay over sub-block I)
+        }
+      }
+      f32x4 gl;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) gl[u] = ed[0][u] * ed[1][u] * ed[2][u] * ed[3][u];
+      if (n16 == 0) *reinterpret_cast<f32x4*>(sm.g + dim0) = gl;
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        const int row = 16 * I + n16;
+        const f16x4 q4 = *reinterpret_cast<const f16x4*>(sm.q + row * QS + dim0);
+        const f16x4 k4 = *reinterpret_cast<const f16x4*>(sm.k + row * QS + dim0);
+        f16x4 ql, qt, kd, kv_1, kv_2, kv_3, klh;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          float e_start = 1.f;  // exp(b at the end of sub-block I-1)
+#pragma unroll
+          for (int L = 0; L < I; ++L) e_start *= ed[L][u];
+          const float qf = (float)q4[u];
+          ql[u] = (f16)(qf * eq[I][u]);
+          qt[u] = (f16)(qf * (eq[I][u] * e_start));
+          const float kf = (float)k4[u] * ek[I][u];
+          kd[u] = (f16)kf;
+          float kx = kf * ed[I][u];  // decayed to the end of sub-block I
+          kv_1[u] = (f16)kx;
+#pragma unroll
+          for (int L = I + 1; L < 4; ++L) {
+            kx *= ed[L][u];
+            if (L == I + 1) kv_2[u] = (f16)kx;
+            if (L == I + 2) kv_3[u] = (f16)kx;
+          }
+          klh[u] = (f16)kx;  // decayed to the chunk end
+        }
+        *reinterpret_cast<f16x4*>(sm.q + row * QS + dim0) = ql;
+        *reinterpret_cast<f16x4*>(sm.qt + row * QS + dim0) = qt;
+        *reinterpret_cast<f16x4*>(sm.k + row * QS + dim0) = kd;
+        if (I <= 2) *reinterpret_cast<f16x4*>(kv1 + row * QS + dim0) = kv_1;
+        if (I <= 1) *reinterpret_cast<f16x4*>(kv2 + row * QS + dim0) = kv_2;
+        if (I == 0) *reinterpret_cast<f16x4*>(kv3 + row * QS + dim0) = kv_3;
+        // transpose the decayed keys to [dim][token] with an identity MFMA
+        const f32x4 tr = mma16(klh, ident, f32x4{0.f, 0.f, 0.f, 0.f});
+        f16x4 trh;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) trh[u] = (f16)tr[u];
+        *reinterpret_cast<f16x4*>(sm.klt + (16 * db + n16) * AS + 16 * I + 4 * g) = trh;
+      }
+    }
+    __syncthreads();
+
+    // ---- Phase A: A^T tiles (rows s in sub-block J, cols t in sub-block I), J <= I.
+    for (int ti = 0; ti < n_tiles; ++ti) {
+      const int code = (tile_codes >> (8 * ti)) & 0xff;
+      const int I = code >> 4, J = code & 0xf;
+      const int gap = I - J;
+      const f16* kb = (gap == 0) ? sm.k : (gap == 1) ? kv1 : (gap == 2) ? kv2 : kv3;
+      const int s_row = 16 * J + n16, t_row = 16 * I + n16;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int d0 = 0; d0 < DK; d0 += 32) {
+        const f16x8 a = *reinterpret_cast<const f16x8*>(kb + s_row * QS + d0 + 8 * g);
+        const f16x8 bq = *reinterpret_cast<const f16x8*>(sm.q + t_row * QS + d0 + 8 * g);
+        acc = mma32(a, bq, acc);
+      }
+      if (gap == 0) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (4 * g + u > n16) acc[u] = 0.f;
+      }
+      f16x4 w;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) w[u] = (f16)acc[u];
+      *reinterpret_cast<f16x4*>(sa + t_row * AS + 16 * J + 4 * g) = w;
+    }
+    // Zero the two upper tiles (0,1) and (2,3) so that every A.V step below is a
+    // full 32-token 16x16x32 MFMA: the accumulation chains never mix MFMA shapes.
+    if (wave >= 2) {
+      const int I = (wave == 2) ? 0 : 2;
+      *reinterpret_cast<f16x4*>(sa + (16 * I + n16) * AS + 16 * (I + 1) + 4 * g) =
+          f16x4{(f16)0.f, (f16)0.f, (f16)0.f, (f16)0.f};
+    }
+    __syncthreads();
+
+    // ---- Phase O: O^T = V^T A^T + S^T Qt^T, then S <- diag(g) S + KL^T V.
+#pragma unroll
+    for (int j = 0; j < StateRegs<DK, DV>::NC; ++j) {
+      const int col0 = 16 * (wave + 4 * j);
+      const int col = col0 + n16;
+      f16x8 sh[DK / 32];
+#pragma unroll
+      for (int rho = 0; rho < DK / 32; ++rho)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          sh[rho][u] = (f16)st.s[2 * rho][j][u];
+          sh[rho][4 + u] = (f16)st.s[2 * rho + 1][j][u];
+        }
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        const int t = 16 * I + n16;
+        const int len = 32 * ((I + 2) / 2);  // causal extent rounded up to 32 tokens
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s0 = 0; s0 < len; s0 += 32) {
+          const f16x8 a = *reinterpret_cast<const f16x8*>(sm.vt + col * AS + s0 + 8 * g);
+          const f16x8 bb = *reinterpret_cast<const f16x8*>(sa + t * AS + s0 + 8 * g);
+          acc = mma32(a, bb, acc);
+        }
+#pragma unroll
+        for (int rho = 0; rho < DK / 32; ++rho) {
+          const int dlo = 32 * rho + 4 * g;
+          const f16x4 qlo = *reinterpret_cast<const f16x4*>(sm.qt + t * QS + dlo);
+          const f16x4 qhi = *reinterpret_cast<const f16x4*>(sm.qt + t * QS + dlo + 16);
+          f16x8 bq;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            bq[u] = qlo[u];
+            bq[4 + u] = qhi[u];
+          }
+          acc = mma32(sh[rho], bq, acc);
+        }
+        f16x4 w;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) w[u] = (f16)acc[u];
+        *reinterpret_cast<f16x4*>(so + t * OS + col0 + 4 * g) = w;
+      }
+    }
+    state_update<f16, DK, DV>(st, sm.klt, sm.vt, sm.g, AS);
+    __syncthreads();
+
+    // ---- Phase W: output rows to their grid cells.
+    constexpr int PO = DV / 8;
+    constexpr int NO = kChunk * PO / kThreads;
+#pragma unroll
+    for (int jj = 0; jj < NO; ++jj) {
+      const int id = tid + kThreads * jj;
+      const int tok = id / PO, pc = id - tok * PO;
+      if (tok < valid) {
+        const size_t o = off_v + (size_t)cell_of(t0 + tok, p.H, p.W, dir) * DV + pc * 8;
+        *reinterpret_cast<uint4*>(out + o) = *reinterpret_cast<const uint4*>(so + tok * OS + pc * 8);
+      }
+    }
+  }
+
+  if (span == p.n_spans - 1 && p.final_state != nullptr) {
+    float* dst = p.final_state + (size_t)bh * DK * DV;
+#pragma unroll
+    for (int j = 0; j < StateRegs<DK, DV>::NC; ++j) {
+      const int col = 16 * (wave + 4 * j) + n16;
+#pragma unroll
+      for (int r = 0; r < StateRegs<DK, DV>::NR; ++r)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) dst[(16 * r + 4 * g + u) * DV + col] = st.s[r][j][u];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Span-summary kernel, float16.  Keeps S^T in the accumulators, wave w owning
+// key dims 16*db.. (db = w, w+4) for all value columns: lane (n, g) of tile cb
+// holds S^T[16cb + 4g + u][16db + n], so each lane scales by one decay factor.
+template <int DK, int DV>
+struct SumSmemH {
+  static constexpr int AS = kChunk + 8;
+  alignas(16) f16 kt[DK * AS];   // k^T [d_k][token]
+  alignas(16) f16 lat[DK * AS];  // log-alpha^T
+  alignas(16) f16 vt[DV * AS];   // V^T
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(kThreads) void span_summary_f16_kernel(FwdParams p) {
+  using SM = SumSmemH<DK, DV>;
+  __shared__ SM sm;
+  constexpr int AS = SM::AS;
+  constexpr int NDB = DK / 64, NCB = DV / 16;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n16 = lane & 15, g = lane >> 4;
+
+  const int bh = blockIdx.x / p.n_spans;
+  const int span = blockIdx.x - bh * p.n_spans;
+  const int b = bh / p.heads;
+  const int dir = (p.scan_dir == 4) ? (b & 3) : p.scan_dir;
+  const size_t off_k = (size_t)bh * p.T * DK;
+  const size_t off_v = (size_t)bh * p.T * DV;
+  const int c_begin = span * p.span_chunks;
+  const int c_end = min(c_begin + p.span_chunks, p.n_chunks);
+  const f16* k = static_cast<const f16*>(p.k);
+  const f16* la = static_cast<const f16*>(p.la);
+  const f16* v = static_cast<const f16*>(p.v);
+
+  // Constant A operands (rows t, cols s of a 16x16 block): strict upper part
+  // (s > t) of the diagonal block and the all-ones block for later sub-blocks,
+  // so that the MFMA yields the decay from token t to the chunk end.
+  f16x4 m_diag, m_ones;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    m_diag[u] = (f16)((4 * g + u > n16) ? 1.f : 0.f);
+    m_ones[u] = (f16)1.f;
+  }
+
+  f32x4 st[NDB][NCB];
+#pragma unroll
+  for (int d = 0; d < NDB; ++d)
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) st[d][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float log_gate[NDB];
+#pragma unroll
+  for (int d = 0; d < NDB; ++d) log_gate[d] = 0.f;
+
+  LoaderH<DK, DV, false, false> ld;
+  ld.load(nullptr, k, la, v, off_k, off_v, c_begin * kChunk, min(kChunk, p.T - c_begin * kChunk),
+          p.H, p.W, dir);
+  for (int c = c_begin; c < c_end; ++c) {
+    __syncthreads();  // previous chunk's reads of the tiles are done
+    ld.store(nullptr, nullptr, 0, sm.kt, sm.lat, sm.vt, AS);
+    if (c + 1 < c_end) {
+      const int t1 = (c + 1) * kChunk;
+      ld.load(nullptr, k, la, v, off_k, off_v, t1, min(kChunk, p.T - t1), p.H, p.W, dir);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) {
+      const int db = wave + 4 * d;
+      const int dim = 16 * db + n16;
+      f16x4 lat4[4];
+#pragma unroll
+      for (int J = 0; J < 4; ++J)
+        lat4[J] = *reinterpret_cast<const f16x4*>(sm.lat + dim * AS + 16 * J + 4 * g);
+      // decay from token 16I+4g+u to the chunk end, at key dim `dim`
+      f32x4 rest[4];
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        f32x4 acc = mma16(m_diag, lat4[I], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int J = I + 1; J < 4; ++J) acc = mma16(m_ones, lat4[J], acc);
+        rest[I] = acc;
+      }
+      // whole-chunk decay of this dim: token 0's remainder plus its own log-alpha
+      const float first = __shfl(rest[0][0] + (float)lat4[0][0], n16, 64);
+      log_gate[d] += first;
+      const float gch = exp2_fast(first * 1.4426950408889634f);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) st[d][cb][u] *= gch;
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        const f16x4 k4 = *reinterpret_cast<const f16x4*>(sm.kt + dim * AS + 16 * I + 4 * g);
+        f16x4 kl;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          kl[u] = (f16)((float)k4[u] * exp2_fast(rest[I][u] * 1.4426950408889634f));
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          const f16x4 vv =
+              *reinterpret_cast<const f16x4*>(sm.vt + (16 * cb + n16) * AS + 16 * I + 4 * g);
+          st[d][cb] = mma16(vv, kl, st[d][cb]);
+        }
+      }
+    }
+  }
+
+  float* dst = p.span_state + ((size_t)bh * p.n_spans + span) * DK * DV;
+#pragma unroll
+  for (int d = 0; d < NDB; ++d) {
+    const int dim = 16 * (wave + 4 * d) + n16;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+      *reinterpret_cast<f32x4*>(dst + dim * DV + 16 * cb + 4 * g) = st[d][cb];
+    if (g == 0) p.span_gate[((size_t)bh * p.n_spans + span) * DK + dim] = exp2_fast(log_gate[d] * 1.4426950408889634f);
+  }
+}
+
+hipError_t mark(hipEvent_t const* events, int i, hipStream_t stream) {
+  return events ? hipEventRecord(events[i], stream) : hipSuccess;
+}
+
+// Kernel choice per element type: float16 runs the MFMA-layout kernels,
+// float32 the generic ones.
 template <class T, int DK, int DV>
-hipError_t launch_variant(const FwdParams& p, hipStream_t stream) {
+struct Family {
+  static constexpr auto summary = span_summary_kernel<T, DK, DV>;
+  static constexpr auto output = chunk_output_kernel<T, DK, DV>;
+};
+template <int DK, int DV>
+struct Family<f16, DK, DV> {
+  static constexpr auto summary = span_summary_f16_kernel<DK, DV>;
+  static constexpr auto output = chunk_output_f16_kernel<DK, DV>;
+};
+
+template <class T, int DK, int DV>
+hipError_t launch_variant(const FwdParams& p, hipStream_t stream, hipEvent_t const* events) {
   const int BH = p.B * p.heads;
+  hipError_t e = mark(events, 0, stream);
+  if (e != hipSuccess) return e;
   if (p.n_spans > 1) {
-    hipLaunchKernelGGL((span_summary_kernel<T, DK, DV>), dim3(BH * p.n_spans), dim3(kThreads), 0,
+    hipLaunchKernelGGL((Family<T, DK, DV>::summary), dim3(BH * p.n_spans), dim3(kThreads), 0,
                        stream, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if ((e = mark(events, 1, stream)) != hipSuccess) return e;
+  if (p.n_spans > 1) {
     hipLaunchKernelGGL((span_scan_kernel<DK, DV>), dim3(BH, DK * DV / kThreads), dim3(kThreads),
                        0, stream, p);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((chunk_output_kernel<T, DK, DV>), dim3(BH * p.n_spans), dim3(kThreads), 0,
-                     stream, p);
-  return hipGetLastError();
+  if ((e = mark(events, 2, stream)) != hipSuccess) return e;
+  hipLaunchKernelGGL((Family<T, DK, DV>::output), dim3(BH * p.n_spans), dim3(kThreads), 0, stream,
+                     p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return mark(events, 3, stream);
 }
 
 }  // namespace
+
+template <class T, int DK, int DV>
+int output_occupancy() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, Family<T, DK, DV>::output, kThreads, 0) !=
+          hipSuccess ||
+      n < 1)
+    n = 1;
+  return n;
+}
+
+int output_blocks_per_cu(Dtype dt, int d_k, int d_v) {
+  if (dt == Dtype::kF16) {
+    if (d_k == 64 && d_v == 64) return output_occupancy<f16, 64, 64>();
+    if (d_k == 64 && d_v == 128) return output_occupancy<f16, 64, 128>();
+    if (d_k == 128 && d_v == 64) return output_occupancy<f16, 128, 64>();
+    if (d_k == 128 && d_v == 128) return output_occupancy<f16, 128, 128>();
+  } else {
+    if (d_k == 64 && d_v == 64) return output_occupancy<float, 64, 64>();
+    if (d_k == 64 && d_v == 128) return output_occupancy<float, 64, 128>();
+  }
+  return 1;
+}
 
 bool has_variant(Dtype dt, int d_k, int d_v) {
   if (dt == Dtype::kF16)
@@ -697,15 +1277,16 @@ bool has_variant(Dtype dt, int d_k, int d_v) {
   return d_k == 64 && (d_v == 64 || d_v == 128);
 }
 
-hipError_t launch_forward(Dtype dt, int d_k, int d_v, const FwdParams& p, hipStream_t stream) {
+hipError_t launch_forward(Dtype dt, int d_k, int d_v, const FwdParams& p, hipStream_t stream,
+                          hipEvent_t const* ev) {
   if (dt == Dtype::kF16) {
-    if (d_k == 64 && d_v == 64) return launch_variant<f16, 64, 64>(p, stream);
-    if (d_k == 64 && d_v == 128) return launch_variant<f16, 64, 128>(p, stream);
-    if (d_k == 128 && d_v == 64) return launch_variant<f16, 128, 64>(p, stream);
-    if (d_k == 128 && d_v == 128) return launch_variant<f16, 128, 128>(p, stream);
+    if (d_k == 64 && d_v == 64) return launch_variant<f16, 64, 64>(p, stream, ev);
+    if (d_k == 64 && d_v == 128) return launch_variant<f16, 64, 128>(p, stream, ev);
+    if (d_k == 128 && d_v == 64) return launch_variant<f16, 128, 64>(p, stream, ev);
+    if (d_k == 128 && d_v == 128) return launch_variant<f16, 128, 128>(p, stream, ev);
   } else {
-    if (d_k == 64 && d_v == 64) return launch_variant<float, 64, 64>(p, stream);
-    if (d_k == 64 && d_v == 128) return launch_variant<float, 64, 128>(p, stream);
+    if (d_k == 64 && d_v == 64) return launch_variant<float, 64, 64>(p, stream, ev);
+    if (d_k == 64 && d_v == 128) return launch_variant<float, 64, 128>(p, stream, ev);
   }
   return hipErrorInvalidValue;
 }

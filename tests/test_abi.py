@@ -69,3 +69,22 @@ def test_argument_errors(dtype):
 def test_fp32_entry_rejects_unbuilt_key_dim():
     assert call("fp32", d_k=128) == -3
     assert call("fp16", d_k=128, scan_dir=9) == -5           # direction checked first
+
+
+def test_kernel_event_hook_validation():
+    lib = _lib.load()
+    assert _lib.set_kernel_events([]) == 0
+    assert _lib.set_kernel_events([1, 2, 3]) == -2
+    assert _lib.set_kernel_events([1, 2, None, 4]) == -1
+    assert lib.gla_set_kernel_events(None, 4) == -1
+    assert _lib.set_kernel_events([]) == 0
+
+
+def test_plan_spans_argument_errors():
+    import ctypes
+    lib = _lib.load()
+    a, b = ctypes.c_int(0), ctypes.c_int(0)
+    assert lib.gla_plan_spans(0, 1, 12, 128, 128, 64, 64, 64, None, ctypes.byref(b)) == -1
+    assert lib.gla_plan_spans(0, 1, 12, 128, 128, 64, 64, 32, ctypes.byref(a), ctypes.byref(b)) == -3
+    assert lib.gla_plan_spans(1, 1, 12, 128, 128, 128, 64, 64, ctypes.byref(a), ctypes.byref(b)) == -3
+    assert lib.gla_plan_spans(0, 0, 12, 128, 128, 64, 64, 64, ctypes.byref(a), ctypes.byref(b)) == -2

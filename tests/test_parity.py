@@ -160,3 +160,12 @@ def test_explicit_stream():
     ro, rs = gla_forward(q, k, v, la, 1)
     check(o, ro, True, "stream out")
     check(st, rs, True, "stream state")
+
+
+def test_span_plan_covers_sequence():
+    _torch()
+    from recurrent_vision_token_amd import _lib
+    for name, wl in WORKLOADS.items():
+        m, n = _lib.plan_spans(wl.dtype, wl.B, wl.heads, wl.H, wl.W, wl.d_k, wl.d_v, wl.chunk)
+        n_chunks = -(-wl.T // 64)
+        assert m >= 1 and n >= 1 and (n - 1) * m < n_chunks <= n * m, name
