@@ -220,6 +220,9 @@ def main():
     ap.add_argument("--workload", default="hires16.4k")
     ap.add_argument("--secondary", default="gtr1.6k", help="'' to skip")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="also run one device-to-device copy of this many MB (a kernel of "
+                         "known traffic, to scale hardware byte counters against)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -237,6 +240,15 @@ def main():
     load()  # fails loudly if the HIP library is not built
     if not torch.cuda.is_available():
         raise RuntimeError("bench.py needs a HIP device")
+
+    if args.copy_calibration_mb > 0:
+        n = args.copy_calibration_mb << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: %d bytes read, %d bytes written" % (n, n))
+        del src, dst
 
     wl = WORKLOADS[args.workload]
     runner, ms_step, mean = time_workload(wl, torch, args.steps, args.warmup)

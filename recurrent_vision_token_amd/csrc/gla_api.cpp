@@ -63,29 +63,18 @@ int span_override() {
   return value;
 }
 
-// Chunks per span.  The output kernel's time is the longest chain of chunks any
-// workgroup slot processes; with W = bh * ceil(n_chunks / m) workgroups over
-// `slots` resident slots that is ceil(W / slots) * m.  Take the smallest m that
-// minimises it (shorter spans also mean a cheaper span scan), and no split at
-// all when the sequences alone fill the slots.
+// Chunks per span: the smallest span length whose output workgroups fit in
+// one wave of resident slots (bh * ceil(n_chunks / m) <= slots), so no slot
+// runs a second span after the others finish; no split at all when the
+// sequences alone fill the slots.  Shorter spans would add waves, and longer
+// ones lengthen every workgroup's sequential chain.
 int plan_span_chunks(long long bh, int n_chunks, int slots) {
   const int forced = span_override();
   if (forced > 0) return forced < n_chunks ? forced : n_chunks;
   if (bh >= slots) return n_chunks;
-  // one wave of workgroups at m1 chunks each bounds the optimum from above
-  const long long per_seq = slots / bh;
-  const int m1 = (int)((n_chunks + per_seq - 1) / per_seq);
-  long long best_cost = -1;
-  int best_m = n_chunks;
-  for (int m = 1; m <= m1; ++m) {
-    const long long wgs = bh * ((n_chunks + m - 1) / m);
-    const long long cost = ((wgs + slots - 1) / slots) * m;
-    if (best_cost < 0 || cost < best_cost) {
-      best_cost = cost;
-      best_m = m;
-    }
-  }
-  return best_m;
+  const long long per_seq = slots / bh;  // >= 1 spans per sequence fit
+  const long long m = (n_chunks + per_seq - 1) / per_seq;
+  return (int)(m < 1 ? 1 : m);
 }
 
 int forward(gla::Dtype dt, size_t esize, const void* q, const void* k, const void* v,
@@ -142,6 +131,8 @@ int forward(gla::Dtype dt, size_t esize, const void* q, const void* k, const voi
   p.H = H;
   p.W = W;
   p.T = (int)T;
+  gla::fast_div_constants((unsigned)W, &p.div_w_m, &p.div_w_s);
+  gla::fast_div_constants((unsigned)H, &p.div_h_m, &p.div_h_s);
   p.scan_dir = scan_dir;
   p.n_chunks = n_chunks;
   p.span_chunks = span_chunks;
@@ -165,6 +156,21 @@ int forward(gla::Dtype dt, size_t esize, const void* q, const void* k, const voi
 }
 
 }  // namespace
+
+namespace gla {
+
+// Division by an invariant integer with a multiply and a shift (Granlund &
+// Montgomery, PLDI 1994): with s = ceil(log2 d) and m = floor(2^32 (2^s - d) / d) + 1,
+// t / d = (umulhi(t, m) + t) >> s for all t < 2^31 (the sum then fits 32 bits).
+void fast_div_constants(unsigned int d, unsigned int* m, int* s) {
+  int sh = 0;
+  while ((1ULL << sh) < d) ++sh;
+  const unsigned long long num = ((1ULL << sh) - d) << 32;
+  *m = (unsigned int)(num / d + 1);
+  *s = sh;
+}
+
+}  // namespace gla
 
 extern "C" {
 

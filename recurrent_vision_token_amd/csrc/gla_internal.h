@@ -20,11 +20,18 @@ struct FwdParams {
   float* span_state;    // [BH][n_spans][d_k][d_v] span summaries, then entry states
   float* span_gate;     // [BH][n_spans][d_k] product of the span's gates
   int B, heads, H, W, T;
+  // t / W and t / H as (umulhi(t, m) + t) >> s, exact for t < 2^31
+  unsigned int div_w_m, div_h_m;
+  int div_w_s, div_h_s;
   int scan_dir;
   int n_chunks;         // ceil(T / 64)
   int span_chunks;      // chunks handled by one workgroup of the output kernel
   int n_spans;          // ceil(n_chunks / span_chunks)
 };
+
+// Multiply-shift constants for dividing t < 2^31 by d >= 1:
+// t / d == (umulhi(t, m) + t) >> s.
+void fast_div_constants(unsigned int d, unsigned int* m, int* s);
 
 // Output-kernel workgroups resident per CU for this variant (occupancy).
 int output_blocks_per_cu(Dtype dt, int d_k, int d_v);

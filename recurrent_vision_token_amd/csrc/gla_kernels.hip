@@ -76,17 +76,43 @@ __device__ __forceinline__ float fexp(float x) {
   }
 }
 
-// Scan step t -> row-major grid cell for one of the four directions.
-__device__ __forceinline__ int cell_of(int t, int H, int W, int dir) {
-  if (dir == 0) return t;
-  if (dir == 1) {
-    const int r = t / W;
-    return r * W + (W - 1 - (t - r * W));
+// Scan step t -> row-major grid cell for one of the four directions, with the
+// divisions by W or H done by precomputed multiply-shift constants.
+struct GridMap {
+  int H, W, dir;
+  unsigned int mw, mh;
+  int sw, sh;
+  __device__ __forceinline__ static int div(int t, unsigned int m, int s) {
+    return (int)((__umulhi((unsigned)t, m) + (unsigned)t) >> s);
   }
-  const int c = t / H;
-  const int r = t - c * H;
-  return (dir == 2 ? r : (H - 1 - r)) * W + c;
+  __device__ __forceinline__ int cell(int t) const {
+    if (dir == 0) return t;
+    if (dir == 1) {
+      const int r = div(t, mw, sw);
+      return r * W + (W - 1 - (t - r * W));
+    }
+    const int c = div(t, mh, sh);
+    const int r = t - c * H;
+    return (dir == 2 ? r : (H - 1 - r)) * W + c;
+  }
+};
+
+__device__ __forceinline__ GridMap grid_map(const FwdParams& p, int b) {
+  GridMap g;
+  g.H = p.H;
+  g.W = p.W;
+  g.dir = (p.scan_dir == 4) ? (b & 3) : p.scan_dir;
+  g.mw = p.div_w_m;
+  g.mh = p.div_h_m;
+  g.sw = p.div_w_s;
+  g.sh = p.div_h_s;
+  return g;
 }
+
+// Row of key / value dim d in a transposed [dim][token] tile: one padding row
+// after every 8 dims, so that the 8 lanes writing dims 8pc+u (pc = 0..7) of a
+// token pair land in different LDS banks.
+__device__ __forceinline__ constexpr int trow(int d) { return d + (d >> 3); }
 
 __device__ __forceinline__ f32x4 mma32(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -154,8 +180,7 @@ struct Loader {
 
   template <bool WITH_Q>
   __device__ __forceinline__ void load(const T* q, const T* k, const T* la, const T* v,
-                                       size_t off_k, size_t off_v, int t0, int valid, int H,
-                                       int W, int dir) {
+                                       size_t off_k, size_t off_v, int t0, int valid, const GridMap& gm) {
     const int tid = threadIdx.x;
     const uint4 zero = make_uint4(0, 0, 0, 0);
 #pragma unroll
@@ -164,7 +189,7 @@ struct Loader {
       const int tok = id / PPT_K;
       const int pc = id - tok * PPT_K;
       if (tok < valid) {
-        const size_t o = off_k + (size_t)cell_of(t0 + tok, H, W, dir) * DK + pc * EPP;
+        const size_t o = off_k + (size_t)gm.cell(t0 + tok) * DK + pc * EPP;
         if (WITH_Q) rq[j] = ld(q, o);
         rk[j] = ld(k, o);
         rl[j] = ld(la, o);
@@ -183,7 +208,7 @@ struct Loader {
       for (int h = 0; h < 2; ++h) {
         const int tok = 2 * tp + h;
         rv[2 * j + h] = (tok < valid)
-                            ? ld(v, off_v + (size_t)cell_of(t0 + tok, H, W, dir) * DV + pc * EPP)
+                            ? ld(v, off_v + (size_t)gm.cell(t0 + tok) * DV + pc * EPP)
                             : zero;
       }
     }
@@ -278,7 +303,7 @@ __global__ __launch_bounds__(kThreads) void span_summary_kernel(FwdParams p) {
   const int bh = blockIdx.x / p.n_spans;
   const int span = blockIdx.x - bh * p.n_spans;
   const int b = bh / p.heads;
-  const int dir = (p.scan_dir == 4) ? (b & 3) : p.scan_dir;
+  const GridMap gm = grid_map(p, b);
   const size_t off_k = (size_t)bh * p.T * DK;
   const size_t off_v = (size_t)bh * p.T * DV;
   const int c_begin = span * p.span_chunks;
@@ -302,16 +327,14 @@ __global__ __launch_bounds__(kThreads) void span_summary_kernel(FwdParams p) {
   Loader<T, DK, DV> ld;
   {
     const int t0 = c_begin * kChunk;
-    ld.template load<false>(nullptr, k, la, v, off_k, off_v, t0, min(kChunk, p.T - t0), p.H, p.W,
-                            dir);
+    ld.template load<false>(nullptr, k, la, v, off_k, off_v, t0, min(kChunk, p.T - t0), gm);
   }
   for (int c = c_begin; c < c_end; ++c) {
     __syncthreads();  // previous chunk's MFMA reads of vt / klt are done
     ld.template store<false>(nullptr, sm.k, sm.la, sm.vt, QS, AS);
     if (c + 1 < c_end) {
       const int t0 = (c + 1) * kChunk;
-      ld.template load<false>(nullptr, k, la, v, off_k, off_v, t0, min(kChunk, p.T - t0), p.H,
-                              p.W, dir);
+      ld.template load<false>(nullptr, k, la, v, off_k, off_v, t0, min(kChunk, p.T - t0), gm);
     }
     __syncthreads();
     // Cumulative decay per (key dim, sub-block) and the decayed keys k_s*exp(b_last-b_s).
@@ -435,7 +458,7 @@ __global__ __launch_bounds__(kThreads) void chunk_output_kernel(FwdParams p) {
   const int bh = blockIdx.x / p.n_spans;
   const int span = blockIdx.x - bh * p.n_spans;
   const int b = bh / p.heads;
-  const int dir = (p.scan_dir == 4) ? (b & 3) : p.scan_dir;
+  const GridMap gm = grid_map(p, b);
   const size_t off_k = (size_t)bh * p.T * DK;
   const size_t off_v = (size_t)bh * p.T * DV;
   const int c_begin = span * p.span_chunks;
@@ -476,7 +499,7 @@ __global__ __launch_bounds__(kThreads) void chunk_output_kernel(FwdParams p) {
   Loader<T, DK, DV> ld;
   {
     const int t0 = c_begin * kChunk;
-    ld.template load<true>(q, k, la, v, off_k, off_v, t0, min(kChunk, p.T - t0), p.H, p.W, dir);
+    ld.template load<true>(q, k, la, v, off_k, off_v, t0, min(kChunk, p.T - t0), gm);
   }
   for (int c = c_begin; c < c_end; ++c) {
     const int t0 = c * kChunk;
@@ -484,8 +507,7 @@ __global__ __launch_bounds__(kThreads) void chunk_output_kernel(FwdParams p) {
     ld.template store<true>(sm.q, sm.k, sm.la, sm.vt, QS, AS);
     if (c + 1 < c_end) {
       const int t1 = t0 + kChunk;
-      ld.template load<true>(q, k, la, v, off_k, off_v, t1, min(kChunk, p.T - t1), p.H, p.W,
-                             dir);
+      ld.template load<true>(q, k, la, v, off_k, off_v, t1, min(kChunk, p.T - t1), gm);
     }
     __syncthreads();
 
@@ -663,7 +685,7 @@ __global__ __launch_bounds__(kThreads) void chunk_output_kernel(FwdParams p) {
       const int tok = id / PPT_O;
       const int pc = id - tok * PPT_O;
       if (tok < valid) {
-        const size_t o = off_v + (size_t)cell_of(t0 + tok, p.H, p.W, dir) * DV + pc * EPP;
+        const size_t o = off_v + (size_t)gm.cell(t0 + tok) * DV + pc * EPP;
         *reinterpret_cast<uint4*>(out + o) =
             *reinterpret_cast<const uint4*>(sm.o + tok * OS + pc * EPP);
       }
@@ -717,14 +739,15 @@ struct OutSmemH {
   static constexpr int OS = DV + 8;      // [token][d_v] rows
   static constexpr int KV_ROWS = 48 + 32 + 16;
   static constexpr int KV_ELEMS = (KV_ROWS * QS > kChunk * OS) ? KV_ROWS * QS : kChunk * OS;
-  static constexpr int LAT_ELEMS = (DK * AS > kChunk * AS) ? DK * AS : kChunk * AS;
+  static constexpr int LAT_ELEMS =
+      (trow(DK) * AS > kChunk * AS) ? trow(DK) * AS : kChunk * AS;
   alignas(16) f16 q[kChunk * QS];    // raw q, then q_t*exp(c_t)   (c: decay inside the sub-block)
   alignas(16) f16 qt[kChunk * QS];   // q_t*exp(b_t)               (b: decay from the chunk start)
   alignas(16) f16 k[kChunk * QS];    // raw k, then k_s*exp(-c_s)
   alignas(16) f16 kv[KV_ELEMS];      // k decayed to the end of its sub-block (rows 0..47), of the
                                      // next one (48..79), of the one after (80..95); then O staging
-  alignas(16) f16 lat[LAT_ELEMS];    // log-alpha^T [d_k][token], then A[t][s]
-  alignas(16) f16 vt[DV * AS];       // V^T [d_v][token]
+  alignas(16) f16 lat[LAT_ELEMS];    // log-alpha^T [trow(d_k)][token], then A[t][s]
+  alignas(16) f16 vt[trow(DV) * AS]; // V^T [trow(d_v)][token]
   alignas(16) f16 klt[DK * AS];      // (k_s*exp(b_last-b_s))^T [d_k][token]
   alignas(16) float g[DK];           // exp(b_last)
 };
@@ -748,8 +771,7 @@ struct LoaderH {
   }
 
   __device__ __forceinline__ void load(const f16* q, const f16* k, const f16* la, const f16* v,
-                                       size_t off_k, size_t off_v, int t0, int valid, int H,
-                                       int W, int dir) {
+                                       size_t off_k, size_t off_v, int t0, int valid, const GridMap& gm) {
     const int tid = threadIdx.x;
     const uint4 z = make_uint4(0, 0, 0, 0);
     if (WITH_Q || K_ROWS) {
@@ -758,7 +780,7 @@ struct LoaderH {
         const int id = tid + kThreads * j;
         const int tok = id / PK, pc = id - tok * PK;
         const bool in = tok < valid;
-        const size_t o = in ? off_k + (size_t)cell_of(t0 + tok, H, W, dir) * DK + pc * 8 : 0;
+        const size_t o = in ? off_k + (size_t)gm.cell(t0 + tok) * DK + pc * 8 : 0;
         if (WITH_Q) rq[j] = in ? ld(q + o) : z;
         if (K_ROWS) rk[j] = in ? ld(k + o) : z;
       }
@@ -771,7 +793,7 @@ struct LoaderH {
       for (int h = 0; h < 2; ++h) {
         const int tok = 2 * tp + h;
         const bool in = tok < valid;
-        const size_t o = in ? off_k + (size_t)cell_of(t0 + tok, H, W, dir) * DK + pc * 8 : 0;
+        const size_t o = in ? off_k + (size_t)gm.cell(t0 + tok) * DK + pc * 8 : 0;
         rl[2 * j + h] = in ? ld(la + o) : z;
         if (!K_ROWS) rk[2 * j + h] = in ? ld(k + o) : z;
       }
@@ -785,7 +807,7 @@ struct LoaderH {
         const int tok = 2 * tp + h;
         const bool in = tok < valid;
         rv[2 * j + h] =
-            in ? ld(v + off_v + (size_t)cell_of(t0 + tok, H, W, dir) * DV + pc * 8) : z;
+            in ? ld(v + off_v + (size_t)gm.cell(t0 + tok) * DV + pc * 8) : z;
       }
     }
   }
@@ -800,7 +822,7 @@ struct LoaderH {
       f16x2 pr;
       pr[0] = x[u];
       pr[1] = y[u];
-      *reinterpret_cast<f16x2*>(dst + (8 * pc + u) * AS + 2 * tp) = pr;
+      *reinterpret_cast<f16x2*>(dst + (9 * pc + u) * AS + 2 * tp) = pr;  // row trow(8pc+u)
     }
   }
 
@@ -864,7 +886,7 @@ __global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 2 : 1) void chun
   const int bh = blockIdx.x / p.n_spans;
   const int span = blockIdx.x - bh * p.n_spans;
   const int b = bh / p.heads;
-  const int dir = (p.scan_dir == 4) ? (b & 3) : p.scan_dir;
+  const GridMap gm = grid_map(p, b);
   const size_t off_k = (size_t)bh * p.T * DK;
   const size_t off_v = (size_t)bh * p.T * DV;
   const int c_begin = span * p.span_chunks;
@@ -905,57 +927,64 @@ __global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 2 : 1) void chun
   f16* const sa = sm.lat;  // score tile reuses the log-alpha^T region
 
   LoaderH<DK, DV, true, true> ld;
-  ld.load(q, k, la, v, off_k, off_v, c_begin * kChunk, min(kChunk, p.T - c_begin * kChunk), p.H,
-          p.W, dir);
+  ld.load(q, k, la, v, off_k, off_v, c_begin * kChunk, min(kChunk, p.T - c_begin * kChunk), gm);
   for (int c = c_begin; c < c_end; ++c) {
     const int t0 = c * kChunk;
     const int valid = min(kChunk, p.T - t0);
     ld.store(sm.q, sm.k, QS, nullptr, sm.lat, sm.vt, AS);
     if (c + 1 < c_end) {
       const int t1 = t0 + kChunk;
-      ld.load(q, k, la, v, off_k, off_v, t1, min(kChunk, p.T - t1), p.H, p.W, dir);
+      ld.load(q, k, la, v, off_k, off_v, t1, min(kChunk, p.T - t1), gm);
     }
     __syncthreads();
 
     // ---- Phase P: wave w owns key dims 16*db .. 16*db+15, db = w (+4).
+    // All LDS operands of the phase are read up front, then consumed.
 #pragma unroll
     for (int dbi = 0; dbi < DK / 64; ++dbi) {
       const int db = wave + 4 * dbi;
       const int dim0 = 16 * db + 4 * g;  // this lane's 4 key dims in the row layout
-      f32x4 eq[4], ek[4], ed[4];
+      f16x4 lat4[4], q4[4], k4[4];
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        lat4[I] = *reinterpret_cast<const f16x4*>(sm.lat + trow(16 * db + n16) * AS + 16 * I + 4 * g);
+        q4[I] = *reinterpret_cast<const f16x4*>(sm.q + (16 * I + n16) * QS + dim0);
+        k4[I] = *reinterpret_cast<const f16x4*>(sm.k + (16 * I + n16) * QS + dim0);
+      }
+      f32x4 c2[4];
 #pragma unroll
       for (int I = 0; I < 4; ++I) {
         // c*log2(e) at token 16I+n16, dims dim0..dim0+3
-        const f16x4 a = *reinterpret_cast<const f16x4*>(sm.lat + (16 * db + n16) * AS + 16 * I + 4 * g);
-        f32x4 c2 = {0.f, 0.f, 0.f, 0.f};
-        c2 = mma16(a, u_hi, c2);
-        c2 = mma16(a, u_lo, c2);
+        c2[I] = mma16(lat4[I], u_hi, f32x4{0.f, 0.f, 0.f, 0.f});
+        c2[I] = mma16(lat4[I], u_lo, c2[I]);
+      }
+      f32x4 eq[4], ek[4], ed[4];
+#pragma unroll
+      for (int I = 0; I < 4; ++I)
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          eq[I][u] = exp2_fast(c2[u]);
-          ek[I][u] = exp2_fast(-c2[u]);
+          eq[I][u] = exp2_fast(c2[I][u]);
+          ek[I][u] = exp2_fast(-c2[I][u]);
           ed[I][u] = row_bcast15(eq[I][u]);  // exp(decay over sub-block I)
         }
-      }
       f32x4 gl;
 #pragma unroll
       for (int u = 0; u < 4; ++u) gl[u] = ed[0][u] * ed[1][u] * ed[2][u] * ed[3][u];
       if (n16 == 0) *reinterpret_cast<f32x4*>(sm.g + dim0) = gl;
+      f16x4 klh[4];
 #pragma unroll
       for (int I = 0; I < 4; ++I) {
         const int row = 16 * I + n16;
-        const f16x4 q4 = *reinterpret_cast<const f16x4*>(sm.q + row * QS + dim0);
-        const f16x4 k4 = *reinterpret_cast<const f16x4*>(sm.k + row * QS + dim0);
-        f16x4 ql, qt, kd, kv_1, kv_2, kv_3, klh;
+        f16x4 ql, qt, kd, kv_1, kv_2, kv_3;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           float e_start = 1.f;  // exp(b at the end of sub-block I-1)
 #pragma unroll
           for (int L = 0; L < I; ++L) e_start *= ed[L][u];
-          const float qf = (float)q4[u];
+          const float qf = (float)q4[I][u];
           ql[u] = (f16)(qf * eq[I][u]);
           qt[u] = (f16)(qf * (eq[I][u] * e_start));
-          const float kf = (float)k4[u] * ek[I][u];
+          const float kf = (float)k4[I][u] * ek[I][u];
           kd[u] = (f16)kf;
           float kx = kf * ed[I][u];  // decayed to the end of sub-block I
           kv_1[u] = (f16)kx;
@@ -965,7 +994,7 @@ __global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 2 : 1) void chun
             if (L == I + 1) kv_2[u] = (f16)kx;
             if (L == I + 2) kv_3[u] = (f16)kx;
           }
-          klh[u] = (f16)kx;  // decayed to the chunk end
+          klh[I][u] = (f16)kx;  // decayed to the chunk end
         }
         *reinterpret_cast<f16x4*>(sm.q + row * QS + dim0) = ql;
         *reinterpret_cast<f16x4*>(sm.qt + row * QS + dim0) = qt;
@@ -973,8 +1002,11 @@ __global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 2 : 1) void chun
         if (I <= 2) *reinterpret_cast<f16x4*>(kv1 + row * QS + dim0) = kv_1;
         if (I <= 1) *reinterpret_cast<f16x4*>(kv2 + row * QS + dim0) = kv_2;
         if (I == 0) *reinterpret_cast<f16x4*>(kv3 + row * QS + dim0) = kv_3;
-        // transpose the decayed keys to [dim][token] with an identity MFMA
-        const f32x4 tr = mma16(klh, ident, f32x4{0.f, 0.f, 0.f, 0.f});
+      }
+      // transpose the decayed keys to [dim][token] with identity MFMAs
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        const f32x4 tr = mma16(klh[I], ident, f32x4{0.f, 0.f, 0.f, 0.f});
         f16x4 trh;
 #pragma unroll
         for (int u = 0; u < 4; ++u) trh[u] = (f16)tr[u];
@@ -984,35 +1016,49 @@ __global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 2 : 1) void chun
     __syncthreads();
 
     // ---- Phase A: A^T tiles (rows s in sub-block J, cols t in sub-block I), J <= I.
-    for (int ti = 0; ti < n_tiles; ++ti) {
-      const int code = (tile_codes >> (8 * ti)) & 0xff;
-      const int I = code >> 4, J = code & 0xf;
-      const int gap = I - J;
-      const f16* kb = (gap == 0) ? sm.k : (gap == 1) ? kv1 : (gap == 2) ? kv2 : kv3;
-      const int s_row = 16 * J + n16, t_row = 16 * I + n16;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // Waves 2 and 3 also zero the upper tiles (0,1) and (2,3) so that every A.V
+    // step below is a full 32-token 16x16x32 MFMA: accumulation chains never mix
+    // MFMA shapes.
+    {
+      f16x8 ta[3][DK / 32], tb[3][DK / 32];
 #pragma unroll
-      for (int d0 = 0; d0 < DK; d0 += 32) {
-        const f16x8 a = *reinterpret_cast<const f16x8*>(kb + s_row * QS + d0 + 8 * g);
-        const f16x8 bq = *reinterpret_cast<const f16x8*>(sm.q + t_row * QS + d0 + 8 * g);
-        acc = mma32(a, bq, acc);
+      for (int ti = 0; ti < 3; ++ti) {
+        if (ti < n_tiles) {
+          const int code = (tile_codes >> (8 * ti)) & 0xff;
+          const int I = code >> 4, J = code & 0xf;
+          const int gap = I - J;
+          const f16* kb = (gap == 0) ? sm.k : (gap == 1) ? kv1 : (gap == 2) ? kv2 : kv3;
+#pragma unroll
+          for (int st = 0; st < DK / 32; ++st) {
+            ta[ti][st] = *reinterpret_cast<const f16x8*>(kb + (16 * J + n16) * QS + 32 * st + 8 * g);
+            tb[ti][st] = *reinterpret_cast<const f16x8*>(sm.q + (16 * I + n16) * QS + 32 * st + 8 * g);
+          }
+        }
       }
-      if (gap == 0) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (4 * g + u > n16) acc[u] = 0.f;
+      for (int ti = 0; ti < 3; ++ti) {
+        if (ti < n_tiles) {
+          const int code = (tile_codes >> (8 * ti)) & 0xff;
+          const int I = code >> 4, J = code & 0xf;
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int st = 0; st < DK / 32; ++st) acc = mma32(ta[ti][st], tb[ti][st], acc);
+          if (I == J) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              if (4 * g + u > n16) acc[u] = 0.f;
+          }
+          f16x4 w;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) w[u] = (f16)acc[u];
+          *reinterpret_cast<f16x4*>(sa + (16 * I + n16) * AS + 16 * J + 4 * g) = w;
+        }
       }
-      f16x4 w;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) w[u] = (f16)acc[u];
-      *reinterpret_cast<f16x4*>(sa + t_row * AS + 16 * J + 4 * g) = w;
-    }
-    // Zero the two upper tiles (0,1) and (2,3) so that every A.V step below is a
-    // full 32-token 16x16x32 MFMA: the accumulation chains never mix MFMA shapes.
-    if (wave >= 2) {
-      const int I = (wave == 2) ? 0 : 2;
-      *reinterpret_cast<f16x4*>(sa + (16 * I + n16) * AS + 16 * (I + 1) + 4 * g) =
-          f16x4{(f16)0.f, (f16)0.f, (f16)0.f, (f16)0.f};
+      if (wave >= 2) {
+        const int I = (wave == 2) ? 0 : 2;
+        *reinterpret_cast<f16x4*>(sa + (16 * I + n16) * AS + 16 * (I + 1) + 4 * g) =
+            f16x4{(f16)0.f, (f16)0.f, (f16)0.f, (f16)0.f};
+      }
     }
     __syncthreads();
 
@@ -1021,6 +1067,29 @@ __global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 2 : 1) void chun
     for (int j = 0; j < StateRegs<DK, DV>::NC; ++j) {
       const int col0 = 16 * (wave + 4 * j);
       const int col = col0 + n16;
+      // operands, read up front
+      f16x8 va[2], sb[6], qb[4][DK / 32];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        va[h] = *reinterpret_cast<const f16x8*>(sm.vt + trow(col) * AS + 32 * h + 8 * g);
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        const int t = 16 * I + n16;
+#pragma unroll
+        for (int h = 0; h < (I + 2) / 2; ++h)
+          sb[(I < 3 ? I : 4) + h] = *reinterpret_cast<const f16x8*>(sa + t * AS + 32 * h + 8 * g);
+#pragma unroll
+        for (int rho = 0; rho < DK / 32; ++rho) {
+          const int dlo = 32 * rho + 4 * g;
+          const f16x4 qlo = *reinterpret_cast<const f16x4*>(sm.qt + t * QS + dlo);
+          const f16x4 qhi = *reinterpret_cast<const f16x4*>(sm.qt + t * QS + dlo + 16);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            qb[I][rho][u] = qlo[u];
+            qb[I][rho][4 + u] = qhi[u];
+          }
+        }
+      }
       f16x8 sh[DK / 32];
 #pragma unroll
       for (int rho = 0; rho < DK / 32; ++rho)
@@ -1032,34 +1101,36 @@ __global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 2 : 1) void chun
 #pragma unroll
       for (int I = 0; I < 4; ++I) {
         const int t = 16 * I + n16;
-        const int len = 32 * ((I + 2) / 2);  // causal extent rounded up to 32 tokens
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s0 = 0; s0 < len; s0 += 32) {
-          const f16x8 a = *reinterpret_cast<const f16x8*>(sm.vt + col * AS + s0 + 8 * g);
-          const f16x8 bb = *reinterpret_cast<const f16x8*>(sa + t * AS + s0 + 8 * g);
-          acc = mma32(a, bb, acc);
-        }
+        for (int h = 0; h < (I + 2) / 2; ++h) acc = mma32(va[h], sb[(I < 3 ? I : 4) + h], acc);
 #pragma unroll
-        for (int rho = 0; rho < DK / 32; ++rho) {
-          const int dlo = 32 * rho + 4 * g;
-          const f16x4 qlo = *reinterpret_cast<const f16x4*>(sm.qt + t * QS + dlo);
-          const f16x4 qhi = *reinterpret_cast<const f16x4*>(sm.qt + t * QS + dlo + 16);
-          f16x8 bq;
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            bq[u] = qlo[u];
-            bq[4 + u] = qhi[u];
-          }
-          acc = mma32(sh[rho], bq, acc);
-        }
+        for (int rho = 0; rho < DK / 32; ++rho) acc = mma32(sh[rho], qb[I][rho], acc);
         f16x4 w;
 #pragma unroll
         for (int u = 0; u < 4; ++u) w[u] = (f16)acc[u];
         *reinterpret_cast<f16x4*>(so + t * OS + col0 + 4 * g) = w;
       }
+      // state update for this column block: S <- diag(g) S + KL^T V
+      f16x8 ka[StateRegs<DK, DV>::NR][2];
+      f32x4 gv[StateRegs<DK, DV>::NR];
+#pragma unroll
+      for (int r = 0; r < StateRegs<DK, DV>::NR; ++r) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          ka[r][h] = *reinterpret_cast<const f16x8*>(sm.klt + (16 * r + n16) * AS + 32 * h + 8 * g);
+        gv[r] = *reinterpret_cast<const f32x4*>(sm.g + 16 * r + 4 * g);
+      }
+#pragma unroll
+      for (int r = 0; r < StateRegs<DK, DV>::NR; ++r) {
+        f32x4 acc = st.s[r][j];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[u] *= gv[r][u];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) acc = mma32(ka[r][h], va[h], acc);
+        st.s[r][j] = acc;
+      }
     }
-    state_update<f16, DK, DV>(st, sm.klt, sm.vt, sm.g, AS);
     __syncthreads();
 
     // ---- Phase W: output rows to their grid cells.
@@ -1070,7 +1141,7 @@ __global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 2 : 1) void chun
       const int id = tid + kThreads * jj;
       const int tok = id / PO, pc = id - tok * PO;
       if (tok < valid) {
-        const size_t o = off_v + (size_t)cell_of(t0 + tok, p.H, p.W, dir) * DV + pc * 8;
+        const size_t o = off_v + (size_t)gm.cell(t0 + tok) * DV + pc * 8;
         *reinterpret_cast<uint4*>(out + o) = *reinterpret_cast<const uint4*>(so + tok * OS + pc * 8);
       }
     }
@@ -1096,9 +1167,9 @@ __global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 2 : 1) void chun
 template <int DK, int DV>
 struct SumSmemH {
   static constexpr int AS = kChunk + 8;
-  alignas(16) f16 kt[DK * AS];   // k^T [d_k][token]
-  alignas(16) f16 lat[DK * AS];  // log-alpha^T
-  alignas(16) f16 vt[DV * AS];   // V^T
+  alignas(16) f16 kt[trow(DK) * AS];   // k^T [trow(d_k)][token]
+  alignas(16) f16 lat[trow(DK) * AS];  // log-alpha^T
+  alignas(16) f16 vt[trow(DV) * AS];   // V^T
 };
 
 template <int DK, int DV>
@@ -1114,7 +1185,7 @@ __global__ __launch_bounds__(kThreads) void span_summary_f16_kernel(FwdParams p)
   const int bh = blockIdx.x / p.n_spans;
   const int span = blockIdx.x - bh * p.n_spans;
   const int b = bh / p.heads;
-  const int dir = (p.scan_dir == 4) ? (b & 3) : p.scan_dir;
+  const GridMap gm = grid_map(p, b);
   const size_t off_k = (size_t)bh * p.T * DK;
   const size_t off_v = (size_t)bh * p.T * DV;
   const int c_begin = span * p.span_chunks;
@@ -1144,13 +1215,13 @@ __global__ __launch_bounds__(kThreads) void span_summary_f16_kernel(FwdParams p)
 
   LoaderH<DK, DV, false, false> ld;
   ld.load(nullptr, k, la, v, off_k, off_v, c_begin * kChunk, min(kChunk, p.T - c_begin * kChunk),
-          p.H, p.W, dir);
+          gm);
   for (int c = c_begin; c < c_end; ++c) {
     __syncthreads();  // previous chunk's reads of the tiles are done
     ld.store(nullptr, nullptr, 0, sm.kt, sm.lat, sm.vt, AS);
     if (c + 1 < c_end) {
       const int t1 = (c + 1) * kChunk;
-      ld.load(nullptr, k, la, v, off_k, off_v, t1, min(kChunk, p.T - t1), p.H, p.W, dir);
+      ld.load(nullptr, k, la, v, off_k, off_v, t1, min(kChunk, p.T - t1), gm);
     }
     __syncthreads();
 #pragma unroll
@@ -1160,7 +1231,7 @@ __global__ __launch_bounds__(kThreads) void span_summary_f16_kernel(FwdParams p)
       f16x4 lat4[4];
 #pragma unroll
       for (int J = 0; J < 4; ++J)
-        lat4[J] = *reinterpret_cast<const f16x4*>(sm.lat + dim * AS + 16 * J + 4 * g);
+        lat4[J] = *reinterpret_cast<const f16x4*>(sm.lat + trow(dim) * AS + 16 * J + 4 * g);
       // decay from token 16I+4g+u to the chunk end, at key dim `dim`
       f32x4 rest[4];
 #pragma unroll
@@ -1180,7 +1251,7 @@ __global__ __launch_bounds__(kThreads) void span_summary_f16_kernel(FwdParams p)
         for (int u = 0; u < 4; ++u) st[d][cb][u] *= gch;
 #pragma unroll
       for (int I = 0; I < 4; ++I) {
-        const f16x4 k4 = *reinterpret_cast<const f16x4*>(sm.kt + dim * AS + 16 * I + 4 * g);
+        const f16x4 k4 = *reinterpret_cast<const f16x4*>(sm.kt + trow(dim) * AS + 16 * I + 4 * g);
         f16x4 kl;
 #pragma unroll
         for (int u = 0; u < 4; ++u)
@@ -1188,7 +1259,7 @@ __global__ __launch_bounds__(kThreads) void span_summary_f16_kernel(FwdParams p)
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
           const f16x4 vv =
-              *reinterpret_cast<const f16x4*>(sm.vt + (16 * cb + n16) * AS + 16 * I + 4 * g);
+              *reinterpret_cast<const f16x4*>(sm.vt + trow(16 * cb + n16) * AS + 16 * I + 4 * g);
           st[d][cb] = mma16(vv, kl, st[d][cb]);
         }
       }

@@ -64,6 +64,15 @@ def test_small_grids(dtype, H, W, d):
     parity(q, k, v, la, d, dtype == "fp16", "%s %dx%d dir %d" % (dtype, H, W, d))
 
 
+@pytest.mark.parametrize("d", [0, 1, 2, 3])
+@pytest.mark.parametrize("H,W", [(37, 53), (129, 7), (5, 211)])
+def test_odd_grids_multi_span(H, W, d):
+    # several spans per sequence, a ragged tail chunk, and non-power-of-two
+    # divisors in the scan-direction remap
+    q, k, v, la = make_inputs(1, 2, H, W, 64, 64, "fp16", 1.0, seed=H + W + d)
+    parity(q, k, v, la, d, True, "fp16 %dx%d dir %d" % (H, W, d))
+
+
 @pytest.mark.parametrize("dk,dv,dtype", [(64, 128, "fp16"), (128, 64, "fp16"),
                                          (128, 128, "fp16"), (64, 128, "fp32")])
 @pytest.mark.parametrize("d", [0, 3])
