@@ -87,21 +87,33 @@ class Runner:
         self.cursor = 0
         torch.cuda.synchronize()
 
+        # raw C-ABI arguments of every set, so the timed loop only marshals ints
+        from recurrent_vision_token_amd import _lib
+        lib = _lib.load()
+        self.fn = lib.gla_chunk_fwd if wl.dtype == "fp16" else lib.gla_chunk_fwd_f32
+        stream = torch.cuda.current_stream(self.dev).cuda_stream
+        self.args = [(q.data_ptr(), k.data_ptr(), v.data_ptr(), la.data_ptr(), d, wl.B, wl.heads,
+                      wl.H, wl.W, wl.d_k, wl.d_v, wl.chunk, out.data_ptr(), fs.data_ptr(), stream)
+                     for (q, k, v, la, out, fs, d) in self.sets]
+
     def step(self, events=None):
         """One pass of the call list; events: list of 4-event lists, one per call."""
         from recurrent_vision_token_amd import _lib
-        from recurrent_vision_token_amd import gla_chunk_fwd
         for c in range(len(self.wl.calls)):
-            q, k, v, la, out, fs, d = self.sets[self.cursor]
+            a = self.args[self.cursor]
             self.cursor = (self.cursor + 1) % len(self.sets)
             if events is not None:
                 rc = _lib.set_kernel_events([e.cuda_event for e in events[c]])
                 if rc != 0:
                     raise RuntimeError("gla_set_kernel_events failed: %d" % rc)
-            gla_chunk_fwd(q, k, v, la, d, out=out, final_state=fs)
+            rc = self.fn(*a)
+            if rc != 0:
+                raise RuntimeError("gla_chunk_fwd failed: %d" % rc)
 
 
 def time_workload(wl, torch, steps, warmup):
+    """Timed loop (no instrumentation), then an event-instrumented pass of the
+    same length for the per-kernel durations."""
     r = Runner(wl, torch)
     ncall = len(wl.calls)
     log("[bench] %s: %d device input sets (%.0f MB), %d calls/step" %
@@ -109,6 +121,16 @@ def time_workload(wl, torch, steps, warmup):
     for _ in range(warmup):
         r.step()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        r.step()
+    t_issue = time.perf_counter()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / steps
+    log("[bench] %s: host issue %.1f us/call, wall %.1f us/call" %
+        (wl.name, (t_issue - t0) * 1e6 / (steps * ncall), (t1 - t0) * 1e6 / (steps * ncall)))
+
     evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(ncall)]
            for _ in range(steps)]
     stream = torch.cuda.current_stream()
@@ -117,12 +139,9 @@ def time_workload(wl, torch, steps, warmup):
             for e in per_call:
                 e.record(stream)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for s in range(steps):
         r.step(evs[s])
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / steps
     k_ms = {"span_summary": [], "span_scan": [], "chunk_output": [], "call": []}
     for per_step in evs:
         for e in per_step:

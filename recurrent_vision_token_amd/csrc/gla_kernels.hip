@@ -114,6 +114,11 @@ __device__ __forceinline__ GridMap grid_map(const FwdParams& p, int b) {
 // token pair land in different LDS banks.
 __device__ __forceinline__ constexpr int trow(int d) { return d + (d >> 3); }
 
+// Branch-free select of a loaded 16-byte piece.
+__device__ __forceinline__ uint4 sel(bool c, uint4 a, uint4 b) {
+  return make_uint4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
+}
+
 __device__ __forceinline__ f32x4 mma32(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
@@ -398,48 +403,67 @@ __global__ __launch_bounds__(kThreads) void span_summary_kernel(FwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 2: sequential scan over spans, elementwise over the state.  Replaces
-// each span summary by the state entering that span.
+// Kernel 2: scan over spans, elementwise over the d_k x d_v state, turning each
+// span summary (G_s, L_s) into the state entering span s:
+//   E_0 = 0,  E_{s+1} = diag(G_s) E_s + L_s.
+// The combine (G, L) o (G', L') = (G G', diag(G') L + L') is associative, so
+// spans are taken in rounds of kScanSeg segments of kScanU spans, one wave per
+// segment: each lane loads its segment's summaries at once (one memory round
+// trip), folds them from zero, the folds are exchanged through LDS to give
+// every segment its carry-in, and the same registers then yield the entry
+// states.
+constexpr int kScanSeg = 4;
+constexpr int kScanU = 32;
+constexpr int kScanElems = kThreads / kScanSeg;   // state elements per workgroup
+
 template <int DK, int DV>
 __global__ __launch_bounds__(kThreads) void span_scan_kernel(FwdParams p) {
+  __shared__ float seg_l[kScanSeg][kScanElems];
+  __shared__ float seg_g[kScanSeg][kScanElems];
   const int bh = blockIdx.x;
-  const int e = blockIdx.y * kThreads + threadIdx.x;  // element of the d_k x d_v state
+  const int seg = threadIdx.x / kScanElems;
+  const int le = threadIdx.x - seg * kScanElems;
+  const int e = blockIdx.y * kScanElems + le;
   const int dim = e / DV;
-  const size_t sbase = (size_t)bh * p.n_spans * DK * DV + e;
-  const size_t gbase = (size_t)bh * p.n_spans * DK + dim;
-  float s = 0.f;
-  int sp = 0;
-  constexpr int U = 32;  // summaries loaded ahead of the dependent chain
-  for (; sp + U <= p.n_spans; sp += U) {
-    float L[U], G[U];
+  float* const L = p.span_state + (size_t)bh * p.n_spans * DK * DV + e;
+  const float* const G = p.span_gate + (size_t)bh * p.n_spans * DK + dim;
+
+  float carry = 0.f;  // state entering the current round
+  for (int r0 = 0; r0 < p.n_spans; r0 += kScanSeg * kScanU) {
+    const int s0 = r0 + seg * kScanU;
+    float l[kScanU], gg[kScanU];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      L[u] = p.span_state[sbase + (size_t)(sp + u) * DK * DV];
-      G[u] = p.span_gate[gbase + (size_t)(sp + u) * DK];
+    for (int u = 0; u < kScanU; ++u) {
+      // slots past the last span re-read span 0 and are neutralised (no
+      // branches around the loads, so all of them are in flight together)
+      const bool in = s0 + u < p.n_spans;
+      const int sp = in ? s0 + u : 0;
+      const float lv = L[(size_t)sp * DK * DV];
+      const float gv = G[(size_t)sp * DK];
+      l[u] = in ? lv : 0.f;
+      gg[u] = in ? gv : 1.f;
+    }
+    float fl = 0.f, fg = 1.f;
+#pragma unroll
+    for (int u = 0; u < kScanU; ++u) {
+      fl = gg[u] * fl + l[u];
+      fg *= gg[u];
+    }
+    seg_l[seg][le] = fl;
+    seg_g[seg][le] = fg;
+    __syncthreads();
+    float run = carry, next = carry;
+    for (int j = 0; j < kScanSeg; ++j) {
+      if (j < seg) run = seg_g[j][le] * run + seg_l[j][le];
+      next = seg_g[j][le] * next + seg_l[j][le];
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      p.span_state[sbase + (size_t)(sp + u) * DK * DV] = s;
-      s = G[u] * s + L[u];
+    for (int u = 0; u < kScanU; ++u) {
+      if (s0 + u < p.n_spans) L[(size_t)(s0 + u) * DK * DV] = run;
+      run = gg[u] * run + l[u];
     }
-  }
-  const int rest = p.n_spans - sp;
-  if (rest > 0) {
-    float L[U], G[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (u < rest) {
-        L[u] = p.span_state[sbase + (size_t)(sp + u) * DK * DV];
-        G[u] = p.span_gate[gbase + (size_t)(sp + u) * DK];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (u < rest) {
-        p.span_state[sbase + (size_t)(sp + u) * DK * DV] = s;
-        s = G[u] * s + L[u];
-      }
-    }
+    carry = next;
+    __syncthreads();  // the LDS folds are reused by the next round
   }
 }
 
@@ -732,25 +756,6 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 constexpr float kLog2eHi = 1.4423828125f;          // fp16(log2 e)
 constexpr float kLog2eLo = 1.4426950408889634f - 1.4423828125f;
 
-template <int DK, int DV>
-struct OutSmemH {
-  static constexpr int QS = DK + 8;      // [token][d_k] rows
-  static constexpr int AS = kChunk + 8;  // [*][token] rows
-  static constexpr int OS = DV + 8;      // [token][d_v] rows
-  static constexpr int KV_ROWS = 48 + 32 + 16;
-  static constexpr int KV_ELEMS = (KV_ROWS * QS > kChunk * OS) ? KV_ROWS * QS : kChunk * OS;
-  static constexpr int LAT_ELEMS =
-      (trow(DK) * AS > kChunk * AS) ? trow(DK) * AS : kChunk * AS;
-  alignas(16) f16 q[kChunk * QS];    // raw q, then q_t*exp(c_t)   (c: decay inside the sub-block)
-  alignas(16) f16 qt[kChunk * QS];   // q_t*exp(b_t)               (b: decay from the chunk start)
-  alignas(16) f16 k[kChunk * QS];    // raw k, then k_s*exp(-c_s)
-  alignas(16) f16 kv[KV_ELEMS];      // k decayed to the end of its sub-block (rows 0..47), of the
-                                     // next one (48..79), of the one after (80..95); then O staging
-  alignas(16) f16 lat[LAT_ELEMS];    // log-alpha^T [trow(d_k)][token], then A[t][s]
-  alignas(16) f16 vt[trow(DV) * AS]; // V^T [trow(d_v)][token]
-  alignas(16) f16 klt[DK * AS];      // (k_s*exp(b_last-b_s))^T [d_k][token]
-  alignas(16) float g[DK];           // exp(b_last)
-};
 
 // Row pieces of q and k, token-pair pieces of log-alpha and v (for the
 // transposed tiles).  Pieces past the sequence end read as zero.
@@ -765,6 +770,9 @@ struct LoaderH {
   uint4 rk[K_ROWS ? NK : 2 * NKP];
   uint4 rl[2 * NKP];
   uint4 rv[2 * NVP];
+  // validity of each piece (bit j: row piece j, bit 16+i: pair piece i, bit
+  // 24+i: v pair piece i); invalid pieces are zeroed when staged
+  uint32_t okm;
 
   __device__ __forceinline__ static uint4 ld(const f16* p) {
     return *reinterpret_cast<const uint4*>(p);
@@ -773,16 +781,19 @@ struct LoaderH {
   __device__ __forceinline__ void load(const f16* q, const f16* k, const f16* la, const f16* v,
                                        size_t off_k, size_t off_v, int t0, int valid, const GridMap& gm) {
     const int tid = threadIdx.x;
-    const uint4 z = make_uint4(0, 0, 0, 0);
+    okm = 0;
     if (WITH_Q || K_ROWS) {
 #pragma unroll
       for (int j = 0; j < NK; ++j) {
         const int id = tid + kThreads * j;
         const int tok = id / PK, pc = id - tok * PK;
         const bool in = tok < valid;
-        const size_t o = in ? off_k + (size_t)gm.cell(t0 + tok) * DK + pc * 8 : 0;
-        if (WITH_Q) rq[j] = in ? ld(q + o) : z;
-        if (K_ROWS) rk[j] = in ? ld(k + o) : z;
+        // out-of-range lanes read the sequence's first row and drop it when
+        // staging: no branches around the loads, so waits can count them
+        const size_t o = off_k + (size_t)gm.cell(in ? t0 + tok : 0) * DK + pc * 8;
+        if (WITH_Q) rq[j] = ld(q + o);
+        if (K_ROWS) rk[j] = ld(k + o);
+        okm |= (in ? 1u : 0u) << j;
       }
     }
 #pragma unroll
@@ -793,9 +804,10 @@ struct LoaderH {
       for (int h = 0; h < 2; ++h) {
         const int tok = 2 * tp + h;
         const bool in = tok < valid;
-        const size_t o = in ? off_k + (size_t)gm.cell(t0 + tok) * DK + pc * 8 : 0;
-        rl[2 * j + h] = in ? ld(la + o) : z;
-        if (!K_ROWS) rk[2 * j + h] = in ? ld(k + o) : z;
+        const size_t o = off_k + (size_t)gm.cell(in ? t0 + tok : 0) * DK + pc * 8;
+        rl[2 * j + h] = ld(la + o);
+        if (!K_ROWS) rk[2 * j + h] = ld(k + o);
+        okm |= (in ? 1u : 0u) << (16 + 2 * j + h);
       }
     }
 #pragma unroll
@@ -806,8 +818,8 @@ struct LoaderH {
       for (int h = 0; h < 2; ++h) {
         const int tok = 2 * tp + h;
         const bool in = tok < valid;
-        rv[2 * j + h] =
-            in ? ld(v + off_v + (size_t)gm.cell(t0 + tok) * DV + pc * 8) : z;
+        rv[2 * j + h] = ld(v + off_v + (size_t)gm.cell(in ? t0 + tok : 0) * DV + pc * 8);
+        okm |= (in ? 1u : 0u) << (24 + 2 * j + h);
       }
     }
   }
@@ -829,27 +841,31 @@ struct LoaderH {
   __device__ __forceinline__ void store(f16* sq, f16* sk, int QS, f16* skt, f16* slat, f16* svt,
                                         int AS) const {
     const int tid = threadIdx.x;
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    auto ok = [&](int bit) { return ((okm >> bit) & 1u) != 0; };
     if (WITH_Q || K_ROWS) {
 #pragma unroll
       for (int j = 0; j < NK; ++j) {
         const int id = tid + kThreads * j;
         const int tok = id / PK, pc = id - tok * PK;
-        if (WITH_Q) *reinterpret_cast<uint4*>(sq + tok * QS + pc * 8) = rq[j];
-        if (K_ROWS) *reinterpret_cast<uint4*>(sk + tok * QS + pc * 8) = rk[j];
+        if (WITH_Q) *reinterpret_cast<uint4*>(sq + tok * QS + pc * 8) = sel(ok(j), rq[j], z);
+        if (K_ROWS) *reinterpret_cast<uint4*>(sk + tok * QS + pc * 8) = sel(ok(j), rk[j], z);
       }
     }
 #pragma unroll
     for (int j = 0; j < NKP; ++j) {
       const int id = tid + kThreads * j;
       const int tp = id / PK, pc = id - tp * PK;
-      put_pair_t(slat, AS, pc, tp, rl[2 * j], rl[2 * j + 1]);
-      if (!K_ROWS) put_pair_t(skt, AS, pc, tp, rk[2 * j], rk[2 * j + 1]);
+      const bool a = ok(16 + 2 * j), b = ok(17 + 2 * j);
+      put_pair_t(slat, AS, pc, tp, sel(a, rl[2 * j], z), sel(b, rl[2 * j + 1], z));
+      if (!K_ROWS) put_pair_t(skt, AS, pc, tp, sel(a, rk[2 * j], z), sel(b, rk[2 * j + 1], z));
     }
 #pragma unroll
     for (int j = 0; j < NVP; ++j) {
       const int id = tid + kThreads * j;
       const int tp = id / PV, pc = id - tp * PV;
-      put_pair_t(svt, AS, pc, tp, rv[2 * j], rv[2 * j + 1]);
+      put_pair_t(svt, AS, pc, tp, sel(ok(24 + 2 * j), rv[2 * j], z),
+                 sel(ok(25 + 2 * j), rv[2 * j + 1], z));
     }
   }
 };
@@ -872,13 +888,134 @@ __device__ __forceinline__ f16x4 identity16() {
 }
 
 // ---------------------------------------------------------------------------
-// Output kernel, float16.
+// Output kernel, float16.  The span is walked in 32-token steps (two 16-token
+// sub-blocks), which keeps the shared tiles near 37 KB so four workgroups (four
+// waves per SIMD) share a CU.  Per step:
+//   stage  : q, k row-major; log-alpha and v transposed (token pairs)
+//   P      : wave w owns key dims 16w.. : in-sub-block cumulative decay c by
+//            MFMA, exp(+-c), DPP broadcast of the sub-block decays, anchored
+//            q / k, q decayed from the step start, keys decayed to the end of
+//            sub-block 0 and to the step end (transposed by an identity MFMA)
+//   A      : score tiles (0,0), (1,0), (1,1); tile (0,1) is zeroed
+//   O      : wave w owns value columns 16w.. : O^T = V^T A^T + S^T Qt^T, then
+//            S <- diag(exp(b_end)) S + KL^T V
+//   W      : output rows to their grid cells
+constexpr int kStep = 32;
+
+__host__ __device__ constexpr int trow_h(int d) { return d + (d >> 3); }
+
 template <int DK, int DV>
-__global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 2 : 1) void chunk_output_f16_kernel(
+struct StepSmem {
+  static constexpr int QS = DK + 8;      // [token][d_k] rows
+  static constexpr int AS = kStep + 8;   // [*][token] rows
+  static constexpr int OS = DV + 8;      // [token][d_v] rows
+  static constexpr int LAT_ELEMS =
+      (trow_h(DK) * AS > kStep * AS) ? trow_h(DK) * AS : kStep * AS;
+  alignas(16) f16 q[kStep * QS];     // raw q, then q_t*exp(c_t)  (c: decay inside the sub-block)
+  alignas(16) f16 qt[kStep * QS];    // q_t*exp(b_t)              (b: decay from the step start)
+  alignas(16) f16 k[kStep * QS];     // raw k, then k_s*exp(-c_s)
+  alignas(16) f16 kv[kSub * QS];     // sub-block 0 keys decayed to the end of sub-block 0
+  alignas(16) f16 lat[LAT_ELEMS];    // log-alpha^T [trow(d_k)][token], then A[t][s]
+  alignas(16) f16 vt[trow_h(DV) * AS];
+  alignas(16) f16 klt[DK * AS];      // keys decayed to the step end, [d_k][token]
+  alignas(16) f16 o[kStep * OS];     // output staging
+  alignas(16) float g[DK];           // exp(decay over the step)
+};
+
+// One 32-token step of q, k (row pieces) and log-alpha, v (token-pair pieces).
+template <int DK, int DV>
+struct StepLoader {
+  static constexpr int PK = DK / 8, PV = DV / 8;
+  static constexpr int NQ = kStep * PK / kThreads;                 // q / k row pieces per thread
+  static constexpr int NPAIR = (kStep / 2) * (PK + PV);            // la + v pair items
+  static constexpr int NP = (NPAIR + kThreads - 1) / kThreads;     // pair items per thread
+  static_assert(NQ >= 1 && (kStep / 2) * PK % 64 == 0 && NPAIR % 64 == 0, "tile shape");
+  uint4 rq[NQ], rk[NQ], rp[2 * NP];
+  uint32_t okm;  // bit j: row piece j valid; bit 8+i: pair piece i valid
+
+  __device__ __forceinline__ static uint4 ld(const f16* p) {
+    return *reinterpret_cast<const uint4*>(p);
+  }
+
+  __device__ __forceinline__ void load(const f16* q, const f16* k, const f16* la, const f16* v,
+                                       size_t off_k, size_t off_v, int t0, int valid,
+                                       const GridMap& gm) {
+    const int tid = threadIdx.x;
+    okm = 0;
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      const int id = tid + kThreads * j;
+      const int tok = id / PK, pc = id - tok * PK;
+      const bool in = tok < valid;
+      const size_t o = off_k + (size_t)gm.cell(in ? t0 + tok : 0) * DK + pc * 8;
+      rq[j] = ld(q + o);
+      rk[j] = ld(k + o);
+      okm |= (in ? 1u : 0u) << j;
+    }
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const int id = tid + kThreads * j;
+      if (id < NPAIR) {
+        const bool is_la = id < (kStep / 2) * PK;
+        const int rel = is_la ? id : id - (kStep / 2) * PK;
+        const int pp = is_la ? PK : PV;
+        const int tp = rel / pp, pc = rel - tp * pp;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int tok = 2 * tp + h;
+          const bool in = tok < valid;
+          const size_t cell = (size_t)gm.cell(in ? t0 + tok : 0);
+          const f16* src = is_la ? la + off_k + cell * DK + pc * 8 : v + off_v + cell * DV + pc * 8;
+          rp[2 * j + h] = ld(src);
+          okm |= (in ? 1u : 0u) << (8 + 2 * j + h);
+        }
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(StepSmem<DK, DV>& sm) const {
+    constexpr int QS = StepSmem<DK, DV>::QS, AS = StepSmem<DK, DV>::AS;
+    const int tid = threadIdx.x;
+    const uint4 z = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      const int id = tid + kThreads * j;
+      const int tok = id / PK, pc = id - tok * PK;
+      const bool in = ((okm >> j) & 1u) != 0;
+      *reinterpret_cast<uint4*>(sm.q + tok * QS + pc * 8) = sel(in, rq[j], z);
+      *reinterpret_cast<uint4*>(sm.k + tok * QS + pc * 8) = sel(in, rk[j], z);
+    }
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const int id = tid + kThreads * j;
+      if (id < NPAIR) {
+        const bool is_la = id < (kStep / 2) * PK;
+        const int rel = is_la ? id : id - (kStep / 2) * PK;
+        const int pp = is_la ? PK : PV;
+        const int tp = rel / pp, pc = rel - tp * pp;
+        f16* dst = is_la ? sm.lat : sm.vt;
+        const f16x8 x = __builtin_bit_cast(f16x8, sel(((okm >> (8 + 2 * j)) & 1u) != 0, rp[2 * j], z));
+        const f16x8 y =
+            __builtin_bit_cast(f16x8, sel(((okm >> (9 + 2 * j)) & 1u) != 0, rp[2 * j + 1], z));
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          f16x2 pr;
+          pr[0] = x[u];
+          pr[1] = y[u];
+          *reinterpret_cast<f16x2*>(dst + (9 * pc + u) * AS + 2 * tp) = pr;  // row trow(8pc+u)
+        }
+      }
+    }
+  }
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 4 : (DK == 128 && DV == 128) ? 1 : 2) void chunk_output_f16_kernel(
     FwdParams p) {
-  using SM = OutSmemH<DK, DV>;
+  using SM = StepSmem<DK, DV>;
   __shared__ SM sm;
   constexpr int QS = SM::QS, AS = SM::AS, OS = SM::OS;
+  constexpr int NR = DK / 16, NC = DV / 64;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n16 = lane & 15, g = lane >> 4;
@@ -889,8 +1026,8 @@ __global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 2 : 1) void chun
   const GridMap gm = grid_map(p, b);
   const size_t off_k = (size_t)bh * p.T * DK;
   const size_t off_v = (size_t)bh * p.T * DV;
-  const int c_begin = span * p.span_chunks;
-  const int c_end = min(c_begin + p.span_chunks, p.n_chunks);
+  const int t_begin = span * p.span_chunks * kChunk;
+  const int t_end = min(t_begin + p.span_chunks * kChunk, p.T);
 
   const f16* q = static_cast<const f16*>(p.q);
   const f16* k = static_cast<const f16*>(p.k);
@@ -898,114 +1035,95 @@ __global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 2 : 1) void chun
   const f16* v = static_cast<const f16*>(p.v);
   f16* out = static_cast<f16*>(p.out);
 
-  StateRegs<DK, DV> st;
+  // State tiles: wave w owns value columns 16(w + 4j) .. ; tile (r, j) holds
+  // S[16r + 4g + u][16(w + 4j) + n] in lane (g, n).
+  f32x4 st[NR][NC];
   {
     const float* src =
         (span > 0) ? p.span_state + ((size_t)bh * p.n_spans + span) * DK * DV : nullptr;
 #pragma unroll
-    for (int j = 0; j < StateRegs<DK, DV>::NC; ++j) {
+    for (int j = 0; j < NC; ++j) {
       const int col = 16 * (wave + 4 * j) + n16;
 #pragma unroll
-      for (int r = 0; r < StateRegs<DK, DV>::NR; ++r)
+      for (int r = 0; r < NR; ++r)
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          st.s[r][j][u] = src ? src[(16 * r + 4 * g + u) * DV + col] : 0.f;
+        for (int u = 0; u < 4; ++u) st[r][j][u] = src ? src[(16 * r + 4 * g + u) * DV + col] : 0.f;
     }
   }
 
   const f16x4 u_hi = upper_incl(kLog2eHi), u_lo = upper_incl(kLog2eLo);
   const f16x4 ident = identity16();
-  const uint32_t tile_codes = (wave == 0) ? 0x313000u
-                            : (wave == 1) ? 0x321110u
-                            : (wave == 2) ? 0x2120u
-                                          : 0x3322u;
-  const int n_tiles = (wave < 2) ? 3 : 2;
-  f16* const kv1 = sm.kv;
-  f16* const kv2 = sm.kv + 48 * QS;
-  f16* const kv3 = sm.kv + 80 * QS;
-  f16* const so = sm.kv;   // output staging reuses the key-variant region
   f16* const sa = sm.lat;  // score tile reuses the log-alpha^T region
 
-  LoaderH<DK, DV, true, true> ld;
-  ld.load(q, k, la, v, off_k, off_v, c_begin * kChunk, min(kChunk, p.T - c_begin * kChunk), gm);
-  for (int c = c_begin; c < c_end; ++c) {
-    const int t0 = c * kChunk;
-    const int valid = min(kChunk, p.T - t0);
-    ld.store(sm.q, sm.k, QS, nullptr, sm.lat, sm.vt, AS);
-    if (c + 1 < c_end) {
-      const int t1 = t0 + kChunk;
-      ld.load(q, k, la, v, off_k, off_v, t1, min(kChunk, p.T - t1), gm);
-    }
+  StepLoader<DK, DV> ld;
+  ld.load(q, k, la, v, off_k, off_v, t_begin, min(kStep, t_end - t_begin), gm);
+  for (int t0 = t_begin; t0 < t_end; t0 += kStep) {
+    const int valid = min(kStep, t_end - t0);
+    ld.store(sm);
+    if (t0 + kStep < t_end) ld.load(q, k, la, v, off_k, off_v, t0 + kStep, min(kStep, t_end - t0 - kStep), gm);
     __syncthreads();
 
-    // ---- Phase P: wave w owns key dims 16*db .. 16*db+15, db = w (+4).
-    // All LDS operands of the phase are read up front, then consumed.
+    // ---- Phase P
 #pragma unroll
     for (int dbi = 0; dbi < DK / 64; ++dbi) {
       const int db = wave + 4 * dbi;
-      const int dim0 = 16 * db + 4 * g;  // this lane's 4 key dims in the row layout
-      f16x4 lat4[4], q4[4], k4[4];
+      const int dim0 = 16 * db + 4 * g;
+      f16x4 lat4[2], q4[2], k4[2];
 #pragma unroll
-      for (int I = 0; I < 4; ++I) {
-        lat4[I] = *reinterpret_cast<const f16x4*>(sm.lat + trow(16 * db + n16) * AS + 16 * I + 4 * g);
+      for (int I = 0; I < 2; ++I) {
+        lat4[I] = *reinterpret_cast<const f16x4*>(sm.lat + trow_h(16 * db + n16) * AS + 16 * I + 4 * g);
         q4[I] = *reinterpret_cast<const f16x4*>(sm.q + (16 * I + n16) * QS + dim0);
         k4[I] = *reinterpret_cast<const f16x4*>(sm.k + (16 * I + n16) * QS + dim0);
       }
-      f32x4 c2[4];
+      f32x4 c2[2];
 #pragma unroll
-      for (int I = 0; I < 4; ++I) {
-        // c*log2(e) at token 16I+n16, dims dim0..dim0+3
+      for (int I = 0; I < 2; ++I) {
         c2[I] = mma16(lat4[I], u_hi, f32x4{0.f, 0.f, 0.f, 0.f});
         c2[I] = mma16(lat4[I], u_lo, c2[I]);
       }
-      f32x4 eq[4], ek[4], ed[4];
+      f32x4 eq[2], ek[2], ed[2];
 #pragma unroll
-      for (int I = 0; I < 4; ++I)
+      for (int I = 0; I < 2; ++I)
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           eq[I][u] = exp2_fast(c2[I][u]);
           ek[I][u] = exp2_fast(-c2[I][u]);
           ed[I][u] = row_bcast15(eq[I][u]);  // exp(decay over sub-block I)
         }
-      f32x4 gl;
+      if (n16 == 0) {
+        f32x4 gl;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) gl[u] = ed[0][u] * ed[1][u] * ed[2][u] * ed[3][u];
-      if (n16 == 0) *reinterpret_cast<f32x4*>(sm.g + dim0) = gl;
-      f16x4 klh[4];
+        for (int u = 0; u < 4; ++u) gl[u] = ed[0][u] * ed[1][u];
+        *reinterpret_cast<f32x4*>(sm.g + dim0) = gl;
+      }
+      f16x4 klh[2];
 #pragma unroll
-      for (int I = 0; I < 4; ++I) {
+      for (int I = 0; I < 2; ++I) {
         const int row = 16 * I + n16;
-        f16x4 ql, qt, kd, kv_1, kv_2, kv_3;
+        f16x4 ql, qt, kd, kv0;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          float e_start = 1.f;  // exp(b at the end of sub-block I-1)
-#pragma unroll
-          for (int L = 0; L < I; ++L) e_start *= ed[L][u];
           const float qf = (float)q4[I][u];
+          const float eqs = (I == 0) ? eq[I][u] : eq[I][u] * ed[0][u];
           ql[u] = (f16)(qf * eq[I][u]);
-          qt[u] = (f16)(qf * (eq[I][u] * e_start));
+          qt[u] = (f16)(qf * eqs);
           const float kf = (float)k4[I][u] * ek[I][u];
           kd[u] = (f16)kf;
-          float kx = kf * ed[I][u];  // decayed to the end of sub-block I
-          kv_1[u] = (f16)kx;
-#pragma unroll
-          for (int L = I + 1; L < 4; ++L) {
-            kx *= ed[L][u];
-            if (L == I + 1) kv_2[u] = (f16)kx;
-            if (L == I + 2) kv_3[u] = (f16)kx;
+          const float kend = kf * ed[I][u];  // decayed to the end of sub-block I
+          if (I == 0) {
+            kv0[u] = (f16)kend;
+            klh[I][u] = (f16)(kend * ed[1][u]);
+          } else {
+            klh[I][u] = (f16)kend;
           }
-          klh[I][u] = (f16)kx;  // decayed to the chunk end
         }
         *reinterpret_cast<f16x4*>(sm.q + row * QS + dim0) = ql;
         *reinterpret_cast<f16x4*>(sm.qt + row * QS + dim0) = qt;
         *reinterpret_cast<f16x4*>(sm.k + row * QS + dim0) = kd;
-        if (I <= 2) *reinterpret_cast<f16x4*>(kv1 + row * QS + dim0) = kv_1;
-        if (I <= 1) *reinterpret_cast<f16x4*>(kv2 + row * QS + dim0) = kv_2;
-        if (I == 0) *reinterpret_cast<f16x4*>(kv3 + row * QS + dim0) = kv_3;
+        if (I == 0) *reinterpret_cast<f16x4*>(sm.kv + n16 * QS + dim0) = kv0;
       }
-      // transpose the decayed keys to [dim][token] with identity MFMAs
 #pragma unroll
-      for (int I = 0; I < 4; ++I) {
+      for (int I = 0; I < 2; ++I) {
         const f32x4 tr = mma16(klh[I], ident, f32x4{0.f, 0.f, 0.f, 0.f});
         f16x4 trh;
 #pragma unroll
@@ -1015,69 +1133,45 @@ __global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 2 : 1) void chun
     }
     __syncthreads();
 
-    // ---- Phase A: A^T tiles (rows s in sub-block J, cols t in sub-block I), J <= I.
-    // Waves 2 and 3 also zero the upper tiles (0,1) and (2,3) so that every A.V
-    // step below is a full 32-token 16x16x32 MFMA: accumulation chains never mix
-    // MFMA shapes.
-    {
-      f16x8 ta[3][DK / 32], tb[3][DK / 32];
+    // ---- Phase A: wave 0 -> (0,0), wave 1 -> (1,0), wave 2 -> (1,1), wave 3 zeroes (0,1).
+    if (wave < 3) {
+      const int I = (wave == 0) ? 0 : 1, J = (wave == 2) ? 1 : 0;
+      const f16* kb = (I != J) ? sm.kv : sm.k + 16 * J * QS;
+      f16x8 ta[DK / 32], tb[DK / 32];
 #pragma unroll
-      for (int ti = 0; ti < 3; ++ti) {
-        if (ti < n_tiles) {
-          const int code = (tile_codes >> (8 * ti)) & 0xff;
-          const int I = code >> 4, J = code & 0xf;
-          const int gap = I - J;
-          const f16* kb = (gap == 0) ? sm.k : (gap == 1) ? kv1 : (gap == 2) ? kv2 : kv3;
-#pragma unroll
-          for (int st = 0; st < DK / 32; ++st) {
-            ta[ti][st] = *reinterpret_cast<const f16x8*>(kb + (16 * J + n16) * QS + 32 * st + 8 * g);
-            tb[ti][st] = *reinterpret_cast<const f16x8*>(sm.q + (16 * I + n16) * QS + 32 * st + 8 * g);
-          }
-        }
+      for (int st2 = 0; st2 < DK / 32; ++st2) {
+        ta[st2] = *reinterpret_cast<const f16x8*>(kb + n16 * QS + 32 * st2 + 8 * g);
+        tb[st2] = *reinterpret_cast<const f16x8*>(sm.q + (16 * I + n16) * QS + 32 * st2 + 8 * g);
       }
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ti = 0; ti < 3; ++ti) {
-        if (ti < n_tiles) {
-          const int code = (tile_codes >> (8 * ti)) & 0xff;
-          const int I = code >> 4, J = code & 0xf;
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int st2 = 0; st2 < DK / 32; ++st2) acc = mma32(ta[st2], tb[st2], acc);
+      if (I == J) {
 #pragma unroll
-          for (int st = 0; st < DK / 32; ++st) acc = mma32(ta[ti][st], tb[ti][st], acc);
-          if (I == J) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-              if (4 * g + u > n16) acc[u] = 0.f;
-          }
-          f16x4 w;
-#pragma unroll
-          for (int u = 0; u < 4; ++u) w[u] = (f16)acc[u];
-          *reinterpret_cast<f16x4*>(sa + (16 * I + n16) * AS + 16 * J + 4 * g) = w;
-        }
+        for (int u = 0; u < 4; ++u)
+          if (4 * g + u > n16) acc[u] = 0.f;
       }
-      if (wave >= 2) {
-        const int I = (wave == 2) ? 0 : 2;
-        *reinterpret_cast<f16x4*>(sa + (16 * I + n16) * AS + 16 * (I + 1) + 4 * g) =
-            f16x4{(f16)0.f, (f16)0.f, (f16)0.f, (f16)0.f};
-      }
+      f16x4 w;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) w[u] = (f16)acc[u];
+      *reinterpret_cast<f16x4*>(sa + (16 * I + n16) * AS + 16 * J + 4 * g) = w;
+    } else {
+      *reinterpret_cast<f16x4*>(sa + n16 * AS + 16 + 4 * g) =
+          f16x4{(f16)0.f, (f16)0.f, (f16)0.f, (f16)0.f};
     }
     __syncthreads();
 
-    // ---- Phase O: O^T = V^T A^T + S^T Qt^T, then S <- diag(g) S + KL^T V.
+    // ---- Phase O
 #pragma unroll
-    for (int j = 0; j < StateRegs<DK, DV>::NC; ++j) {
+    for (int j = 0; j < NC; ++j) {
       const int col0 = 16 * (wave + 4 * j);
       const int col = col0 + n16;
-      // operands, read up front
-      f16x8 va[2], sb[6], qb[4][DK / 32];
+      const f16x8 va = *reinterpret_cast<const f16x8*>(sm.vt + trow_h(col) * AS + 8 * g);
+      f16x8 sb[2], qb[2][DK / 32];
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-        va[h] = *reinterpret_cast<const f16x8*>(sm.vt + trow(col) * AS + 32 * h + 8 * g);
-#pragma unroll
-      for (int I = 0; I < 4; ++I) {
+      for (int I = 0; I < 2; ++I) {
         const int t = 16 * I + n16;
-#pragma unroll
-        for (int h = 0; h < (I + 2) / 2; ++h)
-          sb[(I < 3 ? I : 4) + h] = *reinterpret_cast<const f16x8*>(sa + t * AS + 32 * h + 8 * g);
+        sb[I] = *reinterpret_cast<const f16x8*>(sa + t * AS + 8 * g);
 #pragma unroll
         for (int rho = 0; rho < DK / 32; ++rho) {
           const int dlo = 32 * rho + 4 * g;
@@ -1090,59 +1184,50 @@ __global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 2 : 1) void chun
           }
         }
       }
+      f32x4 gv[NR];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) gv[r] = *reinterpret_cast<const f32x4*>(sm.g + 16 * r + 4 * g);
       f16x8 sh[DK / 32];
 #pragma unroll
       for (int rho = 0; rho < DK / 32; ++rho)
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          sh[rho][u] = (f16)st.s[2 * rho][j][u];
-          sh[rho][4 + u] = (f16)st.s[2 * rho + 1][j][u];
+          sh[rho][u] = (f16)st[2 * rho][j][u];
+          sh[rho][4 + u] = (f16)st[2 * rho + 1][j][u];
         }
 #pragma unroll
-      for (int I = 0; I < 4; ++I) {
+      for (int I = 0; I < 2; ++I) {
         const int t = 16 * I + n16;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int h = 0; h < (I + 2) / 2; ++h) acc = mma32(va[h], sb[(I < 3 ? I : 4) + h], acc);
+        f32x4 acc = mma32(va, sb[I], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int rho = 0; rho < DK / 32; ++rho) acc = mma32(sh[rho], qb[I][rho], acc);
         f16x4 w;
 #pragma unroll
         for (int u = 0; u < 4; ++u) w[u] = (f16)acc[u];
-        *reinterpret_cast<f16x4*>(so + t * OS + col0 + 4 * g) = w;
+        *reinterpret_cast<f16x4*>(sm.o + t * OS + col0 + 4 * g) = w;
       }
-      // state update for this column block: S <- diag(g) S + KL^T V
-      f16x8 ka[StateRegs<DK, DV>::NR][2];
-      f32x4 gv[StateRegs<DK, DV>::NR];
+      // S <- diag(exp(b_end)) S + KL^T V
 #pragma unroll
-      for (int r = 0; r < StateRegs<DK, DV>::NR; ++r) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          ka[r][h] = *reinterpret_cast<const f16x8*>(sm.klt + (16 * r + n16) * AS + 32 * h + 8 * g);
-        gv[r] = *reinterpret_cast<const f32x4*>(sm.g + 16 * r + 4 * g);
-      }
-#pragma unroll
-      for (int r = 0; r < StateRegs<DK, DV>::NR; ++r) {
-        f32x4 acc = st.s[r][j];
+      for (int r = 0; r < NR; ++r) {
+        const f16x8 kar = *reinterpret_cast<const f16x8*>(sm.klt + (16 * r + n16) * AS + 8 * g);
+        f32x4 acc = st[r][j];
 #pragma unroll
         for (int u = 0; u < 4; ++u) acc[u] *= gv[r][u];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) acc = mma32(ka[r][h], va[h], acc);
-        st.s[r][j] = acc;
+        st[r][j] = mma32(kar, va, acc);
       }
     }
     __syncthreads();
 
-    // ---- Phase W: output rows to their grid cells.
+    // ---- Phase W
     constexpr int PO = DV / 8;
-    constexpr int NO = kChunk * PO / kThreads;
+    constexpr int NO = kStep * PO / kThreads;
 #pragma unroll
     for (int jj = 0; jj < NO; ++jj) {
       const int id = tid + kThreads * jj;
       const int tok = id / PO, pc = id - tok * PO;
       if (tok < valid) {
         const size_t o = off_v + (size_t)gm.cell(t0 + tok) * DV + pc * 8;
-        *reinterpret_cast<uint4*>(out + o) = *reinterpret_cast<const uint4*>(so + tok * OS + pc * 8);
+        *reinterpret_cast<uint4*>(out + o) = *reinterpret_cast<const uint4*>(sm.o + tok * OS + pc * 8);
       }
     }
   }
@@ -1150,12 +1235,12 @@ __global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 2 : 1) void chun
   if (span == p.n_spans - 1 && p.final_state != nullptr) {
     float* dst = p.final_state + (size_t)bh * DK * DV;
 #pragma unroll
-    for (int j = 0; j < StateRegs<DK, DV>::NC; ++j) {
+    for (int j = 0; j < NC; ++j) {
       const int col = 16 * (wave + 4 * j) + n16;
 #pragma unroll
-      for (int r = 0; r < StateRegs<DK, DV>::NR; ++r)
+      for (int r = 0; r < NR; ++r)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) dst[(16 * r + 4 * g + u) * DV + col] = st.s[r][j][u];
+        for (int u = 0; u < 4; ++u) dst[(16 * r + 4 * g + u) * DV + col] = st[r][j][u];
     }
   }
 }
@@ -1213,57 +1298,68 @@ __global__ __launch_bounds__(kThreads) void span_summary_f16_kernel(FwdParams p)
 #pragma unroll
   for (int d = 0; d < NDB; ++d) log_gate[d] = 0.f;
 
-  LoaderH<DK, DV, false, false> ld;
-  ld.load(nullptr, k, la, v, off_k, off_v, c_begin * kChunk, min(kChunk, p.T - c_begin * kChunk),
-          gm);
-  for (int c = c_begin; c < c_end; ++c) {
-    __syncthreads();  // previous chunk's reads of the tiles are done
-    ld.store(nullptr, nullptr, 0, sm.kt, sm.lat, sm.vt, AS);
-    if (c + 1 < c_end) {
-      const int t1 = (c + 1) * kChunk;
-      ld.load(nullptr, k, la, v, off_k, off_v, t1, min(kChunk, p.T - t1), gm);
-    }
-    __syncthreads();
+  // Two chunks of loads in flight.  The loop is unrolled by two with
+  // unconditional loads, so the compiler can wait for just the older chunk: a
+  // chunk index past the span reads nothing and stages zeros, and an all-zero
+  // chunk (no keys, no values, log-alpha 0) leaves the state unchanged.
+  const int t_stop = min(c_end * kChunk, p.T);
+  auto valid_of = [&](int c) { return max(0, min(kChunk, t_stop - c * kChunk)); };
+  LoaderH<DK, DV, false, false> ld0, ld1;
+  ld0.load(nullptr, k, la, v, off_k, off_v, c_begin * kChunk, valid_of(c_begin), gm);
+  ld1.load(nullptr, k, la, v, off_k, off_v, (c_begin + 1) * kChunk, valid_of(c_begin + 1), gm);
+  auto compute_chunk = [&]() {
 #pragma unroll
-    for (int d = 0; d < NDB; ++d) {
-      const int db = wave + 4 * d;
-      const int dim = 16 * db + n16;
-      f16x4 lat4[4];
-#pragma unroll
-      for (int J = 0; J < 4; ++J)
-        lat4[J] = *reinterpret_cast<const f16x4*>(sm.lat + trow(dim) * AS + 16 * J + 4 * g);
-      // decay from token 16I+4g+u to the chunk end, at key dim `dim`
-      f32x4 rest[4];
-#pragma unroll
-      for (int I = 0; I < 4; ++I) {
-        f32x4 acc = mma16(m_diag, lat4[I], f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-        for (int J = I + 1; J < 4; ++J) acc = mma16(m_ones, lat4[J], acc);
-        rest[I] = acc;
-      }
-      // whole-chunk decay of this dim: token 0's remainder plus its own log-alpha
-      const float first = __shfl(rest[0][0] + (float)lat4[0][0], n16, 64);
-      log_gate[d] += first;
-      const float gch = exp2_fast(first * 1.4426950408889634f);
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) st[d][cb][u] *= gch;
-#pragma unroll
-      for (int I = 0; I < 4; ++I) {
-        const f16x4 k4 = *reinterpret_cast<const f16x4*>(sm.kt + trow(dim) * AS + 16 * I + 4 * g);
-        f16x4 kl;
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          kl[u] = (f16)((float)k4[u] * exp2_fast(rest[I][u] * 1.4426950408889634f));
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          const f16x4 vv =
-              *reinterpret_cast<const f16x4*>(sm.vt + trow(16 * cb + n16) * AS + 16 * I + 4 * g);
-          st[d][cb] = mma16(vv, kl, st[d][cb]);
+      for (int d = 0; d < NDB; ++d) {
+        const int db = wave + 4 * d;
+        const int dim = 16 * db + n16;
+        f16x4 lat4[4];
+  #pragma unroll
+        for (int J = 0; J < 4; ++J)
+          lat4[J] = *reinterpret_cast<const f16x4*>(sm.lat + trow(dim) * AS + 16 * J + 4 * g);
+        // decay from token 16I+4g+u to the chunk end, at key dim `dim`
+        f32x4 rest[4];
+  #pragma unroll
+        for (int I = 0; I < 4; ++I) {
+          f32x4 acc = mma16(m_diag, lat4[I], f32x4{0.f, 0.f, 0.f, 0.f});
+  #pragma unroll
+          for (int J = I + 1; J < 4; ++J) acc = mma16(m_ones, lat4[J], acc);
+          rest[I] = acc;
+        }
+        // whole-chunk decay of this dim: token 0's remainder plus its own log-alpha
+        const float first = __shfl(rest[0][0] + (float)lat4[0][0], n16, 64);
+        log_gate[d] += first;
+        const float gch = exp2_fast(first * 1.4426950408889634f);
+  #pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+  #pragma unroll
+          for (int u = 0; u < 4; ++u) st[d][cb][u] *= gch;
+  #pragma unroll
+        for (int I = 0; I < 4; ++I) {
+          const f16x4 k4 = *reinterpret_cast<const f16x4*>(sm.kt + trow(dim) * AS + 16 * I + 4 * g);
+          f16x4 kl;
+  #pragma unroll
+          for (int u = 0; u < 4; ++u)
+            kl[u] = (f16)((float)k4[u] * exp2_fast(rest[I][u] * 1.4426950408889634f));
+  #pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) {
+            const f16x4 vv =
+                *reinterpret_cast<const f16x4*>(sm.vt + trow(16 * cb + n16) * AS + 16 * I + 4 * g);
+            st[d][cb] = mma16(vv, kl, st[d][cb]);
+          }
         }
       }
-    }
+  };
+  for (int c = c_begin; c < c_end; c += 2) {
+    __syncthreads();  // previous chunk's reads of the tiles are done
+    ld0.store(nullptr, nullptr, 0, sm.kt, sm.lat, sm.vt, AS);
+    ld0.load(nullptr, k, la, v, off_k, off_v, (c + 2) * kChunk, valid_of(c + 2), gm);
+    __syncthreads();
+    compute_chunk();
+    __syncthreads();
+    ld1.store(nullptr, nullptr, 0, sm.kt, sm.lat, sm.vt, AS);
+    ld1.load(nullptr, k, la, v, off_k, off_v, (c + 3) * kChunk, valid_of(c + 3), gm);
+    __syncthreads();
+    compute_chunk();
   }
 
   float* dst = p.span_state + ((size_t)bh * p.n_spans + span) * DK * DV;
@@ -1306,7 +1402,7 @@ hipError_t launch_variant(const FwdParams& p, hipStream_t stream, hipEvent_t con
   }
   if ((e = mark(events, 1, stream)) != hipSuccess) return e;
   if (p.n_spans > 1) {
-    hipLaunchKernelGGL((span_scan_kernel<DK, DV>), dim3(BH, DK * DV / kThreads), dim3(kThreads),
+    hipLaunchKernelGGL((span_scan_kernel<DK, DV>), dim3(BH, DK * DV / kScanElems), dim3(kThreads),
                        0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
