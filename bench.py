@@ -97,7 +97,7 @@ class Runner:
                      for (q, k, v, la, out, fs, d) in self.sets]
 
     def step(self, events=None):
-        """One pass of the call list; events: list of 4-event lists, one per call."""
+        """One pass of the call list; events: list of 6-event lists, one per call."""
         from recurrent_vision_token_amd import _lib
         for c in range(len(self.wl.calls)):
             a = self.args[self.cursor]
@@ -131,7 +131,7 @@ def time_workload(wl, torch, steps, warmup):
     log("[bench] %s: host issue %.1f us/call, wall %.1f us/call" %
         (wl.name, (t_issue - t0) * 1e6 / (steps * ncall), (t1 - t0) * 1e6 / (steps * ncall)))
 
-    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(ncall)]
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(ncall)]
            for _ in range(steps)]
     stream = torch.cuda.current_stream()
     for per_step in evs:                      # materialise the HIP events
@@ -146,9 +146,9 @@ def time_workload(wl, torch, steps, warmup):
     for per_step in evs:
         for e in per_step:
             k_ms["span_summary"].append(e[0].elapsed_time(e[1]))
-            k_ms["span_scan"].append(e[1].elapsed_time(e[2]))
-            k_ms["chunk_output"].append(e[2].elapsed_time(e[3]))
-            k_ms["call"].append(e[0].elapsed_time(e[3]))
+            k_ms["span_scan"].append(e[2].elapsed_time(e[3]))
+            k_ms["chunk_output"].append(e[4].elapsed_time(e[5]))
+            k_ms["call"].append(e[0].elapsed_time(e[5]))
     mean = {k: sum(v) / len(v) for k, v in k_ms.items()}
     return r, ms_step, mean
 
@@ -231,6 +231,54 @@ def summarize(wl, ms_step, mean):
     }
 
 
+def counters_to_traffic(fetch_dir, write_dir, copy_mb, workload):
+    """Per-launch HBM bytes from two rocprofv3 --pmc runs (FETCH_SIZE, then
+    WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads for
+    the device copy of known size that the runs include.  Writes
+    profiles/traffic_<workload>.json and prints a markdown summary."""
+    import csv
+    import statistics
+
+    def per_kernel(d, counter):
+        vals = {}
+        for row in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
+            if row["Counter_Name"] != counter:
+                continue
+            name = row["Kernel_Name"]
+            key = next((k for k in ("span_summary", "span_scan", "chunk_output") if k in name), None)
+            if key is None and "copy" in name.lower():
+                key = "copy"
+            if key is not None:
+                vals.setdefault(key, []).append(float(row["Counter_Value"]))
+        return {k: statistics.mean(v) for k, v in vals.items()}
+
+    f = per_kernel(fetch_dir, "FETCH_SIZE")
+    w = per_kernel(write_dir, "WRITE_SIZE")
+    copy_bytes = copy_mb << 20
+    f_scale = copy_bytes / (f["copy"] * 1024.0)
+    w_scale = copy_bytes / (w["copy"] * 1024.0)
+    src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    rec = {"workload": workload, "kernel_source_sha256": src_hash, "copy_bytes": copy_bytes,
+           "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
+    lines = ["| kernel | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | HBM read (MB) | HBM write (MB) | total (MB) |",
+             "|---|---|---|---|---|---|"]
+    for k in ("span_summary", "span_scan", "chunk_output"):
+        if k not in f:
+            continue
+        rd = f[k] * 1024.0 * f_scale
+        wr = w[k] * 1024.0 * w_scale
+        rec["kernels"][k] = {"fetch_kib": f[k], "write_kib": w[k], "hbm_read_bytes": rd,
+                             "hbm_write_bytes": wr, "hbm_bytes_per_launch": rd + wr}
+        lines.append("| %s | %.0f | %.0f | %.1f | %.1f | %.1f |" % (k, f[k], w[k], rd / 1e6, wr / 1e6,
+                                                                  (rd + wr) / 1e6))
+    out = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+    json.dump(rec, open(out, "w"), indent=1)
+    print("copy kernel of %d bytes: FETCH_SIZE %.0f KiB (scale %.3f), WRITE_SIZE %.0f KiB (scale %.3f)"
+          % (copy_bytes, f["copy"], f_scale, w["copy"], w_scale))
+    print("\n".join(lines))
+    print("wrote", out)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -242,8 +290,14 @@ def main():
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run one device-to-device copy of this many MB (a kernel of "
                          "known traffic, to scale hardware byte counters against)")
+    ap.add_argument("--counters-to-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc output folders into profiles/traffic_*.json")
     args = ap.parse_args()
 
+    if args.counters_to_traffic:
+        counters_to_traffic(args.counters_to_traffic[0], args.counters_to_traffic[1],
+                            args.copy_calibration_mb or 256, args.workload)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(sequences shard across GPUs with no communication; see the design notes). "

@@ -105,14 +105,14 @@ int gla_plan_spans(int use_f32, int B, int heads, int H, int W, int d_k, int d_v
 
 /*
  * Measurement hook (for benchmarks and profilers, not needed for computing).
- * events: n = 4 hipEvent_t handles (as void*), or n = 0 to clear.  The next
- * forward call made by the calling thread records events[0] before its first
- * kernel, events[1] after the span-summary kernel, events[2] after the
- * span-scan kernel (when a sequence is not split into spans, events[0..2] are
- * recorded back to back) and events[3] after the output kernel, all on that
- * call's stream; the hook then clears itself.  The caller owns the events.
- * Returns GLA_ERR_NULL if n = 4 and a handle is NULL, GLA_ERR_SHAPE if n is
- * neither 0 nor 4.
+ * events: n = 6 hipEvent_t handles (as void*), or n = 0 to clear.  The next
+ * forward call made by the calling thread has each of its three kernels (span
+ * summary, span scan, output) record a start / stop pair, events[2i] and
+ * events[2i+1], from its own dispatch (hipExtLaunchKernelGGL), so the interval
+ * is that kernel's execution; a kernel the call does not run (no span split)
+ * records its pair back to back.  The hook then clears itself.  The caller
+ * owns the events.  Returns GLA_ERR_NULL if n = 6 and a handle is NULL,
+ * GLA_ERR_SHAPE if n is neither 0 nor 6.
  */
 int gla_set_kernel_events(void* const* events, int n);
 

@@ -109,7 +109,7 @@ def gla_chunk_fwd(q, k, v, log_alpha, scan_dir, chunk=64, out=None, final_state=
 
 
 def set_kernel_events(handles):
-    """Arm the measurement hook with four hipEvent_t handles (ints), or clear it."""
+    """Arm the measurement hook with six hipEvent_t handles (ints), or clear it."""
     lib = load()
     if not handles:
         return lib.gla_set_kernel_events(None, 0)

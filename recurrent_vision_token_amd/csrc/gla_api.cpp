@@ -23,7 +23,7 @@ struct Range {
 bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 
 // Events of the measurement hook, per calling thread (see gla_set_kernel_events).
-thread_local hipEvent_t t_events[4];
+thread_local hipEvent_t t_events[6];
 thread_local bool t_events_set = false;
 
 // Output-kernel workgroup slots per device (CUs x resident workgroups per CU),
@@ -224,11 +224,11 @@ int gla_set_kernel_events(void* const* events, int n) {
     t_events_set = false;
     return GLA_OK;
   }
-  if (n != 4) return GLA_ERR_SHAPE;
+  if (n != 6) return GLA_ERR_SHAPE;
   if (events == nullptr) return GLA_ERR_NULL;
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 6; ++i)
     if (events[i] == nullptr) return GLA_ERR_NULL;
-  for (int i = 0; i < 4; ++i) t_events[i] = static_cast<hipEvent_t>(events[i]);
+  for (int i = 0; i < 6; ++i) t_events[i] = static_cast<hipEvent_t>(events[i]);
   t_events_set = true;
   return GLA_OK;
 }

@@ -32,6 +32,7 @@
 // The scan direction is an index remap applied to every 16-byte row load and
 // store (cell = pi(t)); no transposed copy of any tensor is made.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <type_traits>
@@ -1373,10 +1374,6 @@ __global__ __launch_bounds__(kThreads) void span_summary_f16_kernel(FwdParams p)
   }
 }
 
-hipError_t mark(hipEvent_t const* events, int i, hipStream_t stream) {
-  return events ? hipEventRecord(events[i], stream) : hipSuccess;
-}
-
 // Kernel choice per element type: float16 runs the MFMA-layout kernels,
 // float32 the generic ones.
 template <class T, int DK, int DV>
@@ -1390,27 +1387,58 @@ struct Family<f16, DK, DV> {
   static constexpr auto output = chunk_output_f16_kernel<DK, DV>;
 };
 
-template <class T, int DK, int DV>
-hipError_t launch_variant(const FwdParams& p, hipStream_t stream, hipEvent_t const* events) {
-  const int BH = p.B * p.heads;
-  hipError_t e = mark(events, 0, stream);
+// Launch one kernel; with measurement events, the dispatch itself records
+// start / stop (hipExtLaunchKernelGGL), so the interval is the kernel's own.
+template <class K>
+hipError_t launch_one(K kernel, dim3 grid, hipStream_t stream, const FwdParams& p,
+                      hipEvent_t const* ev, int slot) {
+  if (ev != nullptr) {
+    hipExtLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, ev[2 * slot], ev[2 * slot + 1], 0,
+                          p);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+// A kernel that is not launched still gets its event pair (zero length).
+hipError_t skip_one(hipStream_t stream, hipEvent_t const* ev, int slot) {
+  if (ev == nullptr) return hipSuccess;
+  hipError_t e = hipEventRecord(ev[2 * slot], stream);
   if (e != hipSuccess) return e;
+  return hipEventRecord(ev[2 * slot + 1], stream);
+}
+
+template <class T, int DK, int DV>
+hipError_t launch_variant(const FwdParams& p, hipStream_t stream, hipEvent_t const* ev) {
+  const int BH = p.B * p.heads;
+  hipError_t e;
   if (p.n_spans > 1) {
-    hipLaunchKernelGGL((Family<T, DK, DV>::summary), dim3(BH * p.n_spans), dim3(kThreads), 0,
-                       stream, p);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_one(Family<T, DK, DV>::summary, dim3(BH * p.n_spans), stream, p, ev, 0)) !=
+        hipSuccess)
+      return e;
+    if ((e = launch_one(span_scan_kernel<DK, DV>, dim3(BH, DK * DV / kScanElems), stream, p, ev,
+                        1)) != hipSuccess)
+      return e;
+  } else {
+    if ((e = skip_one(stream, ev, 0)) != hipSuccess) return e;
+    if ((e = skip_one(stream, ev, 1)) != hipSuccess) return e;
   }
-  if ((e = mark(events, 1, stream)) != hipSuccess) return e;
-  if (p.n_spans > 1) {
-    hipLaunchKernelGGL((span_scan_kernel<DK, DV>), dim3(BH, DK * DV / kScanElems), dim3(kThreads),
-                       0, stream, p);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+  return launch_one(Family<T, DK, DV>::output, dim3(BH * p.n_spans), stream, p, ev, 2);
+}
+
+hipError_t launch_forward_impl(Dtype dt, int d_k, int d_v, const FwdParams& p, hipStream_t stream,
+                               hipEvent_t const* ev) {
+  if (dt == Dtype::kF16) {
+    if (d_k == 64 && d_v == 64) return launch_variant<f16, 64, 64>(p, stream, ev);
+    if (d_k == 64 && d_v == 128) return launch_variant<f16, 64, 128>(p, stream, ev);
+    if (d_k == 128 && d_v == 64) return launch_variant<f16, 128, 64>(p, stream, ev);
+    if (d_k == 128 && d_v == 128) return launch_variant<f16, 128, 128>(p, stream, ev);
+  } else {
+    if (d_k == 64 && d_v == 64) return launch_variant<float, 64, 64>(p, stream, ev);
+    if (d_k == 64 && d_v == 128) return launch_variant<float, 64, 128>(p, stream, ev);
   }
-  if ((e = mark(events, 2, stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL((Family<T, DK, DV>::output), dim3(BH * p.n_spans), dim3(kThreads), 0, stream,
-                     p);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  return mark(events, 3, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -1446,16 +1474,7 @@ bool has_variant(Dtype dt, int d_k, int d_v) {
 
 hipError_t launch_forward(Dtype dt, int d_k, int d_v, const FwdParams& p, hipStream_t stream,
                           hipEvent_t const* ev) {
-  if (dt == Dtype::kF16) {
-    if (d_k == 64 && d_v == 64) return launch_variant<f16, 64, 64>(p, stream, ev);
-    if (d_k == 64 && d_v == 128) return launch_variant<f16, 64, 128>(p, stream, ev);
-    if (d_k == 128 && d_v == 64) return launch_variant<f16, 128, 64>(p, stream, ev);
-    if (d_k == 128 && d_v == 128) return launch_variant<f16, 128, 128>(p, stream, ev);
-  } else {
-    if (d_k == 64 && d_v == 64) return launch_variant<float, 64, 64>(p, stream, ev);
-    if (d_k == 64 && d_v == 128) return launch_variant<float, 64, 128>(p, stream, ev);
-  }
-  return hipErrorInvalidValue;
+  return launch_forward_impl(dt, d_k, d_v, p, stream, ev);
 }
 
 }  // namespace gla

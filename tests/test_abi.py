@@ -74,9 +74,9 @@ def test_fp32_entry_rejects_unbuilt_key_dim():
 def test_kernel_event_hook_validation():
     lib = _lib.load()
     assert _lib.set_kernel_events([]) == 0
-    assert _lib.set_kernel_events([1, 2, 3]) == -2
-    assert _lib.set_kernel_events([1, 2, None, 4]) == -1
-    assert lib.gla_set_kernel_events(None, 4) == -1
+    assert _lib.set_kernel_events([1, 2, 3, 4]) == -2
+    assert _lib.set_kernel_events([1, 2, None, 4, 5, 6]) == -1
+    assert lib.gla_set_kernel_events(None, 6) == -1
     assert _lib.set_kernel_events([]) == 0
 
 
