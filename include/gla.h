@@ -22,6 +22,8 @@
  * Layout (all tensors dense, row-major, contiguous, 16-byte aligned):
  *   q, k, log_alpha : [B][heads][H][W][d_k]
  *   v, out          : [B][heads][H][W][d_v]      (out in grid order)
+ *   One sequence's rows of one tensor, H*W*max(d_k, d_v) elements, must span
+ *   less than 2 GiB (they are addressed with 32-bit byte offsets).
  *   final_state     : [B][heads][d_k][d_v] float32, the state after the last
  *                     scan step; may be NULL.
  *
@@ -61,7 +63,8 @@ enum {
 enum {
   GLA_OK = 0,
   GLA_ERR_NULL = -1,          /* a required pointer is NULL                     */
-  GLA_ERR_SHAPE = -2,         /* B, heads, H or W < 1, or a size overflows      */
+  GLA_ERR_SHAPE = -2,         /* B, heads, H or W < 1, a size overflows, or one
+                                 sequence's rows of a tensor reach 2 GiB          */
   GLA_ERR_UNSUPPORTED = -3,   /* d_k / d_v / chunk combination not built        */
   GLA_ERR_ALIGN = -4,         /* a tensor pointer is not 16-byte aligned        */
   GLA_ERR_SCAN_DIR = -5,      /* scan_dir outside 0..4                          */

@@ -88,6 +88,8 @@ int forward(gla::Dtype dt, size_t esize, const void* q, const void* k, const voi
   if (T > (1LL << 30) || BH > (1LL << 30)) return GLA_ERR_SHAPE;
   const long long dmax = d_k > d_v ? d_k : d_v;
   if (BH * T > (1LL << 62) / (dmax * 8)) return GLA_ERR_SHAPE;
+  // one sequence's rows of one tensor are addressed with 32-bit byte offsets
+  if (T * dmax * (long long)esize >= (1LL << 31)) return GLA_ERR_SHAPE;
   if (chunk != kChunk || !gla::has_variant(dt, d_k, d_v)) return GLA_ERR_UNSUPPORTED;
   const void* tens[5] = {q, k, v, la, out};
   for (const void* t : tens)

@@ -120,6 +120,47 @@ __device__ __forceinline__ uint4 sel(bool c, uint4 a, uint4 b) {
   return make_uint4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
 }
 
+// Row access of the float16 kernels goes through buffer resources, one per
+// tensor and sequence: offsets are 32-bit byte offsets inside the sequence's
+// rows, and an offset at or past their end (kNoRow) reads zeros and drops
+// stores.  Rows past the span or the sequence thus need no branch and no
+// select, every load is issued unconditionally, and each wait for a staged
+// tile counts exactly the loads issued after it.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+constexpr uint32_t kNoRow = 0x80000000u;     // beyond every sequence (its rows span < 2 GiB)
+constexpr int kRawBufferWord3 = 0x00020000;  // untyped buffer, 32-bit elements (gfx9 family)
+
+__device__ __forceinline__ rsrc_t seq_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRawBufferWord3);
+}
+__device__ __forceinline__ uint4 bload(rsrc_t r, uint32_t off) {
+  const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(x[0], x[1], x[2], x[3]);
+}
+__device__ __forceinline__ void bstore(rsrc_t r, uint32_t off, uint4 d) {
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4{d.x, d.y, d.z, d.w}, r, off, 0, 0);
+}
+
+// The rows of one (batch, head) sequence: q, k, log-alpha [T][d_k], v, out [T][d_v].
+struct SeqBufs {
+  rsrc_t q, k, la, v, out;
+};
+template <int DK, int DV>
+__device__ __forceinline__ SeqBufs seq_bufs(const FwdParams& p, int bh) {
+  typedef _Float16 h;
+  const uint32_t kb = (uint32_t)p.T * DK * 2, vb = (uint32_t)p.T * DV * 2;
+  const size_t ok = (size_t)bh * p.T * DK, ov = (size_t)bh * p.T * DV;
+  SeqBufs s;
+  s.q = seq_rsrc(static_cast<const h*>(p.q) + ok, kb);
+  s.k = seq_rsrc(static_cast<const h*>(p.k) + ok, kb);
+  s.la = seq_rsrc(static_cast<const h*>(p.la) + ok, kb);
+  s.v = seq_rsrc(static_cast<const h*>(p.v) + ov, vb);
+  s.out = seq_rsrc(static_cast<h*>(p.out) + ov, vb);
+  return s;
+}
+
 __device__ __forceinline__ f32x4 mma32(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
@@ -731,19 +772,20 @@ __global__ __launch_bounds__(kThreads) void chunk_output_kernel(FwdParams p) {
 }
 
 // ===========================================================================
-// Float16 kernels.  The per-chunk elementwise work (cumulative decay, anchored
-// q / k scalings, decayed keys) runs in MFMA-friendly register layouts so that
-// every LDS access is a 64- or 128-bit vector op:
-//  * log-alpha is staged transposed ([d_k][token]); cumulative sums over tokens
-//    are 16x16x16 MFMAs against constant triangular matrices (log2(e) folded
-//    in as an exact hi + lo pair), landing either as "4 key dims of one token
-//    per lane" (output kernel) or "4 tokens of one key dim per lane" (summary);
+// Float16 kernels.  Chunk data moves from memory into LDS with buffer loads
+// that write LDS directly (no registers, no staging code), row-major with a
+// bank-spreading swizzle, and the operands that reduce over tokens are read
+// back transposed (ds_read_b64_tr_b16).  The per-chunk elementwise work
+// (cumulative decay, anchored q / k scalings, decayed keys) runs in MFMA
+// register layouts:
+//  * cumulative sums over tokens are 16x16x16 MFMAs against constant
+//    triangular matrices, landing as "4 key dims of one token per lane"
+//    (output kernel, log2(e) folded in as an exact hi + lo pair) or "4 tokens
+//    of one key dim per lane" (summary);
 //  * the decay over each 16-token sub-block is broadcast along each 16-lane
 //    row with DPP, so the per-(dim, sub-block) factors need no exp and no LDS;
 //  * keys are pre-scaled into the variants the causal score tiles need, so the
-//    score MFMAs read unscaled operands;
-//  * the decayed keys for the state update are transposed with an identity
-//    MFMA (exact: one non-zero product per output).
+//    score MFMAs read unscaled operands.
 
 __device__ __forceinline__ float row_bcast15(float x) {
   // every lane of a 16-lane row receives the row's lane 15 value
@@ -758,121 +800,8 @@ constexpr float kLog2eHi = 1.4423828125f;          // fp16(log2 e)
 constexpr float kLog2eLo = 1.4426950408889634f - 1.4423828125f;
 
 
-// Row pieces of q and k, token-pair pieces of log-alpha and v (for the
-// transposed tiles).  Pieces past the sequence end read as zero.
-template <int DK, int DV, bool WITH_Q, bool K_ROWS>
-struct LoaderH {
-  static constexpr int PK = DK / 8, PV = DV / 8;   // 16-byte pieces per token row
-  static constexpr int NK = kChunk * PK / kThreads;          // row pieces per thread
-  static constexpr int NKP = (kChunk / 2) * PK / kThreads;   // d_k token pairs per thread
-  static constexpr int NVP = (kChunk / 2) * PV / kThreads;   // d_v token pairs per thread
-  static_assert(NK >= 1 && NKP >= 1 && NVP >= 1, "tile too small");
-  uint4 rq[WITH_Q ? NK : 1];
-  uint4 rk[K_ROWS ? NK : 2 * NKP];
-  uint4 rl[2 * NKP];
-  uint4 rv[2 * NVP];
-  // validity of each piece (bit j: row piece j, bit 16+i: pair piece i, bit
-  // 24+i: v pair piece i); invalid pieces are zeroed when staged
-  uint32_t okm;
-
-  __device__ __forceinline__ static uint4 ld(const f16* p) {
-    return *reinterpret_cast<const uint4*>(p);
-  }
-
-  __device__ __forceinline__ void load(const f16* q, const f16* k, const f16* la, const f16* v,
-                                       size_t off_k, size_t off_v, int t0, int valid, const GridMap& gm) {
-    const int tid = threadIdx.x;
-    okm = 0;
-    if (WITH_Q || K_ROWS) {
-#pragma unroll
-      for (int j = 0; j < NK; ++j) {
-        const int id = tid + kThreads * j;
-        const int tok = id / PK, pc = id - tok * PK;
-        const bool in = tok < valid;
-        // out-of-range lanes read the sequence's first row and drop it when
-        // staging: no branches around the loads, so waits can count them
-        const size_t o = off_k + (size_t)gm.cell(in ? t0 + tok : 0) * DK + pc * 8;
-        if (WITH_Q) rq[j] = ld(q + o);
-        if (K_ROWS) rk[j] = ld(k + o);
-        okm |= (in ? 1u : 0u) << j;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < NKP; ++j) {
-      const int id = tid + kThreads * j;
-      const int tp = id / PK, pc = id - tp * PK;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int tok = 2 * tp + h;
-        const bool in = tok < valid;
-        const size_t o = off_k + (size_t)gm.cell(in ? t0 + tok : 0) * DK + pc * 8;
-        rl[2 * j + h] = ld(la + o);
-        if (!K_ROWS) rk[2 * j + h] = ld(k + o);
-        okm |= (in ? 1u : 0u) << (16 + 2 * j + h);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < NVP; ++j) {
-      const int id = tid + kThreads * j;
-      const int tp = id / PV, pc = id - tp * PV;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int tok = 2 * tp + h;
-        const bool in = tok < valid;
-        rv[2 * j + h] = ld(v + off_v + (size_t)gm.cell(in ? t0 + tok : 0) * DV + pc * 8);
-        okm |= (in ? 1u : 0u) << (24 + 2 * j + h);
-      }
-    }
-  }
-
-  // Write a token pair (a, b) of 8-element pieces transposed: dst[(8pc+u)*AS + 2tp].
-  __device__ __forceinline__ static void put_pair_t(f16* dst, int AS, int pc, int tp, uint4 a,
-                                                    uint4 b) {
-    const f16x8 x = __builtin_bit_cast(f16x8, a);
-    const f16x8 y = __builtin_bit_cast(f16x8, b);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      f16x2 pr;
-      pr[0] = x[u];
-      pr[1] = y[u];
-      *reinterpret_cast<f16x2*>(dst + (9 * pc + u) * AS + 2 * tp) = pr;  // row trow(8pc+u)
-    }
-  }
-
-  __device__ __forceinline__ void store(f16* sq, f16* sk, int QS, f16* skt, f16* slat, f16* svt,
-                                        int AS) const {
-    const int tid = threadIdx.x;
-    const uint4 z = make_uint4(0, 0, 0, 0);
-    auto ok = [&](int bit) { return ((okm >> bit) & 1u) != 0; };
-    if (WITH_Q || K_ROWS) {
-#pragma unroll
-      for (int j = 0; j < NK; ++j) {
-        const int id = tid + kThreads * j;
-        const int tok = id / PK, pc = id - tok * PK;
-        if (WITH_Q) *reinterpret_cast<uint4*>(sq + tok * QS + pc * 8) = sel(ok(j), rq[j], z);
-        if (K_ROWS) *reinterpret_cast<uint4*>(sk + tok * QS + pc * 8) = sel(ok(j), rk[j], z);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < NKP; ++j) {
-      const int id = tid + kThreads * j;
-      const int tp = id / PK, pc = id - tp * PK;
-      const bool a = ok(16 + 2 * j), b = ok(17 + 2 * j);
-      put_pair_t(slat, AS, pc, tp, sel(a, rl[2 * j], z), sel(b, rl[2 * j + 1], z));
-      if (!K_ROWS) put_pair_t(skt, AS, pc, tp, sel(a, rk[2 * j], z), sel(b, rk[2 * j + 1], z));
-    }
-#pragma unroll
-    for (int j = 0; j < NVP; ++j) {
-      const int id = tid + kThreads * j;
-      const int tp = id / PV, pc = id - tp * PV;
-      put_pair_t(svt, AS, pc, tp, sel(ok(24 + 2 * j), rv[2 * j], z),
-                 sel(ok(25 + 2 * j), rv[2 * j + 1], z));
-    }
-  }
-};
-
-// Constant 16x16x16 MFMA B operands, lane (n, g) holding rows 4g..4g+3 of column n:
-// U[s][t] = (s <= t) * v, and the identity.
+// Constant 16x16x16 MFMA B operand, lane (n, g) holding rows 4g..4g+3 of
+// column n: U[s][t] = (s <= t) * v.
 __device__ __forceinline__ f16x4 upper_incl(float v) {
   const int lane = threadIdx.x & 63, n16 = lane & 15, g = lane >> 4;
   f16x4 r;
@@ -880,164 +809,151 @@ __device__ __forceinline__ f16x4 upper_incl(float v) {
   for (int u = 0; u < 4; ++u) r[u] = (f16)((4 * g + u <= n16) ? v : 0.f);
   return r;
 }
-__device__ __forceinline__ f16x4 identity16() {
-  const int lane = threadIdx.x & 63, n16 = lane & 15, g = lane >> 4;
-  f16x4 r;
-#pragma unroll
-  for (int u = 0; u < 4; ++u) r[u] = (f16)((4 * g + u == n16) ? 1.f : 0.f);
-  return r;
+
+// ---------------------------------------------------------------------------
+// Row-major chunk tiles in LDS, filled straight from memory by buffer loads
+// that write LDS: one wave instruction moves 1 KB, lane l's 16 bytes landing at
+// byte 16 l of the block, and a lane whose offset is out of range writes zeros.
+// A tile row holds one token's d values (RB = 2d bytes); its 16-byte piece p is
+// stored at piece p ^ (row & 7), which spreads row reads and the transposed
+// reads below evenly over the LDS banks.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __fp16 lds_h4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8): at most n vector-memory operations outstanding, or no LDS
+// operation outstanding.
+__host__ __device__ constexpr int vmcnt_imm(int n) {
+  return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14);
+}
+constexpr int kLgkmZero = 15 | (7 << 4) | (0 << 8) | (3 << 14);
+
+// Waits and barriers are explicit around the LDS-writing loads: the fence in
+// __syncthreads would wait for every such load in flight, including the ones
+// filling the other buffer.  The empty asm statements keep the compiler from
+// moving memory accesses across the wait and the barrier.
+template <int WAITCNT>
+__device__ __forceinline__ void wait_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(WAITCNT);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Source offset of this lane's 16 bytes in block `blk` (1 KB) of a tile with
+// RB-byte rows; rows of chunk-local tokens at or past `valid` get an offset
+// past the buffer, so they read as zero.  Branch-free on purpose: a lane-
+// dependent branch here would split one LDS-writing load into two partial
+// ones and upset the explicit wait counts.
+template <int RB>
+__device__ __forceinline__ uint32_t dma_offset(int blk, int t0, int valid, const GridMap& gm) {
+  const int lane = threadIdx.x & 63;
+  const int byte = blk * 1024 + 16 * lane;
+  const int r = byte / RB, pp = (byte % RB) / 16;
+  const uint32_t off = (uint32_t)gm.cell(t0 + r) * RB + (uint32_t)((pp ^ (r & 7)) * 16);
+  return off | ((uint32_t)(r >= valid) << 31);
+}
+__device__ __forceinline__ void dma16(rsrc_t src, f16* block, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void_t*)block, 16, off, 0, 0, 0);
+}
+
+// Transposed read of the 16 x 16 block at (row0, col0) of a swizzled tile
+// (ds_read_b64_tr_b16): lane (i, g) = (lane % 16, lane / 16) receives rows
+// row0 + 4g .. row0 + 4g + 3 of column col0 + i, i.e. the MFMA operand that
+// reduces over rows.  Lane j of each 16-lane group addresses row 4g + j / 4,
+// columns 4 (j % 4) .. + 3 of the block.
+template <int RB>
+__device__ __forceinline__ f16x4 tr_read(const f16* tile, int row0, int col0) {
+  const int lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
+  const int row = row0 + 4 * g + (j >> 2);
+  const int col = col0 + 4 * (j & 3);
+  const f16* a = tile + row * (RB / 2) + (((col >> 3) ^ (row & 7)) << 3) + (col & 4);
+  const lds_h4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4f16((__attribute__((address_space(3))) lds_h4_t*)(lds_void_t*)a);
+  return __builtin_bit_cast(f16x4, x);
+}
+
+__device__ __forceinline__ f16x8 cat8(f16x4 a, f16x4 b) {
+  return f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
 // ---------------------------------------------------------------------------
 // Output kernel, float16.  The span is walked in 32-token steps (two 16-token
-// sub-blocks), which keeps the shared tiles near 37 KB so four workgroups (four
-// waves per SIMD) share a CU.  Per step:
-//   stage  : q, k row-major; log-alpha and v transposed (token pairs)
-//   P      : wave w owns key dims 16w.. : in-sub-block cumulative decay c by
-//            MFMA, exp(+-c), DPP broadcast of the sub-block decays, anchored
-//            q / k, q decayed from the step start, keys decayed to the end of
-//            sub-block 0 and to the step end (transposed by an identity MFMA)
-//   A      : score tiles (0,0), (1,0), (1,1); tile (0,1) is zeroed
-//   O      : wave w owns value columns 16w.. : O^T = V^T A^T + S^T Qt^T, then
-//            S <- diag(exp(b_end)) S + KL^T V
-//   W      : output rows to their grid cells
+// sub-blocks).  q, k, log-alpha and v of a step land row-major in LDS straight
+// from memory (LDS-writing loads, two step buffers, the next step loading
+// while this one is computed).  Per step:
+//   P : wave w owns key dims 16w.. : cumulative decay c inside each sub-block
+//       by MFMA (log-alpha read transposed), exp(+-c), DPP broadcast of the
+//       sub-block decays; writes, in place of q, k, log-alpha, the anchored
+//       q*exp(c), k*exp(-c) and the keys decayed to the step end, plus q
+//       decayed from the step start and the sub-block 0 keys decayed to its
+//       end; packed float16 products
+//   O : wave w owns value columns 16w.. : the three causal score tiles in
+//       transposed orientation (A^T, computed by every wave: cheaper than a
+//       barrier), O^T = V^T A^T + S^T Qt^T with the score tiles used straight
+//       from the accumulators, outputs stored from registers to their grid
+//       cells, then S <- diag(exp(b_end)) S + KL^T V.
+// The x32 MFMAs that reduce over tokens use one token-slot order for both
+// operands: slots 8g..8g+3 hold tokens 4g..4g+3 of sub-block 0 and slots
+// 8g+4..8g+7 the same tokens of sub-block 1, which is what two transposed
+// 16x16 reads (or two 16x16 accumulator tiles) deliver.
 constexpr int kStep = 32;
 
-__host__ __device__ constexpr int trow_h(int d) { return d + (d >> 3); }
+// element offset of (row, col) in a swizzled tile with RB-byte rows (col % 4 == 0)
+template <int RB>
+__device__ __forceinline__ int swz(int row, int col) {
+  return row * (RB / 2) + (((col >> 3) ^ (row & 7)) << 3) + (col & 7);
+}
+__device__ __forceinline__ f16x4 ld64(const f16* a) { return *reinterpret_cast<const f16x4*>(a); }
+__device__ __forceinline__ f16x8 ld128(const f16* a) { return *reinterpret_cast<const f16x8*>(a); }
+__device__ __forceinline__ void st64(f16* a, f16x4 x) { *reinterpret_cast<f16x4*>(a) = x; }
+__device__ __forceinline__ f16x4 to_f16(f32x4 x) { return __builtin_convertvector(x, f16x4); }
 
 template <int DK, int DV>
-struct StepSmem {
-  static constexpr int QS = DK + 8;      // [token][d_k] rows
-  static constexpr int AS = kStep + 8;   // [*][token] rows
-  static constexpr int OS = DV + 8;      // [token][d_v] rows
-  static constexpr int LAT_ELEMS =
-      (trow_h(DK) * AS > kStep * AS) ? trow_h(DK) * AS : kStep * AS;
-  alignas(16) f16 q[kStep * QS];     // raw q, then q_t*exp(c_t)  (c: decay inside the sub-block)
-  alignas(16) f16 qt[kStep * QS];    // q_t*exp(b_t)              (b: decay from the step start)
-  alignas(16) f16 k[kStep * QS];     // raw k, then k_s*exp(-c_s)
-  alignas(16) f16 kv[kSub * QS];     // sub-block 0 keys decayed to the end of sub-block 0
-  alignas(16) f16 lat[LAT_ELEMS];    // log-alpha^T [trow(d_k)][token], then A[t][s]
-  alignas(16) f16 vt[trow_h(DV) * AS];
-  alignas(16) f16 klt[DK * AS];      // keys decayed to the step end, [d_k][token]
-  alignas(16) f16 o[kStep * OS];     // output staging
-  alignas(16) float g[DK];           // exp(decay over the step)
+struct StepTiles {
+  f16* q;
+  f16* k;
+  f16* la;
+  f16* v;
 };
 
-// One 32-token step of q, k (row pieces) and log-alpha, v (token-pair pieces).
-template <int DK, int DV>
-struct StepLoader {
-  static constexpr int PK = DK / 8, PV = DV / 8;
-  static constexpr int NQ = kStep * PK / kThreads;                 // q / k row pieces per thread
-  static constexpr int NPAIR = (kStep / 2) * (PK + PV);            // la + v pair items
-  static constexpr int NP = (NPAIR + kThreads - 1) / kThreads;     // pair items per thread
-  static_assert(NQ >= 1 && (kStep / 2) * PK % 64 == 0 && NPAIR % 64 == 0, "tile shape");
-  uint4 rq[NQ], rk[NQ], rp[2 * NP];
-  uint32_t okm;  // bit j: row piece j valid; bit 8+i: pair piece i valid
-
-  __device__ __forceinline__ static uint4 ld(const f16* p) {
-    return *reinterpret_cast<const uint4*>(p);
-  }
-
-  __device__ __forceinline__ void load(const f16* q, const f16* k, const f16* la, const f16* v,
-                                       size_t off_k, size_t off_v, int t0, int valid,
-                                       const GridMap& gm) {
-    const int tid = threadIdx.x;
-    okm = 0;
-#pragma unroll
-    for (int j = 0; j < NQ; ++j) {
-      const int id = tid + kThreads * j;
-      const int tok = id / PK, pc = id - tok * PK;
-      const bool in = tok < valid;
-      const size_t o = off_k + (size_t)gm.cell(in ? t0 + tok : 0) * DK + pc * 8;
-      rq[j] = ld(q + o);
-      rk[j] = ld(k + o);
-      okm |= (in ? 1u : 0u) << j;
-    }
-#pragma unroll
-    for (int j = 0; j < NP; ++j) {
-      const int id = tid + kThreads * j;
-      if (id < NPAIR) {
-        const bool is_la = id < (kStep / 2) * PK;
-        const int rel = is_la ? id : id - (kStep / 2) * PK;
-        const int pp = is_la ? PK : PV;
-        const int tp = rel / pp, pc = rel - tp * pp;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int tok = 2 * tp + h;
-          const bool in = tok < valid;
-          const size_t cell = (size_t)gm.cell(in ? t0 + tok : 0);
-          const f16* src = is_la ? la + off_k + cell * DK + pc * 8 : v + off_v + cell * DV + pc * 8;
-          rp[2 * j + h] = ld(src);
-          okm |= (in ? 1u : 0u) << (8 + 2 * j + h);
-        }
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store(StepSmem<DK, DV>& sm) const {
-    constexpr int QS = StepSmem<DK, DV>::QS, AS = StepSmem<DK, DV>::AS;
-    const int tid = threadIdx.x;
-    const uint4 z = make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int j = 0; j < NQ; ++j) {
-      const int id = tid + kThreads * j;
-      const int tok = id / PK, pc = id - tok * PK;
-      const bool in = ((okm >> j) & 1u) != 0;
-      *reinterpret_cast<uint4*>(sm.q + tok * QS + pc * 8) = sel(in, rq[j], z);
-      *reinterpret_cast<uint4*>(sm.k + tok * QS + pc * 8) = sel(in, rk[j], z);
-    }
-#pragma unroll
-    for (int j = 0; j < NP; ++j) {
-      const int id = tid + kThreads * j;
-      if (id < NPAIR) {
-        const bool is_la = id < (kStep / 2) * PK;
-        const int rel = is_la ? id : id - (kStep / 2) * PK;
-        const int pp = is_la ? PK : PV;
-        const int tp = rel / pp, pc = rel - tp * pp;
-        f16* dst = is_la ? sm.lat : sm.vt;
-        const f16x8 x = __builtin_bit_cast(f16x8, sel(((okm >> (8 + 2 * j)) & 1u) != 0, rp[2 * j], z));
-        const f16x8 y =
-            __builtin_bit_cast(f16x8, sel(((okm >> (9 + 2 * j)) & 1u) != 0, rp[2 * j + 1], z));
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          f16x2 pr;
-          pr[0] = x[u];
-          pr[1] = y[u];
-          *reinterpret_cast<f16x2*>(dst + (9 * pc + u) * AS + 2 * tp) = pr;  // row trow(8pc+u)
-        }
-      }
-    }
-  }
-};
+// s_waitcnt immediate: at most n vector-memory operations and no LDS
+// operation outstanding.
+__host__ __device__ constexpr int vmcnt_lgkm0_imm(int n) {
+  return (n & 15) | (7 << 4) | ((n >> 4) << 14);
+}
 
 template <int DK, int DV>
 __global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 4 : (DK == 128 && DV == 128) ? 1 : 2) void chunk_output_f16_kernel(
     FwdParams p) {
-  using SM = StepSmem<DK, DV>;
-  __shared__ SM sm;
-  constexpr int QS = SM::QS, AS = SM::AS, OS = SM::OS;
-  constexpr int NR = DK / 16, NC = DV / 64;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  constexpr int RBK = 2 * DK, RBV = 2 * DV;
+  constexpr int NR = DK / 16, NC = DV / 64, NRHO = DK / 32;
+  constexpr int NBK = RBK / 128, NBV = RBV / 128;  // 1 KB blocks per wave and tile of one step
+  constexpr int NSTORE = 2 * NC;                    // output stores per wave and step
+  static_assert(NSTORE < 64, "vmcnt range");
+  // separate LDS objects per buffer, so the compiler's own waits for the
+  // LDS-writing loads can tell them apart
+  __shared__ __attribute__((aligned(16))) f16 q0[kStep * DK], k0[kStep * DK], la0[kStep * DK], v0[kStep * DV];
+  __shared__ __attribute__((aligned(16))) f16 q1[kStep * DK], k1[kStep * DK], la1[kStep * DK], v1[kStep * DV];
+  __shared__ __attribute__((aligned(16))) f16 sqt[kStep * DK];  // q decayed from the step start
+  __shared__ __attribute__((aligned(16))) f16 skv[kSub * DK];   // sub-block 0 keys decayed to its end
+  __shared__ __attribute__((aligned(16))) float sgd[DK];        // exp(decay over the step)
+  const StepTiles<DK, DV> slot0{q0, k0, la0, v0}, slot1{q1, k1, la1, v1};
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n16 = lane & 15, g = lane >> 4;
 
   const int bh = blockIdx.x / p.n_spans;
   const int span = blockIdx.x - bh * p.n_spans;
   const int b = bh / p.heads;
   const GridMap gm = grid_map(p, b);
-  const size_t off_k = (size_t)bh * p.T * DK;
-  const size_t off_v = (size_t)bh * p.T * DV;
+  const SeqBufs sb = seq_bufs<DK, DV>(p, bh);
   const int t_begin = span * p.span_chunks * kChunk;
   const int t_end = min(t_begin + p.span_chunks * kChunk, p.T);
-
-  const f16* q = static_cast<const f16*>(p.q);
-  const f16* k = static_cast<const f16*>(p.k);
-  const f16* la = static_cast<const f16*>(p.la);
-  const f16* v = static_cast<const f16*>(p.v);
-  f16* out = static_cast<f16*>(p.out);
+  const int n_steps = (t_end - t_begin + kStep - 1) / kStep;
 
   // State tiles: wave w owns value columns 16(w + 4j) .. ; tile (r, j) holds
-  // S[16r + 4g + u][16(w + 4j) + n] in lane (g, n).
+  // S[16r + 4g + u][16(w + 4j) + n] in lane (n, g).
   f32x4 st[NR][NC];
   {
     const float* src =
@@ -1052,19 +968,31 @@ __global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 4 : (DK == 128 &
     }
   }
 
+  auto issue = [&](const StepTiles<DK, DV>& s, int step) {
+    const int t0 = t_begin + kStep * step;
+    const int valid = max(0, min(kStep, t_end - t0));
+#pragma unroll
+    for (int i = 0; i < NBK; ++i) {
+      const int blk = wave * NBK + i;
+      const uint32_t off = dma_offset<RBK>(blk, t0, valid, gm);
+      dma16(sb.q, s.q + blk * 512, off);
+      dma16(sb.k, s.k + blk * 512, off);
+      dma16(sb.la, s.la + blk * 512, off);
+      if (RBV == RBK) dma16(sb.v, s.v + blk * 512, off);
+    }
+    if (RBV != RBK) {
+#pragma unroll
+      for (int i = 0; i < NBV; ++i) {
+        const int blk = wave * NBV + i;
+        dma16(sb.v, s.v + blk * 512, dma_offset<RBV>(blk, t0, valid, gm));
+      }
+    }
+  };
+
   const f16x4 u_hi = upper_incl(kLog2eHi), u_lo = upper_incl(kLog2eLo);
-  const f16x4 ident = identity16();
-  f16* const sa = sm.lat;  // score tile reuses the log-alpha^T region
 
-  StepLoader<DK, DV> ld;
-  ld.load(q, k, la, v, off_k, off_v, t_begin, min(kStep, t_end - t_begin), gm);
-  for (int t0 = t_begin; t0 < t_end; t0 += kStep) {
-    const int valid = min(kStep, t_end - t0);
-    ld.store(sm);
-    if (t0 + kStep < t_end) ld.load(q, k, la, v, off_k, off_v, t0 + kStep, min(kStep, t_end - t0 - kStep), gm);
-    __syncthreads();
-
-    // ---- Phase P
+  // ---- P: per-dim decays and the scaled operands of the step
+  auto phase_p = [&](const StepTiles<DK, DV>& s) {
 #pragma unroll
     for (int dbi = 0; dbi < DK / 64; ++dbi) {
       const int db = wave + 4 * dbi;
@@ -1072,296 +1000,290 @@ __global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 4 : (DK == 128 &
       f16x4 lat4[2], q4[2], k4[2];
 #pragma unroll
       for (int I = 0; I < 2; ++I) {
-        lat4[I] = *reinterpret_cast<const f16x4*>(sm.lat + trow_h(16 * db + n16) * AS + 16 * I + 4 * g);
-        q4[I] = *reinterpret_cast<const f16x4*>(sm.q + (16 * I + n16) * QS + dim0);
-        k4[I] = *reinterpret_cast<const f16x4*>(sm.k + (16 * I + n16) * QS + dim0);
+        lat4[I] = tr_read<RBK>(s.la, 16 * I, 16 * db);
+        q4[I] = ld64(s.q + swz<RBK>(16 * I + n16, dim0));
+        k4[I] = ld64(s.k + swz<RBK>(16 * I + n16, dim0));
       }
-      f32x4 c2[2];
+      // c2[I]: lane (t, g) holds log2-scaled cumulative decay of token
+      // 16I + t at key dims dim0 .. dim0 + 3
+      f32x4 c2[2], eq[2], ek[2], ed[2];
 #pragma unroll
       for (int I = 0; I < 2; ++I) {
         c2[I] = mma16(lat4[I], u_hi, f32x4{0.f, 0.f, 0.f, 0.f});
         c2[I] = mma16(lat4[I], u_lo, c2[I]);
-      }
-      f32x4 eq[2], ek[2], ed[2];
-#pragma unroll
-      for (int I = 0; I < 2; ++I)
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           eq[I][u] = exp2_fast(c2[I][u]);
           ek[I][u] = exp2_fast(-c2[I][u]);
           ed[I][u] = row_bcast15(eq[I][u]);  // exp(decay over sub-block I)
         }
-      if (n16 == 0) {
-        f32x4 gl;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) gl[u] = ed[0][u] * ed[1][u];
-        *reinterpret_cast<f32x4*>(sm.g + dim0) = gl;
       }
-      f16x4 klh[2];
+      if (n16 == 0) *reinterpret_cast<f32x4*>(sgd + dim0) = ed[0] * ed[1];
 #pragma unroll
       for (int I = 0; I < 2; ++I) {
         const int row = 16 * I + n16;
-        f16x4 ql, qt, kd, kv0;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float qf = (float)q4[I][u];
-          const float eqs = (I == 0) ? eq[I][u] : eq[I][u] * ed[0][u];
-          ql[u] = (f16)(qf * eq[I][u]);
-          qt[u] = (f16)(qf * eqs);
-          const float kf = (float)k4[I][u] * ek[I][u];
-          kd[u] = (f16)kf;
-          const float kend = kf * ed[I][u];  // decayed to the end of sub-block I
-          if (I == 0) {
-            kv0[u] = (f16)kend;
-            klh[I][u] = (f16)(kend * ed[1][u]);
-          } else {
-            klh[I][u] = (f16)kend;
-          }
+        const f16x4 ql = q4[I] * to_f16(eq[I]);
+        const f16x4 qt = (I == 0) ? ql : q4[I] * to_f16(eq[I] * ed[0]);
+        const f16x4 kd = k4[I] * to_f16(ek[I]);
+        const f16x4 kend = kd * to_f16(ed[I]);  // decayed to the end of sub-block I
+        st64(s.q + swz<RBK>(row, dim0), ql);
+        st64(sqt + swz<RBK>(row, dim0), qt);
+        st64(s.k + swz<RBK>(row, dim0), kd);
+        if (I == 0) {
+          st64(skv + swz<RBK>(n16, dim0), kend);
+          st64(s.la + swz<RBK>(row, dim0), kend * to_f16(ed[1]));
+        } else {
+          st64(s.la + swz<RBK>(row, dim0), kend);
         }
-        *reinterpret_cast<f16x4*>(sm.q + row * QS + dim0) = ql;
-        *reinterpret_cast<f16x4*>(sm.qt + row * QS + dim0) = qt;
-        *reinterpret_cast<f16x4*>(sm.k + row * QS + dim0) = kd;
-        if (I == 0) *reinterpret_cast<f16x4*>(sm.kv + n16 * QS + dim0) = kv0;
-      }
-#pragma unroll
-      for (int I = 0; I < 2; ++I) {
-        const f32x4 tr = mma16(klh[I], ident, f32x4{0.f, 0.f, 0.f, 0.f});
-        f16x4 trh;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) trh[u] = (f16)tr[u];
-        *reinterpret_cast<f16x4*>(sm.klt + (16 * db + n16) * AS + 16 * I + 4 * g) = trh;
       }
     }
-    __syncthreads();
+  };
 
-    // ---- Phase A: wave 0 -> (0,0), wave 1 -> (1,0), wave 2 -> (1,1), wave 3 zeroes (0,1).
-    if (wave < 3) {
-      const int I = (wave == 0) ? 0 : 1, J = (wave == 2) ? 1 : 0;
-      const f16* kb = (I != J) ? sm.kv : sm.k + 16 * J * QS;
-      f16x8 ta[DK / 32], tb[DK / 32];
+  // ---- O: scores, outputs, state update
+  auto phase_o = [&](const StepTiles<DK, DV>& s, int step) {
+    const int t0 = t_begin + kStep * step;
+    const int valid = max(0, min(kStep, t_end - t0));
+    // A^T tiles: lane (t, g) holds A[t][s = 4g + u] of the tile
+    f32x4 d00 = {0.f, 0.f, 0.f, 0.f}, d01 = d00, d11 = d00;
 #pragma unroll
-      for (int st2 = 0; st2 < DK / 32; ++st2) {
-        ta[st2] = *reinterpret_cast<const f16x8*>(kb + n16 * QS + 32 * st2 + 8 * g);
-        tb[st2] = *reinterpret_cast<const f16x8*>(sm.q + (16 * I + n16) * QS + 32 * st2 + 8 * g);
-      }
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int st2 = 0; st2 < DK / 32; ++st2) acc = mma32(ta[st2], tb[st2], acc);
-      if (I == J) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (4 * g + u > n16) acc[u] = 0.f;
-      }
-      f16x4 w;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) w[u] = (f16)acc[u];
-      *reinterpret_cast<f16x4*>(sa + (16 * I + n16) * AS + 16 * J + 4 * g) = w;
-    } else {
-      *reinterpret_cast<f16x4*>(sa + n16 * AS + 16 + 4 * g) =
-          f16x4{(f16)0.f, (f16)0.f, (f16)0.f, (f16)0.f};
+    for (int rho = 0; rho < NRHO; ++rho) {
+      const int col = 32 * rho + 8 * g;
+      const f16x8 kd0 = ld128(s.k + swz<RBK>(n16, col));
+      const f16x8 kd1 = ld128(s.k + swz<RBK>(16 + n16, col));
+      const f16x8 kv = ld128(skv + swz<RBK>(n16, col));
+      const f16x8 qa = ld128(s.q + swz<RBK>(n16, col));
+      const f16x8 qb = ld128(s.q + swz<RBK>(16 + n16, col));
+      d00 = mma32(kd0, qa, d00);
+      d01 = mma32(kv, qb, d01);
+      d11 = mma32(kd1, qb, d11);
     }
-    __syncthreads();
-
-    // ---- Phase O
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (4 * g + u > n16) {
+        d00[u] = 0.f;
+        d11[u] = 0.f;
+      }
+    const f16x4 z4 = {(f16)0.f, (f16)0.f, (f16)0.f, (f16)0.f};
+    f16x8 sbt[2];
+    sbt[0] = cat8(to_f16(d00), z4);
+    sbt[1] = cat8(to_f16(d01), to_f16(d11));
+    uint32_t orow[2];
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+      const int t = 16 * T + n16;
+      orow[T] = ((uint32_t)gm.cell(t0 + t) * RBV) | ((uint32_t)(t >= valid) << 31);
+    }
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
       const int col0 = 16 * (wave + 4 * j);
-      const int col = col0 + n16;
-      const f16x8 va = *reinterpret_cast<const f16x8*>(sm.vt + trow_h(col) * AS + 8 * g);
-      f16x8 sb[2], qb[2][DK / 32];
+      const f16x8 va = cat8(tr_read<RBV>(s.v, 0, col0), tr_read<RBV>(s.v, 16, col0));
+      f16x8 sh[NRHO];
 #pragma unroll
-      for (int I = 0; I < 2; ++I) {
-        const int t = 16 * I + n16;
-        sb[I] = *reinterpret_cast<const f16x8*>(sa + t * AS + 8 * g);
+      for (int rho = 0; rho < NRHO; ++rho) sh[rho] = cat8(to_f16(st[2 * rho][j]), to_f16(st[2 * rho + 1][j]));
 #pragma unroll
-        for (int rho = 0; rho < DK / 32; ++rho) {
-          const int dlo = 32 * rho + 4 * g;
-          const f16x4 qlo = *reinterpret_cast<const f16x4*>(sm.qt + t * QS + dlo);
-          const f16x4 qhi = *reinterpret_cast<const f16x4*>(sm.qt + t * QS + dlo + 16);
+      for (int T = 0; T < 2; ++T) {
+        const int row = 16 * T + n16;
+        f32x4 acc = mma32(va, sbt[T], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            qb[I][rho][u] = qlo[u];
-            qb[I][rho][4 + u] = qhi[u];
-          }
+        for (int rho = 0; rho < NRHO; ++rho) {
+          const f16x8 qtb = cat8(ld64(sqt + swz<RBK>(row, 32 * rho + 4 * g)),
+                                 ld64(sqt + swz<RBK>(row, 32 * rho + 16 + 4 * g)));
+          acc = mma32(sh[rho], qtb, acc);
         }
+        const f16x4 o = to_f16(acc);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o), sb.out,
+                                              orow[T] + (uint32_t)((col0 + 4 * g) * 2), 0, 0);
       }
-      f32x4 gv[NR];
-#pragma unroll
-      for (int r = 0; r < NR; ++r) gv[r] = *reinterpret_cast<const f32x4*>(sm.g + 16 * r + 4 * g);
-      f16x8 sh[DK / 32];
-#pragma unroll
-      for (int rho = 0; rho < DK / 32; ++rho)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          sh[rho][u] = (f16)st[2 * rho][j][u];
-          sh[rho][4 + u] = (f16)st[2 * rho + 1][j][u];
-        }
-#pragma unroll
-      for (int I = 0; I < 2; ++I) {
-        const int t = 16 * I + n16;
-        f32x4 acc = mma32(va, sb[I], f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-        for (int rho = 0; rho < DK / 32; ++rho) acc = mma32(sh[rho], qb[I][rho], acc);
-        f16x4 w;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) w[u] = (f16)acc[u];
-        *reinterpret_cast<f16x4*>(sm.o + t * OS + col0 + 4 * g) = w;
-      }
-      // S <- diag(exp(b_end)) S + KL^T V
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
-        const f16x8 kar = *reinterpret_cast<const f16x8*>(sm.klt + (16 * r + n16) * AS + 8 * g);
-        f32x4 acc = st[r][j];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) acc[u] *= gv[r][u];
-        st[r][j] = mma32(kar, va, acc);
+        const f16x8 kar = cat8(tr_read<RBK>(s.la, 0, 16 * r), tr_read<RBK>(s.la, 16, 16 * r));
+        const f32x4 gv = *reinterpret_cast<const f32x4*>(sgd + 16 * r + 4 * g);
+        st[r][j] = mma32(kar, va, st[r][j] * gv);
       }
     }
-    __syncthreads();
+  };
 
-    // ---- Phase W
-    constexpr int PO = DV / 8;
-    constexpr int NO = kStep * PO / kThreads;
-#pragma unroll
-    for (int jj = 0; jj < NO; ++jj) {
-      const int id = tid + kThreads * jj;
-      const int tok = id / PO, pc = id - tok * PO;
-      if (tok < valid) {
-        const size_t o = off_v + (size_t)gm.cell(t0 + tok) * DV + pc * 8;
-        *reinterpret_cast<uint4*>(out + o) = *reinterpret_cast<const uint4*>(sm.o + tok * OS + pc * 8);
-      }
-    }
+  issue(slot0, 0);
+  wait_barrier<vmcnt_imm(0)>();  // the entry state and step 0 have landed
+  for (int step = 0; step < n_steps; step += 2) {
+    issue(slot1, step + 1);
+    phase_p(slot0);
+    wait_barrier<kLgkmZero>();
+    phase_o(slot0, step);
+    // step + 1 has landed (only this step's output stores may be in flight)
+    // and every wave is done with slot0
+    wait_barrier<vmcnt_lgkm0_imm(NSTORE)>();
+    if (step + 1 >= n_steps) break;
+    issue(slot0, step + 2);
+    phase_p(slot1);
+    wait_barrier<kLgkmZero>();
+    phase_o(slot1, step + 1);
+    wait_barrier<vmcnt_lgkm0_imm(NSTORE)>();
   }
+  // loads past the span's end (zero fills) must land before the workgroup's
+  // LDS can be handed on
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
   if (span == p.n_spans - 1 && p.final_state != nullptr) {
+    // the lane index is recomputed here (mbcnt) and passed through an empty
+    // asm, so the compiler forms these addresses here rather than holding
+    // them across the loop
+    int l = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    asm volatile("" : "+v"(l));
     float* dst = p.final_state + (size_t)bh * DK * DV;
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
-      const int col = 16 * (wave + 4 * j) + n16;
+      const int col = 16 * (wave + 4 * j) + (l & 15);
 #pragma unroll
       for (int r = 0; r < NR; ++r)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) dst[(16 * r + 4 * g + u) * DV + col] = st[r][j][u];
+        for (int u = 0; u < 4; ++u) dst[(16 * r + 4 * (l >> 4) + u) * DV + col] = st[r][j][u];
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Span-summary kernel, float16.  Keeps S^T in the accumulators, wave w owning
-// key dims 16*db.. (db = w, w+4) for all value columns: lane (n, g) of tile cb
-// holds S^T[16cb + 4g + u][16db + n], so each lane scales by one decay factor.
+// Span-summary kernel, float16.  One workgroup per (batch*head, span) folds
+// the span's chunks into (prod alpha, state reached from zero).  Chunks are
+// taken last to first, so each key is scaled by its whole decay to the span
+// end up front (k_t * exp(sum of log-alpha after t)) and the state is never
+// rescaled: S^T += V^T Kl over the span.
+//
+// Wave w owns key dims 16 db .. (db = w, w + 4): S^T tile cb sits in lane
+// (n, g) as S^T[16 cb + 4g + u][16 db + n].  Per chunk and key block:
+//   - log-alpha and k arrive transposed from the tiles (lane (n, g): tokens
+//     4g..4g+3 of dim n in each 16-token sub-block J);
+//   - G, the decay from the chunk end to the span end, runs through an MFMA
+//     chain: rest_J = U . la_J + G_J (U strictly upper triangular: the decay
+//     after token t inside sub-block J) and G_{J-1} = 1 . la_J + G_J;
+//   - Kl_J = k_J * exp(rest_J) in packed float16;
+//   - S^T += V^T Kl as 16x16x32 MFMAs over sub-block pairs: the 32 token slots
+//     of lane group g hold tokens 4g.. of the first sub-block, then of the
+//     second, for both operands.
 template <int DK, int DV>
-struct SumSmemH {
-  static constexpr int AS = kChunk + 8;
-  alignas(16) f16 kt[trow(DK) * AS];   // k^T [trow(d_k)][token]
-  alignas(16) f16 lat[trow(DK) * AS];  // log-alpha^T
-  alignas(16) f16 vt[trow(DV) * AS];   // V^T
+struct SumTile {
+  f16* k;
+  f16* la;
+  f16* v;
 };
 
 template <int DK, int DV>
 __global__ __launch_bounds__(kThreads) void span_summary_f16_kernel(FwdParams p) {
-  using SM = SumSmemH<DK, DV>;
-  __shared__ SM sm;
-  constexpr int AS = SM::AS;
+  // six separate LDS objects, so the compiler's own waits for the LDS-writing
+  // loads can tell the tiles apart
+  __shared__ __attribute__((aligned(16))) f16 k0[kChunk * DK], la0[kChunk * DK], v0[kChunk * DV];
+  __shared__ __attribute__((aligned(16))) f16 k1[kChunk * DK], la1[kChunk * DK], v1[kChunk * DV];
+  const SumTile<DK, DV> slot0{k0, la0, v0}, slot1{k1, la1, v1};
   constexpr int NDB = DK / 64, NCB = DV / 16;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  constexpr int RBK = 2 * DK, RBV = 2 * DV;
+  constexpr int NBK = RBK / 64, NBV = RBV / 64;  // 1 KB blocks per wave and tile
+  constexpr int NDMA = 2 * NBK + NBV;             // LDS-writing loads per wave and chunk
+  static_assert(NDMA < 64, "vmcnt range");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n16 = lane & 15, g = lane >> 4;
 
   const int bh = blockIdx.x / p.n_spans;
   const int span = blockIdx.x - bh * p.n_spans;
   const int b = bh / p.heads;
   const GridMap gm = grid_map(p, b);
-  const size_t off_k = (size_t)bh * p.T * DK;
-  const size_t off_v = (size_t)bh * p.T * DV;
+  const SeqBufs sb = seq_bufs<DK, DV>(p, bh);
   const int c_begin = span * p.span_chunks;
   const int c_end = min(c_begin + p.span_chunks, p.n_chunks);
-  const f16* k = static_cast<const f16*>(p.k);
-  const f16* la = static_cast<const f16*>(p.la);
-  const f16* v = static_cast<const f16*>(p.v);
 
-  // Constant A operands (rows t, cols s of a 16x16 block): strict upper part
-  // (s > t) of the diagonal block and the all-ones block for later sub-blocks,
-  // so that the MFMA yields the decay from token t to the chunk end.
-  f16x4 m_diag, m_ones;
+  // Fill a tile buffer with chunk c; a chunk before the span loads nothing.
+  auto issue = [&](const SumTile<DK, DV>& s, int c) {
+    const int t0 = c * kChunk;
+    const int valid = c >= c_begin ? min(kChunk, p.T - t0) : 0;
+#pragma unroll
+    for (int i = 0; i < NBK; ++i) {
+      const int blk = wave * NBK + i;
+      const uint32_t off = dma_offset<RBK>(blk, t0, valid, gm);
+      dma16(sb.k, s.k + blk * 512, off);
+      dma16(sb.la, s.la + blk * 512, off);
+      if (RBV == RBK) dma16(sb.v, s.v + blk * 512, off);
+    }
+    if (RBV != RBK) {
+#pragma unroll
+      for (int i = 0; i < NBV; ++i) {
+        const int blk = wave * NBV + i;
+        dma16(sb.v, s.v + blk * 512, dma_offset<RBV>(blk, t0, valid, gm));
+      }
+    }
+  };
+
+  // A operands: strictly upper triangular (s > t) and all-ones 16x16 blocks.
+  f16x4 m_upper, m_ones;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    m_diag[u] = (f16)((4 * g + u > n16) ? 1.f : 0.f);
+    m_upper[u] = (f16)((4 * g + u > n16) ? 1.f : 0.f);
     m_ones[u] = (f16)1.f;
   }
 
   f32x4 st[NDB][NCB];
+  f32x4 gdec[NDB];  // decay (log) from the current chunk's end to the span end, per key dim
 #pragma unroll
-  for (int d = 0; d < NDB; ++d)
+  for (int d = 0; d < NDB; ++d) {
+    gdec[d] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) st[d][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float log_gate[NDB];
-#pragma unroll
-  for (int d = 0; d < NDB; ++d) log_gate[d] = 0.f;
+  }
 
-  // Two chunks of loads in flight.  The loop is unrolled by two with
-  // unconditional loads, so the compiler can wait for just the older chunk: a
-  // chunk index past the span reads nothing and stages zeros, and an all-zero
-  // chunk (no keys, no values, log-alpha 0) leaves the state unchanged.
-  const int t_stop = min(c_end * kChunk, p.T);
-  auto valid_of = [&](int c) { return max(0, min(kChunk, t_stop - c * kChunk)); };
-  LoaderH<DK, DV, false, false> ld0, ld1;
-  ld0.load(nullptr, k, la, v, off_k, off_v, c_begin * kChunk, valid_of(c_begin), gm);
-  ld1.load(nullptr, k, la, v, off_k, off_v, (c_begin + 1) * kChunk, valid_of(c_begin + 1), gm);
-  auto compute_chunk = [&]() {
+  auto fold = [&](const SumTile<DK, DV>& s) {
 #pragma unroll
-      for (int d = 0; d < NDB; ++d) {
-        const int db = wave + 4 * d;
-        const int dim = 16 * db + n16;
-        f16x4 lat4[4];
-  #pragma unroll
-        for (int J = 0; J < 4; ++J)
-          lat4[J] = *reinterpret_cast<const f16x4*>(sm.lat + trow(dim) * AS + 16 * J + 4 * g);
-        // decay from token 16I+4g+u to the chunk end, at key dim `dim`
-        f32x4 rest[4];
-  #pragma unroll
-        for (int I = 0; I < 4; ++I) {
-          f32x4 acc = mma16(m_diag, lat4[I], f32x4{0.f, 0.f, 0.f, 0.f});
-  #pragma unroll
-          for (int J = I + 1; J < 4; ++J) acc = mma16(m_ones, lat4[J], acc);
-          rest[I] = acc;
-        }
-        // whole-chunk decay of this dim: token 0's remainder plus its own log-alpha
-        const float first = __shfl(rest[0][0] + (float)lat4[0][0], n16, 64);
-        log_gate[d] += first;
-        const float gch = exp2_fast(first * 1.4426950408889634f);
-  #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb)
-  #pragma unroll
-          for (int u = 0; u < 4; ++u) st[d][cb][u] *= gch;
-  #pragma unroll
-        for (int I = 0; I < 4; ++I) {
-          const f16x4 k4 = *reinterpret_cast<const f16x4*>(sm.kt + trow(dim) * AS + 16 * I + 4 * g);
-          f16x4 kl;
-  #pragma unroll
-          for (int u = 0; u < 4; ++u)
-            kl[u] = (f16)((float)k4[u] * exp2_fast(rest[I][u] * 1.4426950408889634f));
-  #pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) {
-            const f16x4 vv =
-                *reinterpret_cast<const f16x4*>(sm.vt + trow(16 * cb + n16) * AS + 16 * I + 4 * g);
-            st[d][cb] = mma16(vv, kl, st[d][cb]);
-          }
+    for (int d = 0; d < NDB; ++d) {
+      const int db = wave + 4 * d;
+      f16x4 lat[4], kt[4];
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        lat[J] = tr_read<RBK>(s.la, 16 * J, 16 * db);
+        kt[J] = tr_read<RBK>(s.k, 16 * J, 16 * db);
+      }
+      f32x4 rest[4];
+      f32x4 c = gdec[d];
+#pragma unroll
+      for (int J = 3; J >= 0; --J) {
+        rest[J] = mma16(m_upper, lat[J], c);
+        c = mma16(m_ones, lat[J], c);
+      }
+      gdec[d] = c;
+      f16x4 kl[4];
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        f32x4 e;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) e[u] = exp2_fast(rest[J][u] * 1.4426950408889634f);
+        kl[J] = kt[J] * __builtin_convertvector(e, f16x4);
+      }
+#pragma unroll
+      for (int P = 0; P < 2; ++P) {
+        const f16x8 bk = cat8(kl[2 * P], kl[2 * P + 1]);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          const f16x8 av = cat8(tr_read<RBV>(s.v, 32 * P, 16 * cb), tr_read<RBV>(s.v, 32 * P + 16, 16 * cb));
+          st[d][cb] = mma32(av, bk, st[d][cb]);
         }
       }
+    }
   };
-  for (int c = c_begin; c < c_end; c += 2) {
-    __syncthreads();  // previous chunk's reads of the tiles are done
-    ld0.store(nullptr, nullptr, 0, sm.kt, sm.lat, sm.vt, AS);
-    ld0.load(nullptr, k, la, v, off_k, off_v, (c + 2) * kChunk, valid_of(c + 2), gm);
-    __syncthreads();
-    compute_chunk();
-    __syncthreads();
-    ld1.store(nullptr, nullptr, 0, sm.kt, sm.lat, sm.vt, AS);
-    ld1.load(nullptr, k, la, v, off_k, off_v, (c + 3) * kChunk, valid_of(c + 3), gm);
-    __syncthreads();
-    compute_chunk();
+
+  issue(slot0, c_end - 1);
+  issue(slot1, c_end - 2);
+  for (int c = c_end - 1; c >= c_begin; c -= 2) {
+    wait_barrier<vmcnt_imm(NDMA)>();  // every wave's part of slot0 has landed
+    fold(slot0);
+    wait_barrier<kLgkmZero>();        // every wave's reads of slot0 are done
+    issue(slot0, c - 2);
+    wait_barrier<vmcnt_imm(NDMA)>();
+    if (c - 1 >= c_begin) fold(slot1);
+    wait_barrier<kLgkmZero>();
+    issue(slot1, c - 3);
   }
+  // the trailing loads target chunks before the span (zero fills): let them
+  // land before the workgroup's LDS can be handed on
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
   float* dst = p.span_state + ((size_t)bh * p.n_spans + span) * DK * DV;
 #pragma unroll
@@ -1370,7 +1292,9 @@ __global__ __launch_bounds__(kThreads) void span_summary_f16_kernel(FwdParams p)
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
       *reinterpret_cast<f32x4*>(dst + dim * DV + 16 * cb + 4 * g) = st[d][cb];
-    if (g == 0) p.span_gate[((size_t)bh * p.n_spans + span) * DK + dim] = exp2_fast(log_gate[d] * 1.4426950408889634f);
+    if (g == 0)
+      p.span_gate[((size_t)bh * p.n_spans + span) * DK + dim] =
+          exp2_fast(gdec[d][0] * 1.4426950408889634f);
   }
 }
 

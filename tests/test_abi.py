@@ -55,6 +55,10 @@ def test_argument_errors(dtype):
     for kw in ("B", "heads", "H", "W"):
         assert call(dtype, **{kw: 0}) == -2, kw
     assert call(dtype, H=1 << 16, W=1 << 16) == -2          # T beyond 2^30
+    # one sequence's rows of one tensor reach 2 GiB (32-bit byte offsets)
+    dk = 128 if dtype == "fp16" else 64
+    assert call(dtype, B=1, heads=1, H=4096, W=2048, d_k=dk) == -2
+    assert call(dtype, B=1, heads=1, H=4096, W=2047, d_k=dk) != -2
     assert call(dtype, chunk=32) == -3
     assert call(dtype, d_k=96) == -3
     assert call(dtype, d_v=32) == -3
