@@ -885,8 +885,7 @@ __device__ __forceinline__ f16x8 cat8(f16x4 a, f16x4 b) {
 //       by MFMA (log-alpha read transposed), exp(+-c), DPP broadcast of the
 //       sub-block decays; writes, in place of q, k, log-alpha, the anchored
 //       q*exp(c), k*exp(-c) and the keys decayed to the step end, plus q
-//       decayed from the step start and the sub-block 0 keys decayed to its
-//       end; packed float16 products
+//       decayed from the step start; packed float16 products
 //   O : wave w owns value columns 16w.. : the three causal score tiles in
 //       transposed orientation (A^T, computed by every wave: cheaper than a
 //       barrier), O^T = V^T A^T + S^T Qt^T with the score tiles used straight
@@ -930,12 +929,12 @@ __global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 4 : (DK == 128 &
   constexpr int NBK = RBK / 128, NBV = RBV / 128;  // 1 KB blocks per wave and tile of one step
   constexpr int NSTORE = 2 * NC;                    // output stores per wave and step
   static_assert(NSTORE < 64, "vmcnt range");
-  // separate LDS objects per buffer, so the compiler's own waits for the
-  // LDS-writing loads can tell them apart
+  // Two step buffers (the next step loads while this one is computed; a
+  // third buffer measured slower).  Separate LDS objects per buffer, so the
+  // compiler's own waits for the LDS-writing loads can tell them apart.
   __shared__ __attribute__((aligned(16))) f16 q0[kStep * DK], k0[kStep * DK], la0[kStep * DK], v0[kStep * DV];
   __shared__ __attribute__((aligned(16))) f16 q1[kStep * DK], k1[kStep * DK], la1[kStep * DK], v1[kStep * DV];
   __shared__ __attribute__((aligned(16))) f16 sqt[kStep * DK];  // q decayed from the step start
-  __shared__ __attribute__((aligned(16))) f16 skv[kSub * DK];   // sub-block 0 keys decayed to its end
   __shared__ __attribute__((aligned(16))) float sgd[DK];        // exp(decay over the step)
   const StepTiles<DK, DV> slot0{q0, k0, la0, v0}, slot1{q1, k1, la1, v1};
 
@@ -1029,12 +1028,7 @@ __global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 4 : (DK == 128 &
         st64(s.q + swz<RBK>(row, dim0), ql);
         st64(sqt + swz<RBK>(row, dim0), qt);
         st64(s.k + swz<RBK>(row, dim0), kd);
-        if (I == 0) {
-          st64(skv + swz<RBK>(n16, dim0), kend);
-          st64(s.la + swz<RBK>(row, dim0), kend * to_f16(ed[1]));
-        } else {
-          st64(s.la + swz<RBK>(row, dim0), kend);
-        }
+        st64(s.la + swz<RBK>(row, dim0), (I == 0) ? kend * to_f16(ed[1]) : kend);
       }
     }
   };
@@ -1048,13 +1042,15 @@ __global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 4 : (DK == 128 &
 #pragma unroll
     for (int rho = 0; rho < NRHO; ++rho) {
       const int col = 32 * rho + 8 * g;
+      // tile (s in 0, t in 1): exp(b_t - b_s) splits into q_t exp(b_t) (Qt)
+      // and k_s exp(-c_s) (Kd), since b = c inside sub-block 0
       const f16x8 kd0 = ld128(s.k + swz<RBK>(n16, col));
       const f16x8 kd1 = ld128(s.k + swz<RBK>(16 + n16, col));
-      const f16x8 kv = ld128(skv + swz<RBK>(n16, col));
       const f16x8 qa = ld128(s.q + swz<RBK>(n16, col));
       const f16x8 qb = ld128(s.q + swz<RBK>(16 + n16, col));
+      const f16x8 qt1 = ld128(sqt + swz<RBK>(16 + n16, col));
       d00 = mma32(kd0, qa, d00);
-      d01 = mma32(kv, qb, d01);
+      d01 = mma32(kd0, qt1, d01);
       d11 = mma32(kd1, qb, d11);
     }
 #pragma unroll
@@ -1103,21 +1099,22 @@ __global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 4 : (DK == 128 &
     }
   };
 
+  auto run_step = [&](const StepTiles<DK, DV>& s, int step) {
+    phase_p(s);
+    wait_barrier<kLgkmZero>();
+    phase_o(s, step);
+  };
+  // Before step s the loads in flight are step s and the stores of s - 1.
   issue(slot0, 0);
   wait_barrier<vmcnt_imm(0)>();  // the entry state and step 0 have landed
   for (int step = 0; step < n_steps; step += 2) {
     issue(slot1, step + 1);
-    phase_p(slot0);
-    wait_barrier<kLgkmZero>();
-    phase_o(slot0, step);
-    // step + 1 has landed (only this step's output stores may be in flight)
-    // and every wave is done with slot0
-    wait_barrier<vmcnt_lgkm0_imm(NSTORE)>();
+    run_step(slot0, step);
     if (step + 1 >= n_steps) break;
+    wait_barrier<vmcnt_lgkm0_imm(NSTORE)>();  // step + 1 landed; slot0 free
     issue(slot0, step + 2);
-    phase_p(slot1);
-    wait_barrier<kLgkmZero>();
-    phase_o(slot1, step + 1);
+    run_step(slot1, step + 1);
+    if (step + 2 >= n_steps) break;
     wait_barrier<vmcnt_lgkm0_imm(NSTORE)>();
   }
   // loads past the span's end (zero fills) must land before the workgroup's
