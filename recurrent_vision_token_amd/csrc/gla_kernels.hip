@@ -789,8 +789,8 @@ __global__ __launch_bounds__(kThreads) void chunk_output_kernel(FwdParams p) {
 
 __device__ __forceinline__ float row_bcast15(float x) {
   // every lane of a 16-lane row receives the row's lane 15 value
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
-                                                                0x15F, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x15F,
+                                                             0xF, 0xF, false));
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -853,6 +853,20 @@ __device__ __forceinline__ uint32_t dma_offset(int blk, int t0, int valid, const
   const uint32_t off = (uint32_t)gm.cell(t0 + r) * RB + (uint32_t)((pp ^ (r & 7)) * 16);
   return off | ((uint32_t)(r >= valid) << 31);
 }
+// The same, also handing back the row's grid cell with the out-of-range flag
+// in bit 31 (for the lanes that load piece 0 of a row, first_piece is set).
+template <int RB>
+__device__ __forceinline__ uint32_t dma_offset_cell(int blk, int t0, int valid, const GridMap& gm,
+                                                    uint32_t* cell_flag, bool* first_piece) {
+  const int lane = threadIdx.x & 63;
+  const int byte = blk * 1024 + 16 * lane;
+  const int r = byte / RB, pp = (byte % RB) / 16;
+  const uint32_t flag = (uint32_t)(r >= valid) << 31;
+  const uint32_t cell = (uint32_t)gm.cell(t0 + r);
+  *cell_flag = cell | flag;
+  *first_piece = pp == 0;
+  return (cell * RB + (uint32_t)((pp ^ (r & 7)) * 16)) | flag;
+}
 __device__ __forceinline__ void dma16(rsrc_t src, f16* block, uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void_t*)block, 16, off, 0, 0, 0);
 }
@@ -902,6 +916,13 @@ template <int RB>
 __device__ __forceinline__ int swz(int row, int col) {
   return row * (RB / 2) + (((col >> 3) ^ (row & 7)) << 3) + (col & 7);
 }
+// Column of key dim d (d % 4 == 0, four dims kept together) in token-slot
+// order: within each 32-dim group, dims 4g..4g+3 and 16+4g..16+4g+3 sit side
+// by side at 8g.., so one 128-bit read yields an x32 MFMA operand.
+__device__ __forceinline__ int qt_slot(int d) {
+  const int r = d & 31;
+  return (d & ~31) + (r < 16 ? 2 * r : 2 * (r - 16) + 4);
+}
 __device__ __forceinline__ f16x4 ld64(const f16* a) { return *reinterpret_cast<const f16x4*>(a); }
 __device__ __forceinline__ f16x8 ld128(const f16* a) { return *reinterpret_cast<const f16x8*>(a); }
 __device__ __forceinline__ void st64(f16* a, f16x4 x) { *reinterpret_cast<f16x4*>(a) = x; }
@@ -934,8 +955,11 @@ __global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 4 : (DK == 128 &
   // compiler's own waits for the LDS-writing loads can tell them apart.
   __shared__ __attribute__((aligned(16))) f16 q0[kStep * DK], k0[kStep * DK], la0[kStep * DK], v0[kStep * DV];
   __shared__ __attribute__((aligned(16))) f16 q1[kStep * DK], k1[kStep * DK], la1[kStep * DK], v1[kStep * DV];
-  __shared__ __attribute__((aligned(16))) f16 sqt[kStep * DK];  // q decayed from the step start
-  __shared__ __attribute__((aligned(16))) float sgd[DK];        // exp(decay over the step)
+  // q decayed from the step start, columns in token-slot order (see qt_slot)
+  __shared__ __attribute__((aligned(16))) f16 sqt[kStep * DK];
+  __shared__ __attribute__((aligned(16))) float sgd[DK];  // exp(decay over the step)
+  // grid cell of each step row (bit 31: past the span), per step buffer
+  __shared__ uint32_t srow[2][kStep];
   const StepTiles<DK, DV> slot0{q0, k0, la0, v0}, slot1{q1, k1, la1, v1};
 
   const int lane = threadIdx.x & 63;
@@ -967,13 +991,16 @@ __global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 4 : (DK == 128 &
     }
   }
 
-  auto issue = [&](const StepTiles<DK, DV>& s, int step) {
+  auto issue = [&](const StepTiles<DK, DV>& s, uint32_t* rows, int step) {
     const int t0 = t_begin + kStep * step;
     const int valid = max(0, min(kStep, t_end - t0));
 #pragma unroll
     for (int i = 0; i < NBK; ++i) {
       const int blk = wave * NBK + i;
-      const uint32_t off = dma_offset<RBK>(blk, t0, valid, gm);
+      uint32_t cf;
+      bool first;
+      const uint32_t off = dma_offset_cell<RBK>(blk, t0, valid, gm, &cf, &first);
+      if (first) rows[(blk * 1024 + 16 * lane) / RBK] = cf;
       dma16(sb.q, s.q + blk * 512, off);
       dma16(sb.k, s.k + blk * 512, off);
       dma16(sb.la, s.la + blk * 512, off);
@@ -1026,7 +1053,7 @@ __global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 4 : (DK == 128 &
         const f16x4 kd = k4[I] * to_f16(ek[I]);
         const f16x4 kend = kd * to_f16(ed[I]);  // decayed to the end of sub-block I
         st64(s.q + swz<RBK>(row, dim0), ql);
-        st64(sqt + swz<RBK>(row, dim0), qt);
+        st64(sqt + swz<RBK>(row, qt_slot(dim0)), qt);
         st64(s.k + swz<RBK>(row, dim0), kd);
         st64(s.la + swz<RBK>(row, dim0), (I == 0) ? kend * to_f16(ed[1]) : kend);
       }
@@ -1034,9 +1061,7 @@ __global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 4 : (DK == 128 &
   };
 
   // ---- O: scores, outputs, state update
-  auto phase_o = [&](const StepTiles<DK, DV>& s, int step) {
-    const int t0 = t_begin + kStep * step;
-    const int valid = max(0, min(kStep, t_end - t0));
+  auto phase_o = [&](const StepTiles<DK, DV>& s, const uint32_t* rows) {
     // A^T tiles: lane (t, g) holds A[t][s = 4g + u] of the tile
     f32x4 d00 = {0.f, 0.f, 0.f, 0.f}, d01 = d00, d11 = d00;
 #pragma unroll
@@ -1048,7 +1073,9 @@ __global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 4 : (DK == 128 &
       const f16x8 kd1 = ld128(s.k + swz<RBK>(16 + n16, col));
       const f16x8 qa = ld128(s.q + swz<RBK>(n16, col));
       const f16x8 qb = ld128(s.q + swz<RBK>(16 + n16, col));
-      const f16x8 qt1 = ld128(sqt + swz<RBK>(16 + n16, col));
+      // Qt columns are in token-slot order: gather the natural dims col..col+7
+      const f16x8 qt1 = cat8(ld64(sqt + swz<RBK>(16 + n16, qt_slot(col))),
+                             ld64(sqt + swz<RBK>(16 + n16, qt_slot(col + 4))));
       d00 = mma32(kd0, qa, d00);
       d01 = mma32(kd0, qt1, d01);
       d11 = mma32(kd1, qb, d11);
@@ -1066,8 +1093,8 @@ __global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 4 : (DK == 128 &
     uint32_t orow[2];
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
-      const int t = 16 * T + n16;
-      orow[T] = ((uint32_t)gm.cell(t0 + t) * RBV) | ((uint32_t)(t >= valid) << 31);
+      const uint32_t cf = rows[16 * T + n16];
+      orow[T] = (cf & 0x7fffffffu) * RBV | (cf & 0x80000000u);
     }
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
@@ -1081,11 +1108,8 @@ __global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 4 : (DK == 128 &
         const int row = 16 * T + n16;
         f32x4 acc = mma32(va, sbt[T], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-        for (int rho = 0; rho < NRHO; ++rho) {
-          const f16x8 qtb = cat8(ld64(sqt + swz<RBK>(row, 32 * rho + 4 * g)),
-                                 ld64(sqt + swz<RBK>(row, 32 * rho + 16 + 4 * g)));
-          acc = mma32(sh[rho], qtb, acc);
-        }
+        for (int rho = 0; rho < NRHO; ++rho)
+          acc = mma32(sh[rho], ld128(sqt + swz<RBK>(row, 32 * rho + 8 * g)), acc);
         const f16x4 o = to_f16(acc);
         __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o), sb.out,
                                               orow[T] + (uint32_t)((col0 + 4 * g) * 2), 0, 0);
@@ -1099,21 +1123,21 @@ __global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 4 : (DK == 128 &
     }
   };
 
-  auto run_step = [&](const StepTiles<DK, DV>& s, int step) {
+  auto run_step = [&](const StepTiles<DK, DV>& s, const uint32_t* rows) {
     phase_p(s);
     wait_barrier<kLgkmZero>();
-    phase_o(s, step);
+    phase_o(s, rows);
   };
   // Before step s the loads in flight are step s and the stores of s - 1.
-  issue(slot0, 0);
+  issue(slot0, srow[0], 0);
   wait_barrier<vmcnt_imm(0)>();  // the entry state and step 0 have landed
   for (int step = 0; step < n_steps; step += 2) {
-    issue(slot1, step + 1);
-    run_step(slot0, step);
+    issue(slot1, srow[1], step + 1);
+    run_step(slot0, srow[0]);
     if (step + 1 >= n_steps) break;
     wait_barrier<vmcnt_lgkm0_imm(NSTORE)>();  // step + 1 landed; slot0 free
-    issue(slot0, step + 2);
-    run_step(slot1, step + 1);
+    issue(slot0, srow[0], step + 2);
+    run_step(slot1, srow[1]);
     if (step + 2 >= n_steps) break;
     wait_barrier<vmcnt_lgkm0_imm(NSTORE)>();
   }
