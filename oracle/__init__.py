@@ -8,5 +8,6 @@ from .gla_oracle import (  # noqa: F401
     SCAN_T2B,
     batch_directions,
     gla_forward,
+    log_alpha_from_logits,
     scan_order,
 )

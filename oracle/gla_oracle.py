@@ -82,6 +82,23 @@ def batch_directions(B, scan_dir):
     return [scan_dir] * B
 
 
+def log_alpha_from_logits(z, tau):
+    """Forget-gate activation: log alpha = logsigmoid(z) / tau, in float64.
+
+    The pages describe a learnable forget gate on the key side (GTR news
+    write-up, section "What linear attention saves"); its activation is read
+    as the usual gated-linear-attention one, alpha = sigmoid(z)^(1/tau), which
+    is also how the synthetic workloads draw their gates (logsigmoid of a
+    normal draw, divided by 16).  logsigmoid(z) = -log(1 + exp(-z)) is
+    evaluated as min(z, 0) - log1p(exp(-|z|)), which never overflows.
+    """
+    tau = float(tau)
+    if not (tau > 0.0 and np.isfinite(tau)):
+        raise ValueError("tau must be positive and finite")
+    z = np.asarray(z, dtype=np.float64)
+    return (np.minimum(z, 0.0) - np.log1p(np.exp(-np.abs(z)))) / tau
+
+
 def gla_forward(q, k, v, log_alpha, scan_dir, initial_state=None):
     """Token-by-token recurrence in float64.
 

@@ -8,7 +8,10 @@ for d_k = 1), direction / grid invariants, linearity, state consistency,
 composition across a split of the scan, and causality.  Together they catch a
 dropped term, a sign flip in the gate, decay applied after the add instead of
 before, exclusive instead of inclusive outputs, decay on the value side, a
-wrong scan order, and transposed operands.
+wrong scan order, and transposed operands.  The initial-state input is pinned
+by the brute-force form with the state's own decay written out and by
+linearity; the gate activation by closed forms, the logsigmoid identity,
+its tails and scipy's independent log_expit.
 """
 
 import json
@@ -265,3 +268,71 @@ def test_causality(d):
     fa = o_a.reshape(1, 2, H * W, -1)[:, :, early]
     fb = o_b.reshape(1, 2, H * W, -1)[:, :, early]
     assert np.array_equal(fa, fb)
+
+
+# ------------------------------------------------- initial state, gate logits
+
+@pytest.mark.parametrize("d", [0, 2, 3])
+def test_brute_force_with_initial_state(d):
+    # o_t = q_t (diag(prod_{r<=t} alpha_r) S0 + sum_{s<=t} ...): the initial
+    # state is decayed by every step up to and including t, written out by hand
+    rng = np.random.default_rng(40 + d)
+    q, k, v, la = rand_inputs(rng, 1, 2, 3, 4, 3, 2)
+    s0 = rng.standard_normal((1, 2, 3, 2))
+    out, fin = gla_forward(q, k, v, la, d, initial_state=s0)
+    bo, bf = brute_force(q, k, v, la, d)
+    H, W, T = 3, 4, 12
+    perm = scan_order(H, W, d)
+    for h in range(2):
+        Q = q[0, h].reshape(T, 3)[perm]
+        L = la[0, h].reshape(T, 3)[perm]
+        for t in range(T):
+            extra = np.zeros(2)
+            for i in range(3):
+                extra += Q[t, i] * np.exp(sum(L[r, i] for r in range(t + 1))) * s0[0, h, i]
+            bo.reshape(1, 2, T, 2)[0, h, perm[t]] += extra
+        for i in range(3):
+            bf[0, h, i] += np.exp(sum(L[r, i] for r in range(T))) * s0[0, h, i]
+    assert rel(out, bo) < TOL
+    assert rel(fin, bf) < TOL
+
+
+def test_initial_state_enters_linearly():
+    # the outputs are affine in the initial state: doubling it doubles the
+    # difference from the zero-state run
+    rng = np.random.default_rng(44)
+    q, k, v, la = rand_inputs(rng, 2, 2, 4, 3, 4, 3)
+    s0 = rng.standard_normal((2, 2, 4, 3))
+    o0, f0 = gla_forward(q, k, v, la, 1)
+    o1, f1 = gla_forward(q, k, v, la, 1, initial_state=s0)
+    o2, f2 = gla_forward(q, k, v, la, 1, initial_state=2 * s0)
+    assert rel(o2 - o0, 2 * (o1 - o0)) < TOL
+    assert rel(f2 - f0, 2 * (f1 - f0)) < TOL
+
+
+def test_gate_activation_closed_forms():
+    from oracle import log_alpha_from_logits as act
+    ln2 = np.log(2.0)
+    assert abs(act(0.0, 1.0) + ln2) < 1e-15
+    assert abs(act(0.0, 16.0) + ln2 / 16) < 1e-16
+    # sigmoid(ln 3) = 3/4
+    assert abs(act(np.log(3.0), 2.0) - np.log(0.75) / 2) < 1e-15
+    # logsigmoid(z) - logsigmoid(-z) = z for any z
+    z = np.linspace(-40, 40, 161)
+    assert np.max(np.abs(act(z, 1.0) - act(-z, 1.0) - z)) < 1e-12
+    # tails: -log(1 + e^-z) ~ -e^-z for large z, ~ z for very negative z
+    assert abs(act(40.0, 1.0) + np.exp(-40.0)) < 1e-30
+    assert abs(act(-800.0, 1.0) + 800.0) < 1e-12
+    # alpha = sigmoid(z)^(1/tau), checked against a direct evaluation
+    zz = np.linspace(-8, 8, 33)
+    assert np.max(np.abs(np.exp(16.0 * act(zz, 16.0)) - 1.0 / (1.0 + np.exp(-zz)))) < 1e-15
+    for bad in (0.0, -1.0, np.inf, np.nan):
+        with pytest.raises(ValueError):
+            act(0.0, bad)
+
+
+def test_gate_activation_matches_scipy():
+    from scipy.special import log_expit
+    from oracle import log_alpha_from_logits as act
+    z = np.random.default_rng(45).standard_normal(1000) * 6
+    assert np.max(np.abs(act(z, 16.0) - log_expit(z) / 16.0)) < 1e-15
