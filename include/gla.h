@@ -59,12 +59,19 @@ enum {
   GLA_SCAN_ROTATE_BATCH = 4
 };
 
+/* gate_mode values of gla_chunk_fwd_ex */
+enum {
+  GLA_GATE_LOG_ALPHA = 0,     /* `gate` holds log_alpha, as in gla_chunk_fwd          */
+  GLA_GATE_LOGITS = 1         /* `gate` holds logits z: log_alpha = logsigmoid(z)/tau */
+};
+
 /* status codes */
 enum {
   GLA_OK = 0,
   GLA_ERR_NULL = -1,          /* a required pointer is NULL                     */
-  GLA_ERR_SHAPE = -2,         /* B, heads, H or W < 1, a size overflows, or one
-                                 sequence's rows of a tensor reach 2 GiB          */
+  GLA_ERR_SHAPE = -2,         /* B, heads, H or W < 1, a size overflows, one
+                                 sequence's rows of a tensor reach 2 GiB, or tau
+                                 is not positive and finite                      */
   GLA_ERR_UNSUPPORTED = -3,   /* d_k / d_v / chunk combination not built        */
   GLA_ERR_ALIGN = -4,         /* a tensor pointer is not 16-byte aligned        */
   GLA_ERR_SCAN_DIR = -5,      /* scan_dir outside 0..4                          */
@@ -84,6 +91,35 @@ enum {
 int gla_chunk_fwd(const void* q, const void* k, const void* v, const void* log_alpha,
                   int scan_dir, int B, int heads, int H, int W, int d_k, int d_v, int chunk,
                   void* out, float* final_state, void* stream);
+
+/*
+ * Extended float16 entry: gla_chunk_fwd plus an initial state and a fused
+ * forget-gate activation.
+ *
+ * The pages describe a learnable forget gate on the key side (GTR news
+ * write-up, section "What linear attention saves"); with gate_mode =
+ * GLA_GATE_LOGITS the kernels read the gate's pre-activation logits z (same
+ * layout and type as log_alpha) and use log_alpha = logsigmoid(z) / tau, i.e.
+ * alpha = sigmoid(z)^(1/tau), computed in float32 and rounded to float16
+ * where the kernels use it.  This saves the separate pass that would write
+ * log_alpha.  tau must be positive and finite (16 in the GTR-style
+ * workloads).  With GLA_GATE_LOG_ALPHA, `gate` is log_alpha and tau is
+ * ignored.
+ *
+ * initial_state: [B][heads][d_k][d_v] float32, the state before the first scan
+ * step (NULL = zero), as when resuming a scan that was cut into pieces: the
+ * final_state of one call fed to the next reproduces the uncut scan.
+ * final_state may be the same pointer as initial_state (updated in place);
+ * any other overlap between them, or between initial_state and out, is
+ * GLA_ERR_ALIAS.  Alignment: 4 bytes.
+ *
+ * Errors as gla_chunk_fwd, plus GLA_ERR_UNSUPPORTED for an unknown gate_mode
+ * (checked first) and GLA_ERR_SHAPE for a bad tau.
+ */
+int gla_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* gate, int gate_mode,
+                     float tau, const float* initial_state, int scan_dir, int B, int heads, int H,
+                     int W, int d_k, int d_v, int chunk, void* out, float* final_state,
+                     void* stream);
 
 /*
  * Float32 entry: every tensor float32, float32 MFMA tiles, float32 state.

@@ -17,8 +17,9 @@ STATUS = {
     0: "GLA_OK", -1: "GLA_ERR_NULL", -2: "GLA_ERR_SHAPE", -3: "GLA_ERR_UNSUPPORTED",
     -4: "GLA_ERR_ALIGN", -5: "GLA_ERR_SCAN_DIR", -6: "GLA_ERR_ALIAS", -7: "GLA_ERR_HIP",
 }
-EXPORTED = ("gla_chunk_fwd", "gla_chunk_fwd_f32", "gla_plan_spans", "gla_set_kernel_events",
-            "gla_status_str", "gla_version")
+EXPORTED = ("gla_chunk_fwd", "gla_chunk_fwd_ex", "gla_chunk_fwd_f32", "gla_plan_spans",
+            "gla_set_kernel_events", "gla_status_str", "gla_version")
+GATE_MODES = {"log_alpha": 0, "logits": 1}
 
 _lib = None
 
@@ -44,6 +45,8 @@ def load():
         fn = getattr(lib, name)
         fn.argtypes = sig
         fn.restype = ctypes.c_int
+    lib.gla_chunk_fwd_ex.argtypes = [vp, vp, vp, vp, i, ctypes.c_float, vp] + sig[4:]
+    lib.gla_chunk_fwd_ex.restype = ctypes.c_int
     lib.gla_status_str.argtypes = [ctypes.c_int]
     lib.gla_status_str.restype = ctypes.c_char_p
     lib.gla_plan_spans.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i)]
@@ -68,14 +71,14 @@ def raw_call(dtype, q, k, v, la, scan_dir, B, heads, H, W, d_k, d_v, chunk, out,
     return fn(q, k, v, la, scan_dir, B, heads, H, W, d_k, d_v, chunk, out, final_state, stream)
 
 
-def gla_chunk_fwd(q, k, v, log_alpha, scan_dir, chunk=64, out=None, final_state=None,
-                  want_final_state=True, stream=None):
-    """Chunkwise GLA forward on device tensors.
+def raw_call_ex(q, k, v, gate, gate_mode, tau, initial_state, scan_dir, B, heads, H, W, d_k,
+                d_v, chunk, out, final_state, stream):
+    """Call gla_chunk_fwd_ex with integer pointers; returns the status code."""
+    return load().gla_chunk_fwd_ex(q, k, v, gate, gate_mode, tau, initial_state, scan_dir, B,
+                                   heads, H, W, d_k, d_v, chunk, out, final_state, stream)
 
-    q, k, log_alpha: [B, heads, H, W, d_k]; v: [B, heads, H, W, d_v]; all float16
-    (or all float32), contiguous, on one HIP device.  Returns (out, final_state);
-    final_state is float32 [B, heads, d_k, d_v] or None.
-    """
+
+def _check(q, k, v, log_alpha):
     import torch
 
     tens = (q, k, v, log_alpha)
@@ -92,6 +95,21 @@ def gla_chunk_fwd(q, k, v, log_alpha, scan_dir, chunk=64, out=None, final_state=
         raise ValueError("shape mismatch among q, k, v, log_alpha")
     if not all(t.is_contiguous() for t in tens):
         raise ValueError("tensors must be contiguous")
+    return B, heads, H, W, d_k, d_v
+
+
+def gla_chunk_fwd(q, k, v, log_alpha, scan_dir, chunk=64, out=None, final_state=None,
+                  want_final_state=True, stream=None):
+    """Chunkwise GLA forward on device tensors.
+
+    q, k, log_alpha: [B, heads, H, W, d_k]; v: [B, heads, H, W, d_v]; all float16
+    (or all float32), contiguous, on one HIP device.  Returns (out, final_state);
+    final_state is float32 [B, heads, d_k, d_v] or None.
+    """
+    import torch
+
+    B, heads, H, W, d_k, d_v = _check(q, k, v, log_alpha)
+    dt = q.dtype
     dev = q.device
     if out is None:
         out = torch.empty((B, heads, H, W, d_v), dtype=dt, device=dev)
@@ -103,6 +121,46 @@ def gla_chunk_fwd(q, k, v, log_alpha, scan_dir, chunk=64, out=None, final_state=
     rc = raw_call("fp16" if dt == torch.float16 else "fp32", q.data_ptr(), k.data_ptr(),
                   v.data_ptr(), log_alpha.data_ptr(), int(scan_dir), B, heads, H, W, d_k, d_v,
                   int(chunk), out.data_ptr(), fs_ptr, stream)
+    if rc != GLA_OK:
+        raise GlaError(rc, status_str(rc))
+    return out, final_state
+
+
+def gla_chunk_fwd_ex(q, k, v, gate, scan_dir, gate_mode="log_alpha", tau=16.0,
+                     initial_state=None, chunk=64, out=None, final_state=None,
+                     want_final_state=True, stream=None):
+    """Extended float16 forward: optional initial state and fused gate activation.
+
+    gate holds log_alpha (gate_mode "log_alpha") or the gate logits z
+    (gate_mode "logits", log_alpha = logsigmoid(z) / tau); same shape and
+    dtype as q.  initial_state: float32 [B, heads, d_k, d_v] or None; it may be
+    passed as final_state too, to update the state in place.
+    """
+    import torch
+
+    B, heads, H, W, d_k, d_v = _check(q, k, v, gate)
+    if q.dtype != torch.float16:
+        raise ValueError("gla_chunk_fwd_ex takes float16 tensors")
+    if gate_mode not in GATE_MODES:
+        raise ValueError("gate_mode must be one of %s" % sorted(GATE_MODES))
+    dev = q.device
+    init_ptr = None
+    if initial_state is not None:
+        if (initial_state.dtype != torch.float32 or not initial_state.is_contiguous() or
+                tuple(initial_state.shape) != (B, heads, d_k, d_v) or initial_state.device != dev):
+            raise ValueError("initial_state must be contiguous float32 [B, heads, d_k, d_v] "
+                             "on the tensors' device")
+        init_ptr = initial_state.data_ptr()
+    if out is None:
+        out = torch.empty((B, heads, H, W, d_v), dtype=q.dtype, device=dev)
+    if final_state is None and want_final_state:
+        final_state = torch.empty((B, heads, d_k, d_v), dtype=torch.float32, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    fs_ptr = final_state.data_ptr() if final_state is not None else None
+    rc = raw_call_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), gate.data_ptr(),
+                     GATE_MODES[gate_mode], float(tau), init_ptr, int(scan_dir), B, heads, H, W,
+                     d_k, d_v, int(chunk), out.data_ptr(), fs_ptr, stream)
     if rc != GLA_OK:
         raise GlaError(rc, status_str(rc))
     return out, final_state

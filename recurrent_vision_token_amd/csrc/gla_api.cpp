@@ -4,6 +4,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <atomic>
+#include <cmath>
 #include <cstdint>
 #include <cstdlib>
 #include <mutex>
@@ -28,15 +29,16 @@ thread_local bool t_events_set = false;
 
 // Output-kernel workgroup slots per device (CUs x resident workgroups per CU),
 // read once per (device, variant).
-constexpr int kVariants = 8;
+constexpr int kVariants = 16;
 std::atomic<int> g_slots[kMaxDevices][kVariants];
 
-int variant_index(gla::Dtype dt, int d_k, int d_v) {
-  return (dt == gla::Dtype::kF16 ? 0 : 4) + (d_k == 128 ? 2 : 0) + (d_v == 128 ? 1 : 0);
+int variant_index(gla::Dtype dt, int d_k, int d_v, bool gate_logits) {
+  return (dt == gla::Dtype::kF16 ? 0 : 4) + (d_k == 128 ? 2 : 0) + (d_v == 128 ? 1 : 0) +
+         (gate_logits ? 8 : 0);
 }
 
-int output_slots(int dev, gla::Dtype dt, int d_k, int d_v) {
-  const int vi = variant_index(dt, d_k, d_v);
+int output_slots(int dev, gla::Dtype dt, int d_k, int d_v, bool gate_logits) {
+  const int vi = variant_index(dt, d_k, d_v, gate_logits);
   if (dev < 0 || dev >= kMaxDevices) return 256;
   int n = g_slots[dev][vi].load(std::memory_order_relaxed);
   if (n > 0) return n;
@@ -44,7 +46,7 @@ int output_slots(int dev, gla::Dtype dt, int d_k, int d_v) {
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       cus <= 0)
     cus = 256;
-  n = cus * gla::output_blocks_per_cu(dt, d_k, d_v);
+  n = cus * gla::output_blocks_per_cu(dt, d_k, d_v, gate_logits);
   g_slots[dev][vi].store(n, std::memory_order_relaxed);
   return n;
 }
@@ -77,9 +79,17 @@ int plan_span_chunks(long long bh, int n_chunks, int slots) {
   return (int)(m < 1 ? 1 : m);
 }
 
+// Optional inputs of the extended entry point.
+struct Extras {
+  bool gate_logits = false;               // `la` holds gate logits (fused activation)
+  float tau = 1.f;                        // activation temperature (gate_logits only)
+  const float* initial_state = nullptr;   // [B][heads][d_k][d_v], null = zero state
+};
+
 int forward(gla::Dtype dt, size_t esize, const void* q, const void* k, const void* v,
             const void* la, int scan_dir, int B, int heads, int H, int W, int d_k, int d_v,
-            int chunk, void* out, float* final_state, void* stream, int* plan_only = nullptr) {
+            int chunk, void* out, float* final_state, void* stream, int* plan_only = nullptr,
+            const Extras& ex = Extras()) {
   if (scan_dir < 0 || scan_dir > 4) return GLA_ERR_SCAN_DIR;
   if (!q || !k || !v || !la || !out) return GLA_ERR_NULL;
   if (B < 1 || heads < 1 || H < 1 || W < 1 || d_k < 1 || d_v < 1) return GLA_ERR_SHAPE;
@@ -91,10 +101,15 @@ int forward(gla::Dtype dt, size_t esize, const void* q, const void* k, const voi
   // one sequence's rows of one tensor are addressed with 32-bit byte offsets
   if (T * dmax * (long long)esize >= (1LL << 31)) return GLA_ERR_SHAPE;
   if (chunk != kChunk || !gla::has_variant(dt, d_k, d_v)) return GLA_ERR_UNSUPPORTED;
+  if (ex.gate_logits && dt != gla::Dtype::kF16) return GLA_ERR_UNSUPPORTED;
+  if (ex.gate_logits && !(std::isfinite(ex.tau) && ex.tau > 0.f && std::isfinite(1.f / ex.tau)))
+    return GLA_ERR_SHAPE;
   const void* tens[5] = {q, k, v, la, out};
   for (const void* t : tens)
     if (reinterpret_cast<uintptr_t>(t) % 16 != 0) return GLA_ERR_ALIGN;
   if (final_state && reinterpret_cast<uintptr_t>(final_state) % 4 != 0) return GLA_ERR_ALIGN;
+  if (ex.initial_state && reinterpret_cast<uintptr_t>(ex.initial_state) % 4 != 0)
+    return GLA_ERR_ALIGN;
 
   const uintptr_t nk = (uintptr_t)(BH * T * d_k) * esize;
   const uintptr_t nv = (uintptr_t)(BH * T * d_v) * esize;
@@ -102,17 +117,27 @@ int forward(gla::Dtype dt, size_t esize, const void* q, const void* k, const voi
   const Range rv{(uintptr_t)v, (uintptr_t)v + nv}, rl{(uintptr_t)la, (uintptr_t)la + nk};
   const Range ro{(uintptr_t)out, (uintptr_t)out + nv};
   if (overlap(ro, rq) || overlap(ro, rk) || overlap(ro, rv) || overlap(ro, rl)) return GLA_ERR_ALIAS;
+  const uintptr_t ns = (uintptr_t)(BH * d_k * d_v) * sizeof(float);
   if (final_state) {
-    const Range rf{(uintptr_t)final_state,
-                   (uintptr_t)final_state + (uintptr_t)(BH * d_k * d_v) * sizeof(float)};
+    const Range rf{(uintptr_t)final_state, (uintptr_t)final_state + ns};
     if (overlap(rf, rq) || overlap(rf, rk) || overlap(rf, rv) || overlap(rf, rl) || overlap(rf, ro))
+      return GLA_ERR_ALIAS;
+  }
+  if (ex.initial_state) {
+    // read-only, may share memory with the inputs; the final state may
+    // overwrite it in place (same pointer) but not overlap it partially
+    const Range ri{(uintptr_t)ex.initial_state, (uintptr_t)ex.initial_state + ns};
+    if (overlap(ri, ro)) return GLA_ERR_ALIAS;
+    if (final_state && (const void*)final_state != (const void*)ex.initial_state &&
+        overlap(ri, Range{(uintptr_t)final_state, (uintptr_t)final_state + ns}))
       return GLA_ERR_ALIAS;
   }
 
   const int n_chunks = (int)((T + kChunk - 1) / kChunk);
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return GLA_ERR_HIP;
-  const int span_chunks = plan_span_chunks(BH, n_chunks, output_slots(dev, dt, d_k, d_v));
+  const int span_chunks =
+      plan_span_chunks(BH, n_chunks, output_slots(dev, dt, d_k, d_v, ex.gate_logits));
   const int n_spans = (n_chunks + span_chunks - 1) / span_chunks;
   if (BH * n_spans > (1LL << 31) - 1) return GLA_ERR_SHAPE;
   if (plan_only != nullptr) {
@@ -128,6 +153,8 @@ int forward(gla::Dtype dt, size_t esize, const void* q, const void* k, const voi
   p.la = la;
   p.out = out;
   p.final_state = final_state;
+  p.initial_state = ex.initial_state;
+  p.inv_tau = ex.gate_logits ? 1.f / ex.tau : 1.f;
   p.B = B;
   p.heads = heads;
   p.H = H;
@@ -152,7 +179,7 @@ int forward(gla::Dtype dt, size_t esize, const void* q, const void* k, const voi
   }
   const hipEvent_t* ev = t_events_set ? t_events : nullptr;
   t_events_set = false;
-  const hipError_t e = gla::launch_forward(dt, d_k, d_v, p, st, ev);
+  const hipError_t e = gla::launch_forward(dt, d_k, d_v, ex.gate_logits, p, st, ev);
   if (ws != nullptr && hipFreeAsync(ws, st) != hipSuccess) return GLA_ERR_HIP;
   return e == hipSuccess ? GLA_OK : GLA_ERR_HIP;
 }
@@ -182,6 +209,23 @@ int gla_chunk_fwd(const void* q, const void* k, const void* v, const void* log_a
   try {
     return forward(gla::Dtype::kF16, 2, q, k, v, log_alpha, scan_dir, B, heads, H, W, d_k, d_v,
                    chunk, out, final_state, stream);
+  } catch (...) {
+    return GLA_ERR_HIP;
+  }
+}
+
+int gla_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* gate, int gate_mode,
+                     float tau, const float* initial_state, int scan_dir, int B, int heads, int H,
+                     int W, int d_k, int d_v, int chunk, void* out, float* final_state,
+                     void* stream) {
+  try {
+    if (gate_mode != GLA_GATE_LOG_ALPHA && gate_mode != GLA_GATE_LOGITS) return GLA_ERR_UNSUPPORTED;
+    Extras ex;
+    ex.gate_logits = gate_mode == GLA_GATE_LOGITS;
+    ex.tau = tau;
+    ex.initial_state = initial_state;
+    return forward(gla::Dtype::kF16, 2, q, k, v, gate, scan_dir, B, heads, H, W, d_k, d_v, chunk,
+                   out, final_state, stream, nullptr, ex);
   } catch (...) {
     return GLA_ERR_HIP;
   }
@@ -239,7 +283,7 @@ const char* gla_status_str(int status) {
   switch (status) {
     case GLA_OK: return "ok";
     case GLA_ERR_NULL: return "a required pointer is NULL";
-    case GLA_ERR_SHAPE: return "B, heads, H or W below 1, or a size too large";
+    case GLA_ERR_SHAPE: return "a size or scalar argument out of range";
     case GLA_ERR_UNSUPPORTED: return "unsupported chunk / d_k / d_v combination";
     case GLA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
     case GLA_ERR_SCAN_DIR: return "scan_dir must be 0..4";
@@ -249,6 +293,6 @@ const char* gla_status_str(int status) {
   }
 }
 
-int gla_version(void) { return 100; }
+int gla_version(void) { return 110; }
 
 }  // extern "C"

@@ -17,6 +17,8 @@ struct FwdParams {
   const void* la;
   void* out;
   float* final_state;   // may be null
+  const float* initial_state;  // [B][heads][d_k][d_v], may be null (zero state)
+  float inv_tau;        // 1 / tau when `la` holds gate logits (fused activation)
   float* span_state;    // [BH][n_spans][d_k][d_v] span summaries, then entry states
   float* span_gate;     // [BH][n_spans][d_k] product of the span's gates
   int B, heads, H, W, T;
@@ -34,15 +36,17 @@ struct FwdParams {
 void fast_div_constants(unsigned int d, unsigned int* m, int* s);
 
 // Output-kernel workgroups resident per CU for this variant (occupancy).
-int output_blocks_per_cu(Dtype dt, int d_k, int d_v);
+int output_blocks_per_cu(Dtype dt, int d_k, int d_v, bool gate_logits);
 
 // True when a kernel family is compiled for this (dtype, d_k, d_v).
 bool has_variant(Dtype dt, int d_k, int d_v);
 
 // Enqueue the span-summary, span-scan and output kernels on `stream`.
 // The caller has validated p and supplied a workspace when n_spans > 1.
-// events: null, or four hipEvent_t recorded around the kernels (see gla.h).
-hipError_t launch_forward(Dtype dt, int d_k, int d_v, const FwdParams& p, hipStream_t stream,
-                          hipEvent_t const* events);
+// events: null, or six hipEvent_t recorded around the kernels (see gla.h).
+// gate_logits: `la` holds gate logits z and the kernels use
+// log alpha = logsigmoid(z) * inv_tau (float16 only).
+hipError_t launch_forward(Dtype dt, int d_k, int d_v, bool gate_logits, const FwdParams& p,
+                          hipStream_t stream, hipEvent_t const* events);
 
 }  // namespace gla

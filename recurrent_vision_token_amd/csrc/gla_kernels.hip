@@ -470,7 +470,9 @@ __global__ __launch_bounds__(kThreads) void span_scan_kernel(FwdParams p) {
   float* const L = p.span_state + (size_t)bh * p.n_spans * DK * DV + e;
   const float* const G = p.span_gate + (size_t)bh * p.n_spans * DK + dim;
 
-  float carry = 0.f;  // state entering the current round
+  // state entering the current round; the first round starts from the
+  // initial state, which the scan also writes as span 0's entry state
+  float carry = p.initial_state ? p.initial_state[(size_t)bh * DK * DV + e] : 0.f;
   for (int r0 = 0; r0 < p.n_spans; r0 += kScanSeg * kScanU) {
     const int s0 = r0 + seg * kScanU;
     float l[kScanU], gg[kScanU];
@@ -540,7 +542,8 @@ __global__ __launch_bounds__(kThreads) void chunk_output_kernel(FwdParams p) {
   StateRegs<DK, DV> st;
   {
     const float* src =
-        (span > 0) ? p.span_state + ((size_t)bh * p.n_spans + span) * DK * DV : nullptr;
+        (p.n_spans > 1) ? p.span_state + ((size_t)bh * p.n_spans + span) * DK * DV
+        : p.initial_state ? p.initial_state + (size_t)bh * DK * DV : nullptr;
 #pragma unroll
     for (int j = 0; j < StateRegs<DK, DV>::NC; ++j) {
       const int col = 16 * (wave + 4 * j) + n16;
@@ -928,6 +931,33 @@ __device__ __forceinline__ f16x8 ld128(const f16* a) { return *reinterpret_cast<
 __device__ __forceinline__ void st64(f16* a, f16x4 x) { *reinterpret_cast<f16x4*>(a) = x; }
 __device__ __forceinline__ f16x4 to_f16(f32x4 x) { return __builtin_convertvector(x, f16x4); }
 
+// Fused gate activation: log alpha = logsigmoid(z) / tau from gate logits z,
+// as min(z, 0) - ln(1 + e^{-|z|}) (no overflow for any z), with ln(1 + t) by
+// its series below t = 1/64, where 1 + t would drop t's low bits.
+__device__ __forceinline__ float logsigmoid_scaled(float z, float inv_tau) {
+  const float t = exp2_fast(-fabsf(z) * 1.4426950408889634f);
+  const float series = t * (1.f - t * (0.5f - t * (1.f / 3.f)));
+  const float l = t < 0.015625f ? series : __builtin_amdgcn_logf(1.f + t) * 0.6931471805599453f;
+  return (fminf(z, 0.f) - l) * inv_tau;
+}
+// Log-alpha of a transposed 16 x 16 read (lane (i, g): rows row0 + 4g + u):
+// the tile value itself, or with GATE the activation of the logits there.
+// Rows at or past `valid` (zero fills) must not decay, so they get 0 rather
+// than logsigmoid(0).
+template <bool GATE>
+__device__ __forceinline__ f16x4 log_alpha_of(f16x4 x, float inv_tau, int row0, int valid) {
+  if constexpr (!GATE) {
+    return x;
+  } else {
+    const int g = (threadIdx.x & 63) >> 4;
+    f32x4 r;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      r[u] = (row0 + 4 * g + u < valid) ? logsigmoid_scaled((float)x[u], inv_tau) : 0.f;
+    return to_f16(r);
+  }
+}
+
 template <int DK, int DV>
 struct StepTiles {
   f16* q;
@@ -942,7 +972,7 @@ __host__ __device__ constexpr int vmcnt_lgkm0_imm(int n) {
   return (n & 15) | (7 << 4) | ((n >> 4) << 14);
 }
 
-template <int DK, int DV>
+template <int DK, int DV, bool GATE>
 __global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 4 : (DK == 128 && DV == 128) ? 1 : 2) void chunk_output_f16_kernel(
     FwdParams p) {
   constexpr int RBK = 2 * DK, RBV = 2 * DV;
@@ -980,7 +1010,8 @@ __global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 4 : (DK == 128 &
   f32x4 st[NR][NC];
   {
     const float* src =
-        (span > 0) ? p.span_state + ((size_t)bh * p.n_spans + span) * DK * DV : nullptr;
+        (p.n_spans > 1) ? p.span_state + ((size_t)bh * p.n_spans + span) * DK * DV
+        : p.initial_state ? p.initial_state + (size_t)bh * DK * DV : nullptr;
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
       const int col = 16 * (wave + 4 * j) + n16;
@@ -1018,7 +1049,7 @@ __global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 4 : (DK == 128 &
   const f16x4 u_hi = upper_incl(kLog2eHi), u_lo = upper_incl(kLog2eLo);
 
   // ---- P: per-dim decays and the scaled operands of the step
-  auto phase_p = [&](const StepTiles<DK, DV>& s) {
+  auto phase_p = [&](const StepTiles<DK, DV>& s, int valid) {
 #pragma unroll
     for (int dbi = 0; dbi < DK / 64; ++dbi) {
       const int db = wave + 4 * dbi;
@@ -1026,7 +1057,7 @@ __global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 4 : (DK == 128 &
       f16x4 lat4[2], q4[2], k4[2];
 #pragma unroll
       for (int I = 0; I < 2; ++I) {
-        lat4[I] = tr_read<RBK>(s.la, 16 * I, 16 * db);
+        lat4[I] = log_alpha_of<GATE>(tr_read<RBK>(s.la, 16 * I, 16 * db), p.inv_tau, 16 * I, valid);
         q4[I] = ld64(s.q + swz<RBK>(16 * I + n16, dim0));
         k4[I] = ld64(s.k + swz<RBK>(16 * I + n16, dim0));
       }
@@ -1123,8 +1154,10 @@ __global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 4 : (DK == 128 &
     }
   };
 
-  auto run_step = [&](const StepTiles<DK, DV>& s, const uint32_t* rows) {
-    phase_p(s);
+  // rows of step `step` inside the span
+  auto valid_rows = [&](int step) { return max(0, min(kStep, t_end - t_begin - kStep * step)); };
+  auto run_step = [&](const StepTiles<DK, DV>& s, const uint32_t* rows, int step) {
+    phase_p(s, valid_rows(step));
     wait_barrier<kLgkmZero>();
     phase_o(s, rows);
   };
@@ -1133,11 +1166,11 @@ __global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 4 : (DK == 128 &
   wait_barrier<vmcnt_imm(0)>();  // the entry state and step 0 have landed
   for (int step = 0; step < n_steps; step += 2) {
     issue(slot1, srow[1], step + 1);
-    run_step(slot0, srow[0]);
+    run_step(slot0, srow[0], step);
     if (step + 1 >= n_steps) break;
     wait_barrier<vmcnt_lgkm0_imm(NSTORE)>();  // step + 1 landed; slot0 free
     issue(slot0, srow[0], step + 2);
-    run_step(slot1, srow[1]);
+    run_step(slot1, srow[1], step + 1);
     if (step + 2 >= n_steps) break;
     wait_barrier<vmcnt_lgkm0_imm(NSTORE)>();
   }
@@ -1189,7 +1222,7 @@ struct SumTile {
   f16* v;
 };
 
-template <int DK, int DV>
+template <int DK, int DV, bool GATE>
 __global__ __launch_bounds__(kThreads) void span_summary_f16_kernel(FwdParams p) {
   // six separate LDS objects, so the compiler's own waits for the LDS-writing
   // loads can tell the tiles apart
@@ -1251,14 +1284,15 @@ __global__ __launch_bounds__(kThreads) void span_summary_f16_kernel(FwdParams p)
     for (int cb = 0; cb < NCB; ++cb) st[d][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  auto fold = [&](const SumTile<DK, DV>& s) {
+  auto fold = [&](const SumTile<DK, DV>& s, int c) {
+    const int valid = min(kChunk, p.T - c * kChunk);
 #pragma unroll
     for (int d = 0; d < NDB; ++d) {
       const int db = wave + 4 * d;
       f16x4 lat[4], kt[4];
 #pragma unroll
       for (int J = 0; J < 4; ++J) {
-        lat[J] = tr_read<RBK>(s.la, 16 * J, 16 * db);
+        lat[J] = log_alpha_of<GATE>(tr_read<RBK>(s.la, 16 * J, 16 * db), p.inv_tau, 16 * J, valid);
         kt[J] = tr_read<RBK>(s.k, 16 * J, 16 * db);
       }
       f32x4 rest[4];
@@ -1293,11 +1327,11 @@ __global__ __launch_bounds__(kThreads) void span_summary_f16_kernel(FwdParams p)
   issue(slot1, c_end - 2);
   for (int c = c_end - 1; c >= c_begin; c -= 2) {
     wait_barrier<vmcnt_imm(NDMA)>();  // every wave's part of slot0 has landed
-    fold(slot0);
+    fold(slot0, c);
     wait_barrier<kLgkmZero>();        // every wave's reads of slot0 are done
     issue(slot0, c - 2);
     wait_barrier<vmcnt_imm(NDMA)>();
-    if (c - 1 >= c_begin) fold(slot1);
+    if (c - 1 >= c_begin) fold(slot1, c - 1);
     wait_barrier<kLgkmZero>();
     issue(slot1, c - 3);
   }
@@ -1321,15 +1355,16 @@ __global__ __launch_bounds__(kThreads) void span_summary_f16_kernel(FwdParams p)
 
 // Kernel choice per element type: float16 runs the MFMA-layout kernels,
 // float32 the generic ones.
-template <class T, int DK, int DV>
+template <class T, int DK, int DV, bool GATE>
 struct Family {
+  static_assert(!GATE, "the fused gate activation is built for float16 only");
   static constexpr auto summary = span_summary_kernel<T, DK, DV>;
   static constexpr auto output = chunk_output_kernel<T, DK, DV>;
 };
-template <int DK, int DV>
-struct Family<f16, DK, DV> {
-  static constexpr auto summary = span_summary_f16_kernel<DK, DV>;
-  static constexpr auto output = chunk_output_f16_kernel<DK, DV>;
+template <int DK, int DV, bool GATE>
+struct Family<f16, DK, DV, GATE> {
+  static constexpr auto summary = span_summary_f16_kernel<DK, DV, GATE>;
+  static constexpr auto output = chunk_output_f16_kernel<DK, DV, GATE>;
 };
 
 // Launch one kernel; with measurement events, the dispatch itself records
@@ -1354,14 +1389,13 @@ hipError_t skip_one(hipStream_t stream, hipEvent_t const* ev, int slot) {
   return hipEventRecord(ev[2 * slot + 1], stream);
 }
 
-template <class T, int DK, int DV>
+template <class T, int DK, int DV, bool GATE>
 hipError_t launch_variant(const FwdParams& p, hipStream_t stream, hipEvent_t const* ev) {
+  using F = Family<T, DK, DV, GATE>;
   const int BH = p.B * p.heads;
   hipError_t e;
   if (p.n_spans > 1) {
-    if ((e = launch_one(Family<T, DK, DV>::summary, dim3(BH * p.n_spans), stream, p, ev, 0)) !=
-        hipSuccess)
-      return e;
+    if ((e = launch_one(F::summary, dim3(BH * p.n_spans), stream, p, ev, 0)) != hipSuccess) return e;
     if ((e = launch_one(span_scan_kernel<DK, DV>, dim3(BH, DK * DV / kScanElems), stream, p, ev,
                         1)) != hipSuccess)
       return e;
@@ -1369,44 +1403,55 @@ hipError_t launch_variant(const FwdParams& p, hipStream_t stream, hipEvent_t con
     if ((e = skip_one(stream, ev, 0)) != hipSuccess) return e;
     if ((e = skip_one(stream, ev, 1)) != hipSuccess) return e;
   }
-  return launch_one(Family<T, DK, DV>::output, dim3(BH * p.n_spans), stream, p, ev, 2);
+  return launch_one(F::output, dim3(BH * p.n_spans), stream, p, ev, 2);
 }
 
-hipError_t launch_forward_impl(Dtype dt, int d_k, int d_v, const FwdParams& p, hipStream_t stream,
-                               hipEvent_t const* ev) {
+template <int DK, int DV>
+hipError_t launch_f16(bool gate_logits, const FwdParams& p, hipStream_t stream, hipEvent_t const* ev) {
+  return gate_logits ? launch_variant<f16, DK, DV, true>(p, stream, ev)
+                     : launch_variant<f16, DK, DV, false>(p, stream, ev);
+}
+
+hipError_t launch_forward_impl(Dtype dt, int d_k, int d_v, bool gate_logits, const FwdParams& p,
+                               hipStream_t stream, hipEvent_t const* ev) {
   if (dt == Dtype::kF16) {
-    if (d_k == 64 && d_v == 64) return launch_variant<f16, 64, 64>(p, stream, ev);
-    if (d_k == 64 && d_v == 128) return launch_variant<f16, 64, 128>(p, stream, ev);
-    if (d_k == 128 && d_v == 64) return launch_variant<f16, 128, 64>(p, stream, ev);
-    if (d_k == 128 && d_v == 128) return launch_variant<f16, 128, 128>(p, stream, ev);
-  } else {
-    if (d_k == 64 && d_v == 64) return launch_variant<float, 64, 64>(p, stream, ev);
-    if (d_k == 64 && d_v == 128) return launch_variant<float, 64, 128>(p, stream, ev);
+    if (d_k == 64 && d_v == 64) return launch_f16<64, 64>(gate_logits, p, stream, ev);
+    if (d_k == 64 && d_v == 128) return launch_f16<64, 128>(gate_logits, p, stream, ev);
+    if (d_k == 128 && d_v == 64) return launch_f16<128, 64>(gate_logits, p, stream, ev);
+    if (d_k == 128 && d_v == 128) return launch_f16<128, 128>(gate_logits, p, stream, ev);
+  } else if (!gate_logits) {
+    if (d_k == 64 && d_v == 64) return launch_variant<float, 64, 64, false>(p, stream, ev);
+    if (d_k == 64 && d_v == 128) return launch_variant<float, 64, 128, false>(p, stream, ev);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-template <class T, int DK, int DV>
+template <class T, int DK, int DV, bool GATE>
 int output_occupancy() {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, Family<T, DK, DV>::output, kThreads, 0) !=
-          hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, Family<T, DK, DV, GATE>::output, kThreads,
+                                                   0) != hipSuccess ||
       n < 1)
     n = 1;
   return n;
 }
 
-int output_blocks_per_cu(Dtype dt, int d_k, int d_v) {
+template <int DK, int DV>
+int f16_occupancy(bool gate_logits) {
+  return gate_logits ? output_occupancy<f16, DK, DV, true>() : output_occupancy<f16, DK, DV, false>();
+}
+
+int output_blocks_per_cu(Dtype dt, int d_k, int d_v, bool gate_logits) {
   if (dt == Dtype::kF16) {
-    if (d_k == 64 && d_v == 64) return output_occupancy<f16, 64, 64>();
-    if (d_k == 64 && d_v == 128) return output_occupancy<f16, 64, 128>();
-    if (d_k == 128 && d_v == 64) return output_occupancy<f16, 128, 64>();
-    if (d_k == 128 && d_v == 128) return output_occupancy<f16, 128, 128>();
+    if (d_k == 64 && d_v == 64) return f16_occupancy<64, 64>(gate_logits);
+    if (d_k == 64 && d_v == 128) return f16_occupancy<64, 128>(gate_logits);
+    if (d_k == 128 && d_v == 64) return f16_occupancy<128, 64>(gate_logits);
+    if (d_k == 128 && d_v == 128) return f16_occupancy<128, 128>(gate_logits);
   } else {
-    if (d_k == 64 && d_v == 64) return output_occupancy<float, 64, 64>();
-    if (d_k == 64 && d_v == 128) return output_occupancy<float, 64, 128>();
+    if (d_k == 64 && d_v == 64) return output_occupancy<float, 64, 64, false>();
+    if (d_k == 64 && d_v == 128) return output_occupancy<float, 64, 128, false>();
   }
   return 1;
 }
@@ -1417,9 +1462,9 @@ bool has_variant(Dtype dt, int d_k, int d_v) {
   return d_k == 64 && (d_v == 64 || d_v == 128);
 }
 
-hipError_t launch_forward(Dtype dt, int d_k, int d_v, const FwdParams& p, hipStream_t stream,
-                          hipEvent_t const* ev) {
-  return launch_forward_impl(dt, d_k, d_v, p, stream, ev);
+hipError_t launch_forward(Dtype dt, int d_k, int d_v, bool gate_logits, const FwdParams& p,
+                          hipStream_t stream, hipEvent_t const* ev) {
+  return launch_forward_impl(dt, d_k, d_v, gate_logits, p, stream, ev);
 }
 
 }  // namespace gla

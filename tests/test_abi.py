@@ -70,6 +70,33 @@ def test_argument_errors(dtype):
     assert call(dtype, fs=OUT + 1024) == -6                  # final_state inside out
 
 
+def call_ex(gate_mode=1, tau=16.0, init=None, fs=FS, out=OUT, **kw):
+    a = dict(q=Q, k=K, v=V, la=LA, scan_dir=0, B=1, heads=2, H=8, W=8, d_k=64, d_v=64, chunk=64)
+    a.update(kw)
+    return _lib.raw_call_ex(a["q"], a["k"], a["v"], a["la"], gate_mode, tau, init, a["scan_dir"],
+                            a["B"], a["heads"], a["H"], a["W"], a["d_k"], a["d_v"], a["chunk"],
+                            out, fs, None)
+
+
+def test_extended_entry_argument_errors():
+    ns = 2 * 64 * 64 * 4                                     # bytes of one state tensor
+    init = P[6]
+    assert call_ex(gate_mode=2) == -3                        # unknown gate mode, checked first
+    assert call_ex(gate_mode=-1, scan_dir=9) == -3
+    for bad in (0.0, -1.0, float("inf"), float("nan"), 1e-45):
+        assert call_ex(gate_mode=1, tau=bad) == -2, bad
+    assert call_ex(gate_mode=0, tau=0.0) not in (-2, -3)     # tau ignored for log_alpha
+    assert call_ex(init=init + 2) == -4                      # misaligned initial state
+    assert call_ex(init=OUT + 64) == -6                      # initial state inside out
+    assert call_ex(init=init, fs=init) not in (-6,)          # in-place state update allowed
+    assert call_ex(init=init, fs=init + ns // 2) == -6       # partial overlap rejected
+    assert call_ex(init=init, fs=init - ns + 4) == -6
+    assert call_ex(init=Q) not in (-6,)                      # may share memory with inputs
+    assert call_ex(q=None) == -1
+    assert call_ex(scan_dir=7) == -5
+    assert call_ex(chunk=32) == -3
+
+
 def test_fp32_entry_rejects_unbuilt_key_dim():
     assert call("fp32", d_k=128) == -3
     assert call("fp16", d_k=128, scan_dir=9) == -5           # direction checked first
