@@ -62,9 +62,13 @@ def kernel_bytes(wl, n_spans):
 
 
 class Runner:
-    """Device copies of a workload's inputs, cycled across calls."""
+    """Device copies of a workload's inputs, cycled across calls.
 
-    def __init__(self, wl, torch, min_sets_bytes=2 * LLC_BYTES):
+    ext=True drives the extended entry point instead: the gate tensor is taken
+    as gate logits (fused activation, tau 16) and every call starts from a
+    stored initial state."""
+
+    def __init__(self, wl, torch, min_sets_bytes=2 * LLC_BYTES, ext=False):
         from recurrent_vision_token_amd.workloads import workload_inputs
         self.torch = torch
         self.wl = wl
@@ -83,18 +87,28 @@ class Runner:
                 q, k, v, la = (torch.from_numpy(x).to(self.dev) for x in host[seed])
                 out = torch.empty(v.shape, dtype=v.dtype, device=self.dev)
                 fs = torch.empty((wl.B, wl.heads, wl.d_k, wl.d_v), dtype=torch.float32, device=self.dev)
-                self.sets.append((q, k, v, la, out, fs, d))
+                init = torch.full((wl.B, wl.heads, wl.d_k, wl.d_v), 0.01, dtype=torch.float32,
+                                  device=self.dev) if ext else None
+                self.sets.append((q, k, v, la, out, fs, d, init))
         self.cursor = 0
         torch.cuda.synchronize()
 
         # raw C-ABI arguments of every set, so the timed loop only marshals ints
         from recurrent_vision_token_amd import _lib
         lib = _lib.load()
-        self.fn = lib.gla_chunk_fwd if wl.dtype == "fp16" else lib.gla_chunk_fwd_f32
         stream = torch.cuda.current_stream(self.dev).cuda_stream
-        self.args = [(q.data_ptr(), k.data_ptr(), v.data_ptr(), la.data_ptr(), d, wl.B, wl.heads,
-                      wl.H, wl.W, wl.d_k, wl.d_v, wl.chunk, out.data_ptr(), fs.data_ptr(), stream)
-                     for (q, k, v, la, out, fs, d) in self.sets]
+        if ext:
+            self.fn = lib.gla_chunk_fwd_ex
+            self.args = [(q.data_ptr(), k.data_ptr(), v.data_ptr(), la.data_ptr(), 1, 16.0,
+                          init.data_ptr(), d, wl.B, wl.heads, wl.H, wl.W, wl.d_k, wl.d_v,
+                          wl.chunk, out.data_ptr(), fs.data_ptr(), stream)
+                         for (q, k, v, la, out, fs, d, init) in self.sets]
+        else:
+            self.fn = lib.gla_chunk_fwd if wl.dtype == "fp16" else lib.gla_chunk_fwd_f32
+            self.args = [(q.data_ptr(), k.data_ptr(), v.data_ptr(), la.data_ptr(), d, wl.B,
+                          wl.heads, wl.H, wl.W, wl.d_k, wl.d_v, wl.chunk, out.data_ptr(),
+                          fs.data_ptr(), stream)
+                         for (q, k, v, la, out, fs, d, _) in self.sets]
 
     def step(self, events=None):
         """One pass of the call list; events: list of 6-event lists, one per call."""
@@ -111,10 +125,10 @@ class Runner:
                 raise RuntimeError("gla_chunk_fwd failed: %d" % rc)
 
 
-def time_workload(wl, torch, steps, warmup):
+def time_workload(wl, torch, steps, warmup, ext=False):
     """Timed loop (no instrumentation), then an event-instrumented pass of the
     same length for the per-kernel durations."""
-    r = Runner(wl, torch)
+    r = Runner(wl, torch, ext=ext)
     ncall = len(wl.calls)
     log("[bench] %s: %d device input sets (%.0f MB), %d calls/step" %
         (wl.name, len(r.sets), len(r.sets) * algorithmic(wl)["bytes"] / 1e6, ncall))
@@ -203,12 +217,16 @@ def describe(wl):
              wl.gate_std, sorted(set(s for s, _ in wl.calls)), dirs, len(wl.calls)))
 
 
-def summarize(wl, ms_step, mean):
+def summarize(wl, ms_step, mean, ext=False):
     alg = algorithmic(wl)
+    if ext:  # the initial state is read once more per (b, h)
+        alg["bytes"] += wl.B * wl.heads * wl.d_k * wl.d_v * 4
     ncall = len(wl.calls)
     tokens_step = ncall * wl.B * wl.T
     spans = n_spans_of(wl)
     kb = kernel_bytes(wl, spans)
+    if ext:
+        kb["span_scan" if spans > 1 else "chunk_output"] += wl.B * wl.heads * wl.d_k * wl.d_v * 4
     present = [k for k in kb if mean[k] > 0]
     dom = max(present, key=lambda k: mean[k])
     ach = kb[dom] / (mean[dom] * 1e-3) / 1e9
@@ -287,6 +305,8 @@ def main():
     ap.add_argument("--workload", default="hires16.4k")
     ap.add_argument("--secondary", default="gtr1.6k", help="'' to skip")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ext", action="store_true",
+                    help="skip the extended entry point (fused gate + initial state) line")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run one device-to-device copy of this many MB (a kernel of "
                          "known traffic, to scale hardware byte counters against)")
@@ -340,6 +360,17 @@ def main():
         log("[bench] %s: %.3f ms/step, %.3e tokens/s, GPU %.2f us/call" %
             (wl2.name, ms2, s2["value"], s2["path"]["gpu_us_per_call"]))
 
+    ext = None
+    if not args.no_ext and wl.dtype == "fp16":
+        _, ms3, mean3 = time_workload(wl, torch, args.steps, args.warmup, ext=True)
+        s3 = summarize(wl, ms3, mean3, ext=True)
+        ext = {"entry": "gla_chunk_fwd_ex: gate logits with fused logsigmoid(z)/16 activation, "
+                        "initial state", "workload": describe(wl), "value": s3["value"],
+               "unit": "tokens/s", "ms_per_step": round(ms3, 4), "roofline": s3["roofline"],
+               "path": s3["path"]}
+        log("[bench] %s extended entry: %.3f ms/step, %.3e tokens/s, kernels %s" %
+            (wl.name, ms3, s3["value"], s3["path"]["kernel_us"]))
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, runner.host)
@@ -364,6 +395,7 @@ def main():
         "path": main_sum["path"],
         "cpu_baseline": cpu,
         "secondary": secondary,
+        "fused_gate_initial_state": ext,
     }
     print(json.dumps(line), flush=True)
 
