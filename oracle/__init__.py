@@ -1,4 +1,4 @@
-"""CPU oracle (test infrastructure only): see gla_oracle.py."""
+"""CPU oracle (test infrastructure only): see gla_oracle.py and swiglu_oracle.py."""
 
 from .gla_oracle import (  # noqa: F401
     SCAN_B2T,
@@ -11,3 +11,4 @@ from .gla_oracle import (  # noqa: F401
     log_alpha_from_logits,
     scan_order,
 )
+from .swiglu_oracle import depthwise_conv3x3, silu, spatial_swiglu  # noqa: F401

@@ -85,3 +85,50 @@ def workload_inputs(wl: Workload, seed: int, B=None, heads=None):
     """Inputs of one call of a named workload (B / heads may be overridden)."""
     return make_inputs(B or wl.B, heads or wl.heads, wl.H, wl.W, wl.d_k, wl.d_v,
                        wl.dtype, wl.gate_std, seed)
+
+
+# Spatial SwiGLU step on the same grids.  The hidden width is 8/3 of the model
+# width (the usual SwiGLU ratio): 768 = 12 heads x 64 -> 2048 channels at
+# 16.4K; 1024 = 16 x 64 -> 2736 (8/3 x 1024 rounded up to a multiple of 16)
+# at 768x768.
+@dataclass(frozen=True)
+class SwigluWorkload:
+    name: str
+    B: int
+    H: int
+    W: int
+    C: int
+    seed: int
+
+    @property
+    def T(self):
+        return self.H * self.W
+
+
+SWIGLU_WORKLOADS = {
+    "swiglu_hires16.4k": SwigluWorkload("swiglu_hires16.4k", 1, 128, 128, 2048, 5),
+    "swiglu_img768": SwigluWorkload("swiglu_img768", 1, 48, 48, 2736, 6),
+}
+
+
+def make_swiglu_inputs(B, H, W, C, seed=0, bias=True, packed=False):
+    """Return (gate, value, weight, bias) as float16 numpy arrays.
+
+    Recipe: numpy.random.default_rng(seed); gate and value ~ N(0, 1) drawn in
+    that order, [B, H, W, C] each (the pre-activations of two linear
+    projections of normalised tokens); weight [C, 3, 3] and bias [C] ~
+    U(-1/3, 1/3), the default initialisation bound 1/sqrt(fan_in) of a 3x3
+    depthwise layer (fan_in = 9).  With packed=True gate and value are
+    returned as two views into one [B, H, W, 2C] array (gate first), the
+    layout of a single fused up-projection.
+    """
+    rng = np.random.default_rng(seed)
+    shp = (B, H, W, C)
+    g = rng.standard_normal(shp, dtype=np.float32).astype(np.float16)
+    v = rng.standard_normal(shp, dtype=np.float32).astype(np.float16)
+    w = rng.uniform(-1.0 / 3.0, 1.0 / 3.0, (C, 3, 3)).astype(np.float16)
+    b = rng.uniform(-1.0 / 3.0, 1.0 / 3.0, C).astype(np.float16) if bias else None
+    if packed:
+        both = np.concatenate([g, v], axis=-1)
+        g, v = both[..., :C], both[..., C:]
+    return g, v, w, b
