@@ -1,6 +1,7 @@
 /*
  * gla.h - C ABI of the chunkwise gated-linear-attention forward pass with
- * key-only decay over an H x W patch grid, for AMD Instinct MI355X (gfx950).
+ * key-only decay over an H x W patch grid, for AMD Instinct MI355X (gfx950),
+ * and of the Spatial SwiGLU step that follows it in each block.
  *
  * Operation (GTR news write-up, tokendh.com, section "What linear attention
  * saves": a running d_k x d_v summary, a learnable forget gate, decay on the
@@ -72,10 +73,11 @@ enum {
   GLA_ERR_SHAPE = -2,         /* B, heads, H or W < 1, a size overflows, one
                                  sequence's rows of a tensor reach 2 GiB, or tau
                                  is not positive and finite                      */
-  GLA_ERR_UNSUPPORTED = -3,   /* d_k / d_v / chunk combination not built        */
+  GLA_ERR_UNSUPPORTED = -3,   /* d_k / d_v / chunk combination not built, or a
+                                 channel count that is not a multiple of 8       */
   GLA_ERR_ALIGN = -4,         /* a tensor pointer is not 16-byte aligned        */
   GLA_ERR_SCAN_DIR = -5,      /* scan_dir outside 0..4                          */
-  GLA_ERR_ALIAS = -6,         /* out or final_state overlaps another tensor     */
+  GLA_ERR_ALIAS = -6,         /* an output overlaps another tensor              */
   GLA_ERR_HIP = -7            /* a HIP runtime call failed while enqueueing     */
 };
 
@@ -143,13 +145,54 @@ int gla_plan_spans(int use_f32, int B, int heads, int H, int W, int d_k, int d_v
                    int* span_chunks, int* n_spans);
 
 /*
+ * Spatial SwiGLU step (float16), the other token mixer of each GTR block:
+ *
+ *   out[b,y,x,c] = silu(gate[b,y,x,c]) *
+ *                  (bias[c] + sum_{i,j=0..2} weight[c][i][j] * value[b, y+i-1, x+j-1, c])
+ *
+ * SwiGLU with a 3x3 depthwise convolution inserted in its value branch, each
+ * channel filtered with its own kernel, so that a patch sees its eight grid
+ * neighbours directly (GTR news write-up, tokendh.com, section "The flaw of
+ * one-way scanning and GTR's fix", the Spatial SwiGLU and depthwise
+ * convolution notes).  silu(g) = g / (1 + exp(-g)).  Readings where the pages
+ * are silent: zero padding of one cell, stride 1 (output grid = input grid);
+ * taps applied as a cross-correlation (tap (i, j) weighs the neighbour at
+ * row offset i-1, column offset j-1, as deep-learning convolution layers do);
+ * an optional per-channel bias before the gate multiplies.  The projections
+ * that produce gate and value, and the one after, are dense matrix products
+ * and not part of this call.
+ *
+ * Layout (float16, channels last):
+ *   gate, value : B*H*W tokens in grid order [B][H][W], token n at element
+ *                 n * ld_in; its C channels contiguous.  ld_in = C for two
+ *                 separate tensors, ld_in = 2C for the halves of one fused
+ *                 [B][H][W][2C] projection (value = gate + C).
+ *   weight      : [C][3][3] (a [C][1][3][3] layer weight as is).
+ *   bias        : [C], or NULL for none.
+ *   out         : [B][H][W][C], contiguous.
+ * Arithmetic: each tap is a float16 x float16 product summed in float32, the
+ * gate activation in float32, out rounded to nearest even.
+ * Supported: C and ld_in multiples of 8, ld_in >= C; one image's rows
+ * (H*W*ld_in elements) below 2 GiB.  Pointers 16-byte aligned.  out may not
+ * overlap any input (a tile still reads its neighbours' values).
+ * Ownership and errors as gla_chunk_fwd: asynchronous on `stream`, the caller
+ * owns every buffer, all checks before any HIP call, nothing enqueued on
+ * failure.  GLA_ERR_NULL (gate, value, weight or out NULL), GLA_ERR_SHAPE
+ * (a size < 1, ld_in < C, a size overflow), GLA_ERR_UNSUPPORTED (C or ld_in
+ * not a multiple of 8), GLA_ERR_ALIGN, GLA_ERR_ALIAS.
+ */
+int gla_spatial_swiglu(const void* gate, const void* value, int ld_in, const void* weight,
+                       const void* bias, int B, int H, int W, int C, void* out, void* stream);
+
+/*
  * Measurement hook (for benchmarks and profilers, not needed for computing).
  * events: n = 6 hipEvent_t handles (as void*), or n = 0 to clear.  The next
  * forward call made by the calling thread has each of its three kernels (span
  * summary, span scan, output) record a start / stop pair, events[2i] and
  * events[2i+1], from its own dispatch (hipExtLaunchKernelGGL), so the interval
  * is that kernel's execution; a kernel the call does not run (no span split)
- * records its pair back to back.  The hook then clears itself.  The caller
+ * records its pair back to back.  A gla_spatial_swiglu call instead records
+ * events[0] / events[1] around its one kernel.  The hook then clears itself.  The caller
  * owns the events.  Returns GLA_ERR_NULL if n = 6 and a handle is NULL,
  * GLA_ERR_SHAPE if n is neither 0 nor 6.
  */

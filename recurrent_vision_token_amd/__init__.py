@@ -5,14 +5,16 @@ as hand-written HIP kernels for AMD Instinct MI355X (gfx950).
     out, final_state = gla_chunk_fwd_ex(q, k, v, gate_logits, scan_dir,
                                         gate_mode="logits", tau=16.0,
                                         initial_state=state)
+    h = spatial_swiglu(gate, value, weight, bias)   # the block's SwiGLU mixer
 
 The heavy lifting is in libgla.so (C ABI: include/gla.h); this package is a
 thin binding around it plus the seeded synthetic workloads.
 """
 
-from ._lib import GlaError, gla_chunk_fwd, gla_chunk_fwd_ex, load, status_str  # noqa: F401
+from ._lib import (GlaError, gla_chunk_fwd, gla_chunk_fwd_ex, load, spatial_swiglu,  # noqa: F401
+                   status_str)
 
 SCAN_L2R, SCAN_R2L, SCAN_T2B, SCAN_B2T, SCAN_ROTATE_BATCH = 0, 1, 2, 3, 4
 
-__all__ = ["gla_chunk_fwd", "gla_chunk_fwd_ex", "GlaError", "load", "status_str", "SCAN_L2R",
+__all__ = ["gla_chunk_fwd", "gla_chunk_fwd_ex", "spatial_swiglu", "GlaError", "load", "status_str", "SCAN_L2R",
            "SCAN_R2L", "SCAN_T2B", "SCAN_B2T", "SCAN_ROTATE_BATCH"]

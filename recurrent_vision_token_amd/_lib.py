@@ -18,7 +18,7 @@ STATUS = {
     -4: "GLA_ERR_ALIGN", -5: "GLA_ERR_SCAN_DIR", -6: "GLA_ERR_ALIAS", -7: "GLA_ERR_HIP",
 }
 EXPORTED = ("gla_chunk_fwd", "gla_chunk_fwd_ex", "gla_chunk_fwd_f32", "gla_plan_spans",
-            "gla_set_kernel_events", "gla_status_str", "gla_version")
+            "gla_set_kernel_events", "gla_spatial_swiglu", "gla_status_str", "gla_version")
 GATE_MODES = {"log_alpha": 0, "logits": 1}
 
 _lib = None
@@ -47,6 +47,8 @@ def load():
         fn.restype = ctypes.c_int
     lib.gla_chunk_fwd_ex.argtypes = [vp, vp, vp, vp, i, ctypes.c_float, vp] + sig[4:]
     lib.gla_chunk_fwd_ex.restype = ctypes.c_int
+    lib.gla_spatial_swiglu.argtypes = [vp, vp, i, vp, vp, i, i, i, i, vp, vp]
+    lib.gla_spatial_swiglu.restype = ctypes.c_int
     lib.gla_status_str.argtypes = [ctypes.c_int]
     lib.gla_status_str.restype = ctypes.c_char_p
     lib.gla_plan_spans.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i)]
@@ -164,6 +166,52 @@ def gla_chunk_fwd_ex(q, k, v, gate, scan_dir, gate_mode="log_alpha", tau=16.0,
     if rc != GLA_OK:
         raise GlaError(rc, status_str(rc))
     return out, final_state
+
+
+def raw_call_swiglu(gate, value, ld_in, weight, bias, B, H, W, C, out, stream):
+    """Call gla_spatial_swiglu with integer pointers; returns the status code."""
+    return load().gla_spatial_swiglu(gate, value, ld_in, weight, bias, B, H, W, C, out, stream)
+
+
+def spatial_swiglu(gate, value, weight, bias=None, out=None, stream=None):
+    """Spatial SwiGLU step: silu(gate) * (3x3 depthwise conv of value + bias).
+
+    gate, value: float16 device tensors [B, H, W, C] with unit channel stride
+    and equal, dense token strides (ld >= C elements between tokens: C for
+    separate tensors, 2C for the two halves of one [B, H, W, 2C] projection).
+    weight: float16 [C, 3, 3] or [C, 1, 3, 3]; bias: float16 [C] or None.
+    Returns out, float16 [B, H, W, C] contiguous.
+    """
+    import torch
+
+    tens = [gate, value, weight] + ([bias] if bias is not None else [])
+    if not all(isinstance(t, torch.Tensor) and t.is_cuda for t in tens):
+        raise ValueError("gate, value, weight, bias must be device tensors")
+    if any(t.dtype != torch.float16 for t in tens):
+        raise ValueError("spatial_swiglu takes float16 tensors")
+    if gate.dim() != 4 or value.shape != gate.shape:
+        raise ValueError("gate and value must be [B, H, W, C] of one shape")
+    B, H, W, C = gate.shape
+    ld = gate.stride(2)
+    dense = (ld, W * ld, H * W * ld)
+    for t in (gate, value):
+        if t.stride(3) != 1 or (t.stride(2), t.stride(1), t.stride(0)) != dense:
+            raise ValueError("gate and value need unit channel stride and equal dense token "
+                             "strides")
+    if weight.numel() != C * 9 or not weight.is_contiguous():
+        raise ValueError("weight must be contiguous [C, 3, 3]")
+    if bias is not None and (bias.numel() != C or not bias.is_contiguous()):
+        raise ValueError("bias must be contiguous [C]")
+    if out is None:
+        out = torch.empty((B, H, W, C), dtype=torch.float16, device=gate.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(gate.device).cuda_stream
+    rc = raw_call_swiglu(gate.data_ptr(), value.data_ptr(), ld, weight.data_ptr(),
+                         bias.data_ptr() if bias is not None else None, B, H, W, C,
+                         out.data_ptr(), stream)
+    if rc != GLA_OK:
+        raise GlaError(rc, status_str(rc))
+    return out
 
 
 def set_kernel_events(handles):

@@ -242,6 +242,58 @@ int gla_chunk_fwd_f32(const float* q, const float* k, const float* v, const floa
   }
 }
 
+int gla_spatial_swiglu(const void* gate, const void* value, int ld_in, const void* weight,
+                       const void* bias, int B, int H, int W, int C, void* out, void* stream) {
+  try {
+    if (!gate || !value || !weight || !out) return GLA_ERR_NULL;
+    if (B < 1 || H < 1 || W < 1 || C < 1 || ld_in < C) return GLA_ERR_SHAPE;
+    if (C % 8 != 0 || ld_in % 8 != 0) return GLA_ERR_UNSUPPORTED;
+    const long long HW = (long long)H * W;
+    // one image's tokens are addressed with 32-bit byte offsets
+    if (HW * ld_in * 2 >= (1LL << 31) || (long long)C * 18 >= (1LL << 31)) return GLA_ERR_SHAPE;
+    const void* tens[5] = {gate, value, weight, bias, out};
+    for (const void* t : tens)
+      if (reinterpret_cast<uintptr_t>(t) % 16 != 0) return GLA_ERR_ALIGN;
+    gla::SwigluParams p{};
+    p.rows_per_tile = gla::swiglu_rows_per_tile(H);
+    p.row_tiles = (int)((H + p.rows_per_tile - 1) / p.rows_per_tile);
+    p.col_tiles = (W + 31) / 32;
+    p.ch_tiles = (C + 63) / 64;
+    const long long tiles = (long long)B * p.row_tiles * p.col_tiles * p.ch_tiles;
+    if (tiles > (1LL << 31) - 1) return GLA_ERR_SHAPE;
+    // the output may overlap none of the inputs (its neighbours' values are
+    // still to be read when a tile writes)
+    const uintptr_t n_in = (uintptr_t)((B * HW - 1) * ld_in + C) * 2;
+    const uintptr_t n_out = (uintptr_t)(B * HW * C) * 2;
+    const Range ro{(uintptr_t)out, (uintptr_t)out + n_out};
+    if (overlap(ro, Range{(uintptr_t)gate, (uintptr_t)gate + n_in}) ||
+        overlap(ro, Range{(uintptr_t)value, (uintptr_t)value + n_in}) ||
+        overlap(ro, Range{(uintptr_t)weight, (uintptr_t)weight + (uintptr_t)C * 18}) ||
+        (bias && overlap(ro, Range{(uintptr_t)bias, (uintptr_t)bias + (uintptr_t)C * 2})))
+      return GLA_ERR_ALIAS;
+    p.gate = gate;
+    p.value = value;
+    p.weight = weight;
+    p.bias = bias;
+    p.out = out;
+    p.B = B;
+    p.H = H;
+    p.W = W;
+    p.C = C;
+    p.ld_in = ld_in;
+    p.ld_out = C;
+    p.n_tiles = (int)tiles;
+    const bool ev = t_events_set;
+    t_events_set = false;
+    const hipError_t e = gla::launch_spatial_swiglu(p, static_cast<hipStream_t>(stream),
+                                                    ev ? t_events[0] : nullptr,
+                                                    ev ? t_events[1] : nullptr);
+    return e == hipSuccess ? GLA_OK : GLA_ERR_HIP;
+  } catch (...) {
+    return GLA_ERR_HIP;
+  }
+}
+
 int gla_plan_spans(int use_f32, int B, int heads, int H, int W, int d_k, int d_v, int chunk,
                    int* span_chunks, int* n_spans) {
   if (span_chunks == nullptr || n_spans == nullptr) return GLA_ERR_NULL;
@@ -284,15 +336,15 @@ const char* gla_status_str(int status) {
     case GLA_OK: return "ok";
     case GLA_ERR_NULL: return "a required pointer is NULL";
     case GLA_ERR_SHAPE: return "a size or scalar argument out of range";
-    case GLA_ERR_UNSUPPORTED: return "unsupported chunk / d_k / d_v combination";
+    case GLA_ERR_UNSUPPORTED: return "unsupported chunk / d_k / d_v / channel combination";
     case GLA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
     case GLA_ERR_SCAN_DIR: return "scan_dir must be 0..4";
-    case GLA_ERR_ALIAS: return "out or final_state overlaps another tensor";
+    case GLA_ERR_ALIAS: return "an output overlaps another tensor";
     case GLA_ERR_HIP: return "a HIP runtime call failed";
     default: return "unknown status";
   }
 }
 
-int gla_version(void) { return 110; }
+int gla_version(void) { return 120; }
 
 }  // extern "C"

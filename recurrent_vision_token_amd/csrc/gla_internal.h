@@ -49,4 +49,26 @@ bool has_variant(Dtype dt, int d_k, int d_v);
 hipError_t launch_forward(Dtype dt, int d_k, int d_v, bool gate_logits, const FwdParams& p,
                           hipStream_t stream, hipEvent_t const* events);
 
+// One call of the Spatial SwiGLU step (float16), already validated on the host.
+struct SwigluParams {
+  const void* gate;     // [B][H][W] tokens of ld_in elements, first C used
+  const void* value;    // same layout as gate
+  const void* weight;   // [C][3][3]
+  const void* bias;     // [C] or null (no bias)
+  void* out;            // [B][H][W] tokens of ld_out elements
+  int B, H, W, C;
+  int ld_in, ld_out;
+  int rows_per_tile;    // 8, 16 or 32 grid rows per workgroup
+  int row_tiles, col_tiles, ch_tiles;
+  int n_tiles;          // B * row_tiles * col_tiles * ch_tiles workgroups
+};
+
+// Grid rows per workgroup tile for an H-row grid.
+int swiglu_rows_per_tile(int H);
+
+// Enqueue the Spatial SwiGLU kernel on `stream`; start / stop (may be null)
+// are recorded around its dispatch.
+hipError_t launch_spatial_swiglu(const SwigluParams& p, hipStream_t stream, hipEvent_t start,
+                                 hipEvent_t stop);
+
 }  // namespace gla
