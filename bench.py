@@ -11,6 +11,10 @@ so that the bytes touched between two reuses of a copy exceed the 256 MB
 last-level (Infinity) cache: every call streams from HBM as a real layer
 stack would, instead of re-reading cache-resident data.
 
+Beside it, the same protocol times the block's other token mixer, the
+Spatial SwiGLU step (gla_spatial_swiglu) on the 16.4K grid with 2048 hidden
+channels, reported under "spatial_swiglu".
+
 Prints ONE JSON line on stdout; details go to stderr.
 """
 
@@ -30,6 +34,12 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 MFMA, published
 LLC_BYTES = 256 << 20           # Infinity Cache
 KERNEL_SRC = os.path.join(ROOT, "recurrent_vision_token_amd", "csrc", "gla_kernels.hip")
+SWIGLU_SRC = os.path.join(ROOT, "recurrent_vision_token_amd", "csrc", "swiglu_kernels.hip")
+KERNEL_NAMES = ("span_summary", "span_scan", "chunk_output", "spatial_swiglu")
+
+
+def source_of(kernel):
+    return SWIGLU_SRC if kernel == "spatial_swiglu" else KERNEL_SRC
 
 
 def log(*a):
@@ -167,6 +177,115 @@ def time_workload(wl, torch, steps, warmup, ext=False):
     return r, ms_step, mean
 
 
+SWIGLU_WORKLOAD = "swiglu_hires16.4k"
+
+
+def swiglu_bytes(swl):
+    """Algorithmic bytes of one Spatial SwiGLU call: read gate and value, write
+    out (2 bytes per channel each, 6 * C per token), plus the 3x3 weights and
+    the bias."""
+    return swl.B * swl.T * swl.C * 2 * 3 + swl.C * 10 * 2
+
+
+class SwigluRunner:
+    """Device copies of the Spatial SwiGLU inputs, cycled across calls like Runner."""
+
+    def __init__(self, swl, torch, min_sets_bytes=2 * LLC_BYTES):
+        from recurrent_vision_token_amd import _lib
+        from recurrent_vision_token_amd.workloads import make_swiglu_inputs
+        self.swl = swl
+        dev = torch.device("cuda:0")
+        self.host = make_swiglu_inputs(swl.B, swl.H, swl.W, swl.C, seed=swl.seed)
+        g, v, w, b = self.host
+        wt, bt = torch.from_numpy(w).to(dev), torch.from_numpy(b).to(dev)
+        reps = max(2, math.ceil(min_sets_bytes / swiglu_bytes(swl)))
+        self.sets = []
+        for _ in range(reps):
+            gt, vt = torch.from_numpy(g).to(dev), torch.from_numpy(v).to(dev)
+            self.sets.append((gt, vt, torch.empty_like(gt)))
+        self.keep = (wt, bt)
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        self.fn = _lib.load().gla_spatial_swiglu
+        self.args = [(gt.data_ptr(), vt.data_ptr(), swl.C, wt.data_ptr(), bt.data_ptr(), swl.B,
+                      swl.H, swl.W, swl.C, o.data_ptr(), stream) for (gt, vt, o) in self.sets]
+        self.cursor = 0
+        torch.cuda.synchronize()
+
+    def step(self, events=None):
+        from recurrent_vision_token_amd import _lib
+        a = self.args[self.cursor]
+        self.cursor = (self.cursor + 1) % len(self.sets)
+        if events is not None:
+            rc = _lib.set_kernel_events([e.cuda_event for e in events])
+            if rc != 0:
+                raise RuntimeError("gla_set_kernel_events failed: %d" % rc)
+        rc = self.fn(*a)
+        if rc != 0:
+            raise RuntimeError("gla_spatial_swiglu failed: %d" % rc)
+
+
+def time_swiglu(swl, torch, steps, warmup):
+    """Wall-clock loop of single calls, then an event-instrumented pass for the
+    kernel's own duration (recorded by its dispatch, on the call's stream)."""
+    r = SwigluRunner(swl, torch)
+    log("[bench] %s: %d device input sets (%.0f MB)" %
+        (swl.name, len(r.sets), len(r.sets) * swiglu_bytes(swl) / 1e6))
+    for _ in range(warmup):
+        r.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        r.step()
+    torch.cuda.synchronize()
+    ms_call = (time.perf_counter() - t0) * 1e3 / steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    stream = torch.cuda.current_stream()
+    for per_call in evs:
+        for e in per_call:
+            e.record(stream)
+    torch.cuda.synchronize()
+    for e in evs:
+        r.step(e)
+    torch.cuda.synchronize()
+    k_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / len(evs)
+    return r, ms_call, k_ms
+
+
+def swiglu_cpu_baseline(swl, host):
+    """The Spatial SwiGLU oracle as it stands (numpy float64) on the full image."""
+    from oracle import spatial_swiglu
+    g, v, w, b = host
+    t0 = time.perf_counter()
+    c0 = time.process_time()
+    spatial_swiglu(g, v, w, b)
+    wall = time.perf_counter() - t0
+    cores = max(1, int(round((time.process_time() - c0) / wall)))
+    return {"value": swl.B * swl.T / wall, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": "one full call (%s, numpy float64), %.1f s wall" % (swl.name, wall)}
+
+
+def swiglu_summary(swl, ms_call, k_ms, cpu):
+    nb = swiglu_bytes(swl)
+    ach = nb / (k_ms * 1e-3) / 1e9
+    return {
+        "entry": "gla_spatial_swiglu: silu(gate) * (3x3 depthwise conv of value + bias)",
+        "workload": "%s: B=%d, %dx%d grid (%d tokens), C=%d channels, fp16, gate/value "
+                    "~ N(0,1), weights/bias ~ U(-1/3, 1/3), seed %d" %
+                    (swl.name, swl.B, swl.H, swl.W, swl.T, swl.C, swl.seed),
+        "value": swl.B * swl.T / (ms_call * 1e-3),
+        "unit": "tokens/s",
+        "ms_per_call": round(ms_call, 4),
+        "dtype": "f16",
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic_from_profiles(SWIGLU_WORKLOAD, "spatial_swiglu")
+                     if swl.name == SWIGLU_WORKLOAD else None,
+                     "kernel": "spatial_swiglu", "algorithmic_bytes_per_launch": nb,
+                     "avg_launch_us": round(k_ms * 1e3, 2)},
+        "cpu_baseline": cpu,
+    }
+
+
 def n_spans_of(wl):
     from recurrent_vision_token_amd import _lib
     return _lib.plan_spans(wl.dtype, wl.B, wl.heads, wl.H, wl.W, wl.d_k, wl.d_v, wl.chunk)[1]
@@ -179,10 +298,11 @@ def traffic_from_profiles(wl_name, kernel):
         return None
     try:
         rec = json.load(open(path))
-        src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
-        if rec.get("kernel_source_sha256") != src_hash:
+        src_hash = hashlib.sha256(open(source_of(kernel), "rb").read()).hexdigest()
+        k = rec["kernels"][kernel]
+        if k.get("kernel_source_sha256", rec.get("kernel_source_sha256")) != src_hash:
             return None
-        return rec["kernels"][kernel]["hbm_bytes_per_launch"]
+        return k["hbm_bytes_per_launch"]
     except Exception:
         return None
 
@@ -263,7 +383,7 @@ def counters_to_traffic(fetch_dir, write_dir, copy_mb, workload):
             if row["Counter_Name"] != counter:
                 continue
             name = row["Kernel_Name"]
-            key = next((k for k in ("span_summary", "span_scan", "chunk_output") if k in name), None)
+            key = next((k for k in KERNEL_NAMES if k in name), None)
             if key is None and "copy" in name.lower():
                 key = "copy"
             if key is not None:
@@ -275,26 +395,31 @@ def counters_to_traffic(fetch_dir, write_dir, copy_mb, workload):
     copy_bytes = copy_mb << 20
     f_scale = copy_bytes / (f["copy"] * 1024.0)
     w_scale = copy_bytes / (w["copy"] * 1024.0)
-    src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
-    rec = {"workload": workload, "kernel_source_sha256": src_hash, "copy_bytes": copy_bytes,
-           "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
     lines = ["| kernel | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | HBM read (MB) | HBM write (MB) | total (MB) |",
              "|---|---|---|---|---|---|"]
-    for k in ("span_summary", "span_scan", "chunk_output"):
+    recs = {}
+    for k in KERNEL_NAMES:
         if k not in f:
             continue
         rd = f[k] * 1024.0 * f_scale
         wr = w[k] * 1024.0 * w_scale
+        wl_name = SWIGLU_WORKLOAD if k == "spatial_swiglu" else workload
+        rec = recs.setdefault(wl_name, {"workload": wl_name, "copy_bytes": copy_bytes,
+                                        "fetch_scale": f_scale, "write_scale": w_scale,
+                                        "kernels": {}})
         rec["kernels"][k] = {"fetch_kib": f[k], "write_kib": w[k], "hbm_read_bytes": rd,
-                             "hbm_write_bytes": wr, "hbm_bytes_per_launch": rd + wr}
+                             "hbm_write_bytes": wr, "hbm_bytes_per_launch": rd + wr,
+                             "kernel_source_sha256":
+                                 hashlib.sha256(open(source_of(k), "rb").read()).hexdigest()}
         lines.append("| %s | %.0f | %.0f | %.1f | %.1f | %.1f |" % (k, f[k], w[k], rd / 1e6, wr / 1e6,
                                                                   (rd + wr) / 1e6))
-    out = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
-    json.dump(rec, open(out, "w"), indent=1)
+    for wl_name, rec in recs.items():
+        out = os.path.join(ROOT, "profiles", "traffic_%s.json" % wl_name)
+        json.dump(rec, open(out, "w"), indent=1)
+        print("wrote", out)
     print("copy kernel of %d bytes: FETCH_SIZE %.0f KiB (scale %.3f), WRITE_SIZE %.0f KiB (scale %.3f)"
           % (copy_bytes, f["copy"], f_scale, w["copy"], w_scale))
     print("\n".join(lines))
-    print("wrote", out)
 
 
 def main():
@@ -307,6 +432,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ext", action="store_true",
                     help="skip the extended entry point (fused gate + initial state) line")
+    ap.add_argument("--swiglu", default=SWIGLU_WORKLOAD,
+                    help="Spatial SwiGLU workload to time beside the attention path ('' to skip)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run one device-to-device copy of this many MB (a kernel of "
                          "known traffic, to scale hardware byte counters against)")
@@ -371,6 +498,17 @@ def main():
         log("[bench] %s extended entry: %.3f ms/step, %.3e tokens/s, kernels %s" %
             (wl.name, ms3, s3["value"], s3["path"]["kernel_us"]))
 
+    swiglu = None
+    if args.swiglu:
+        from recurrent_vision_token_amd.workloads import SWIGLU_WORKLOADS
+        swl = SWIGLU_WORKLOADS[args.swiglu]
+        srun, ms_sw, k_sw = time_swiglu(swl, torch, max(20, args.steps), max(5, args.warmup))
+        sw_cpu = None if args.no_cpu_baseline else swiglu_cpu_baseline(swl, srun.host)
+        swiglu = swiglu_summary(swl, ms_sw, k_sw, sw_cpu)
+        log("[bench] %s: %.2f us/call wall, kernel %.2f us, %.3e tokens/s, %.0f GB/s" %
+            (swl.name, ms_sw * 1e3, k_sw * 1e3, swiglu["value"], swiglu["roofline"]["achieved"]))
+        del srun
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, runner.host)
@@ -396,6 +534,7 @@ def main():
         "cpu_baseline": cpu,
         "secondary": secondary,
         "fused_gate_initial_state": ext,
+        "spatial_swiglu": swiglu,
     }
     print(json.dumps(line), flush=True)
 

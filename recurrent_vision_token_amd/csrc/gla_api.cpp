@@ -255,12 +255,11 @@ int gla_spatial_swiglu(const void* gate, const void* value, int ld_in, const voi
     for (const void* t : tens)
       if (reinterpret_cast<uintptr_t>(t) % 16 != 0) return GLA_ERR_ALIGN;
     gla::SwigluParams p{};
-    p.rows_per_tile = gla::swiglu_rows_per_tile(H);
-    p.row_tiles = (int)((H + p.rows_per_tile - 1) / p.rows_per_tile);
-    p.col_tiles = (W + 31) / 32;
-    p.ch_tiles = (C + 63) / 64;
-    const long long tiles = (long long)B * p.row_tiles * p.col_tiles * p.ch_tiles;
-    if (tiles > (1LL << 31) - 1) return GLA_ERR_SHAPE;
+    p.B = B;
+    p.H = H;
+    p.W = W;
+    p.C = C;
+    if (!gla::swiglu_plan(p)) return GLA_ERR_SHAPE;
     // the output may overlap none of the inputs (its neighbours' values are
     // still to be read when a tile writes)
     const uintptr_t n_in = (uintptr_t)((B * HW - 1) * ld_in + C) * 2;
@@ -276,13 +275,8 @@ int gla_spatial_swiglu(const void* gate, const void* value, int ld_in, const voi
     p.weight = weight;
     p.bias = bias;
     p.out = out;
-    p.B = B;
-    p.H = H;
-    p.W = W;
-    p.C = C;
     p.ld_in = ld_in;
     p.ld_out = C;
-    p.n_tiles = (int)tiles;
     const bool ev = t_events_set;
     t_events_set = false;
     const hipError_t e = gla::launch_spatial_swiglu(p, static_cast<hipStream_t>(stream),

@@ -63,8 +63,9 @@ struct SwigluParams {
   int n_tiles;          // B * row_tiles * col_tiles * ch_tiles workgroups
 };
 
-// Grid rows per workgroup tile for an H-row grid.
-int swiglu_rows_per_tile(int H);
+// Fill the work split of p (rows_per_tile, the tile counts and n_tiles) from
+// B, H, W, C; false when the launch would be too large.
+bool swiglu_plan(SwigluParams& p);
 
 // Enqueue the Spatial SwiGLU kernel on `stream`; start / stop (may be null)
 // are recorded around its dispatch.

@@ -19,7 +19,10 @@
 //   * each lane walks down its column keeping the 3x3 window of V in registers:
 //     per output row it loads one new row of V (its own column and the two
 //     neighbours - the neighbours are lines the same wave fetches, so they hit
-//     in L1/L2) and one row of G, one row ahead of the arithmetic;
+//     in L1/L2) and one row of G, two rows ahead of the arithmetic;
+//   * G is read and h written non-temporally (each touched once), which keeps
+//     the cached V rows that neighbouring tiles read again as halo; this is
+//     worth about a fifth of the kernel time on a 16K-token grid;
 //   * outside the grid, past the channel count, or past the tile's rows, the
 //     byte offset is set beyond the buffer, so the buffer load returns zeros
 //     (which is exactly the zero padding) and the store is dropped - no branch;
@@ -32,6 +35,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "gla_internal.h"
 
@@ -53,8 +57,13 @@ constexpr int kRawBufferWord3 = 0x00020000;  // untyped buffer, 32-bit elements
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRawBufferWord3);
 }
+// Cache policy of the loads and stores: kStream marks an access non-temporal,
+// for data touched once (the gate rows and the outputs), so it does not push
+// out the value rows that neighbouring tiles read again as their halo.
+constexpr int kKeep = 0, kStream = 2;
+template <int POLICY = kKeep>
 __device__ __forceinline__ f16x8 load8(rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  return __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, POLICY));
 }
 
 // silu(g) = g / (1 + e^-g), with e^-g as a hardware exp2; for g below about
@@ -92,11 +101,6 @@ __global__ __launch_bounds__(kThreads) void spatial_swiglu_f16_kernel(SwigluPara
   const f16* gate = static_cast<const f16*>(p.gate) + img * p.ld_in;
   const f16* value = static_cast<const f16*>(p.value) + img * p.ld_in;
   f16* out = static_cast<f16*>(p.out) + img * p.ld_out;
-  // the rows of one image; the last token's row ends at its C-th channel
-  const uint32_t in_bytes = (uint32_t)(((size_t)(p.H * W - 1) * p.ld_in + p.C) * 2);
-  const uint32_t out_bytes = (uint32_t)(((size_t)(p.H * W - 1) * p.ld_out + p.C) * 2);
-  const rsrc_t rg = make_rsrc(gate, in_bytes), rv = make_rsrc(value, in_bytes);
-  const rsrc_t ro = make_rsrc(out, out_bytes);
 
   // weights [C][3][3] and bias [C]: this lane's 8 channels, 72 + 8 halves
   const rsrc_t rw = make_rsrc(p.weight, (uint32_t)p.C * 18);
@@ -107,35 +111,54 @@ __global__ __launch_bounds__(kThreads) void spatial_swiglu_f16_kernel(SwigluPara
   for (int k = 0; k < 9; ++k) wr[k] = load8(rw, ch_ok ? (uint32_t)c0 * 18 + 16 * k : kOut);
   const f16x8 bias = load8(rb, ch_ok ? (uint32_t)c0 * 2 : kOut);
 
-  // byte offset of channel c0 at (row, col), or past the buffer when the cell
-  // is outside the grid or the lane has no channels
+  // Addressing: one buffer resource per grid row (wave-uniform, built on the
+  // scalar unit each step), whose range is that row's tokens - or nothing for
+  // a row outside the grid, so the whole row reads zeros - and three lane
+  // offsets fixed for the whole walk, set past the row for a neighbour
+  // outside the grid or a lane without channels.
   const bool x_ok = ch_ok && x < W, xm_ok = x_ok && x >= 1, xp_ok = x_ok && x + 1 < W;
-  const uint32_t ld2 = (uint32_t)p.ld_in * 2, lo2 = (uint32_t)p.ld_out * 2;
-  const uint32_t colm = (uint32_t)(x - 1) * ld2 + c0 * 2;
-  const uint32_t row_stride = (uint32_t)W * ld2;
-  auto voff = [&](int row, int dx, bool ok) -> uint32_t {
-    return (ok && row >= 0 && row < p.H) ? (uint32_t)row * row_stride + colm + dx * ld2 : kOut;
+  const uint32_t ld2 = (uint32_t)p.ld_in * 2;
+  const uint32_t oc = (uint32_t)x * ld2 + (uint32_t)c0 * 2;
+  const uint32_t om = xm_ok ? oc - ld2 : kOut, o0 = x_ok ? oc : kOut, op = xp_ok ? oc + ld2 : kOut;
+  const uint32_t os = x_ok ? ((uint32_t)x * p.ld_out + c0) * 2 : kOut;
+  const size_t in_row = (size_t)W * p.ld_in, out_row = (size_t)W * p.ld_out;
+  const uint32_t in_row_bytes = (uint32_t)(((W - 1) * (size_t)p.ld_in + p.C) * 2);
+  const uint32_t out_row_bytes = (uint32_t)(((W - 1) * (size_t)p.ld_out + p.C) * 2);
+  const int H = p.H;
+  auto row_of = [&](const f16* base, int row) -> rsrc_t {
+    const bool in = row >= 0 && row < H;
+    return make_rsrc(base + (in ? row : 0) * in_row, in ? in_row_bytes : 0u);
   };
 
   // window rows: a = y-1, m = y, d = y+1; columns 0/1/2 = x-1, x, x+1
-  f16x8 a0 = load8(rv, voff(r0 - 1, 0, xm_ok)), a1 = load8(rv, voff(r0 - 1, 1, x_ok)),
-        a2 = load8(rv, voff(r0 - 1, 2, xp_ok));
-  f16x8 m0 = load8(rv, voff(r0, 0, xm_ok)), m1 = load8(rv, voff(r0, 1, x_ok)),
-        m2 = load8(rv, voff(r0, 2, xp_ok));
-  f16x8 d0 = load8(rv, voff(r0 + 1, 0, xm_ok)), d1 = load8(rv, voff(r0 + 1, 1, x_ok)),
-        d2 = load8(rv, voff(r0 + 1, 2, xp_ok));
-  f16x8 g = load8(rg, voff(r0, 1, x_ok));
+  rsrc_t rr = row_of(value, r0 - 1);
+  f16x8 a0 = load8(rr, om), a1 = load8(rr, o0), a2 = load8(rr, op);
+  rr = row_of(value, r0);
+  f16x8 m0 = load8(rr, om), m1 = load8(rr, o0), m2 = load8(rr, op);
+  rr = row_of(value, r0 + 1);
+  f16x8 d0 = load8(rr, om), d1 = load8(rr, o0), d2 = load8(rr, op);
+  f16x8 g = load8<kStream>(row_of(gate, r0), o0);
+  rr = row_of(value, r0 + 2 <= r1 ? r0 + 2 : -1);
+  f16x8 n0 = load8(rr, om), n1 = load8(rr, o0), n2 = load8(rr, op);
+  f16x8 gn = load8<kStream>(row_of(gate, r0 + 1 < r1 ? r0 + 1 : -1), o0);
 
 #pragma unroll
   for (int s = 0; s < ROWS; ++s) {
     const int y = r0 + s;
     if (y >= r1) break;
     // one row ahead: V row y+2 (needed up to row r1) and G row y+1 (up to r1-1)
-    const int yv = y + 2 <= r1 ? y + 2 : -1;
-    const int yg = y + 1 < r1 ? y + 1 : -1;
-    const f16x8 n0 = load8(rv, voff(yv, 0, xm_ok)), n1 = load8(rv, voff(yv, 1, x_ok)),
-                n2 = load8(rv, voff(yv, 2, xp_ok));
-    const f16x8 gn = load8(rg, voff(yg, 1, x_ok));
+    const rsrc_t rn = row_of(value, y + 3 <= r1 ? y + 3 : -1);
+    const f16x8 nn0 = load8(rn, om), nn1 = load8(rn, o0), nn2 = load8(rn, op);
+    const f16x8 gnn = load8<kStream>(row_of(gate, y + 2 < r1 ? y + 2 : -1), o0);
+
+    // Fresh names for the window and the weights in every row step: each
+    // half is then used by exactly one tap per step, so every tap becomes one
+    // mixed-precision FMA on the packed halves instead of a float32 copy of
+    // the window and weights being kept live across steps.
+#pragma unroll
+    for (int k = 0; k < 9; ++k) asm volatile("" : "+v"(wr[k]));
+    asm volatile("" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(m0), "+v"(m1), "+v"(m2));
+    asm volatile("" : "+v"(d0), "+v"(d1), "+v"(d2));
 
     f16x8 h;
 #pragma unroll
@@ -149,19 +172,36 @@ __global__ __launch_bounds__(kThreads) void spatial_swiglu_f16_kernel(SwigluPara
 #undef TAP
       h[c] = (f16)(silu((float)g[c]) * acc);
     }
-    const uint32_t so = x_ok ? ((uint32_t)y * W + x) * lo2 + c0 * 2 : kOut;
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, h), ro, so, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, h),
+                                           make_rsrc(out + y * out_row, out_row_bytes), os, 0, kStream);
 
     a0 = m0; a1 = m1; a2 = m2;
     m0 = d0; m1 = d1; m2 = d2;
     d0 = n0; d1 = n1; d2 = n2;
+    n0 = nn0; n1 = nn1; n2 = nn2;
     g = gn;
+    gn = gnn;
   }
 }
 
 }  // namespace
 
-int swiglu_rows_per_tile(int H) { return H >= 64 ? 16 : 8; }
+bool swiglu_plan(SwigluParams& p) {
+  int rows = p.H >= 64 ? 16 : 8;
+  const char* e = std::getenv("GLA_SWIGLU_ROWS");  // tuning override: 8, 16 or 32
+  if (e != nullptr) {
+    const int r = std::atoi(e);
+    if (r == 8 || r == 16 || r == 32) rows = r;
+  }
+  p.rows_per_tile = rows;
+  p.row_tiles = (p.H + rows - 1) / rows;
+  p.col_tiles = (p.W + kTileCols - 1) / kTileCols;
+  p.ch_tiles = (p.C + kTileCh - 1) / kTileCh;
+  const long long tiles = (long long)p.B * p.row_tiles * p.col_tiles * p.ch_tiles;
+  if (tiles > (1LL << 31) - 1) return false;
+  p.n_tiles = (int)tiles;
+  return true;
+}
 
 hipError_t launch_spatial_swiglu(const SwigluParams& p, hipStream_t stream, hipEvent_t start,
                                  hipEvent_t stop) {

@@ -43,3 +43,32 @@ def test_fast_division(d):
     if d <= 300:
         for t in range(0, 70 * d):
             assert fast_div(t, m, s) == t // d
+
+
+# The Spatial SwiGLU kernel numbers its tiles so that each of the 8 XCDs,
+# which receive launch slots round robin (slot i on XCD i % 8), gets one
+# contiguous run of tiles: slot i -> x * (n // 8) + min(x, n % 8) + i // 8
+# with x = i % 8.  Restated here and checked to be a permutation whose runs
+# are contiguous per XCD.
+def xcd_tile(i, n):
+    per, rem = n // 8, n % 8
+    x = i % 8
+    return x * per + min(x, rem) + i // 8
+
+
+@pytest.mark.parametrize("n", list(range(1, 70)) + [255, 256, 257, 1023, 1024, 2048, 4099])
+def test_xcd_contiguous_tile_order_is_a_permutation(n):
+    tiles = [xcd_tile(i, n) for i in range(n)]
+    assert sorted(tiles) == list(range(n))
+    for x in range(8):
+        run = sorted(t for i, t in enumerate(tiles) if i % 8 == x)
+        assert run == list(range(run[0], run[0] + len(run))) if run else True
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    root = __import__("os").path.dirname(__import__("os").path.dirname(__file__))
+    r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], cwd=root,
+                       stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
