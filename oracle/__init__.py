@@ -1,4 +1,4 @@
-"""CPU oracle (test infrastructure only): see gla_oracle.py and swiglu_oracle.py."""
+"""CPU oracle (test infrastructure only): see gla_oracle.py, swiglu_oracle.py and saga_oracle.py."""
 
 from .gla_oracle import (  # noqa: F401
     SCAN_B2T,
@@ -12,3 +12,4 @@ from .gla_oracle import (  # noqa: F401
     scan_order,
 )
 from .swiglu_oracle import depthwise_conv3x3, silu, spatial_swiglu  # noqa: F401
+from .saga_oracle import saga_forward, saga_kv  # noqa: F401

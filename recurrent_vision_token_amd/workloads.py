@@ -132,3 +132,41 @@ def make_swiglu_inputs(B, H, W, C, seed=0, bias=True, packed=False):
         both = np.concatenate([g, v], axis=-1)
         g, v = both[..., :C], both[..., C:]
     return g, v, w, b
+
+
+# SAGA-style non-causal gated linear attention on the same token counts.
+@dataclass(frozen=True)
+class SagaWorkload:
+    name: str
+    B: int
+    heads: int
+    N: int
+    d_k: int
+    d_v: int
+    seed: int
+
+
+SAGA_WORKLOADS = {
+    "saga_hires16.4k": SagaWorkload("saga_hires16.4k", 1, 12, 128 * 128, 64, 64, 7),
+    "saga_batched": SagaWorkload("saga_batched", 32, 16, 64 * 64, 128, 64, 8),
+}
+
+
+def make_saga_inputs(B, heads, N, d_k, d_v, seed=0):
+    """Return (q, k, v, a, b) as float16 numpy arrays.
+
+    Recipe: numpy.random.default_rng(seed) draws z_q, z_k, z_v, z_a, z_b
+    ~ N(0, 1) (float32) in that order; q, k, v = z / 8 as for the attention
+    workloads; the gates a = sigmoid(z_a) [B, heads, N, d_k] and
+    b = sigmoid(z_b) [B, heads, N, d_v], values in (0, 1).
+    """
+    rng = np.random.default_rng(seed)
+    sk, sv = (B, heads, N, d_k), (B, heads, N, d_v)
+    q = (rng.standard_normal(sk, dtype=np.float32) * np.float32(0.125)).astype(np.float16)
+    k = (rng.standard_normal(sk, dtype=np.float32) * np.float32(0.125)).astype(np.float16)
+    v = (rng.standard_normal(sv, dtype=np.float32) * np.float32(0.125)).astype(np.float16)
+    za = rng.standard_normal(sk, dtype=np.float32)
+    zb = rng.standard_normal(sv, dtype=np.float32)
+    a = (np.float32(1.0) / (np.float32(1.0) + np.exp(-za))).astype(np.float16)
+    b = (np.float32(1.0) / (np.float32(1.0) + np.exp(-zb))).astype(np.float16)
+    return q, k, v, a, b
