@@ -1,7 +1,8 @@
 /*
  * gla.h - C ABI of the chunkwise gated-linear-attention forward pass with
  * key-only decay over an H x W patch grid, for AMD Instinct MI355X (gfx950),
- * and of the Spatial SwiGLU step that follows it in each block.
+ * of the Spatial SwiGLU step that follows it in each block, and of the
+ * SAGA-style non-causal gated linear attention.
  *
  * Operation (GTR news write-up, tokendh.com, section "What linear attention
  * saves": a running d_k x d_v summary, a learnable forget gate, decay on the
@@ -183,6 +184,38 @@ int gla_plan_spans(int use_f32, int B, int heads, int H, int W, int d_k, int d_v
  */
 int gla_spatial_swiglu(const void* gate, const void* value, int ld_in, const void* weight,
                        const void* bias, int B, int H, int W, int C, void* out, void* stream);
+
+/*
+ * SAGA-style non-causal gated linear attention (float16):
+ *
+ *   KV = (K * A)^T (V * B),   O = Q KV      per (batch, head)
+ *
+ * Each token's key-value map k_i^T v_i is scaled element by element by a gate
+ * alpha_i^T beta_i before the maps are summed; by the Hadamard-product
+ * identity the gate is applied to K and V instead, so no per-token map is
+ * formed (SAGA summary, gist.science, Methodology sections A and B).  Every
+ * token attends to all N tokens of its sequence (no causal order).  The gates
+ * are inputs (produced upstream); no normaliser or scale is applied.
+ *
+ * Layout (dense, contiguous, 16-byte aligned, float16):
+ *   q, k, alpha : [B][heads][N][d_k]
+ *   v, beta, out: [B][heads][N][d_v]
+ *   kv          : [B][heads][d_k][d_v] float32, the gated maps; may be NULL.
+ * Arithmetic: k*alpha and v*beta rounded to float16, maps accumulated on
+ * 16-bit MFMA tiles in float32 (span partials summed in a fixed order, so
+ * results are bitwise reproducible), then read as float16 scaled by a power
+ * of two per 16 value columns; out rounded to nearest even.
+ * Supported: d_k, d_v in {64, 128}; one sequence's rows of a tensor below
+ * 2 GiB.  out and kv may not overlap any input or each other.
+ * Ownership and errors as gla_chunk_fwd (a stream-ordered workspace is taken
+ * and released on `stream`): GLA_ERR_NULL, GLA_ERR_SHAPE, GLA_ERR_UNSUPPORTED
+ * (d_k / d_v), GLA_ERR_ALIGN, GLA_ERR_ALIAS.  With the measurement hook armed
+ * the accumulation, reduction and output kernels record event pairs 0, 1, 2
+ * (the reduction's pair back to back when one span covers a sequence).
+ */
+int gla_saga_fwd(const void* q, const void* k, const void* v, const void* alpha,
+                 const void* beta, int B, int heads, int N, int d_k, int d_v, void* out, float* kv,
+                 void* stream);
 
 /*
  * Measurement hook (for benchmarks and profilers, not needed for computing).

@@ -6,15 +6,16 @@ as hand-written HIP kernels for AMD Instinct MI355X (gfx950).
                                         gate_mode="logits", tau=16.0,
                                         initial_state=state)
     h = spatial_swiglu(gate, value, weight, bias)   # the block's SwiGLU mixer
+    o, kv = saga_fwd(q, k, v, alpha, beta)          # non-causal gated linear attention
 
 The heavy lifting is in libgla.so (C ABI: include/gla.h); this package is a
 thin binding around it plus the seeded synthetic workloads.
 """
 
-from ._lib import (GlaError, gla_chunk_fwd, gla_chunk_fwd_ex, load, spatial_swiglu,  # noqa: F401
-                   status_str)
+from ._lib import (GlaError, gla_chunk_fwd, gla_chunk_fwd_ex, load, saga_fwd,  # noqa: F401
+                   spatial_swiglu, status_str)
 
 SCAN_L2R, SCAN_R2L, SCAN_T2B, SCAN_B2T, SCAN_ROTATE_BATCH = 0, 1, 2, 3, 4
 
-__all__ = ["gla_chunk_fwd", "gla_chunk_fwd_ex", "spatial_swiglu", "GlaError", "load", "status_str", "SCAN_L2R",
+__all__ = ["gla_chunk_fwd", "gla_chunk_fwd_ex", "spatial_swiglu", "saga_fwd", "GlaError", "load", "status_str", "SCAN_L2R",
            "SCAN_R2L", "SCAN_T2B", "SCAN_B2T", "SCAN_ROTATE_BATCH"]

@@ -18,7 +18,8 @@ STATUS = {
     -4: "GLA_ERR_ALIGN", -5: "GLA_ERR_SCAN_DIR", -6: "GLA_ERR_ALIAS", -7: "GLA_ERR_HIP",
 }
 EXPORTED = ("gla_chunk_fwd", "gla_chunk_fwd_ex", "gla_chunk_fwd_f32", "gla_plan_spans",
-            "gla_set_kernel_events", "gla_spatial_swiglu", "gla_status_str", "gla_version")
+            "gla_saga_fwd", "gla_set_kernel_events", "gla_spatial_swiglu", "gla_status_str",
+            "gla_version")
 GATE_MODES = {"log_alpha": 0, "logits": 1}
 
 _lib = None
@@ -48,6 +49,8 @@ def load():
     lib.gla_chunk_fwd_ex.argtypes = [vp, vp, vp, vp, i, ctypes.c_float, vp] + sig[4:]
     lib.gla_chunk_fwd_ex.restype = ctypes.c_int
     lib.gla_spatial_swiglu.argtypes = [vp, vp, i, vp, vp, i, i, i, i, vp, vp]
+    lib.gla_saga_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp]
+    lib.gla_saga_fwd.restype = ctypes.c_int
     lib.gla_spatial_swiglu.restype = ctypes.c_int
     lib.gla_status_str.argtypes = [ctypes.c_int]
     lib.gla_status_str.restype = ctypes.c_char_p
@@ -212,6 +215,50 @@ def spatial_swiglu(gate, value, weight, bias=None, out=None, stream=None):
     if rc != GLA_OK:
         raise GlaError(rc, status_str(rc))
     return out
+
+
+def raw_call_saga(q, k, v, alpha, beta, B, heads, N, d_k, d_v, out, kv, stream):
+    """Call gla_saga_fwd with integer pointers; returns the status code."""
+    return load().gla_saga_fwd(q, k, v, alpha, beta, B, heads, N, d_k, d_v, out, kv, stream)
+
+
+def saga_fwd(q, k, v, alpha, beta, out=None, kv=None, want_kv=False, stream=None):
+    """SAGA-style non-causal gated linear attention O = Q [(K * A)^T (V * B)].
+
+    q, k, alpha: float16 [B, heads, N, d_k]; v, beta: float16 [B, heads, N, d_v];
+    contiguous, on one device.  Returns (out float16 [B, heads, N, d_v], kv),
+    kv the float32 gated key-value maps [B, heads, d_k, d_v] when want_kv (or a
+    kv tensor is passed), else None.
+    """
+    import torch
+
+    tens = (q, k, v, alpha, beta)
+    if not all(isinstance(t, torch.Tensor) and t.is_cuda for t in tens):
+        raise ValueError("q, k, v, alpha, beta must be device tensors")
+    if any(t.dtype != torch.float16 for t in tens):
+        raise ValueError("saga_fwd takes float16 tensors")
+    if q.dim() != 4:
+        raise ValueError("expected [B, heads, N, d] tensors")
+    B, heads, N, d_k = q.shape
+    d_v = v.shape[-1]
+    if (k.shape != q.shape or alpha.shape != q.shape or tuple(v.shape[:3]) != (B, heads, N)
+            or beta.shape != v.shape):
+        raise ValueError("shape mismatch among q, k, v, alpha, beta")
+    if not all(t.is_contiguous() for t in tens):
+        raise ValueError("tensors must be contiguous")
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, heads, N, d_v), dtype=torch.float16, device=dev)
+    if kv is None and want_kv:
+        kv = torch.empty((B, heads, d_k, d_v), dtype=torch.float32, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = raw_call_saga(q.data_ptr(), k.data_ptr(), v.data_ptr(), alpha.data_ptr(), beta.data_ptr(),
+                       B, heads, N, d_k, d_v, out.data_ptr(),
+                       kv.data_ptr() if kv is not None else None, stream)
+    if rc != GLA_OK:
+        raise GlaError(rc, status_str(rc))
+    return out, kv
 
 
 def set_kernel_events(handles):

@@ -288,6 +288,81 @@ int gla_spatial_swiglu(const void* gate, const void* value, int ld_in, const voi
   }
 }
 
+int gla_saga_fwd(const void* q, const void* k, const void* v, const void* alpha,
+                 const void* beta, int B, int heads, int N, int d_k, int d_v, void* out, float* kv,
+                 void* stream) {
+  try {
+    if (!q || !k || !v || !alpha || !beta || !out) return GLA_ERR_NULL;
+    if (B < 1 || heads < 1 || N < 1 || d_k < 1 || d_v < 1) return GLA_ERR_SHAPE;
+    if (!gla::saga_has_variant(d_k, d_v)) return GLA_ERR_UNSUPPORTED;
+    const long long BH = (long long)B * heads;
+    const long long dmax = d_k > d_v ? d_k : d_v;
+    // one sequence's rows of one tensor are addressed with 32-bit byte offsets
+    if ((long long)N * dmax * 2 >= (1LL << 31) || BH > (1LL << 30)) return GLA_ERR_SHAPE;
+    const void* tens[6] = {q, k, v, alpha, beta, out};
+    for (const void* t : tens)
+      if (reinterpret_cast<uintptr_t>(t) % 16 != 0) return GLA_ERR_ALIGN;
+    if (kv && reinterpret_cast<uintptr_t>(kv) % 16 != 0) return GLA_ERR_ALIGN;
+    const uintptr_t nk = (uintptr_t)(BH * N * d_k) * 2, nv = (uintptr_t)(BH * N * d_v) * 2;
+    const Range ins[5] = {{(uintptr_t)q, (uintptr_t)q + nk}, {(uintptr_t)k, (uintptr_t)k + nk},
+                          {(uintptr_t)v, (uintptr_t)v + nv}, {(uintptr_t)alpha, (uintptr_t)alpha + nk},
+                          {(uintptr_t)beta, (uintptr_t)beta + nv}};
+    const Range ro{(uintptr_t)out, (uintptr_t)out + nv};
+    for (const Range& r : ins)
+      if (overlap(ro, r)) return GLA_ERR_ALIAS;
+    if (kv) {
+      const Range rk{(uintptr_t)kv, (uintptr_t)kv + (uintptr_t)(BH * d_k * d_v) * sizeof(float)};
+      if (overlap(rk, ro)) return GLA_ERR_ALIAS;
+      for (const Range& r : ins)
+        if (overlap(rk, r)) return GLA_ERR_ALIAS;
+    }
+
+    gla::SagaParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.a = alpha;
+    p.b = beta;
+    p.out = out;
+    p.B = B;
+    p.heads = heads;
+    p.N = N;
+    p.d_k = d_k;
+    p.d_v = d_v;
+    const int ct = gla::saga_chunk_tokens(), ot = gla::saga_out_tokens();
+    p.n_chunks = (N + ct - 1) / ct;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return GLA_ERR_HIP;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    // about two accumulation workgroups per CU: spans of whole chunks
+    const long long want = (2LL * cus + BH - 1) / BH;
+    const int spans = (int)(want < 1 ? 1 : (want > p.n_chunks ? p.n_chunks : want));
+    p.span_chunks = (p.n_chunks + spans - 1) / spans;
+    p.n_spans = (p.n_chunks + p.span_chunks - 1) / p.span_chunks;
+    p.n_tblocks = (N + ot - 1) / ot;
+    if (BH * p.n_spans > (1LL << 31) - 1 || BH * p.n_tblocks > (1LL << 31) - 1) return GLA_ERR_SHAPE;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const size_t map = (size_t)d_k * d_v;
+    const size_t ws_floats = (kv ? 0 : BH * map) + (p.n_spans > 1 ? BH * p.n_spans * map : 0);
+    void* ws = nullptr;
+    if (ws_floats > 0 && hipMallocAsync(&ws, ws_floats * sizeof(float), st) != hipSuccess)
+      return GLA_ERR_HIP;
+    float* wsf = static_cast<float*>(ws);
+    p.kv = kv ? kv : wsf;
+    p.partial = p.n_spans > 1 ? (kv ? wsf : wsf + BH * map) : nullptr;
+    const hipEvent_t* ev = t_events_set ? t_events : nullptr;
+    t_events_set = false;
+    const hipError_t e = gla::launch_saga(p, st, ev);
+    if (ws != nullptr && hipFreeAsync(ws, st) != hipSuccess) return GLA_ERR_HIP;
+    return e == hipSuccess ? GLA_OK : GLA_ERR_HIP;
+  } catch (...) {
+    return GLA_ERR_HIP;
+  }
+}
+
 int gla_plan_spans(int use_f32, int B, int heads, int H, int W, int d_k, int d_v, int chunk,
                    int* span_chunks, int* n_spans) {
   if (span_chunks == nullptr || n_spans == nullptr) return GLA_ERR_NULL;
@@ -339,6 +414,6 @@ const char* gla_status_str(int status) {
   }
 }
 
-int gla_version(void) { return 120; }
+int gla_version(void) { return 130; }
 
 }  // extern "C"

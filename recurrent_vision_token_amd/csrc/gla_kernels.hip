@@ -37,17 +37,11 @@
 #include <stdint.h>
 #include <type_traits>
 
+#include "gla_device.h"
 #include "gla_internal.h"
 
 namespace gla {
 namespace {
-
-typedef _Float16 f16;
-typedef f16 f16x8 __attribute__((ext_vector_type(8)));
-typedef f16 f16x4 __attribute__((ext_vector_type(4)));
-typedef f16 f16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kChunk = 64;     // tokens per chunk
 constexpr int kSub = 16;       // tokens per sub-block (one MFMA tile edge)
@@ -126,15 +120,7 @@ __device__ __forceinline__ uint4 sel(bool c, uint4 a, uint4 b) {
 // stores.  Rows past the span or the sequence thus need no branch and no
 // select, every load is issued unconditionally, and each wait for a staged
 // tile counts exactly the loads issued after it.
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 constexpr uint32_t kNoRow = 0x80000000u;     // beyond every sequence (its rows span < 2 GiB)
-constexpr int kRawBufferWord3 = 0x00020000;  // untyped buffer, 32-bit elements (gfx9 family)
-
-__device__ __forceinline__ rsrc_t seq_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRawBufferWord3);
-}
 __device__ __forceinline__ uint4 bload(rsrc_t r, uint32_t off) {
   const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
   return make_uint4(x[0], x[1], x[2], x[3]);
@@ -161,15 +147,6 @@ __device__ __forceinline__ SeqBufs seq_bufs(const FwdParams& p, int bh) {
   return s;
 }
 
-__device__ __forceinline__ f32x4 mma32(f16x8 a, f16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mma16(f16x4 a, f16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mma4(float a, float b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
 
 // Pair index of sub-block pair (I, J), J < I, in the factor table.
 __device__ __forceinline__ constexpr int pair_index(int I, int J) { return I * (I - 1) / 2 + J; }
@@ -796,7 +773,6 @@ __device__ __forceinline__ float row_bcast15(float x) {
                                                              0xF, 0xF, false));
 }
 
-__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // log2(e) split into two binary16 values whose sum is log2(e) to ~1e-7.
 constexpr float kLog2eHi = 1.4423828125f;          // fp16(log2 e)
@@ -813,36 +789,8 @@ __device__ __forceinline__ f16x4 upper_incl(float v) {
   return r;
 }
 
-// ---------------------------------------------------------------------------
-// Row-major chunk tiles in LDS, filled straight from memory by buffer loads
-// that write LDS: one wave instruction moves 1 KB, lane l's 16 bytes landing at
-// byte 16 l of the block, and a lane whose offset is out of range writes zeros.
-// A tile row holds one token's d values (RB = 2d bytes); its 16-byte piece p is
-// stored at piece p ^ (row & 7), which spreads row reads and the transposed
-// reads below evenly over the LDS banks.
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __fp16 lds_h4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
 
-// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
-// lgkmcnt 11:8): at most n vector-memory operations outstanding, or no LDS
-// operation outstanding.
-__host__ __device__ constexpr int vmcnt_imm(int n) {
-  return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14);
-}
-constexpr int kLgkmZero = 15 | (7 << 4) | (0 << 8) | (3 << 14);
-
-// Waits and barriers are explicit around the LDS-writing loads: the fence in
-// __syncthreads would wait for every such load in flight, including the ones
-// filling the other buffer.  The empty asm statements keep the compiler from
-// moving memory accesses across the wait and the barrier.
-template <int WAITCNT>
-__device__ __forceinline__ void wait_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(WAITCNT);
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
+// Chunk tiles in LDS are filled by the LDS-writing loads of gla_device.h.
 // Source offset of this lane's 16 bytes in block `blk` (1 KB) of a tile with
 // RB-byte rows; rows of chunk-local tokens at or past `valid` get an offset
 // past the buffer, so they read as zero.  Branch-free on purpose: a lane-
@@ -870,28 +818,6 @@ __device__ __forceinline__ uint32_t dma_offset_cell(int blk, int t0, int valid, 
   *first_piece = pp == 0;
   return (cell * RB + (uint32_t)((pp ^ (r & 7)) * 16)) | flag;
 }
-__device__ __forceinline__ void dma16(rsrc_t src, f16* block, uint32_t off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void_t*)block, 16, off, 0, 0, 0);
-}
-
-// Transposed read of the 16 x 16 block at (row0, col0) of a swizzled tile
-// (ds_read_b64_tr_b16): lane (i, g) = (lane % 16, lane / 16) receives rows
-// row0 + 4g .. row0 + 4g + 3 of column col0 + i, i.e. the MFMA operand that
-// reduces over rows.  Lane j of each 16-lane group addresses row 4g + j / 4,
-// columns 4 (j % 4) .. + 3 of the block.
-template <int RB>
-__device__ __forceinline__ f16x4 tr_read(const f16* tile, int row0, int col0) {
-  const int lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
-  const int row = row0 + 4 * g + (j >> 2);
-  const int col = col0 + 4 * (j & 3);
-  const f16* a = tile + row * (RB / 2) + (((col >> 3) ^ (row & 7)) << 3) + (col & 4);
-  const lds_h4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4f16((__attribute__((address_space(3))) lds_h4_t*)(lds_void_t*)a);
-  return __builtin_bit_cast(f16x4, x);
-}
-
-__device__ __forceinline__ f16x8 cat8(f16x4 a, f16x4 b) {
-  return f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
 
 // ---------------------------------------------------------------------------
 // Output kernel, float16.  The span is walked in 32-token steps (two 16-token
@@ -914,11 +840,6 @@ __device__ __forceinline__ f16x8 cat8(f16x4 a, f16x4 b) {
 // 16x16 reads (or two 16x16 accumulator tiles) deliver.
 constexpr int kStep = 32;
 
-// element offset of (row, col) in a swizzled tile with RB-byte rows (col % 4 == 0)
-template <int RB>
-__device__ __forceinline__ int swz(int row, int col) {
-  return row * (RB / 2) + (((col >> 3) ^ (row & 7)) << 3) + (col & 7);
-}
 // Column of key dim d (d % 4 == 0, four dims kept together) in token-slot
 // order: within each 32-dim group, dims 4g..4g+3 and 16+4g..16+4g+3 sit side
 // by side at 8g.., so one 128-bit read yields an x32 MFMA operand.
@@ -926,10 +847,6 @@ __device__ __forceinline__ int qt_slot(int d) {
   const int r = d & 31;
   return (d & ~31) + (r < 16 ? 2 * r : 2 * (r - 16) + 4);
 }
-__device__ __forceinline__ f16x4 ld64(const f16* a) { return *reinterpret_cast<const f16x4*>(a); }
-__device__ __forceinline__ f16x8 ld128(const f16* a) { return *reinterpret_cast<const f16x8*>(a); }
-__device__ __forceinline__ void st64(f16* a, f16x4 x) { *reinterpret_cast<f16x4*>(a) = x; }
-__device__ __forceinline__ f16x4 to_f16(f32x4 x) { return __builtin_convertvector(x, f16x4); }
 
 // Fused gate activation: log alpha = logsigmoid(z) / tau from gate logits z,
 // as min(z, 0) - ln(1 + e^{-|z|}) (no overflow for any z), with ln(1 + t) by
@@ -966,11 +883,6 @@ struct StepTiles {
   f16* v;
 };
 
-// s_waitcnt immediate: at most n vector-memory operations and no LDS
-// operation outstanding.
-__host__ __device__ constexpr int vmcnt_lgkm0_imm(int n) {
-  return (n & 15) | (7 << 4) | ((n >> 4) << 14);
-}
 
 template <int DK, int DV, bool GATE>
 __global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 4 : (DK == 128 && DV == 128) ? 1 : 2) void chunk_output_f16_kernel(

@@ -160,3 +160,28 @@ def test_spatial_swiglu_argument_errors():
         assert call_sw(bias=None) not in (-1, -2, -3, -4, -6)  # bias is optional
         assert call_sw(value=P[0] + 128, ld=128) not in (-2, -3, -4, -6)  # fused halves
         assert call_sw(H=1024, W=1023, C=1024) not in (-2,)
+
+
+def call_saga(q=P[0], k=P[1], v=P[2], a=P[3], b=P[4], B=1, heads=2, N=300, d_k=64, d_v=64,
+              out=P[5], kv=P[6]):
+    return _lib.raw_call_saga(q, k, v, a, b, B, heads, N, d_k, d_v, out, kv, None)
+
+
+def test_saga_argument_errors():
+    for kw in ("q", "k", "v", "a", "b", "out"):
+        assert call_saga(**{kw: None}) == -1, kw
+    for kw in ("B", "heads", "N", "d_k", "d_v"):
+        assert call_saga(**{kw: 0}) == -2, kw
+    assert call_saga(d_k=96) == -3
+    assert call_saga(d_v=32) == -3
+    assert call_saga(N=1 << 24, d_k=64, d_v=64) == -2       # a sequence's rows reach 2 GiB
+    assert call_saga(q=P[0] + 8) == -4
+    assert call_saga(out=P[5] + 2) == -4
+    assert call_saga(kv=P[6] + 4) == -4
+    assert call_saga(out=P[0]) == -6                         # out aliases q
+    assert call_saga(out=P[4] + 64) == -6                    # out overlaps beta
+    assert call_saga(kv=P[5] + 1024) == -6                   # kv inside out
+    assert call_saga(kv=P[1]) == -6                          # kv aliases k
+    if NO_DEVICE:
+        assert call_saga(kv=None) not in (-1, -2, -3, -4, -6)  # kv is optional
+        assert call_saga(N=(1 << 24) - 1) not in (-2,)
