@@ -336,8 +336,13 @@ int gla_saga_fwd(const void* q, const void* k, const void* v, const void* alpha,
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
       cus = 256;
-    // about two accumulation workgroups per CU: spans of whole chunks
-    const long long want = (2LL * cus + BH - 1) / BH;
+    // a few accumulation workgroups per CU: spans of whole steps
+    static const int per_cu = [] {
+      const char* e = std::getenv("GLA_SAGA_WG_PER_CU");  // tuning override
+      const int v = e ? std::atoi(e) : 0;
+      return (v >= 1 && v <= 16) ? v : 3;
+    }();
+    const long long want = ((long long)per_cu * cus + BH - 1) / BH;
     const int spans = (int)(want < 1 ? 1 : (want > p.n_chunks ? p.n_chunks : want));
     p.span_chunks = (p.n_chunks + spans - 1) / spans;
     p.n_spans = (p.n_chunks + p.span_chunks - 1) / p.span_chunks;
@@ -346,13 +351,13 @@ int gla_saga_fwd(const void* q, const void* k, const void* v, const void* alpha,
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     const size_t map = (size_t)d_k * d_v;
-    const size_t ws_floats = (kv ? 0 : BH * map) + (p.n_spans > 1 ? BH * p.n_spans * map : 0);
+    const size_t ws_floats = BH * map + BH * p.n_spans * map;   // transposed maps, partials
     void* ws = nullptr;
-    if (ws_floats > 0 && hipMallocAsync(&ws, ws_floats * sizeof(float), st) != hipSuccess)
-      return GLA_ERR_HIP;
+    if (hipMallocAsync(&ws, ws_floats * sizeof(float), st) != hipSuccess) return GLA_ERR_HIP;
     float* wsf = static_cast<float*>(ws);
-    p.kv = kv ? kv : wsf;
-    p.partial = p.n_spans > 1 ? (kv ? wsf : wsf + BH * map) : nullptr;
+    p.kv = kv;
+    p.kvt = wsf;
+    p.partial = wsf + BH * map;
     const hipEvent_t* ev = t_events_set ? t_events : nullptr;
     t_events_set = false;
     const hipError_t e = gla::launch_saga(p, st, ev);

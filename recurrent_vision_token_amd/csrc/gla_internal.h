@@ -81,11 +81,12 @@ struct SagaParams {
   const void* a;        // key-side gates [B][heads][N][d_k]
   const void* b;        // value-side gates [B][heads][N][d_v]
   void* out;            // [B][heads][N][d_v]
-  float* kv;            // [B*heads][d_k][d_v] gated key-value maps
-  float* partial;       // [B*heads][n_spans][d_k][d_v] span partials (n_spans > 1)
+  float* kv;            // [B*heads][d_k][d_v] gated key-value maps, or null
+  float* kvt;           // [B*heads][d_v][d_k] the maps transposed (workspace)
+  float* partial;       // [B*heads][n_spans][d_k][d_v] span partials (workspace)
   int B, heads, N, d_k, d_v;
-  int n_chunks;         // ceil(N / saga_chunk_tokens())
-  int span_chunks;      // chunks per span of the accumulation kernel
+  int n_chunks;         // ceil(N / saga_chunk_tokens()) accumulation steps
+  int span_chunks;      // steps per span of the accumulation kernel
   int n_spans;          // ceil(n_chunks / span_chunks)
   int n_tblocks;        // ceil(N / saga_out_tokens()) output workgroups per (b, h)
 };
@@ -94,7 +95,7 @@ int saga_chunk_tokens();
 int saga_out_tokens();
 bool saga_has_variant(int d_k, int d_v);
 
-// Enqueue the accumulation, reduction (n_spans > 1) and output kernels;
+// Enqueue the accumulation, reduction and output kernels;
 // events: null, or six hipEvent_t recorded around the three kernels.
 hipError_t launch_saga(const SagaParams& p, hipStream_t stream, hipEvent_t const* events);
 

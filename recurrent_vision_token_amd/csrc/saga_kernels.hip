@@ -8,12 +8,12 @@
 // summary, gist.science, Methodology sections A and B).
 //
 // Three kernels:
-//   1. saga_kv_partial : one workgroup per (batch*head, span of 64-token
-//      chunks) accumulates its span's (K*A)^T (V*B) on the matrix cores - the
+//   1. saga_kv_partial : one workgroup per (batch*head, span of 32-token
+//      steps) accumulates its span's (K*A)^T (V*B) on the matrix cores - the
 //      key-value accumulation of the attention path's chunk summaries, with
 //      the gates in place of the decay;
-//   2. saga_kv_reduce  : sums the span partials in a fixed order (skipped when
-//      one span covers the sequence);
+//   2. saga_kv_reduce  : sums the span partials in a fixed order and writes
+//      the map, also transposed for kernel 3;
 //   3. saga_out        : O^T = KV^T Q^T, 16 tokens by 16 value dims per MFMA,
 //      queries read straight from memory into the MFMA operand layout.
 // Chunk tiles move into LDS with LDS-writing buffer loads and are read back
@@ -30,8 +30,9 @@ namespace gla {
 namespace {
 
 constexpr int kThreads = 256;   // four wave64s
-constexpr int kChunk = 64;      // tokens per chunk (tile rows)
-constexpr int kOutTokens = 128; // tokens per output workgroup
+constexpr int kStepTokens = 32; // tokens per accumulation step (tile rows)
+constexpr int kOutTokens = 256; // tokens per output workgroup
+constexpr int kSpanGroups = 4;  // span groups summed side by side in the reduction
 
 // Source offset of this lane's 16 bytes in block `blk` (1 KB) of a tile with
 // RB-byte rows holding tokens t0.., swizzled like the attention tiles; rows
@@ -45,6 +46,13 @@ __device__ __forceinline__ uint32_t tile_offset(int blk, int t0, int valid) {
   return off | ((uint32_t)(r >= valid) << 31);
 }
 
+// LDS-writing load with the non-temporal policy: the accumulation reads its
+// inputs exactly once, so they are kept from displacing cached data (about
+// 10 % faster on the 16K-token workload).
+__device__ __forceinline__ void dma16_stream(rsrc_t src, f16* block, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void_t*)block, 16, off, 0, 0, 2);
+}
+
 template <int DK, int DV>
 struct SagaTile {
   f16* k;
@@ -53,25 +61,26 @@ struct SagaTile {
   f16* b;
 };
 
-// Kernel 1.  Wave w owns key dims 16 db.. (db = w, w + 4, ...); the map
-// tile cb sits in lane (n, g) as KV^T[16 cb + 4g + u][16 db + n].  Per chunk,
-// k * alpha and v * beta are formed in packed float16 from transposed tile
-// reads (lane (n, g): tokens 4g..4g+3 of dim n in each 16-token sub-block)
-// and KV^T += (V*B)^T (K*A) runs as 16x16x32 MFMAs over sub-block pairs.
+// Kernel 1.  One workgroup per (batch*head, span of 32-token steps).  Wave w
+// owns key dims 16 db.. (db = w, w + 4, ...); the map tile cb sits in lane
+// (n, g) as KV^T[16 cb + 4g + u][16 db + n].  Per step, k * alpha and v * beta
+// are formed in packed float16 from transposed tile reads (lane (n, g):
+// tokens 4g..4g+3 of dim n in each 16-token half) and KV^T += (V*B)^T (K*A)
+// is one 16x16x32 MFMA per (db, cb) tile.  Two step buffers: the next step
+// loads while this one is folded.
 template <int DK, int DV>
 __global__ __launch_bounds__(kThreads) void saga_kv_partial_kernel(SagaParams p) {
+  constexpr int T = kStepTokens;
   // eight separate LDS objects, so the compiler's own waits for the
   // LDS-writing loads can tell the tiles apart
-  __shared__ __attribute__((aligned(16))) f16 k0[kChunk * DK], a0[kChunk * DK], v0[kChunk * DV],
-      b0[kChunk * DV];
-  __shared__ __attribute__((aligned(16))) f16 k1[kChunk * DK], a1[kChunk * DK], v1[kChunk * DV],
-      b1[kChunk * DV];
+  __shared__ __attribute__((aligned(16))) f16 k0[T * DK], a0[T * DK], v0[T * DV], b0[T * DV];
+  __shared__ __attribute__((aligned(16))) f16 k1[T * DK], a1[T * DK], v1[T * DV], b1[T * DV];
   const SagaTile<DK, DV> slot0{k0, a0, v0, b0}, slot1{k1, a1, v1, b1};
   constexpr int NDB = DK / 64, NCB = DV / 16;
   constexpr int RBK = 2 * DK, RBV = 2 * DV;
-  constexpr int NBK = RBK / 64, NBV = RBV / 64;  // 1 KB blocks per wave and tile
-  constexpr int NDMA = 2 * NBK + 2 * NBV;         // LDS-writing loads per wave and chunk
-  static_assert(NDMA < 64, "vmcnt range");
+  constexpr int NBK = RBK * T / 4096, NBV = RBV * T / 4096;  // 1 KB blocks per wave and tile
+  constexpr int NDMA = 2 * NBK + 2 * NBV;                     // LDS-writing loads per wave and step
+  static_assert(NBK >= 1 && NBV >= 1 && NDMA < 64, "tile split");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n16 = lane & 15, g = lane >> 4;
@@ -86,23 +95,23 @@ __global__ __launch_bounds__(kThreads) void saga_kv_partial_kernel(SagaParams p)
   const int c_begin = span * p.span_chunks;
   const int c_end = min(c_begin + p.span_chunks, p.n_chunks);
 
-  // Fill a tile buffer with chunk c; a chunk past the span loads nothing.
+  // Fill a tile buffer with step c; a step past the span loads nothing.
   auto issue = [&](const SagaTile<DK, DV>& s, int c) {
-    const int t0 = c * kChunk;
-    const int valid = c < c_end ? min(kChunk, p.N - t0) : 0;
+    const int t0 = c * T;
+    const int valid = c < c_end ? min(T, p.N - t0) : 0;
 #pragma unroll
     for (int i = 0; i < NBK; ++i) {
       const int blk = wave * NBK + i;
       const uint32_t off = tile_offset<RBK>(blk, t0, valid);
-      dma16(rk, s.k + blk * 512, off);
-      dma16(ra, s.a + blk * 512, off);
+      dma16_stream(rk, s.k + blk * 512, off);
+      dma16_stream(ra, s.a + blk * 512, off);
     }
 #pragma unroll
     for (int i = 0; i < NBV; ++i) {
       const int blk = wave * NBV + i;
       const uint32_t off = tile_offset<RBV>(blk, t0, valid);
-      dma16(rv, s.v + blk * 512, off);
-      dma16(rb, s.b + blk * 512, off);
+      dma16_stream(rv, s.v + blk * 512, off);
+      dma16_stream(rb, s.b + blk * 512, off);
     }
   };
 
@@ -116,20 +125,13 @@ __global__ __launch_bounds__(kThreads) void saga_kv_partial_kernel(SagaParams p)
 #pragma unroll
     for (int d = 0; d < NDB; ++d) {
       const int db = wave + 4 * d;
-      f16x4 ka[4];
+      const f16x8 bk = cat8(tr_read<RBK>(s.k, 0, 16 * db) * tr_read<RBK>(s.a, 0, 16 * db),
+                            tr_read<RBK>(s.k, 16, 16 * db) * tr_read<RBK>(s.a, 16, 16 * db));
 #pragma unroll
-      for (int J = 0; J < 4; ++J)
-        ka[J] = tr_read<RBK>(s.k, 16 * J, 16 * db) * tr_read<RBK>(s.a, 16 * J, 16 * db);
-#pragma unroll
-      for (int P = 0; P < 2; ++P) {
-        const f16x8 bk = cat8(ka[2 * P], ka[2 * P + 1]);
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          const f16x4 lo = tr_read<RBV>(s.v, 32 * P, 16 * cb) * tr_read<RBV>(s.b, 32 * P, 16 * cb);
-          const f16x4 hi =
-              tr_read<RBV>(s.v, 32 * P + 16, 16 * cb) * tr_read<RBV>(s.b, 32 * P + 16, 16 * cb);
-          st[d][cb] = mma32(cat8(lo, hi), bk, st[d][cb]);
-        }
+      for (int cb = 0; cb < NCB; ++cb) {
+        const f16x4 lo = tr_read<RBV>(s.v, 0, 16 * cb) * tr_read<RBV>(s.b, 0, 16 * cb);
+        const f16x4 hi = tr_read<RBV>(s.v, 16, 16 * cb) * tr_read<RBV>(s.b, 16, 16 * cb);
+        st[d][cb] = mma32(cat8(lo, hi), bk, st[d][cb]);
       }
     }
   };
@@ -146,13 +148,12 @@ __global__ __launch_bounds__(kThreads) void saga_kv_partial_kernel(SagaParams p)
     wait_barrier<kLgkmZero>();
     issue(slot1, c + 3);
   }
-  // the trailing loads target chunks past the span (zero fills): let them land
+  // the trailing loads target steps past the span (zero fills): let them land
   // before the workgroup's LDS can be handed on
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
-  float* dst = p.n_spans == 1 ? p.kv + (size_t)bh * DK * DV
-                              : p.partial + ((size_t)bh * p.n_spans + span) * DK * DV;
+  float* dst = p.partial + ((size_t)bh * p.n_spans + span) * DK * DV;
 #pragma unroll
   for (int d = 0; d < NDB; ++d) {
     const int dim = 16 * (wave + 4 * d) + n16;
@@ -162,28 +163,51 @@ __global__ __launch_bounds__(kThreads) void saga_kv_partial_kernel(SagaParams p)
   }
 }
 
-// Kernel 2: kv[bh] = sum over spans of the partials, in span order.
+// Kernel 2: kv[bh] = sum of the span partials, in a fixed order, written as
+// the caller's [d_k][d_v] map (when asked for) and transposed, [d_v][d_k],
+// for the output kernel.  A workgroup owns 256 map elements (64 columns of
+// 4); its four thread groups sum every fourth span, one load per span in
+// flight per thread, and the four sums are added in group order.
 template <int DK, int DV>
 __global__ __launch_bounds__(kThreads) void saga_kv_reduce_kernel(SagaParams p) {
+  __shared__ f32x4 part[kSpanGroups][64];
   const int bh = blockIdx.x;
-  const int e = (blockIdx.y * kThreads + threadIdx.x) * 4;
+  const int col = threadIdx.x & 63, grp = threadIdx.x >> 6;
+  const int e = (blockIdx.y * 64 + col) * 4;   // first of 4 consecutive map elements
   const float* src = p.partial + (size_t)bh * p.n_spans * DK * DV + e;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < p.n_spans; ++s) acc += *reinterpret_cast<const f32x4*>(src + (size_t)s * DK * DV);
-  *reinterpret_cast<f32x4*>(p.kv + (size_t)bh * DK * DV + e) = acc;
+#pragma unroll 4
+  for (int s = grp; s < p.n_spans; s += kSpanGroups)
+    acc += *reinterpret_cast<const f32x4*>(src + (size_t)s * DK * DV);
+  part[grp][col] = acc;
+  __syncthreads();
+  if (grp == 0) {
+    const f32x4 sum = ((part[0][col] + part[1][col]) + part[2][col]) + part[3][col];
+    if (p.kv != nullptr) *reinterpret_cast<f32x4*>(p.kv + (size_t)bh * DK * DV + e) = sum;
+    const int i = e / DV, j = e % DV;   // the 4 elements are (i, j .. j + 3)
+    float* kvt = p.kvt + (size_t)bh * DK * DV;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) kvt[(j + u) * DK + i] = sum[u];
+  }
 }
 
-// Kernel 3.  Wave w owns value dims 16 jb.. (jb = w, w + 4, ...).  Its MFMA A
-// operands are KV^T rows 16 jb + n, key dims 32 rho + 8g .. + 7 (lane (n, g)),
-// scaled by a power of two that brings the wave's largest |KV| entry to
-// [2^14, 2^15) before the float16 conversion (exact to undo, and it keeps
-// both large and tiny maps inside float16); the B operand of 16 tokens is
-// lane (n, g) = the 16 bytes of token n at key dims 32 rho + 8g, loaded
-// straight from memory.  Out lane (n, g) holds tokens n, value dims
-// 16 jb + 4g .. + 3: one 8-byte store.
+// Kernel 3.  Each wave takes 16-token blocks of its workgroup's 256 tokens and
+// computes all value dims, as O^T = KV^T Q^T in 16x16x32 MFMAs (rows: value
+// dims, columns: tokens, reduction: key dims).
+//  * B operand: lane (n, g) holds the 16 bytes of token n at key dims
+//    32 rho + 8g .. + 7, loaded straight from memory (64 bytes per token per
+//    instruction).
+//  * A operands: MFMA m's row r is value dim 32 (m / 2) + 8 (r / 4) +
+//    4 (m % 2) + r % 4, so lane (n, g) ends up with value dims
+//    32 s + 8g .. + 7 of token n from MFMAs 2s and 2s + 1: one 16-byte store
+//    per s, and the four lane groups of a store fill 64 contiguous bytes.
+//    Rows come from the transposed map as two 16-byte loads, scaled by a power
+//    of two that brings each MFMA's largest |KV| entry to [2^14, 2^15) before
+//    the float16 conversion (exact to undo; it keeps both large and tiny maps
+//    inside float16).
 template <int DK, int DV>
 __global__ __launch_bounds__(kThreads) void saga_out_kernel(SagaParams p) {
-  constexpr int NRHO = DK / 32, NJW = DV / 64;
+  constexpr int NRHO = DK / 32, NM = DV / 16;
   constexpr int RBK = 2 * DK, RBV = 2 * DV;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -193,55 +217,77 @@ __global__ __launch_bounds__(kThreads) void saga_out_kernel(SagaParams p) {
 
   const rsrc_t rq = seq_rsrc(static_cast<const f16*>(p.q) + (size_t)bh * p.N * DK, (uint32_t)p.N * RBK);
   const rsrc_t ro = seq_rsrc(static_cast<f16*>(p.out) + (size_t)bh * p.N * DV, (uint32_t)p.N * RBV);
-  const float* kv = p.kv + (size_t)bh * DK * DV;
+  const float* kvt = p.kvt + (size_t)bh * DK * DV;
 
-  f16x8 am[NJW][NRHO];
-  float unscale[NJW];
-#pragma unroll
-  for (int jj = 0; jj < NJW; ++jj) {
-    const int j = 16 * (wave + 4 * jj) + n16;
-    float vals[NRHO][8];
-    float mx = 0.f;
+  // With 64 key dims every block's queries are requested first, so their
+  // latency overlaps the map reads below; with 128 the registers this takes
+  // cost more occupancy than the overlap gains, and each block loads its own.
+  constexpr int NBLK = kOutTokens / 64;
+  constexpr bool kAhead = DK == 64;
+  auto load_q = [&](f16x8* qv, int blk) {
+    const int t = t_begin + 16 * (4 * blk + wave) + n16;
+    const uint32_t ok = t < p.N ? 0u : 0x80000000u;
 #pragma unroll
     for (int rho = 0; rho < NRHO; ++rho)
+      qv[rho] = __builtin_bit_cast(
+          f16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                     rq, ((uint32_t)t * RBK + (uint32_t)(32 * rho + 8 * g) * 2) | ok, 0, 0));
+  };
+  f16x8 qa[kAhead ? NBLK : 1][NRHO];
+  if constexpr (kAhead) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        vals[rho][e] = kv[(32 * rho + 8 * g + e) * DV + j];
-        mx = fmaxf(mx, fabsf(vals[rho][e]));
-      }
+    for (int blk = 0; blk < NBLK; ++blk) load_q(qa[blk], blk);
+  }
+
+  f16x8 am[NM][NRHO];
+  float unscale[NM];
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
+  for (int m = 0; m < NM; ++m) {
+    const int dim = 32 * (m >> 1) + 8 * (n16 >> 2) + 4 * (m & 1) + (n16 & 3);
+    f32x4 lo[NRHO], hi[NRHO];
+    float mx = 0.f;
+#pragma unroll
+    for (int rho = 0; rho < NRHO; ++rho) {
+      const float* row = kvt + dim * DK + 32 * rho + 8 * g;
+      lo[rho] = *reinterpret_cast<const f32x4*>(row);
+      hi[rho] = *reinterpret_cast<const f32x4*>(row + 4);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) mx = fmaxf(mx, fmaxf(fabsf(lo[rho][u]), fabsf(hi[rho][u])));
+    }
+#pragma unroll
+    for (int k = 32; k >= 1; k >>= 1) mx = fmaxf(mx, __shfl_xor(mx, k));
     int ex = 0;
     (void)frexpf(mx, &ex);                    // mx = f * 2^ex, f in [0.5, 1)
     const int sh = (mx > 0.f) ? 15 - ex : 0;  // scaled maximum in [2^14, 2^15)
     const float scale = ldexpf(1.f, sh);
-    unscale[jj] = ldexpf(1.f, -sh);
+    unscale[m] = ldexpf(1.f, -sh);
 #pragma unroll
     for (int rho = 0; rho < NRHO; ++rho)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) am[jj][rho][e] = (f16)(vals[rho][e] * scale);
+      am[m][rho] = cat8(to_f16(lo[rho] * scale), to_f16(hi[rho] * scale));
   }
 
 #pragma unroll
-  for (int T = 0; T < kOutTokens / 16; ++T) {
-    const int t = t_begin + 16 * T + n16;
+  for (int blk = 0; blk < NBLK; ++blk) {
+    const int t = t_begin + 16 * (4 * blk + wave) + n16;
     const uint32_t row_ok = t < p.N ? 0u : 0x80000000u;
-    f16x8 qb[NRHO];
+    f16x8 qn[NRHO];
+    if constexpr (!kAhead) load_q(qn, blk);
+    const f16x8* qb = kAhead ? qa[blk] : qn;
 #pragma unroll
-    for (int rho = 0; rho < NRHO; ++rho)
-      qb[rho] = __builtin_bit_cast(
-          f16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                     rq, ((uint32_t)t * RBK + (uint32_t)(32 * rho + 8 * g) * 2) | row_ok, 0, 0));
+    for (int s2 = 0; s2 < NM / 2; ++s2) {
+      f32x4 acc[2];
 #pragma unroll
-    for (int jj = 0; jj < NJW; ++jj) {
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int h = 0; h < 2; ++h) {
+        acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int rho = 0; rho < NRHO; ++rho) acc = mma32(am[jj][rho], qb[rho], acc);
-      const f16x4 o = to_f16(acc * unscale[jj]);
-      const int jb = wave + 4 * jj;
-      __builtin_amdgcn_raw_buffer_store_b64(
-          __builtin_bit_cast(u32x2, o), ro,
-          ((uint32_t)t * RBV + (uint32_t)(16 * jb + 4 * g) * 2) | row_ok, 0, 0);
+        for (int rho = 0; rho < NRHO; ++rho)
+          acc[h] = mma32(am[2 * s2 + h][rho], qb[rho], acc[h]);
+        acc[h] *= unscale[2 * s2 + h];
+      }
+      const f16x8 o = cat8(to_f16(acc[0]), to_f16(acc[1]));
+      __builtin_amdgcn_raw_buffer_store_b128(
+          __builtin_bit_cast(u32x4, o), ro,
+          ((uint32_t)t * RBV + (uint32_t)(32 * s2 + 8 * g) * 2) | row_ok, 0, 0);
     }
   }
 }
@@ -265,20 +311,15 @@ hipError_t launch_saga_variant(const SagaParams& p, hipStream_t stream, hipEvent
   if ((e = launch_k(saga_kv_partial_kernel<DK, DV>, dim3(BH * p.n_spans), stream, p, ev, 0)) !=
       hipSuccess)
     return e;
-  if (p.n_spans > 1) {
-    if ((e = launch_k(saga_kv_reduce_kernel<DK, DV>, dim3(BH, DK * DV / (4 * kThreads)), stream, p,
-                      ev, 1)) != hipSuccess)
-      return e;
-  } else if (ev != nullptr) {
-    if ((e = hipEventRecord(ev[2], stream)) != hipSuccess) return e;
-    if ((e = hipEventRecord(ev[3], stream)) != hipSuccess) return e;
-  }
+  if ((e = launch_k(saga_kv_reduce_kernel<DK, DV>, dim3(BH, DK * DV / 256), stream, p, ev, 1)) !=
+      hipSuccess)
+    return e;
   return launch_k(saga_out_kernel<DK, DV>, dim3(BH * p.n_tblocks), stream, p, ev, 2);
 }
 
 }  // namespace
 
-int saga_chunk_tokens() { return kChunk; }
+int saga_chunk_tokens() { return kStepTokens; }
 int saga_out_tokens() { return kOutTokens; }
 
 bool saga_has_variant(int d_k, int d_v) {
