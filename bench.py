@@ -13,7 +13,8 @@ stack would, instead of re-reading cache-resident data.
 
 Beside it, the same protocol times the block's other token mixer, the
 Spatial SwiGLU step (gla_spatial_swiglu) on the 16.4K grid with 2048 hidden
-channels, reported under "spatial_swiglu".
+channels, reported under "spatial_swiglu", and the SAGA-style non-causal
+gated linear attention (gla_saga_fwd) on the same token count, under "saga".
 
 Prints ONE JSON line on stdout; details go to stderr.
 """
@@ -35,11 +36,27 @@ MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 MFMA, published
 LLC_BYTES = 256 << 20           # Infinity Cache
 KERNEL_SRC = os.path.join(ROOT, "recurrent_vision_token_amd", "csrc", "gla_kernels.hip")
 SWIGLU_SRC = os.path.join(ROOT, "recurrent_vision_token_amd", "csrc", "swiglu_kernels.hip")
-KERNEL_NAMES = ("span_summary", "span_scan", "chunk_output", "spatial_swiglu")
+SAGA_SRC = os.path.join(ROOT, "recurrent_vision_token_amd", "csrc", "saga_kernels.hip")
+KERNEL_NAMES = ("span_summary", "span_scan", "chunk_output", "spatial_swiglu", "saga_kv_partial",
+                "saga_kv_reduce", "saga_out")
+
+
+DEVICE_HDR = os.path.join(ROOT, "recurrent_vision_token_amd", "csrc", "gla_device.h")
 
 
 def source_of(kernel):
-    return SWIGLU_SRC if kernel == "spatial_swiglu" else KERNEL_SRC
+    if kernel == "spatial_swiglu":
+        return SWIGLU_SRC
+    return SAGA_SRC if kernel.startswith("saga") else KERNEL_SRC
+
+
+def source_hash(kernel):
+    """Hash of the device code a kernel is built from (its file and the shared
+    device header)."""
+    h = hashlib.sha256()
+    for path in (source_of(kernel), DEVICE_HDR):
+        h.update(open(path, "rb").read())
+    return h.hexdigest()
 
 
 def log(*a):
@@ -286,6 +303,120 @@ def swiglu_summary(swl, ms_call, k_ms, cpu):
     }
 
 
+SAGA_WORKLOAD = "saga_hires16.4k"
+
+
+def saga_bytes(swl):
+    """Algorithmic bytes of one SAGA call: read q, k, v and the two gates,
+    write out (fp16); and of its dominant kernel, the map accumulation, which
+    reads k, v and the gates."""
+    th = swl.B * swl.heads * swl.N
+    return th * 2 * (3 * swl.d_k + 3 * swl.d_v), th * 2 * (2 * swl.d_k + 2 * swl.d_v)
+
+
+class SagaRunner:
+    """Device copies of the SAGA inputs, cycled across calls like Runner."""
+
+    def __init__(self, swl, torch, min_sets_bytes=2 * LLC_BYTES):
+        from recurrent_vision_token_amd import _lib
+        from recurrent_vision_token_amd.workloads import make_saga_inputs
+        self.swl = swl
+        dev = torch.device("cuda:0")
+        self.host = make_saga_inputs(swl.B, swl.heads, swl.N, swl.d_k, swl.d_v, seed=swl.seed)
+        reps = max(2, math.ceil(min_sets_bytes / saga_bytes(swl)[0]))
+        self.sets = []
+        for _ in range(reps):
+            t = [torch.from_numpy(x).to(dev) for x in self.host]
+            self.sets.append((t, torch.empty_like(t[2])))
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        self.fn = _lib.load().gla_saga_fwd
+        self.args = [tuple(x.data_ptr() for x in t) + (swl.B, swl.heads, swl.N, swl.d_k, swl.d_v,
+                                                       o.data_ptr(), None, stream)
+                     for (t, o) in self.sets]
+        self.cursor = 0
+        torch.cuda.synchronize()
+
+    def step(self, events=None):
+        from recurrent_vision_token_amd import _lib
+        a = self.args[self.cursor]
+        self.cursor = (self.cursor + 1) % len(self.sets)
+        if events is not None:
+            rc = _lib.set_kernel_events([e.cuda_event for e in events])
+            if rc != 0:
+                raise RuntimeError("gla_set_kernel_events failed: %d" % rc)
+        rc = self.fn(*a)
+        if rc != 0:
+            raise RuntimeError("gla_saga_fwd failed: %d" % rc)
+
+
+def time_saga(swl, torch, steps, warmup):
+    """Wall-clock loop of single calls, then an event-instrumented pass for the
+    three kernels' own durations."""
+    r = SagaRunner(swl, torch)
+    log("[bench] %s: %d device input sets (%.0f MB)" %
+        (swl.name, len(r.sets), len(r.sets) * saga_bytes(swl)[0] / 1e6))
+    for _ in range(warmup):
+        r.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        r.step()
+    torch.cuda.synchronize()
+    ms_call = (time.perf_counter() - t0) * 1e3 / steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    stream = torch.cuda.current_stream()
+    for per_call in evs:
+        for e in per_call:
+            e.record(stream)
+    torch.cuda.synchronize()
+    for e in evs:
+        r.step(e)
+    torch.cuda.synchronize()
+    names = ("saga_kv_partial", "saga_kv_reduce", "saga_out")
+    k_ms = {n: sum(e[2 * i].elapsed_time(e[2 * i + 1]) for e in evs) / len(evs)
+            for i, n in enumerate(names)}
+    k_ms["call"] = sum(e[0].elapsed_time(e[5]) for e in evs) / len(evs)
+    return r, ms_call, k_ms
+
+
+def saga_cpu_baseline(swl, host):
+    """The SAGA oracle as it stands (numpy float64 matrix products) on the full workload."""
+    from oracle import saga_forward
+    t0 = time.perf_counter()
+    c0 = time.process_time()
+    saga_forward(*host)
+    wall = time.perf_counter() - t0
+    cores = max(1, int(round((time.process_time() - c0) / wall)))
+    return {"value": swl.B * swl.N / wall, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": "one full call (%s, numpy float64), %.2f s wall" % (swl.name, wall)}
+
+
+def saga_summary(swl, ms_call, k_ms, cpu):
+    total, acc = saga_bytes(swl)
+    ach = acc / (k_ms["saga_kv_partial"] * 1e-3) / 1e9
+    path = total / (k_ms["call"] * 1e-3) / 1e9
+    return {
+        "entry": "gla_saga_fwd: O = Q [(K*A)^T (V*B)], non-causal",
+        "workload": "%s: B=%d, heads=%d, N=%d tokens, d_k=%d, d_v=%d, fp16, q/k/v ~ N(0,1)/8, "
+                    "gates sigmoid(N(0,1)), seed %d" %
+                    (swl.name, swl.B, swl.heads, swl.N, swl.d_k, swl.d_v, swl.seed),
+        "value": swl.B * swl.N / (ms_call * 1e-3),
+        "unit": "tokens/s",
+        "ms_per_call": round(ms_call, 4),
+        "dtype": "f16",
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic_from_profiles(SAGA_WORKLOAD, "saga_kv_partial")
+                     if swl.name == SAGA_WORKLOAD else None,
+                     "kernel": "saga_kv_partial", "algorithmic_bytes_per_launch": acc,
+                     "avg_launch_us": round(k_ms["saga_kv_partial"] * 1e3, 2)},
+        "path": {"gpu_us_per_call": round(k_ms["call"] * 1e3, 2), "algorithmic_bytes_per_call": total,
+                 "achieved_GBps": round(path, 1), "hbm_frac": round(path / HBM_PEAK_GBPS, 4),
+                 "kernel_us": {k: round(v * 1e3, 2) for k, v in k_ms.items() if k != "call"}},
+        "cpu_baseline": cpu,
+    }
+
+
 def n_spans_of(wl):
     from recurrent_vision_token_amd import _lib
     return _lib.plan_spans(wl.dtype, wl.B, wl.heads, wl.H, wl.W, wl.d_k, wl.d_v, wl.chunk)[1]
@@ -298,9 +429,8 @@ def traffic_from_profiles(wl_name, kernel):
         return None
     try:
         rec = json.load(open(path))
-        src_hash = hashlib.sha256(open(source_of(kernel), "rb").read()).hexdigest()
         k = rec["kernels"][kernel]
-        if k.get("kernel_source_sha256", rec.get("kernel_source_sha256")) != src_hash:
+        if k.get("kernel_source_sha256") != source_hash(kernel):
             return None
         return k["hbm_bytes_per_launch"]
     except Exception:
@@ -388,7 +518,9 @@ def counters_to_traffic(fetch_dir, write_dir, copy_mb, workload):
                 key = "copy"
             if key is not None:
                 vals.setdefault(key, []).append(float(row["Counter_Value"]))
-        return {k: statistics.mean(v) for k, v in vals.items()}
+        # the calibration copy is the largest copy dispatch of the run (input
+        # uploads may show up as smaller copy kernels)
+        return {k: (max(v) if k == "copy" else statistics.mean(v)) for k, v in vals.items()}
 
     f = per_kernel(fetch_dir, "FETCH_SIZE")
     w = per_kernel(write_dir, "WRITE_SIZE")
@@ -403,14 +535,14 @@ def counters_to_traffic(fetch_dir, write_dir, copy_mb, workload):
             continue
         rd = f[k] * 1024.0 * f_scale
         wr = w[k] * 1024.0 * w_scale
-        wl_name = SWIGLU_WORKLOAD if k == "spatial_swiglu" else workload
+        wl_name = (SWIGLU_WORKLOAD if k == "spatial_swiglu" else
+                   SAGA_WORKLOAD if k.startswith("saga") else workload)
         rec = recs.setdefault(wl_name, {"workload": wl_name, "copy_bytes": copy_bytes,
                                         "fetch_scale": f_scale, "write_scale": w_scale,
                                         "kernels": {}})
         rec["kernels"][k] = {"fetch_kib": f[k], "write_kib": w[k], "hbm_read_bytes": rd,
                              "hbm_write_bytes": wr, "hbm_bytes_per_launch": rd + wr,
-                             "kernel_source_sha256":
-                                 hashlib.sha256(open(source_of(k), "rb").read()).hexdigest()}
+                             "kernel_source_sha256": source_hash(k)}
         lines.append("| %s | %.0f | %.0f | %.1f | %.1f | %.1f |" % (k, f[k], w[k], rd / 1e6, wr / 1e6,
                                                                   (rd + wr) / 1e6))
     for wl_name, rec in recs.items():
@@ -434,6 +566,8 @@ def main():
                     help="skip the extended entry point (fused gate + initial state) line")
     ap.add_argument("--swiglu", default=SWIGLU_WORKLOAD,
                     help="Spatial SwiGLU workload to time beside the attention path ('' to skip)")
+    ap.add_argument("--saga", default=SAGA_WORKLOAD,
+                    help="SAGA non-causal gated attention workload to time ('' to skip)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run one device-to-device copy of this many MB (a kernel of "
                          "known traffic, to scale hardware byte counters against)")
@@ -509,6 +643,17 @@ def main():
             (swl.name, ms_sw * 1e3, k_sw * 1e3, swiglu["value"], swiglu["roofline"]["achieved"]))
         del srun
 
+    saga = None
+    if args.saga:
+        from recurrent_vision_token_amd.workloads import SAGA_WORKLOADS
+        gwl = SAGA_WORKLOADS[args.saga]
+        grun, ms_g, k_g = time_saga(gwl, torch, max(20, args.steps), max(5, args.warmup))
+        g_cpu = None if args.no_cpu_baseline else saga_cpu_baseline(gwl, grun.host)
+        saga = saga_summary(gwl, ms_g, k_g, g_cpu)
+        log("[bench] %s: %.2f us/call wall, kernels %s, %.3e tokens/s" %
+            (gwl.name, ms_g * 1e3, saga["path"]["kernel_us"], saga["value"]))
+        del grun
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, runner.host)
@@ -535,6 +680,7 @@ def main():
         "secondary": secondary,
         "fused_gate_initial_state": ext,
         "spatial_swiglu": swiglu,
+        "saga": saga,
     }
     print(json.dumps(line), flush=True)
 
