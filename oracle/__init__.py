@@ -7,6 +7,7 @@ from .gla_oracle import (  # noqa: F401
     SCAN_ROTATE_BATCH,
     SCAN_T2B,
     batch_directions,
+    gla_backward,
     gla_forward,
     log_alpha_from_logits,
     scan_order,

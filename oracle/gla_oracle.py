@@ -146,3 +146,90 @@ def gla_forward(q, k, v, log_alpha, scan_dir, initial_state=None):
             out[bs, :, p, :] = np.einsum("...i,...ij->...j", qf[bs, :, p, :], S)
         final[bs] = S
     return out.reshape(B, nh, H, W, dv), final
+
+
+def gla_backward(q, k, v, log_alpha, d_out, scan_dir, d_final_state=None, initial_state=None,
+                 segment=64):
+    """Gradients of the recurrence, float64, by reverse mode token by token.
+
+    For L = sum(d_out * out) + sum(d_final_state * final_state), with out and
+    final_state those of gla_forward, returns
+    (dq, dk, dv, dlog_alpha, d_initial_state): the first four shaped like
+    their inputs, d_initial_state [B, heads, d_k, d_v] (the gradient with
+    respect to the state before the first scan step, whether or not one was
+    given).
+
+    The adjoint of the state, G_t = dL/dS_t, runs backwards along the scan:
+    G_t gathers q_t^T d_out_t and what flows back from S_{t+1} through the
+    decay, G_t = q_t^T d_out_t + diag(alpha_{t+1}) G_{t+1}, starting from
+    d_final_state.  Differentiating S_t = diag(alpha_t) S_{t-1} + k_t^T v_t
+    and o_t = q_t S_t then gives
+        dq_t = S_t d_out_t^T,  dk_t = G_t v_t^T,  dv_t = k_t G_t,
+        dlog_alpha_t[i] = alpha_t[i] * sum_j G_t[i, j] S_{t-1}[i, j],
+    and dL/dS_{-1} = diag(alpha_0) G_0.  The forward states are recomputed per
+    segment of `segment` steps from states saved at segment starts.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    la = np.asarray(log_alpha, dtype=np.float64)
+    do = np.asarray(d_out, dtype=np.float64)
+    B, nh, H, W, dk = q.shape
+    dv = v.shape[-1]
+    if (k.shape != q.shape or la.shape != q.shape or v.shape[:-1] != q.shape[:-1]
+            or do.shape != v.shape):
+        raise ValueError("shape mismatch among q, k, v, log_alpha, d_out")
+    T = H * W
+    qf = q.reshape(B, nh, T, dk)
+    kf = k.reshape(B, nh, T, dk)
+    vf = v.reshape(B, nh, T, dv)
+    dof = do.reshape(B, nh, T, dv)
+    af = np.exp(la.reshape(B, nh, T, dk))
+    init = (np.zeros((B, nh, dk, dv)) if initial_state is None
+            else np.asarray(initial_state, dtype=np.float64))
+    dfin = (np.zeros((B, nh, dk, dv)) if d_final_state is None
+            else np.asarray(d_final_state, dtype=np.float64))
+    if init.shape != (B, nh, dk, dv) or dfin.shape != (B, nh, dk, dv):
+        raise ValueError("states must be [B, heads, d_k, d_v]")
+
+    dq = np.zeros_like(qf)
+    dkk = np.zeros_like(kf)
+    dvv = np.zeros_like(vf)
+    dla = np.zeros_like(qf)
+    dinit = np.zeros((B, nh, dk, dv))
+    dirs = batch_directions(B, scan_dir)
+    for d in sorted(set(dirs)):
+        bs = np.array([b for b in range(B) if dirs[b] == d], dtype=np.int64)
+        perm = scan_order(H, W, d)
+        starts = list(range(0, T, segment))
+        # forward: the state before each segment
+        saved = []
+        S = init[bs].copy()
+        for t in range(T):
+            if t % segment == 0:
+                saved.append(S.copy())
+            p = perm[t]
+            S = af[bs, :, p, :][..., :, None] * S + \
+                kf[bs, :, p, :][..., :, None] * vf[bs, :, p, :][..., None, :]
+        # backward, segment by segment from the end
+        G = dfin[bs].copy()
+        for m in range(len(starts) - 1, -1, -1):
+            t0, t1 = starts[m], min(T, starts[m] + segment)
+            states = [saved[m]]                      # states[i] = S_{t0 + i - 1}
+            for t in range(t0, t1):
+                p = perm[t]
+                states.append(af[bs, :, p, :][..., :, None] * states[-1] +
+                              kf[bs, :, p, :][..., :, None] * vf[bs, :, p, :][..., None, :])
+            for t in range(t1 - 1, t0 - 1, -1):
+                p = perm[t]
+                S_t, S_prev = states[t - t0 + 1], states[t - t0]
+                a_t = af[bs, :, p, :]
+                G = G + qf[bs, :, p, :][..., :, None] * dof[bs, :, p, :][..., None, :]
+                dq[bs, :, p, :] = np.einsum("...ij,...j->...i", S_t, dof[bs, :, p, :])
+                dkk[bs, :, p, :] = np.einsum("...ij,...j->...i", G, vf[bs, :, p, :])
+                dvv[bs, :, p, :] = np.einsum("...i,...ij->...j", kf[bs, :, p, :], G)
+                dla[bs, :, p, :] = a_t * np.einsum("...ij,...ij->...i", G, S_prev)
+                G = a_t[..., :, None] * G
+        dinit[bs] = G
+    return (dq.reshape(q.shape), dkk.reshape(k.shape), dvv.reshape(v.shape),
+            dla.reshape(q.shape), dinit)
