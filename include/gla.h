@@ -146,6 +146,42 @@ int gla_plan_spans(int use_f32, int B, int heads, int H, int W, int d_k, int d_v
                    int* span_chunks, int* n_spans);
 
 /*
+ * Backward pass (float16; d_k = d_v = 64, chunk = 64): the gradients of
+ *
+ *   L = sum(d_out * out) + sum(d_final_state * final_state)
+ *
+ * for the forward call on the same q, k, v, log_alpha, scan_dir and
+ * initial_state.  The adjoint of the state, G_t = dL/dS_t, runs backwards
+ * along the scan, G_t = q_t^T dO_t + diag(alpha_{t+1}) G_{t+1} from
+ * G = d_final_state, and gives dq_t = S_t dO_t, dk_t = G_t v_t,
+ * dv_t = k_t G_t, dlog_alpha_t = alpha_t * rowsum(G_t * S_{t-1}) and
+ * d_initial_state = diag(alpha_0) G_0; the pass is chunkwise like the
+ * forward one (GTR news write-up, sections "What linear attention saves" and
+ * "Where the speed comes from"): forward entry states and the adjoint states
+ * entering each chunk from its right come from the span-summary / span-scan
+ * kernels (the adjoint recurrence is the forward one read from the end), then
+ * every chunk computes its gradients independently.
+ *
+ * Layout as gla_chunk_fwd; d_out is [B][heads][H][W][d_v] float16;
+ * d_final_state and initial_state are float32 [B][heads][d_k][d_v] or NULL
+ * (zero).  Outputs: dq, dk, dlog_alpha [B][heads][H][W][d_k] and dv
+ * [B][heads][H][W][d_v] float16 (rounded to nearest even), d_initial_state
+ * float32 [B][heads][d_k][d_v] or NULL (not wanted).  Pointers 16-byte
+ * aligned; no output may overlap an input or another output.  A
+ * stream-ordered workspace of B*heads*(2*n_chunks + 1)*(d_k*d_v + d_k) floats
+ * is taken and released on `stream`.  Domain as gla_chunk_fwd, plus
+ * d_out . v and its kin within float16 range.  Errors as gla_chunk_fwd
+ * (GLA_ERR_UNSUPPORTED for any other d_k, d_v or chunk).  With the
+ * measurement hook armed, event pairs bracket the forward-state kernels
+ * (events 0, 1), the adjoint-state kernels (2, 3) and the chunk kernel (4, 5).
+ */
+int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* log_alpha,
+                  const void* d_out, const float* d_final_state, const float* initial_state,
+                  int scan_dir, int B, int heads, int H, int W, int d_k, int d_v, int chunk,
+                  void* dq, void* dk, void* dv, void* dlog_alpha, float* d_initial_state,
+                  void* stream);
+
+/*
  * Spatial SwiGLU step (float16), the other token mixer of each GTR block:
  *
  *   out[b,y,x,c] = silu(gate[b,y,x,c]) *

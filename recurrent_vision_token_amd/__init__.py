@@ -5,6 +5,7 @@ as hand-written HIP kernels for AMD Instinct MI355X (gfx950).
     out, final_state = gla_chunk_fwd_ex(q, k, v, gate_logits, scan_dir,
                                         gate_mode="logits", tau=16.0,
                                         initial_state=state)
+    dq, dk, dv, dla, _ = gla_chunk_bwd(q, k, v, log_alpha, d_out, scan_dir)
     h = spatial_swiglu(gate, value, weight, bias)   # the block's SwiGLU mixer
     o, kv = saga_fwd(q, k, v, alpha, beta)          # non-causal gated linear attention
 
@@ -12,10 +13,11 @@ The heavy lifting is in libgla.so (C ABI: include/gla.h); this package is a
 thin binding around it plus the seeded synthetic workloads.
 """
 
-from ._lib import (GlaError, gla_chunk_fwd, gla_chunk_fwd_ex, load, saga_fwd,  # noqa: F401
-                   spatial_swiglu, status_str)
+from ._lib import (GlaError, gla_chunk_bwd, gla_chunk_fwd, gla_chunk_fwd_ex, load,  # noqa: F401
+                   saga_fwd, spatial_swiglu, status_str)
 
 SCAN_L2R, SCAN_R2L, SCAN_T2B, SCAN_B2T, SCAN_ROTATE_BATCH = 0, 1, 2, 3, 4
 
-__all__ = ["gla_chunk_fwd", "gla_chunk_fwd_ex", "spatial_swiglu", "saga_fwd", "GlaError", "load", "status_str", "SCAN_L2R",
+__all__ = ["gla_chunk_fwd", "gla_chunk_fwd_ex", "gla_chunk_bwd", "spatial_swiglu", "saga_fwd",
+           "GlaError", "load", "status_str", "SCAN_L2R",
            "SCAN_R2L", "SCAN_T2B", "SCAN_B2T", "SCAN_ROTATE_BATCH"]

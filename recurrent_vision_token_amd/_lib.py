@@ -17,7 +17,8 @@ STATUS = {
     0: "GLA_OK", -1: "GLA_ERR_NULL", -2: "GLA_ERR_SHAPE", -3: "GLA_ERR_UNSUPPORTED",
     -4: "GLA_ERR_ALIGN", -5: "GLA_ERR_SCAN_DIR", -6: "GLA_ERR_ALIAS", -7: "GLA_ERR_HIP",
 }
-EXPORTED = ("gla_chunk_fwd", "gla_chunk_fwd_ex", "gla_chunk_fwd_f32", "gla_plan_spans",
+EXPORTED = ("gla_chunk_bwd", "gla_chunk_fwd", "gla_chunk_fwd_ex", "gla_chunk_fwd_f32",
+            "gla_plan_spans",
             "gla_saga_fwd", "gla_set_kernel_events", "gla_spatial_swiglu", "gla_status_str",
             "gla_version")
 GATE_MODES = {"log_alpha": 0, "logits": 1}
@@ -50,6 +51,9 @@ def load():
     lib.gla_chunk_fwd_ex.restype = ctypes.c_int
     lib.gla_spatial_swiglu.argtypes = [vp, vp, i, vp, vp, i, i, i, i, vp, vp]
     lib.gla_saga_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp]
+    lib.gla_chunk_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i,
+                                  vp, vp, vp, vp, vp, vp]
+    lib.gla_chunk_bwd.restype = ctypes.c_int
     lib.gla_saga_fwd.restype = ctypes.c_int
     lib.gla_spatial_swiglu.restype = ctypes.c_int
     lib.gla_status_str.argtypes = [ctypes.c_int]
@@ -215,6 +219,54 @@ def spatial_swiglu(gate, value, weight, bias=None, out=None, stream=None):
     if rc != GLA_OK:
         raise GlaError(rc, status_str(rc))
     return out
+
+
+def raw_call_bwd(q, k, v, la, d_out, d_final, init, scan_dir, B, heads, H, W, d_k, d_v, chunk,
+                 dq, dk, dv, dla, d_init, stream):
+    """Call gla_chunk_bwd with integer pointers; returns the status code."""
+    return load().gla_chunk_bwd(q, k, v, la, d_out, d_final, init, scan_dir, B, heads, H, W, d_k,
+                                d_v, chunk, dq, dk, dv, dla, d_init, stream)
+
+
+def gla_chunk_bwd(q, k, v, log_alpha, d_out, scan_dir, d_final_state=None, initial_state=None,
+                  want_d_initial_state=False, chunk=64, stream=None):
+    """Chunkwise backward pass (float16, d_k = d_v = 64).
+
+    Gradients of sum(d_out * out) + sum(d_final_state * final_state) for the
+    forward call gla_chunk_fwd / gla_chunk_fwd_ex(q, k, v, log_alpha, scan_dir,
+    initial_state=...).  Returns (dq, dk, dv, dlog_alpha, d_initial_state):
+    float16 tensors shaped like q, k, v, log_alpha, and the float32 gradient of
+    the state before the first step when want_d_initial_state, else None.
+    """
+    import torch
+
+    B, heads, H, W, d_k, d_v = _check(q, k, v, log_alpha)
+    if q.dtype != torch.float16:
+        raise ValueError("gla_chunk_bwd takes float16 tensors")
+    if (not isinstance(d_out, torch.Tensor) or d_out.dtype != torch.float16 or d_out.shape != v.shape
+            or not d_out.is_contiguous() or d_out.device != q.device):
+        raise ValueError("d_out must be a contiguous float16 tensor shaped like v")
+    dev = q.device
+    for name, st in (("d_final_state", d_final_state), ("initial_state", initial_state)):
+        if st is not None and (st.dtype != torch.float32 or not st.is_contiguous() or
+                               tuple(st.shape) != (B, heads, d_k, d_v) or st.device != dev):
+            raise ValueError("%s must be contiguous float32 [B, heads, d_k, d_v]" % name)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    dla = torch.empty_like(log_alpha)
+    d_init = (torch.empty((B, heads, d_k, d_v), dtype=torch.float32, device=dev)
+              if want_d_initial_state else None)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    ptr = lambda t: t.data_ptr() if t is not None else None
+    rc = raw_call_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), log_alpha.data_ptr(),
+                      d_out.data_ptr(), ptr(d_final_state), ptr(initial_state), int(scan_dir), B,
+                      heads, H, W, d_k, d_v, int(chunk), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                      dla.data_ptr(), ptr(d_init), stream)
+    if rc != GLA_OK:
+        raise GlaError(rc, status_str(rc))
+    return dq, dk, dv, dla, d_init
 
 
 def raw_call_saga(q, k, v, alpha, beta, B, heads, N, d_k, d_v, out, kv, stream):

@@ -42,17 +42,20 @@ def build(verbose=False):
     logs = []
     s_obj = os.path.join(BUILD, "swiglu_kernels.o")
     g_obj = os.path.join(BUILD, "saga_kernels.o")
+    b_obj = os.path.join(BUILD, "gla_bwd_kernels.o")
     logs.append(_run([hipcc] + HIP_FLAGS + ["-I", INCLUDE, "-I", CSRC, "-c",
                                             os.path.join(CSRC, "gla_kernels.hip"), "-o", k_obj]))
     logs.append(_run([hipcc] + HIP_FLAGS + ["-I", INCLUDE, "-I", CSRC, "-c",
                                             os.path.join(CSRC, "swiglu_kernels.hip"), "-o", s_obj]))
     logs.append(_run([hipcc] + HIP_FLAGS + ["-I", INCLUDE, "-I", CSRC, "-c",
                                             os.path.join(CSRC, "saga_kernels.hip"), "-o", g_obj]))
+    logs.append(_run([hipcc] + HIP_FLAGS + ["-I", INCLUDE, "-I", CSRC, "-c",
+                                            os.path.join(CSRC, "gla_bwd_kernels.hip"), "-o", b_obj]))
     logs.append(_run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-D__HIP_PLATFORM_AMD__",
                       "-I", os.path.join(ROCM, "include"), "-I", INCLUDE, "-I", CSRC, "-c",
                       os.path.join(CSRC, "gla_api.cpp"), "-o", a_obj]))
     tmp = LIB + ".tmp"
-    logs.append(_run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", k_obj, s_obj, g_obj, a_obj,
+    logs.append(_run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", k_obj, s_obj, g_obj, b_obj, a_obj,
                       "-o", tmp]))
     os.replace(tmp, LIB)
     if verbose:

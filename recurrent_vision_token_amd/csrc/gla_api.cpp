@@ -288,6 +288,127 @@ int gla_spatial_swiglu(const void* gate, const void* value, int ld_in, const voi
   }
 }
 
+int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* log_alpha,
+                  const void* d_out, const float* d_final_state, const float* initial_state,
+                  int scan_dir, int B, int heads, int H, int W, int d_k, int d_v, int chunk,
+                  void* dq, void* dk, void* dv, void* dlog_alpha, float* d_initial_state,
+                  void* stream) {
+  try {
+    if (scan_dir < 0 || scan_dir > 4) return GLA_ERR_SCAN_DIR;
+    if (!q || !k || !v || !log_alpha || !d_out || !dq || !dk || !dv || !dlog_alpha)
+      return GLA_ERR_NULL;
+    if (B < 1 || heads < 1 || H < 1 || W < 1 || d_k < 1 || d_v < 1) return GLA_ERR_SHAPE;
+    const long long T = (long long)H * W;
+    const long long BH = (long long)B * heads;
+    if (T > (1LL << 30) || BH > (1LL << 30)) return GLA_ERR_SHAPE;
+    const long long dmax = d_k > d_v ? d_k : d_v;
+    if (T * dmax * 2 >= (1LL << 31)) return GLA_ERR_SHAPE;
+    if (chunk != kChunk || d_k != 64 || d_v != 64) return GLA_ERR_UNSUPPORTED;
+    const void* half_t[9] = {q, k, v, log_alpha, d_out, dq, dk, dv, dlog_alpha};
+    for (const void* t : half_t)
+      if (reinterpret_cast<uintptr_t>(t) % 16 != 0) return GLA_ERR_ALIGN;
+    const void* f32_t[3] = {d_final_state, initial_state, d_initial_state};
+    for (const void* t : f32_t)
+      if (t && reinterpret_cast<uintptr_t>(t) % 16 != 0) return GLA_ERR_ALIGN;
+    const uintptr_t nk = (uintptr_t)(BH * T * d_k) * 2, nv = (uintptr_t)(BH * T * d_v) * 2;
+    const uintptr_t ns = (uintptr_t)(BH * d_k * d_v) * sizeof(float);
+    const Range ins[7] = {{(uintptr_t)q, (uintptr_t)q + nk},
+                          {(uintptr_t)k, (uintptr_t)k + nk},
+                          {(uintptr_t)v, (uintptr_t)v + nv},
+                          {(uintptr_t)log_alpha, (uintptr_t)log_alpha + nk},
+                          {(uintptr_t)d_out, (uintptr_t)d_out + nv},
+                          {(uintptr_t)d_final_state, (uintptr_t)d_final_state + (d_final_state ? ns : 0)},
+                          {(uintptr_t)initial_state, (uintptr_t)initial_state + (initial_state ? ns : 0)}};
+    const Range outs[5] = {{(uintptr_t)dq, (uintptr_t)dq + nk},
+                           {(uintptr_t)dk, (uintptr_t)dk + nk},
+                           {(uintptr_t)dv, (uintptr_t)dv + nv},
+                           {(uintptr_t)dlog_alpha, (uintptr_t)dlog_alpha + nk},
+                           {(uintptr_t)d_initial_state,
+                            (uintptr_t)d_initial_state + (d_initial_state ? ns : 0)}};
+    for (int a = 0; a < 5; ++a) {
+      for (const Range& r : ins)
+        if (overlap(outs[a], r)) return GLA_ERR_ALIAS;
+      for (int b2 = a + 1; b2 < 5; ++b2)
+        if (overlap(outs[a], outs[b2])) return GLA_ERR_ALIAS;
+    }
+
+    const int n_chunks = (int)((T + kChunk - 1) / kChunk);
+    if (BH * n_chunks > (1LL << 31) - 1) return GLA_ERR_SHAPE;
+    gla::FwdParams f{};
+    f.q = q;
+    f.k = k;
+    f.v = v;
+    f.la = log_alpha;
+    f.out = dq;  // not touched by the state kernels
+    f.initial_state = initial_state;
+    f.inv_tau = 1.f;
+    f.B = B;
+    f.heads = heads;
+    f.H = H;
+    f.W = W;
+    f.T = (int)T;
+    gla::fast_div_constants((unsigned)W, &f.div_w_m, &f.div_w_s);
+    gla::fast_div_constants((unsigned)H, &f.div_h_m, &f.div_h_s);
+    f.scan_dir = scan_dir;
+    f.n_chunks = n_chunks;
+    f.span_chunks = 1;
+    f.n_spans = n_chunks;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const size_t map = (size_t)d_k * d_v;
+    const size_t fwd_floats = (size_t)BH * n_chunks * (map + d_k);
+    const size_t adj_floats = (size_t)BH * (n_chunks + 1) * (map + d_k);
+    void* ws = nullptr;
+    if (hipMallocAsync(&ws, (fwd_floats + adj_floats) * sizeof(float), st) != hipSuccess)
+      return GLA_ERR_HIP;
+    float* w = static_cast<float*>(ws);
+    f.span_state = w;
+    f.span_gate = w + (size_t)BH * n_chunks * map;
+    gla::FwdParams a = f;
+    a.k = q;
+    a.v = d_out;
+    a.initial_state = d_final_state;
+    a.span_state = w + fwd_floats;
+    a.span_gate = a.span_state + (size_t)BH * (n_chunks + 1) * map;
+    a.adj_slots = n_chunks + 1;
+
+    gla::BwdParams pb{};
+    pb.q = q;
+    pb.k = k;
+    pb.v = v;
+    pb.la = log_alpha;
+    pb.dout = d_out;
+    pb.dq = dq;
+    pb.dk = dk;
+    pb.dv = dv;
+    pb.dla = dlog_alpha;
+    pb.fwd_state = f.span_state;
+    pb.adj_state = a.span_state;
+    pb.d_initial_state = d_initial_state;
+    pb.B = B;
+    pb.heads = heads;
+    pb.H = H;
+    pb.W = W;
+    pb.T = (int)T;
+    pb.div_w_m = f.div_w_m;
+    pb.div_h_m = f.div_h_m;
+    pb.div_w_s = f.div_w_s;
+    pb.div_h_s = f.div_h_s;
+    pb.scan_dir = scan_dir;
+    pb.n_chunks = n_chunks;
+
+    const hipEvent_t* ev = t_events_set ? t_events : nullptr;
+    t_events_set = false;
+    hipError_t e = gla::launch_bwd_states(d_k, d_v, f, a, st, ev);
+    if (e == hipSuccess)
+      e = gla::launch_bwd_chunks(d_k, d_v, pb, st, ev ? ev[4] : nullptr, ev ? ev[5] : nullptr);
+    if (hipFreeAsync(ws, st) != hipSuccess) return GLA_ERR_HIP;
+    return e == hipSuccess ? GLA_OK : GLA_ERR_HIP;
+  } catch (...) {
+    return GLA_ERR_HIP;
+  }
+}
+
 int gla_saga_fwd(const void* q, const void* k, const void* v, const void* alpha,
                  const void* beta, int B, int heads, int N, int d_k, int d_v, void* out, float* kv,
                  void* stream) {
@@ -419,6 +540,6 @@ const char* gla_status_str(int status) {
   }
 }
 
-int gla_version(void) { return 130; }
+int gla_version(void) { return 140; }
 
 }  // extern "C"

@@ -1,0 +1,402 @@
+// Backward pass of the chunkwise gated linear attention with key-only decay,
+// for gfx950 (CDNA4, MI355X), float16 tensors, d_k = d_v = 64.
+//
+// Gradients of L = <dO, O> + <dS_final, S_final> for the recurrence
+// S_t = diag(alpha_t) S_{t-1} + k_t^T v_t, o_t = q_t S_t (GTR news write-up,
+// tokendh.com, section "What linear attention saves"), computed chunkwise
+// like the forward pass (section "Where the speed comes from"): the state's
+// adjoint G_t = dL/dS_t runs backwards along the scan,
+// G_t = q_t^T dO_t + diag(alpha_{t+1}) G_{t+1}, which is the forward
+// recurrence read from the end, so the same summary / scan kernels give
+//   E_c : the forward state entering chunk c (summaries of k, v), and
+//   R_c : the adjoint entering chunk c from its right,
+//         R_{c-1} = diag(g_c) R_c + (Q * exp(B))^T dO  over chunk c,
+// after which every chunk is independent.  With B the inclusive cumulative
+// log-decay inside the chunk, for t, s in the chunk:
+//   dq_t = e^{B_t} E_c dO_t + sum_{s<=t} (dO_t . v_s) k_s e^{B_t - B_s}
+//   dk_t = e^{B_end - B_t} R_c v_t + sum_{s>=t} (v_t . dO_s) q_s e^{B_s - B_t}
+//   dv_t = (k_t e^{B_end - B_t}) R_c + sum_{s>=t} ((k_t e^{-B_t}) . (q_s e^{B_s})) dO_s
+//   dlog_alpha_t = sum_{s>=t, s in chunk} (q_s dq_s - k_s dk_s) + rowsum(E_{c+1} * R_c)
+// (the last term is the same sum over every later token, by the adjoint
+// identity dlog_alpha_t = alpha_t * rowsum(G_t * S_{t-1}) at the chunk's end).
+//
+// The chunk kernel (one workgroup per (batch*head, chunk), wave w owning key
+// dims and value dims 16w..16w+15):
+//   1. q, k, v, log-alpha and dO land in LDS (LDS-writing loads, swizzled
+//      rows); B is summed per key dim in float32;
+//   2. float16 operand tiles with every decay factor bounded: Qs = q e^{c}
+//      (c = B - B at the 16-token sub-block start, in [-10, 0]), Kd = k decayed
+//      to its sub-block's end, Ke = k decayed to the chunk's end; the diagonal
+//      sub-blocks use Kd times the sub-block decay back (<= e^10), and the
+//      factors between sub-blocks (<= 1) scale 16x16 accumulators in float32;
+//   3. the score tiles dO V^T, V dO^T and (Q e^B)(K e^-B)^T are formed per
+//      sub-block pair on the matrix cores (every wave forms the ones it needs;
+//      the accumulator of one is the next MFMA's operand, no LDS round trip),
+//      then dq, dk, dv as 16x16 MFMA tiles, outputs rounded to float16 and
+//      stored to their grid cells (scan-order remap as in the forward pass);
+//   4. E_{c+1} = diag(e^{B_end}) E_c + Ke^T V, its row sums against R_c give
+//      the carry, and dlog_alpha is a suffix sum across the 16 lanes of each
+//      tile row plus the later sub-blocks' totals.
+
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gla_device.h"
+#include "gla_internal.h"
+#include "gla_tiles.h"
+
+namespace gla {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kChunk = 64;
+
+__device__ __forceinline__ float ex(float x) { return exp2_fast(x * 1.4426950408889634f); }
+
+__device__ __forceinline__ f16x8 ld8f(const float* a) {
+  const f32x4 lo = *reinterpret_cast<const f32x4*>(a);
+  const f32x4 hi = *reinterpret_cast<const f32x4*>(a + 4);
+  return cat8(to_f16(lo), to_f16(hi));
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
+  static_assert(DK == 64 && DV == 64, "built for 64 key and value dims");
+  constexpr int RB = 128;  // bytes per tile row
+  __shared__ __attribute__((aligned(16))) f16 tq[kChunk * DK], tk[kChunk * DK], tv[kChunk * DV];
+  __shared__ __attribute__((aligned(16))) f16 tla[kChunk * DK], tdo[kChunk * DV];
+  __shared__ __attribute__((aligned(16))) f16 tqs[kChunk * DK], tkd[kChunk * DK];
+  __shared__ __attribute__((aligned(16))) float sB[kChunk * DK];
+  __shared__ float sTot[4][DK];
+  __shared__ float sBst[5][DK];   // B before sub-block I (I = 0..3), [4] = chunk total
+  __shared__ float sCarry[4][DK];
+  __shared__ uint32_t srow[kChunk];
+  f16* const tke = tla;           // k decayed to the chunk end, in place of log-alpha
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n16 = lane & 15, g = lane >> 4;
+
+  const int bh = blockIdx.x / p.n_chunks;
+  const int c = blockIdx.x - bh * p.n_chunks;
+  const int b = bh / p.heads;
+  GridMap gm;
+  gm.H = p.H;
+  gm.W = p.W;
+  gm.dir = (p.scan_dir == 4) ? (b & 3) : p.scan_dir;
+  gm.mw = p.div_w_m;
+  gm.mh = p.div_h_m;
+  gm.sw = p.div_w_s;
+  gm.sh = p.div_h_s;
+
+  const uint32_t seq_bytes = (uint32_t)p.T * RB;
+  const size_t so = (size_t)bh * p.T * DK;
+  const rsrc_t rq = seq_rsrc(static_cast<const f16*>(p.q) + so, seq_bytes);
+  const rsrc_t rk = seq_rsrc(static_cast<const f16*>(p.k) + so, seq_bytes);
+  const rsrc_t rla = seq_rsrc(static_cast<const f16*>(p.la) + so, seq_bytes);
+  const rsrc_t rv = seq_rsrc(static_cast<const f16*>(p.v) + so, seq_bytes);
+  const rsrc_t rdo = seq_rsrc(static_cast<const f16*>(p.dout) + so, seq_bytes);
+  const rsrc_t wdq = seq_rsrc(static_cast<f16*>(p.dq) + so, seq_bytes);
+  const rsrc_t wdk = seq_rsrc(static_cast<f16*>(p.dk) + so, seq_bytes);
+  const rsrc_t wdv = seq_rsrc(static_cast<f16*>(p.dv) + so, seq_bytes);
+  const rsrc_t wdla = seq_rsrc(static_cast<f16*>(p.dla) + so, seq_bytes);
+  const float* E = p.fwd_state + ((size_t)bh * p.n_chunks + c) * DK * DV;
+  const float* R = p.adj_state + ((size_t)bh * (p.n_chunks + 1) + (p.n_chunks - 1 - c)) * DK * DV;
+
+  // ---- 1. tiles, cumulative log-decay
+  const int t0 = c * kChunk;
+  const int valid = min(kChunk, p.T - t0);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int blk = wave * 2 + i;
+    uint32_t cf;
+    bool first;
+    const uint32_t off = dma_offset_cell<RB>(blk, t0, valid, gm, &cf, &first);
+    if (first) srow[(blk * 1024 + 16 * lane) / RB] = cf;
+    dma16(rq, tq + blk * 512, off);
+    dma16(rk, tk + blk * 512, off);
+    dma16(rv, tv + blk * 512, off);
+    dma16(rla, tla + blk * 512, off);
+    dma16(rdo, tdo + blk * 512, off);
+  }
+  wait_barrier<vmcnt_lgkm0_imm(0)>();  // tiles landed, row table written
+
+  {
+    const int i = tid & 63, J = tid >> 6;
+    float run = 0.f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int t = 16 * J + u;
+      run += (float)tla[swz<RB>(t, i)];
+      sB[t * DK + i] = run;
+    }
+    sTot[J][i] = run;
+    __syncthreads();
+    float off = 0.f;
+    for (int j = 0; j < J; ++j) off += sTot[j][i];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) sB[(16 * J + u) * DK + i] += off;
+    if (J == 0) {
+      float acc = 0.f;
+      sBst[0][i] = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc += sTot[j][i];
+        sBst[j + 1][i] = acc;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- 2. bounded float16 operand tiles
+  {
+    const int i = tid & 63, J = tid >> 6;
+    const float bs = sBst[J][i], bs1 = sBst[J + 1][i], be = sBst[4][i];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int t = 16 * J + u;
+      const int e = swz<RB>(t, i);
+      const float bt = sB[t * DK + i];
+      const float q = (float)tq[e], k = (float)tk[e];
+      tqs[e] = (f16)(q * ex(bt - bs));
+      tkd[e] = (f16)(k * ex(bs1 - bt));
+      tke[e] = (f16)(k * ex(be - bt));
+    }
+  }
+  __syncthreads();
+
+  const int kb = wave;          // key dims 16 kb .. owned by this wave (dq, dk, dla)
+  const int vb = wave;          // value dims 16 vb .. (dv, next state rows)
+  const int ki = 16 * kb + 4 * g;  // first of the lane's 4 key dims in a dq / dk tile
+  const int vj = 16 * vb + 4 * g;
+
+  // E and R rows of this wave's key dims, as float16 MFMA A operands
+  // (lane (n, g): row 16 kb + n, columns 32 h + 8g .. + 7)
+  f16x8 ea[2], ra[2], rta[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    ea[h] = ld8f(E + (16 * kb + n16) * DV + 32 * h + 8 * g);
+    ra[h] = ld8f(R + (16 * kb + n16) * DV + 32 * h + 8 * g);
+    // R^T rows 16 vb + n: R[32 h + 8g + e][16 vb + n]
+    f16x8 x;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (f16)R[(32 * h + 8 * g + e) * DV + 16 * vb + n16];
+    rta[h] = x;
+  }
+
+  auto row_off = [&](int t, int col) -> uint32_t {
+    const uint32_t cf = srow[t];
+    return ((cf & 0x7fffffffu) * RB + (uint32_t)col * 2) | (cf & 0x80000000u);
+  };
+  auto store4 = [&](rsrc_t dst, int t, int col, f32x4 x) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, to_f16(x)), dst, row_off(t, col),
+                                          0, 0);
+  };
+
+  // ---- 3a. dq (rows: key dims of this wave, columns: tokens of sub-block I)
+  f32x4 dqv[4];
+#pragma unroll
+  for (int I = 0; I < 4; ++I) {
+    const f16x8 dob0 = ld128(tdo + swz<RB>(16 * I + n16, 8 * g));
+    const f16x8 dob1 = ld128(tdo + swz<RB>(16 * I + n16, 32 + 8 * g));
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int J = 0; J <= I; ++J) {
+      // (V dO^T)[s in J][t in I]: lane (n, g) holds s = 16J + 4g + u, t = 16I + n
+      f32x4 sc = mma32(ld128(tv + swz<RB>(16 * J + n16, 8 * g)), dob0, f32x4{0.f, 0.f, 0.f, 0.f});
+      sc = mma32(ld128(tv + swz<RB>(16 * J + n16, 32 + 8 * g)), dob1, sc);
+      if (J == I) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) sc[u] = (4 * g + u <= n16) ? sc[u] : 0.f;
+      }
+      f16x4 aop = tr_read<RB>(tkd, 16 * J, 16 * kb);  // Kd^T: key dim 16 kb + n, tokens 16J + 4g..
+      if (J == I) {
+        // back to the sub-block start: k e^{-c} = Kd e^{B(J+1) - B(J)} ... per key dim n
+        const int in = 16 * kb + n16;
+        aop = aop * (f16)ex(sBst[J][in] - sBst[J + 1][in]);
+      }
+      f32x4 tt = mma16(aop, to_f16(sc), f32x4{0.f, 0.f, 0.f, 0.f});
+      if (J < I) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) tt[u] *= ex(sBst[I][ki + u] - sBst[J + 1][ki + u]);
+      }
+      acc += tt;
+    }
+    // inter-chunk: (E dO^T)[key dim][token]
+    f32x4 ed = mma32(ea[0], dob0, f32x4{0.f, 0.f, 0.f, 0.f});
+    ed = mma32(ea[1], dob1, ed);
+    const int t = 16 * I + n16;
+    f32x4 dq;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float bst = sBst[I][ki + u];
+      dq[u] = ex(sB[t * DK + ki + u] - bst) * (acc[u] + ex(bst) * ed[u]);
+    }
+    dqv[I] = dq;
+    store4(wdq, t, ki, dq);
+  }
+
+  // ---- 3b. dk (rows: key dims of this wave, columns: tokens of sub-block J)
+  f32x4 dkv[4];
+#pragma unroll
+  for (int J = 0; J < 4; ++J) {
+    const f16x8 vb0 = ld128(tv + swz<RB>(16 * J + n16, 8 * g));
+    const f16x8 vb1 = ld128(tv + swz<RB>(16 * J + n16, 32 + 8 * g));
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int I = J; I < 4; ++I) {
+      // (dO V^T)[s in I][t in J]: lane (n, g) holds s = 16I + 4g + u, t = 16J + n
+      f32x4 sc = mma32(ld128(tdo + swz<RB>(16 * I + n16, 8 * g)), vb0, f32x4{0.f, 0.f, 0.f, 0.f});
+      sc = mma32(ld128(tdo + swz<RB>(16 * I + n16, 32 + 8 * g)), vb1, sc);
+      if (I == J) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) sc[u] = (4 * g + u >= n16) ? sc[u] : 0.f;
+      }
+      f32x4 tt = mma16(tr_read<RB>(tqs, 16 * I, 16 * kb), to_f16(sc), f32x4{0.f, 0.f, 0.f, 0.f});
+      if (I > J) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) tt[u] *= ex(sBst[I][ki + u] - sBst[J][ki + u]);
+      }
+      acc += tt;
+    }
+    // inter-chunk: (R V^T)[key dim][token]
+    f32x4 rv = mma32(ra[0], vb0, f32x4{0.f, 0.f, 0.f, 0.f});
+    rv = mma32(ra[1], vb1, rv);
+    const int t = 16 * J + n16;
+    f32x4 dk;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float bst = sBst[J][ki + u];
+      dk[u] = ex(bst - sB[t * DK + ki + u]) * (acc[u] + ex(sBst[4][ki + u] - bst) * rv[u]);
+    }
+    dkv[J] = dk;
+    store4(wdk, t, ki, dk);
+  }
+
+  // ---- 3c. dv (rows: value dims of this wave, columns: tokens of sub-block J)
+#pragma unroll
+  for (int J = 0; J < 4; ++J) {
+    f16x8 kx0 = ld128(tkd + swz<RB>(16 * J + n16, 8 * g));
+    f16x8 kx1 = ld128(tkd + swz<RB>(16 * J + n16, 32 + 8 * g));
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int I = J; I < 4; ++I) {
+      // ((Q e^B)(K e^-B)^T)[s in I][t in J], bounded operands: Qs rows of I,
+      // and Kd rows of J scaled by e^{B(I) - B(J+1)} (<= 1) for I > J, or by
+      // e^{B(J) - B(J+1)} (>= 1, back to the sub-block start) for I = J;
+      // the factor sits on the contraction index and is applied to Qs here
+      f16x8 qa0 = ld128(tqs + swz<RB>(16 * I + n16, 8 * g));
+      f16x8 qa1 = ld128(tqs + swz<RB>(16 * I + n16, 32 + 8 * g));
+      const int top = (I == J) ? J : I;
+      f16x8 f0, f1;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        f0[e] = (f16)ex(sBst[top][8 * g + e] - sBst[J + 1][8 * g + e]);
+        f1[e] = (f16)ex(sBst[top][32 + 8 * g + e] - sBst[J + 1][32 + 8 * g + e]);
+      }
+      if (I == J) {
+        // the >= 1 factor goes on the keys (Qs stays <= |q|)
+        kx0 = kx0 * f0;
+        kx1 = kx1 * f1;
+      } else {
+        qa0 = qa0 * f0;
+        qa1 = qa1 * f1;
+      }
+      f32x4 sc = mma32(qa0, kx0, f32x4{0.f, 0.f, 0.f, 0.f});
+      sc = mma32(qa1, kx1, sc);
+      if (I == J) {
+        kx0 = ld128(tkd + swz<RB>(16 * J + n16, 8 * g));
+        kx1 = ld128(tkd + swz<RB>(16 * J + n16, 32 + 8 * g));
+#pragma unroll
+        for (int u = 0; u < 4; ++u) sc[u] = (4 * g + u >= n16) ? sc[u] : 0.f;
+      }
+      acc = mma16(tr_read<RB>(tdo, 16 * I, 16 * vb), to_f16(sc), acc);
+    }
+    // inter-chunk: (R^T Ke^T)[value dim][token]
+    f32x4 rk = mma32(rta[0], ld128(tke + swz<RB>(16 * J + n16, 8 * g)), f32x4{0.f, 0.f, 0.f, 0.f});
+    rk = mma32(rta[1], ld128(tke + swz<RB>(16 * J + n16, 32 + 8 * g)), rk);
+    store4(wdv, 16 * J + n16, vj, acc + rk);
+  }
+
+  // ---- 4. next state, carry, dlog_alpha
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc) {
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int P = 0; P < 2; ++P) {
+      const f16x8 av = cat8(tr_read<RB>(tv, 32 * P, 16 * vb), tr_read<RB>(tv, 32 * P + 16, 16 * vb));
+      const f16x8 bk = cat8(tr_read<RB>(tke, 32 * P, 16 * kc), tr_read<RB>(tke, 32 * P + 16, 16 * kc));
+      acc = mma32(av, bk, acc);
+    }
+    // lane (n, g): E_next[i = 16 kc + n][j = 16 vb + 4g + u]
+    const int i = 16 * kc + n16;
+    const float ebe = ex(sBst[4][i]);
+    const f32x4 e4 = *reinterpret_cast<const f32x4*>(E + i * DV + vj);
+    const f32x4 r4 = *reinterpret_cast<const f32x4*>(R + i * DV + vj);
+    float part = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) part += (ebe * e4[u] + acc[u]) * r4[u];
+    part += __shfl_xor(part, 16);
+    part += __shfl_xor(part, 32);
+    if (g == 0) sCarry[vb][i] = part;
+  }
+  __syncthreads();
+
+  {
+    f32x4 running;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      running[u] = ((sCarry[0][ki + u] + sCarry[1][ki + u]) + sCarry[2][ki + u]) + sCarry[3][ki + u];
+#pragma unroll
+    for (int I = 3; I >= 0; --I) {
+      const int t = 16 * I + n16;
+      const f16x4 q4 = ld64(tq + swz<RB>(t, ki));
+      const f16x4 k4 = ld64(tk + swz<RB>(t, ki));
+      f32x4 x;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[u] = (float)q4[u] * dqv[I][u] - (float)k4[u] * dkv[I][u];
+      // suffix sums over the 16 tokens of the tile row (lanes n .. 15)
+#pragma unroll
+      for (int sft = 1; sft < 16; sft <<= 1) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float y = __shfl_down(x[u], sft, 16);
+          x[u] += (n16 + sft < 16) ? y : 0.f;
+        }
+      }
+      f32x4 dla;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        dla[u] = x[u] + running[u];
+        running[u] += __shfl(x[u], 0, 16);
+      }
+      store4(wdla, t, ki, dla);
+    }
+  }
+
+  if (c == 0 && p.d_initial_state != nullptr) {
+    const float* src = p.adj_state + ((size_t)bh * (p.n_chunks + 1) + p.n_chunks) * DK * DV;
+    float* dst = p.d_initial_state + (size_t)bh * DK * DV;
+    for (int e = tid * 4; e < DK * DV; e += kThreads * 4)
+      *reinterpret_cast<f32x4*>(dst + e) = *reinterpret_cast<const f32x4*>(src + e);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_bwd_chunks(int d_k, int d_v, const BwdParams& p, hipStream_t stream,
+                             hipEvent_t start, hipEvent_t stop) {
+  if (d_k != 64 || d_v != 64) return hipErrorInvalidValue;
+  const dim3 grid(p.B * p.heads * p.n_chunks), block(kThreads);
+  const auto kernel = chunk_bwd_f16_kernel<64, 64>;
+  if (start != nullptr || stop != nullptr) {
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, start, stop, 0, p);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace gla

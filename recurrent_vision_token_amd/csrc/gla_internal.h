@@ -29,6 +29,7 @@ struct FwdParams {
   int n_chunks;         // ceil(T / 64)
   int span_chunks;      // chunks handled by one workgroup of the output kernel
   int n_spans;          // ceil(n_chunks / span_chunks)
+  int adj_slots;        // backward pass: summary slots per sequence of the adjoint scan
 };
 
 // Multiply-shift constants for dividing t < 2^31 by d >= 1:
@@ -48,6 +49,44 @@ bool has_variant(Dtype dt, int d_k, int d_v);
 // log alpha = logsigmoid(z) * inv_tau (float16 only).
 hipError_t launch_forward(Dtype dt, int d_k, int d_v, bool gate_logits, const FwdParams& p,
                           hipStream_t stream, hipEvent_t const* events);
+
+// Backward pass, float16, d_k = d_v = 64.  `fwd` describes the forward
+// tensors with one chunk per span (n_spans = n_chunks) and the forward-state
+// workspace; `adj` the adjoint summaries: k = q, v = the output gradient,
+// initial_state = the final-state gradient (or null), adj_slots = n_chunks + 1
+// and its own workspace.  Runs the span-summary and span-scan kernels for
+// both; events: null, or at least four hipEvent_t, recorded at the start of
+// the forward summary, the end of its scan, the start of the adjoint summary
+// and the end of its scan.
+hipError_t launch_bwd_states(int d_k, int d_v, const FwdParams& fwd, const FwdParams& adj,
+                             hipStream_t stream, hipEvent_t const* events);
+
+// The chunk kernel of the backward pass: one workgroup per (batch*head,
+// chunk) turns the chunk's tiles, its forward entry state and the adjoint
+// state entering it from the right into dq, dk, dv and dlog_alpha.
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* la;
+  const void* dout;         // [B][heads][H][W][d_v]
+  void* dq;                 // [B][heads][H][W][d_k]
+  void* dk;
+  void* dv;                 // [B][heads][H][W][d_v]
+  void* dla;                // [B][heads][H][W][d_k]
+  const float* fwd_state;   // [BH][n_chunks][d_k][d_v] entry state of each chunk
+  const float* adj_state;   // [BH][n_chunks + 1][d_k][d_v]: slot n_chunks - 1 - c enters chunk c
+                            // from the right; slot n_chunks is dL/dS_{-1}
+  float* d_initial_state;   // [BH][d_k][d_v], or null
+  int B, heads, H, W, T;
+  unsigned int div_w_m, div_h_m;
+  int div_w_s, div_h_s;
+  int scan_dir;
+  int n_chunks;
+};
+
+hipError_t launch_bwd_chunks(int d_k, int d_v, const BwdParams& p, hipStream_t stream,
+                             hipEvent_t start, hipEvent_t stop);
 
 // One call of the Spatial SwiGLU step (float16), already validated on the host.
 struct SwigluParams {

@@ -39,6 +39,7 @@
 
 #include "gla_device.h"
 #include "gla_internal.h"
+#include "gla_tiles.h"
 
 namespace gla {
 namespace {
@@ -71,39 +72,6 @@ __device__ __forceinline__ float fexp(float x) {
   }
 }
 
-// Scan step t -> row-major grid cell for one of the four directions, with the
-// divisions by W or H done by precomputed multiply-shift constants.
-struct GridMap {
-  int H, W, dir;
-  unsigned int mw, mh;
-  int sw, sh;
-  __device__ __forceinline__ static int div(int t, unsigned int m, int s) {
-    return (int)((__umulhi((unsigned)t, m) + (unsigned)t) >> s);
-  }
-  __device__ __forceinline__ int cell(int t) const {
-    if (dir == 0) return t;
-    if (dir == 1) {
-      const int r = div(t, mw, sw);
-      return r * W + (W - 1 - (t - r * W));
-    }
-    const int c = div(t, mh, sh);
-    const int r = t - c * H;
-    return (dir == 2 ? r : (H - 1 - r)) * W + c;
-  }
-};
-
-__device__ __forceinline__ GridMap grid_map(const FwdParams& p, int b) {
-  GridMap g;
-  g.H = p.H;
-  g.W = p.W;
-  g.dir = (p.scan_dir == 4) ? (b & 3) : p.scan_dir;
-  g.mw = p.div_w_m;
-  g.mh = p.div_h_m;
-  g.sw = p.div_w_s;
-  g.sh = p.div_h_s;
-  return g;
-}
-
 // Row of key / value dim d in a transposed [dim][token] tile: one padding row
 // after every 8 dims, so that the 8 lanes writing dims 8pc+u (pc = 0..7) of a
 // token pair land in different LDS banks.
@@ -114,13 +82,6 @@ __device__ __forceinline__ uint4 sel(bool c, uint4 a, uint4 b) {
   return make_uint4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
 }
 
-// Row access of the float16 kernels goes through buffer resources, one per
-// tensor and sequence: offsets are 32-bit byte offsets inside the sequence's
-// rows, and an offset at or past their end (kNoRow) reads zeros and drops
-// stores.  Rows past the span or the sequence thus need no branch and no
-// select, every load is issued unconditionally, and each wait for a staged
-// tile counts exactly the loads issued after it.
-constexpr uint32_t kNoRow = 0x80000000u;     // beyond every sequence (its rows span < 2 GiB)
 __device__ __forceinline__ uint4 bload(rsrc_t r, uint32_t off) {
   const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
   return make_uint4(x[0], x[1], x[2], x[3]);
@@ -128,25 +89,6 @@ __device__ __forceinline__ uint4 bload(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ void bstore(rsrc_t r, uint32_t off, uint4 d) {
   __builtin_amdgcn_raw_buffer_store_b128(u32x4{d.x, d.y, d.z, d.w}, r, off, 0, 0);
 }
-
-// The rows of one (batch, head) sequence: q, k, log-alpha [T][d_k], v, out [T][d_v].
-struct SeqBufs {
-  rsrc_t q, k, la, v, out;
-};
-template <int DK, int DV>
-__device__ __forceinline__ SeqBufs seq_bufs(const FwdParams& p, int bh) {
-  typedef _Float16 h;
-  const uint32_t kb = (uint32_t)p.T * DK * 2, vb = (uint32_t)p.T * DV * 2;
-  const size_t ok = (size_t)bh * p.T * DK, ov = (size_t)bh * p.T * DV;
-  SeqBufs s;
-  s.q = seq_rsrc(static_cast<const h*>(p.q) + ok, kb);
-  s.k = seq_rsrc(static_cast<const h*>(p.k) + ok, kb);
-  s.la = seq_rsrc(static_cast<const h*>(p.la) + ok, kb);
-  s.v = seq_rsrc(static_cast<const h*>(p.v) + ov, vb);
-  s.out = seq_rsrc(static_cast<h*>(p.out) + ov, vb);
-  return s;
-}
-
 
 // Pair index of sub-block pair (I, J), J < I, in the factor table.
 __device__ __forceinline__ constexpr int pair_index(int I, int J) { return I * (I - 1) / 2 + J; }
@@ -790,35 +732,6 @@ __device__ __forceinline__ f16x4 upper_incl(float v) {
 }
 
 
-// Chunk tiles in LDS are filled by the LDS-writing loads of gla_device.h.
-// Source offset of this lane's 16 bytes in block `blk` (1 KB) of a tile with
-// RB-byte rows; rows of chunk-local tokens at or past `valid` get an offset
-// past the buffer, so they read as zero.  Branch-free on purpose: a lane-
-// dependent branch here would split one LDS-writing load into two partial
-// ones and upset the explicit wait counts.
-template <int RB>
-__device__ __forceinline__ uint32_t dma_offset(int blk, int t0, int valid, const GridMap& gm) {
-  const int lane = threadIdx.x & 63;
-  const int byte = blk * 1024 + 16 * lane;
-  const int r = byte / RB, pp = (byte % RB) / 16;
-  const uint32_t off = (uint32_t)gm.cell(t0 + r) * RB + (uint32_t)((pp ^ (r & 7)) * 16);
-  return off | ((uint32_t)(r >= valid) << 31);
-}
-// The same, also handing back the row's grid cell with the out-of-range flag
-// in bit 31 (for the lanes that load piece 0 of a row, first_piece is set).
-template <int RB>
-__device__ __forceinline__ uint32_t dma_offset_cell(int blk, int t0, int valid, const GridMap& gm,
-                                                    uint32_t* cell_flag, bool* first_piece) {
-  const int lane = threadIdx.x & 63;
-  const int byte = blk * 1024 + 16 * lane;
-  const int r = byte / RB, pp = (byte % RB) / 16;
-  const uint32_t flag = (uint32_t)(r >= valid) << 31;
-  const uint32_t cell = (uint32_t)gm.cell(t0 + r);
-  *cell_flag = cell | flag;
-  *first_piece = pp == 0;
-  return (cell * RB + (uint32_t)((pp ^ (r & 7)) * 16)) | flag;
-}
-
 // ---------------------------------------------------------------------------
 // Output kernel, float16.  The span is walked in 32-token steps (two 16-token
 // sub-blocks).  q, k, log-alpha and v of a step land row-major in LDS straight
@@ -1134,7 +1047,16 @@ struct SumTile {
   f16* v;
 };
 
-template <int DK, int DV, bool GATE>
+//
+// ADJ instantiates the same kernel for the backward pass's adjoint summaries
+// (spans of one chunk): with q in place of k and the output gradient in place
+// of v it folds dR = (Q * exp(B))^T dO, B the decay from the chunk start
+// through each token (inclusive), and writes summary c to slot
+// adj_slots - 2 - c, so that the scan over the slots runs from the end of the
+// sequence to its start; the first chunk also writes the neutral summary
+// (gate 1, state 0) into the last slot, whose entry state is then the
+// gradient of the state before the first step.
+template <int DK, int DV, bool GATE, bool ADJ = false>
 __global__ __launch_bounds__(kThreads) void span_summary_f16_kernel(FwdParams p) {
   // six separate LDS objects, so the compiler's own waits for the LDS-writing
   // loads can tell the tiles apart
@@ -1179,11 +1101,12 @@ __global__ __launch_bounds__(kThreads) void span_summary_f16_kernel(FwdParams p)
     }
   };
 
-  // A operands: strictly upper triangular (s > t) and all-ones 16x16 blocks.
+  // A operands: strictly upper triangular (s > t; lower inclusive, s <= t,
+  // for the adjoint) and all-ones 16x16 blocks.
   f16x4 m_upper, m_ones;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    m_upper[u] = (f16)((4 * g + u > n16) ? 1.f : 0.f);
+    m_upper[u] = (f16)((ADJ ? (4 * g + u <= n16) : (4 * g + u > n16)) ? 1.f : 0.f);
     m_ones[u] = (f16)1.f;
   }
 
@@ -1209,10 +1132,18 @@ __global__ __launch_bounds__(kThreads) void span_summary_f16_kernel(FwdParams p)
       }
       f32x4 rest[4];
       f32x4 c = gdec[d];
+      if constexpr (ADJ) {
 #pragma unroll
-      for (int J = 3; J >= 0; --J) {
-        rest[J] = mma16(m_upper, lat[J], c);
-        c = mma16(m_ones, lat[J], c);
+        for (int J = 0; J < 4; ++J) {
+          rest[J] = mma16(m_upper, lat[J], c);
+          c = mma16(m_ones, lat[J], c);
+        }
+      } else {
+#pragma unroll
+        for (int J = 3; J >= 0; --J) {
+          rest[J] = mma16(m_upper, lat[J], c);
+          c = mma16(m_ones, lat[J], c);
+        }
       }
       gdec[d] = c;
       f16x4 kl[4];
@@ -1252,7 +1183,9 @@ __global__ __launch_bounds__(kThreads) void span_summary_f16_kernel(FwdParams p)
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
-  float* dst = p.span_state + ((size_t)bh * p.n_spans + span) * DK * DV;
+  const size_t slots = ADJ ? (size_t)p.adj_slots : (size_t)p.n_spans;
+  const size_t slot = ADJ ? (size_t)(p.adj_slots - 2 - span) : (size_t)span;
+  float* dst = p.span_state + ((size_t)bh * slots + slot) * DK * DV;
 #pragma unroll
   for (int d = 0; d < NDB; ++d) {
     const int dim = 16 * (wave + 4 * d) + n16;
@@ -1260,8 +1193,16 @@ __global__ __launch_bounds__(kThreads) void span_summary_f16_kernel(FwdParams p)
     for (int cb = 0; cb < NCB; ++cb)
       *reinterpret_cast<f32x4*>(dst + dim * DV + 16 * cb + 4 * g) = st[d][cb];
     if (g == 0)
-      p.span_gate[((size_t)bh * p.n_spans + span) * DK + dim] =
+      p.span_gate[((size_t)bh * slots + slot) * DK + dim] =
           exp2_fast(gdec[d][0] * 1.4426950408889634f);
+    if (ADJ && span == 0) {
+      // neutral summary in the last slot
+      float* last = p.span_state + ((size_t)bh * slots + slots - 1) * DK * DV;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+        *reinterpret_cast<f32x4*>(last + dim * DV + 16 * cb + 4 * g) = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (g == 0) p.span_gate[((size_t)bh * slots + slots - 1) * DK + dim] = 1.f;
+    }
   }
 }
 
@@ -1377,6 +1318,55 @@ bool has_variant(Dtype dt, int d_k, int d_v) {
 hipError_t launch_forward(Dtype dt, int d_k, int d_v, bool gate_logits, const FwdParams& p,
                           hipStream_t stream, hipEvent_t const* ev) {
   return launch_forward_impl(dt, d_k, d_v, gate_logits, p, stream, ev);
+}
+
+namespace {
+
+// A kernel launch whose dispatch records `start` and / or `stop` (either may
+// be null), so one event pair can bracket several kernels.
+template <class K>
+hipError_t launch_marked(K kernel, dim3 grid, hipStream_t stream, const FwdParams& p,
+                         hipEvent_t start, hipEvent_t stop) {
+  if (start != nullptr || stop != nullptr) {
+    hipExtLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, start, stop, 0, p);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+template <int DK, int DV>
+hipError_t launch_bwd_states_variant(const FwdParams& fwd, const FwdParams& adj,
+                                     hipStream_t stream, hipEvent_t const* ev) {
+  const int BH = fwd.B * fwd.heads;
+  const dim3 scan_grid(BH, DK * DV / kScanElems);
+  hipError_t e;
+  // forward entry state of every chunk
+  if ((e = launch_marked(span_summary_f16_kernel<DK, DV, false, false>, dim3(BH * fwd.n_spans),
+                         stream, fwd, ev ? ev[0] : nullptr, nullptr)) != hipSuccess)
+    return e;
+  if ((e = launch_marked(span_scan_kernel<DK, DV>, scan_grid, stream, fwd, nullptr,
+                         ev ? ev[1] : nullptr)) != hipSuccess)
+    return e;
+  // adjoint state entering every chunk from its right, and the gradient of
+  // the state before the first step in the extra last slot
+  FwdParams sum = adj;
+  sum.n_spans = adj.adj_slots - 1;
+  if ((e = launch_marked(span_summary_f16_kernel<DK, DV, false, true>, dim3(BH * sum.n_spans),
+                         stream, sum, ev ? ev[2] : nullptr, nullptr)) != hipSuccess)
+    return e;
+  FwdParams scan = adj;
+  scan.n_spans = adj.adj_slots;
+  return launch_marked(span_scan_kernel<DK, DV>, scan_grid, stream, scan, nullptr,
+                       ev ? ev[3] : nullptr);
+}
+
+}  // namespace
+
+hipError_t launch_bwd_states(int d_k, int d_v, const FwdParams& fwd, const FwdParams& adj,
+                             hipStream_t stream, hipEvent_t const* ev) {
+  if (d_k == 64 && d_v == 64) return launch_bwd_states_variant<64, 64>(fwd, adj, stream, ev);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace gla

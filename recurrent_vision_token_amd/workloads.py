@@ -170,3 +170,17 @@ def make_saga_inputs(B, heads, N, d_k, d_v, seed=0):
     a = (np.float32(1.0) / (np.float32(1.0) + np.exp(-za))).astype(np.float16)
     b = (np.float32(1.0) / (np.float32(1.0) + np.exp(-zb))).astype(np.float16)
     return q, k, v, a, b
+
+
+def make_bwd_inputs(B, heads, H, W, d_v, d_k=64, seed=0):
+    """Return (d_out, d_final_state, initial_state) for the backward pass.
+
+    Recipe: numpy.random.default_rng(seed) draws d_out ~ N(0, 1) as float16
+    [B, heads, H, W, d_v], then d_final_state and initial_state ~ N(0, 1) / 8
+    as float32 [B, heads, d_k, d_v], in that order.
+    """
+    rng = np.random.default_rng(seed)
+    do = rng.standard_normal((B, heads, H, W, d_v), dtype=np.float32).astype(np.float16)
+    dfin = (rng.standard_normal((B, heads, d_k, d_v), dtype=np.float32) * np.float32(0.125))
+    init = (rng.standard_normal((B, heads, d_k, d_v), dtype=np.float32) * np.float32(0.125))
+    return do, dfin, init
