@@ -67,7 +67,8 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) f16 tq[kChunk * DK], tk[kChunk * DK], tv[kChunk * DV];
   __shared__ __attribute__((aligned(16))) f16 tla[kChunk * DK], tdo[kChunk * DV];
   __shared__ __attribute__((aligned(16))) f16 tqs[kChunk * DK], tkd[kChunk * DK];
-  __shared__ __attribute__((aligned(16))) float sB[kChunk * DK];
+  __shared__ __attribute__((aligned(16))) float sEc[kChunk * DK];  // e^{c_t}, c = decay since the sub-block start
+  __shared__ __attribute__((aligned(16))) f16 sF[5][5][DK];  // e^{Bst_a - Bst_b} per key dim
   __shared__ float sTot[4][DK];
   __shared__ float sBst[5][DK];   // B before sub-block I (I = 0..3), [4] = chunk total
   __shared__ float sCarry[4][DK];
@@ -123,21 +124,35 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
   }
   wait_barrier<vmcnt_lgkm0_imm(0)>();  // tiles landed, row table written
 
+  // Thread (key dim i, sub-block J) walks its 16 tokens: alpha_t = e^{la_t},
+  // e^{c_t} as a running product from the sub-block start and the decay to
+  // the sub-block end as a running product from its end; one exponential per
+  // token.
   {
     const int i = tid & 63, J = tid >> 6;
-    float run = 0.f;
+    float al[16];
+    float tot = 0.f, ec = 1.f;
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       const int t = 16 * J + u;
-      run += (float)tla[swz<RB>(t, i)];
-      sB[t * DK + i] = run;
+      const int e = swz<RB>(t, i);
+      const float la = (float)tla[e];
+      al[u] = ex(la);
+      tot += la;
+      ec *= al[u];
+      sEc[t * DK + i] = ec;
+      tqs[e] = (f16)((float)tq[e] * ec);
     }
-    sTot[J][i] = run;
-    __syncthreads();
-    float off = 0.f;
-    for (int j = 0; j < J; ++j) off += sTot[j][i];
+    float sfx = 1.f, kf[16];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) sB[(16 * J + u) * DK + i] += off;
+    for (int u = 15; u >= 0; --u) {
+      const int e = swz<RB>(16 * J + u, i);
+      kf[u] = (float)tk[e] * sfx;   // k decayed to the sub-block end
+      tkd[e] = (f16)kf[u];
+      sfx *= al[u];
+    }
+    sTot[J][i] = tot;
+    __syncthreads();
     if (J == 0) {
       float acc = 0.f;
       sBst[0][i] = 0.f;
@@ -147,22 +162,20 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
         sBst[j + 1][i] = acc;
       }
     }
-  }
-  __syncthreads();
-
-  // ---- 2. bounded float16 operand tiles
-  {
-    const int i = tid & 63, J = tid >> 6;
-    const float bs = sBst[J][i], bs1 = sBst[J + 1][i], be = sBst[4][i];
+    __syncthreads();
+    // k decayed to the chunk end = k decayed to its sub-block end times the
+    // decay of the later sub-blocks (log-alpha's tile is free now)
+    const float to_end = ex(sBst[4][i] - sBst[J + 1][i]);
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       const int t = 16 * J + u;
       const int e = swz<RB>(t, i);
-      const float bt = sB[t * DK + i];
-      const float q = (float)tq[e], k = (float)tk[e];
-      tqs[e] = (f16)(q * ex(bt - bs));
-      tkd[e] = (f16)(k * ex(bs1 - bt));
-      tke[e] = (f16)(k * ex(be - bt));
+      tke[e] = (f16)(kf[u] * to_end);
+    }
+    // factors between sub-block boundaries
+    for (int ab = J; ab < 25; ab += 4) {
+      const int a = ab / 5, bb = ab % 5;
+      sF[a][bb][i] = (f16)ex(sBst[a][i] - sBst[bb][i]);
     }
   }
   __syncthreads();
@@ -213,14 +226,14 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
       }
       f16x4 aop = tr_read<RB>(tkd, 16 * J, 16 * kb);  // Kd^T: key dim 16 kb + n, tokens 16J + 4g..
       if (J == I) {
-        // back to the sub-block start: k e^{-c} = Kd e^{B(J+1) - B(J)} ... per key dim n
-        const int in = 16 * kb + n16;
-        aop = aop * (f16)ex(sBst[J][in] - sBst[J + 1][in]);
+        // back to the sub-block start: k e^{-c} = Kd e^{Bst_J - Bst_{J+1}}, per key dim n
+        aop = aop * sF[J][J + 1][16 * kb + n16];
       }
       f32x4 tt = mma16(aop, to_f16(sc), f32x4{0.f, 0.f, 0.f, 0.f});
       if (J < I) {
+        const f16x4 f = ld64(&sF[I][J + 1][ki]);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) tt[u] *= ex(sBst[I][ki + u] - sBst[J + 1][ki + u]);
+        for (int u = 0; u < 4; ++u) tt[u] *= (float)f[u];
       }
       acc += tt;
     }
@@ -228,12 +241,11 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
     f32x4 ed = mma32(ea[0], dob0, f32x4{0.f, 0.f, 0.f, 0.f});
     ed = mma32(ea[1], dob1, ed);
     const int t = 16 * I + n16;
+    const f32x4 ec = *reinterpret_cast<const f32x4*>(&sEc[t * DK + ki]);
+    const f16x4 fb = ld64(&sF[I][0][ki]);
     f32x4 dq;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float bst = sBst[I][ki + u];
-      dq[u] = ex(sB[t * DK + ki + u] - bst) * (acc[u] + ex(bst) * ed[u]);
-    }
+    for (int u = 0; u < 4; ++u) dq[u] = ec[u] * (acc[u] + (float)fb[u] * ed[u]);
     dqv[I] = dq;
     store4(wdq, t, ki, dq);
   }
@@ -256,8 +268,9 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
       }
       f32x4 tt = mma16(tr_read<RB>(tqs, 16 * I, 16 * kb), to_f16(sc), f32x4{0.f, 0.f, 0.f, 0.f});
       if (I > J) {
+        const f16x4 f = ld64(&sF[I][J][ki]);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) tt[u] *= ex(sBst[I][ki + u] - sBst[J][ki + u]);
+        for (int u = 0; u < 4; ++u) tt[u] *= (float)f[u];
       }
       acc += tt;
     }
@@ -265,12 +278,12 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
     f32x4 rv = mma32(ra[0], vb0, f32x4{0.f, 0.f, 0.f, 0.f});
     rv = mma32(ra[1], vb1, rv);
     const int t = 16 * J + n16;
+    const f32x4 ec = *reinterpret_cast<const f32x4*>(&sEc[t * DK + ki]);
+    const f16x4 fe = ld64(&sF[4][J][ki]);
     f32x4 dk;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float bst = sBst[J][ki + u];
-      dk[u] = ex(bst - sB[t * DK + ki + u]) * (acc[u] + ex(sBst[4][ki + u] - bst) * rv[u]);
-    }
+    for (int u = 0; u < 4; ++u)
+      dk[u] = __builtin_amdgcn_rcpf(ec[u]) * (acc[u] + (float)fe[u] * rv[u]);
     dkv[J] = dk;
     store4(wdk, t, ki, dk);
   }
@@ -290,12 +303,8 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
       f16x8 qa0 = ld128(tqs + swz<RB>(16 * I + n16, 8 * g));
       f16x8 qa1 = ld128(tqs + swz<RB>(16 * I + n16, 32 + 8 * g));
       const int top = (I == J) ? J : I;
-      f16x8 f0, f1;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        f0[e] = (f16)ex(sBst[top][8 * g + e] - sBst[J + 1][8 * g + e]);
-        f1[e] = (f16)ex(sBst[top][32 + 8 * g + e] - sBst[J + 1][32 + 8 * g + e]);
-      }
+      const f16x8 f0 = ld128(&sF[top][J + 1][8 * g]);
+      const f16x8 f1 = ld128(&sF[top][J + 1][32 + 8 * g]);
       if (I == J) {
         // the >= 1 factor goes on the keys (Qs stays <= |q|)
         kx0 = kx0 * f0;
