@@ -11,7 +11,8 @@ so that the bytes touched between two reuses of a copy exceed the 256 MB
 last-level (Infinity) cache: every call streams from HBM as a real layer
 stack would, instead of re-reading cache-resident data.
 
-Beside it, the same protocol times the block's other token mixer, the
+Beside it, the same protocol times the backward pass of the same workload
+(gla_chunk_bwd, under "backward"), the block's other token mixer, the
 Spatial SwiGLU step (gla_spatial_swiglu) on the 16.4K grid with 2048 hidden
 channels, reported under "spatial_swiglu", and the SAGA-style non-causal
 gated linear attention (gla_saga_fwd) on the same token count, under "saga".
@@ -37,8 +38,9 @@ LLC_BYTES = 256 << 20           # Infinity Cache
 KERNEL_SRC = os.path.join(ROOT, "recurrent_vision_token_amd", "csrc", "gla_kernels.hip")
 SWIGLU_SRC = os.path.join(ROOT, "recurrent_vision_token_amd", "csrc", "swiglu_kernels.hip")
 SAGA_SRC = os.path.join(ROOT, "recurrent_vision_token_amd", "csrc", "saga_kernels.hip")
+BWD_SRC = os.path.join(ROOT, "recurrent_vision_token_amd", "csrc", "gla_bwd_kernels.hip")
 KERNEL_NAMES = ("span_summary", "span_scan", "chunk_output", "spatial_swiglu", "saga_kv_partial",
-                "saga_kv_reduce", "saga_out")
+                "saga_kv_reduce", "saga_out", "chunk_bwd")
 
 
 DEVICE_HDR = os.path.join(ROOT, "recurrent_vision_token_amd", "csrc", "gla_device.h")
@@ -47,14 +49,22 @@ DEVICE_HDR = os.path.join(ROOT, "recurrent_vision_token_amd", "csrc", "gla_devic
 def source_of(kernel):
     if kernel == "spatial_swiglu":
         return SWIGLU_SRC
+    if kernel == "chunk_bwd":
+        return BWD_SRC
     return SAGA_SRC if kernel.startswith("saga") else KERNEL_SRC
+
+
+TILES_HDR = os.path.join(ROOT, "recurrent_vision_token_amd", "csrc", "gla_tiles.h")
 
 
 def source_hash(kernel):
     """Hash of the device code a kernel is built from (its file and the shared
-    device header)."""
+    device headers)."""
     h = hashlib.sha256()
-    for path in (source_of(kernel), DEVICE_HDR):
+    paths = [source_of(kernel), DEVICE_HDR]
+    if source_of(kernel) in (KERNEL_SRC, BWD_SRC):
+        paths.append(TILES_HDR)
+    for path in paths:
         h.update(open(path, "rb").read())
     return h.hexdigest()
 
@@ -299,6 +309,137 @@ def swiglu_summary(swl, ms_call, k_ms, cpu):
                      if swl.name == SWIGLU_WORKLOAD else None,
                      "kernel": "spatial_swiglu", "algorithmic_bytes_per_launch": nb,
                      "avg_launch_us": round(k_ms * 1e3, 2)},
+        "cpu_baseline": cpu,
+    }
+
+
+class BwdRunner:
+    """Device copies of a workload's inputs plus output gradients, cycled
+    across backward calls like Runner; every call passes an initial state and
+    a final-state gradient and asks for all five gradients."""
+
+    def __init__(self, wl, torch, min_sets_bytes=2 * LLC_BYTES):
+        from recurrent_vision_token_amd import _lib
+        from recurrent_vision_token_amd.workloads import make_bwd_inputs, workload_inputs
+        self.wl = wl
+        dev = torch.device("cuda:0")
+        self.host = {}
+        for seed, _ in wl.calls:
+            if seed not in self.host:
+                self.host[seed] = workload_inputs(wl, seed) + make_bwd_inputs(
+                    wl.B, wl.heads, wl.H, wl.W, wl.d_v, wl.d_k, seed=seed + 1000)
+        per_call = bwd_bytes(wl)["call"]
+        reps = max(1, math.ceil(min_sets_bytes / (per_call * len(wl.calls))))
+        self.sets = []
+        for _ in range(reps):
+            for seed, d in wl.calls:
+                x = [torch.from_numpy(a).to(dev) for a in self.host[seed]]
+                outs = [torch.empty_like(x[i]) for i in (0, 1, 2, 3)] + [torch.empty_like(x[6])]
+                self.sets.append((x, outs, d))
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        self.fn = _lib.load().gla_chunk_bwd
+        self.args = [tuple(t.data_ptr() for t in x[:5]) + (x[5].data_ptr(), x[6].data_ptr(), d,
+                                                           wl.B, wl.heads, wl.H, wl.W, wl.d_k,
+                                                           wl.d_v, wl.chunk) +
+                     tuple(o.data_ptr() for o in outs) + (stream,)
+                     for (x, outs, d) in self.sets]
+        self.cursor = 0
+        torch.cuda.synchronize()
+
+    def step(self, events=None):
+        from recurrent_vision_token_amd import _lib
+        for c in range(len(self.wl.calls)):
+            a = self.args[self.cursor]
+            self.cursor = (self.cursor + 1) % len(self.sets)
+            if events is not None:
+                rc = _lib.set_kernel_events([e.cuda_event for e in events[c]])
+                if rc != 0:
+                    raise RuntimeError("gla_set_kernel_events failed: %d" % rc)
+            rc = self.fn(*a)
+            if rc != 0:
+                raise RuntimeError("gla_chunk_bwd failed: %d" % rc)
+
+
+def bwd_bytes(wl):
+    """Algorithmic bytes of one backward call: read q, k, v, log_alpha, d_out,
+    write dq, dk, dv, dlog_alpha (fp16), the states in and out (fp32); and the
+    chunk kernel's own traffic, which adds the forward and adjoint state of
+    every chunk (fp32) to the tensors."""
+    th = wl.B * wl.heads * wl.T
+    bh = wl.B * wl.heads
+    st = wl.d_k * wl.d_v * 4
+    n = -(-wl.T // wl.chunk)
+    tensors = th * 2 * (3 * wl.d_k + 2 * wl.d_v) + th * 2 * (3 * wl.d_k + wl.d_v)
+    return {"call": tensors + 3 * bh * st, "chunk_bwd": tensors + 2 * bh * n * st + bh * st}
+
+
+def time_bwd(wl, torch, steps, warmup):
+    r = BwdRunner(wl, torch)
+    ncall = len(wl.calls)
+    log("[bench] %s backward: %d device sets (%.0f MB), %d calls/step" %
+        (wl.name, len(r.sets), len(r.sets) * bwd_bytes(wl)["call"] / 1e6, ncall))
+    for _ in range(warmup):
+        r.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        r.step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(ncall)]
+           for _ in range(steps)]
+    stream = torch.cuda.current_stream()
+    for per_step in evs:
+        for per_call in per_step:
+            for e in per_call:
+                e.record(stream)
+    torch.cuda.synchronize()
+    for s_ in range(steps):
+        r.step(evs[s_])
+    torch.cuda.synchronize()
+    flat = [e for per_step in evs for e in per_step]
+    k_ms = {"forward_states": sum(e[0].elapsed_time(e[1]) for e in flat) / len(flat),
+            "adjoint_states": sum(e[2].elapsed_time(e[3]) for e in flat) / len(flat),
+            "chunk_bwd": sum(e[4].elapsed_time(e[5]) for e in flat) / len(flat),
+            "call": sum(e[0].elapsed_time(e[5]) for e in flat) / len(flat)}
+    return r, ms_step, k_ms
+
+
+def bwd_cpu_baseline(wl, host):
+    """The backward oracle as it stands on one full call of the workload."""
+    from oracle import gla_backward
+    seed, d = wl.calls[0]
+    q, k, v, la, do, dfin, init = host[seed]
+    t0 = time.perf_counter()
+    c0 = time.process_time()
+    gla_backward(q, k, v, la, do, d, d_final_state=dfin, initial_state=init)
+    wall = time.perf_counter() - t0
+    cores = max(1, int(round((time.process_time() - c0) / wall)))
+    return {"value": wl.B * wl.T / wall, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": "one full backward call (%s, direction %d, numpy float64 reverse token "
+                      "loop), %.1f s wall" % (wl.name, d, wall)}
+
+
+def bwd_summary(wl, ms_step, k_ms, cpu):
+    nb = bwd_bytes(wl)
+    ach = nb["chunk_bwd"] / (k_ms["chunk_bwd"] * 1e-3) / 1e9
+    path = nb["call"] / (k_ms["call"] * 1e-3) / 1e9
+    tokens = len(wl.calls) * wl.B * wl.T
+    return {
+        "entry": "gla_chunk_bwd: dq, dk, dv, dlog_alpha, d_initial_state (fp16, fp32 states)",
+        "workload": describe(wl) + "; d_out ~ N(0,1), d_final_state and initial_state ~ N(0,1)/8",
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "ms_per_step": round(ms_step, 4),
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic_from_profiles(wl.name, "chunk_bwd"),
+                     "kernel": "chunk_bwd", "algorithmic_bytes_per_launch": nb["chunk_bwd"],
+                     "avg_launch_us": round(k_ms["chunk_bwd"] * 1e3, 2)},
+        "path": {"gpu_us_per_call": round(k_ms["call"] * 1e3, 2),
+                 "algorithmic_bytes_per_call": nb["call"],
+                 "achieved_GBps": round(path, 1), "hbm_frac": round(path / HBM_PEAK_GBPS, 4),
+                 "kernel_us": {k: round(v * 1e3, 2) for k, v in k_ms.items() if k != "call"}},
         "cpu_baseline": cpu,
     }
 
@@ -566,6 +707,8 @@ def main():
                     help="skip the extended entry point (fused gate + initial state) line")
     ap.add_argument("--swiglu", default=SWIGLU_WORKLOAD,
                     help="Spatial SwiGLU workload to time beside the attention path ('' to skip)")
+    ap.add_argument("--no-bwd", action="store_true",
+                    help="skip the backward pass line (gla_chunk_bwd on the main workload)")
     ap.add_argument("--saga", default=SAGA_WORKLOAD,
                     help="SAGA non-causal gated attention workload to time ('' to skip)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -632,6 +775,15 @@ def main():
         log("[bench] %s extended entry: %.3f ms/step, %.3e tokens/s, kernels %s" %
             (wl.name, ms3, s3["value"], s3["path"]["kernel_us"]))
 
+    bwd = None
+    if not args.no_bwd and wl.dtype == "fp16" and wl.d_k == 64 and wl.d_v == 64:
+        brun, ms_b, k_b = time_bwd(wl, torch, max(10, args.steps // 4), max(3, args.warmup // 4))
+        b_cpu = None if args.no_cpu_baseline else bwd_cpu_baseline(wl, brun.host)
+        bwd = bwd_summary(wl, ms_b, k_b, b_cpu)
+        log("[bench] %s backward: %.3f ms/step, %.3e tokens/s, kernels %s" %
+            (wl.name, ms_b, bwd["value"], bwd["path"]["kernel_us"]))
+        del brun
+
     swiglu = None
     if args.swiglu:
         from recurrent_vision_token_amd.workloads import SWIGLU_WORKLOADS
@@ -679,6 +831,7 @@ def main():
         "cpu_baseline": cpu,
         "secondary": secondary,
         "fused_gate_initial_state": ext,
+        "backward": bwd,
         "spatial_swiglu": swiglu,
         "saga": saga,
     }
