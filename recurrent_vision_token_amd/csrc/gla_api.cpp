@@ -351,26 +351,27 @@ int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* log_a
     gla::fast_div_constants((unsigned)H, &f.div_h_m, &f.div_h_s);
     f.scan_dir = scan_dir;
     f.n_chunks = n_chunks;
-    f.span_chunks = 1;
-    f.n_spans = n_chunks;
+    f.span_chunks = 2;  // the chunk kernel forms the other chunk's state of a pair
+    f.n_spans = (n_chunks + 1) / 2;
+    const int n_spans = f.n_spans;
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     const size_t map = (size_t)d_k * d_v;
-    const size_t fwd_floats = (size_t)BH * n_chunks * (map + d_k);
-    const size_t adj_floats = (size_t)BH * (n_chunks + 1) * (map + d_k);
+    const size_t fwd_floats = (size_t)BH * n_spans * (map + d_k);
+    const size_t adj_floats = (size_t)BH * (n_spans + 1) * (map + d_k);
     void* ws = nullptr;
     if (hipMallocAsync(&ws, (fwd_floats + adj_floats) * sizeof(float), st) != hipSuccess)
       return GLA_ERR_HIP;
     float* w = static_cast<float*>(ws);
     f.span_state = w;
-    f.span_gate = w + (size_t)BH * n_chunks * map;
+    f.span_gate = w + (size_t)BH * n_spans * map;
     gla::FwdParams a = f;
     a.k = q;
     a.v = d_out;
     a.initial_state = d_final_state;
     a.span_state = w + fwd_floats;
-    a.span_gate = a.span_state + (size_t)BH * (n_chunks + 1) * map;
-    a.adj_slots = n_chunks + 1;
+    a.span_gate = a.span_state + (size_t)BH * (n_spans + 1) * map;
+    a.adj_slots = n_spans + 1;
 
     gla::BwdParams pb{};
     pb.q = q;
@@ -396,6 +397,7 @@ int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* log_a
     pb.div_h_s = f.div_h_s;
     pb.scan_dir = scan_dir;
     pb.n_chunks = n_chunks;
+    pb.n_spans = n_spans;
 
     const hipEvent_t* ev = t_events_set ? t_events : nullptr;
     t_events_set = false;

@@ -103,12 +103,28 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
   const rsrc_t wdk = seq_rsrc(static_cast<f16*>(p.dk) + so, seq_bytes);
   const rsrc_t wdv = seq_rsrc(static_cast<f16*>(p.dv) + so, seq_bytes);
   const rsrc_t wdla = seq_rsrc(static_cast<f16*>(p.dla) + so, seq_bytes);
-  const float* E = p.fwd_state + ((size_t)bh * p.n_chunks + c) * DK * DV;
-  const float* R = p.adj_state + ((size_t)bh * (p.n_chunks + 1) + (p.n_chunks - 1 - c)) * DK * DV;
+  // Chunk c is position pos of span sp (two chunks per span).  The span
+  // states give the forward state entering the span's first chunk and the
+  // adjoint entering its last chunk from the right; the other chunk of a
+  // two-chunk span forms the missing one from its partner's tiles:
+  //   second chunk: E_c = diag(g_{c-1}) E_span + (Ke_{c-1})^T V_{c-1}
+  //   first chunk:  R_c = diag(g_{c+1}) R_span + (Q_{c+1} e^{B})^T dO_{c+1}
+  const int sp = c >> 1, pos = c & 1;
+  const int span_len = min(2, p.n_chunks - 2 * sp);
+  const bool e_from_partner = pos == 1;
+  const bool r_from_partner = pos == 0 && span_len == 2;
+  const float* E_span = p.fwd_state + ((size_t)bh * p.n_spans + sp) * DK * DV;
+  const float* R_span =
+      p.adj_state + ((size_t)bh * (p.n_spans + 1) + (p.n_spans - 1 - sp)) * DK * DV;
+  float* const stage = sEc;  // the partner-formed state, before sEc is needed
+  const float* E = e_from_partner ? stage : E_span;
+  const float* R = r_from_partner ? stage : R_span;
 
-  // ---- 1. tiles, cumulative log-decay
+  // ---- 1. tiles (and the partner's: keys or queries, log-alpha, values or
+  // output gradients into the operand-tile and sEc areas), cumulative decay
   const int t0 = c * kChunk;
   const int valid = min(kChunk, p.T - t0);
+  f16* const pv = reinterpret_cast<f16*>(sEc);  // partner value tile (8 KB of sEc)
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int blk = wave * 2 + i;
@@ -122,7 +138,114 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
     dma16(rla, tla + blk * 512, off);
     dma16(rdo, tdo + blk * 512, off);
   }
+  if (e_from_partner || r_from_partner) {
+    const int tp = e_from_partner ? t0 - kChunk : t0 + kChunk;
+    const int vp = min(kChunk, p.T - tp);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int blk = wave * 2 + i;
+      const uint32_t off = dma_offset<RB>(blk, tp, vp, gm);
+      dma16(e_from_partner ? rk : rq, tqs + blk * 512, off);
+      dma16(rla, tkd + blk * 512, off);
+      dma16(e_from_partner ? rv : rdo, pv + blk * 512, off);
+    }
+  }
   wait_barrier<vmcnt_lgkm0_imm(0)>();  // tiles landed, row table written
+
+  if (e_from_partner || r_from_partner) {
+    // partner decay profile per key dim: keys decayed to the partner's end
+    // (exclusive of the token), or queries decayed from its start (inclusive)
+    const int i = tid & 63, J = tid >> 6;
+    float al[16], tot = 0.f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const float la = (float)tkd[swz<RB>(16 * J + u, i)];
+      al[u] = ex(la);
+      tot += la;
+    }
+    sTot[J][i] = tot;
+    __syncthreads();
+    float before = 0.f, after = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      before += j < J ? sTot[j][i] : 0.f;
+      after += j > J ? sTot[j][i] : 0.f;
+    }
+    if (J == 0) sCarry[0][i] = ex(sTot[0][i] + sTot[1][i] + sTot[2][i] + sTot[3][i]);
+    if (e_from_partner) {
+      float sfx = ex(after);
+#pragma unroll
+      for (int u = 15; u >= 0; --u) {
+        const int e = swz<RB>(16 * J + u, i);
+        tkd[e] = (f16)((float)tqs[e] * sfx);
+        sfx *= al[u];
+      }
+    } else {
+      float pre = ex(before);
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int e = swz<RB>(16 * J + u, i);
+        pre *= al[u];
+        tkd[e] = (f16)((float)tqs[e] * pre);
+      }
+    }
+    __syncthreads();
+    // wave w: columns 16 w .. of the state, all rows: the partner's
+    // contribution as (values)^T (decayed keys or queries) over its tokens
+    f32x4 st[4];
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int P = 0; P < 2; ++P) {
+        const f16x8 av = cat8(tr_read<RB>(pv, 32 * P, 16 * wave), tr_read<RB>(pv, 32 * P + 16, 16 * wave));
+        const f16x8 bk = cat8(tr_read<RB>(tkd, 32 * P, 16 * kc), tr_read<RB>(tkd, 32 * P + 16, 16 * kc));
+        acc = mma32(av, bk, acc);
+      }
+      st[kc] = acc;
+    }
+    const float* span = e_from_partner ? E_span : R_span;
+    f32x4 x[4];
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const int row = 16 * kc + n16;
+      const f32x4 s4 = *reinterpret_cast<const f32x4*>(span + row * DV + 16 * wave + 4 * g);
+      x[kc] = sCarry[0][row] * s4 + st[kc];
+    }
+    __syncthreads();  // every wave is done with the partner tiles in sEc
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc)
+      *reinterpret_cast<f32x4*>(stage + (16 * kc + n16) * DV + 16 * wave + 4 * g) = x[kc];
+    __syncthreads();
+  }
+
+  // This chunk's states in the layouts the MFMAs below read: E and R rows of
+  // the wave's key dims as float16 A operands (lane (n, g): row 16 kb + n,
+  // columns 32 h + 8g .. + 7), R^T rows of its value dims, and E, R in the
+  // accumulator layout of the next-state update (rows 16 kc + n, columns
+  // 16 w + 4g ..), read now while the staged state is still in place.
+  const int kb = wave;          // key dims 16 kb .. owned by this wave (dq, dk, dla)
+  const int vb = wave;          // value dims 16 vb .. (dv, next state rows)
+  const int ki = 16 * kb + 4 * g;  // first of the lane's 4 key dims in a dq / dk tile
+  const int vj = 16 * vb + 4 * g;
+  f16x8 ea[2], ra[2], rta[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    ea[h] = ld8f(E + (16 * kb + n16) * DV + 32 * h + 8 * g);
+    ra[h] = ld8f(R + (16 * kb + n16) * DV + 32 * h + 8 * g);
+    // R^T rows 16 vb + n: R[32 h + 8g + e][16 vb + n]
+    f16x8 x;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (f16)R[(32 * h + 8 * g + e) * DV + 16 * vb + n16];
+    rta[h] = x;
+  }
+  f32x4 e4s[4], r4s[4];
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc) {
+    e4s[kc] = *reinterpret_cast<const f32x4*>(E + (16 * kc + n16) * DV + vj);
+    r4s[kc] = *reinterpret_cast<const f32x4*>(R + (16 * kc + n16) * DV + vj);
+  }
+  __syncthreads();  // the staging area becomes sEc
 
   // Thread (key dim i, sub-block J) walks its 16 tokens: alpha_t = e^{la_t},
   // e^{c_t} as a running product from the sub-block start and the decay to
@@ -179,25 +302,6 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
     }
   }
   __syncthreads();
-
-  const int kb = wave;          // key dims 16 kb .. owned by this wave (dq, dk, dla)
-  const int vb = wave;          // value dims 16 vb .. (dv, next state rows)
-  const int ki = 16 * kb + 4 * g;  // first of the lane's 4 key dims in a dq / dk tile
-  const int vj = 16 * vb + 4 * g;
-
-  // E and R rows of this wave's key dims, as float16 MFMA A operands
-  // (lane (n, g): row 16 kb + n, columns 32 h + 8g .. + 7)
-  f16x8 ea[2], ra[2], rta[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    ea[h] = ld8f(E + (16 * kb + n16) * DV + 32 * h + 8 * g);
-    ra[h] = ld8f(R + (16 * kb + n16) * DV + 32 * h + 8 * g);
-    // R^T rows 16 vb + n: R[32 h + 8g + e][16 vb + n]
-    f16x8 x;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = (f16)R[(32 * h + 8 * g + e) * DV + 16 * vb + n16];
-    rta[h] = x;
-  }
 
   auto row_off = [&](int t, int col) -> uint32_t {
     const uint32_t cf = srow[t];
@@ -342,8 +446,8 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
     // lane (n, g): E_next[i = 16 kc + n][j = 16 vb + 4g + u]
     const int i = 16 * kc + n16;
     const float ebe = ex(sBst[4][i]);
-    const f32x4 e4 = *reinterpret_cast<const f32x4*>(E + i * DV + vj);
-    const f32x4 r4 = *reinterpret_cast<const f32x4*>(R + i * DV + vj);
+    const f32x4 e4 = e4s[kc];
+    const f32x4 r4 = r4s[kc];
     float part = 0.f;
 #pragma unroll
     for (int u = 0; u < 4; ++u) part += (ebe * e4[u] + acc[u]) * r4[u];
@@ -386,7 +490,7 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
   }
 
   if (c == 0 && p.d_initial_state != nullptr) {
-    const float* src = p.adj_state + ((size_t)bh * (p.n_chunks + 1) + p.n_chunks) * DK * DV;
+    const float* src = p.adj_state + ((size_t)bh * (p.n_spans + 1) + p.n_spans) * DK * DV;
     float* dst = p.d_initial_state + (size_t)bh * DK * DV;
     for (int e = tid * 4; e < DK * DV; e += kThreads * 4)
       *reinterpret_cast<f32x4*>(dst + e) = *reinterpret_cast<const f32x4*>(src + e);

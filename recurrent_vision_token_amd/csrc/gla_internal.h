@@ -74,15 +74,16 @@ struct BwdParams {
   void* dk;
   void* dv;                 // [B][heads][H][W][d_v]
   void* dla;                // [B][heads][H][W][d_k]
-  const float* fwd_state;   // [BH][n_chunks][d_k][d_v] entry state of each chunk
-  const float* adj_state;   // [BH][n_chunks + 1][d_k][d_v]: slot n_chunks - 1 - c enters chunk c
-                            // from the right; slot n_chunks is dL/dS_{-1}
+  const float* fwd_state;   // [BH][n_spans][d_k][d_v] state entering each span of two chunks
+  const float* adj_state;   // [BH][n_spans + 1][d_k][d_v]: slot n_spans - 1 - s enters span s's
+                            // last chunk from the right; slot n_spans is dL/dS_{-1}
   float* d_initial_state;   // [BH][d_k][d_v], or null
   int B, heads, H, W, T;
   unsigned int div_w_m, div_h_m;
   int div_w_s, div_h_s;
   int scan_dir;
   int n_chunks;
+  int n_spans;              // ceil(n_chunks / 2)
 };
 
 hipError_t launch_bwd_chunks(int d_k, int d_v, const BwdParams& p, hipStream_t stream,

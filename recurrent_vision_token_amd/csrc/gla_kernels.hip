@@ -1048,14 +1048,15 @@ struct SumTile {
 };
 
 //
-// ADJ instantiates the same kernel for the backward pass's adjoint summaries
-// (spans of one chunk): with q in place of k and the output gradient in place
-// of v it folds dR = (Q * exp(B))^T dO, B the decay from the chunk start
-// through each token (inclusive), and writes summary c to slot
-// adj_slots - 2 - c, so that the scan over the slots runs from the end of the
-// sequence to its start; the first chunk also writes the neutral summary
-// (gate 1, state 0) into the last slot, whose entry state is then the
-// gradient of the state before the first step.
+// ADJ instantiates the same kernel for the backward pass's adjoint summaries:
+// with q in place of k and the output gradient in place of v it folds
+// dR = (Q * exp(B))^T dO, B the decay from the span start through each token
+// (inclusive): chunks are taken last to first, each from its own start, and
+// the summary of the later chunks is decayed by the chunk's total before it
+// adds in.  Span s's summary goes to slot adj_slots - 2 - s, so that the scan
+// over the slots runs from the end of the sequence to its start; the first
+// span also writes the neutral summary (gate 1, state 0) into the last slot,
+// whose entry state is then the gradient of the state before the first step.
 template <int DK, int DV, bool GATE, bool ADJ = false>
 __global__ __launch_bounds__(kThreads) void span_summary_f16_kernel(FwdParams p) {
   // six separate LDS objects, so the compiler's own waits for the LDS-writing
@@ -1133,11 +1134,18 @@ __global__ __launch_bounds__(kThreads) void span_summary_f16_kernel(FwdParams p)
       f32x4 rest[4];
       f32x4 c = gdec[d];
       if constexpr (ADJ) {
+        // decay from this chunk's start; the later chunks' summary, already
+        // folded, is decayed by this chunk's total before this chunk adds in
+        f32x4 cl = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int J = 0; J < 4; ++J) {
-          rest[J] = mma16(m_upper, lat[J], c);
-          c = mma16(m_ones, lat[J], c);
+          rest[J] = mma16(m_upper, lat[J], cl);
+          cl = mma16(m_ones, lat[J], cl);
         }
+        const float whole = exp2_fast(cl[0] * 1.4426950408889634f);  // key dim 16 db + n
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) st[d][cb] *= whole;
+        c = c + cl;
       } else {
 #pragma unroll
         for (int J = 3; J >= 0; --J) {
