@@ -25,6 +25,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -40,7 +41,23 @@ SWIGLU_SRC = os.path.join(ROOT, "recurrent_vision_token_amd", "csrc", "swiglu_ke
 SAGA_SRC = os.path.join(ROOT, "recurrent_vision_token_amd", "csrc", "saga_kernels.hip")
 BWD_SRC = os.path.join(ROOT, "recurrent_vision_token_amd", "csrc", "gla_bwd_kernels.hip")
 KERNEL_NAMES = ("span_summary", "span_scan", "chunk_output", "spatial_swiglu", "saga_kv_partial",
-                "saga_kv_reduce", "saga_out", "chunk_bwd")
+                "saga_kv_reduce", "saga_out", "chunk_bwd", "bwd_state_summary", "bwd_state_scan",
+                "bwd_adjoint_summary", "bwd_adjoint_scan")
+# the summary and scan kernels carry a last template argument that names their
+# role: 0 the forward pass, 1 the backward pass's forward entry states, 2 its
+# adjoint states
+ROLE_KEYS = {"1": "bwd_state_", "2": "bwd_adjoint_"}
+
+
+def kernel_key(name):
+    """The KERNEL_NAMES entry a (demangled) kernel name belongs to, or None."""
+    for base in ("span_summary", "span_scan"):
+        m = re.search(base + r"\w*<([^>]*)>", name)
+        if m:
+            role = m.group(1).split(",")[-1].strip()
+            prefix = ROLE_KEYS.get(role)
+            return prefix + base.split("_")[1] if prefix else base
+    return next((k for k in KERNEL_NAMES if k in name), None)
 
 
 DEVICE_HDR = os.path.join(ROOT, "recurrent_vision_token_amd", "csrc", "gla_device.h")
@@ -640,7 +657,7 @@ def summarize(wl, ms_step, mean, ext=False):
     }
 
 
-def counters_to_traffic(fetch_dir, write_dir, copy_mb, workload):
+def counters_to_traffic(fetch_dir, write_dir, copy_mb, workload, only=()):
     """Per-launch HBM bytes from two rocprofv3 --pmc runs (FETCH_SIZE, then
     WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads for
     the device copy of known size that the runs include.  Writes
@@ -654,7 +671,7 @@ def counters_to_traffic(fetch_dir, write_dir, copy_mb, workload):
             if row["Counter_Name"] != counter:
                 continue
             name = row["Kernel_Name"]
-            key = next((k for k in KERNEL_NAMES if k in name), None)
+            key = kernel_key(name)
             if key is None and "copy" in name.lower():
                 key = "copy"
             if key is not None:
@@ -672,7 +689,7 @@ def counters_to_traffic(fetch_dir, write_dir, copy_mb, workload):
              "|---|---|---|---|---|---|"]
     recs = {}
     for k in KERNEL_NAMES:
-        if k not in f:
+        if k not in f or (only and k not in only):
             continue
         rd = f[k] * 1024.0 * f_scale
         wr = w[k] * 1024.0 * w_scale
@@ -688,6 +705,10 @@ def counters_to_traffic(fetch_dir, write_dir, copy_mb, workload):
                                                                   (rd + wr) / 1e6))
     for wl_name, rec in recs.items():
         out = os.path.join(ROOT, "profiles", "traffic_%s.json" % wl_name)
+        if only and os.path.exists(out):
+            old = json.load(open(out))
+            old["kernels"].update(rec["kernels"])
+            rec = old
         json.dump(rec, open(out, "w"), indent=1)
         print("wrote", out)
     print("copy kernel of %d bytes: FETCH_SIZE %.0f KiB (scale %.3f), WRITE_SIZE %.0f KiB (scale %.3f)"
@@ -716,11 +737,15 @@ def main():
                          "known traffic, to scale hardware byte counters against)")
     ap.add_argument("--counters-to-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc output folders into profiles/traffic_*.json")
+    ap.add_argument("--traffic-kernels", default="",
+                    help="comma-separated kernels to record with --counters-to-traffic "
+                         "(default: all found; records of other kernels are kept)")
     args = ap.parse_args()
 
     if args.counters_to_traffic:
         counters_to_traffic(args.counters_to_traffic[0], args.counters_to_traffic[1],
-                            args.copy_calibration_mb or 256, args.workload)
+                            args.copy_calibration_mb or 256, args.workload,
+                            [k for k in args.traffic_kernels.split(",") if k])
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "

@@ -373,11 +373,14 @@ __global__ __launch_bounds__(kThreads) void span_summary_kernel(FwdParams p) {
 // trip), folds them from zero, the folds are exchanged through LDS to give
 // every segment its carry-in, and the same registers then yield the entry
 // states.
+constexpr int kRoleForward = 0, kRoleStates = 1, kRoleAdjoint = 2;
 constexpr int kScanSeg = 4;
 constexpr int kScanU = 32;
 constexpr int kScanElems = kThreads / kScanSeg;   // state elements per workgroup
 
-template <int DK, int DV>
+// ROLE only names the launch in traces and counters: 0 the forward pass, 1 the
+// backward pass's forward entry states, 2 its adjoint states.
+template <int DK, int DV, int ROLE = kRoleForward>
 __global__ __launch_bounds__(kThreads) void span_scan_kernel(FwdParams p) {
   __shared__ float seg_l[kScanSeg][kScanElems];
   __shared__ float seg_g[kScanSeg][kScanElems];
@@ -1048,7 +1051,9 @@ struct SumTile {
 };
 
 //
-// ADJ instantiates the same kernel for the backward pass's adjoint summaries:
+// ROLE kRoleStates instantiates the same code, under a name of its own, for the
+// backward pass's forward entry states (spans of several chunks); kRoleAdjoint
+// instantiates it for the backward pass's adjoint summaries:
 // with q in place of k and the output gradient in place of v it folds
 // dR = (Q * exp(B))^T dO, B the decay from the span start through each token
 // (inclusive): chunks are taken last to first, each from its own start, and
@@ -1057,8 +1062,9 @@ struct SumTile {
 // over the slots runs from the end of the sequence to its start; the first
 // span also writes the neutral summary (gate 1, state 0) into the last slot,
 // whose entry state is then the gradient of the state before the first step.
-template <int DK, int DV, bool GATE, bool ADJ = false>
+template <int DK, int DV, bool GATE, int ROLE = kRoleForward>
 __global__ __launch_bounds__(kThreads) void span_summary_f16_kernel(FwdParams p) {
+  constexpr bool ADJ = ROLE == kRoleAdjoint;
   // six separate LDS objects, so the compiler's own waits for the LDS-writing
   // loads can tell the tiles apart
   __shared__ __attribute__((aligned(16))) f16 k0[kChunk * DK], la0[kChunk * DK], v0[kChunk * DV];
@@ -1350,22 +1356,22 @@ hipError_t launch_bwd_states_variant(const FwdParams& fwd, const FwdParams& adj,
   const dim3 scan_grid(BH, DK * DV / kScanElems);
   hipError_t e;
   // forward entry state of every chunk
-  if ((e = launch_marked(span_summary_f16_kernel<DK, DV, false, false>, dim3(BH * fwd.n_spans),
+  if ((e = launch_marked(span_summary_f16_kernel<DK, DV, false, kRoleStates>, dim3(BH * fwd.n_spans),
                          stream, fwd, ev ? ev[0] : nullptr, nullptr)) != hipSuccess)
     return e;
-  if ((e = launch_marked(span_scan_kernel<DK, DV>, scan_grid, stream, fwd, nullptr,
+  if ((e = launch_marked(span_scan_kernel<DK, DV, kRoleStates>, scan_grid, stream, fwd, nullptr,
                          ev ? ev[1] : nullptr)) != hipSuccess)
     return e;
   // adjoint state entering every chunk from its right, and the gradient of
   // the state before the first step in the extra last slot
   FwdParams sum = adj;
   sum.n_spans = adj.adj_slots - 1;
-  if ((e = launch_marked(span_summary_f16_kernel<DK, DV, false, true>, dim3(BH * sum.n_spans),
+  if ((e = launch_marked(span_summary_f16_kernel<DK, DV, false, kRoleAdjoint>, dim3(BH * sum.n_spans),
                          stream, sum, ev ? ev[2] : nullptr, nullptr)) != hipSuccess)
     return e;
   FwdParams scan = adj;
   scan.n_spans = adj.adj_slots;
-  return launch_marked(span_scan_kernel<DK, DV>, scan_grid, stream, scan, nullptr,
+  return launch_marked(span_scan_kernel<DK, DV, kRoleAdjoint>, scan_grid, stream, scan, nullptr,
                        ev ? ev[3] : nullptr);
 }
 
