@@ -83,6 +83,8 @@ def source_hash(kernel):
         paths.append(TILES_HDR)
     for path in paths:
         h.update(open(path, "rb").read())
+    from recurrent_vision_token_amd.build import flags_for
+    h.update(" ".join(flags_for(os.path.basename(source_of(kernel)))).encode())
     return h.hexdigest()
 
 

@@ -26,6 +26,20 @@ HIP_FLAGS = [
 ]
 
 
+# per-source additions: the backward chunk kernel keeps its matrix-core
+# accumulators in ordinary vector registers (the default form parks them in
+# accumulation registers and copies every result out, ~300 extra VALU
+# instructions per wave there)
+EXTRA_FLAGS = {
+    "gla_bwd_kernels.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
+def flags_for(src):
+    """hipcc flags of one device source file (its base name)."""
+    return HIP_FLAGS + EXTRA_FLAGS.get(src, [])
+
+
 def _run(cmd):
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
@@ -43,13 +57,13 @@ def build(verbose=False):
     s_obj = os.path.join(BUILD, "swiglu_kernels.o")
     g_obj = os.path.join(BUILD, "saga_kernels.o")
     b_obj = os.path.join(BUILD, "gla_bwd_kernels.o")
-    logs.append(_run([hipcc] + HIP_FLAGS + ["-I", INCLUDE, "-I", CSRC, "-c",
+    logs.append(_run([hipcc] + flags_for("gla_kernels.hip") + ["-I", INCLUDE, "-I", CSRC, "-c",
                                             os.path.join(CSRC, "gla_kernels.hip"), "-o", k_obj]))
-    logs.append(_run([hipcc] + HIP_FLAGS + ["-I", INCLUDE, "-I", CSRC, "-c",
+    logs.append(_run([hipcc] + flags_for("swiglu_kernels.hip") + ["-I", INCLUDE, "-I", CSRC, "-c",
                                             os.path.join(CSRC, "swiglu_kernels.hip"), "-o", s_obj]))
-    logs.append(_run([hipcc] + HIP_FLAGS + ["-I", INCLUDE, "-I", CSRC, "-c",
+    logs.append(_run([hipcc] + flags_for("saga_kernels.hip") + ["-I", INCLUDE, "-I", CSRC, "-c",
                                             os.path.join(CSRC, "saga_kernels.hip"), "-o", g_obj]))
-    logs.append(_run([hipcc] + HIP_FLAGS + ["-I", INCLUDE, "-I", CSRC, "-c",
+    logs.append(_run([hipcc] + flags_for("gla_bwd_kernels.hip") + ["-I", INCLUDE, "-I", CSRC, "-c",
                                             os.path.join(CSRC, "gla_bwd_kernels.hip"), "-o", b_obj]))
     logs.append(_run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-D__HIP_PLATFORM_AMD__",
                       "-I", os.path.join(ROCM, "include"), "-I", INCLUDE, "-I", CSRC, "-c",

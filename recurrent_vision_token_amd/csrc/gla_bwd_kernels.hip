@@ -54,6 +54,15 @@ constexpr int kChunk = 64;
 
 __device__ __forceinline__ float ex(float x) { return exp2_fast(x * 1.4426950408889634f); }
 
+// DPP moves within the 16-lane rows of a wave: lane n of a row reads lane
+// n + k of the same row (zero past the row's end), or every lane reads lane k.
+constexpr int kRowShl = 0x100, kRowBcast = 0x150;
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+
 __device__ __forceinline__ f16x8 ld8f(const float* a) {
   const f32x4 lo = *reinterpret_cast<const f32x4*>(a);
   const f32x4 hi = *reinterpret_cast<const f32x4*>(a + 4);
@@ -64,10 +73,15 @@ template <int DK, int DV>
 __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
   static_assert(DK == 64 && DV == 64, "built for 64 key and value dims");
   constexpr int RB = 128;  // bytes per tile row
+  // row stride (floats) of sEc and of a state staged there: 4 floats of
+  // padding move consecutive rows 4 banks apart, so 16 lanes reading 16 bytes
+  // each from 16 rows hit 64 different banks
+  constexpr int ES = DK + 4;
+  static_assert(DK == DV, "the staged state shares sEc's row stride");
   __shared__ __attribute__((aligned(16))) f16 tq[kChunk * DK], tk[kChunk * DK], tv[kChunk * DV];
   __shared__ __attribute__((aligned(16))) f16 tla[kChunk * DK], tdo[kChunk * DV];
   __shared__ __attribute__((aligned(16))) f16 tqs[kChunk * DK], tkd[kChunk * DK];
-  __shared__ __attribute__((aligned(16))) float sEc[kChunk * DK];  // e^{c_t}, c = decay since the sub-block start
+  __shared__ __attribute__((aligned(16))) float sEc[kChunk * ES];  // e^{c_t}, c = decay since the sub-block start
   __shared__ __attribute__((aligned(16))) f16 sF[5][5][DK];  // e^{Bst_a - Bst_b} per key dim
   __shared__ float sTot[4][DK];
   __shared__ float sBst[5][DK];   // B before sub-block I (I = 0..3), [4] = chunk total
@@ -119,6 +133,8 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
   float* const stage = sEc;  // the partner-formed state, before sEc is needed
   const float* E = e_from_partner ? stage : E_span;
   const float* R = r_from_partner ? stage : R_span;
+  const int e_ld = e_from_partner ? ES : DV;   // row strides of E and R
+  const int r_ld = r_from_partner ? ES : DV;
 
   // ---- 1. tiles (and the partner's: keys or queries, log-alpha, values or
   // output gradients into the operand-tile and sEc areas), cumulative decay
@@ -215,7 +231,7 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
     __syncthreads();  // every wave is done with the partner tiles in sEc
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc)
-      *reinterpret_cast<f32x4*>(stage + (16 * kc + n16) * DV + 16 * wave + 4 * g) = x[kc];
+      *reinterpret_cast<f32x4*>(stage + (16 * kc + n16) * ES + 16 * wave + 4 * g) = x[kc];
     __syncthreads();
   }
 
@@ -231,19 +247,19 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
   f16x8 ea[2], ra[2], rta[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    ea[h] = ld8f(E + (16 * kb + n16) * DV + 32 * h + 8 * g);
-    ra[h] = ld8f(R + (16 * kb + n16) * DV + 32 * h + 8 * g);
+    ea[h] = ld8f(E + (16 * kb + n16) * e_ld + 32 * h + 8 * g);
+    ra[h] = ld8f(R + (16 * kb + n16) * r_ld + 32 * h + 8 * g);
     // R^T rows 16 vb + n: R[32 h + 8g + e][16 vb + n]
     f16x8 x;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = (f16)R[(32 * h + 8 * g + e) * DV + 16 * vb + n16];
+    for (int e = 0; e < 8; ++e) x[e] = (f16)R[(32 * h + 8 * g + e) * r_ld + 16 * vb + n16];
     rta[h] = x;
   }
   f32x4 e4s[4], r4s[4];
 #pragma unroll
   for (int kc = 0; kc < 4; ++kc) {
-    e4s[kc] = *reinterpret_cast<const f32x4*>(E + (16 * kc + n16) * DV + vj);
-    r4s[kc] = *reinterpret_cast<const f32x4*>(R + (16 * kc + n16) * DV + vj);
+    e4s[kc] = *reinterpret_cast<const f32x4*>(E + (16 * kc + n16) * e_ld + vj);
+    r4s[kc] = *reinterpret_cast<const f32x4*>(R + (16 * kc + n16) * r_ld + vj);
   }
   __syncthreads();  // the staging area becomes sEc
 
@@ -263,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
       al[u] = ex(la);
       tot += la;
       ec *= al[u];
-      sEc[t * DK + i] = ec;
+      sEc[t * ES + i] = ec;
       tqs[e] = (f16)((float)tq[e] * ec);
     }
     float sfx = 1.f, kf[16];
@@ -328,24 +344,18 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) sc[u] = (4 * g + u <= n16) ? sc[u] : 0.f;
       }
-      f16x4 aop = tr_read<RB>(tkd, 16 * J, 16 * kb);  // Kd^T: key dim 16 kb + n, tokens 16J + 4g..
-      if (J == I) {
-        // back to the sub-block start: k e^{-c} = Kd e^{Bst_J - Bst_{J+1}}, per key dim n
-        aop = aop * sF[J][J + 1][16 * kb + n16];
-      }
-      f32x4 tt = mma16(aop, to_f16(sc), f32x4{0.f, 0.f, 0.f, 0.f});
-      if (J < I) {
-        const f16x4 f = ld64(&sF[I][J + 1][ki]);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) tt[u] *= (float)f[u];
-      }
-      acc += tt;
+      // Kd^T: key dim 16 kb + n, tokens 16J + 4g..; the row's factor is the
+      // decay back to the sub-block start, k e^{-c} = Kd e^{Bst_J - Bst_{J+1}}
+      // (>= 1) for J = I, or between the boundaries, e^{Bst_I - Bst_{J+1}}
+      // (<= 1) for J < I
+      const f16 fk = sF[J == I ? J : I][J + 1][16 * kb + n16];
+      acc = mma16(tr_read<RB>(tkd, 16 * J, 16 * kb) * fk, to_f16(sc), acc);
     }
     // inter-chunk: (E dO^T)[key dim][token]
     f32x4 ed = mma32(ea[0], dob0, f32x4{0.f, 0.f, 0.f, 0.f});
     ed = mma32(ea[1], dob1, ed);
     const int t = 16 * I + n16;
-    const f32x4 ec = *reinterpret_cast<const f32x4*>(&sEc[t * DK + ki]);
+    const f32x4 ec = *reinterpret_cast<const f32x4*>(&sEc[t * ES + ki]);
     const f16x4 fb = ld64(&sF[I][0][ki]);
     f32x4 dq;
 #pragma unroll
@@ -370,19 +380,17 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) sc[u] = (4 * g + u >= n16) ? sc[u] : 0.f;
       }
-      f32x4 tt = mma16(tr_read<RB>(tqs, 16 * I, 16 * kb), to_f16(sc), f32x4{0.f, 0.f, 0.f, 0.f});
-      if (I > J) {
-        const f16x4 f = ld64(&sF[I][J][ki]);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) tt[u] *= (float)f[u];
-      }
-      acc += tt;
+      // Qs^T: key dim 16 kb + n, tokens 16I + 4g..; for I > J its row takes
+      // the decay between the boundaries, e^{Bst_I - Bst_J} (<= 1)
+      f16x4 aop = tr_read<RB>(tqs, 16 * I, 16 * kb);
+      if (I > J) aop = aop * sF[I][J][16 * kb + n16];
+      acc = mma16(aop, to_f16(sc), acc);
     }
     // inter-chunk: (R V^T)[key dim][token]
     f32x4 rv = mma32(ra[0], vb0, f32x4{0.f, 0.f, 0.f, 0.f});
     rv = mma32(ra[1], vb1, rv);
     const int t = 16 * J + n16;
-    const f32x4 ec = *reinterpret_cast<const f32x4*>(&sEc[t * DK + ki]);
+    const f32x4 ec = *reinterpret_cast<const f32x4*>(&sEc[t * ES + ki]);
     const f16x4 fe = ld64(&sF[4][J][ki]);
     f32x4 dk;
 #pragma unroll
@@ -472,18 +480,17 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
       for (int u = 0; u < 4; ++u) x[u] = (float)q4[u] * dqv[I][u] - (float)k4[u] * dkv[I][u];
       // suffix sums over the 16 tokens of the tile row (lanes n .. 15)
 #pragma unroll
-      for (int sft = 1; sft < 16; sft <<= 1) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float y = __shfl_down(x[u], sft, 16);
-          x[u] += (n16 + sft < 16) ? y : 0.f;
-        }
+      for (int u = 0; u < 4; ++u) {
+        x[u] += dpp_f<kRowShl + 1>(x[u]);
+        x[u] += dpp_f<kRowShl + 2>(x[u]);
+        x[u] += dpp_f<kRowShl + 4>(x[u]);
+        x[u] += dpp_f<kRowShl + 8>(x[u]);
       }
       f32x4 dla;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         dla[u] = x[u] + running[u];
-        running[u] += __shfl(x[u], 0, 16);
+        running[u] += dpp_f<kRowBcast + 0>(x[u]);   // the row's total (lane 0)
       }
       store4(wdla, t, ki, dla);
     }
