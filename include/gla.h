@@ -33,11 +33,20 @@
  * call validates its arguments on the host, then enqueues its kernels on
  * `stream` (a hipStream_t passed as void*, NULL = the default stream) and
  * returns without waiting; errors raised while the kernels run surface at the
- * caller's next synchronisation.  A temporary workspace, when the sequence is
- * split into spans, is taken and released stream-ordered on `stream`.  The
- * library keeps no pointer after returning and holds no global state besides a
- * one-time read of tuning environment variables, so concurrent calls on
- * different streams are independent.
+ * caller's next synchronisation.
+ *
+ * Workspace: a call that needs scratch memory (span states when the sequence
+ * is split into spans; every backward and SAGA call) uses a device buffer that
+ * the library keeps per (device, stream): allocated on the first such call on
+ * that stream, grown (a new buffer) when a call needs more, and kept until
+ * gla_release_workspaces.  Calls on one stream reuse it in stream order; each
+ * use records an event that the next use on the same stream handle waits on.
+ * Concurrent calls on different streams use different buffers and are
+ * independent.  Under stream capture a call takes a stream-ordered
+ * allocation of its own instead, released in the captured stream order.
+ * Besides this table the library holds no global state but a one-time read
+ * of tuning environment variables and the measurement hook's per-thread
+ * events; it keeps no pointer to caller memory after returning.
  *
  * Errors: every argument check runs before any HIP call; on failure nothing is
  * enqueued and a negative status is returned (see gla_status_str).  Nothing
@@ -138,7 +147,7 @@ int gla_chunk_fwd_f32(const float* q, const float* k, const float* v, const floa
  * of ceil(H*W/64) chunks is cut into n_spans spans of span_chunks chunks (the
  * last may be shorter), one output workgroup per (batch, head, span).  When
  * n_spans > 1 the call also runs the span-summary and span-scan kernels and
- * takes a stream-ordered workspace of B*heads*n_spans*(d_k*d_v + d_k) floats.
+ * uses a workspace of B*heads*n_spans*(d_k*d_v + d_k) floats.
  * use_f32 selects the float32 entry.  Reads device attributes (a HIP call);
  * returns the same argument errors as the forward entry points.
  */
@@ -167,9 +176,9 @@ int gla_plan_spans(int use_f32, int B, int heads, int H, int W, int d_k, int d_v
  * (zero).  Outputs: dq, dk, dlog_alpha [B][heads][H][W][d_k] and dv
  * [B][heads][H][W][d_v] float16 (rounded to nearest even), d_initial_state
  * float32 [B][heads][d_k][d_v] or NULL (not wanted).  Pointers 16-byte
- * aligned; no output may overlap an input or another output.  A
- * stream-ordered workspace of B*heads*(2*n_chunks + 1)*(d_k*d_v + d_k) floats
- * is taken and released on `stream`.  Domain as gla_chunk_fwd, plus
+ * aligned; no output may overlap an input or another output.  The call uses
+ * a workspace of B*heads*(2*n_spans + 1)*(d_k*d_v + d_k) floats, n_spans =
+ * ceil(ceil(H*W/64) / 2).  Domain as gla_chunk_fwd, plus
  * d_out . v and its kin within float16 range.  Errors as gla_chunk_fwd
  * (GLA_ERR_UNSUPPORTED for any other d_k, d_v or chunk).  With the
  * measurement hook armed, event pairs bracket the forward-state kernels
@@ -243,8 +252,9 @@ int gla_spatial_swiglu(const void* gate, const void* value, int ld_in, const voi
  * of two per 16 value columns; out rounded to nearest even.
  * Supported: d_k, d_v in {64, 128}; one sequence's rows of a tensor below
  * 2 GiB.  out and kv may not overlap any input or each other.
- * Ownership and errors as gla_chunk_fwd (a stream-ordered workspace is taken
- * and released on `stream`): GLA_ERR_NULL, GLA_ERR_SHAPE, GLA_ERR_UNSUPPORTED
+ * Ownership and errors as gla_chunk_fwd (with a workspace of
+ * B*heads*d_k*d_v*(1 + s) floats, s the accumulation spans per sequence, a
+ * few workgroups per CU in all): GLA_ERR_NULL, GLA_ERR_SHAPE, GLA_ERR_UNSUPPORTED
  * (d_k / d_v), GLA_ERR_ALIGN, GLA_ERR_ALIAS.  With the measurement hook armed
  * the accumulation, reduction and output kernels record event pairs 0, 1, 2
  * (the reduction's pair back to back when one span covers a sequence).
@@ -266,6 +276,17 @@ int gla_saga_fwd(const void* q, const void* k, const void* v, const void* alpha,
  * GLA_ERR_SHAPE if n is neither 0 nor 6.
  */
 int gla_set_kernel_events(void* const* events, int n);
+
+/*
+ * Frees every workspace buffer the library holds (see "Workspace" above):
+ * for each device that holds one it waits for that device's work
+ * (hipDeviceSynchronize), then frees its buffers; the calling thread's current
+ * device is restored.  Calls made afterwards allocate again.  Must not run
+ * concurrently with calls that are being enqueued.  Returns GLA_OK (also when
+ * nothing is held, without any HIP call) or GLA_ERR_HIP if a HIP call fails
+ * (the table is emptied regardless).
+ */
+int gla_release_workspaces(void);
 
 /* Static, human-readable text for a status code. */
 const char* gla_status_str(int status);

@@ -18,7 +18,7 @@ STATUS = {
     -4: "GLA_ERR_ALIGN", -5: "GLA_ERR_SCAN_DIR", -6: "GLA_ERR_ALIAS", -7: "GLA_ERR_HIP",
 }
 EXPORTED = ("gla_chunk_bwd", "gla_chunk_fwd", "gla_chunk_fwd_ex", "gla_chunk_fwd_f32",
-            "gla_plan_spans",
+            "gla_plan_spans", "gla_release_workspaces",
             "gla_saga_fwd", "gla_set_kernel_events", "gla_spatial_swiglu", "gla_status_str",
             "gla_version")
 GATE_MODES = {"log_alpha": 0, "logits": 1}
@@ -64,6 +64,8 @@ def load():
     lib.gla_set_kernel_events.restype = ctypes.c_int
     lib.gla_version.argtypes = []
     lib.gla_version.restype = ctypes.c_int
+    lib.gla_release_workspaces.argtypes = []
+    lib.gla_release_workspaces.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -311,6 +313,14 @@ def saga_fwd(q, k, v, alpha, beta, out=None, kv=None, want_kv=False, stream=None
     if rc != GLA_OK:
         raise GlaError(rc, status_str(rc))
     return out, kv
+
+
+def release_workspaces():
+    """Free the workspace buffers the library keeps per (device, stream)
+    (waits for the work of every device that holds one)."""
+    rc = load().gla_release_workspaces()
+    if rc != 0:
+        raise GlaError(rc, status_str(rc))
 
 
 def set_kernel_events(handles):

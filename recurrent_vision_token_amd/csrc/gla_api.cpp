@@ -1,5 +1,5 @@
 // Host side of the C ABI declared in include/gla.h: argument validation (all
-// of it before any HIP call), span planning, stream-ordered workspace, launch.
+// of it before any HIP call), span planning, the workspace cache, launch.
 
 #include <hip/hip_runtime_api.h>
 
@@ -8,6 +8,8 @@
 #include <cstdint>
 #include <cstdlib>
 #include <mutex>
+#include <utility>
+#include <vector>
 
 #include "gla.h"
 #include "gla_internal.h"
@@ -22,6 +24,84 @@ struct Range {
 };
 
 bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Workspace cache: one grow-only device buffer per (device, stream), kept
+// until gla_release_workspaces.  Allocating and freeing a workspace around
+// every call would cost tens of microseconds of host time per call (the
+// stream-ordered free alone), more than the kernels of a mid-sized call take.
+// Work on one stream runs in order, so the next call on that stream can reuse
+// the buffer; every use also records an event that the next use waits on,
+// which keeps the order when a destroyed stream's handle value comes back for
+// a new stream.  An outgrown buffer is retired, not freed, since another host
+// thread may just have enqueued work on it; retired buffers are freed with the
+// rest by gla_release_workspaces.  Under stream capture a call takes a
+// stream-ordered allocation of its own (the captured graph owns it).
+struct WsEntry {
+  int dev;
+  hipStream_t stream;
+  void* ptr;
+  size_t bytes;
+  hipEvent_t done;
+  bool used;
+};
+std::mutex g_ws_mu;
+std::vector<WsEntry> g_ws;
+std::vector<std::pair<int, void*>> g_ws_retired;
+
+class WsLease {
+ public:
+  // A buffer of at least `bytes` for the work enqueued next on st.
+  hipError_t acquire(hipStream_t st, size_t bytes) {
+    st_ = st;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(st, &cs);
+    if (e != hipSuccess) return e;
+    if (cs != hipStreamCaptureStatusNone) {
+      captured_ = true;
+      return hipMallocAsync(&ptr_, bytes, st);
+    }
+    int dev = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    WsEntry* w = nullptr;
+    for (WsEntry& x : g_ws)
+      if (x.dev == dev && x.stream == st) w = &x;
+    if (w == nullptr) {
+      WsEntry n{dev, st, nullptr, 0, nullptr, false};
+      if ((e = hipEventCreateWithFlags(&n.done, hipEventDisableTiming)) != hipSuccess) return e;
+      g_ws.push_back(n);
+      w = &g_ws.back();
+    }
+    if (w->used && (e = hipStreamWaitEvent(st, w->done, 0)) != hipSuccess) return e;
+    if (w->bytes < bytes) {
+      const size_t granule = (size_t)1 << 21;
+      const size_t nb = (bytes + granule - 1) / granule * granule;
+      void* fresh = nullptr;
+      if ((e = hipMalloc(&fresh, nb)) != hipSuccess) return e;
+      if (w->ptr != nullptr) g_ws_retired.emplace_back(dev, w->ptr);
+      w->ptr = fresh;
+      w->bytes = nb;
+    }
+    w->used = true;
+    ptr_ = w->ptr;
+    done_ = w->done;
+    return hipSuccess;
+  }
+  // After the call's launches: mark the buffer's last use (or hand the
+  // captured allocation back in stream order).
+  hipError_t finish() {
+    if (ptr_ == nullptr) return hipSuccess;
+    if (captured_) return hipFreeAsync(ptr_, st_);
+    return hipEventRecord(done_, st_);
+  }
+  void* ptr() const { return ptr_; }
+
+ private:
+  hipStream_t st_ = nullptr;
+  void* ptr_ = nullptr;
+  hipEvent_t done_ = nullptr;
+  bool captured_ = false;
+};
 
 // Events of the measurement hook, per calling thread (see gla_set_kernel_events).
 thread_local hipEvent_t t_events[6];
@@ -168,19 +248,18 @@ int forward(gla::Dtype dt, size_t esize, const void* q, const void* k, const voi
   p.n_spans = n_spans;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
-  void* ws = nullptr;
+  WsLease ws;
   if (n_spans > 1) {
     const size_t state_elems = (size_t)BH * n_spans * d_k * d_v;
     const size_t gate_elems = (size_t)BH * n_spans * d_k;
-    if (hipMallocAsync(&ws, (state_elems + gate_elems) * sizeof(float), st) != hipSuccess)
-      return GLA_ERR_HIP;
-    p.span_state = static_cast<float*>(ws);
+    if (ws.acquire(st, (state_elems + gate_elems) * sizeof(float)) != hipSuccess) return GLA_ERR_HIP;
+    p.span_state = static_cast<float*>(ws.ptr());
     p.span_gate = p.span_state + state_elems;
   }
   const hipEvent_t* ev = t_events_set ? t_events : nullptr;
   t_events_set = false;
   const hipError_t e = gla::launch_forward(dt, d_k, d_v, ex.gate_logits, p, st, ev);
-  if (ws != nullptr && hipFreeAsync(ws, st) != hipSuccess) return GLA_ERR_HIP;
+  if (ws.finish() != hipSuccess) return GLA_ERR_HIP;
   return e == hipSuccess ? GLA_OK : GLA_ERR_HIP;
 }
 
@@ -359,10 +438,9 @@ int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* log_a
     const size_t map = (size_t)d_k * d_v;
     const size_t fwd_floats = (size_t)BH * n_spans * (map + d_k);
     const size_t adj_floats = (size_t)BH * (n_spans + 1) * (map + d_k);
-    void* ws = nullptr;
-    if (hipMallocAsync(&ws, (fwd_floats + adj_floats) * sizeof(float), st) != hipSuccess)
-      return GLA_ERR_HIP;
-    float* w = static_cast<float*>(ws);
+    WsLease ws;
+    if (ws.acquire(st, (fwd_floats + adj_floats) * sizeof(float)) != hipSuccess) return GLA_ERR_HIP;
+    float* w = static_cast<float*>(ws.ptr());
     f.span_state = w;
     f.span_gate = w + (size_t)BH * n_spans * map;
     gla::FwdParams a = f;
@@ -404,7 +482,7 @@ int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* log_a
     hipError_t e = gla::launch_bwd_states(d_k, d_v, f, a, st, ev);
     if (e == hipSuccess)
       e = gla::launch_bwd_chunks(d_k, d_v, pb, st, ev ? ev[4] : nullptr, ev ? ev[5] : nullptr);
-    if (hipFreeAsync(ws, st) != hipSuccess) return GLA_ERR_HIP;
+    if (ws.finish() != hipSuccess) return GLA_ERR_HIP;
     return e == hipSuccess ? GLA_OK : GLA_ERR_HIP;
   } catch (...) {
     return GLA_ERR_HIP;
@@ -475,16 +553,16 @@ int gla_saga_fwd(const void* q, const void* k, const void* v, const void* alpha,
     hipStream_t st = static_cast<hipStream_t>(stream);
     const size_t map = (size_t)d_k * d_v;
     const size_t ws_floats = BH * map + BH * p.n_spans * map;   // transposed maps, partials
-    void* ws = nullptr;
-    if (hipMallocAsync(&ws, ws_floats * sizeof(float), st) != hipSuccess) return GLA_ERR_HIP;
-    float* wsf = static_cast<float*>(ws);
+    WsLease ws;
+    if (ws.acquire(st, ws_floats * sizeof(float)) != hipSuccess) return GLA_ERR_HIP;
+    float* wsf = static_cast<float*>(ws.ptr());
     p.kv = kv;
     p.kvt = wsf;
     p.partial = wsf + BH * map;
     const hipEvent_t* ev = t_events_set ? t_events : nullptr;
     t_events_set = false;
     const hipError_t e = gla::launch_saga(p, st, ev);
-    if (ws != nullptr && hipFreeAsync(ws, st) != hipSuccess) return GLA_ERR_HIP;
+    if (ws.finish() != hipSuccess) return GLA_ERR_HIP;
     return e == hipSuccess ? GLA_OK : GLA_ERR_HIP;
   } catch (...) {
     return GLA_ERR_HIP;
@@ -542,6 +620,42 @@ const char* gla_status_str(int status) {
   }
 }
 
-int gla_version(void) { return 140; }
+int gla_release_workspaces(void) {
+  try {
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    if (g_ws.empty() && g_ws_retired.empty()) return GLA_OK;
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return GLA_ERR_HIP;
+    int status = GLA_OK;
+    std::vector<int> devs;
+    for (const WsEntry& w : g_ws) devs.push_back(w.dev);
+    for (const auto& r : g_ws_retired) devs.push_back(r.first);
+    for (size_t i = 0; i < devs.size(); ++i) {
+      bool seen = false;
+      for (size_t j = 0; j < i; ++j) seen = seen || devs[j] == devs[i];
+      if (seen) continue;
+      // every buffer of this device may still be in use by enqueued work
+      if (hipSetDevice(devs[i]) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+        status = GLA_ERR_HIP;
+        continue;
+      }
+      for (const WsEntry& w : g_ws) {
+        if (w.dev != devs[i]) continue;
+        if (w.ptr != nullptr && hipFree(w.ptr) != hipSuccess) status = GLA_ERR_HIP;
+        if (hipEventDestroy(w.done) != hipSuccess) status = GLA_ERR_HIP;
+      }
+      for (const auto& r : g_ws_retired)
+        if (r.first == devs[i] && hipFree(r.second) != hipSuccess) status = GLA_ERR_HIP;
+    }
+    if (hipSetDevice(cur) != hipSuccess) status = GLA_ERR_HIP;
+    g_ws.clear();
+    g_ws_retired.clear();
+    return status;
+  } catch (...) {
+    return GLA_ERR_HIP;
+  }
+}
+
+int gla_version(void) { return 150; }
 
 }  // extern "C"

@@ -44,6 +44,11 @@ def test_library_exports_every_declared_symbol():
         assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
 
 
+def test_release_with_nothing_held_makes_no_hip_call():
+    # no workspace exists in a process that made no accepted call on a device
+    assert _lib.load().gla_release_workspaces() == 0
+
+
 def test_status_strings_and_version():
     for code in range(-7, 1):
         s = _lib.status_str(code)
