@@ -131,10 +131,42 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
   const float* R_span =
       p.adj_state + ((size_t)bh * (p.n_spans + 1) + (p.n_spans - 1 - sp)) * DK * DV;
   float* const stage = sEc;  // the partner-formed state, before sEc is needed
-  const float* E = e_from_partner ? stage : E_span;
-  const float* R = r_from_partner ? stage : R_span;
-  const int e_ld = e_from_partner ? ES : DV;   // row strides of E and R
-  const int r_ld = r_from_partner ? ES : DV;
+  const int kb = wave;          // key dims 16 kb .. owned by this wave (dq, dk, dla)
+  const int vb = wave;          // value dims 16 vb .. (dv, next state rows)
+  const int ki = 16 * kb + 4 * g;  // first of the lane's 4 key dims in a dq / dk tile
+  const int vj = 16 * vb + 4 * g;
+
+  // ---- 0. the span states, read from memory before the tiles so that their
+  // latency hides behind the tiles': E and R in the accumulator layout of the
+  // next-state update (rows 16 kc + n, columns 16 w + 4g ..; for the state a
+  // partner completes, the span's part of it), and, for a state taken as it
+  // is, the MFMA operand layouts below (raw float32 until the tiles landed)
+  f32x4 e4s[4], r4s[4], ea_raw[4], ra_raw[4];
+  float rta_raw[16];
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc) {
+    e4s[kc] = *reinterpret_cast<const f32x4*>(E_span + (16 * kc + n16) * DV + vj);
+    r4s[kc] = *reinterpret_cast<const f32x4*>(R_span + (16 * kc + n16) * DV + vj);
+  }
+  if (!e_from_partner) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      ea_raw[2 * h] = *reinterpret_cast<const f32x4*>(E_span + (16 * kb + n16) * DV + 32 * h + 8 * g);
+      ea_raw[2 * h + 1] =
+          *reinterpret_cast<const f32x4*>(E_span + (16 * kb + n16) * DV + 32 * h + 8 * g + 4);
+    }
+  }
+  if (!r_from_partner) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      ra_raw[2 * h] = *reinterpret_cast<const f32x4*>(R_span + (16 * kb + n16) * DV + 32 * h + 8 * g);
+      ra_raw[2 * h + 1] =
+          *reinterpret_cast<const f32x4*>(R_span + (16 * kb + n16) * DV + 32 * h + 8 * g + 4);
+      // R^T rows 16 vb + n: R[32 h + 8g + e][16 vb + n]
+#pragma unroll
+      for (int e = 0; e < 8; ++e) rta_raw[8 * h + e] = R_span[(32 * h + 8 * g + e) * DV + 16 * vb + n16];
+    }
+  }
 
   // ---- 1. tiles (and the partner's: keys or queries, log-alpha, values or
   // output gradients into the operand-tile and sEc areas), cumulative decay
@@ -167,6 +199,15 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
     }
   }
   wait_barrier<vmcnt_lgkm0_imm(0)>();  // tiles landed, row table written
+  // the raw state values are used from here on only: the empty asm keeps their
+  // conversions (and so the compiler's waits for them) after the wait above
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    asm volatile("" : "+v"(ea_raw[j]), "+v"(ra_raw[j]));
+    asm volatile("" : "+v"(e4s[j]), "+v"(r4s[j]));
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) asm volatile("" : "+v"(rta_raw[j]));
 
   if (e_from_partner || r_from_partner) {
     // partner decay profile per key dim: keys decayed to the partner's end
@@ -220,46 +261,44 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
       }
       st[kc] = acc;
     }
-    const float* span = e_from_partner ? E_span : R_span;
     f32x4 x[4];
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
       const int row = 16 * kc + n16;
-      const f32x4 s4 = *reinterpret_cast<const f32x4*>(span + row * DV + 16 * wave + 4 * g);
-      x[kc] = sCarry[0][row] * s4 + st[kc];
+      x[kc] = sCarry[0][row] * (e_from_partner ? e4s[kc] : r4s[kc]) + st[kc];
+      if (e_from_partner) e4s[kc] = x[kc];
+      else r4s[kc] = x[kc];
     }
     __syncthreads();  // every wave is done with the partner tiles in sEc
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc)
-      *reinterpret_cast<f32x4*>(stage + (16 * kc + n16) * ES + 16 * wave + 4 * g) = x[kc];
+      *reinterpret_cast<f32x4*>(stage + (16 * kc + n16) * ES + vj) = x[kc];
     __syncthreads();
   }
 
-  // This chunk's states in the layouts the MFMAs below read: E and R rows of
-  // the wave's key dims as float16 A operands (lane (n, g): row 16 kb + n,
-  // columns 32 h + 8g .. + 7), R^T rows of its value dims, and E, R in the
-  // accumulator layout of the next-state update (rows 16 kc + n, columns
-  // 16 w + 4g ..), read now while the staged state is still in place.
-  const int kb = wave;          // key dims 16 kb .. owned by this wave (dq, dk, dla)
-  const int vb = wave;          // value dims 16 vb .. (dv, next state rows)
-  const int ki = 16 * kb + 4 * g;  // first of the lane's 4 key dims in a dq / dk tile
-  const int vj = 16 * vb + 4 * g;
+  // This chunk's states as float16 MFMA A operands: E and R rows of the
+  // wave's key dims (lane (n, g): row 16 kb + n, columns 32 h + 8g .. + 7) and
+  // R^T rows of its value dims; a partner-formed state is read from the stage
+  // while it is still in place.
   f16x8 ea[2], ra[2], rta[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    ea[h] = ld8f(E + (16 * kb + n16) * e_ld + 32 * h + 8 * g);
-    ra[h] = ld8f(R + (16 * kb + n16) * r_ld + 32 * h + 8 * g);
-    // R^T rows 16 vb + n: R[32 h + 8g + e][16 vb + n]
+    if (e_from_partner) {
+      ea[h] = ld8f(stage + (16 * kb + n16) * ES + 32 * h + 8 * g);
+    } else {
+      ea[h] = cat8(to_f16(ea_raw[2 * h]), to_f16(ea_raw[2 * h + 1]));
+    }
     f16x8 x;
+    if (r_from_partner) {
+      ra[h] = ld8f(stage + (16 * kb + n16) * ES + 32 * h + 8 * g);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = (f16)R[(32 * h + 8 * g + e) * r_ld + 16 * vb + n16];
+      for (int e = 0; e < 8; ++e) x[e] = (f16)stage[(32 * h + 8 * g + e) * ES + 16 * vb + n16];
+    } else {
+      ra[h] = cat8(to_f16(ra_raw[2 * h]), to_f16(ra_raw[2 * h + 1]));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = (f16)rta_raw[8 * h + e];
+    }
     rta[h] = x;
-  }
-  f32x4 e4s[4], r4s[4];
-#pragma unroll
-  for (int kc = 0; kc < 4; ++kc) {
-    e4s[kc] = *reinterpret_cast<const f32x4*>(E + (16 * kc + n16) * e_ld + vj);
-    r4s[kc] = *reinterpret_cast<const f32x4*>(R + (16 * kc + n16) * r_ld + vj);
   }
   __syncthreads();  // the staging area becomes sEc
 
