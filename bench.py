@@ -25,7 +25,6 @@ import hashlib
 import json
 import math
 import os
-import re
 import sys
 import time
 
@@ -41,22 +40,11 @@ SWIGLU_SRC = os.path.join(ROOT, "recurrent_vision_token_amd", "csrc", "swiglu_ke
 SAGA_SRC = os.path.join(ROOT, "recurrent_vision_token_amd", "csrc", "saga_kernels.hip")
 BWD_SRC = os.path.join(ROOT, "recurrent_vision_token_amd", "csrc", "gla_bwd_kernels.hip")
 KERNEL_NAMES = ("span_summary", "span_scan", "chunk_output", "spatial_swiglu", "saga_kv_partial",
-                "saga_kv_reduce", "saga_out", "chunk_bwd", "bwd_state_summary", "bwd_state_scan",
-                "bwd_adjoint_summary", "bwd_adjoint_scan")
-# the summary and scan kernels carry a last template argument that names their
-# role: 0 the forward pass, 1 the backward pass's forward entry states, 2 its
-# adjoint states
-ROLE_KEYS = {"1": "bwd_state_", "2": "bwd_adjoint_"}
+                "saga_kv_reduce", "saga_out", "chunk_bwd", "bwd_state_summaries", "bwd_state_scans")
 
 
 def kernel_key(name):
     """The KERNEL_NAMES entry a (demangled) kernel name belongs to, or None."""
-    for base in ("span_summary", "span_scan"):
-        m = re.search(base + r"\w*<([^>]*)>", name)
-        if m:
-            role = m.group(1).split(",")[-1].strip()
-            prefix = ROLE_KEYS.get(role)
-            return prefix + base.split("_")[1] if prefix else base
     return next((k for k in KERNEL_NAMES if k in name), None)
 
 
@@ -417,8 +405,8 @@ def time_bwd(wl, torch, steps, warmup):
         r.step(evs[s_])
     torch.cuda.synchronize()
     flat = [e for per_step in evs for e in per_step]
-    k_ms = {"forward_states": sum(e[0].elapsed_time(e[1]) for e in flat) / len(flat),
-            "adjoint_states": sum(e[2].elapsed_time(e[3]) for e in flat) / len(flat),
+    k_ms = {"state_summaries": sum(e[0].elapsed_time(e[1]) for e in flat) / len(flat),
+            "state_scans": sum(e[2].elapsed_time(e[3]) for e in flat) / len(flat),
             "chunk_bwd": sum(e[4].elapsed_time(e[5]) for e in flat) / len(flat),
             "call": sum(e[0].elapsed_time(e[5]) for e in flat) / len(flat)}
     return r, ms_step, k_ms

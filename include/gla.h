@@ -181,8 +181,9 @@ int gla_plan_spans(int use_f32, int B, int heads, int H, int W, int d_k, int d_v
  * ceil(ceil(H*W/64) / 2).  Domain as gla_chunk_fwd, plus
  * d_out . v and its kin within float16 range.  Errors as gla_chunk_fwd
  * (GLA_ERR_UNSUPPORTED for any other d_k, d_v or chunk).  With the
- * measurement hook armed, event pairs bracket the forward-state kernels
- * (events 0, 1), the adjoint-state kernels (2, 3) and the chunk kernel (4, 5).
+ * measurement hook armed, event pairs bracket the kernel that forms both
+ * summaries of every span (events 0, 1), the kernel that scans both (2, 3)
+ * and the chunk kernel (4, 5).
  */
 int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* log_alpha,
                   const void* d_out, const float* d_final_state, const float* initial_state,

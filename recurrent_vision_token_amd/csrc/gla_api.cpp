@@ -443,13 +443,11 @@ int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* log_a
     float* w = static_cast<float*>(ws.ptr());
     f.span_state = w;
     f.span_gate = w + (size_t)BH * n_spans * map;
-    gla::FwdParams a = f;
-    a.k = q;
-    a.v = d_out;
-    a.initial_state = d_final_state;
-    a.span_state = w + fwd_floats;
-    a.span_gate = a.span_state + (size_t)BH * (n_spans + 1) * map;
-    a.adj_slots = n_spans + 1;
+    f.dout = d_out;
+    f.adj_initial = d_final_state;
+    f.adj_state = w + fwd_floats;
+    f.adj_gate = f.adj_state + (size_t)BH * (n_spans + 1) * map;
+    f.adj_slots = n_spans + 1;
 
     gla::BwdParams pb{};
     pb.q = q;
@@ -462,7 +460,7 @@ int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* log_a
     pb.dv = dv;
     pb.dla = dlog_alpha;
     pb.fwd_state = f.span_state;
-    pb.adj_state = a.span_state;
+    pb.adj_state = f.adj_state;
     pb.d_initial_state = d_initial_state;
     pb.B = B;
     pb.heads = heads;
@@ -479,7 +477,7 @@ int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* log_a
 
     const hipEvent_t* ev = t_events_set ? t_events : nullptr;
     t_events_set = false;
-    hipError_t e = gla::launch_bwd_states(d_k, d_v, f, a, st, ev);
+    hipError_t e = gla::launch_bwd_states(d_k, d_v, f, st, ev);
     if (e == hipSuccess)
       e = gla::launch_bwd_chunks(d_k, d_v, pb, st, ev ? ev[4] : nullptr, ev ? ev[5] : nullptr);
     if (ws.finish() != hipSuccess) return GLA_ERR_HIP;

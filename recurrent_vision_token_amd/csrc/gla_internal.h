@@ -29,7 +29,12 @@ struct FwdParams {
   int n_chunks;         // ceil(T / 64)
   int span_chunks;      // chunks handled by one workgroup of the output kernel
   int n_spans;          // ceil(n_chunks / span_chunks)
-  int adj_slots;        // backward pass: summary slots per sequence of the adjoint scan
+  // backward pass: the adjoint recurrence's inputs and summaries
+  int adj_slots;        // summary slots per sequence of the adjoint scan (n_spans + 1)
+  const void* dout;     // the output gradient, in place of v
+  float* adj_state;     // [BH][adj_slots][d_k][d_v]
+  float* adj_gate;      // [BH][adj_slots][d_k]
+  const float* adj_initial;  // the final-state gradient (scan start), may be null
 };
 
 // Multiply-shift constants for dividing t < 2^31 by d >= 1:
@@ -50,16 +55,15 @@ bool has_variant(Dtype dt, int d_k, int d_v);
 hipError_t launch_forward(Dtype dt, int d_k, int d_v, bool gate_logits, const FwdParams& p,
                           hipStream_t stream, hipEvent_t const* events);
 
-// Backward pass, float16, d_k = d_v = 64.  `fwd` describes the forward
-// tensors with one chunk per span (n_spans = n_chunks) and the forward-state
-// workspace; `adj` the adjoint summaries: k = q, v = the output gradient,
-// initial_state = the final-state gradient (or null), adj_slots = n_chunks + 1
-// and its own workspace.  Runs the span-summary and span-scan kernels for
-// both; events: null, or at least four hipEvent_t, recorded at the start of
-// the forward summary, the end of its scan, the start of the adjoint summary
-// and the end of its scan.
-hipError_t launch_bwd_states(int d_k, int d_v, const FwdParams& fwd, const FwdParams& adj,
-                             hipStream_t stream, hipEvent_t const* events);
+// Backward pass, float16, d_k = d_v = 64.  `p` describes the forward
+// tensors (q, k, v, la; spans of span_chunks chunks, n_spans of them) with
+// the forward-state workspace (span_state, span_gate, initial_state) and the
+// adjoint recurrence: dout, adj_state, adj_gate, adj_initial (the final-state
+// gradient) and adj_slots = n_spans + 1.  Runs the fused summaries kernel
+// and the fused scans kernel; events: null, or at least four hipEvent_t, the
+// start / stop of each.
+hipError_t launch_bwd_states(int d_k, int d_v, const FwdParams& p, hipStream_t stream,
+                             hipEvent_t const* events);
 
 // The chunk kernel of the backward pass: one workgroup per (batch*head,
 // chunk) turns the chunk's tiles, its forward entry state and the adjoint

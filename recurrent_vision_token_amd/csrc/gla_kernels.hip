@@ -373,36 +373,37 @@ __global__ __launch_bounds__(kThreads) void span_summary_kernel(FwdParams p) {
 // trip), folds them from zero, the folds are exchanged through LDS to give
 // every segment its carry-in, and the same registers then yield the entry
 // states.
-constexpr int kRoleForward = 0, kRoleStates = 1, kRoleAdjoint = 2;
 constexpr int kScanSeg = 4;
 constexpr int kScanU = 32;
 constexpr int kScanElems = kThreads / kScanSeg;   // state elements per workgroup
 
-// ROLE only names the launch in traces and counters: 0 the forward pass, 1 the
-// backward pass's forward entry states, 2 its adjoint states.
-template <int DK, int DV, int ROLE = kRoleForward>
-__global__ __launch_bounds__(kThreads) void span_scan_kernel(FwdParams p) {
+// One workgroup scans the state elements yb * kScanElems .. of sequence bh
+// over n_spans summaries (state [BH][n_spans][DK][DV], gate [BH][n_spans][DK]),
+// in place.
+template <int DK, int DV>
+__device__ __forceinline__ void span_scan_body(float* span_state, const float* span_gate,
+                                               const float* initial_state, int n_spans, int bh,
+                                               int yb) {
   __shared__ float seg_l[kScanSeg][kScanElems];
   __shared__ float seg_g[kScanSeg][kScanElems];
-  const int bh = blockIdx.x;
   const int seg = threadIdx.x / kScanElems;
   const int le = threadIdx.x - seg * kScanElems;
-  const int e = blockIdx.y * kScanElems + le;
+  const int e = yb * kScanElems + le;
   const int dim = e / DV;
-  float* const L = p.span_state + (size_t)bh * p.n_spans * DK * DV + e;
-  const float* const G = p.span_gate + (size_t)bh * p.n_spans * DK + dim;
+  float* const L = span_state + (size_t)bh * n_spans * DK * DV + e;
+  const float* const G = span_gate + (size_t)bh * n_spans * DK + dim;
 
   // state entering the current round; the first round starts from the
   // initial state, which the scan also writes as span 0's entry state
-  float carry = p.initial_state ? p.initial_state[(size_t)bh * DK * DV + e] : 0.f;
-  for (int r0 = 0; r0 < p.n_spans; r0 += kScanSeg * kScanU) {
+  float carry = initial_state ? initial_state[(size_t)bh * DK * DV + e] : 0.f;
+  for (int r0 = 0; r0 < n_spans; r0 += kScanSeg * kScanU) {
     const int s0 = r0 + seg * kScanU;
     float l[kScanU], gg[kScanU];
 #pragma unroll
     for (int u = 0; u < kScanU; ++u) {
       // slots past the last span re-read span 0 and are neutralised (no
       // branches around the loads, so all of them are in flight together)
-      const bool in = s0 + u < p.n_spans;
+      const bool in = s0 + u < n_spans;
       const int sp = in ? s0 + u : 0;
       const float lv = L[(size_t)sp * DK * DV];
       const float gv = G[(size_t)sp * DK];
@@ -425,11 +426,32 @@ __global__ __launch_bounds__(kThreads) void span_scan_kernel(FwdParams p) {
     }
 #pragma unroll
     for (int u = 0; u < kScanU; ++u) {
-      if (s0 + u < p.n_spans) L[(size_t)(s0 + u) * DK * DV] = run;
+      if (s0 + u < n_spans) L[(size_t)(s0 + u) * DK * DV] = run;
       run = gg[u] * run + l[u];
     }
     carry = next;
     __syncthreads();  // the LDS folds are reused by the next round
+  }
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(kThreads) void span_scan_kernel(FwdParams p) {
+  span_scan_body<DK, DV>(p.span_state, p.span_gate, p.initial_state, p.n_spans, blockIdx.x,
+                         blockIdx.y);
+}
+
+// The backward pass's two scans in one launch: blockIdx.y below half the grid
+// scans the forward summaries (from the initial state), the rest the adjoint
+// summaries (from the final-state gradient; adj_slots slots).
+template <int DK, int DV>
+__global__ __launch_bounds__(kThreads) void bwd_state_scans_kernel(FwdParams p) {
+  constexpr int kBlocks = DK * DV / kScanElems;
+  if ((int)blockIdx.y < kBlocks) {
+    span_scan_body<DK, DV>(p.span_state, p.span_gate, p.initial_state, p.n_spans, blockIdx.x,
+                           blockIdx.y);
+  } else {
+    span_scan_body<DK, DV>(p.adj_state, p.adj_gate, p.adj_initial, p.adj_slots, blockIdx.x,
+                           blockIdx.y - kBlocks);
   }
 }
 
@@ -1050,21 +1072,107 @@ struct SumTile {
   f16* v;
 };
 
-//
-// ROLE kRoleStates instantiates the same code, under a name of its own, for the
-// backward pass's forward entry states (spans of several chunks); kRoleAdjoint
-// instantiates it for the backward pass's adjoint summaries:
-// with q in place of k and the output gradient in place of v it folds
-// dR = (Q * exp(B))^T dO, B the decay from the span start through each token
-// (inclusive): chunks are taken last to first, each from its own start, and
-// the summary of the later chunks is decayed by the chunk's total before it
-// adds in.  Span s's summary goes to slot adj_slots - 2 - s, so that the scan
-// over the slots runs from the end of the sequence to its start; the first
-// span also writes the neutral summary (gate 1, state 0) into the last slot,
-// whose entry state is then the gradient of the state before the first step.
-template <int DK, int DV, bool GATE, int ROLE = kRoleForward>
+// One chunk's part of a span summary, for the wave's key blocks (tiles in
+// LDS; `valid` tokens of the chunk are real).  Chunks are folded last to
+// first.
+//   ADJ false: the forward summary.  gdec holds the decay from this chunk's
+//     end to the span's end; keys are decayed to the span end and
+//     S^T += V^T Kl.
+//   ADJ true: the adjoint summary, with q in place of k and the output
+//     gradient in place of v: dR = (Q * exp(B))^T dO, B the decay from the
+//     span start through each token (inclusive).  Each chunk is taken from
+//     its own start, and the summary of the later chunks, already folded, is
+//     decayed by this chunk's total before this chunk adds in; gdec then
+//     holds the decay of the chunks folded so far.
+template <int DK, int DV, bool GATE, bool ADJ>
+__device__ __forceinline__ void fold_chunk(const SumTile<DK, DV>& s, int valid, float inv_tau,
+                                           f16x4 m_tri, f16x4 m_ones, int wave,
+                                           f32x4 (&st)[DK / 64][DV / 16],
+                                           f32x4 (&gdec)[DK / 64]) {
+  constexpr int NDB = DK / 64, NCB = DV / 16;
+  constexpr int RBK = 2 * DK, RBV = 2 * DV;
+#pragma unroll
+  for (int d = 0; d < NDB; ++d) {
+    const int db = wave + 4 * d;
+    f16x4 lat[4], kt[4];
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+      lat[J] = log_alpha_of<GATE>(tr_read<RBK>(s.la, 16 * J, 16 * db), inv_tau, 16 * J, valid);
+      kt[J] = tr_read<RBK>(s.k, 16 * J, 16 * db);
+    }
+    f32x4 rest[4];
+    f32x4 c = gdec[d];
+    if constexpr (ADJ) {
+      f32x4 cl = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        rest[J] = mma16(m_tri, lat[J], cl);
+        cl = mma16(m_ones, lat[J], cl);
+      }
+      const float whole = exp2_fast(cl[0] * 1.4426950408889634f);  // key dim 16 db + n
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) st[d][cb] *= whole;
+      c = c + cl;
+    } else {
+#pragma unroll
+      for (int J = 3; J >= 0; --J) {
+        rest[J] = mma16(m_tri, lat[J], c);
+        c = mma16(m_ones, lat[J], c);
+      }
+    }
+    gdec[d] = c;
+    f16x4 kl[4];
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+      f32x4 e;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) e[u] = exp2_fast(rest[J][u] * 1.4426950408889634f);
+      kl[J] = kt[J] * __builtin_convertvector(e, f16x4);
+    }
+#pragma unroll
+    for (int P = 0; P < 2; ++P) {
+      const f16x8 bk = cat8(kl[2 * P], kl[2 * P + 1]);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const f16x8 av = cat8(tr_read<RBV>(s.v, 32 * P, 16 * cb), tr_read<RBV>(s.v, 32 * P + 16, 16 * cb));
+        st[d][cb] = mma32(av, bk, st[d][cb]);
+      }
+    }
+  }
+}
+
+// A operands of the decay chains: strictly upper triangular (s > t) for the
+// forward summary, lower triangular inclusive (s <= t) for the adjoint one,
+// and all ones.
+template <bool ADJ>
+__device__ __forceinline__ f16x4 tri_operand(int n16, int g) {
+  f16x4 m;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) m[u] = (f16)((ADJ ? (4 * g + u <= n16) : (4 * g + u > n16)) ? 1.f : 0.f);
+  return m;
+}
+
+// Writes one summary (state rows of the wave's key blocks, gate) to `slot`
+// of the sequence's `slots`.
+template <int DK, int DV>
+__device__ __forceinline__ void store_summary(float* span_state, float* span_gate, int bh,
+                                              size_t slots, size_t slot, int wave, int n16, int g,
+                                              const f32x4 (&st)[DK / 64][DV / 16],
+                                              const f32x4 (&gdec)[DK / 64]) {
+  float* dst = span_state + ((size_t)bh * slots + slot) * DK * DV;
+#pragma unroll
+  for (int d = 0; d < DK / 64; ++d) {
+    const int dim = 16 * (wave + 4 * d) + n16;
+#pragma unroll
+    for (int cb = 0; cb < DV / 16; ++cb)
+      *reinterpret_cast<f32x4*>(dst + dim * DV + 16 * cb + 4 * g) = st[d][cb];
+    if (g == 0)
+      span_gate[((size_t)bh * slots + slot) * DK + dim] = exp2_fast(gdec[d][0] * 1.4426950408889634f);
+  }
+}
+
+template <int DK, int DV, bool GATE>
 __global__ __launch_bounds__(kThreads) void span_summary_f16_kernel(FwdParams p) {
-  constexpr bool ADJ = ROLE == kRoleAdjoint;
   // six separate LDS objects, so the compiler's own waits for the LDS-writing
   // loads can tell the tiles apart
   __shared__ __attribute__((aligned(16))) f16 k0[kChunk * DK], la0[kChunk * DK], v0[kChunk * DV];
@@ -1108,14 +1216,8 @@ __global__ __launch_bounds__(kThreads) void span_summary_f16_kernel(FwdParams p)
     }
   };
 
-  // A operands: strictly upper triangular (s > t; lower inclusive, s <= t,
-  // for the adjoint) and all-ones 16x16 blocks.
-  f16x4 m_upper, m_ones;
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    m_upper[u] = (f16)((ADJ ? (4 * g + u <= n16) : (4 * g + u > n16)) ? 1.f : 0.f);
-    m_ones[u] = (f16)1.f;
-  }
+  const f16x4 m_upper = tri_operand<false>(n16, g);
+  const f16x4 m_ones = f16x4{(f16)1.f, (f16)1.f, (f16)1.f, (f16)1.f};
 
   f32x4 st[NDB][NCB];
   f32x4 gdec[NDB];  // decay (log) from the current chunk's end to the span end, per key dim
@@ -1125,59 +1227,9 @@ __global__ __launch_bounds__(kThreads) void span_summary_f16_kernel(FwdParams p)
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) st[d][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-
   auto fold = [&](const SumTile<DK, DV>& s, int c) {
-    const int valid = min(kChunk, p.T - c * kChunk);
-#pragma unroll
-    for (int d = 0; d < NDB; ++d) {
-      const int db = wave + 4 * d;
-      f16x4 lat[4], kt[4];
-#pragma unroll
-      for (int J = 0; J < 4; ++J) {
-        lat[J] = log_alpha_of<GATE>(tr_read<RBK>(s.la, 16 * J, 16 * db), p.inv_tau, 16 * J, valid);
-        kt[J] = tr_read<RBK>(s.k, 16 * J, 16 * db);
-      }
-      f32x4 rest[4];
-      f32x4 c = gdec[d];
-      if constexpr (ADJ) {
-        // decay from this chunk's start; the later chunks' summary, already
-        // folded, is decayed by this chunk's total before this chunk adds in
-        f32x4 cl = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int J = 0; J < 4; ++J) {
-          rest[J] = mma16(m_upper, lat[J], cl);
-          cl = mma16(m_ones, lat[J], cl);
-        }
-        const float whole = exp2_fast(cl[0] * 1.4426950408889634f);  // key dim 16 db + n
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) st[d][cb] *= whole;
-        c = c + cl;
-      } else {
-#pragma unroll
-        for (int J = 3; J >= 0; --J) {
-          rest[J] = mma16(m_upper, lat[J], c);
-          c = mma16(m_ones, lat[J], c);
-        }
-      }
-      gdec[d] = c;
-      f16x4 kl[4];
-#pragma unroll
-      for (int J = 0; J < 4; ++J) {
-        f32x4 e;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) e[u] = exp2_fast(rest[J][u] * 1.4426950408889634f);
-        kl[J] = kt[J] * __builtin_convertvector(e, f16x4);
-      }
-#pragma unroll
-      for (int P = 0; P < 2; ++P) {
-        const f16x8 bk = cat8(kl[2 * P], kl[2 * P + 1]);
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          const f16x8 av = cat8(tr_read<RBV>(s.v, 32 * P, 16 * cb), tr_read<RBV>(s.v, 32 * P + 16, 16 * cb));
-          st[d][cb] = mma32(av, bk, st[d][cb]);
-        }
-      }
-    }
+    fold_chunk<DK, DV, GATE, false>(s, min(kChunk, p.T - c * kChunk), p.inv_tau, m_upper, m_ones,
+                                    wave, st, gdec);
   };
 
   issue(slot0, c_end - 1);
@@ -1196,26 +1248,105 @@ __global__ __launch_bounds__(kThreads) void span_summary_f16_kernel(FwdParams p)
   // land before the workgroup's LDS can be handed on
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  store_summary<DK, DV>(p.span_state, p.span_gate, bh, p.n_spans, span, wave, n16, g, st, gdec);
+}
 
-  const size_t slots = ADJ ? (size_t)p.adj_slots : (size_t)p.n_spans;
-  const size_t slot = ADJ ? (size_t)(p.adj_slots - 2 - span) : (size_t)span;
-  float* dst = p.span_state + ((size_t)bh * slots + slot) * DK * DV;
+// The backward pass's two summaries of a span in one workgroup: the forward
+// one (k, v; the state entering each span) and the adjoint one (q and the
+// output gradient d_out; the state gradient entering each span from its
+// right), sharing the log-alpha tile.  Span s's adjoint summary goes to slot
+// adj_slots - 2 - s, so that the adjoint scan runs from the end of the
+// sequence to its start; span 0 also writes the neutral summary (gate 1,
+// state 0) into the last slot, whose entry state is then the gradient of the
+// state before the first step.  float16, no fused gate activation.
+template <int DK, int DV>
+__global__ __launch_bounds__(kThreads) void bwd_state_summaries_kernel(FwdParams p) {
+  __shared__ __attribute__((aligned(16))) f16 k0[kChunk * DK], la0[kChunk * DK], v0[kChunk * DV];
+  __shared__ __attribute__((aligned(16))) f16 q0[kChunk * DK], do0[kChunk * DV];
+  __shared__ __attribute__((aligned(16))) f16 k1[kChunk * DK], la1[kChunk * DK], v1[kChunk * DV];
+  __shared__ __attribute__((aligned(16))) f16 q1[kChunk * DK], do1[kChunk * DV];
+  const SumTile<DK, DV> fw0{k0, la0, v0}, fw1{k1, la1, v1};
+  const SumTile<DK, DV> ad0{q0, la0, do0}, ad1{q1, la1, do1};
+  constexpr int NDB = DK / 64, NCB = DV / 16;
+  constexpr int RBK = 2 * DK, RBV = 2 * DV;
+  static_assert(RBK == 128 && RBV == 128, "built for 64 key and value dims");
+  constexpr int NBK = RBK / 64;       // 1 KB blocks per wave and tile
+  constexpr int NDMA = 5 * NBK;       // LDS-writing loads per wave and chunk (k, la, v, q, d_out)
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n16 = lane & 15, g = lane >> 4;
+
+  const int bh = blockIdx.x / p.n_spans;
+  const int span = blockIdx.x - bh * p.n_spans;
+  const int b = bh / p.heads;
+  const GridMap gm = grid_map(p, b);
+  const SeqBufs sb = seq_bufs<DK, DV>(p, bh);
+  const rsrc_t rdo = seq_rsrc(static_cast<const f16*>(p.dout) + (size_t)bh * p.T * DV,
+                              (uint32_t)p.T * RBV);
+  const int c_begin = span * p.span_chunks;
+  const int c_end = min(c_begin + p.span_chunks, p.n_chunks);
+
+  auto issue = [&](const SumTile<DK, DV>& f, const SumTile<DK, DV>& a, int c) {
+    const int t0 = c * kChunk;
+    const int valid = c >= c_begin ? min(kChunk, p.T - t0) : 0;
+#pragma unroll
+    for (int i = 0; i < NBK; ++i) {
+      const int blk = wave * NBK + i;
+      const uint32_t off = dma_offset<RBK>(blk, t0, valid, gm);
+      dma16(sb.k, f.k + blk * 512, off);
+      dma16(sb.la, f.la + blk * 512, off);
+      dma16(sb.v, f.v + blk * 512, off);
+      dma16(sb.q, a.k + blk * 512, off);
+      dma16(rdo, a.v + blk * 512, off);
+    }
+  };
+
+  const f16x4 m_upper = tri_operand<false>(n16, g), m_lower = tri_operand<true>(n16, g);
+  const f16x4 m_ones = f16x4{(f16)1.f, (f16)1.f, (f16)1.f, (f16)1.f};
+  f32x4 st[NDB][NCB], gdec[NDB], sa[NDB][NCB], gadj[NDB];
 #pragma unroll
   for (int d = 0; d < NDB; ++d) {
-    const int dim = 16 * (wave + 4 * d) + n16;
+    gdec[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+    gadj[d] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-      *reinterpret_cast<f32x4*>(dst + dim * DV + 16 * cb + 4 * g) = st[d][cb];
-    if (g == 0)
-      p.span_gate[((size_t)bh * slots + slot) * DK + dim] =
-          exp2_fast(gdec[d][0] * 1.4426950408889634f);
-    if (ADJ && span == 0) {
-      // neutral summary in the last slot
-      float* last = p.span_state + ((size_t)bh * slots + slots - 1) * DK * DV;
+    for (int cb = 0; cb < NCB; ++cb) {
+      st[d][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      sa[d][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  auto fold = [&](const SumTile<DK, DV>& f, const SumTile<DK, DV>& a, int c) {
+    const int valid = min(kChunk, p.T - c * kChunk);
+    fold_chunk<DK, DV, false, false>(f, valid, 1.f, m_upper, m_ones, wave, st, gdec);
+    fold_chunk<DK, DV, false, true>(a, valid, 1.f, m_lower, m_ones, wave, sa, gadj);
+  };
+
+  issue(fw0, ad0, c_end - 1);
+  issue(fw1, ad1, c_end - 2);
+  for (int c = c_end - 1; c >= c_begin; c -= 2) {
+    wait_barrier<vmcnt_imm(NDMA)>();  // every wave's part of slot 0 has landed
+    fold(fw0, ad0, c);
+    wait_barrier<kLgkmZero>();        // every wave's reads of slot 0 are done
+    issue(fw0, ad0, c - 2);
+    wait_barrier<vmcnt_imm(NDMA)>();
+    if (c - 1 >= c_begin) fold(fw1, ad1, c - 1);
+    wait_barrier<kLgkmZero>();
+    issue(fw1, ad1, c - 3);
+  }
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  store_summary<DK, DV>(p.span_state, p.span_gate, bh, p.n_spans, span, wave, n16, g, st, gdec);
+  const size_t slots = p.adj_slots;
+  store_summary<DK, DV>(p.adj_state, p.adj_gate, bh, slots, slots - 2 - span, wave, n16, g, sa,
+                        gadj);
+  if (span == 0) {
+    float* last = p.adj_state + ((size_t)bh * slots + slots - 1) * DK * DV;
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) {
+      const int dim = 16 * (wave + 4 * d) + n16;
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
         *reinterpret_cast<f32x4*>(last + dim * DV + 16 * cb + 4 * g) = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (g == 0) p.span_gate[((size_t)bh * slots + slots - 1) * DK + dim] = 1.f;
+      if (g == 0) p.adj_gate[((size_t)bh * slots + slots - 1) * DK + dim] = 1.f;
     }
   }
 }
@@ -1350,36 +1481,24 @@ hipError_t launch_marked(K kernel, dim3 grid, hipStream_t stream, const FwdParam
 }
 
 template <int DK, int DV>
-hipError_t launch_bwd_states_variant(const FwdParams& fwd, const FwdParams& adj,
-                                     hipStream_t stream, hipEvent_t const* ev) {
-  const int BH = fwd.B * fwd.heads;
-  const dim3 scan_grid(BH, DK * DV / kScanElems);
+hipError_t launch_bwd_states_variant(const FwdParams& p, hipStream_t stream, hipEvent_t const* ev) {
+  const int BH = p.B * p.heads;
   hipError_t e;
-  // forward entry state of every chunk
-  if ((e = launch_marked(span_summary_f16_kernel<DK, DV, false, kRoleStates>, dim3(BH * fwd.n_spans),
-                         stream, fwd, ev ? ev[0] : nullptr, nullptr)) != hipSuccess)
+  // both summaries of every span, then both scans: the forward entry state
+  // of every span, the adjoint state entering every span from its right, and
+  // the gradient of the state before the first step in the adjoint's last slot
+  if ((e = launch_marked(bwd_state_summaries_kernel<DK, DV>, dim3(BH * p.n_spans), stream, p,
+                         ev ? ev[0] : nullptr, ev ? ev[1] : nullptr)) != hipSuccess)
     return e;
-  if ((e = launch_marked(span_scan_kernel<DK, DV, kRoleStates>, scan_grid, stream, fwd, nullptr,
-                         ev ? ev[1] : nullptr)) != hipSuccess)
-    return e;
-  // adjoint state entering every chunk from its right, and the gradient of
-  // the state before the first step in the extra last slot
-  FwdParams sum = adj;
-  sum.n_spans = adj.adj_slots - 1;
-  if ((e = launch_marked(span_summary_f16_kernel<DK, DV, false, kRoleAdjoint>, dim3(BH * sum.n_spans),
-                         stream, sum, ev ? ev[2] : nullptr, nullptr)) != hipSuccess)
-    return e;
-  FwdParams scan = adj;
-  scan.n_spans = adj.adj_slots;
-  return launch_marked(span_scan_kernel<DK, DV, kRoleAdjoint>, scan_grid, stream, scan, nullptr,
-                       ev ? ev[3] : nullptr);
+  return launch_marked(bwd_state_scans_kernel<DK, DV>, dim3(BH, 2 * DK * DV / kScanElems), stream,
+                       p, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr);
 }
 
 }  // namespace
 
-hipError_t launch_bwd_states(int d_k, int d_v, const FwdParams& fwd, const FwdParams& adj,
-                             hipStream_t stream, hipEvent_t const* ev) {
-  if (d_k == 64 && d_v == 64) return launch_bwd_states_variant<64, 64>(fwd, adj, stream, ev);
+hipError_t launch_bwd_states(int d_k, int d_v, const FwdParams& p, hipStream_t stream,
+                             hipEvent_t const* ev) {
+  if (d_k == 64 && d_v == 64) return launch_bwd_states_variant<64, 64>(p, stream, ev);
   return hipErrorInvalidValue;
 }
 
