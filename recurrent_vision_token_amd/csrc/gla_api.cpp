@@ -131,6 +131,18 @@ int output_slots(int dev, gla::Dtype dt, int d_k, int d_v, bool gate_logits) {
   return n;
 }
 
+// CU count per device, read once.
+std::atomic<int> g_cus[kMaxDevices];
+int cu_count(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return 256;
+  int n = g_cus[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  g_cus[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 // Optional override of the chunks handled per output workgroup (0 = automatic).
 int span_override() {
   static std::once_flag once;
@@ -448,6 +460,18 @@ int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* log_a
     f.adj_state = w + fwd_floats;
     f.adj_gate = f.adj_state + (size_t)BH * (n_spans + 1) * map;
     f.adj_slots = n_spans + 1;
+    // the summaries kernel keeps two workgroups per CU (80 KB of LDS each);
+    // each streams enough spans for one round over the chip
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return GLA_ERR_HIP;
+    static const int spw_override = [] {
+      const char* e = std::getenv("GLA_BWD_SPANS_PER_WG");  // tuning override
+      const int v = e ? std::atoi(e) : 0;
+      return (v >= 1 && v <= 64) ? v : 0;
+    }();
+    const long long total_spans = BH * n_spans;
+    const long long wg_slots = 2LL * cu_count(dev);
+    f.spans_per_wg = spw_override ? spw_override : (int)((total_spans + wg_slots - 1) / wg_slots);
 
     gla::BwdParams pb{};
     pb.q = q;

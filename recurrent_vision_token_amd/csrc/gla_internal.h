@@ -35,6 +35,7 @@ struct FwdParams {
   float* adj_state;     // [BH][adj_slots][d_k][d_v]
   float* adj_gate;      // [BH][adj_slots][d_k]
   const float* adj_initial;  // the final-state gradient (scan start), may be null
+  int spans_per_wg;     // spans streamed by one workgroup of the summaries kernel
 };
 
 // Multiply-shift constants for dividing t < 2^31 by d >= 1:

@@ -1251,14 +1251,20 @@ __global__ __launch_bounds__(kThreads) void span_summary_f16_kernel(FwdParams p)
   store_summary<DK, DV>(p.span_state, p.span_gate, bh, p.n_spans, span, wave, n16, g, st, gdec);
 }
 
-// The backward pass's two summaries of a span in one workgroup: the forward
-// one (k, v; the state entering each span) and the adjoint one (q and the
-// output gradient d_out; the state gradient entering each span from its
-// right), sharing the log-alpha tile.  Span s's adjoint summary goes to slot
-// adj_slots - 2 - s, so that the adjoint scan runs from the end of the
-// sequence to its start; span 0 also writes the neutral summary (gate 1,
-// state 0) into the last slot, whose entry state is then the gradient of the
-// state before the first step.  float16, no fused gate activation.
+// The backward pass's two summaries of a span: the forward one (k, v; the
+// state entering each span) and the adjoint one (q and the output gradient
+// d_out; the state gradient entering each span from its right), sharing the
+// log-alpha tile.  Span s's adjoint summary goes to slot adj_slots - 2 - s,
+// so that the adjoint scan runs from the end of the sequence to its start;
+// span 0 also writes the neutral summary (gate 1, state 0) into the last
+// slot, whose entry state is then the gradient of the state before the first
+// step.  float16, no fused gate activation.
+//
+// A workgroup takes spans_per_wg consecutive spans (of the flattened
+// (batch*head, span) order) and streams their chunks through two tile
+// buffers, so that the loads of one chunk overlap the folds of the previous
+// one; a span's summaries are stored when its first chunk (folded last) is
+// done.
 template <int DK, int DV>
 __global__ __launch_bounds__(kThreads) void bwd_state_summaries_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(16))) f16 k0[kChunk * DK], la0[kChunk * DK], v0[kChunk * DV];
@@ -1276,22 +1282,39 @@ __global__ __launch_bounds__(kThreads) void bwd_state_summaries_kernel(FwdParams
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n16 = lane & 15, g = lane >> 4;
 
-  const int bh = blockIdx.x / p.n_spans;
-  const int span = blockIdx.x - bh * p.n_spans;
-  const int b = bh / p.heads;
-  const GridMap gm = grid_map(p, b);
-  const SeqBufs sb = seq_bufs<DK, DV>(p, bh);
-  const rsrc_t rdo = seq_rsrc(static_cast<const f16*>(p.dout) + (size_t)bh * p.T * DV,
-                              (uint32_t)p.T * RBV);
-  const int c_begin = span * p.span_chunks;
-  const int c_end = min(c_begin + p.span_chunks, p.n_chunks);
+  const int sc = p.span_chunks;
+  const long long total = (long long)p.B * p.heads * p.n_spans;
+  const long long s_begin = (long long)blockIdx.x * p.spans_per_wg;
+  const long long s_end = s_begin + p.spans_per_wg < total ? s_begin + p.spans_per_wg : total;
+  const int n_items = (int)(s_end - s_begin) * sc;
 
-  auto issue = [&](const SumTile<DK, DV>& f, const SumTile<DK, DV>& a, int c) {
-    const int t0 = c * kChunk;
-    const int valid = c >= c_begin ? min(kChunk, p.T - t0) : 0;
+  // item i: chunk sc - 1 - i % sc of span s_begin + i / sc (chunks of a span
+  // last to first); an item past the end or past its sequence is empty
+  struct Item {
+    int bh, span, c;
+    bool live;
+  };
+  auto item = [&](int i) {
+    Item it;
+    const long long gs = s_begin + i / sc;
+    it.bh = (int)(gs / p.n_spans);
+    it.span = (int)(gs - (long long)it.bh * p.n_spans);
+    it.c = it.span * sc + (sc - 1 - i % sc);
+    it.live = i < n_items && it.c < p.n_chunks;
+    return it;
+  };
+  auto issue = [&](const SumTile<DK, DV>& f, const SumTile<DK, DV>& a, int i) {
+    const Item it = item(i < n_items ? i : 0);
+    const bool live = i < n_items && it.live;
+    const GridMap gm = grid_map(p, it.bh / p.heads);
+    const SeqBufs sb = seq_bufs<DK, DV>(p, it.bh);
+    const rsrc_t rdo = seq_rsrc(static_cast<const f16*>(p.dout) + (size_t)it.bh * p.T * DV,
+                                (uint32_t)p.T * RBV);
+    const int t0 = it.c * kChunk;
+    const int valid = live ? min(kChunk, p.T - t0) : 0;
 #pragma unroll
-    for (int i = 0; i < NBK; ++i) {
-      const int blk = wave * NBK + i;
+    for (int j = 0; j < NBK; ++j) {
+      const int blk = wave * NBK + j;
       const uint32_t off = dma_offset<RBK>(blk, t0, valid, gm);
       dma16(sb.k, f.k + blk * 512, off);
       dma16(sb.la, f.la + blk * 512, off);
@@ -1304,51 +1327,66 @@ __global__ __launch_bounds__(kThreads) void bwd_state_summaries_kernel(FwdParams
   const f16x4 m_upper = tri_operand<false>(n16, g), m_lower = tri_operand<true>(n16, g);
   const f16x4 m_ones = f16x4{(f16)1.f, (f16)1.f, (f16)1.f, (f16)1.f};
   f32x4 st[NDB][NCB], gdec[NDB], sa[NDB][NCB], gadj[NDB];
-#pragma unroll
-  for (int d = 0; d < NDB; ++d) {
-    gdec[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-    gadj[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      st[d][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      sa[d][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-  }
-  auto fold = [&](const SumTile<DK, DV>& f, const SumTile<DK, DV>& a, int c) {
-    const int valid = min(kChunk, p.T - c * kChunk);
-    fold_chunk<DK, DV, false, false>(f, valid, 1.f, m_upper, m_ones, wave, st, gdec);
-    fold_chunk<DK, DV, false, true>(a, valid, 1.f, m_lower, m_ones, wave, sa, gadj);
-  };
-
-  issue(fw0, ad0, c_end - 1);
-  issue(fw1, ad1, c_end - 2);
-  for (int c = c_end - 1; c >= c_begin; c -= 2) {
-    wait_barrier<vmcnt_imm(NDMA)>();  // every wave's part of slot 0 has landed
-    fold(fw0, ad0, c);
-    wait_barrier<kLgkmZero>();        // every wave's reads of slot 0 are done
-    issue(fw0, ad0, c - 2);
-    wait_barrier<vmcnt_imm(NDMA)>();
-    if (c - 1 >= c_begin) fold(fw1, ad1, c - 1);
-    wait_barrier<kLgkmZero>();
-    issue(fw1, ad1, c - 3);
-  }
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  store_summary<DK, DV>(p.span_state, p.span_gate, bh, p.n_spans, span, wave, n16, g, st, gdec);
-  const size_t slots = p.adj_slots;
-  store_summary<DK, DV>(p.adj_state, p.adj_gate, bh, slots, slots - 2 - span, wave, n16, g, sa,
-                        gadj);
-  if (span == 0) {
-    float* last = p.adj_state + ((size_t)bh * slots + slots - 1) * DK * DV;
+  auto reset = [&]() {
 #pragma unroll
     for (int d = 0; d < NDB; ++d) {
-      const int dim = 16 * (wave + 4 * d) + n16;
+      gdec[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+      gadj[d] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
-        *reinterpret_cast<f32x4*>(last + dim * DV + 16 * cb + 4 * g) = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (g == 0) p.adj_gate[((size_t)bh * slots + slots - 1) * DK + dim] = 1.f;
+      for (int cb = 0; cb < NCB; ++cb) {
+        st[d][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        sa[d][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
     }
+  };
+  reset();
+  const size_t slots = p.adj_slots;
+  // fold item i from the given buffers; after a span's first chunk, store
+  // its summaries and start the next span from zero
+  auto step = [&](const SumTile<DK, DV>& f, const SumTile<DK, DV>& a, int i) {
+    const Item it = item(i);
+    if (it.live) {
+      const int valid = min(kChunk, p.T - it.c * kChunk);
+      fold_chunk<DK, DV, false, false>(f, valid, 1.f, m_upper, m_ones, wave, st, gdec);
+      fold_chunk<DK, DV, false, true>(a, valid, 1.f, m_lower, m_ones, wave, sa, gadj);
+    }
+    if (i % sc == sc - 1) {
+      store_summary<DK, DV>(p.span_state, p.span_gate, it.bh, p.n_spans, it.span, wave, n16, g,
+                            st, gdec);
+      store_summary<DK, DV>(p.adj_state, p.adj_gate, it.bh, slots, slots - 2 - it.span, wave, n16,
+                            g, sa, gadj);
+      if (it.span == 0) {
+        float* last = p.adj_state + ((size_t)it.bh * slots + slots - 1) * DK * DV;
+#pragma unroll
+        for (int d = 0; d < NDB; ++d) {
+          const int dim = 16 * (wave + 4 * d) + n16;
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+            *reinterpret_cast<f32x4*>(last + dim * DV + 16 * cb + 4 * g) =
+                f32x4{0.f, 0.f, 0.f, 0.f};
+          if (g == 0) p.adj_gate[((size_t)it.bh * slots + slots - 1) * DK + dim] = 1.f;
+        }
+      }
+      reset();
+    }
+  };
+
+  issue(fw0, ad0, 0);
+  issue(fw1, ad1, 1);
+  for (int i = 0; i < n_items; i += 2) {
+    wait_barrier<vmcnt_imm(NDMA)>();  // every wave's part of buffer 0 has landed
+    step(fw0, ad0, i);
+    wait_barrier<kLgkmZero>();        // every wave's reads of buffer 0 are done
+    issue(fw0, ad0, i + 2);
+    wait_barrier<vmcnt_imm(NDMA)>();
+    if (i + 1 < n_items) step(fw1, ad1, i + 1);
+    wait_barrier<kLgkmZero>();
+    issue(fw1, ad1, i + 3);
   }
+  // the trailing loads are zero fills: let them land before the workgroup's
+  // LDS can be handed on
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
 
 // Kernel choice per element type: float16 runs the MFMA-layout kernels,
@@ -1487,7 +1525,9 @@ hipError_t launch_bwd_states_variant(const FwdParams& p, hipStream_t stream, hip
   // both summaries of every span, then both scans: the forward entry state
   // of every span, the adjoint state entering every span from its right, and
   // the gradient of the state before the first step in the adjoint's last slot
-  if ((e = launch_marked(bwd_state_summaries_kernel<DK, DV>, dim3(BH * p.n_spans), stream, p,
+  const long long total = (long long)BH * p.n_spans;
+  const dim3 sum_grid((unsigned)((total + p.spans_per_wg - 1) / p.spans_per_wg));
+  if ((e = launch_marked(bwd_state_summaries_kernel<DK, DV>, sum_grid, stream, p,
                          ev ? ev[0] : nullptr, ev ? ev[1] : nullptr)) != hipSuccess)
     return e;
   return launch_marked(bwd_state_scans_kernel<DK, DV>, dim3(BH, 2 * DK * DV / kScanElems), stream,
