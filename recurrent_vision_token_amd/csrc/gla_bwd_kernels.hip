@@ -302,58 +302,76 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
   }
   __syncthreads();  // the staging area becomes sEc
 
-  // Thread (key dim i, sub-block J) walks its 16 tokens: alpha_t = e^{la_t},
-  // e^{c_t} as a running product from the sub-block start and the decay to
-  // the sub-block end as a running product from its end; one exponential per
-  // token.
+  // Thread (key dims 2 i2, 2 i2 + 1; tokens 8h .. 8h + 7 of sub-block J, its
+  // wave) walks its tokens: alpha_t = e^{la_t}, e^{c_t} as a running product
+  // from the sub-block start and the decay to the sub-block end as a running
+  // product from its end, one exponential per token; the two halves of a
+  // sub-block (lanes l and l ^ 32) hand each other their decay products.
   {
-    const int i = tid & 63, J = tid >> 6;
-    float al[16];
-    float tot = 0.f, ec = 1.f;
+    const int i2 = tid & 31, h = (tid >> 5) & 1, J = tid >> 6;
+    const int i = 2 * i2;
+    float al0[8], al1[8];
+    float tot0 = 0.f, tot1 = 0.f, p0 = 1.f, p1 = 1.f;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int t = 16 * J + u;
+    for (int u = 0; u < 8; ++u) {
+      const f16x2 la2 = *reinterpret_cast<const f16x2*>(&tla[swz<RB>(16 * J + 8 * h + u, i)]);
+      const float l0 = (float)la2[0], l1 = (float)la2[1];
+      al0[u] = ex(l0);
+      al1[u] = ex(l1);
+      tot0 += l0;
+      tot1 += l1;
+      p0 *= al0[u];
+      p1 *= al1[u];
+    }
+    const float o0 = __shfl_xor(p0, 32), o1 = __shfl_xor(p1, 32);
+    const float ot0 = __shfl_xor(tot0, 32), ot1 = __shfl_xor(tot1, 32);
+    float ec0 = h ? o0 : 1.f, ec1 = h ? o1 : 1.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int t = 16 * J + 8 * h + u;
       const int e = swz<RB>(t, i);
-      const float la = (float)tla[e];
-      al[u] = ex(la);
-      tot += la;
-      ec *= al[u];
-      sEc[t * ES + i] = ec;
-      tqs[e] = (f16)((float)tq[e] * ec);
+      ec0 *= al0[u];
+      ec1 *= al1[u];
+      *reinterpret_cast<f32x2*>(&sEc[t * ES + i]) = f32x2{ec0, ec1};
+      const f16x2 q2 = *reinterpret_cast<const f16x2*>(&tq[e]);
+      *reinterpret_cast<f16x2*>(&tqs[e]) = f16x2{(f16)((float)q2[0] * ec0), (f16)((float)q2[1] * ec1)};
     }
-    float sfx = 1.f, kf[16];
+    float sfx0 = h ? 1.f : o0, sfx1 = h ? 1.f : o1, kf0[8], kf1[8];
 #pragma unroll
-    for (int u = 15; u >= 0; --u) {
-      const int e = swz<RB>(16 * J + u, i);
-      kf[u] = (float)tk[e] * sfx;   // k decayed to the sub-block end
-      tkd[e] = (f16)kf[u];
-      sfx *= al[u];
+    for (int u = 7; u >= 0; --u) {
+      const int e = swz<RB>(16 * J + 8 * h + u, i);
+      const f16x2 k2 = *reinterpret_cast<const f16x2*>(&tk[e]);
+      kf0[u] = (float)k2[0] * sfx0;   // k decayed to the sub-block end
+      kf1[u] = (float)k2[1] * sfx1;
+      *reinterpret_cast<f16x2*>(&tkd[e]) = f16x2{(f16)kf0[u], (f16)kf1[u]};
+      sfx0 *= al0[u];
+      sfx1 *= al1[u];
     }
-    sTot[J][i] = tot;
+    if (h == 0) *reinterpret_cast<f32x2*>(&sTot[J][i]) = f32x2{tot0 + ot0, tot1 + ot1};
     __syncthreads();
-    if (J == 0) {
+    if (tid < DK) {
       float acc = 0.f;
-      sBst[0][i] = 0.f;
+      sBst[0][tid] = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        acc += sTot[j][i];
-        sBst[j + 1][i] = acc;
+        acc += sTot[j][tid];
+        sBst[j + 1][tid] = acc;
       }
     }
     __syncthreads();
     // k decayed to the chunk end = k decayed to its sub-block end times the
     // decay of the later sub-blocks (log-alpha's tile is free now)
-    const float to_end = ex(sBst[4][i] - sBst[J + 1][i]);
+    const float te0 = ex(sBst[4][i] - sBst[J + 1][i]), te1 = ex(sBst[4][i + 1] - sBst[J + 1][i + 1]);
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int t = 16 * J + u;
-      const int e = swz<RB>(t, i);
-      tke[e] = (f16)(kf[u] * to_end);
+    for (int u = 0; u < 8; ++u) {
+      const int e = swz<RB>(16 * J + 8 * h + u, i);
+      *reinterpret_cast<f16x2*>(&tke[e]) = f16x2{(f16)(kf0[u] * te0), (f16)(kf1[u] * te1)};
     }
-    // factors between sub-block boundaries
-    for (int ab = J; ab < 25; ab += 4) {
+    // factors between sub-block boundaries, thread (key dim, quarter)
+    const int d = tid & 63;
+    for (int ab = tid >> 6; ab < 25; ab += 4) {
       const int a = ab / 5, bb = ab % 5;
-      sF[a][bb][i] = (f16)ex(sBst[a][i] - sBst[bb][i]);
+      sF[a][bb][d] = (f16)ex(sBst[a][d] - sBst[bb][d]);
     }
   }
   __syncthreads();
