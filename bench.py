@@ -169,9 +169,11 @@ class Runner:
                 raise RuntimeError("gla_chunk_fwd failed: %d" % rc)
 
 
-def time_workload(wl, torch, steps, warmup, ext=False):
+def time_workload(wl, torch, steps, warmup, ext=False, extras=False):
     """Timed loop (no instrumentation), then an event-instrumented pass of the
-    same length for the per-kernel durations."""
+    same length for the per-kernel durations.  With extras, also the spread of
+    per-step times (an event pair around every step of a further pass) and a
+    warm figure (every call re-reads one resident input set)."""
     r = Runner(wl, torch, ext=ext)
     ncall = len(wl.calls)
     log("[bench] %s: %d device input sets (%.0f MB), %d calls/step" %
@@ -208,6 +210,34 @@ def time_workload(wl, torch, steps, warmup, ext=False):
             k_ms["chunk_output"].append(e[4].elapsed_time(e[5]))
             k_ms["call"].append(e[0].elapsed_time(e[5]))
     mean = {k: sum(v) / len(v) for k, v in k_ms.items()}
+    if extras:
+        # per-step spread: plain event records between steps (no per-kernel hook)
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        for e in marks:
+            e.record(stream)
+        torch.cuda.synchronize()
+        marks[0].record(stream)
+        for s in range(steps):
+            r.step()
+            marks[s + 1].record(stream)
+        torch.cuda.synchronize()
+        per = sorted(marks[s].elapsed_time(marks[s + 1]) for s in range(steps))
+        pick = lambda f: per[min(len(per) - 1, int(f * (len(per) - 1) + 0.5))]
+        mean["step_ms"] = {"median": pick(0.5), "p10": pick(0.1), "p90": pick(0.9)}
+        # warm: the first set's inputs for every call of the step
+        args = [r.args[0][:4] + a[4:] for a in r.args[:ncall]]
+        for _ in range(warmup):
+            for a in args:
+                r.fn(*a)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            for a in args:
+                rc = r.fn(*a)
+                if rc != 0:
+                    raise RuntimeError("gla_chunk_fwd failed: %d" % rc)
+        torch.cuda.synchronize()
+        mean["warm_ms_step"] = (time.perf_counter() - t0) * 1e3 / steps
     return r, ms_step, mean
 
 
@@ -430,7 +460,8 @@ def bwd_cpu_baseline(wl, host):
 def bwd_summary(wl, ms_step, k_ms, cpu):
     nb = bwd_bytes(wl)
     ach = nb["chunk_bwd"] / (k_ms["chunk_bwd"] * 1e-3) / 1e9
-    path = nb["call"] / (k_ms["call"] * 1e-3) / 1e9
+    wall_call_ms = ms_step / len(wl.calls)
+    path = nb["call"] / (wall_call_ms * 1e-3) / 1e9
     tokens = len(wl.calls) * wl.B * wl.T
     return {
         "entry": "gla_chunk_bwd: dq, dk, dv, dlog_alpha, d_initial_state (fp16, fp32 states)",
@@ -443,7 +474,8 @@ def bwd_summary(wl, ms_step, k_ms, cpu):
                      "traffic": traffic_from_profiles(wl.name, "chunk_bwd"),
                      "kernel": "chunk_bwd", "algorithmic_bytes_per_launch": nb["chunk_bwd"],
                      "avg_launch_us": round(k_ms["chunk_bwd"] * 1e3, 2)},
-        "path": {"gpu_us_per_call": round(k_ms["call"] * 1e3, 2),
+        "path": {"wall_us_per_call": round(wall_call_ms * 1e3, 2),
+                 "event_us_per_call": round(k_ms["call"] * 1e3, 2),
                  "algorithmic_bytes_per_call": nb["call"],
                  "achieved_GBps": round(path, 1), "hbm_frac": round(path / HBM_PEAK_GBPS, 4),
                  "kernel_us": {k: round(v * 1e3, 2) for k, v in k_ms.items() if k != "call"}},
@@ -542,7 +574,7 @@ def saga_cpu_baseline(swl, host):
 def saga_summary(swl, ms_call, k_ms, cpu):
     total, acc = saga_bytes(swl)
     ach = acc / (k_ms["saga_kv_partial"] * 1e-3) / 1e9
-    path = total / (k_ms["call"] * 1e-3) / 1e9
+    path = total / (ms_call * 1e-3) / 1e9
     return {
         "entry": "gla_saga_fwd: O = Q [(K*A)^T (V*B)], non-causal",
         "workload": "%s: B=%d, heads=%d, N=%d tokens, d_k=%d, d_v=%d, fp16, q/k/v ~ N(0,1)/8, "
@@ -558,7 +590,8 @@ def saga_summary(swl, ms_call, k_ms, cpu):
                      if swl.name == SAGA_WORKLOAD else None,
                      "kernel": "saga_kv_partial", "algorithmic_bytes_per_launch": acc,
                      "avg_launch_us": round(k_ms["saga_kv_partial"] * 1e3, 2)},
-        "path": {"gpu_us_per_call": round(k_ms["call"] * 1e3, 2), "algorithmic_bytes_per_call": total,
+        "path": {"wall_us_per_call": round(ms_call * 1e3, 2),
+                 "event_us_per_call": round(k_ms["call"] * 1e3, 2), "algorithmic_bytes_per_call": total,
                  "achieved_GBps": round(path, 1), "hbm_frac": round(path / HBM_PEAK_GBPS, 4),
                  "kernel_us": {k: round(v * 1e3, 2) for k, v in k_ms.items() if k != "call"}},
         "cpu_baseline": cpu,
@@ -586,15 +619,18 @@ def traffic_from_profiles(wl_name, kernel):
 
 
 def cpu_baseline(wl, host, budget_s=12.0):
-    """The oracle as it stands, on a bounded sample of the same workload."""
+    """The oracle as it stands, on a bounded sample of the same workload.
+    Also returns its outputs, [(call index, out, final_state)]."""
     from oracle import gla_forward
     t0 = time.perf_counter()
     c0 = time.process_time()
     tokens = 0
     done = 0
-    for seed, d in wl.calls:
+    refs = []
+    for i, (seed, d) in enumerate(wl.calls):
         q, k, v, la = host[seed]
-        gla_forward(q, k, v, la, d)
+        o, f = gla_forward(q, k, v, la, d)
+        refs.append((i, o, f))
         tokens += wl.B * wl.T
         done += 1
         if time.perf_counter() - t0 > budget_s:
@@ -602,9 +638,101 @@ def cpu_baseline(wl, host, budget_s=12.0):
     wall = time.perf_counter() - t0
     cpu = time.process_time() - c0
     cores = max(1, int(round(cpu / wall)))
-    return {"value": tokens / wall, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": "%d of the %d calls of one step (%s, full size, numpy float64 token loop), "
-                      "%.1f s wall" % (done, len(wl.calls), wl.name, wall)}
+    return ({"value": tokens / wall, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+             "sample": "%d of the %d calls of one step (%s, full size, numpy float64 token loop), "
+                       "%.1f s wall" % (done, len(wl.calls), wl.name, wall)}, refs)
+
+
+def _pool_ready(_):
+    time.sleep(0.3)  # hold the worker, so that every worker of the pool starts now
+    return os.getpid()
+
+
+def _oracle_slice(args):
+    from oracle import gla_forward
+    q, k, v, la, d = args
+    return gla_forward(q, k, v, la, d)
+
+
+def start_oracle_pool(max_workers=16):
+    """Worker processes for the all-cores oracle figure, started (fresh
+    interpreters, spawn) before this process touches the GPU; at most 16, the
+    CPU share of one GPU."""
+    import concurrent.futures
+    import multiprocessing
+    n = max(1, min(max_workers, len(os.sched_getaffinity(0))))
+    pool = concurrent.futures.ProcessPoolExecutor(
+        max_workers=n, mp_context=multiprocessing.get_context("spawn"))
+    pids = set(pool.map(_pool_ready, range(n)))
+    return pool, len(pids)
+
+
+def cpu_baseline_pool(wl, host, pool, workers):
+    """The same oracle over independent (batch, head) sequences in a process
+    pool: the fair all-cores CPU figure (one step of the workload)."""
+    t0 = time.perf_counter()
+    tasks = []
+    for seed, d in wl.calls:
+        q, k, v, la = host[seed]
+        for b in range(wl.B):
+            for h in range(wl.heads):
+                sl = (slice(b, b + 1), slice(h, h + 1))
+                tasks.append((q[sl], k[sl], v[sl], la[sl], d))
+    for _ in pool.map(_oracle_slice, tasks):
+        pass
+    wall = time.perf_counter() - t0
+    return {"value": len(wl.calls) * wl.B * wl.T / wall, "unit": "tokens/s", "cores": workers,
+            "kind": "oracle",
+            "sample": "one step (%d calls) of %s, %d (batch, head) sequences per call spread over "
+                      "%d worker processes, %.1f s wall" % (len(wl.calls), wl.name, wl.B * wl.heads,
+                                                            workers, wall)}
+
+
+def gpu_parity(runner, refs, torch):
+    """Errors of the GPU outputs against the oracle's, for the calls the CPU
+    baseline computed: each call re-run once on its own input set."""
+    import numpy as np
+    worst = {"out": {"rel_fro": 0.0, "max_rel": 0.0, "cosine_min": 1.0},
+             "final_state": {"rel_fro": 0.0, "max_rel": 0.0, "cosine_min": 1.0}}
+    for i, ro, rf in refs:
+        rc = runner.fn(*runner.args[i])
+        if rc != 0:
+            raise RuntimeError("gla_chunk_fwd failed: %d" % rc)
+        torch.cuda.synchronize()
+        q, k, v, la, out, fs = runner.sets[i][:6]
+        for name, got, ref in (("out", out, ro), ("final_state", fs, rf)):
+            g = got.float().cpu().numpy().astype(np.float64).ravel()
+            r = ref.ravel()
+            w = worst[name]
+            w["rel_fro"] = max(w["rel_fro"], float(np.linalg.norm(g - r) / np.linalg.norm(r)))
+            w["max_rel"] = max(w["max_rel"], float(np.abs(g - r).max() / np.abs(r).max()))
+            w["cosine_min"] = min(w["cosine_min"],
+                                  float(g @ r / (np.linalg.norm(g) * np.linalg.norm(r))))
+    for w in worst.values():
+        for k in w:
+            w[k] = float("%.4g" % w[k])
+    return dict(worst, calls_checked=len(refs),
+                bar="rel_fro <= 5e-3 and max_rel <= 2e-2 (fp16); the pages report cosine >= 0.9989")
+
+
+def copy_bandwidth(torch, mb=1024, reps=20):
+    """Device-to-device copy rate (read + write bytes per second): the
+    practical streaming ceiling of this machine."""
+    n = (mb << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    return 2 * n * 4 / (ms * 1e-3) / 1e9
 
 
 def describe(wl):
@@ -628,8 +756,9 @@ def summarize(wl, ms_step, mean, ext=False):
     present = [k for k in kb if mean[k] > 0]
     dom = max(present, key=lambda k: mean[k])
     ach = kb[dom] / (mean[dom] * 1e-3) / 1e9
-    path_gbps = alg["bytes"] / (mean["call"] * 1e-3) / 1e9
-    return {
+    wall_call_ms = ms_step / ncall
+    path_gbps = alg["bytes"] / (wall_call_ms * 1e-3) / 1e9
+    out = {
         "tokens_per_step": tokens_step,
         "value": tokens_step / (ms_step * 1e-3),
         "dominant": dom,
@@ -637,14 +766,25 @@ def summarize(wl, ms_step, mean, ext=False):
                      "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": traffic_from_profiles(wl.name, dom),
                      "kernel": dom, "algorithmic_bytes_per_launch": kb[dom],
                      "avg_launch_us": round(mean[dom] * 1e3, 2)},
-        "path": {"gpu_us_per_call": round(mean["call"] * 1e3, 2),
+        # whole call at the timed loop's wall-clock rate (the instrumented pass
+        # spaces its launches out: event_us_per_call is first summary start to
+        # last output stop there)
+        "path": {"wall_us_per_call": round(wall_call_ms * 1e3, 2),
+                 "event_us_per_call": round(mean["call"] * 1e3, 2),
                  "algorithmic_bytes_per_call": alg["bytes"],
                  "achieved_GBps": round(path_gbps, 1),
                  "hbm_frac": round(path_gbps / HBM_PEAK_GBPS, 4),
-                 "mfma_frac": round(alg["flops"] / (mean["call"] * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+                 "mfma_frac": round(alg["flops"] / (wall_call_ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
                  "kernel_us": {k: round(mean[k] * 1e3, 2) for k in ("span_summary", "span_scan", "chunk_output")},
                  "n_spans": spans},
     }
+    if "step_ms" in mean:
+        out["step_ms"] = {k: round(v, 4) for k, v in mean["step_ms"].items()}
+    if "warm_ms_step" in mean:
+        w = mean["warm_ms_step"]
+        out["warm"] = {"ms_per_step": round(w, 4), "value": tokens_step / (w * 1e-3),
+                       "note": "every call re-reads one resident input set (Infinity Cache hits)"}
+    return out
 
 
 def counters_to_traffic(fetch_dir, write_dir, copy_mb, workload, only=()):
@@ -718,6 +858,10 @@ def main():
                     help="skip the extended entry point (fused gate + initial state) line")
     ap.add_argument("--swiglu", default=SWIGLU_WORKLOAD,
                     help="Spatial SwiGLU workload to time beside the attention path ('' to skip)")
+    ap.add_argument("--no-img768", dest="img768", action="store_false",
+                    help="skip the 768x768-image line (12 calls, one per block)")
+    ap.add_argument("--no-sweep", dest="sweep", action="store_false",
+                    help="skip the time-vs-token-count sweep")
     ap.add_argument("--no-bwd", action="store_true",
                     help="skip the backward pass line (gla_chunk_bwd on the main workload)")
     ap.add_argument("--saga", default=SAGA_WORKLOAD,
@@ -745,9 +889,13 @@ def main():
     if int(os.environ.get("RANK", "0")) != 0:
         return
 
+    pool = None
+    if not args.no_cpu_baseline:
+        pool, pool_workers = start_oracle_pool()   # before any GPU call
+
     import torch
     from recurrent_vision_token_amd import load
-    from recurrent_vision_token_amd.workloads import WORKLOADS
+    from recurrent_vision_token_amd.workloads import WORKLOADS, Workload
 
     load()  # fails loudly if the HIP library is not built
     if not torch.cuda.is_available():
@@ -763,10 +911,10 @@ def main():
         del src, dst
 
     wl = WORKLOADS[args.workload]
-    runner, ms_step, mean = time_workload(wl, torch, args.steps, args.warmup)
+    runner, ms_step, mean = time_workload(wl, torch, args.steps, args.warmup, extras=True)
     main_sum = summarize(wl, ms_step, mean)
-    log("[bench] %s: %.3f ms/step, %.3e tokens/s, GPU %.2f us/call, kernels %s" %
-        (wl.name, ms_step, main_sum["value"], main_sum["path"]["gpu_us_per_call"],
+    log("[bench] %s: %.3f ms/step, %.3e tokens/s, %.2f us/call, kernels %s" %
+        (wl.name, ms_step, main_sum["value"], main_sum["path"]["wall_us_per_call"],
          main_sum["path"]["kernel_us"]))
 
     secondary = None
@@ -776,8 +924,36 @@ def main():
         s2 = summarize(wl2, ms2, mean2)
         secondary = {"workload": describe(wl2), "value": s2["value"], "unit": "tokens/s",
                      "ms_per_step": round(ms2, 4), "roofline": s2["roofline"], "path": s2["path"]}
-        log("[bench] %s: %.3f ms/step, %.3e tokens/s, GPU %.2f us/call" %
-            (wl2.name, ms2, s2["value"], s2["path"]["gpu_us_per_call"]))
+        log("[bench] %s: %.3f ms/step, %.3e tokens/s, %.2f us/call" %
+            (wl2.name, ms2, s2["value"], s2["path"]["wall_us_per_call"]))
+
+    img = None
+    if args.img768:
+        wl4 = WORKLOADS["img768"]
+        _, ms4, mean4 = time_workload(wl4, torch, max(20, args.steps // 2), max(5, args.warmup))
+        s4 = summarize(wl4, ms4, mean4)
+        img = {"workload": describe(wl4), "gla_us_per_image": round(ms4 * 1e3, 2),
+               "value": s4["value"], "unit": "tokens/s", "roofline": s4["roofline"],
+               "path": s4["path"]}
+        log("[bench] %s: %.1f us of attention per image (12 calls), %.3e tokens/s" %
+            (wl4.name, ms4 * 1e3, s4["value"]))
+
+    sweep = None
+    if args.sweep:
+        sweep = []
+        for side in (40, 48, 64, 80, 96, 128):
+            wls = Workload("grid%d" % side, 1, 12, side, side, 64, 64, 64, "fp16", 1.0,
+                           [1, 1, 1, 1], [0, 1, 2, 3])
+            _, msw, meanw = time_workload(wls, torch, 50, 10)
+            sw = summarize(wls, msw, meanw)
+            sweep.append({"grid": "%dx%d" % (side, side), "tokens": side * side,
+                          "us_per_call": round(msw * 1e3 / 4, 2), "tokens_per_s": sw["value"],
+                          "path_hbm_frac": sw["path"]["hbm_frac"]})
+        log("[bench] time vs tokens (B=1, 12 heads, 4 directions): %s" %
+            ", ".join("%s %.1f us" % (x["grid"], x["us_per_call"]) for x in sweep))
+
+    copy_gbps = copy_bandwidth(torch)
+    log("[bench] device copy: %.0f GB/s (read + write)" % copy_gbps)
 
     ext = None
     if not args.no_ext and wl.dtype == "fp16":
@@ -821,10 +997,17 @@ def main():
             (gwl.name, ms_g * 1e3, saga["path"]["kernel_us"], saga["value"]))
         del grun
 
-    cpu = None
+    cpu = cpu_all = parity = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, runner.host)
+        cpu, refs = cpu_baseline(wl, runner.host)
         log("[bench] cpu oracle: %.3e tokens/s on %d core(s)" % (cpu["value"], cpu["cores"]))
+        parity = gpu_parity(runner, refs, torch)
+        log("[bench] parity vs the oracle: %s" % parity)
+        cpu_all = cpu_baseline_pool(wl, runner.host, pool, pool_workers)
+        log("[bench] cpu oracle, all cores: %.3e tokens/s on %d processes" %
+            (cpu_all["value"], cpu_all["cores"]))
+        pool.shutdown()
+    main_sum["roofline"]["frac_of_device_copy"] = round(main_sum["roofline"]["achieved"] / copy_gbps, 4)
 
     line = {
         "metric": METRIC,
@@ -844,7 +1027,14 @@ def main():
         "roofline": main_sum["roofline"],
         "path": main_sum["path"],
         "cpu_baseline": cpu,
+        "cpu_baseline_all_cores": cpu_all,
+        "parity_vs_oracle": parity,
+        "device_copy_GBps": round(copy_gbps, 1),
+        "step_ms": main_sum.get("step_ms"),
+        "warm": main_sum.get("warm"),
         "secondary": secondary,
+        "img768": img,
+        "time_vs_tokens": sweep,
         "fused_gate_initial_state": ext,
         "backward": bwd,
         "spatial_swiglu": swiglu,

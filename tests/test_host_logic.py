@@ -72,3 +72,28 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], cwd=root,
                        stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_all_cores_oracle_pool_matches_the_oracle():
+    # the bench's all-cores CPU figure runs the oracle per (batch, head) slice in
+    # spawned worker processes; the slices must reproduce the whole-tensor call
+    import numpy as np
+    import bench
+    from oracle import gla_forward
+    from recurrent_vision_token_amd.workloads import Workload, make_inputs
+    wl = Workload("pool", 2, 3, 5, 7, 8, 4, 64, "fp32", 1.0, [0, 0], [1, 2])
+    host = {0: make_inputs(2, 3, 5, 7, 8, 4, "fp32", 1.0, seed=0)}
+    pool, workers = bench.start_oracle_pool(max_workers=2)
+    try:
+        line = bench.cpu_baseline_pool(wl, host, pool, workers)
+        q, k, v, la = host[0]
+        slices = [(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1],
+                   la[b:b + 1, h:h + 1], 2) for b in range(2) for h in range(3)]
+        got = list(pool.map(bench._oracle_slice, slices))
+    finally:
+        pool.shutdown()
+    ref_o, ref_f = gla_forward(q, k, v, la, 2)
+    for (b, h), (o, f) in zip([(b, h) for b in range(2) for h in range(3)], got):
+        np.testing.assert_array_equal(o[0, 0], ref_o[b, h])
+        np.testing.assert_array_equal(f[0, 0], ref_f[b, h])
+    assert line["kind"] == "oracle" and line["cores"] == workers and line["value"] > 0
