@@ -640,7 +640,9 @@ def cpu_baseline(wl, host, budget_s=12.0):
     cores = max(1, int(round(cpu / wall)))
     return ({"value": tokens / wall, "unit": "tokens/s", "cores": cores, "kind": "oracle",
              "sample": "%d of the %d calls of one step (%s, full size, numpy float64 token loop), "
-                       "%.1f s wall" % (done, len(wl.calls), wl.name, wall)}, refs)
+                       "%.1f s wall" % (done, len(wl.calls), wl.name, wall),
+             "host_cpus": {"os_cpu_count": os.cpu_count(),
+                           "sched_affinity": len(os.sched_getaffinity(0))}}, refs)
 
 
 def _pool_ready(_):

@@ -450,16 +450,6 @@ int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* log_a
     const size_t map = (size_t)d_k * d_v;
     const size_t fwd_floats = (size_t)BH * n_spans * (map + d_k);
     const size_t adj_floats = (size_t)BH * (n_spans + 1) * (map + d_k);
-    WsLease ws;
-    if (ws.acquire(st, (fwd_floats + adj_floats) * sizeof(float)) != hipSuccess) return GLA_ERR_HIP;
-    float* w = static_cast<float*>(ws.ptr());
-    f.span_state = w;
-    f.span_gate = w + (size_t)BH * n_spans * map;
-    f.dout = d_out;
-    f.adj_initial = d_final_state;
-    f.adj_state = w + fwd_floats;
-    f.adj_gate = f.adj_state + (size_t)BH * (n_spans + 1) * map;
-    f.adj_slots = n_spans + 1;
     // the summaries kernel keeps two workgroups per CU (80 KB of LDS each);
     // each streams enough spans for one round over the chip
     int dev = 0;
@@ -472,6 +462,16 @@ int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* log_a
     const long long total_spans = BH * n_spans;
     const long long wg_slots = 2LL * cu_count(dev);
     f.spans_per_wg = spw_override ? spw_override : (int)((total_spans + wg_slots - 1) / wg_slots);
+    WsLease ws;
+    if (ws.acquire(st, (fwd_floats + adj_floats) * sizeof(float)) != hipSuccess) return GLA_ERR_HIP;
+    float* w = static_cast<float*>(ws.ptr());
+    f.span_state = w;
+    f.span_gate = w + (size_t)BH * n_spans * map;
+    f.dout = d_out;
+    f.adj_initial = d_final_state;
+    f.adj_state = w + fwd_floats;
+    f.adj_gate = f.adj_state + (size_t)BH * (n_spans + 1) * map;
+    f.adj_slots = n_spans + 1;
 
     gla::BwdParams pb{};
     pb.q = q;
