@@ -253,8 +253,8 @@ int gla_spatial_swiglu(const void* gate, const void* value, int ld_in, const voi
  * of two per 16 value columns; out rounded to nearest even.
  * Supported: d_k, d_v in {64, 128}; one sequence's rows of a tensor below
  * 2 GiB.  out and kv may not overlap any input or each other.
- * Ownership and errors as gla_chunk_fwd (with a workspace of
- * B*heads*d_k*d_v*(1 + s) floats, s the accumulation spans per sequence, a
+ * Ownership and errors as gla_chunk_fwd (with a workspace of about
+ * B*heads*d_k*d_v*(s + 1/2) floats, s the accumulation spans per sequence, a
  * few workgroups per CU in all): GLA_ERR_NULL, GLA_ERR_SHAPE, GLA_ERR_UNSUPPORTED
  * (d_k / d_v), GLA_ERR_ALIGN, GLA_ERR_ALIAS.  With the measurement hook armed
  * the accumulation, reduction and output kernels record event pairs 0, 1, 2

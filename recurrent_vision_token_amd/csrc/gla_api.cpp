@@ -574,13 +574,18 @@ int gla_saga_fwd(const void* q, const void* k, const void* v, const void* alpha,
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     const size_t map = (size_t)d_k * d_v;
-    const size_t ws_floats = BH * map + BH * p.n_spans * map;   // transposed maps, partials
+    // the output kernel's float16 operands (half a map per sequence), their
+    // inverse scales (one per 16 value dims x 32 key dims), the span partials
+    const size_t amap_floats = BH * map / 2;
+    const size_t unscale_floats = (BH * (size_t)(d_v / 16) * (d_k / 32) + 3) / 4 * 4;
+    const size_t ws_floats = amap_floats + unscale_floats + BH * p.n_spans * map;
     WsLease ws;
     if (ws.acquire(st, ws_floats * sizeof(float)) != hipSuccess) return GLA_ERR_HIP;
     float* wsf = static_cast<float*>(ws.ptr());
     p.kv = kv;
-    p.kvt = wsf;
-    p.partial = wsf + BH * map;
+    p.amap = wsf;
+    p.unscale = wsf + amap_floats;
+    p.partial = wsf + amap_floats + unscale_floats;
     const hipEvent_t* ev = t_events_set ? t_events : nullptr;
     t_events_set = false;
     const hipError_t e = gla::launch_saga(p, st, ev);

@@ -127,7 +127,9 @@ struct SagaParams {
   const void* b;        // value-side gates [B][heads][N][d_v]
   void* out;            // [B][heads][N][d_v]
   float* kv;            // [B*heads][d_k][d_v] gated key-value maps, or null
-  float* kvt;           // [B*heads][d_v][d_k] the maps transposed (workspace)
+  void* amap;           // [B*heads][d_v/16][d_k/32][64] x 8 float16: the output kernel's
+                        // A operands, each scaled by a power of two (workspace)
+  float* unscale;       // [B*heads][d_v/16][d_k/32] the inverse scales (workspace)
   float* partial;       // [B*heads][n_spans][d_k][d_v] span partials (workspace)
   int B, heads, N, d_k, d_v;
   int n_chunks;         // ceil(N / saga_chunk_tokens()) accumulation steps

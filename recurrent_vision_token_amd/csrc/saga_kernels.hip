@@ -12,8 +12,10 @@
 //      steps) accumulates its span's (K*A)^T (V*B) on the matrix cores - the
 //      key-value accumulation of the attention path's chunk summaries, with
 //      the gates in place of the decay;
-//   2. saga_kv_reduce  : sums the span partials in a fixed order and writes
-//      the map, also transposed for kernel 3;
+//   2. saga_kv_reduce  : sums the span partials in a fixed order, writes the
+//      map, and writes kernel 3's MFMA A operands (the map transposed, scaled
+//      by a power of two per operand of 16 value dims x 32 key dims, float16)
+//      once per (batch*head), so that the output workgroups only load them;
 //   3. saga_out        : O^T = KV^T Q^T, 16 tokens by 16 value dims per MFMA,
 //      queries read straight from memory into the MFMA operand layout.
 // Chunk tiles move into LDS with LDS-writing buffer loads and are read back
@@ -32,7 +34,6 @@ namespace {
 constexpr int kThreads = 256;   // four wave64s
 constexpr int kStepTokens = 32; // tokens per accumulation step (tile rows)
 constexpr int kOutTokens = 256; // tokens per output workgroup
-constexpr int kSpanGroups = 4;  // span groups summed side by side in the reduction
 
 // Source offset of this lane's 16 bytes in block `blk` (1 KB) of a tile with
 // RB-byte rows holding tokens t0.., swizzled like the attention tiles; rows
@@ -168,26 +169,85 @@ __global__ __launch_bounds__(kThreads) void saga_kv_partial_kernel(SagaParams p)
 // for the output kernel.  A workgroup owns 256 map elements (64 columns of
 // 4); its four thread groups sum every fourth span, one load per span in
 // flight per thread, and the four sums are added in group order.
-template <int DK, int DV>
-__global__ __launch_bounds__(kThreads) void saga_kv_reduce_kernel(SagaParams p) {
-  __shared__ f32x4 part[kSpanGroups][64];
-  const int bh = blockIdx.x;
-  const int col = threadIdx.x & 63, grp = threadIdx.x >> 6;
-  const int e = (blockIdx.y * 64 + col) * 4;   // first of 4 consecutive map elements
-  const float* src = p.partial + (size_t)bh * p.n_spans * DK * DV + e;
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int s = grp; s < p.n_spans; s += kSpanGroups)
-    acc += *reinterpret_cast<const f32x4*>(src + (size_t)s * DK * DV);
-  part[grp][col] = acc;
+// MFMA m of the output kernel (16 value dims): its row r is value dim
+// 32 (m / 2) + 8 (r / 4) + 4 (m % 2) + r % 4, so that the output lanes store
+// 16 contiguous bytes (see saga_out_kernel).
+__device__ __forceinline__ int out_row_dim(int m, int r) {
+  return 32 * (m >> 1) + 8 * (r >> 2) + 4 * (m & 1) + (r & 3);
+}
+
+// Kernel 2.  One workgroup of G waves per (batch*head, MFMA m of the output
+// kernel, key block rho of 32 dims): the 16 value dims of m over the key dims
+// of rho.  Wave w sums the span partials s = w, w + G, ..
+// of its elements in order, the sums are added in a fixed order (results are
+// bitwise reproducible), then the map is written (when wanted) and, through
+// LDS, transposed into the output kernel's A operand (m, rho): lane (n, g)
+// holds KV^T[value dim of row n][key dims 32 rho + 8g .. + 7] times 2^sh, sh
+// bringing the largest |KV| of the operand into [2^14, 2^15) (exact to undo;
+// it keeps both large and tiny maps inside float16).
+template <int DK, int DV, int G>
+__global__ __launch_bounds__(64 * G) void saga_kv_reduce_kernel(SagaParams p) {
+  constexpr int NQ = 2;                   // float4 pieces per lane: 32 key dims x 4 pieces / 64
+  constexpr int NRHO = DK / 32;
+  __shared__ f32x4 part[G - 1][64 * NQ];
+  __shared__ float tile[32][17];          // [key dim in rho][row r of MFMA m], padded
+  __shared__ float wmax;
+  const int bh = blockIdx.x, m = blockIdx.y, rho = blockIdx.z;
+  const int lane = threadIdx.x & 63, grp = threadIdx.x >> 6;
+  // piece j of this lane: key dim 32 rho + (64 j + lane) / 4, value dims
+  // out_row_dim(m, 4 q) .. + 3 with q = lane % 4 (4 contiguous columns)
+  f32x4 acc[NQ];
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float* src = p.partial + (size_t)bh * p.n_spans * DK * DV + 32 * rho * DV;
+  for (int s = grp; s < p.n_spans; s += G) {
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      const int i = (64 * j + lane) >> 2, q = lane & 3;
+      acc[j] += *reinterpret_cast<const f32x4*>(src + (size_t)s * DK * DV + i * DV +
+                                                out_row_dim(m, 4 * q));
+    }
+  }
+  if (grp > 0) {
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) part[grp - 1][64 * j + lane] = acc[j];
+  }
   __syncthreads();
   if (grp == 0) {
-    const f32x4 sum = ((part[0][col] + part[1][col]) + part[2][col]) + part[3][col];
-    if (p.kv != nullptr) *reinterpret_cast<f32x4*>(p.kv + (size_t)bh * DK * DV + e) = sum;
-    const int i = e / DV, j = e % DV;   // the 4 elements are (i, j .. j + 3)
-    float* kvt = p.kvt + (size_t)bh * DK * DV;
+    float mx = 0.f;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) kvt[(j + u) * DK + i] = sum[u];
+    for (int j = 0; j < NQ; ++j) {
+      f32x4 sum = acc[j];
+#pragma unroll
+      for (int w = 0; w < G - 1; ++w) sum = sum + part[w][64 * j + lane];
+      const int i = (64 * j + lane) >> 2, q = lane & 3;
+      if (p.kv != nullptr)
+        *reinterpret_cast<f32x4*>(p.kv + (size_t)bh * DK * DV + (32 * rho + i) * DV +
+                                  out_row_dim(m, 4 * q)) = sum;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        tile[i][4 * q + u] = sum[u];
+        mx = fmaxf(mx, fabsf(sum[u]));
+      }
+    }
+#pragma unroll
+    for (int k = 32; k >= 1; k >>= 1) mx = fmaxf(mx, __shfl_xor(mx, k));
+    if (lane == 0) wmax = mx;
+  }
+  __syncthreads();
+  if (grp == 0) {
+    const float mx = wmax;
+    int ex = 0;
+    (void)frexpf(mx, &ex);                    // mx = f * 2^ex, f in [0.5, 1)
+    const int sh = (mx > 0.f) ? 15 - ex : 0;  // scaled maximum in [2^14, 2^15)
+    const float scale = ldexpf(1.f, sh);
+    const size_t op = ((size_t)bh * (DV / 16) + m) * NRHO + rho;
+    if (lane == 0) p.unscale[op] = ldexpf(1.f, -sh);
+    const int n = lane & 15, g = lane >> 4;
+    f16x8 x;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (f16)(tile[8 * g + e][n] * scale);
+    static_cast<f16x8*>(p.amap)[op * 64 + lane] = x;
   }
 }
 
@@ -201,10 +261,8 @@ __global__ __launch_bounds__(kThreads) void saga_kv_reduce_kernel(SagaParams p) 
 //    4 (m % 2) + r % 4, so lane (n, g) ends up with value dims
 //    32 s + 8g .. + 7 of token n from MFMAs 2s and 2s + 1: one 16-byte store
 //    per s, and the four lane groups of a store fill 64 contiguous bytes.
-//    Rows come from the transposed map as two 16-byte loads, scaled by a power
-//    of two that brings each MFMA's largest |KV| entry to [2^14, 2^15) before
-//    the float16 conversion (exact to undo; it keeps both large and tiny maps
-//    inside float16).
+//    Kernel 2 has laid them out (scaled float16, one 16-byte load per lane
+//    and operand); each MFMA's result is multiplied by its inverse scale.
 template <int DK, int DV>
 __global__ __launch_bounds__(kThreads) void saga_out_kernel(SagaParams p) {
   constexpr int NRHO = DK / 32, NM = DV / 16;
@@ -217,7 +275,7 @@ __global__ __launch_bounds__(kThreads) void saga_out_kernel(SagaParams p) {
 
   const rsrc_t rq = seq_rsrc(static_cast<const f16*>(p.q) + (size_t)bh * p.N * DK, (uint32_t)p.N * RBK);
   const rsrc_t ro = seq_rsrc(static_cast<f16*>(p.out) + (size_t)bh * p.N * DV, (uint32_t)p.N * RBV);
-  const float* kvt = p.kvt + (size_t)bh * DK * DV;
+  const f16x8* amap = static_cast<const f16x8*>(p.amap) + (size_t)bh * (DV / 16) * NRHO * 64;
 
   // With 64 key dims every block's queries are requested first, so their
   // latency overlaps the map reads below; with 128 the registers this takes
@@ -240,30 +298,14 @@ __global__ __launch_bounds__(kThreads) void saga_out_kernel(SagaParams p) {
   }
 
   f16x8 am[NM][NRHO];
-  float unscale[NM];
+  float unscale[NM][NRHO];
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
-    const int dim = 32 * (m >> 1) + 8 * (n16 >> 2) + 4 * (m & 1) + (n16 & 3);
-    f32x4 lo[NRHO], hi[NRHO];
-    float mx = 0.f;
 #pragma unroll
     for (int rho = 0; rho < NRHO; ++rho) {
-      const float* row = kvt + dim * DK + 32 * rho + 8 * g;
-      lo[rho] = *reinterpret_cast<const f32x4*>(row);
-      hi[rho] = *reinterpret_cast<const f32x4*>(row + 4);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) mx = fmaxf(mx, fmaxf(fabsf(lo[rho][u]), fabsf(hi[rho][u])));
+      am[m][rho] = amap[(m * NRHO + rho) * 64 + lane];
+      unscale[m][rho] = p.unscale[((size_t)bh * NM + m) * NRHO + rho];
     }
-#pragma unroll
-    for (int k = 32; k >= 1; k >>= 1) mx = fmaxf(mx, __shfl_xor(mx, k));
-    int ex = 0;
-    (void)frexpf(mx, &ex);                    // mx = f * 2^ex, f in [0.5, 1)
-    const int sh = (mx > 0.f) ? 15 - ex : 0;  // scaled maximum in [2^14, 2^15)
-    const float scale = ldexpf(1.f, sh);
-    unscale[m] = ldexpf(1.f, -sh);
-#pragma unroll
-    for (int rho = 0; rho < NRHO; ++rho)
-      am[m][rho] = cat8(to_f16(lo[rho] * scale), to_f16(hi[rho] * scale));
   }
 
 #pragma unroll
@@ -280,9 +322,11 @@ __global__ __launch_bounds__(kThreads) void saga_out_kernel(SagaParams p) {
       for (int h = 0; h < 2; ++h) {
         acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int rho = 0; rho < NRHO; ++rho)
-          acc[h] = mma32(am[2 * s2 + h][rho], qb[rho], acc[h]);
-        acc[h] *= unscale[2 * s2 + h];
+        for (int rho = 0; rho < NRHO; ++rho) {
+          // each key block carries its own scale: undo it before adding
+          const f32x4 part = mma32(am[2 * s2 + h][rho], qb[rho], f32x4{0.f, 0.f, 0.f, 0.f});
+          acc[h] += part * unscale[2 * s2 + h][rho];
+        }
       }
       const f16x8 o = cat8(to_f16(acc[0]), to_f16(acc[1]));
       __builtin_amdgcn_raw_buffer_store_b128(
@@ -294,12 +338,12 @@ __global__ __launch_bounds__(kThreads) void saga_out_kernel(SagaParams p) {
 
 template <class K>
 hipError_t launch_k(K kernel, dim3 grid, hipStream_t stream, const SagaParams& p,
-                    hipEvent_t const* ev, int slot) {
+                    hipEvent_t const* ev, int slot, int threads = kThreads) {
   if (ev != nullptr) {
-    hipExtLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, ev[2 * slot], ev[2 * slot + 1],
+    hipExtLaunchKernelGGL(kernel, grid, dim3(threads), 0, stream, ev[2 * slot], ev[2 * slot + 1],
                           0, p);
   } else {
-    hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(kernel, grid, dim3(threads), 0, stream, p);
   }
   return hipGetLastError();
 }
@@ -311,9 +355,12 @@ hipError_t launch_saga_variant(const SagaParams& p, hipStream_t stream, hipEvent
   if ((e = launch_k(saga_kv_partial_kernel<DK, DV>, dim3(BH * p.n_spans), stream, p, ev, 0)) !=
       hipSuccess)
     return e;
-  if ((e = launch_k(saga_kv_reduce_kernel<DK, DV>, dim3(BH, DK * DV / 256), stream, p, ev, 1)) !=
-      hipSuccess)
-    return e;
+  // eight waves split long span lists, four short ones (measured: 64 spans
+  // per sequence 5.4 against 7.3 us; 2 spans 8.4 against 14.1 us)
+  const dim3 rgrid(BH, DV / 16, DK / 32);
+  e = p.n_spans >= 16 ? launch_k(saga_kv_reduce_kernel<DK, DV, 8>, rgrid, stream, p, ev, 1, 512)
+                      : launch_k(saga_kv_reduce_kernel<DK, DV, 4>, rgrid, stream, p, ev, 1, 256);
+  if (e != hipSuccess) return e;
   return launch_k(saga_out_kernel<DK, DV>, dim3(BH * p.n_tblocks), stream, p, ev, 2);
 }
 

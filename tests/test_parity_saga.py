@@ -10,9 +10,9 @@ derived from the kernels' arithmetic:
     2^-25 absolute in the subnormal range) and their products summed in
     float32 over at most N = 16K tokens (below 2^-10 relative to the sum of
     magnitudes): |dKV| <= 2^-9 (|K A|^T |V B|) + 2^-24 (sum |K A| + sum |V B|);
-  * the map is read as float16 after a power-of-two scaling per 16 value
-    columns: at most 2^-12 of the largest |KV| entry, bounded here by
-    2^-11 max |KV|;
+  * the map is read as float16 after a power-of-two scaling per MFMA operand
+    (16 value columns x 32 key dims): at most 2^-12 of the operand's largest
+    |KV| entry, bounded here by 2^-11 max |KV|;
   * O = Q KV is summed in float32 and rounded to float16 (2^-11 relative).
 
   |dO| <= 2^-11 |O| + |Q| (bound on |dKV| + 2^-11 max|KV|) + 2^-24
