@@ -164,11 +164,6 @@ __global__ __launch_bounds__(kThreads) void saga_kv_partial_kernel(SagaParams p)
   }
 }
 
-// Kernel 2: kv[bh] = sum of the span partials, in a fixed order, written as
-// the caller's [d_k][d_v] map (when asked for) and transposed, [d_v][d_k],
-// for the output kernel.  A workgroup owns 256 map elements (64 columns of
-// 4); its four thread groups sum every fourth span, one load per span in
-// flight per thread, and the four sums are added in group order.
 // MFMA m of the output kernel (16 value dims): its row r is value dim
 // 32 (m / 2) + 8 (r / 4) + 4 (m % 2) + r % 4, so that the output lanes store
 // 16 contiguous bytes (see saga_out_kernel).
