@@ -864,6 +864,8 @@ def main():
                     help="skip the 768x768-image line (12 calls, one per block)")
     ap.add_argument("--no-sweep", dest="sweep", action="store_false",
                     help="skip the time-vs-token-count sweep")
+    ap.add_argument("--no-extras", dest="extras", action="store_false",
+                    help="skip the per-step spread and warm passes of the main workload")
     ap.add_argument("--no-bwd", action="store_true",
                     help="skip the backward pass line (gla_chunk_bwd on the main workload)")
     ap.add_argument("--saga", default=SAGA_WORKLOAD,
@@ -913,7 +915,7 @@ def main():
         del src, dst
 
     wl = WORKLOADS[args.workload]
-    runner, ms_step, mean = time_workload(wl, torch, args.steps, args.warmup, extras=True)
+    runner, ms_step, mean = time_workload(wl, torch, args.steps, args.warmup, extras=args.extras)
     main_sum = summarize(wl, ms_step, mean)
     log("[bench] %s: %.3f ms/step, %.3e tokens/s, %.2f us/call, kernels %s" %
         (wl.name, ms_step, main_sum["value"], main_sum["path"]["wall_us_per_call"],
@@ -954,8 +956,10 @@ def main():
         log("[bench] time vs tokens (B=1, 12 heads, 4 directions): %s" %
             ", ".join("%s %.1f us" % (x["grid"], x["us_per_call"]) for x in sweep))
 
-    copy_gbps = copy_bandwidth(torch)
-    log("[bench] device copy: %.0f GB/s (read + write)" % copy_gbps)
+    # (not in counter runs: their calibration copy must be the run's largest)
+    copy_gbps = None if args.copy_calibration_mb > 0 else copy_bandwidth(torch)
+    if copy_gbps:
+        log("[bench] device copy: %.0f GB/s (read + write)" % copy_gbps)
 
     ext = None
     if not args.no_ext and wl.dtype == "fp16":
@@ -1009,7 +1013,9 @@ def main():
         log("[bench] cpu oracle, all cores: %.3e tokens/s on %d processes" %
             (cpu_all["value"], cpu_all["cores"]))
         pool.shutdown()
-    main_sum["roofline"]["frac_of_device_copy"] = round(main_sum["roofline"]["achieved"] / copy_gbps, 4)
+    if copy_gbps:
+        main_sum["roofline"]["frac_of_device_copy"] = round(
+            main_sum["roofline"]["achieved"] / copy_gbps, 4)
 
     line = {
         "metric": METRIC,
@@ -1031,7 +1037,7 @@ def main():
         "cpu_baseline": cpu,
         "cpu_baseline_all_cores": cpu_all,
         "parity_vs_oracle": parity,
-        "device_copy_GBps": round(copy_gbps, 1),
+        "device_copy_GBps": round(copy_gbps, 1) if copy_gbps else None,
         "step_ms": main_sum.get("step_ms"),
         "warm": main_sum.get("warm"),
         "secondary": secondary,

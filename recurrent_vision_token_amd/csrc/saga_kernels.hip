@@ -171,36 +171,37 @@ __device__ __forceinline__ int out_row_dim(int m, int r) {
   return 32 * (m >> 1) + 8 * (r >> 2) + 4 * (m & 1) + (r & 3);
 }
 
-// Kernel 2.  One workgroup of G waves per (batch*head, MFMA m of the output
-// kernel, key block rho of 32 dims): the 16 value dims of m over the key dims
-// of rho.  Wave w sums the span partials s = w, w + G, ..
-// of its elements in order, the sums are added in a fixed order (results are
-// bitwise reproducible), then the map is written (when wanted) and, through
-// LDS, transposed into the output kernel's A operand (m, rho): lane (n, g)
-// holds KV^T[value dim of row n][key dims 32 rho + 8g .. + 7] times 2^sh, sh
+// Kernel 2.  One workgroup of G waves per (batch*head, pair of MFMAs 2s and
+// 2s + 1 of the output kernel, key block rho of 32 dims): value dims
+// 32 s .. 32 s + 31 (whole 128-byte lines of the partials) over the key dims
+// of rho.  Wave w sums the span partials s' = w, w + G, .. of its elements in
+// order, the sums are added in a fixed order (results are bitwise
+// reproducible), then the map is written (when wanted) and, through LDS,
+// transposed into the output kernel's A operands (m, rho): lane (n, g) holds
+// KV^T[value dim of row n][key dims 32 rho + 8g .. + 7] times 2^sh, sh
 // bringing the largest |KV| of the operand into [2^14, 2^15) (exact to undo;
 // it keeps both large and tiny maps inside float16).
 template <int DK, int DV, int G>
 __global__ __launch_bounds__(64 * G) void saga_kv_reduce_kernel(SagaParams p) {
-  constexpr int NQ = 2;                   // float4 pieces per lane: 32 key dims x 4 pieces / 64
+  constexpr int NQ = 4;                   // float4 pieces per lane: 32 key dims x 8 pieces / 64
   constexpr int NRHO = DK / 32;
   __shared__ f32x4 part[G - 1][64 * NQ];
-  __shared__ float tile[32][17];          // [key dim in rho][row r of MFMA m], padded
-  __shared__ float wmax;
-  const int bh = blockIdx.x, m = blockIdx.y, rho = blockIdx.z;
+  __shared__ float tile[32][2][17];       // [key dim in rho][m - 2s][row r of MFMA m], padded
+  __shared__ float wmax[2];
+  const int bh = blockIdx.x, s2 = blockIdx.y, rho = blockIdx.z;
   const int lane = threadIdx.x & 63, grp = threadIdx.x >> 6;
-  // piece j of this lane: key dim 32 rho + (64 j + lane) / 4, value dims
-  // out_row_dim(m, 4 q) .. + 3 with q = lane % 4 (4 contiguous columns)
+  // piece j of this lane: key dim 32 rho + (64 j + lane) / 8, value dims
+  // 32 s2 + 4 q .. + 3 with q = lane % 8: rows 4 (q / 2) .. + 3 of MFMA
+  // 2 s2 + (q % 2)
   f32x4 acc[NQ];
 #pragma unroll
   for (int j = 0; j < NQ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const float* src = p.partial + (size_t)bh * p.n_spans * DK * DV + 32 * rho * DV;
+  const float* src = p.partial + (size_t)bh * p.n_spans * DK * DV + 32 * rho * DV + 32 * s2;
   for (int s = grp; s < p.n_spans; s += G) {
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
-      const int i = (64 * j + lane) >> 2, q = lane & 3;
-      acc[j] += *reinterpret_cast<const f32x4*>(src + (size_t)s * DK * DV + i * DV +
-                                                out_row_dim(m, 4 * q));
+      const int i = (64 * j + lane) >> 3, q = lane & 7;
+      acc[j] += *reinterpret_cast<const f32x4*>(src + (size_t)s * DK * DV + i * DV + 4 * q);
     }
   }
   if (grp > 0) {
@@ -209,29 +210,36 @@ __global__ __launch_bounds__(64 * G) void saga_kv_reduce_kernel(SagaParams p) {
   }
   __syncthreads();
   if (grp == 0) {
-    float mx = 0.f;
+    float mx[2] = {0.f, 0.f};
+    const int q = lane & 7, h = q & 1;
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
       f32x4 sum = acc[j];
 #pragma unroll
       for (int w = 0; w < G - 1; ++w) sum = sum + part[w][64 * j + lane];
-      const int i = (64 * j + lane) >> 2, q = lane & 3;
+      const int i = (64 * j + lane) >> 3;
       if (p.kv != nullptr)
-        *reinterpret_cast<f32x4*>(p.kv + (size_t)bh * DK * DV + (32 * rho + i) * DV +
-                                  out_row_dim(m, 4 * q)) = sum;
+        *reinterpret_cast<f32x4*>(p.kv + (size_t)bh * DK * DV + (32 * rho + i) * DV + 32 * s2 +
+                                  4 * q) = sum;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        tile[i][4 * q + u] = sum[u];
-        mx = fmaxf(mx, fabsf(sum[u]));
+        tile[i][h][4 * (q >> 1) + u] = sum[u];
+        mx[h] = fmaxf(mx[h], fabsf(sum[u]));
       }
     }
+    // lanes of one parity hold MFMA 2 s2 + parity: reduce each over its lanes
 #pragma unroll
-    for (int k = 32; k >= 1; k >>= 1) mx = fmaxf(mx, __shfl_xor(mx, k));
-    if (lane == 0) wmax = mx;
+    for (int k = 32; k >= 2; k >>= 1) {
+      mx[0] = fmaxf(mx[0], __shfl_xor(mx[0], k));
+      mx[1] = fmaxf(mx[1], __shfl_xor(mx[1], k));
+    }
+    if (lane < 2) wmax[lane] = mx[lane];
   }
   __syncthreads();
-  if (grp == 0) {
-    const float mx = wmax;
+  if (grp < 2) {
+    // wave h writes operand (2 s2 + h, rho)
+    const int h = grp, m = 2 * s2 + h;
+    const float mx = wmax[h];
     int ex = 0;
     (void)frexpf(mx, &ex);                    // mx = f * 2^ex, f in [0.5, 1)
     const int sh = (mx > 0.f) ? 15 - ex : 0;  // scaled maximum in [2^14, 2^15)
@@ -241,7 +249,7 @@ __global__ __launch_bounds__(64 * G) void saga_kv_reduce_kernel(SagaParams p) {
     const int n = lane & 15, g = lane >> 4;
     f16x8 x;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = (f16)(tile[8 * g + e][n] * scale);
+    for (int e = 0; e < 8; ++e) x[e] = (f16)(tile[8 * g + e][h][n] * scale);
     static_cast<f16x8*>(p.amap)[op * 64 + lane] = x;
   }
 }
@@ -352,7 +360,7 @@ hipError_t launch_saga_variant(const SagaParams& p, hipStream_t stream, hipEvent
     return e;
   // eight waves split long span lists, four short ones (measured: 64 spans
   // per sequence 5.4 against 7.3 us; 2 spans 8.4 against 14.1 us)
-  const dim3 rgrid(BH, DV / 16, DK / 32);
+  const dim3 rgrid(BH, DV / 32, DK / 32);
   e = p.n_spans >= 16 ? launch_k(saga_kv_reduce_kernel<DK, DV, 8>, rgrid, stream, p, ev, 1, 512)
                       : launch_k(saga_kv_reduce_kernel<DK, DV, 4>, rgrid, stream, p, ev, 1, 256);
   if (e != hipSuccess) return e;
