@@ -864,6 +864,8 @@ def main():
                     help="skip the 768x768-image line (12 calls, one per block)")
     ap.add_argument("--no-sweep", dest="sweep", action="store_false",
                     help="skip the time-vs-token-count sweep")
+    ap.add_argument("--no-batched", dest="batched", action="store_false",
+                    help="skip the batched line (B=32, 16 heads, 64x64, d_k=128, d_v=64)")
     ap.add_argument("--no-extras", dest="extras", action="store_false",
                     help="skip the per-step spread and warm passes of the main workload")
     ap.add_argument("--no-bwd", action="store_true",
@@ -941,6 +943,16 @@ def main():
                "path": s4["path"]}
         log("[bench] %s: %.1f us of attention per image (12 calls), %.3e tokens/s" %
             (wl4.name, ms4 * 1e3, s4["value"]))
+
+    batched = None
+    if args.batched:
+        wl5 = WORKLOADS["batched"]
+        _, ms5, mean5 = time_workload(wl5, torch, 40, 40)
+        s5 = summarize(wl5, ms5, mean5)
+        batched = {"workload": describe(wl5), "value": s5["value"], "unit": "tokens/s",
+                   "ms_per_call": round(ms5, 4), "roofline": s5["roofline"], "path": s5["path"]}
+        log("[bench] %s: %.1f us per call, %.3e tokens/s, output kernel %.0f GB/s" %
+            (wl5.name, ms5 * 1e3, s5["value"], s5["roofline"]["achieved"]))
 
     sweep = None
     if args.sweep:
@@ -1042,6 +1054,7 @@ def main():
         "warm": main_sum.get("warm"),
         "secondary": secondary,
         "img768": img,
+        "batched": batched,
         "time_vs_tokens": sweep,
         "fused_gate_initial_state": ext,
         "backward": bwd,
