@@ -89,7 +89,7 @@ def test_full_size_16k():
     wl = WORKLOADS["hires16.4k"]
     q, k, v, la = make_inputs(1, wl.heads, wl.H, wl.W, 64, 64, "fp16", wl.gate_std, 3)
     do, dfin, init = make_bwd_inputs(1, wl.heads, wl.H, wl.W, 64, seed=350)
-    for d in (0, 2):
+    for d in (0, 1, 2, 3):
         print("bwd 16.4K dir", d, flush=True)
         got = run(q, k, v, la, do, d, dfin, init)
         ref = gla_backward(q, k, v, la, do, d, d_final_state=dfin, initial_state=init)
