@@ -888,7 +888,7 @@ def main():
                             [k for k in args.traffic_kernels.split(",") if k])
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(sequences shard across GPUs with no communication; see the design notes). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)

@@ -38,8 +38,8 @@ def load():
     if _lib is not None:
         return _lib
     if not os.path.exists(LIB_PATH):
-        raise RuntimeError("libgla.so is not built; run __graft_entry__.build() "
-                           "or python recurrent_vision_token_amd/build.py")
+        raise RuntimeError("libgla.so is not built; run python recurrent_vision_token_amd/build.py "
+                           "(hipcc for gfx950)")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i = ctypes.c_void_p, ctypes.c_int
     sig = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, vp, vp]
