@@ -94,3 +94,26 @@ def test_full_size_16k():
         got = run(q, k, v, la, do, d, dfin, init)
         ref = gla_backward(q, k, v, la, do, d, d_final_state=dfin, initial_state=init)
         check(got, ref, "16.4K dir %d" % d)
+
+
+def test_many_spans_per_summary_workgroup():
+    # 8 x 16 sequences of 64 chunks: 4096 spans of two chunks, so every
+    # workgroup of the summaries kernel streams eight spans (crossing
+    # sequence boundaries) on a 256-CU device; the rotation gives every
+    # sequence group its own direction.  A sample of sequences is held to the
+    # oracle, and the whole output to finiteness.
+    B, heads, H, W = 8, 16, 64, 64
+    q, k, v, la = make_inputs(B, heads, H, W, 64, 64, "fp16", 1.0, 360)
+    do, dfin, init = make_bwd_inputs(B, heads, H, W, 64, seed=361)
+    print("bwd many spans", flush=True)
+    got = run(q, k, v, la, do, 4, dfin, init)
+    for x in got:
+        assert np.all(np.isfinite(x))
+    rng = np.random.default_rng(362)
+    for bh in rng.choice(B * heads, 3, replace=False):
+        b, h = divmod(int(bh), heads)
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        # batch element b scans in direction b % 4
+        ref = gla_backward(q[sl], k[sl], v[sl], la[sl], do[sl], b % 4, d_final_state=dfin[sl],
+                           initial_state=init[sl])
+        check([x[sl] for x in got], ref, "many spans b %d h %d" % (b, h))
