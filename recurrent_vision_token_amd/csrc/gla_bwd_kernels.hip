@@ -211,39 +211,55 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
 
   if (e_from_partner || r_from_partner) {
     // partner decay profile per key dim: keys decayed to the partner's end
-    // (exclusive of the token), or queries decayed from its start (inclusive)
-    const int i = tid & 63, J = tid >> 6;
-    float al[16], tot = 0.f;
+    // (exclusive of the token), or queries decayed from its start (inclusive);
+    // thread (key-dim pair, half of a 16-token sub-block)
+    const int i2 = tid & 31, h = (tid >> 5) & 1, J = tid >> 6;
+    const int i = 2 * i2;
+    float al0[8], al1[8], tot0 = 0.f, tot1 = 0.f;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const float la = (float)tkd[swz<RB>(16 * J + u, i)];
-      al[u] = ex(la);
-      tot += la;
+    for (int u = 0; u < 8; ++u) {
+      const f16x2 la2 = *reinterpret_cast<const f16x2*>(&tkd[swz<RB>(16 * J + 8 * h + u, i)]);
+      const float l0 = (float)la2[0], l1 = (float)la2[1];
+      al0[u] = ex(l0);
+      al1[u] = ex(l1);
+      tot0 += l0;
+      tot1 += l1;
     }
-    sTot[J][i] = tot;
+    const float ot0 = __shfl_xor(tot0, 32), ot1 = __shfl_xor(tot1, 32);
+    if (h == 0) *reinterpret_cast<f32x2*>(&sTot[J][i]) = f32x2{tot0 + ot0, tot1 + ot1};
     __syncthreads();
-    float before = 0.f, after = 0.f;
+    float before0 = 0.f, before1 = 0.f, after0 = 0.f, after1 = 0.f, all0 = 0.f, all1 = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      before += j < J ? sTot[j][i] : 0.f;
-      after += j > J ? sTot[j][i] : 0.f;
+      const f32x2 t2 = *reinterpret_cast<const f32x2*>(&sTot[j][i]);
+      before0 += j < J ? t2[0] : 0.f;
+      before1 += j < J ? t2[1] : 0.f;
+      after0 += j > J ? t2[0] : 0.f;
+      after1 += j > J ? t2[1] : 0.f;
+      all0 += t2[0];
+      all1 += t2[1];
     }
-    if (J == 0) sCarry[0][i] = ex(sTot[0][i] + sTot[1][i] + sTot[2][i] + sTot[3][i]);
+    if (J == 0 && h == 0) *reinterpret_cast<f32x2*>(&sCarry[0][i]) = f32x2{ex(all0), ex(all1)};
     if (e_from_partner) {
-      float sfx = ex(after);
+      // the second half's tokens come after the first's
+      float sfx0 = ex(h ? after0 : after0 + ot0), sfx1 = ex(h ? after1 : after1 + ot1);
 #pragma unroll
-      for (int u = 15; u >= 0; --u) {
-        const int e = swz<RB>(16 * J + u, i);
-        tkd[e] = (f16)((float)tqs[e] * sfx);
-        sfx *= al[u];
+      for (int u = 7; u >= 0; --u) {
+        const int e = swz<RB>(16 * J + 8 * h + u, i);
+        const f16x2 x2 = *reinterpret_cast<const f16x2*>(&tqs[e]);
+        *reinterpret_cast<f16x2*>(&tkd[e]) = f16x2{(f16)((float)x2[0] * sfx0), (f16)((float)x2[1] * sfx1)};
+        sfx0 *= al0[u];
+        sfx1 *= al1[u];
       }
     } else {
-      float pre = ex(before);
+      float pre0 = ex(h ? before0 + ot0 : before0), pre1 = ex(h ? before1 + ot1 : before1);
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int e = swz<RB>(16 * J + u, i);
-        pre *= al[u];
-        tkd[e] = (f16)((float)tqs[e] * pre);
+      for (int u = 0; u < 8; ++u) {
+        const int e = swz<RB>(16 * J + 8 * h + u, i);
+        pre0 *= al0[u];
+        pre1 *= al1[u];
+        const f16x2 x2 = *reinterpret_cast<const f16x2*>(&tqs[e]);
+        *reinterpret_cast<f16x2*>(&tkd[e]) = f16x2{(f16)((float)x2[0] * pre0), (f16)((float)x2[1] * pre1)};
       }
     }
     __syncthreads();
