@@ -44,6 +44,7 @@
  * Concurrent calls on different streams use different buffers and are
  * independent.  Under stream capture a call takes a stream-ordered
  * allocation of its own instead, released in the captured stream order.
+
  * Besides this table the library holds no global state but a one-time read
  * of tuning environment variables and the measurement hook's per-thread
  * events; it keeps no pointer to caller memory after returning.
@@ -103,6 +104,33 @@ enum {
 int gla_chunk_fwd(const void* q, const void* k, const void* v, const void* log_alpha,
                   int scan_dir, int B, int heads, int H, int W, int d_k, int d_v, int chunk,
                   void* out, float* final_state, void* stream);
+
+/*
+ * Execution paths of the float16 forward entries (gla_chunk_fwd,
+ * gla_chunk_fwd_ex), chosen per call; results agree within the float16
+ * tolerance, not bit for bit, since the span split differs:
+ *   three passes: span summaries, the in-order scan of the span boundary
+ *     states, the output pass (three kernels; only the output kernel when the
+ *     sequence is not split into spans);
+ *   two passes (d_k = d_v = 64, short sequences): span summaries, then the
+ *     output pass, whose workgroups fold the initial state and the summaries
+ *     of all earlier spans of their sequence into their own entry state (no
+ *     scan kernel; the work of a span grows with its index, so it is used
+ *     for few spans).  Chosen when a split into 2..16 spans of at most 4
+ *     chunks puts every output workgroup on the device at once.
+ * mode: GLA_FWD_AUTO (default, the rule above), GLA_FWD_THREE_PASS (always
+ * three passes), GLA_FWD_TWO_PASS (two passes whenever the sequence splits
+ * into 2..16 spans, of any length).  Process-wide, for calls made after it;
+ * a tuning and testing switch, both paths meet the same accuracy.  Returns
+ * GLA_OK, or GLA_ERR_SHAPE for an unknown mode.  The environment variable
+ * GLA_SPAN_CHUNKS (a forced span length) selects three passes.
+ */
+enum {
+  GLA_FWD_AUTO = 0,
+  GLA_FWD_THREE_PASS = 1,
+  GLA_FWD_TWO_PASS = 2
+};
+int gla_set_forward_mode(int mode);
 
 /*
  * Extended float16 entry: gla_chunk_fwd plus an initial state and a fused

@@ -14,10 +14,10 @@ thin binding around it plus the seeded synthetic workloads.
 """
 
 from ._lib import (GlaError, gla_chunk_bwd, gla_chunk_fwd, gla_chunk_fwd_ex, load,  # noqa: F401
-                   release_workspaces, saga_fwd, spatial_swiglu, status_str)
+                   release_workspaces, saga_fwd, set_forward_mode, spatial_swiglu, status_str)
 
 SCAN_L2R, SCAN_R2L, SCAN_T2B, SCAN_B2T, SCAN_ROTATE_BATCH = 0, 1, 2, 3, 4
 
 __all__ = ["gla_chunk_fwd", "gla_chunk_fwd_ex", "gla_chunk_bwd", "spatial_swiglu", "saga_fwd",
-           "GlaError", "load", "release_workspaces", "status_str", "SCAN_L2R",
+           "GlaError", "load", "release_workspaces", "set_forward_mode", "status_str", "SCAN_L2R",
            "SCAN_R2L", "SCAN_T2B", "SCAN_B2T", "SCAN_ROTATE_BATCH"]

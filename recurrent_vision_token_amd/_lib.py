@@ -19,8 +19,9 @@ STATUS = {
 }
 EXPORTED = ("gla_chunk_bwd", "gla_chunk_fwd", "gla_chunk_fwd_ex", "gla_chunk_fwd_f32",
             "gla_plan_spans", "gla_release_workspaces",
-            "gla_saga_fwd", "gla_set_kernel_events", "gla_spatial_swiglu", "gla_status_str",
-            "gla_version")
+            "gla_saga_fwd", "gla_set_forward_mode", "gla_set_kernel_events",
+            "gla_spatial_swiglu", "gla_status_str", "gla_version")
+FORWARD_MODES = {"auto": 0, "three_pass": 1, "two_pass": 2}
 GATE_MODES = {"log_alpha": 0, "logits": 1}
 
 _lib = None
@@ -40,6 +41,11 @@ def load():
     if not os.path.exists(LIB_PATH):
         raise RuntimeError("libgla.so is not built; run python recurrent_vision_token_amd/build.py "
                            "(hipcc for gfx950)")
+    # torch first: it brings its own HIP runtime under the same soname as the
+    # system one libgla.so names, and a process gets one of them, the first
+    # loaded.  Loading the library first would put torch on a runtime it was
+    # not built against (torch.cuda then reports no device).
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     vp, i = ctypes.c_void_p, ctypes.c_int
     sig = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, vp, vp]
@@ -66,6 +72,8 @@ def load():
     lib.gla_version.restype = ctypes.c_int
     lib.gla_release_workspaces.argtypes = []
     lib.gla_release_workspaces.restype = ctypes.c_int
+    lib.gla_set_forward_mode.argtypes = [ctypes.c_int]
+    lib.gla_set_forward_mode.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -319,6 +327,16 @@ def release_workspaces():
     """Free the workspace buffers the library keeps per (device, stream)
     (waits for the work of every device that holds one)."""
     rc = load().gla_release_workspaces()
+    if rc != 0:
+        raise GlaError(rc, status_str(rc))
+
+
+def set_forward_mode(mode):
+    """Choose the float16 forward path for later calls, process-wide: "auto",
+    "three_pass" or "two_pass" (see gla_set_forward_mode)."""
+    if mode not in FORWARD_MODES:
+        raise ValueError("mode must be one of %s" % sorted(FORWARD_MODES))
+    rc = load().gla_set_forward_mode(FORWARD_MODES[mode])
     if rc != 0:
         raise GlaError(rc, status_str(rc))
 

@@ -171,6 +171,29 @@ int plan_span_chunks(long long bh, int n_chunks, int slots) {
   return (int)(m < 1 ? 1 : m);
 }
 
+// Forward path choice (gla_set_forward_mode), process-wide.
+std::atomic<int> g_fwd_mode{GLA_FWD_AUTO};
+
+// Longest span (chunks) the automatic choice gives the two-pass path: its
+// output workgroups fold every earlier span's summary into their entry state,
+// which pays off only while the spans are few and short.
+constexpr int kTwoPassAutoChunks = 4;
+
+// Chunks per span for the two-pass path: the shortest span that gives
+// 2 .. kTwoPassMaxSpans spans per sequence with every output workgroup
+// resident at once (in forced mode any span length, and without the
+// residency condition); 0 when there is none.
+int plan_two_pass(long long bh, int n_chunks, int slots, bool forced) {
+  const int max_sc = forced ? n_chunks - 1 : kTwoPassAutoChunks;
+  for (int sc = 1; sc <= max_sc && sc < n_chunks; ++sc) {
+    const long long ns = (n_chunks + sc - 1) / sc;
+    if (ns > gla::kTwoPassMaxSpans) continue;
+    if (!forced && bh * ns > slots) continue;
+    return sc;
+  }
+  return 0;
+}
+
 // Optional inputs of the extended entry point.
 struct Extras {
   bool gate_logits = false;               // `la` holds gate logits (fused activation)
@@ -228,8 +251,13 @@ int forward(gla::Dtype dt, size_t esize, const void* q, const void* k, const voi
   const int n_chunks = (int)((T + kChunk - 1) / kChunk);
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return GLA_ERR_HIP;
-  const int span_chunks =
-      plan_span_chunks(BH, n_chunks, output_slots(dev, dt, d_k, d_v, ex.gate_logits));
+  const int mode = g_fwd_mode.load(std::memory_order_relaxed);
+  const int slots = output_slots(dev, dt, d_k, d_v, ex.gate_logits);
+  int span_chunks = 0;
+  if (mode != GLA_FWD_THREE_PASS && span_override() == 0 && gla::has_two_pass(dt, d_k, d_v))
+    span_chunks = plan_two_pass(BH, n_chunks, slots, mode == GLA_FWD_TWO_PASS);
+  const bool two_pass = span_chunks > 0;
+  if (!two_pass) span_chunks = plan_span_chunks(BH, n_chunks, slots);
   const int n_spans = (n_chunks + span_chunks - 1) / span_chunks;
   if (BH * n_spans > (1LL << 31) - 1) return GLA_ERR_SHAPE;
   if (plan_only != nullptr) {
@@ -270,7 +298,8 @@ int forward(gla::Dtype dt, size_t esize, const void* q, const void* k, const voi
   }
   const hipEvent_t* ev = t_events_set ? t_events : nullptr;
   t_events_set = false;
-  const hipError_t e = gla::launch_forward(dt, d_k, d_v, ex.gate_logits, p, st, ev);
+  const hipError_t e = two_pass ? gla::launch_forward_two_pass(ex.gate_logits, p, st, ev)
+                                : gla::launch_forward(dt, d_k, d_v, ex.gate_logits, p, st, ev);
   if (ws.finish() != hipSuccess) return GLA_ERR_HIP;
   return e == hipSuccess ? GLA_OK : GLA_ERR_HIP;
 }
@@ -619,6 +648,13 @@ int gla_plan_spans(int use_f32, int B, int heads, int H, int W, int d_k, int d_v
   return GLA_OK;
 }
 
+int gla_set_forward_mode(int mode) {
+  if (mode != GLA_FWD_AUTO && mode != GLA_FWD_THREE_PASS && mode != GLA_FWD_TWO_PASS)
+    return GLA_ERR_SHAPE;
+  g_fwd_mode.store(mode, std::memory_order_relaxed);
+  return GLA_OK;
+}
+
 int gla_set_kernel_events(void* const* events, int n) {
   if (n == 0) {
     t_events_set = false;
@@ -683,6 +719,6 @@ int gla_release_workspaces(void) {
   }
 }
 
-int gla_version(void) { return 150; }
+int gla_version(void) { return 160; }
 
 }  // extern "C"

@@ -56,6 +56,19 @@ bool has_variant(Dtype dt, int d_k, int d_v);
 hipError_t launch_forward(Dtype dt, int d_k, int d_v, bool gate_logits, const FwdParams& p,
                           hipStream_t stream, hipEvent_t const* events);
 
+// Two-pass forward (float16, d_k = d_v = 64): the span-summary kernel, with
+// each summary stored in the output kernel's register layout, then the
+// output kernel, whose workgroups fold the initial state and the summaries of
+// all earlier spans of their sequence into their entry state (no scan
+// kernel).  Needs 2 <= n_spans <= kTwoPassMaxSpans and span_state /
+// span_gate as for the three-pass path.  events: null, or six hipEvent_t
+// (pair 0 around the summary kernel, pair 1 back to back, pair 2 around the
+// output kernel).
+constexpr int kTwoPassMaxSpans = 16;
+bool has_two_pass(Dtype dt, int d_k, int d_v);
+hipError_t launch_forward_two_pass(bool gate_logits, const FwdParams& p, hipStream_t stream,
+                                   hipEvent_t const* events);
+
 // Backward pass, float16, d_k = d_v = 64.  `p` describes the forward
 // tensors (q, k, v, la; spans of span_chunks chunks, n_spans of them) with
 // the forward-state workspace (span_state, span_gate, initial_state) and the

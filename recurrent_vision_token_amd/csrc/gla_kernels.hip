@@ -822,55 +822,47 @@ struct StepTiles {
 };
 
 
-template <int DK, int DV, bool GATE>
-__global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 4 : (DK == 128 && DV == 128) ? 1 : 2) void chunk_output_f16_kernel(
-    FwdParams p) {
+// Load one state in the output layout: wave w owns value columns
+// 16(w + 4j) .. ; tile (r, j) holds S[16r + 4g + u][16(w + 4j) + n] in lane
+// (n, g).  src: [DK][DV] float32 row-major, or null (zero state).
+template <int DK, int DV>
+__device__ __forceinline__ void load_state_tiles(const float* src, int wave, int n16, int g,
+                                                 f32x4 (&st)[DK / 16][DV / 64]) {
+#pragma unroll
+  for (int j = 0; j < DV / 64; ++j) {
+    const int col = 16 * (wave + 4 * j) + n16;
+#pragma unroll
+    for (int r = 0; r < DK / 16; ++r)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) st[r][j][u] = src ? src[(16 * r + 4 * g + u) * DV + col] : 0.f;
+  }
+}
+
+// The outputs of one span from its entry state `st` (output layout, see
+// load_state_tiles) through two step buffers; `st` ends as the state after
+// the span, written to final_state for the sequence's last span.  Returns
+// with every load landed.
+template <int DK, int DV, bool GATE, class Entry>
+__device__ __forceinline__ void output_span(const FwdParams& p, int bh, int span,
+                                            const StepTiles<DK, DV>& slot0,
+                                            const StepTiles<DK, DV>& slot1, f16* sqt, float* sgd,
+                                            uint32_t (*srow)[kStep],
+                                            f32x4 (&st)[DK / 16][DV / 64], Entry&& entry) {
   constexpr int RBK = 2 * DK, RBV = 2 * DV;
   constexpr int NR = DK / 16, NC = DV / 64, NRHO = DK / 32;
   constexpr int NBK = RBK / 128, NBV = RBV / 128;  // 1 KB blocks per wave and tile of one step
   constexpr int NSTORE = 2 * NC;                    // output stores per wave and step
   static_assert(NSTORE < 64, "vmcnt range");
-  // Two step buffers (the next step loads while this one is computed; a
-  // third buffer measured slower).  Separate LDS objects per buffer, so the
-  // compiler's own waits for the LDS-writing loads can tell them apart.
-  __shared__ __attribute__((aligned(16))) f16 q0[kStep * DK], k0[kStep * DK], la0[kStep * DK], v0[kStep * DV];
-  __shared__ __attribute__((aligned(16))) f16 q1[kStep * DK], k1[kStep * DK], la1[kStep * DK], v1[kStep * DV];
-  // q decayed from the step start, columns in token-slot order (see qt_slot)
-  __shared__ __attribute__((aligned(16))) f16 sqt[kStep * DK];
-  __shared__ __attribute__((aligned(16))) float sgd[DK];  // exp(decay over the step)
-  // grid cell of each step row (bit 31: past the span), per step buffer
-  __shared__ uint32_t srow[2][kStep];
-  const StepTiles<DK, DV> slot0{q0, k0, la0, v0}, slot1{q1, k1, la1, v1};
-
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n16 = lane & 15, g = lane >> 4;
 
-  const int bh = blockIdx.x / p.n_spans;
-  const int span = blockIdx.x - bh * p.n_spans;
   const int b = bh / p.heads;
   const GridMap gm = grid_map(p, b);
   const SeqBufs sb = seq_bufs<DK, DV>(p, bh);
   const int t_begin = span * p.span_chunks * kChunk;
   const int t_end = min(t_begin + p.span_chunks * kChunk, p.T);
   const int n_steps = (t_end - t_begin + kStep - 1) / kStep;
-
-  // State tiles: wave w owns value columns 16(w + 4j) .. ; tile (r, j) holds
-  // S[16r + 4g + u][16(w + 4j) + n] in lane (n, g).
-  f32x4 st[NR][NC];
-  {
-    const float* src =
-        (p.n_spans > 1) ? p.span_state + ((size_t)bh * p.n_spans + span) * DK * DV
-        : p.initial_state ? p.initial_state + (size_t)bh * DK * DV : nullptr;
-#pragma unroll
-    for (int j = 0; j < NC; ++j) {
-      const int col = 16 * (wave + 4 * j) + n16;
-#pragma unroll
-      for (int r = 0; r < NR; ++r)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) st[r][j][u] = src ? src[(16 * r + 4 * g + u) * DV + col] : 0.f;
-    }
-  }
 
   auto issue = [&](const StepTiles<DK, DV>& s, uint32_t* rows, int step) {
     const int t0 = t_begin + kStep * step;
@@ -1013,6 +1005,7 @@ __global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 4 : (DK == 128 &
   };
   // Before step s the loads in flight are step s and the stores of s - 1.
   issue(slot0, srow[0], 0);
+  entry(st);                     // completes the entry state while step 0 loads
   wait_barrier<vmcnt_imm(0)>();  // the entry state and step 0 have landed
   for (int step = 0; step < n_steps; step += 2) {
     issue(slot1, srow[1], step + 1);
@@ -1044,6 +1037,70 @@ __global__ __launch_bounds__(kThreads, (DK == 64 && DV == 64) ? 4 : (DK == 128 &
 #pragma unroll
         for (int u = 0; u < 4; ++u) dst[(16 * r + 4 * (l >> 4) + u) * DV + col] = st[r][j][u];
     }
+  }
+}
+
+// LOOKBACK (d_k = d_v = 64): the entry state is not read from span_state but
+// formed here from the initial state and the summaries of the earlier spans
+// of the sequence, stored by span_summary_f16_kernel<..., true> in this
+// kernel's register layout: S_entry = g_{s-1} (... (g_0 S_init + A_0) ...) +
+// A_{s-1}, the scan's recurrence, with four summaries' loads in flight at a
+// time, overlapping the first step's tile loads.
+template <int DK, int DV, bool GATE, bool LOOKBACK = false>
+__global__ __launch_bounds__(kThreads, LOOKBACK ? 2 : (DK == 64 && DV == 64) ? 4 : (DK == 128 && DV == 128) ? 1 : 2) void chunk_output_f16_kernel(
+    FwdParams p) {
+  static_assert(!LOOKBACK || (DK == 64 && DV == 64), "look-back: d_k = d_v = 64");
+  // Two step buffers (the next step loads while this one is computed; a
+  // third buffer measured slower).  Separate LDS objects per buffer, so the
+  // compiler's own waits for the LDS-writing loads can tell them apart.
+  __shared__ __attribute__((aligned(16))) f16 q0[kStep * DK], k0[kStep * DK], la0[kStep * DK], v0[kStep * DV];
+  __shared__ __attribute__((aligned(16))) f16 q1[kStep * DK], k1[kStep * DK], la1[kStep * DK], v1[kStep * DV];
+  // q decayed from the step start, columns in token-slot order (see qt_slot)
+  __shared__ __attribute__((aligned(16))) f16 sqt[kStep * DK];
+  __shared__ __attribute__((aligned(16))) float sgd[DK];  // exp(decay over the step)
+  // grid cell of each step row (bit 31: past the span), per step buffer
+  __shared__ uint32_t srow[2][kStep];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int bh = blockIdx.x / p.n_spans;
+  const int span = blockIdx.x - bh * p.n_spans;
+  f32x4 st[DK / 16][DV / 64];
+  const StepTiles<DK, DV> slot0{q0, k0, la0, v0}, slot1{q1, k1, la1, v1};
+  if constexpr (!LOOKBACK) {
+    load_state_tiles<DK, DV>(
+        (p.n_spans > 1) ? p.span_state + ((size_t)bh * p.n_spans + span) * DK * DV
+        : p.initial_state ? p.initial_state + (size_t)bh * DK * DV : nullptr,
+        wave, lane & 15, lane >> 4, st);
+    output_span<DK, DV, GATE>(p, bh, span, slot0, slot1, sqt, sgd, srow, st, [](auto&) {});
+  } else {
+    const int g = lane >> 4;
+    load_state_tiles<DK, DV>(p.initial_state ? p.initial_state + (size_t)bh * DK * DV : nullptr,
+                             wave, lane & 15, g, st);
+    auto fold_earlier = [&](f32x4 (&s)[DK / 16][DV / 64]) {
+      const float* A =
+          p.span_state + (size_t)bh * p.n_spans * DK * DV + ((size_t)wave * 4 * 64 + lane) * 4;
+      const float* G = p.span_gate + (size_t)bh * p.n_spans * DK + 4 * g;
+      constexpr int NB = 4;  // summaries in flight
+      for (int j0 = 0; j0 < span; j0 += NB) {
+        f32x4 av[NB][DK / 16], gv[NB][DK / 16];
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+          const int j = min(j0 + i, span - 1);
+#pragma unroll
+          for (int r = 0; r < DK / 16; ++r) {
+            av[i][r] = *reinterpret_cast<const f32x4*>(A + (size_t)j * DK * DV + r * 256);
+            gv[i][r] = *reinterpret_cast<const f32x4*>(G + (size_t)j * DK + 16 * r);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+          if (j0 + i < span)
+#pragma unroll
+            for (int r = 0; r < DK / 16; ++r) s[r][0] = gv[i][r] * s[r][0] + av[i][r];
+      }
+    };
+    output_span<DK, DV, GATE>(p, bh, span, slot0, slot1, sqt, sgd, srow, st, fold_earlier);
   }
 }
 
@@ -1171,13 +1228,15 @@ __device__ __forceinline__ void store_summary(float* span_state, float* span_gat
   }
 }
 
+// The span's summary (st, gdec as in fold_chunk, from zero) through the two
+// tile buffers; returns with every load landed, the buffers still being read
+// by other waves (a barrier must come before they are refilled).
 template <int DK, int DV, bool GATE>
-__global__ __launch_bounds__(kThreads) void span_summary_f16_kernel(FwdParams p) {
-  // six separate LDS objects, so the compiler's own waits for the LDS-writing
-  // loads can tell the tiles apart
-  __shared__ __attribute__((aligned(16))) f16 k0[kChunk * DK], la0[kChunk * DK], v0[kChunk * DV];
-  __shared__ __attribute__((aligned(16))) f16 k1[kChunk * DK], la1[kChunk * DK], v1[kChunk * DV];
-  const SumTile<DK, DV> slot0{k0, la0, v0}, slot1{k1, la1, v1};
+__device__ __forceinline__ void summarize_span(const FwdParams& p, int bh, int span,
+                                               const SumTile<DK, DV>& slot0,
+                                               const SumTile<DK, DV>& slot1,
+                                               f32x4 (&st)[DK / 64][DV / 16],
+                                               f32x4 (&gdec)[DK / 64]) {
   constexpr int NDB = DK / 64, NCB = DV / 16;
   constexpr int RBK = 2 * DK, RBV = 2 * DV;
   constexpr int NBK = RBK / 64, NBV = RBV / 64;  // 1 KB blocks per wave and tile
@@ -1187,8 +1246,6 @@ __global__ __launch_bounds__(kThreads) void span_summary_f16_kernel(FwdParams p)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n16 = lane & 15, g = lane >> 4;
 
-  const int bh = blockIdx.x / p.n_spans;
-  const int span = blockIdx.x - bh * p.n_spans;
   const int b = bh / p.heads;
   const GridMap gm = grid_map(p, b);
   const SeqBufs sb = seq_bufs<DK, DV>(p, bh);
@@ -1219,8 +1276,7 @@ __global__ __launch_bounds__(kThreads) void span_summary_f16_kernel(FwdParams p)
   const f16x4 m_upper = tri_operand<false>(n16, g);
   const f16x4 m_ones = f16x4{(f16)1.f, (f16)1.f, (f16)1.f, (f16)1.f};
 
-  f32x4 st[NDB][NCB];
-  f32x4 gdec[NDB];  // decay (log) from the current chunk's end to the span end, per key dim
+  // gdec: decay (log) from the current chunk's end to the span end, per key dim
 #pragma unroll
   for (int d = 0; d < NDB; ++d) {
     gdec[d] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1248,7 +1304,62 @@ __global__ __launch_bounds__(kThreads) void span_summary_f16_kernel(FwdParams p)
   // land before the workgroup's LDS can be handed on
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  store_summary<DK, DV>(p.span_state, p.span_gate, bh, p.n_spans, span, wave, n16, g, st, gdec);
+}
+
+// One summary stored where chunk_output_f16_kernel<..., true> reads it
+// (d_k = d_v = 64): lane (n, g) of wave w holds S[16 w + n][16 cb + 4g + u];
+// in the output kernel's layout that element belongs to wave cb, row block
+// r = w, lane (4g + u) + 16 (n / 4), component n % 4, and the summary is
+// [wave][r][lane][4] floats, so each reader lane loads 16-byte pieces.  Each
+// wave's four 1 KB blocks go through its own 4 KB of LDS (`stage`, free once
+// the workgroup is past the barrier before this call) and out as 16-byte
+// stores.
+template <int DK, int DV>
+__device__ __forceinline__ void store_summary_out_layout(const FwdParams& p, int bh, int span,
+                                                         int wave, int lane, float* stage,
+                                                         const f32x4 (&st)[DK / 64][DV / 16],
+                                                         const f32x4 (&gdec)[DK / 64]) {
+  static_assert(DK == 64 && DV == 64, "output layout: d_k = d_v = 64");
+  const int n16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int cb = 0; cb < DV / 16; ++cb)
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      stage[cb * 256 + (4 * g + u + 16 * (n16 >> 2)) * 4 + (n16 & 3)] = st[0][cb][u];
+  float* dst = p.span_state + ((size_t)bh * p.n_spans + span) * DK * DV;
+#pragma unroll
+  for (int cb = 0; cb < DV / 16; ++cb)
+    *reinterpret_cast<f32x4*>(dst + (cb * 4 + wave) * 256 + 4 * lane) =
+        *reinterpret_cast<const f32x4*>(stage + cb * 256 + 4 * lane);
+  if (g == 0)
+    p.span_gate[((size_t)bh * p.n_spans + span) * DK + 16 * wave + n16] =
+        exp2_fast(gdec[0][0] * 1.4426950408889634f);
+}
+
+// OUT_LAYOUT: store the summary for the two-pass path's output kernel
+// (store_summary_out_layout) instead of row-major for the scan.
+template <int DK, int DV, bool GATE, bool OUT_LAYOUT = false>
+__global__ __launch_bounds__(kThreads) void span_summary_f16_kernel(FwdParams p) {
+  // six separate LDS objects, so the compiler's own waits for the LDS-writing
+  // loads can tell the tiles apart
+  __shared__ __attribute__((aligned(16))) f16 k0[kChunk * DK], la0[kChunk * DK], v0[kChunk * DV];
+  __shared__ __attribute__((aligned(16))) f16 k1[kChunk * DK], la1[kChunk * DK], v1[kChunk * DV];
+  const int bh = blockIdx.x / p.n_spans;
+  const int span = blockIdx.x - bh * p.n_spans;
+  f32x4 st[DK / 64][DV / 16];
+  f32x4 gdec[DK / 64];
+  summarize_span<DK, DV, GATE>(p, bh, span, SumTile<DK, DV>{k0, la0, v0},
+                               SumTile<DK, DV>{k1, la1, v1}, st, gdec);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if constexpr (OUT_LAYOUT) {
+    __syncthreads();  // every wave is done reading the tiles
+    store_summary_out_layout<DK, DV>(p, bh, span, wave, lane,
+                                     reinterpret_cast<float*>(wave < 2 ? k0 : la0) + (wave & 1) * 1024,
+                                     st, gdec);
+  } else
+    store_summary<DK, DV>(p.span_state, p.span_gate, bh, p.n_spans, span, wave, lane & 15,
+                          lane >> 4, st, gdec);
 }
 
 // The backward pass's two summaries of a span: the forward one (k, v; the
@@ -1496,6 +1607,28 @@ bool has_variant(Dtype dt, int d_k, int d_v) {
   if (dt == Dtype::kF16)
     return (d_k == 64 || d_k == 128) && (d_v == 64 || d_v == 128);
   return d_k == 64 && (d_v == 64 || d_v == 128);
+}
+
+bool has_two_pass(Dtype dt, int d_k, int d_v) {
+  return dt == Dtype::kF16 && d_k == 64 && d_v == 64;
+}
+
+template <bool GATE>
+hipError_t launch_two_pass_variant(const FwdParams& p, hipStream_t stream, hipEvent_t const* ev) {
+  const dim3 grid((unsigned)(p.B * p.heads * p.n_spans));
+  hipError_t e;
+  if ((e = launch_one(span_summary_f16_kernel<64, 64, GATE, true>, grid, stream, p, ev, 0)) !=
+      hipSuccess)
+    return e;
+  if ((e = skip_one(stream, ev, 1)) != hipSuccess) return e;
+  return launch_one(chunk_output_f16_kernel<64, 64, GATE, true>, grid, stream, p, ev, 2);
+}
+
+hipError_t launch_forward_two_pass(bool gate_logits, const FwdParams& p, hipStream_t stream,
+                                   hipEvent_t const* ev) {
+  if (p.n_spans < 2 || p.n_spans > kTwoPassMaxSpans) return hipErrorInvalidValue;
+  return gate_logits ? launch_two_pass_variant<true>(p, stream, ev)
+                     : launch_two_pass_variant<false>(p, stream, ev);
 }
 
 hipError_t launch_forward(Dtype dt, int d_k, int d_v, bool gate_logits, const FwdParams& p,
