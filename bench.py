@@ -92,16 +92,23 @@ def algorithmic(wl):
             "flops": flops, "token_heads": th}
 
 
-def kernel_bytes(wl, n_spans):
-    """Algorithmic bytes each kernel of one call moves (its own reads and writes)."""
+def kernel_bytes(wl, n_spans, kernels=3):
+    """Algorithmic bytes each kernel of one call moves (its own reads and writes).
+    kernels = 2 is the two-pass path: no scan, and the output workgroup of span
+    s reads the summaries (state and gate) of spans 0..s-1."""
     es = 2 if wl.dtype == "fp16" else 4
     th = wl.B * wl.heads * wl.T
     bh = wl.B * wl.heads
     st = wl.d_k * wl.d_v * 4
-    out = {"chunk_output": th * es * (3 * wl.d_k + 2 * wl.d_v) + bh * st + (bh * n_spans * st if n_spans > 1 else 0)}
+    if kernels == 2:
+        entry = bh * n_spans * (n_spans - 1) // 2 * (st + 4 * wl.d_k)
+    else:
+        entry = bh * n_spans * st if n_spans > 1 else 0
+    out = {"chunk_output": th * es * (3 * wl.d_k + 2 * wl.d_v) + bh * st + entry}
     if n_spans > 1:
         out["span_summary"] = th * es * (2 * wl.d_k + wl.d_v) + bh * n_spans * (st + 4 * wl.d_k)
-        out["span_scan"] = bh * n_spans * (2 * st + 4 * wl.d_k)
+        if kernels == 3:
+            out["span_scan"] = bh * n_spans * (2 * st + 4 * wl.d_k)
     return out
 
 
@@ -598,9 +605,11 @@ def saga_summary(swl, ms_call, k_ms, cpu):
     }
 
 
-def n_spans_of(wl):
+def plan_of(wl):
+    """(n_spans, kernels) of the forward call on the current device."""
     from recurrent_vision_token_amd import _lib
-    return _lib.plan_spans(wl.dtype, wl.B, wl.heads, wl.H, wl.W, wl.d_k, wl.d_v, wl.chunk)[1]
+    _, ns, kernels = _lib.plan_forward(wl.dtype, wl.B, wl.heads, wl.H, wl.W, wl.d_k, wl.d_v, wl.chunk)
+    return ns, kernels
 
 
 def traffic_from_profiles(wl_name, kernel):
@@ -751,10 +760,10 @@ def summarize(wl, ms_step, mean, ext=False):
         alg["bytes"] += wl.B * wl.heads * wl.d_k * wl.d_v * 4
     ncall = len(wl.calls)
     tokens_step = ncall * wl.B * wl.T
-    spans = n_spans_of(wl)
-    kb = kernel_bytes(wl, spans)
+    spans, kernels = plan_of(wl)
+    kb = kernel_bytes(wl, spans, kernels)
     if ext:
-        kb["span_scan" if spans > 1 else "chunk_output"] += wl.B * wl.heads * wl.d_k * wl.d_v * 4
+        kb["span_scan" if kernels == 3 else "chunk_output"] += wl.B * wl.heads * wl.d_k * wl.d_v * 4
     present = [k for k in kb if mean[k] > 0]
     dom = max(present, key=lambda k: mean[k])
     ach = kb[dom] / (mean[dom] * 1e-3) / 1e9
@@ -778,7 +787,7 @@ def summarize(wl, ms_step, mean, ext=False):
                  "hbm_frac": round(path_gbps / HBM_PEAK_GBPS, 4),
                  "mfma_frac": round(alg["flops"] / (wall_call_ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
                  "kernel_us": {k: round(mean[k] * 1e3, 2) for k in ("span_summary", "span_scan", "chunk_output")},
-                 "n_spans": spans},
+                 "n_spans": spans, "kernels": kernels},
     }
     if "step_ms" in mean:
         out["step_ms"] = {k: round(v, 4) for k, v in mean["step_ms"].items()}

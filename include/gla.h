@@ -174,11 +174,16 @@ int gla_chunk_fwd_f32(const float* q, const float* k, const float* v, const floa
  * Work split the forward call would use on the current device: each sequence
  * of ceil(H*W/64) chunks is cut into n_spans spans of span_chunks chunks (the
  * last may be shorter), one output workgroup per (batch, head, span).  When
- * n_spans > 1 the call also runs the span-summary and span-scan kernels and
- * uses a workspace of B*heads*n_spans*(d_k*d_v + d_k) floats.
- * use_f32 selects the float32 entry.  Reads device attributes (a HIP call);
- * returns the same argument errors as the forward entry points.
+ * n_spans > 1 the call also runs the span-summary kernel, and the span-scan
+ * kernel on the three-pass path, and uses a workspace of
+ * B*heads*n_spans*(d_k*d_v + d_k) floats.  gla_plan_forward also gives the
+ * number of kernels the call runs: 1 (no split), 2 (two-pass path) or 3
+ * (three-pass path; see gla_set_forward_mode).  use_f32 selects the float32
+ * entry.  Reads device attributes (a HIP call); returns the same argument
+ * errors as the forward entry points, and GLA_ERR_NULL for a NULL output.
  */
+int gla_plan_forward(int use_f32, int B, int heads, int H, int W, int d_k, int d_v, int chunk,
+                     int* span_chunks, int* n_spans, int* kernels);
 int gla_plan_spans(int use_f32, int B, int heads, int H, int W, int d_k, int d_v, int chunk,
                    int* span_chunks, int* n_spans);
 

@@ -18,7 +18,7 @@ STATUS = {
     -4: "GLA_ERR_ALIGN", -5: "GLA_ERR_SCAN_DIR", -6: "GLA_ERR_ALIAS", -7: "GLA_ERR_HIP",
 }
 EXPORTED = ("gla_chunk_bwd", "gla_chunk_fwd", "gla_chunk_fwd_ex", "gla_chunk_fwd_f32",
-            "gla_plan_spans", "gla_release_workspaces",
+            "gla_plan_forward", "gla_plan_spans", "gla_release_workspaces",
             "gla_saga_fwd", "gla_set_forward_mode", "gla_set_kernel_events",
             "gla_spatial_swiglu", "gla_status_str", "gla_version")
 FORWARD_MODES = {"auto": 0, "three_pass": 1, "two_pass": 2}
@@ -66,6 +66,9 @@ def load():
     lib.gla_status_str.restype = ctypes.c_char_p
     lib.gla_plan_spans.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i)]
     lib.gla_plan_spans.restype = ctypes.c_int
+    lib.gla_plan_forward.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i),
+                                     ctypes.POINTER(i)]
+    lib.gla_plan_forward.restype = ctypes.c_int
     lib.gla_set_kernel_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
     lib.gla_set_kernel_events.restype = ctypes.c_int
     lib.gla_version.argtypes = []
@@ -348,6 +351,17 @@ def set_kernel_events(handles):
         return lib.gla_set_kernel_events(None, 0)
     arr = (ctypes.c_void_p * len(handles))(*handles)
     return lib.gla_set_kernel_events(arr, len(handles))
+
+
+def plan_forward(dtype, B, heads, H, W, d_k, d_v, chunk=64):
+    """(span_chunks, n_spans, kernels) the forward call would use on the current
+    device; kernels is 1 (no split), 2 (two-pass path) or 3 (three passes)."""
+    a, b, c = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
+    rc = load().gla_plan_forward(1 if dtype == "fp32" else 0, B, heads, H, W, d_k, d_v, chunk,
+                                 ctypes.byref(a), ctypes.byref(b), ctypes.byref(c))
+    if rc != GLA_OK:
+        raise GlaError(rc, status_str(rc))
+    return a.value, b.value, c.value
 
 
 def plan_spans(dtype, B, heads, H, W, d_k, d_v, chunk=64):

@@ -263,6 +263,7 @@ int forward(gla::Dtype dt, size_t esize, const void* q, const void* k, const voi
   if (plan_only != nullptr) {
     plan_only[0] = span_chunks;
     plan_only[1] = n_spans;
+    plan_only[2] = two_pass ? 2 : n_spans > 1 ? 3 : 1;
     return GLA_OK;
   }
 
@@ -625,14 +626,14 @@ int gla_saga_fwd(const void* q, const void* k, const void* v, const void* alpha,
   }
 }
 
-int gla_plan_spans(int use_f32, int B, int heads, int H, int W, int d_k, int d_v, int chunk,
-                   int* span_chunks, int* n_spans) {
-  if (span_chunks == nullptr || n_spans == nullptr) return GLA_ERR_NULL;
+int gla_plan_forward(int use_f32, int B, int heads, int H, int W, int d_k, int d_v, int chunk,
+                     int* span_chunks, int* n_spans, int* kernels) {
+  if (span_chunks == nullptr || n_spans == nullptr || kernels == nullptr) return GLA_ERR_NULL;
   // Validation only looks at pointer values; these placeholders are distinct,
   // aligned and never dereferenced.
   const uintptr_t base = (uintptr_t)1 << 40;
   const uintptr_t gap = (uintptr_t)1 << 38;
-  int plan[2] = {0, 0};
+  int plan[3] = {0, 0, 0};
   int rc;
   try {
     rc = forward(use_f32 ? gla::Dtype::kF32 : gla::Dtype::kF16, use_f32 ? 4 : 2,
@@ -645,7 +646,15 @@ int gla_plan_spans(int use_f32, int B, int heads, int H, int W, int d_k, int d_v
   if (rc != GLA_OK) return rc;
   *span_chunks = plan[0];
   *n_spans = plan[1];
+  *kernels = plan[2];
   return GLA_OK;
+}
+
+int gla_plan_spans(int use_f32, int B, int heads, int H, int W, int d_k, int d_v, int chunk,
+                   int* span_chunks, int* n_spans) {
+  int kernels = 0;
+  return gla_plan_forward(use_f32, B, heads, H, W, d_k, d_v, chunk, span_chunks, n_spans,
+                          &kernels);
 }
 
 int gla_set_forward_mode(int mode) {

@@ -97,3 +97,20 @@ def test_all_cores_oracle_pool_matches_the_oracle():
         np.testing.assert_array_equal(o[0, 0], ref_o[b, h])
         np.testing.assert_array_equal(f[0, 0], ref_f[b, h])
     assert line["kind"] == "oracle" and line["cores"] == workers and line["value"] > 0
+
+
+def test_kernel_bytes_of_both_forward_paths():
+    # the two-pass output kernel reads every earlier span's summary (state and
+    # gate); the three-pass one reads one entry state per span
+    import bench
+    from recurrent_vision_token_amd.workloads import WORKLOADS
+    wl = WORKLOADS["gtr1.6k"]
+    bh, st, gate = wl.B * wl.heads, 64 * 64 * 4, 64 * 4
+    io = wl.B * wl.heads * wl.T * 2 * (3 * 64 + 2 * 64)
+    three = bench.kernel_bytes(wl, 13, 3)
+    two = bench.kernel_bytes(wl, 13, 2)
+    assert three["chunk_output"] == io + bh * st + bh * 13 * st
+    assert two["chunk_output"] == io + bh * st + bh * (13 * 12 // 2) * (st + gate)
+    assert "span_scan" in three and "span_scan" not in two
+    assert two["span_summary"] == three["span_summary"]
+    assert bench.kernel_bytes(wl, 1, 1) == {"chunk_output": io + bh * st}
