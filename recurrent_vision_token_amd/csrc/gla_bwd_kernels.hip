@@ -141,30 +141,39 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
   // next-state update (rows 16 kc + n, columns 16 w + 4g ..; for the state a
   // partner completes, the span's part of it), and, for a state taken as it
   // is, the MFMA operand layouts below (raw float32 until the tiles landed)
+  // (32-bit byte offsets from the workgroup's span-state bases, so each load
+  // is one uniform base plus one lane offset)
   f32x4 e4s[4], r4s[4], ea_raw[4], ra_raw[4];
   float rta_raw[16];
+  auto ld4 = [](const float* base, uint32_t byte_off) {
+    return *reinterpret_cast<const f32x4*>(reinterpret_cast<const char*>(base) + byte_off);
+  };
+  auto ld1 = [](const float* base, uint32_t byte_off) {
+    return *reinterpret_cast<const float*>(reinterpret_cast<const char*>(base) + byte_off);
+  };
+  const uint32_t o_acc = 4u * (uint32_t)(n16 * DV + vj);            // row n, columns vj ..
+  const uint32_t o_op = 4u * (uint32_t)((16 * kb + n16) * DV + 8 * g);  // row 16 kb + n, cols 8g ..
+  const uint32_t o_t = 4u * (uint32_t)(8 * g * DV + 16 * vb + n16);   // R[8g][16 vb + n]
 #pragma unroll
   for (int kc = 0; kc < 4; ++kc) {
-    e4s[kc] = *reinterpret_cast<const f32x4*>(E_span + (16 * kc + n16) * DV + vj);
-    r4s[kc] = *reinterpret_cast<const f32x4*>(R_span + (16 * kc + n16) * DV + vj);
+    e4s[kc] = ld4(E_span, o_acc + 4u * 16 * kc * DV);
+    r4s[kc] = ld4(R_span, o_acc + 4u * 16 * kc * DV);
   }
   if (!e_from_partner) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      ea_raw[2 * h] = *reinterpret_cast<const f32x4*>(E_span + (16 * kb + n16) * DV + 32 * h + 8 * g);
-      ea_raw[2 * h + 1] =
-          *reinterpret_cast<const f32x4*>(E_span + (16 * kb + n16) * DV + 32 * h + 8 * g + 4);
+      ea_raw[2 * h] = ld4(E_span, o_op + 4u * 32 * h);
+      ea_raw[2 * h + 1] = ld4(E_span, o_op + 4u * (32 * h + 4));
     }
   }
   if (!r_from_partner) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      ra_raw[2 * h] = *reinterpret_cast<const f32x4*>(R_span + (16 * kb + n16) * DV + 32 * h + 8 * g);
-      ra_raw[2 * h + 1] =
-          *reinterpret_cast<const f32x4*>(R_span + (16 * kb + n16) * DV + 32 * h + 8 * g + 4);
+      ra_raw[2 * h] = ld4(R_span, o_op + 4u * 32 * h);
+      ra_raw[2 * h + 1] = ld4(R_span, o_op + 4u * (32 * h + 4));
       // R^T rows 16 vb + n: R[32 h + 8g + e][16 vb + n]
 #pragma unroll
-      for (int e = 0; e < 8; ++e) rta_raw[8 * h + e] = R_span[(32 * h + 8 * g + e) * DV + 16 * vb + n16];
+      for (int e = 0; e < 8; ++e) rta_raw[8 * h + e] = ld1(R_span, o_t + 4u * (32 * h + e) * DV);
     }
   }
 
