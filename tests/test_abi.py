@@ -136,6 +136,30 @@ def test_plan_spans_argument_errors():
     assert lib.gla_plan_spans(0, 0, 12, 128, 128, 64, 64, 64, ctypes.byref(a), ctypes.byref(b)) == -2
 
 
+def test_plan_forward_argument_errors():
+    import ctypes
+    lib = _lib.load()
+    a, b, c = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
+    assert lib.gla_plan_forward(0, 1, 12, 128, 128, 64, 64, 64, ctypes.byref(a), ctypes.byref(b),
+                                None) == -1
+    assert lib.gla_plan_forward(0, 1, 12, 128, 128, 64, 64, 32, ctypes.byref(a), ctypes.byref(b),
+                                ctypes.byref(c)) == -3
+    assert lib.gla_plan_forward(0, 1, 0, 128, 128, 64, 64, 64, ctypes.byref(a), ctypes.byref(b),
+                                ctypes.byref(c)) == -2
+
+
+def test_forward_mode_setter():
+    # a host-only setting: no HIP call, so this runs without a device
+    lib = _lib.load()
+    for bad in (-1, 3, 99):
+        assert lib.gla_set_forward_mode(bad) == -2
+    for mode in ("three_pass", "two_pass", "auto"):
+        _lib.set_forward_mode(mode)
+    with pytest.raises(ValueError):
+        _lib.set_forward_mode("single")
+    assert lib.gla_set_forward_mode(0) == 0
+
+
 def call_sw(gate=P[0], value=P[1], ld=None, weight=P[2], bias=P[3], B=1, H=16, W=16, C=64,
             out=P[4]):
     return _lib.raw_call_swiglu(gate, value, C if ld is None else ld, weight, bias, B, H, W, C,

@@ -218,3 +218,21 @@ def test_graph_replay():
             assert torch.equal(out, o_ref) and torch.equal(fs, s_ref), rep
             o2, _ = gla_chunk_fwd(*x, 0)                   # eager work between replays
             torch.cuda.synchronize()
+
+
+def test_forced_mode_where_two_passes_do_not_apply():
+    # forcing two passes leaves other head dims, float32 and single-chunk
+    # sequences on their usual paths, with the same results
+    from recurrent_vision_token_amd._lib import plan_forward
+    print("two pass: forced mode elsewhere", flush=True)
+    with forward_mode("two_pass"):
+        assert plan_forward("fp16", 1, 12, 40, 40, 64, 64)[2] == 2
+        assert plan_forward("fp16", 1, 12, 40, 40, 128, 64)[2] == 3
+        assert plan_forward("fp32", 1, 12, 40, 40, 64, 64)[2] == 3
+        assert plan_forward("fp16", 1, 12, 8, 8, 64, 64)[2] == 1
+        x = make_inputs(1, 2, 24, 21, 128, 64, "fp16", 1.0, seed=77)
+        o, s = fwd(x, 3)
+    ro, rs = gla_forward(*x, 3)
+    check(o, ro, "d_k 128 out")
+    check(s, rs, "d_k 128 final_state")
+
