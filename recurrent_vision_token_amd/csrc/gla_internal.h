@@ -19,7 +19,8 @@ struct FwdParams {
   float* final_state;   // may be null
   const float* initial_state;  // [B][heads][d_k][d_v], may be null (zero state)
   float inv_tau;        // 1 / tau when `la` holds gate logits (fused activation)
-  float* span_state;    // [BH][n_spans][d_k][d_v] span summaries, then entry states
+  float* span_state;    // [BH][n_spans][d_k][d_v] span summaries, then entry states (three
+                        // passes), or summaries in the output kernel's layout (two passes)
   float* span_gate;     // [BH][n_spans][d_k] product of the span's gates
   int B, heads, H, W, T;
   // t / W and t / H as (umulhi(t, m) + t) >> s, exact for t < 2^31

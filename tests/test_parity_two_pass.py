@@ -136,7 +136,7 @@ def test_forced_long_spans(H, W):
 
 
 def test_extended_entry():
-    # fused gate activation and an initial state on the single-pass path
+    # fused gate activation and an initial state on the two-pass path
     from recurrent_vision_token_amd import gla_chunk_fwd_ex
     print("two pass: extended entry", flush=True)
     torch = _torch()
