@@ -236,3 +236,20 @@ def test_forced_mode_where_two_passes_do_not_apply():
     check(o, ro, "d_k 128 out")
     check(s, rs, "d_k 128 final_state")
 
+
+
+def test_forced_two_pass_more_workgroups_than_the_device_holds():
+    # 8 x 16 sequences of 13 spans: 1664 output workgroups, several rounds on
+    # the device (the path has no waits between workgroups); three sampled
+    # sequences against the oracle
+    print("two pass: many sequences", flush=True)
+    B, heads, H, W = 8, 16, 40, 40
+    x = make_inputs(B, heads, H, W, 64, 64, "fp16", 1.0, seed=91)
+    with forward_mode("two_pass"):
+        assert plan(B, heads, H, W) == (2, 13)
+        o, s = fwd(x, 4)
+    for b, h in ((0, 0), (3, 7), (7, 15)):
+        xs = [t[b:b + 1, h:h + 1] for t in x]
+        ro, rs = gla_forward(*xs, b % 4)
+        check(o[b:b + 1, h:h + 1], ro, "out b%d h%d" % (b, h))
+        check(s[b:b + 1, h:h + 1], rs, "final_state b%d h%d" % (b, h))
