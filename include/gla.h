@@ -128,7 +128,8 @@ int gla_chunk_fwd(const void* q, const void* k, const void* v, const void* log_a
 enum {
   GLA_FWD_AUTO = 0,
   GLA_FWD_THREE_PASS = 1,
-  GLA_FWD_TWO_PASS = 2
+  GLA_FWD_TWO_PASS = 2,
+  GLA_FWD_SINGLE_PASS = 3
 };
 int gla_set_forward_mode(int mode);
 

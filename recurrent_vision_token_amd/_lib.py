@@ -21,7 +21,7 @@ EXPORTED = ("gla_chunk_bwd", "gla_chunk_fwd", "gla_chunk_fwd_ex", "gla_chunk_fwd
             "gla_plan_forward", "gla_plan_spans", "gla_release_workspaces",
             "gla_saga_fwd", "gla_set_forward_mode", "gla_set_kernel_events",
             "gla_spatial_swiglu", "gla_status_str", "gla_version")
-FORWARD_MODES = {"auto": 0, "three_pass": 1, "two_pass": 2}
+FORWARD_MODES = {"auto": 0, "three_pass": 1, "two_pass": 2, "single_pass": 3}
 GATE_MODES = {"log_alpha": 0, "logits": 1}
 
 _lib = None

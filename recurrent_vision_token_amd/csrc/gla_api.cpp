@@ -41,6 +41,8 @@ struct WsEntry {
   hipStream_t stream;
   void* ptr;
   size_t bytes;
+  unsigned int* sync;   // hand-off words of the single-pass forward (never shared)
+  size_t sync_words;
   hipEvent_t done;
   bool used;
 };
@@ -48,26 +50,39 @@ std::mutex g_ws_mu;
 std::vector<WsEntry> g_ws;
 std::vector<std::pair<int, void*>> g_ws_retired;
 
+// One call's use of the cache.  The cache lock is held from acquire() until
+// finish() (or the end of the lease), so the launches of two host threads'
+// calls on one stream cannot interleave on the same buffers.
 class WsLease {
  public:
-  // A buffer of at least `bytes` for the work enqueued next on st.
-  hipError_t acquire(hipStream_t st, size_t bytes) {
+  // A buffer of at least `bytes` for the work enqueued next on st, and with
+  // sync_words > 0 also the stream's hand-off words (at least that many,
+  // zero when first allocated).
+  hipError_t acquire(hipStream_t st, size_t bytes, size_t sync_words = 0) {
     st_ = st;
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     hipError_t e = hipStreamIsCapturing(st, &cs);
     if (e != hipSuccess) return e;
     if (cs != hipStreamCaptureStatusNone) {
       captured_ = true;
-      return hipMallocAsync(&ptr_, bytes, st);
+      if ((e = hipMallocAsync(&ptr_, bytes, st)) != hipSuccess) return e;
+      if (sync_words > 0) {
+        void* sp = nullptr;
+        if ((e = hipMallocAsync(&sp, sync_words * sizeof(unsigned int), st)) != hipSuccess) return e;
+        sync_ = static_cast<unsigned int*>(sp);
+        // a kernel, not a memset node, clears them in the captured graph
+        if ((e = gla::launch_zero_words(sync_, sync_words, st)) != hipSuccess) return e;
+      }
+      return hipSuccess;
     }
     int dev = 0;
     if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
-    std::lock_guard<std::mutex> lock(g_ws_mu);
+    lock_ = std::unique_lock<std::mutex>(g_ws_mu);
     WsEntry* w = nullptr;
     for (WsEntry& x : g_ws)
       if (x.dev == dev && x.stream == st) w = &x;
     if (w == nullptr) {
-      WsEntry n{dev, st, nullptr, 0, nullptr, false};
+      WsEntry n{dev, st, nullptr, 0, nullptr, 0, nullptr, false};
       if ((e = hipEventCreateWithFlags(&n.done, hipEventDisableTiming)) != hipSuccess) return e;
       g_ws.push_back(n);
       w = &g_ws.back();
@@ -82,25 +97,51 @@ class WsLease {
       w->ptr = fresh;
       w->bytes = nb;
     }
+    if (w->sync_words < sync_words) {
+      const size_t granule = (size_t)1 << 14;
+      const size_t nw = (sync_words + granule - 1) / granule * granule;
+      void* fresh = nullptr;
+      if ((e = hipMalloc(&fresh, nw * sizeof(unsigned int))) != hipSuccess) return e;
+      // stream-ordered: earlier calls on this stream still use the old words
+      if ((e = hipMemsetAsync(fresh, 0, nw * sizeof(unsigned int), st)) != hipSuccess) {
+        (void)hipFree(fresh);
+        return e;
+      }
+      if (w->sync != nullptr) g_ws_retired.emplace_back(dev, w->sync);
+      w->sync = static_cast<unsigned int*>(fresh);
+      w->sync_words = nw;
+    }
     w->used = true;
     ptr_ = w->ptr;
+    sync_ = w->sync;
     done_ = w->done;
     return hipSuccess;
   }
-  // After the call's launches: mark the buffer's last use (or hand the
-  // captured allocation back in stream order).
+  // After the call's launches: mark the buffers' last use (or hand the
+  // captured allocations back in stream order), then let other calls in.
   hipError_t finish() {
-    if (ptr_ == nullptr) return hipSuccess;
-    if (captured_) return hipFreeAsync(ptr_, st_);
-    return hipEventRecord(done_, st_);
+    hipError_t e = hipSuccess;
+    if (captured_) {
+      if (ptr_ != nullptr) e = hipFreeAsync(ptr_, st_);
+      if (sync_ != nullptr && e == hipSuccess) e = hipFreeAsync(sync_, st_);
+    } else if (ptr_ != nullptr) {
+      e = hipEventRecord(done_, st_);
+    }
+    ptr_ = nullptr;
+    sync_ = nullptr;
+    if (lock_.owns_lock()) lock_.unlock();
+    return e;
   }
   void* ptr() const { return ptr_; }
+  unsigned int* sync() const { return sync_; }
 
  private:
   hipStream_t st_ = nullptr;
   void* ptr_ = nullptr;
+  unsigned int* sync_ = nullptr;
   hipEvent_t done_ = nullptr;
   bool captured_ = false;
+  std::unique_lock<std::mutex> lock_;
 };
 
 // Events of the measurement hook, per calling thread (see gla_set_kernel_events).
@@ -128,6 +169,22 @@ int output_slots(int dev, gla::Dtype dt, int d_k, int d_v, bool gate_logits) {
     cus = 256;
   n = cus * gla::output_blocks_per_cu(dt, d_k, d_v, gate_logits);
   g_slots[dev][vi].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Single-pass workgroup slots per device (CUs x resident workgroups per CU),
+// read once per (device, gate variant).
+std::atomic<int> g_fused_slots[kMaxDevices][2];
+int fused_slots(int dev, bool gate_logits) {
+  if (dev < 0 || dev >= kMaxDevices) return 256;
+  int n = g_fused_slots[dev][gate_logits ? 1 : 0].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  n = cus * gla::fused_blocks_per_cu(gate_logits);
+  g_fused_slots[dev][gate_logits ? 1 : 0].store(n, std::memory_order_relaxed);
   return n;
 }
 
@@ -252,18 +309,28 @@ int forward(gla::Dtype dt, size_t esize, const void* q, const void* k, const voi
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return GLA_ERR_HIP;
   const int mode = g_fwd_mode.load(std::memory_order_relaxed);
-  const int slots = output_slots(dev, dt, d_k, d_v, ex.gate_logits);
   int span_chunks = 0;
-  if (mode != GLA_FWD_THREE_PASS && span_override() == 0 && gla::has_two_pass(dt, d_k, d_v))
-    span_chunks = plan_two_pass(BH, n_chunks, slots, mode == GLA_FWD_TWO_PASS);
-  const bool two_pass = span_chunks > 0;
-  if (!two_pass) span_chunks = plan_span_chunks(BH, n_chunks, slots);
+  bool fused = false, two_pass = false;
+  if (mode == GLA_FWD_SINGLE_PASS && span_override() == 0 && gla::has_fused(dt, d_k, d_v)) {
+    // single pass: every span's workgroup resident at once keeps the
+    // look-back short
+    span_chunks = plan_span_chunks(BH, n_chunks, fused_slots(dev, ex.gate_logits));
+    fused = true;
+  }
+  if (!fused) {
+    const int slots = output_slots(dev, dt, d_k, d_v, ex.gate_logits);
+    if (mode != GLA_FWD_THREE_PASS && mode != GLA_FWD_SINGLE_PASS && span_override() == 0 &&
+        gla::has_two_pass(dt, d_k, d_v))
+      span_chunks = plan_two_pass(BH, n_chunks, slots, mode == GLA_FWD_TWO_PASS);
+    two_pass = span_chunks > 0;
+    if (!two_pass) span_chunks = plan_span_chunks(BH, n_chunks, slots);
+  }
   const int n_spans = (n_chunks + span_chunks - 1) / span_chunks;
-  if (BH * n_spans > (1LL << 31) - 1) return GLA_ERR_SHAPE;
+  if (BH * n_spans > (1LL << 31) - 1 - gla::kSyncFlags) return GLA_ERR_SHAPE;
   if (plan_only != nullptr) {
     plan_only[0] = span_chunks;
     plan_only[1] = n_spans;
-    plan_only[2] = two_pass ? 2 : n_spans > 1 ? 3 : 1;
+    plan_only[2] = fused ? 1 : two_pass ? 2 : n_spans > 1 ? 3 : 1;
     return GLA_OK;
   }
 
@@ -290,7 +357,15 @@ int forward(gla::Dtype dt, size_t esize, const void* q, const void* k, const voi
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   WsLease ws;
-  if (n_spans > 1) {
+  if (fused) {
+    // span summaries (gate product + state) and one hand-off word per span
+    const size_t agg_floats = (size_t)BH * n_spans * gla::kAggFloats;
+    if (ws.acquire(st, agg_floats * sizeof(float), gla::kSyncFlags + (size_t)BH * n_spans) !=
+        hipSuccess)
+      return GLA_ERR_HIP;
+    p.agg = static_cast<float*>(ws.ptr());
+    p.sync = ws.sync();
+  } else if (n_spans > 1) {
     const size_t state_elems = (size_t)BH * n_spans * d_k * d_v;
     const size_t gate_elems = (size_t)BH * n_spans * d_k;
     if (ws.acquire(st, (state_elems + gate_elems) * sizeof(float)) != hipSuccess) return GLA_ERR_HIP;
@@ -299,8 +374,9 @@ int forward(gla::Dtype dt, size_t esize, const void* q, const void* k, const voi
   }
   const hipEvent_t* ev = t_events_set ? t_events : nullptr;
   t_events_set = false;
-  const hipError_t e = two_pass ? gla::launch_forward_two_pass(ex.gate_logits, p, st, ev)
-                                : gla::launch_forward(dt, d_k, d_v, ex.gate_logits, p, st, ev);
+  const hipError_t e = fused      ? gla::launch_forward_fused(ex.gate_logits, p, st, ev)
+                       : two_pass ? gla::launch_forward_two_pass(ex.gate_logits, p, st, ev)
+                                  : gla::launch_forward(dt, d_k, d_v, ex.gate_logits, p, st, ev);
   if (ws.finish() != hipSuccess) return GLA_ERR_HIP;
   return e == hipSuccess ? GLA_OK : GLA_ERR_HIP;
 }
@@ -658,7 +734,8 @@ int gla_plan_spans(int use_f32, int B, int heads, int H, int W, int d_k, int d_v
 }
 
 int gla_set_forward_mode(int mode) {
-  if (mode != GLA_FWD_AUTO && mode != GLA_FWD_THREE_PASS && mode != GLA_FWD_TWO_PASS)
+  if (mode != GLA_FWD_AUTO && mode != GLA_FWD_THREE_PASS && mode != GLA_FWD_TWO_PASS &&
+      mode != GLA_FWD_SINGLE_PASS)
     return GLA_ERR_SHAPE;
   g_fwd_mode.store(mode, std::memory_order_relaxed);
   return GLA_OK;
@@ -714,6 +791,7 @@ int gla_release_workspaces(void) {
       for (const WsEntry& w : g_ws) {
         if (w.dev != devs[i]) continue;
         if (w.ptr != nullptr && hipFree(w.ptr) != hipSuccess) status = GLA_ERR_HIP;
+        if (w.sync != nullptr && hipFree(w.sync) != hipSuccess) status = GLA_ERR_HIP;
         if (hipEventDestroy(w.done) != hipSuccess) status = GLA_ERR_HIP;
       }
       for (const auto& r : g_ws_retired)

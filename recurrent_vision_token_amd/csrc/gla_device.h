@@ -80,6 +80,13 @@ __host__ __device__ constexpr int vmcnt_lgkm0_imm(int n) {
 __device__ __forceinline__ void dma16(rsrc_t src, f16* block, uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void_t*)block, 16, off, 0, 0, 0);
 }
+// The same with a cache policy: AUX bit 1 marks the data non-temporal (read
+// for the last time; the caches need not keep it).
+constexpr int kAuxNT = 2;
+template <int AUX>
+__device__ __forceinline__ void dma16p(rsrc_t src, f16* block, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void_t*)block, 16, off, 0, 0, AUX);
+}
 
 // Transposed read of the 16 x 16 block at (row0, col0) of a swizzled tile
 // (ds_read_b64_tr_b16): lane (i, g) = (lane % 16, lane / 16) receives rows

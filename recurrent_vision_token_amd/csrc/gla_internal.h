@@ -37,7 +37,32 @@ struct FwdParams {
   float* adj_gate;      // [BH][adj_slots][d_k]
   const float* adj_initial;  // the final-state gradient (scan start), may be null
   int spans_per_wg;     // spans streamed by one workgroup of the summaries kernel
+  // single-pass forward: hand-off words and span aggregates
+  unsigned int* sync;   // [0] ticket, [1] finished workgroups, [2] epoch, [3] error bits,
+                        // then one ready flag per (batch*head, span) from word kSyncFlags on
+  float* agg;           // [BH][n_spans][64 + d_k * d_v]: gate product, then state
 };
+
+// Single-pass forward (float16, d_k = d_v = 64): one kernel; each workgroup
+// summarises its span, publishes the summary, folds the summaries of the
+// earlier spans of its sequence into its entry state as soon as they are
+// published, then computes the span's outputs.  Needs p.sync (kSyncFlags +
+// B*heads*n_spans words, zero before first use and left consistent by every
+// call) and p.agg (B*heads*n_spans*kAggFloats floats).  events: null or six
+// hipEvent_t; pair 2 brackets the kernel, pairs 0 and 1 are recorded back to
+// back.
+constexpr int kSyncFlags = 64;
+constexpr int kAggFloats = 64 + 64 * 64;
+bool has_fused(Dtype dt, int d_k, int d_v);
+int fused_blocks_per_cu(bool gate_logits);
+hipError_t launch_forward_fused(bool gate_logits, const FwdParams& p, hipStream_t stream,
+                                hipEvent_t const* events);
+// Error bits a single-pass call left in its hand-off words (bit 0: a wait
+// for an earlier span's summary timed out).
+constexpr unsigned int kSyncErrTimeout = 1u;
+// Zero `words` 32-bit words at p on `stream` with a kernel (usable under
+// stream capture, where a memset node is avoided).
+hipError_t launch_zero_words(unsigned int* p, size_t words, hipStream_t stream);
 
 // Multiply-shift constants for dividing t < 2^31 by d >= 1:
 // t / d == (umulhi(t, m) + t) >> s.

@@ -734,29 +734,6 @@ __global__ __launch_bounds__(kThreads) void chunk_output_kernel(FwdParams p) {
 //  * keys are pre-scaled into the variants the causal score tiles need, so the
 //    score MFMAs read unscaled operands.
 
-__device__ __forceinline__ float row_bcast15(float x) {
-  // every lane of a 16-lane row receives the row's lane 15 value
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x15F,
-                                                             0xF, 0xF, false));
-}
-
-
-// log2(e) split into two binary16 values whose sum is log2(e) to ~1e-7.
-constexpr float kLog2eHi = 1.4423828125f;          // fp16(log2 e)
-constexpr float kLog2eLo = 1.4426950408889634f - 1.4423828125f;
-
-
-// Constant 16x16x16 MFMA B operand, lane (n, g) holding rows 4g..4g+3 of
-// column n: U[s][t] = (s <= t) * v.
-__device__ __forceinline__ f16x4 upper_incl(float v) {
-  const int lane = threadIdx.x & 63, n16 = lane & 15, g = lane >> 4;
-  f16x4 r;
-#pragma unroll
-  for (int u = 0; u < 4; ++u) r[u] = (f16)((4 * g + u <= n16) ? v : 0.f);
-  return r;
-}
-
-
 // ---------------------------------------------------------------------------
 // Output kernel, float16.  The span is walked in 32-token steps (two 16-token
 // sub-blocks).  q, k, log-alpha and v of a step land row-major in LDS straight
@@ -784,33 +761,6 @@ constexpr int kStep = 32;
 __device__ __forceinline__ int qt_slot(int d) {
   const int r = d & 31;
   return (d & ~31) + (r < 16 ? 2 * r : 2 * (r - 16) + 4);
-}
-
-// Fused gate activation: log alpha = logsigmoid(z) / tau from gate logits z,
-// as min(z, 0) - ln(1 + e^{-|z|}) (no overflow for any z), with ln(1 + t) by
-// its series below t = 1/64, where 1 + t would drop t's low bits.
-__device__ __forceinline__ float logsigmoid_scaled(float z, float inv_tau) {
-  const float t = exp2_fast(-fabsf(z) * 1.4426950408889634f);
-  const float series = t * (1.f - t * (0.5f - t * (1.f / 3.f)));
-  const float l = t < 0.015625f ? series : __builtin_amdgcn_logf(1.f + t) * 0.6931471805599453f;
-  return (fminf(z, 0.f) - l) * inv_tau;
-}
-// Log-alpha of a transposed 16 x 16 read (lane (i, g): rows row0 + 4g + u):
-// the tile value itself, or with GATE the activation of the logits there.
-// Rows at or past `valid` (zero fills) must not decay, so they get 0 rather
-// than logsigmoid(0).
-template <bool GATE>
-__device__ __forceinline__ f16x4 log_alpha_of(f16x4 x, float inv_tau, int row0, int valid) {
-  if constexpr (!GATE) {
-    return x;
-  } else {
-    const int g = (threadIdx.x & 63) >> 4;
-    f32x4 r;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      r[u] = (row0 + 4 * g + u < valid) ? logsigmoid_scaled((float)x[u], inv_tau) : 0.f;
-    return to_f16(r);
-  }
 }
 
 template <int DK, int DV>

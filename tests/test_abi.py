@@ -151,9 +151,9 @@ def test_plan_forward_argument_errors():
 def test_forward_mode_setter():
     # a host-only setting: no HIP call, so this runs without a device
     lib = _lib.load()
-    for bad in (-1, 3, 99):
+    for bad in (-1, 4, 99):
         assert lib.gla_set_forward_mode(bad) == -2
-    for mode in ("three_pass", "two_pass", "auto"):
+    for mode in ("three_pass", "two_pass", "single_pass", "auto"):
         _lib.set_forward_mode(mode)
     with pytest.raises(ValueError):
         _lib.set_forward_mode("single")

@@ -1,0 +1,273 @@
+"""GPU parity of the single-pass forward path against the oracle.
+
+The single-pass path (one kernel: each workgroup summarises its span,
+publishes the summary, folds the published summaries of the earlier spans of
+its sequence into its entry state, then writes its outputs) is the automatic
+choice for float16 sequences with d_k = d_v = 64 that split into spans;
+gla_set_forward_mode forces it.  Every case is held to the float16 bar of the
+spec tolerance against the oracle: odd and degenerate grids in every
+direction, the configured workloads at full size, the extended entry, the
+state updated in place, strong forgetting (the exact token-by-token steps),
+many calls on one stream, sequences that need several rounds of workgroups,
+and graph replay.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import gla_forward, log_alpha_from_logits
+from recurrent_vision_token_amd.workloads import WORKLOADS, make_inputs, workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+FP16_REL, FP16_MAX = 5e-3, 2e-2
+
+
+def _torch():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    return torch
+
+
+class forward_mode:
+    """Force a forward path for the block, then go back to automatic."""
+
+    def __init__(self, mode):
+        self.mode = mode
+
+    def __enter__(self):
+        from recurrent_vision_token_amd import set_forward_mode
+        set_forward_mode(self.mode)
+
+    def __exit__(self, *exc):
+        from recurrent_vision_token_amd import set_forward_mode
+        set_forward_mode("auto")
+
+
+def dev(*xs):
+    torch = _torch()
+    return [torch.from_numpy(np.ascontiguousarray(x)).to("cuda:0") for x in xs]
+
+
+def host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def check(got, ref, what):
+    assert np.all(np.isfinite(got)), what + ": non-finite values"
+    err = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
+    mx = np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30)
+    assert err <= FP16_REL and mx <= FP16_MAX, "%s: rel %.3g max %.3g" % (what, err, mx)
+
+
+def fwd(inputs, d, **kw):
+    from recurrent_vision_token_amd import gla_chunk_fwd
+    out, fs = gla_chunk_fwd(*dev(*inputs), d, **kw)
+    _torch().cuda.synchronize()
+    return host(out), host(fs)
+
+
+def fwd_ex(q, k, v, gate, d, gate_mode, init, tau=16.0):
+    from recurrent_vision_token_amd import gla_chunk_fwd_ex
+    torch = _torch()
+    tq, tk, tv, tg = dev(q, k, v, gate)
+    ti = dev(init)[0] if init is not None else None
+    out, fs = gla_chunk_fwd_ex(tq, tk, tv, tg, d, gate_mode=gate_mode, tau=tau, initial_state=ti)
+    torch.cuda.synchronize()
+    return host(out), host(fs)
+
+
+def test_plan():
+    from recurrent_vision_token_amd._lib import plan_forward
+    print("single pass: plan", flush=True)
+    # forced: the configured float16 d = 64 workloads run as one kernel
+    with forward_mode("single_pass"):
+        for (B, heads, H, W) in ((1, 12, 40, 40), (1, 16, 48, 48), (1, 12, 128, 128)):
+            sc, ns, kern = plan_forward("fp16", B, heads, H, W, 64, 64)
+            assert kern == 1 and ns > 1, (B, heads, H, W, sc, ns, kern)
+    # other head dims and float32 keep their paths
+    assert plan_forward("fp16", 32, 16, 64, 64, 128, 64)[2] in (1, 3)
+    assert plan_forward("fp32", 1, 12, 40, 40, 64, 64)[2] == 3
+    with forward_mode("single_pass"):
+        # forced: sequences that fill the device alone run unsplit in one kernel
+        sc, ns, kern = plan_forward("fp16", 64, 16, 40, 40, 64, 64)
+        assert (ns, kern) == (1, 1)
+
+
+@pytest.mark.parametrize("d", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("H,W", [(7, 9), (21, 29), (40, 40), (9, 113), (1, 37), (29, 1), (1, 1)])
+def test_single_pass_against_oracle(H, W, d):
+    B = 4 if d == 4 else 1
+    print("single pass: %dx%d dir %d" % (H, W, d), flush=True)
+    x = make_inputs(B, 3, H, W, 64, 64, "fp16", 1.0, seed=11 * H + W + d)
+    with forward_mode("single_pass"):
+        o, s = fwd(x, d)
+    ro, rs = gla_forward(*x, d)
+    check(o, ro, "out")
+    check(s, rs, "final_state")
+
+
+@pytest.mark.parametrize("name", ["gtr1.6k", "img768", "hires16.4k"])
+def test_workloads_full_size(name):
+    wl = WORKLOADS[name]
+    print("single pass: workload %s" % name, flush=True)
+    calls = list(zip(wl.seeds, wl.dirs))[:4]
+    for seed, d in calls:
+        x = workload_inputs(wl, seed)
+        ro, rs = gla_forward(*x, d)
+        with forward_mode("single_pass"):
+            o, s = fwd(x, d)
+        check(o, ro, "%s dir %d out" % (name, d))
+        check(s, rs, "%s dir %d final_state" % (name, d))
+
+
+def test_extended_entry():
+    # fused gate activation and an initial state
+    print("single pass: extended entry", flush=True)
+    rng = np.random.default_rng(21)
+    q, k, v, _ = make_inputs(2, 3, 33, 27, 64, 64, "fp16", 1.0, seed=22)
+    z = (rng.standard_normal(q.shape) * 2.0).astype(np.float16)
+    init = (rng.standard_normal((2, 3, 64, 64)) * 0.5).astype(np.float32)
+    la = log_alpha_from_logits(z, 16.0)
+    for d in (0, 2, 4):
+        with forward_mode("single_pass"):
+            o, s = fwd_ex(q, k, v, z, d, "logits", init)
+        ro, rs = gla_forward(q, k, v, la, d, initial_state=init)
+        check(o, ro, "ex out dir %d" % d)
+        check(s, rs, "ex final_state dir %d" % d)
+
+
+def test_state_updated_in_place():
+    # final_state and initial_state the same buffer, several spans per sequence
+    from recurrent_vision_token_amd import gla_chunk_fwd_ex
+    torch = _torch()
+    print("single pass: state in place", flush=True)
+    rng = np.random.default_rng(23)
+    q, k, v, la = make_inputs(1, 3, 64, 64, 64, 64, "fp16", 1.0, seed=24)
+    init = (rng.standard_normal((1, 3, 64, 64)) * 0.5).astype(np.float32)
+    ro, rs = gla_forward(q, k, v, la, 1, initial_state=init)
+    tq, tk, tv, tl, ts = dev(q, k, v, la, init)
+    with forward_mode("single_pass"):
+        out, fs = gla_chunk_fwd_ex(tq, tk, tv, tl, 1, initial_state=ts, final_state=ts)
+    torch.cuda.synchronize()
+    check(host(out), ro, "out")
+    check(host(ts), rs, "state in place")
+
+
+@pytest.mark.parametrize("case", ["la_minus2", "logits_minus30", "alpha_to_zero", "mixed"])
+def test_strong_forgetting(case):
+    # decays far outside the scaled-operand range take the exact steps
+    print("single pass: strong forgetting %s" % case, flush=True)
+    B, heads, H, W = 1, 2, 19, 23
+    q, k, v, la = make_inputs(B, heads, H, W, 64, 64, "fp16", 1.0, seed=31)
+    rng = np.random.default_rng(32)
+    init = (rng.standard_normal((B, heads, 64, 64)) * 0.25).astype(np.float32)
+    for d in (0, 3):
+        if case == "logits_minus30":
+            z = np.full(q.shape, -30.0, dtype=np.float16)
+            with forward_mode("single_pass"):
+                o, s = fwd_ex(q, k, v, z, d, "logits", init)
+            ref_la = log_alpha_from_logits(z, 16.0)
+        else:
+            if case == "la_minus2":
+                gl = np.full(q.shape, -2.0, dtype=np.float16)
+            elif case == "alpha_to_zero":
+                gl = np.full(q.shape, -1.0e4, dtype=np.float16)
+            else:
+                # strong decay in a few key dims of some rows only
+                gl = la.copy()
+                gl[:, :, ::3, :, 5] = -3.0
+                gl[:, :, 7, :, 40:44] = -60.0
+            with forward_mode("single_pass"):
+                o, s = fwd_ex(q, k, v, gl, d, "log_alpha", init)
+            ref_la = gl
+        ro, rs = gla_forward(q, k, v, ref_la, d, initial_state=init)
+        check(o, ro, "%s dir %d out" % (case, d))
+        check(s, rs, "%s dir %d final_state" % (case, d))
+
+
+def test_many_calls_one_stream():
+    # many calls of two shapes in a row on one stream, mixed with three-pass
+    # calls; every single-pass result equals that call's own first result
+    from recurrent_vision_token_amd import gla_chunk_fwd, release_workspaces
+    torch = _torch()
+    print("single pass: many calls", flush=True)
+    shapes = [(1, 12, 40, 40, 1), (2, 5, 70, 31, 2)]
+    inputs = [dev(*make_inputs(B, h, H, W, 64, 64, "fp16", 1.0, seed=s)) for B, h, H, W, s in shapes]
+    ref = []
+    for i, x in enumerate(inputs):
+        release_workspaces()
+        with forward_mode("single_pass"):
+            o, s = gla_chunk_fwd(*x, i)
+        torch.cuda.synchronize()
+        ref.append((o.clone(), s.clone()))
+    for i, (B, h, H, W, s) in enumerate(shapes):
+        ro, rs = gla_forward(*make_inputs(B, h, H, W, 64, 64, "fp16", 1.0, seed=s), i)
+        check(host(ref[i][0]), ro, "reference out %d" % i)
+        check(host(ref[i][1]), rs, "reference final_state %d" % i)
+    outs = []
+    for n in range(40):
+        i = (n // 3) % 2
+        mode = "three_pass" if n % 7 == 6 else "single_pass"
+        with forward_mode(mode):
+            o, s = gla_chunk_fwd(*inputs[i], i)
+        outs.append((n, i, mode, o, s))
+    torch.cuda.synchronize()
+    for n, i, mode, o, s in outs:
+        if mode == "single_pass":
+            assert torch.equal(o, ref[i][0]) and torch.equal(s, ref[i][1]), (n, i)
+        else:
+            check(host(o), host(ref[i][0]), "three-pass call %d" % n)
+
+
+def test_more_workgroups_than_the_device_holds():
+    # 64 x 16 sequences of 4 chunks, forced single pass: 1024 unsplit
+    # workgroups in several rounds; sampled sequences against the oracle
+    print("single pass: many sequences", flush=True)
+    B, heads, H, W = 64, 16, 16, 16
+    x = make_inputs(B, heads, H, W, 64, 64, "fp16", 1.0, seed=41)
+    with forward_mode("single_pass"):
+        o, s = fwd(x, 4)
+    for b, h in ((0, 0), (13, 7), (63, 15)):
+        xs = [t[b:b + 1, h:h + 1] for t in x]
+        ro, rs = gla_forward(*xs, b % 4)
+        check(o[b:b + 1, h:h + 1], ro, "out b%d h%d" % (b, h))
+        check(s[b:b + 1, h:h + 1], rs, "final_state b%d h%d" % (b, h))
+
+
+def test_graph_replay():
+    torch = _torch()
+    from recurrent_vision_token_amd import gla_chunk_fwd
+    print("single pass: graph replay", flush=True)
+    x = dev(*make_inputs(1, 12, 40, 40, 64, 64, "fp16", 1.0, seed=51))
+    with forward_mode("single_pass"):
+        o_ref, s_ref = gla_chunk_fwd(*x, 2)
+        torch.cuda.synchronize()
+        o_ref, s_ref = o_ref.clone(), s_ref.clone()
+        stream = torch.cuda.Stream()
+        out = torch.empty_like(o_ref)
+        fs = torch.empty_like(s_ref)
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            gla_chunk_fwd(*x, 2, out=out, final_state=fs, stream=stream.cuda_stream)  # warm-up
+        stream.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            gla_chunk_fwd(*x, 2, out=out, final_state=fs, stream=stream.cuda_stream)
+        for rep in range(4):
+            out.zero_()
+            fs.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, o_ref) and torch.equal(fs, s_ref), rep
+            gla_chunk_fwd(*x, 0)                         # eager work between replays
+            torch.cuda.synchronize()
+
+
+def test_deterministic():
+    print("single pass: deterministic", flush=True)
+    x = make_inputs(1, 12, 128, 128, 64, 64, "fp16", 2.0, seed=3)
+    with forward_mode("single_pass"):
+        a = fwd(x, 2)
+        b = fwd(x, 2)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
