@@ -612,8 +612,13 @@ def plan_of(wl):
     return ns, kernels
 
 
+TRAFFIC_NOTE = ("L2-miss bytes per launch: FETCH_SIZE + WRITE_SIZE, scaled against a copy "
+                "kernel of known size; misses served by the Infinity Cache count too")
+
+
 def traffic_from_profiles(wl_name, kernel):
-    """HBM bytes per launch from committed counter runs, if they match this source."""
+    """L2-miss bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-scaled) from
+    committed counter runs, if they match this source."""
     path = os.path.join(ROOT, "profiles", "traffic_%s.json" % wl_name)
     if not os.path.exists(path):
         return None
@@ -766,7 +771,10 @@ def summarize(wl, ms_step, mean, ext=False):
         kb["span_scan" if kernels == 3 else "chunk_output"] += wl.B * wl.heads * wl.d_k * wl.d_v * 4
     present = [k for k in kb if mean[k] > 0]
     dom = max(present, key=lambda k: mean[k])
-    ach = kb[dom] / (mean[dom] * 1e-3) / 1e9
+    # the call's method bytes over the dominant kernel's launch (one launch
+    # covers every token and head of the call), and that kernel's own bytes
+    ach = alg["bytes"] / (mean[dom] * 1e-3) / 1e9
+    own = kb[dom] / (mean[dom] * 1e-3) / 1e9
     wall_call_ms = ms_step / ncall
     path_gbps = alg["bytes"] / (wall_call_ms * 1e-3) / 1e9
     out = {
@@ -775,8 +783,11 @@ def summarize(wl, ms_step, mean, ext=False):
         "dominant": dom,
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": traffic_from_profiles(wl.name, dom),
-                     "kernel": dom, "algorithmic_bytes_per_launch": kb[dom],
-                     "avg_launch_us": round(mean[dom] * 1e3, 2)},
+                     "traffic_counts": TRAFFIC_NOTE,
+                     "kernel": dom, "algorithmic_bytes_per_launch": alg["bytes"],
+                     "avg_launch_us": round(mean[dom] * 1e3, 2),
+                     "kernel_bytes_per_launch": kb[dom],
+                     "dominant_kernel_frac": round(own / HBM_PEAK_GBPS, 4)},
         # whole call at the timed loop's wall-clock rate (the instrumented pass
         # spaces its launches out: event_us_per_call is first summary start to
         # last output stop there)
@@ -826,7 +837,8 @@ def counters_to_traffic(fetch_dir, write_dir, copy_mb, workload, only=()):
     copy_bytes = copy_mb << 20
     f_scale = copy_bytes / (f["copy"] * 1024.0)
     w_scale = copy_bytes / (w["copy"] * 1024.0)
-    lines = ["| kernel | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | HBM read (MB) | HBM write (MB) | total (MB) |",
+    lines = ["| kernel | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | L2-miss read (MB) | L2-miss write (MB) | "
+             "total (MB) |",
              "|---|---|---|---|---|---|"]
     recs = {}
     for k in KERNEL_NAMES:

@@ -120,6 +120,32 @@ def _check(q, k, v, log_alpha):
     return B, heads, H, W, d_k, d_v
 
 
+def _check_out(t, name, shape, dtype, dev):
+    """Raise ValueError unless a caller-supplied output tensor fits the call."""
+    import torch
+
+    if (not isinstance(t, torch.Tensor) or t.dtype != dtype or tuple(t.shape) != tuple(shape)
+            or not t.is_contiguous() or t.device != dev):
+        raise ValueError("%s must be a contiguous %s tensor of shape %s on %s"
+                         % (name, str(dtype).replace("torch.", ""), list(shape), dev))
+
+
+def _outputs(B, heads, H, W, d_k, d_v, dt, dev, out, final_state, want_final_state):
+    """Check or allocate the forward outputs (out, final_state)."""
+    import torch
+
+    if out is None:
+        out = torch.empty((B, heads, H, W, d_v), dtype=dt, device=dev)
+    else:
+        _check_out(out, "out", (B, heads, H, W, d_v), dt, dev)
+    if final_state is None:
+        if want_final_state:
+            final_state = torch.empty((B, heads, d_k, d_v), dtype=torch.float32, device=dev)
+    else:
+        _check_out(final_state, "final_state", (B, heads, d_k, d_v), torch.float32, dev)
+    return out, final_state
+
+
 def gla_chunk_fwd(q, k, v, log_alpha, scan_dir, chunk=64, out=None, final_state=None,
                   want_final_state=True, stream=None):
     """Chunkwise GLA forward on device tensors.
@@ -133,10 +159,8 @@ def gla_chunk_fwd(q, k, v, log_alpha, scan_dir, chunk=64, out=None, final_state=
     B, heads, H, W, d_k, d_v = _check(q, k, v, log_alpha)
     dt = q.dtype
     dev = q.device
-    if out is None:
-        out = torch.empty((B, heads, H, W, d_v), dtype=dt, device=dev)
-    if final_state is None and want_final_state:
-        final_state = torch.empty((B, heads, d_k, d_v), dtype=torch.float32, device=dev)
+    out, final_state = _outputs(B, heads, H, W, d_k, d_v, dt, dev, out, final_state,
+                                want_final_state)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
     fs_ptr = final_state.data_ptr() if final_state is not None else None
@@ -173,10 +197,8 @@ def gla_chunk_fwd_ex(q, k, v, gate, scan_dir, gate_mode="log_alpha", tau=16.0,
             raise ValueError("initial_state must be contiguous float32 [B, heads, d_k, d_v] "
                              "on the tensors' device")
         init_ptr = initial_state.data_ptr()
-    if out is None:
-        out = torch.empty((B, heads, H, W, d_v), dtype=q.dtype, device=dev)
-    if final_state is None and want_final_state:
-        final_state = torch.empty((B, heads, d_k, d_v), dtype=torch.float32, device=dev)
+    out, final_state = _outputs(B, heads, H, W, d_k, d_v, q.dtype, dev, out, final_state,
+                                want_final_state)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
     fs_ptr = final_state.data_ptr() if final_state is not None else None
@@ -224,6 +246,8 @@ def spatial_swiglu(gate, value, weight, bias=None, out=None, stream=None):
         raise ValueError("bias must be contiguous [C]")
     if out is None:
         out = torch.empty((B, H, W, C), dtype=torch.float16, device=gate.device)
+    else:
+        _check_out(out, "out", (B, H, W, C), torch.float16, gate.device)
     if stream is None:
         stream = torch.cuda.current_stream(gate.device).cuda_stream
     rc = raw_call_swiglu(gate.data_ptr(), value.data_ptr(), ld, weight.data_ptr(),
@@ -314,8 +338,13 @@ def saga_fwd(q, k, v, alpha, beta, out=None, kv=None, want_kv=False, stream=None
     dev = q.device
     if out is None:
         out = torch.empty((B, heads, N, d_v), dtype=torch.float16, device=dev)
-    if kv is None and want_kv:
-        kv = torch.empty((B, heads, d_k, d_v), dtype=torch.float32, device=dev)
+    else:
+        _check_out(out, "out", (B, heads, N, d_v), torch.float16, dev)
+    if kv is None:
+        if want_kv:
+            kv = torch.empty((B, heads, d_k, d_v), dtype=torch.float32, device=dev)
+    else:
+        _check_out(kv, "kv", (B, heads, d_k, d_v), torch.float32, dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
     rc = raw_call_saga(q.data_ptr(), k.data_ptr(), v.data_ptr(), alpha.data_ptr(), beta.data_ptr(),
@@ -336,7 +365,7 @@ def release_workspaces():
 
 def set_forward_mode(mode):
     """Choose the float16 forward path for later calls, process-wide: "auto",
-    "three_pass" or "two_pass" (see gla_set_forward_mode)."""
+    "three_pass", "two_pass" or "single_pass" (see gla_set_forward_mode)."""
     if mode not in FORWARD_MODES:
         raise ValueError("mode must be one of %s" % sorted(FORWARD_MODES))
     rc = load().gla_set_forward_mode(FORWARD_MODES[mode])

@@ -317,10 +317,15 @@ int forward(gla::Dtype dt, size_t esize, const void* q, const void* k, const voi
     span_chunks = plan_span_chunks(BH, n_chunks, fused_slots(dev, ex.gate_logits));
     fused = true;
   }
+  // every two-pass output workgroup reads the initial state, and the last
+  // span's writes the final state with no order between them: an in-place
+  // update (same pointer) takes three passes, where the reads come first
+  const bool in_place =
+      ex.initial_state != nullptr && (const void*)final_state == (const void*)ex.initial_state;
   if (!fused) {
     const int slots = output_slots(dev, dt, d_k, d_v, ex.gate_logits);
-    if (mode != GLA_FWD_THREE_PASS && mode != GLA_FWD_SINGLE_PASS && span_override() == 0 &&
-        gla::has_two_pass(dt, d_k, d_v))
+    if (mode != GLA_FWD_THREE_PASS && mode != GLA_FWD_SINGLE_PASS && !in_place &&
+        span_override() == 0 && gla::has_two_pass(dt, d_k, d_v))
       span_chunks = plan_two_pass(BH, n_chunks, slots, mode == GLA_FWD_TWO_PASS);
     two_pass = span_chunks > 0;
     if (!two_pass) span_chunks = plan_span_chunks(BH, n_chunks, slots);

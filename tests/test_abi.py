@@ -82,6 +82,29 @@ def test_argument_errors(dtype):
     assert call(dtype, fs=OUT + 1024) == -6                  # final_state inside out
 
 
+def test_binding_checks_caller_outputs():
+    # caller-supplied outputs are checked for shape, dtype, layout and device
+    # before any pointer reaches the library (host-only helpers)
+    dev = torch.device("cpu")
+    good = torch.empty(2, 3, 4, 5, 8, dtype=torch.float16)
+    _lib._check_out(good, "out", (2, 3, 4, 5, 8), torch.float16, dev)
+    bad = [good.float(),                                      # dtype
+           good[..., :4],                                     # shape
+           torch.empty(2, 3, 4, 8, 5, dtype=torch.float16).transpose(3, 4),  # not contiguous
+           torch.empty(2, 3, 4, 5, 8, dtype=torch.float16, device="meta"),   # device
+           None]
+    for t in bad:
+        with pytest.raises(ValueError):
+            _lib._check_out(t, "out", (2, 3, 4, 5, 8), torch.float16, dev)
+    out, fs = _lib._outputs(2, 3, 4, 5, 64, 8, torch.float16, dev, good, None, False)
+    assert out is good and fs is None
+    with pytest.raises(ValueError, match="final_state"):
+        _lib._outputs(2, 3, 4, 5, 64, 8, torch.float16, dev, good,
+                      torch.empty(2, 3, 64, 8, dtype=torch.float16), True)
+    with pytest.raises(ValueError, match="out"):
+        _lib._outputs(2, 3, 4, 5, 64, 8, torch.float16, dev, good[:1], None, True)
+
+
 def call_ex(gate_mode=1, tau=16.0, init=None, fs=FS, out=OUT, **kw):
     a = dict(q=Q, k=K, v=V, la=LA, scan_dir=0, B=1, heads=2, H=8, W=8, d_k=64, d_v=64, chunk=64)
     a.update(kw)

@@ -253,3 +253,28 @@ def test_forced_two_pass_more_workgroups_than_the_device_holds():
         ro, rs = gla_forward(*xs, b % 4)
         check(o[b:b + 1, h:h + 1], ro, "out b%d h%d" % (b, h))
         check(s[b:b + 1, h:h + 1], rs, "final_state b%d h%d" % (b, h))
+
+
+def test_in_place_state_update_with_more_workgroups_than_the_device_holds():
+    # final_state == initial_state: every two-pass output workgroup reads the
+    # initial state while the last span's workgroup writes the final state, so
+    # an in-place call takes three passes even when two are forced; checked on
+    # 1664 output workgroups' worth of sequences, sampled against the oracle
+    from recurrent_vision_token_amd import gla_chunk_fwd_ex
+    print("two pass: in-place state, many sequences", flush=True)
+    torch = _torch()
+    B, heads, H, W = 8, 16, 40, 40
+    x = make_inputs(B, heads, H, W, 64, 64, "fp16", 1.0, seed=93)
+    init = (np.random.default_rng(94).standard_normal((B, heads, 64, 64)) * 0.5).astype(np.float32)
+    with forward_mode("two_pass"):
+        assert plan(B, heads, H, W) == (2, 13)
+        tq, tk, tv, tl, ts = dev(*x, init)
+        out, fs = gla_chunk_fwd_ex(tq, tk, tv, tl, 4, initial_state=ts, final_state=ts)
+        torch.cuda.synchronize()
+    assert fs.data_ptr() == ts.data_ptr()
+    o, s = host(out), host(ts)
+    for b, h in ((0, 0), (2, 5), (5, 9), (7, 15)):
+        xs = [t[b:b + 1, h:h + 1] for t in x]
+        ro, rs = gla_forward(*xs, b % 4, initial_state=init[b:b + 1, h:h + 1])
+        check(o[b:b + 1, h:h + 1], ro, "in-place out b%d h%d" % (b, h))
+        check(s[b:b + 1, h:h + 1], rs, "in-place final_state b%d h%d" % (b, h))

@@ -107,6 +107,56 @@ def test_two_streams_interleaved():
         assert np.array_equal(ho, ref[i][0]) and np.array_equal(hs, ref[i][1]), i
 
 
+@pytest.mark.parametrize("mode", ["auto", "single_pass"])
+def test_two_host_threads_on_one_stream(mode):
+    # the workspace cache's lock is held from a call's lookup until its last
+    # launch, so two threads' calls on one stream never interleave their
+    # launches on the stream's buffers; sizes differ, so the buffers are
+    # regrown and reused while the other thread's work is queued
+    import threading
+
+    torch = _torch()
+    from recurrent_vision_token_amd import gla_chunk_fwd, set_forward_mode
+    print("workspace: two threads, one stream, %s" % mode, flush=True)
+    cases = [FWD[0], FWD[1]]
+    inputs = [dev_tensors(*make_inputs(B, h, H, W, 64, 64, "fp16", 1.0, seed=s))
+              for (B, h, H, W, s) in cases]
+    try:
+        set_forward_mode(mode)
+        ref = []
+        for (q, k, v, la) in inputs:
+            o, s = gla_chunk_fwd(q, k, v, la, 3)
+            torch.cuda.synchronize()
+            ref.append(host(o, s))
+        st = torch.cuda.Stream()
+        results = [[], []]
+        errors = []
+
+        def worker(j):
+            try:
+                q, k, v, la = inputs[j]
+                with torch.cuda.stream(st):
+                    for _ in range(24):
+                        results[j].append(gla_chunk_fwd(q, k, v, la, 3, stream=st.cuda_stream))
+            except Exception as e:  # reported below, in the test's thread
+                errors.append(e)
+
+        threads = [threading.Thread(target=worker, args=(j,)) for j in range(2)]
+        for t in threads:
+            t.start()
+        for t in threads:
+            t.join()
+        torch.cuda.synchronize()
+    finally:
+        set_forward_mode("auto")
+    assert not errors, errors
+    for j in range(2):
+        assert len(results[j]) == 24
+        for o, s in results[j]:
+            ho, hs = host(o, s)
+            assert np.array_equal(ho, ref[j][0]) and np.array_equal(hs, ref[j][1]), cases[j]
+
+
 def test_backward_and_saga_reuse():
     torch = _torch()
     from recurrent_vision_token_amd import gla_chunk_bwd, release_workspaces, saga_fwd
