@@ -89,7 +89,9 @@ enum {
   GLA_ERR_ALIGN = -4,         /* a tensor pointer is not 16-byte aligned        */
   GLA_ERR_SCAN_DIR = -5,      /* scan_dir outside 0..4                          */
   GLA_ERR_ALIAS = -6,         /* an output overlaps another tensor              */
-  GLA_ERR_HIP = -7            /* a HIP runtime call failed while enqueueing     */
+  GLA_ERR_HIP = -7,           /* a HIP runtime call failed while enqueueing     */
+  GLA_ERR_SCRATCH = -8        /* gla_chunk_fwd_noalloc: the work split needs more
+                                 span states than its fixed scratch holds       */
 };
 
 /*
@@ -132,6 +134,37 @@ enum {
   GLA_FWD_SINGLE_PASS = 3
 };
 int gla_set_forward_mode(int mode);
+
+/*
+ * No-allocation variant of gla_chunk_fwd, for callers that cannot allocate
+ * device memory while they call (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments, layout, semantics
+ * and errors as gla_chunk_fwd, plus GLA_ERR_SCRATCH.
+ *
+ * The span states of a split sequence live in one fixed device array of
+ * GLA_NOALLOC_SCRATCH_BYTES, part of the library's device code: each device
+ * gets its own copy when the library's code is loaded there and holds it until
+ * the process ends; the call looks up the current device's copy on its first
+ * use there (hipGetSymbolAddress) and allocates and frees nothing.  The call
+ * takes the work split gla_chunk_fwd would take (gla_plan_forward), except
+ * that the single-pass mode is not used: its hand-off words would need an
+ * allocation, so under that mode the call takes the automatic choice.  The
+ * span states take B*heads*n_spans*(d_k*d_v + d_k) floats; an automatic split
+ * has at most one span per resident output workgroup, which on an MI355X
+ * stays within the array for every supported d_k, d_v.  A split that does not
+ * fit (a forced one: gla_set_forward_mode with two or three passes, or
+ * GLA_SPAN_CHUNKS) returns GLA_ERR_SCRATCH before anything is enqueued.
+ *
+ * The array is shared by every call on its device and keeps whatever the last
+ * call left; nothing in it needs to start at zero (every state is written
+ * before it is read).  Calls on one stream run in order; calls that overlap in
+ * time on one device (different streams) race on the array and their results
+ * are undefined.
+ */
+#define GLA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int gla_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* log_alpha,
+                          int scan_dir, int B, int heads, int H, int W, int d_k, int d_v,
+                          int chunk, void* out, float* final_state, void* stream);
 
 /*
  * Extended float16 entry: gla_chunk_fwd plus an initial state and a fused

@@ -16,8 +16,12 @@ GLA_OK = 0
 STATUS = {
     0: "GLA_OK", -1: "GLA_ERR_NULL", -2: "GLA_ERR_SHAPE", -3: "GLA_ERR_UNSUPPORTED",
     -4: "GLA_ERR_ALIGN", -5: "GLA_ERR_SCAN_DIR", -6: "GLA_ERR_ALIAS", -7: "GLA_ERR_HIP",
+    -8: "GLA_ERR_SCRATCH",
 }
+# size of the fixed device array of gla_chunk_fwd_noalloc (GLA_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 32 << 20
 EXPORTED = ("gla_chunk_bwd", "gla_chunk_fwd", "gla_chunk_fwd_ex", "gla_chunk_fwd_f32",
+            "gla_chunk_fwd_noalloc",
             "gla_plan_forward", "gla_plan_spans", "gla_release_workspaces",
             "gla_saga_fwd", "gla_set_forward_mode", "gla_set_kernel_events",
             "gla_spatial_swiglu", "gla_status_str", "gla_version")
@@ -49,7 +53,7 @@ def load():
     lib = ctypes.CDLL(LIB_PATH)
     vp, i = ctypes.c_void_p, ctypes.c_int
     sig = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, vp, vp]
-    for name in ("gla_chunk_fwd", "gla_chunk_fwd_f32"):
+    for name in ("gla_chunk_fwd", "gla_chunk_fwd_f32", "gla_chunk_fwd_noalloc"):
         fn = getattr(lib, name)
         fn.argtypes = sig
         fn.restype = ctypes.c_int
@@ -91,6 +95,13 @@ def raw_call(dtype, q, k, v, la, scan_dir, B, heads, H, W, d_k, d_v, chunk, out,
     lib = load()
     fn = lib.gla_chunk_fwd if dtype == "fp16" else lib.gla_chunk_fwd_f32
     return fn(q, k, v, la, scan_dir, B, heads, H, W, d_k, d_v, chunk, out, final_state, stream)
+
+
+def raw_call_noalloc(q, k, v, la, scan_dir, B, heads, H, W, d_k, d_v, chunk, out, final_state,
+                     stream):
+    """Call gla_chunk_fwd_noalloc with integer pointers; returns the status code."""
+    return load().gla_chunk_fwd_noalloc(q, k, v, la, scan_dir, B, heads, H, W, d_k, d_v, chunk,
+                                        out, final_state, stream)
 
 
 def raw_call_ex(q, k, v, gate, gate_mode, tau, initial_state, scan_dir, B, heads, H, W, d_k,
@@ -167,6 +178,32 @@ def gla_chunk_fwd(q, k, v, log_alpha, scan_dir, chunk=64, out=None, final_state=
     rc = raw_call("fp16" if dt == torch.float16 else "fp32", q.data_ptr(), k.data_ptr(),
                   v.data_ptr(), log_alpha.data_ptr(), int(scan_dir), B, heads, H, W, d_k, d_v,
                   int(chunk), out.data_ptr(), fs_ptr, stream)
+    if rc != GLA_OK:
+        raise GlaError(rc, status_str(rc))
+    return out, final_state
+
+
+def gla_chunk_fwd_noalloc(q, k, v, log_alpha, scan_dir, out, final_state=None, chunk=64,
+                          stream=None):
+    """Float16 forward through gla_chunk_fwd_noalloc (no device allocation in
+    the call): the caller passes out (float16 [B, heads, H, W, d_v]) and
+    optionally final_state (float32 [B, heads, d_k, d_v]).  Same results as
+    gla_chunk_fwd; returns (out, final_state)."""
+    import torch
+
+    B, heads, H, W, d_k, d_v = _check(q, k, v, log_alpha)
+    if q.dtype != torch.float16:
+        raise ValueError("gla_chunk_fwd_noalloc takes float16 tensors")
+    dev = q.device
+    _check_out(out, "out", (B, heads, H, W, d_v), torch.float16, dev)
+    if final_state is not None:
+        _check_out(final_state, "final_state", (B, heads, d_k, d_v), torch.float32, dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    fs_ptr = final_state.data_ptr() if final_state is not None else None
+    rc = raw_call_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), log_alpha.data_ptr(),
+                          int(scan_dir), B, heads, H, W, d_k, d_v, int(chunk), out.data_ptr(),
+                          fs_ptr, stream)
     if rc != GLA_OK:
         raise GlaError(rc, status_str(rc))
     return out, final_state

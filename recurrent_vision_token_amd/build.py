@@ -60,6 +60,7 @@ def build(verbose=False):
     g_obj = os.path.join(BUILD, "saga_kernels.o")
     b_obj = os.path.join(BUILD, "gla_bwd_kernels.o")
     f_obj = os.path.join(BUILD, "gla_fused.o")
+    n_obj = os.path.join(BUILD, "gla_noalloc.o")
     logs.append(_run([hipcc] + flags_for("gla_kernels.hip") + ["-I", INCLUDE, "-I", CSRC, "-c",
                                             os.path.join(CSRC, "gla_kernels.hip"), "-o", k_obj]))
     logs.append(_run([hipcc] + flags_for("swiglu_kernels.hip") + ["-I", INCLUDE, "-I", CSRC, "-c",
@@ -70,11 +71,13 @@ def build(verbose=False):
                                             os.path.join(CSRC, "gla_bwd_kernels.hip"), "-o", b_obj]))
     logs.append(_run([hipcc] + flags_for("gla_fused.hip") + ["-I", INCLUDE, "-I", CSRC, "-c",
                                             os.path.join(CSRC, "gla_fused.hip"), "-o", f_obj]))
+    logs.append(_run([hipcc] + flags_for("gla_noalloc.hip") + ["-I", INCLUDE, "-I", CSRC, "-c",
+                                            os.path.join(CSRC, "gla_noalloc.hip"), "-o", n_obj]))
     logs.append(_run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-D__HIP_PLATFORM_AMD__",
                       "-I", os.path.join(ROCM, "include"), "-I", INCLUDE, "-I", CSRC, "-c",
                       os.path.join(CSRC, "gla_api.cpp"), "-o", a_obj]))
     tmp = LIB + ".tmp"
-    logs.append(_run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", k_obj, s_obj, g_obj, b_obj, f_obj, a_obj,
+    logs.append(_run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", k_obj, s_obj, g_obj, b_obj, f_obj, n_obj, a_obj,
                       "-o", tmp]))
     os.replace(tmp, LIB)
     if verbose:

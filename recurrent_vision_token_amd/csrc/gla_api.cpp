@@ -256,6 +256,10 @@ struct Extras {
   bool gate_logits = false;               // `la` holds gate logits (fused activation)
   float tau = 1.f;                        // activation temperature (gate_logits only)
   const float* initial_state = nullptr;   // [B][heads][d_k][d_v], null = zero state
+  // fixed scratch instead of the workspace cache (no allocation): the
+  // current device's buffer of scratch_bytes, looked up only when used
+  void* (*scratch_of)(int dev) = nullptr;
+  size_t scratch_bytes = 0;
 };
 
 int forward(gla::Dtype dt, size_t esize, const void* q, const void* k, const void* v,
@@ -308,7 +312,11 @@ int forward(gla::Dtype dt, size_t esize, const void* q, const void* k, const voi
   const int n_chunks = (int)((T + kChunk - 1) / kChunk);
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return GLA_ERR_HIP;
-  const int mode = g_fwd_mode.load(std::memory_order_relaxed);
+  const bool no_alloc = ex.scratch_of != nullptr;
+  // the single pass needs hand-off words that start at zero, which a fixed
+  // scratch does not keep: without allocation its mode means automatic
+  int mode = g_fwd_mode.load(std::memory_order_relaxed);
+  if (no_alloc && mode == GLA_FWD_SINGLE_PASS) mode = GLA_FWD_AUTO;
   int span_chunks = 0;
   bool fused = false, two_pass = false;
   if (mode == GLA_FWD_SINGLE_PASS && span_override() == 0 && gla::has_fused(dt, d_k, d_v)) {
@@ -332,6 +340,9 @@ int forward(gla::Dtype dt, size_t esize, const void* q, const void* k, const voi
   }
   const int n_spans = (n_chunks + span_chunks - 1) / span_chunks;
   if (BH * n_spans > (1LL << 31) - 1 - gla::kSyncFlags) return GLA_ERR_SHAPE;
+  if (no_alloc && n_spans > 1 &&
+      (size_t)(BH * n_spans) * (size_t)(d_k * d_v + d_k) * sizeof(float) > ex.scratch_bytes)
+    return GLA_ERR_SCRATCH;
   if (plan_only != nullptr) {
     plan_only[0] = span_chunks;
     plan_only[1] = n_spans;
@@ -362,7 +373,14 @@ int forward(gla::Dtype dt, size_t esize, const void* q, const void* k, const voi
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   WsLease ws;
-  if (fused) {
+  if (no_alloc) {
+    if (n_spans > 1) {
+      float* base = static_cast<float*>(ex.scratch_of(dev));
+      if (base == nullptr) return GLA_ERR_HIP;
+      p.span_state = base;
+      p.span_gate = base + (size_t)BH * n_spans * d_k * d_v;
+    }
+  } else if (fused) {
     // span summaries (gate product + state) and one hand-off word per span
     const size_t agg_floats = (size_t)BH * n_spans * gla::kAggFloats;
     if (ws.acquire(st, agg_floats * sizeof(float), gla::kSyncFlags + (size_t)BH * n_spans) !=
@@ -399,6 +417,21 @@ void fast_div_constants(unsigned int d, unsigned int* m, int* s) {
   const unsigned long long num = ((1ULL << sh) - d) << 32;
   *m = (unsigned int)(num / d + 1);
   *s = sh;
+}
+
+int forward_no_alloc(const void* q, const void* k, const void* v, const void* log_alpha,
+                     int scan_dir, int B, int heads, int H, int W, int d_k, int d_v, int chunk,
+                     void* out, float* final_state, void* stream, void* (*scratch_of)(int dev),
+                     size_t scratch_bytes) {
+  try {
+    Extras ex;
+    ex.scratch_of = scratch_of;
+    ex.scratch_bytes = scratch_bytes;
+    return forward(Dtype::kF16, 2, q, k, v, log_alpha, scan_dir, B, heads, H, W, d_k, d_v, chunk,
+                   out, final_state, stream, nullptr, ex);
+  } catch (...) {
+    return GLA_ERR_HIP;
+  }
 }
 
 }  // namespace gla
@@ -770,6 +803,8 @@ const char* gla_status_str(int status) {
     case GLA_ERR_SCAN_DIR: return "scan_dir must be 0..4";
     case GLA_ERR_ALIAS: return "an output overlaps another tensor";
     case GLA_ERR_HIP: return "a HIP runtime call failed";
+    case GLA_ERR_SCRATCH:
+      return "the work split needs more span states than the fixed scratch holds";
     default: return "unknown status";
   }
 }

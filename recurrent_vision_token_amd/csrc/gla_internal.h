@@ -68,6 +68,14 @@ hipError_t launch_zero_words(unsigned int* p, size_t words, hipStream_t stream);
 // t / d == (umulhi(t, m) + t) >> s.
 void fast_div_constants(unsigned int d, unsigned int* m, int* s);
 
+// Float16 forward with its span states in a caller-fixed device buffer
+// instead of the workspace cache: scratch_of(dev) gives the current device's
+// buffer of scratch_bytes (null on failure); nothing is allocated.
+int forward_no_alloc(const void* q, const void* k, const void* v, const void* log_alpha,
+                     int scan_dir, int B, int heads, int H, int W, int d_k, int d_v, int chunk,
+                     void* out, float* final_state, void* stream, void* (*scratch_of)(int dev),
+                     size_t scratch_bytes);
+
 // Output-kernel workgroups resident per CU for this variant (occupancy).
 int output_blocks_per_cu(Dtype dt, int d_k, int d_v, bool gate_logits);
 

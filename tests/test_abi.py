@@ -31,6 +31,11 @@ def declared_functions():
 
 def call(dtype="fp16", q=Q, k=K, v=V, la=LA, scan_dir=0, B=1, heads=2, H=8, W=8, d_k=64,
          d_v=64, chunk=64, out=OUT, fs=FS):
+    """dtype "fp16" / "fp32" selects gla_chunk_fwd / gla_chunk_fwd_f32, "noalloc"
+    the float16 entry without allocation."""
+    if dtype == "noalloc":
+        return _lib.raw_call_noalloc(q, k, v, la, scan_dir, B, heads, H, W, d_k, d_v, chunk, out,
+                                     fs, None)
     return _lib.raw_call(dtype, q, k, v, la, scan_dir, B, heads, H, W, d_k, d_v, chunk, out, fs,
                          None)
 
@@ -50,14 +55,14 @@ def test_release_with_nothing_held_makes_no_hip_call():
 
 
 def test_status_strings_and_version():
-    for code in range(-7, 1):
+    for code in range(-8, 1):
         s = _lib.status_str(code)
         assert s and s != "unknown status"
     assert _lib.status_str(-99) == "unknown status"
     assert _lib.load().gla_version() >= 100
 
 
-@pytest.mark.parametrize("dtype", ["fp16", "fp32"])
+@pytest.mark.parametrize("dtype", ["fp16", "fp32", "noalloc"])
 def test_argument_errors(dtype):
     assert call(dtype, scan_dir=5) == -5
     assert call(dtype, scan_dir=-1) == -5
@@ -67,7 +72,7 @@ def test_argument_errors(dtype):
         assert call(dtype, **{kw: 0}) == -2, kw
     assert call(dtype, H=1 << 16, W=1 << 16) == -2          # T beyond 2^30
     # one sequence's rows of one tensor reach 2 GiB (32-bit byte offsets)
-    dk = 128 if dtype == "fp16" else 64
+    dk = 64 if dtype == "fp32" else 128
     assert call(dtype, B=1, heads=1, H=4096, W=2048, d_k=dk) == -2
     if NO_DEVICE:
         assert call(dtype, B=1, heads=1, H=4096, W=2047, d_k=dk) != -2
@@ -80,6 +85,15 @@ def test_argument_errors(dtype):
     assert call(dtype, out=Q) == -6                          # out aliases q
     assert call(dtype, out=V + 64) == -6                     # out overlaps v
     assert call(dtype, fs=OUT + 1024) == -6                  # final_state inside out
+
+
+def test_noalloc_entry_is_float16_only_and_checks_first():
+    # the scratch lookup is a HIP call; every argument check comes before it
+    assert call("noalloc", d_k=96) == -3
+    assert call("noalloc", out=K) == -6
+    assert _lib.NOALLOC_SCRATCH_BYTES == 32 << 20
+    text = open(HEADER).read()
+    assert re.search(r"#define GLA_NOALLOC_SCRATCH_BYTES \(32u << 20\)", text)
 
 
 def test_binding_checks_caller_outputs():
