@@ -46,6 +46,10 @@
 #include "gla_internal.h"
 #include "gla_tiles.h"
 
+#ifndef GLA_FOLD_NB
+#define GLA_FOLD_NB 8
+#endif
+
 namespace gla {
 namespace {
 
@@ -640,6 +644,12 @@ __global__ __launch_bounds__(kFThreads, 1) void fused_fwd_kernel(FwdParams p) {
       __hip_atomic_store(&p.sync[kSyncFlags + bh * p.n_spans + span], epoch + 1u, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
   }
+  // the first two steps of phase C load during the look-back (buffers 0 and
+  // 1 hold no join scratch)
+  if (!is_o) {
+    issue_step<true>(c, B.b[0], 0, hsel);
+    issue_step<true>(c, B.b[1], 1, hsel);
+  }
 
   // ---- look-back: wait for the summaries of spans 0 .. span-1, fold them
   f32x4 ea = init_a, eb = init_b;
@@ -668,20 +678,23 @@ __global__ __launch_bounds__(kFThreads, 1) void fused_fwd_kernel(FwdParams p) {
     __syncthreads();
     ea = f32x4{0.f, 0.f, 0.f, 0.f};
     eb = ea;
-    constexpr int NB = 8;   // summaries whose loads are in flight together
+    constexpr int NB = GLA_FOLD_NB;   // summaries whose loads are in flight together
     for (int j0 = 0; j0 < span; j0 += NB) {
       f32x4 la[NB], lb[NB];
       float gj[NB];
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
-        const int jj = min(j0 + i, span - 1);
-        const uint32_t base = (uint32_t)(jj * kAggFloats) * 4u;
-        la[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              agg, base + (uint32_t)(64 + r * 64 + c0) * 4u, 0, kAuxSC1));
-        lb[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              agg, base + (uint32_t)(64 + r * 64 + c0 + 4) * 4u, 0, kAuxSC1));
-        gj[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                              agg, base + (uint32_t)r * 4u, 0, kAuxSC1));
+        // only existing summaries are read (span is workgroup-uniform): these
+        // loads go past the caches, and every workgroup folds at once
+        if (j0 + i < span) {
+          const uint32_t base = (uint32_t)((j0 + i) * kAggFloats) * 4u;
+          la[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                agg, base + (uint32_t)(64 + r * 64 + c0) * 4u, 0, kAuxSC1));
+          lb[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                agg, base + (uint32_t)(64 + r * 64 + c0 + 4) * 4u, 0, kAuxSC1));
+          gj[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                agg, base + (uint32_t)r * 4u, 0, kAuxSC1));
+        }
       }
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
@@ -701,12 +714,7 @@ __global__ __launch_bounds__(kFThreads, 1) void fused_fwd_kernel(FwdParams p) {
     *reinterpret_cast<f32x4*>(scratch_row(L1, r) + c0 + 4) = e1b;
   }
   __syncthreads();
-  if (!is_o) {
-    // the first two steps of phase C load while the O-waves pick up their
-    // entry states (buffers 0 and 1 hold no scratch)
-    issue_step<true>(c, B.b[0], 0, hsel);
-    issue_step<true>(c, B.b[1], 1, hsel);
-  } else {
+  if (is_o) {
     if (sig == 0) state_from_scratch(L0, hsel, S);
     else state_from_scratch(L1, hsel, S);
   }
