@@ -45,9 +45,15 @@
  * independent.  Under stream capture a call takes a stream-ordered
  * allocation of its own instead, released in the captured stream order.
 
- * Besides this table the library holds no global state but a one-time read
- * of tuning environment variables and the measurement hook's per-thread
- * events; it keeps no pointer to caller memory after returning.
+ * Besides this table the library holds, process-wide: the forward mode
+ * (gla_set_forward_mode), per-device caches of the resident workgroup slots
+ * and CU count (read once from the device), a one-time read of tuning
+ * environment variables, the measurement hook's per-thread events, and the
+ * no-allocation entry's per-device array address.  With the single-pass
+ * mode each stream's workspace also holds hand-off words (ticket and
+ * finish counters, an epoch and one flag per span) that the kernel leaves
+ * consistent for the next call on that stream.  The library keeps no
+ * pointer to caller memory after returning.
  *
  * Errors: every argument check runs before any HIP call; on failure nothing is
  * enqueued and a negative status is returned (see gla_status_str).  Nothing
@@ -99,9 +105,15 @@ enum {
  * float32.  Arithmetic: per-chunk cumulative log-decay in float32, 16-bit MFMA
  * tiles with float32 accumulation, float32 state; out is rounded to nearest
  * even.  Supported: chunk = 64, d_k in {64, 128}, d_v in {64, 128}.
- * Numerical domain: log_alpha finite and <= 0, with the decay summed over any
- * 16 consecutive scan steps of one key dim >= -10 (so the 16-bit key factors
- * of the diagonal sub-blocks stay finite).
+ * Numerical domain: log_alpha finite and <= 0, of any strength.  A 32-token
+ * step in which a scaled float16 operand could leave its range (a decay
+ * below -10 in log2, about -6.9 in natural log, over 16 steps of one key dim,
+ * or keys -- on the single-pass path queries or keys -- of magnitude 32 and
+ * above) is computed exactly, token by token in float32, on every path
+ * (strong forgetting: log-alpha of -2 per step, alpha -> 0).  Otherwise the
+ * within-step attention scores q_t . k_s e^{b_t - b_s}, the state entries
+ * and the outputs must lie in the float16 range (they pass through float16
+ * MFMA operands or are stored as float16).
  */
 int gla_chunk_fwd(const void* q, const void* k, const void* v, const void* log_alpha,
                   int scan_dir, int B, int heads, int H, int W, int d_k, int d_v, int chunk,
@@ -119,13 +131,24 @@ int gla_chunk_fwd(const void* q, const void* k, const void* v, const void* log_a
  *     of all earlier spans of their sequence into their own entry state (no
  *     scan kernel; the work of a span grows with its index, so it is used
  *     for few spans).  Chosen when a split into 2..16 spans of at most 4
- *     chunks puts every output workgroup on the device at once.
+ *     chunks puts every output workgroup on the device at once, and the call
+ *     does not update its state in place (final_state == initial_state
+ *     takes three passes);
+ *   single pass (d_k = d_v = 64, only when forced): one kernel; each
+ *     workgroup summarises its span, publishes the summary and a flag, folds
+ *     the earlier spans' published summaries into its entry state and
+ *     writes its outputs.  A 32-token step whose decay would push the
+ *     float16 scaled operands out of range is computed exactly token by
+ *     token, so this path has no domain limit on log_alpha beyond being
+ *     finite and <= 0.
  * mode: GLA_FWD_AUTO (default, the rule above), GLA_FWD_THREE_PASS (always
  * three passes), GLA_FWD_TWO_PASS (two passes whenever the sequence splits
- * into 2..16 spans, of any length).  Process-wide, for calls made after it;
- * a tuning and testing switch, both paths meet the same accuracy.  Returns
- * GLA_OK, or GLA_ERR_SHAPE for an unknown mode.  The environment variable
- * GLA_SPAN_CHUNKS (a forced span length) selects three passes.
+ * into 2..16 spans, of any length), GLA_FWD_SINGLE_PASS (the single pass
+ * for d_k = d_v = 64, else the automatic choice).  Process-wide, for calls
+ * made after it; a tuning and testing switch, all paths meet the same
+ * accuracy.  Returns GLA_OK, or GLA_ERR_SHAPE for an unknown mode.  The
+ * environment variable GLA_SPAN_CHUNKS (a forced span length) selects three
+ * passes.
  */
 enum {
   GLA_FWD_AUTO = 0,

@@ -36,9 +36,9 @@
 //   Qb = q e^{b - a}, Kb = k e^{a - b}, Khat = k e^{b_end - b} (<= 1),
 //   O  = mask(Qb Kb^T) V + Qb diag(e^a) S,
 //   S <- diag(e^{b_end}) S + Khat^T V.
-// A step whose half-step decay leaves 2^10 in some key dim, or whose keys
-// reach 128 in magnitude, is computed exactly token by token from the raw
-// tiles instead (the P-waves agree on that before they overwrite anything).
+// A step whose half-step decay leaves 2^10 in some key dim, or whose queries
+// or keys reach 32 in magnitude, is computed exactly token by token from the
+// raw tiles instead (the P-waves agree on that before they overwrite anything).
 
 #include <hip/hip_ext.h>
 
@@ -243,6 +243,7 @@ __device__ __forceinline__ void p_step(const FwdParams& p, const Ctx& c, const F
         qo[dbi][I] = q4[I] * to_f16(eq);
         ko[dbi][I] = k4[I] * to_f16(ek);
         kmax = __builtin_elementwise_max(kmax, __builtin_bit_cast(u16x4, k4[I]) & (unsigned short)0x7fff);
+        kmax = __builtin_elementwise_max(kmax, __builtin_bit_cast(u16x4, q4[I]) & (unsigned short)0x7fff);
       } else {
 #pragma unroll
         for (int u = 0; u < 4; ++u) eh[u] = exp2_fast(e2[u] - x[I][u]);
@@ -252,10 +253,10 @@ __device__ __forceinline__ void p_step(const FwdParams& p, const Ctx& c, const F
   }
   bool exact = false;
   if constexpr (OUT) {
-    // |k| >= 128 (binary16 0x5800 and above, NaN included) leaves too little
-    // headroom for Kb
-    bad |= __builtin_elementwise_max(kmax.xy, kmax.zw)[0] >= 0x5800 ||
-           __builtin_elementwise_max(kmax.xy, kmax.zw)[1] >= 0x5800;
+    // |q| or |k| >= 32 (binary16 0x5000 and above, NaN included): times a
+    // factor up to 2^10, Qb or Kb could leave the float16 range
+    bad |= __builtin_elementwise_max(kmax.xy, kmax.zw)[0] >= 0x5000 ||
+           __builtin_elementwise_max(kmax.xy, kmax.zw)[1] >= 0x5000;
     exact = agree_exact(pf, kh, tag, __builtin_amdgcn_ballot_w64(bad) != 0);
   }
   if (!exact) {

@@ -754,6 +754,9 @@ __global__ __launch_bounds__(kThreads) void chunk_output_kernel(FwdParams p) {
 // 8g+4..8g+7 the same tokens of sub-block 1, which is what two transposed
 // 16x16 reads (or two 16x16 accumulator tiles) deliver.
 constexpr int kStep = 32;
+// log2 of the largest key factor exp(-c) the fast step path forms
+constexpr float kKeyFactorLog2 = 10.f;
+typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
 
 // Column of key dim d (d % 4 == 0, four dims kept together) in token-slot
 // order: within each 32-dim group, dims 4g..4g+3 and 16+4g..16+4g+3 sit side
@@ -796,7 +799,7 @@ template <int DK, int DV, bool GATE, class Entry>
 __device__ __forceinline__ void output_span(const FwdParams& p, int bh, int span,
                                             const StepTiles<DK, DV>& slot0,
                                             const StepTiles<DK, DV>& slot1, f16* sqt, float* sgd,
-                                            uint32_t (*srow)[kStep],
+                                            uint32_t (*srow)[kStep], uint32_t* sxf,
                                             f32x4 (&st)[DK / 16][DV / 64], Entry&& entry) {
   constexpr int RBK = 2 * DK, RBV = 2 * DV;
   constexpr int NR = DK / 16, NC = DV / 64, NRHO = DK / 32;
@@ -840,8 +843,13 @@ __device__ __forceinline__ void output_span(const FwdParams& p, int bh, int span
 
   const f16x4 u_hi = upper_incl(kLog2eHi), u_lo = upper_incl(kLog2eLo);
 
-  // ---- P: per-dim decays and the scaled operands of the step
-  auto phase_p = [&](const StepTiles<DK, DV>& s, int valid) {
+  // ---- P: per-dim decays and the scaled operands of the step.  A step in
+  // which some key factor exp(-c) would exceed 2^10, or some key reaches 32
+  // in magnitude (its scaled copy could leave the float16 range), is marked
+  // in *xf with `tag`; the O phase then computes it exactly (phase_x).
+  auto phase_p = [&](const StepTiles<DK, DV>& s, int valid, uint32_t* xf, uint32_t tag) {
+    bool bad = false;
+    u16x4 kmax = {0, 0, 0, 0};
 #pragma unroll
     for (int dbi = 0; dbi < DK / 64; ++dbi) {
       const int db = wave + 4 * dbi;
@@ -865,7 +873,9 @@ __device__ __forceinline__ void output_span(const FwdParams& p, int bh, int span
           eq[I][u] = exp2_fast(c2[I][u]);
           ek[I][u] = exp2_fast(-c2[I][u]);
           ed[I][u] = row_bcast15(eq[I][u]);  // exp(decay over sub-block I)
+          bad |= !(c2[I][u] >= -kKeyFactorLog2);
         }
+        kmax = __builtin_elementwise_max(kmax, __builtin_bit_cast(u16x4, k4[I]) & (unsigned short)0x7fff);
       }
       if (n16 == 0) *reinterpret_cast<f32x4*>(sgd + dim0) = ed[0] * ed[1];
 #pragma unroll
@@ -881,10 +891,70 @@ __device__ __forceinline__ void output_span(const FwdParams& p, int bh, int span
         st64(s.la + swz<RBK>(row, dim0), (I == 0) ? kend * to_f16(ed[1]) : kend);
       }
     }
+    // |k| >= 32 (binary16 0x5000 and above, NaN included)
+    const u16x4 km = __builtin_elementwise_max(kmax, kmax.wzyx);
+    bad |= km[0] >= 0x5000 || km[1] >= 0x5000;
+    if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) *xf = tag;
+  };
+
+  // ---- exact step: the recurrence token by token in float32, on this
+  // wave's state columns, from the raw q, k and log-alpha (loaded again: the
+  // P phase overwrote them; v is untouched)
+  auto phase_x = [&](const StepTiles<DK, DV>& s, const uint32_t* rows, int step) {
+    const int t0 = t_begin + kStep * step;
+    const int valid = max(0, min(kStep, t_end - t0));
+#pragma unroll
+    for (int i = 0; i < NBK; ++i) {
+      const int blk = wave * NBK + i;
+      const uint32_t off = dma_offset<RBK>(blk, t0, valid, gm);
+      dma16(sb.q, s.q + blk * 512, off);
+      dma16(sb.k, s.k + blk * 512, off);
+      dma16(sb.la, s.la + blk * 512, off);
+    }
+    wait_barrier<vmcnt_imm(0)>();
+    for (int t = 0; t < valid; ++t) {
+      float vf[NC], part[NC];
+#pragma unroll
+      for (int j = 0; j < NC; ++j) {
+        vf[j] = (float)s.v[swz<RBV>(t, 16 * (wave + 4 * j) + n16)];
+        part[j] = 0.f;
+      }
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const f16x4 la4 = ld64(s.la + swz<RBK>(t, 16 * r + 4 * g));
+        const f16x4 k4 = ld64(s.k + swz<RBK>(t, 16 * r + 4 * g));
+        const f16x4 q4 = ld64(s.q + swz<RBK>(t, 16 * r + 4 * g));
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float la = GATE ? logsigmoid_scaled((float)la4[u], p.inv_tau) : (float)la4[u];
+          const float al = exp2_fast(la * 1.4426950408889634f);
+#pragma unroll
+          for (int j = 0; j < NC; ++j) {
+            st[r][j][u] = al * st[r][j][u] + (float)k4[u] * vf[j];
+            part[j] += (float)q4[u] * st[r][j][u];
+          }
+        }
+      }
+      const uint32_t orow_t = (rows[t] & 0x7fffffffu) * RBV;
+#pragma unroll
+      for (int j = 0; j < NC; ++j) {
+        float o = part[j] + __shfl_xor(part[j], 16);
+        o += __shfl_xor(o, 32);
+        if (g == 0)
+          __builtin_amdgcn_raw_buffer_store_b16(
+              __builtin_bit_cast(unsigned short, (f16)o), sb.out,
+              orow_t + (uint32_t)((16 * (wave + 4 * j) + n16) * 2), 0, 0);
+      }
+    }
   };
 
   // ---- O: scores, outputs, state update
-  auto phase_o = [&](const StepTiles<DK, DV>& s, const uint32_t* rows) {
+  auto phase_o = [&](const StepTiles<DK, DV>& s, const uint32_t* rows, const uint32_t* xf,
+                     uint32_t tag, int step) {
+    if (__builtin_amdgcn_readfirstlane(*xf) == tag) {
+      phase_x(s, rows, step);
+      return;
+    }
     // A^T tiles: lane (t, g) holds A[t][s = 4g + u] of the tile
     f32x4 d00 = {0.f, 0.f, 0.f, 0.f}, d01 = d00, d11 = d00;
 #pragma unroll
@@ -948,10 +1018,13 @@ __device__ __forceinline__ void output_span(const FwdParams& p, int bh, int span
 
   // rows of step `step` inside the span
   auto valid_rows = [&](int step) { return max(0, min(kStep, t_end - t_begin - kStep * step)); };
+  // steps alternate between the two buffers; a step's exactness mark is its
+  // index + 1 in its buffer's word (0 when the kernel starts)
   auto run_step = [&](const StepTiles<DK, DV>& s, const uint32_t* rows, int step) {
-    phase_p(s, valid_rows(step));
+    uint32_t* xf = sxf + (step & 1);
+    phase_p(s, valid_rows(step), xf, (uint32_t)step + 1u);
     wait_barrier<kLgkmZero>();
-    phase_o(s, rows);
+    phase_o(s, rows, xf, (uint32_t)step + 1u, step);
   };
   // Before step s the loads in flight are step s and the stores of s - 1.
   issue(slot0, srow[0], 0);
@@ -1010,6 +1083,10 @@ __global__ __launch_bounds__(kThreads, LOOKBACK ? 2 : (DK == 64 && DV == 64) ? 4
   __shared__ __attribute__((aligned(16))) float sgd[DK];  // exp(decay over the step)
   // grid cell of each step row (bit 31: past the span), per step buffer
   __shared__ uint32_t srow[2][kStep];
+  // exactness mark of the step in each buffer (see output_span)
+  __shared__ uint32_t sxf[2];
+  if (threadIdx.x < 2) sxf[threadIdx.x] = 0u;
+  __syncthreads();
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1022,7 +1099,7 @@ __global__ __launch_bounds__(kThreads, LOOKBACK ? 2 : (DK == 64 && DV == 64) ? 4
         (p.n_spans > 1) ? p.span_state + ((size_t)bh * p.n_spans + span) * DK * DV
         : p.initial_state ? p.initial_state + (size_t)bh * DK * DV : nullptr,
         wave, lane & 15, lane >> 4, st);
-    output_span<DK, DV, GATE>(p, bh, span, slot0, slot1, sqt, sgd, srow, st, [](auto&) {});
+    output_span<DK, DV, GATE>(p, bh, span, slot0, slot1, sqt, sgd, srow, sxf, st, [](auto&) {});
   } else {
     const int g = lane >> 4;
     load_state_tiles<DK, DV>(p.initial_state ? p.initial_state + (size_t)bh * DK * DV : nullptr,
@@ -1050,7 +1127,7 @@ __global__ __launch_bounds__(kThreads, LOOKBACK ? 2 : (DK == 64 && DV == 64) ? 4
             for (int r = 0; r < DK / 16; ++r) s[r][0] = gv[i][r] * s[r][0] + av[i][r];
       }
     };
-    output_span<DK, DV, GATE>(p, bh, span, slot0, slot1, sqt, sgd, srow, st, fold_earlier);
+    output_span<DK, DV, GATE>(p, bh, span, slot0, slot1, sqt, sgd, srow, sxf, st, fold_earlier);
   }
 }
 

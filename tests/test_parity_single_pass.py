@@ -2,9 +2,9 @@
 
 The single-pass path (one kernel: each workgroup summarises its span,
 publishes the summary, folds the published summaries of the earlier spans of
-its sequence into its entry state, then writes its outputs) is the automatic
-choice for float16 sequences with d_k = d_v = 64 that split into spans;
-gla_set_forward_mode forces it.  Every case is held to the float16 bar of the
+its sequence into its entry state, then writes its outputs) serves float16
+sequences with d_k = d_v = 64 when gla_set_forward_mode forces it (the
+automatic choice does not take it).  Every case is held to the float16 bar of the
 spec tolerance against the oracle: odd and degenerate grids in every
 direction, the configured workloads at full size, the extended entry, the
 state updated in place, strong forgetting (the exact token-by-token steps),
