@@ -220,7 +220,7 @@ int gla_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* ga
 
 /*
  * Float32 entry: every tensor float32, float32 MFMA tiles, float32 state.
- * Same arguments and semantics.  Supported: chunk = 64, d_k = 64,
+ * Same arguments and semantics.  Supported: chunk = 64, d_k in {64, 128},
  * d_v in {64, 128}.  Domain: log_alpha finite and <= 0, 16-step decay >= -80.
  */
 int gla_chunk_fwd_f32(const float* q, const float* k, const float* v, const float* log_alpha,

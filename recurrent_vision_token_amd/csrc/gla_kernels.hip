@@ -48,67 +48,45 @@ constexpr int kChunk = 64;     // tokens per chunk
 constexpr int kSub = 16;       // tokens per sub-block (one MFMA tile edge)
 constexpr int kThreads = 256;  // four wave64s
 
+// Element traits of the generic (float32) kernels.
 template <class T>
 struct Elt;
 template <>
-struct Elt<f16> {
-  static constexpr int kPerPiece = 8;  // elements per 16-byte row piece
-  static constexpr int kPad = 8;       // LDS row padding (elements)
-  typedef f16x8 piece_t;               // one 16-byte piece as a vector
-};
-template <>
 struct Elt<float> {
-  static constexpr int kPerPiece = 4;
-  static constexpr int kPad = 4;
-  typedef f32x4 piece_t;
+  static constexpr int kPerPiece = 4;  // elements per 16-byte row piece
+  static constexpr int kPad = 4;       // LDS row padding (elements)
+  typedef f32x4 piece_t;               // one 16-byte piece as a vector
 };
 
 template <class T>
 __device__ __forceinline__ float fexp(float x) {
-  if constexpr (std::is_same<T, float>::value) {
-    return expf(x);
-  } else {
-    return __expf(x);
-  }
-}
-
-// Row of key / value dim d in a transposed [dim][token] tile: one padding row
-// after every 8 dims, so that the 8 lanes writing dims 8pc+u (pc = 0..7) of a
-// token pair land in different LDS banks.
-__device__ __forceinline__ constexpr int trow(int d) { return d + (d >> 3); }
-
-// Branch-free select of a loaded 16-byte piece.
-__device__ __forceinline__ uint4 sel(bool c, uint4 a, uint4 b) {
-  return make_uint4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
-}
-
-__device__ __forceinline__ uint4 bload(rsrc_t r, uint32_t off) {
-  const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-  return make_uint4(x[0], x[1], x[2], x[3]);
-}
-__device__ __forceinline__ void bstore(rsrc_t r, uint32_t off, uint4 d) {
-  __builtin_amdgcn_raw_buffer_store_b128(u32x4{d.x, d.y, d.z, d.w}, r, off, 0, 0);
+  return expf(x);
 }
 
 // Pair index of sub-block pair (I, J), J < I, in the factor table.
 __device__ __forceinline__ constexpr int pair_index(int I, int J) { return I * (I - 1) / 2 + J; }
 
 // ---------------------------------------------------------------------------
-// Shared-memory tiles of one chunk.
+// Shared-memory tiles of one chunk (float32 output kernel).  Two tiles are
+// reused within a chunk so that d_k = 128 fits (160 KB at d_v = 128):
+// log-alpha arrives transposed in the tile of the decayed keys (each
+// (key dim, sub-block) item reads its own 16 entries before it overwrites
+// them), and the output staging shares the key tile, which is dead once the
+// score tiles are formed.
 template <class T, int DK, int DV>
 struct ChunkSmem {
   static constexpr int P = Elt<T>::kPad;
   static constexpr int QS = DK + P;      // row stride: [token][d_k] tiles
   static constexpr int AS = kChunk + P;  // row stride: [*][token] tiles
   static constexpr int OS = DV + P;      // row stride: [token][d_v] tile
-  static constexpr int LA_ELEMS = kChunk * QS;
-  static constexpr int A_ELEMS = kChunk * AS;
   alignas(16) T q[kChunk * QS];    // raw q, then q_t*exp(c_t)
-  alignas(16) T k[kChunk * QS];    // raw k, then k_s*exp(-c_s)
-  alignas(16) T la[(LA_ELEMS > A_ELEMS) ? LA_ELEMS : A_ELEMS];  // raw log-alpha, then A[t][s]
+  union {
+    alignas(16) T k[kChunk * QS];  // raw k, then k_s*exp(-c_s)
+    alignas(16) T o[kChunk * OS];  // output staging [token][d_v]
+  };
+  alignas(16) T sa[kChunk * AS];   // A^T tiles: A[t][s] at [t][s]
   alignas(16) T vt[DV * AS];       // V^T [d_v][token]
-  alignas(16) T klt[DK * AS];      // (k_s*exp(b_last-b_s))^T [d_k][token]
-  alignas(16) T o[kChunk * OS];    // output staging [token][d_v]
+  alignas(16) T klt[DK * AS];      // log-alpha^T, then (k_s*exp(b_last-b_s))^T [d_k][token]
   alignas(16) float e[4 * DK];     // exp(Bst_I): decay from chunk start to sub-block I
   alignas(16) float f[6 * DK];     // exp(Bst_I - Bst_J), J < I
   alignas(16) float g[DK];         // exp(b_last): decay over the whole chunk
@@ -180,8 +158,9 @@ struct Loader {
     }
   }
 
-  // Registers -> shared tiles: q, k, la row-major; v transposed to [d_v][token].
-  template <bool WITH_Q>
+  // Registers -> shared tiles: q, k row-major; la row-major, or with LA_T
+  // transposed to [d_k][token] (row stride AS); v transposed to [d_v][token].
+  template <bool WITH_Q, bool LA_T = false>
   __device__ __forceinline__ void store(T* sq, T* sk, T* sla, T* svt, int QS, int AS) const {
     const int tid = threadIdx.x;
 #pragma unroll
@@ -192,7 +171,14 @@ struct Loader {
       const int o = tok * QS + pc * EPP;
       if (WITH_Q) *reinterpret_cast<uint4*>(sq + o) = rq[j];
       *reinterpret_cast<uint4*>(sk + o) = rk[j];
-      *reinterpret_cast<uint4*>(sla + o) = rl[j];
+      if constexpr (LA_T) {
+        typedef typename Elt<T>::piece_t piece_t;
+        const piece_t l = __builtin_bit_cast(piece_t, rl[j]);
+#pragma unroll
+        for (int u = 0; u < EPP; ++u) sla[(pc * EPP + u) * AS + tok] = l[u];
+      } else {
+        *reinterpret_cast<uint4*>(sla + o) = rl[j];
+      }
     }
 #pragma unroll
     for (int j = 0; j < NVP; ++j) {
@@ -239,18 +225,9 @@ __device__ __forceinline__ void state_update(StateRegs<DK, DV>& st, const T* klt
 #pragma unroll
       for (int u = 0; u < 4; ++u) acc[u] *= gch[16 * r + 4 * g + u];
       const int dim = 16 * r + n16;
-      if constexpr (std::is_same<T, f16>::value) {
 #pragma unroll
-        for (int s0 = 0; s0 < kChunk; s0 += 32) {
-          const f16x8 a = *reinterpret_cast<const f16x8*>(klt + dim * AS + s0 + 8 * g);
-          const f16x8 b = *reinterpret_cast<const f16x8*>(vt + col * AS + s0 + 8 * g);
-          acc = mma32(a, b, acc);
-        }
-      } else {
-#pragma unroll
-        for (int s0 = 0; s0 < kChunk; s0 += 4)
-          acc = mma4(klt[dim * AS + s0 + g], vt[col * AS + s0 + g], acc);
-      }
+      for (int s0 = 0; s0 < kChunk; s0 += 4)
+        acc = mma4(klt[dim * AS + s0 + g], vt[col * AS + s0 + g], acc);
       st.s[r][j] = acc;
     }
   }
@@ -463,7 +440,7 @@ __global__ __launch_bounds__(kThreads) void chunk_output_kernel(FwdParams p) {
   __shared__ SM sm;
   constexpr int QS = SM::QS, AS = SM::AS, OS = SM::OS;
   constexpr int EPP = Elt<T>::kPerPiece;
-  constexpr bool kF16 = std::is_same<T, f16>::value;
+  static_assert(std::is_same<T, float>::value, "the float16 output kernel is chunk_output_f16_kernel");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n16 = lane & 15, g = lane >> 4;
 
@@ -517,7 +494,8 @@ __global__ __launch_bounds__(kThreads) void chunk_output_kernel(FwdParams p) {
   for (int c = c_begin; c < c_end; ++c) {
     const int t0 = c * kChunk;
     const int valid = min(kChunk, p.T - t0);
-    ld.template store<true>(sm.q, sm.k, sm.la, sm.vt, QS, AS);
+    if (c > c_begin) __syncthreads();  // the previous chunk's rows are out of sm.o (= sm.k)
+    ld.template store<true, true>(sm.q, sm.k, sm.klt, sm.vt, QS, AS);
     if (c + 1 < c_end) {
       const int t1 = t0 + kChunk;
       ld.template load<true>(q, k, la, v, off_k, off_v, t1, min(kChunk, p.T - t1), gm);
@@ -534,7 +512,7 @@ __global__ __launch_bounds__(kThreads) void chunk_output_kernel(FwdParams p) {
       float c_run = 0.f;
 #pragma unroll
       for (int r = 0; r < kSub; ++r) {
-        c_run += (float)sm.la[(kSub * J + r) * QS + i];
+        c_run += (float)sm.klt[i * AS + kSub * J + r];   // log-alpha^T
         cs[r] = c_run;
       }
       const int base = lane & ~3;
@@ -577,7 +555,7 @@ __global__ __launch_bounds__(kThreads) void chunk_output_kernel(FwdParams p) {
     __syncthreads();
 
     // Phase A: A[t][s] for s <= t as transposed 16x16 tiles (rows s, cols t).
-    T* sa = sm.la;
+    T* sa = sm.sa;
     for (int ti = 0; ti < n_tiles; ++ti) {
       const int code = (tile_codes >> (8 * ti)) & 0xff;
       const int I = code >> 4, J = code & 0xf;
@@ -585,24 +563,11 @@ __global__ __launch_bounds__(kThreads) void chunk_output_kernel(FwdParams p) {
       const int t_row = kSub * I + n16;  // query token supplying the B operand
       const float* F = (J < I) ? sm.f + pair_index(I, J) * DK : nullptr;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (kF16) {
-#pragma unroll
-        for (int d0 = 0; d0 < DK; d0 += 32) {
-          f16x8 a = *reinterpret_cast<const f16x8*>(sm.k + s_row * QS + d0 + 8 * g);
-          if (F) {
-#pragma unroll
-            for (int u = 0; u < 8; ++u) a[u] = (f16)((float)a[u] * F[d0 + 8 * g + u]);
-          }
-          const f16x8 bq = *reinterpret_cast<const f16x8*>(sm.q + t_row * QS + d0 + 8 * g);
-          acc = mma32(a, bq, acc);
-        }
-      } else {
 #pragma unroll 8
-        for (int d0 = 0; d0 < DK; d0 += 4) {
-          float a = sm.k[s_row * QS + d0 + g];
-          if (F) a *= F[d0 + g];
-          acc = mma4(a, sm.q[t_row * QS + d0 + g], acc);
-        }
+      for (int d0 = 0; d0 < DK; d0 += 4) {
+        float a = sm.k[s_row * QS + d0 + g];
+        if (F) a *= F[d0 + g];
+        acc = mma4(a, sm.q[t_row * QS + d0 + g], acc);
       }
       // lane holds A^T[s = 16J + 4g + u][t = 16I + n16]
       if (I == J) {
@@ -624,60 +589,22 @@ __global__ __launch_bounds__(kThreads) void chunk_output_kernel(FwdParams p) {
     for (int j = 0; j < StateRegs<DK, DV>::NC; ++j) {
       const int col0 = 16 * (wave + 4 * j);
       const int col = col0 + n16;
-      f16x8 sh[DK / 32];
-      if constexpr (kF16) {
-#pragma unroll
-        for (int rho = 0; rho < DK / 32; ++rho)
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            sh[rho][u] = (f16)st.s[2 * rho][j][u];
-            sh[rho][4 + u] = (f16)st.s[2 * rho + 1][j][u];
-          }
-      }
 #pragma unroll
       for (int I = 0; I < 4; ++I) {
         const int t = kSub * I + n16;
         const int len = kSub * (I + 1);
         const float* E = sm.e + I * DK;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (kF16) {
-#pragma unroll
-          for (int s0 = 0; s0 + 32 <= len; s0 += 32) {
-            const f16x8 a = *reinterpret_cast<const f16x8*>(sm.vt + col * AS + s0 + 8 * g);
-            const f16x8 bb = *reinterpret_cast<const f16x8*>(sa + t * AS + s0 + 8 * g);
-            acc = mma32(a, bb, acc);
-          }
-          if (len & 16) {
-            const int s0 = len - 16;
-            const f16x4 a = *reinterpret_cast<const f16x4*>(sm.vt + col * AS + s0 + 4 * g);
-            const f16x4 bb = *reinterpret_cast<const f16x4*>(sa + t * AS + s0 + 4 * g);
-            acc = mma16(a, bb, acc);
-          }
-#pragma unroll
-          for (int rho = 0; rho < DK / 32; ++rho) {
-            const int dlo = 32 * rho + 4 * g, dhi = dlo + 16;
-            const f16x4 qlo = *reinterpret_cast<const f16x4*>(sm.q + t * QS + dlo);
-            const f16x4 qhi = *reinterpret_cast<const f16x4*>(sm.q + t * QS + dhi);
-            f16x8 bq;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              bq[u] = (f16)((float)qlo[u] * E[dlo + u]);
-              bq[4 + u] = (f16)((float)qhi[u] * E[dhi + u]);
-            }
-            acc = mma32(sh[rho], bq, acc);
-          }
-        } else {
 #pragma unroll 4
-          for (int s0 = 0; s0 < len; s0 += 4)
-            acc = mma4(sm.vt[col * AS + s0 + g], sa[t * AS + s0 + g], acc);
+        for (int s0 = 0; s0 < len; s0 += 4)
+          acc = mma4(sm.vt[col * AS + s0 + g], sa[t * AS + s0 + g], acc);
 #pragma unroll
-          for (int r = 0; r < DK / 16; ++r)
+        for (int r = 0; r < DK / 16; ++r)
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const int d = 16 * r + 4 * g + u;
-              acc = mma4(st.s[r][j][u], sm.q[t * QS + d] * E[d], acc);
-            }
-        }
+          for (int u = 0; u < 4; ++u) {
+            const int d = 16 * r + 4 * g + u;
+            acc = mma4(st.s[r][j][u], sm.q[t * QS + d] * E[d], acc);
+          }
         // lane holds O^T[col0 + 4g + u][t]
         typedef T quad_t __attribute__((ext_vector_type(4)));
         quad_t w;
@@ -1596,6 +1523,8 @@ hipError_t launch_forward_impl(Dtype dt, int d_k, int d_v, bool gate_logits, con
   } else if (!gate_logits) {
     if (d_k == 64 && d_v == 64) return launch_variant<float, 64, 64, false>(p, stream, ev);
     if (d_k == 64 && d_v == 128) return launch_variant<float, 64, 128, false>(p, stream, ev);
+    if (d_k == 128 && d_v == 64) return launch_variant<float, 128, 64, false>(p, stream, ev);
+    if (d_k == 128 && d_v == 128) return launch_variant<float, 128, 128, false>(p, stream, ev);
   }
   return hipErrorInvalidValue;
 }
@@ -1626,14 +1555,15 @@ int output_blocks_per_cu(Dtype dt, int d_k, int d_v, bool gate_logits) {
   } else {
     if (d_k == 64 && d_v == 64) return output_occupancy<float, 64, 64, false>();
     if (d_k == 64 && d_v == 128) return output_occupancy<float, 64, 128, false>();
+    if (d_k == 128 && d_v == 64) return output_occupancy<float, 128, 64, false>();
+    if (d_k == 128 && d_v == 128) return output_occupancy<float, 128, 128, false>();
   }
   return 1;
 }
 
 bool has_variant(Dtype dt, int d_k, int d_v) {
-  if (dt == Dtype::kF16)
-    return (d_k == 64 || d_k == 128) && (d_v == 64 || d_v == 128);
-  return d_k == 64 && (d_v == 64 || d_v == 128);
+  (void)dt;
+  return (d_k == 64 || d_k == 128) && (d_v == 64 || d_v == 128);
 }
 
 bool has_two_pass(Dtype dt, int d_k, int d_v) {

@@ -164,13 +164,6 @@ __global__ __launch_bounds__(kThreads) void saga_kv_partial_kernel(SagaParams p)
   }
 }
 
-// MFMA m of the output kernel (16 value dims): its row r is value dim
-// 32 (m / 2) + 8 (r / 4) + 4 (m % 2) + r % 4, so that the output lanes store
-// 16 contiguous bytes (see saga_out_kernel).
-__device__ __forceinline__ int out_row_dim(int m, int r) {
-  return 32 * (m >> 1) + 8 * (r >> 2) + 4 * (m & 1) + (r & 3);
-}
-
 // Kernel 2.  One workgroup of G waves per (batch*head, pair of MFMAs 2s and
 // 2s + 1 of the output kernel, key block rho of 32 dims): value dims
 // 32 s .. 32 s + 31 (whole 128-byte lines of the partials) over the key dims

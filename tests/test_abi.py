@@ -72,10 +72,11 @@ def test_argument_errors(dtype):
         assert call(dtype, **{kw: 0}) == -2, kw
     assert call(dtype, H=1 << 16, W=1 << 16) == -2          # T beyond 2^30
     # one sequence's rows of one tensor reach 2 GiB (32-bit byte offsets)
-    dk = 64 if dtype == "fp32" else 128
-    assert call(dtype, B=1, heads=1, H=4096, W=2048, d_k=dk) == -2
+    dk = 128
+    w = 1024 if dtype == "fp32" else 2048      # rows of 512 (fp32) or 256 bytes
+    assert call(dtype, B=1, heads=1, H=4096, W=w, d_k=dk) == -2
     if NO_DEVICE:
-        assert call(dtype, B=1, heads=1, H=4096, W=2047, d_k=dk) != -2
+        assert call(dtype, B=1, heads=1, H=4096, W=w - 1, d_k=dk) != -2
     assert call(dtype, chunk=32) == -3
     assert call(dtype, d_k=96) == -3
     assert call(dtype, d_v=32) == -3
@@ -149,9 +150,11 @@ def test_extended_entry_argument_errors():
     assert call_ex(chunk=32) == -3
 
 
-def test_fp32_entry_rejects_unbuilt_key_dim():
-    assert call("fp32", d_k=128) == -3
-    assert call("fp16", d_k=128, scan_dir=9) == -5           # direction checked first
+def test_unbuilt_head_dims_are_rejected():
+    for dtype in ("fp16", "fp32", "noalloc"):
+        for dk, dv in ((96, 64), (256, 64), (64, 256), (32, 32)):
+            assert call(dtype, d_k=dk, d_v=dv) == -3, (dtype, dk, dv)
+    assert call("fp32", d_k=96, scan_dir=9) == -5            # direction checked first
 
 
 def test_kernel_event_hook_validation():
@@ -169,7 +172,7 @@ def test_plan_spans_argument_errors():
     a, b = ctypes.c_int(0), ctypes.c_int(0)
     assert lib.gla_plan_spans(0, 1, 12, 128, 128, 64, 64, 64, None, ctypes.byref(b)) == -1
     assert lib.gla_plan_spans(0, 1, 12, 128, 128, 64, 64, 32, ctypes.byref(a), ctypes.byref(b)) == -3
-    assert lib.gla_plan_spans(1, 1, 12, 128, 128, 128, 64, 64, ctypes.byref(a), ctypes.byref(b)) == -3
+    assert lib.gla_plan_spans(1, 1, 12, 128, 128, 96, 64, 64, ctypes.byref(a), ctypes.byref(b)) == -3
     assert lib.gla_plan_spans(0, 0, 12, 128, 128, 64, 64, 64, ctypes.byref(a), ctypes.byref(b)) == -2
 
 

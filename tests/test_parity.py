@@ -74,7 +74,8 @@ def test_odd_grids_multi_span(H, W, d):
 
 
 @pytest.mark.parametrize("dk,dv,dtype", [(64, 128, "fp16"), (128, 64, "fp16"),
-                                         (128, 128, "fp16"), (64, 128, "fp32")])
+                                         (128, 128, "fp16"), (64, 128, "fp32"),
+                                         (128, 64, "fp32"), (128, 128, "fp32")])
 @pytest.mark.parametrize("d", [0, 3])
 def test_head_dims(dk, dv, dtype, d):
     q, k, v, la = make_inputs(1, 2, 24, 21, dk, dv, dtype, 1.0, seed=dk + dv + d)
