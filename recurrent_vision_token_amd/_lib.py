@@ -10,7 +10,9 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libgla.so")
+# GLA_LIBRARY names another build of the same library (the host-sanitizer
+# build, libgla_san.so); by default the in-tree libgla.so
+LIB_PATH = os.environ.get("GLA_LIBRARY") or os.path.join(PKG, "libgla.so")
 
 GLA_OK = 0
 STATUS = {
@@ -43,8 +45,8 @@ def load():
     if _lib is not None:
         return _lib
     if not os.path.exists(LIB_PATH):
-        raise RuntimeError("libgla.so is not built; run python recurrent_vision_token_amd/build.py "
-                           "(hipcc for gfx950)")
+        raise RuntimeError("%s is not built; run python recurrent_vision_token_amd/build.py "
+                           "(hipcc for gfx950)" % LIB_PATH)
     # torch first: it brings its own HIP runtime under the same soname as the
     # system one libgla.so names, and a process gets one of them, the first
     # loaded.  Loading the library first would put torch on a runtime it was

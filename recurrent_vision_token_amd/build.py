@@ -50,7 +50,20 @@ def _run(cmd):
     return out
 
 
-def build(verbose=False):
+# Host sanitizer build (CPU checking of the C-ABI layer): with sanitize=True
+# (command line: --sanitize) gla_api.cpp, the only host-logic source, is also
+# compiled by g++ with AddressSanitizer and UndefinedBehaviorSanitizer and
+# linked with the same device objects into libgla_san.so.  Load it with the
+# sanitizer runtimes preloaded, e.g.
+#   LD_PRELOAD="$(gcc -print-file-name=libasan.so) $(gcc -print-file-name=libubsan.so)" \
+#   ASAN_OPTIONS=detect_leaks=0 GLA_LIBRARY=recurrent_vision_token_amd/libgla_san.so \
+#   python -m pytest tests/test_abi.py tests/test_host_logic.py -m "not gpu"
+LIB_SAN = os.path.join(PKG, "libgla_san.so")
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+             "-fno-omit-frame-pointer", "-g"]
+
+
+def build(verbose=False, sanitize=False):
     hipcc = shutil.which("hipcc") or os.path.join(ROCM, "bin", "hipcc")
     os.makedirs(BUILD, exist_ok=True)
     k_obj = os.path.join(BUILD, "gla_kernels.o")
@@ -73,17 +86,29 @@ def build(verbose=False):
                                             os.path.join(CSRC, "gla_fused.hip"), "-o", f_obj]))
     logs.append(_run([hipcc] + flags_for("gla_noalloc.hip") + ["-I", INCLUDE, "-I", CSRC, "-c",
                                             os.path.join(CSRC, "gla_noalloc.hip"), "-o", n_obj]))
-    logs.append(_run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-D__HIP_PLATFORM_AMD__",
-                      "-I", os.path.join(ROCM, "include"), "-I", INCLUDE, "-I", CSRC, "-c",
-                      os.path.join(CSRC, "gla_api.cpp"), "-o", a_obj]))
+    api_flags = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-D__HIP_PLATFORM_AMD__",
+                 "-I", os.path.join(ROCM, "include"), "-I", INCLUDE, "-I", CSRC]
+    dev_objs = [k_obj, s_obj, g_obj, b_obj, f_obj, n_obj]
+    logs.append(_run(["g++"] + api_flags + ["-c", os.path.join(CSRC, "gla_api.cpp"), "-o", a_obj]))
     tmp = LIB + ".tmp"
-    logs.append(_run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", k_obj, s_obj, g_obj, b_obj, f_obj, n_obj, a_obj,
+    logs.append(_run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC"] + dev_objs + [a_obj,
                       "-o", tmp]))
     os.replace(tmp, LIB)
+    if sanitize:
+        # the same device objects, the host layer instrumented; g++ links its
+        # own sanitizer runtimes
+        san_obj = os.path.join(BUILD, "gla_api_san.o")
+        logs.append(_run(["g++"] + SAN_FLAGS + api_flags +
+                         ["-c", os.path.join(CSRC, "gla_api.cpp"), "-o", san_obj]))
+        tmp = LIB_SAN + ".tmp"
+        logs.append(_run(["g++", "-shared"] + SAN_FLAGS + dev_objs + [san_obj] +
+                         ["-L", os.path.join(ROCM, "lib"), "-lamdhip64", "-o", tmp]))
+        os.replace(tmp, LIB_SAN)
     if verbose:
         print("\n".join(x for x in logs if x.strip()))
     return LIB
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import sys
+    print(build(verbose=True, sanitize="--sanitize" in sys.argv[1:]))
