@@ -172,6 +172,22 @@ int output_slots(int dev, gla::Dtype dt, int d_k, int d_v, bool gate_logits) {
   return n;
 }
 
+// Two-pass output workgroup slots per device (its look-back output kernel's
+// own residency), read once per (device, gate variant).
+std::atomic<int> g_tp_slots[kMaxDevices][2];
+int two_pass_slots(int dev, bool gate_logits) {
+  if (dev < 0 || dev >= kMaxDevices) return 256;
+  int n = g_tp_slots[dev][gate_logits ? 1 : 0].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  n = cus * gla::two_pass_blocks_per_cu(gate_logits);
+  g_tp_slots[dev][gate_logits ? 1 : 0].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 // Single-pass workgroup slots per device (CUs x resident workgroups per CU),
 // read once per (device, gate variant).
 std::atomic<int> g_fused_slots[kMaxDevices][2];
@@ -334,7 +350,8 @@ int forward(gla::Dtype dt, size_t esize, const void* q, const void* k, const voi
     const int slots = output_slots(dev, dt, d_k, d_v, ex.gate_logits);
     if (mode != GLA_FWD_THREE_PASS && mode != GLA_FWD_SINGLE_PASS && !in_place &&
         span_override() == 0 && gla::has_two_pass(dt, d_k, d_v))
-      span_chunks = plan_two_pass(BH, n_chunks, slots, mode == GLA_FWD_TWO_PASS);
+      span_chunks = plan_two_pass(BH, n_chunks, two_pass_slots(dev, ex.gate_logits),
+                                  mode == GLA_FWD_TWO_PASS);
     two_pass = span_chunks > 0;
     if (!two_pass) span_chunks = plan_span_chunks(BH, n_chunks, slots);
   }

@@ -100,6 +100,8 @@ hipError_t launch_forward(Dtype dt, int d_k, int d_v, bool gate_logits, const Fw
 // output kernel).
 constexpr int kTwoPassMaxSpans = 16;
 bool has_two_pass(Dtype dt, int d_k, int d_v);
+// Resident workgroups per CU of the two-pass output kernel.
+int two_pass_blocks_per_cu(bool gate_logits);
 hipError_t launch_forward_two_pass(bool gate_logits, const FwdParams& p, hipStream_t stream,
                                    hipEvent_t const* events);
 

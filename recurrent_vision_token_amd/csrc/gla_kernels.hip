@@ -1570,6 +1570,16 @@ bool has_two_pass(Dtype dt, int d_k, int d_v) {
   return dt == Dtype::kF16 && d_k == 64 && d_v == 64;
 }
 
+int two_pass_blocks_per_cu(bool gate_logits) {
+  int n = 0;
+  const hipError_t e =
+      gate_logits ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                        &n, chunk_output_f16_kernel<64, 64, true, true>, kThreads, 0)
+                  : hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                        &n, chunk_output_f16_kernel<64, 64, false, true>, kThreads, 0);
+  return (e != hipSuccess || n < 1) ? 1 : n;
+}
+
 template <bool GATE>
 hipError_t launch_two_pass_variant(const FwdParams& p, hipStream_t stream, hipEvent_t const* ev) {
   const dim3 grid((unsigned)(p.B * p.heads * p.n_spans));
