@@ -217,6 +217,29 @@ def time_workload(wl, torch, steps, warmup, ext=False, extras=False):
             k_ms["chunk_output"].append(e[4].elapsed_time(e[5]))
             k_ms["call"].append(e[0].elapsed_time(e[5]))
     mean = {k: sum(v) / len(v) for k, v in k_ms.items()}
+    # the measurement protocol of the pages' comparison: an event pair around
+    # every call (no per-kernel hook), 20 warm-up calls, the median of at
+    # least 100 calls (cycling the input sets and directions)
+    n_calls = max(100, steps * ncall)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(n_calls + 1)]
+    for e in marks:
+        e.record(stream)
+    for i in range(20):
+        rc = r.fn(*r.args[i % len(r.args)])
+        if rc != 0:
+            raise RuntimeError("gla_chunk_fwd failed: %d" % rc)
+    torch.cuda.synchronize()
+    marks[0].record(stream)
+    for i in range(n_calls):
+        rc = r.fn(*r.args[i % len(r.args)])
+        if rc != 0:
+            raise RuntimeError("gla_chunk_fwd failed: %d" % rc)
+        marks[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per_call = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(n_calls))
+    pc = lambda f: per_call[min(n_calls - 1, int(f * (n_calls - 1) + 0.5))]
+    mean["per_call_ms"] = {"median": pc(0.5), "p10": pc(0.1), "p90": pc(0.9), "calls": n_calls,
+                           "warmup_calls": 20}
     if extras:
         # per-step spread: plain event records between steps (no per-kernel hook)
         marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
@@ -812,6 +835,12 @@ def summarize(wl, ms_step, mean, ext=False):
                  "kernel_us": {k: round(mean[k] * 1e3, 2) for k in ("span_summary", "span_scan", "chunk_output")},
                  "n_spans": spans, "kernels": kernels},
     }
+    if "per_call_ms" in mean:
+        m = mean["per_call_ms"]
+        out["per_call_us"] = {"median": round(m["median"] * 1e3, 2), "p10": round(m["p10"] * 1e3, 2),
+                              "p90": round(m["p90"] * 1e3, 2), "calls": m["calls"],
+                              "warmup_calls": m["warmup_calls"],
+                              "protocol": "event pair around every call, median"}
     if "step_ms" in mean:
         out["step_ms"] = {k: round(v, 4) for k, v in mean["step_ms"].items()}
     if "warm_ms_step" in mean:
@@ -962,7 +991,8 @@ def main():
         _, ms2, mean2 = time_workload(wl2, torch, max(20, args.steps), max(5, args.warmup))
         s2 = summarize(wl2, ms2, mean2)
         secondary = {"workload": describe(wl2), "value": s2["value"], "unit": "tokens/s",
-                     "ms_per_step": round(ms2, 4), "roofline": s2["roofline"], "path": s2["path"]}
+                     "ms_per_step": round(ms2, 4), "roofline": s2["roofline"], "path": s2["path"],
+                     "per_call_us": s2.get("per_call_us")}
         log("[bench] %s: %.3f ms/step, %.3e tokens/s, %.2f us/call" %
             (wl2.name, ms2, s2["value"], s2["path"]["wall_us_per_call"]))
 
@@ -1083,6 +1113,7 @@ def main():
         "cpu_baseline_all_cores": cpu_all,
         "parity_vs_oracle": parity,
         "device_copy_GBps": round(copy_gbps, 1) if copy_gbps else None,
+        "per_call_us": main_sum.get("per_call_us"),
         "step_ms": main_sum.get("step_ms"),
         "warm": main_sum.get("warm"),
         "secondary": secondary,

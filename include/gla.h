@@ -245,7 +245,7 @@ int gla_plan_spans(int use_f32, int B, int heads, int H, int W, int d_k, int d_v
                    int* span_chunks, int* n_spans);
 
 /*
- * Backward pass (float16; d_k = d_v = 64, chunk = 64): the gradients of
+ * Backward pass (float16; d_k, d_v in {64, 128}, chunk = 64): the gradients of
  *
  *   L = sum(d_out * out) + sum(d_final_state * final_state)
  *
@@ -266,14 +266,22 @@ int gla_plan_spans(int use_f32, int B, int heads, int H, int W, int d_k, int d_v
  * (zero).  Outputs: dq, dk, dlog_alpha [B][heads][H][W][d_k] and dv
  * [B][heads][H][W][d_v] float16 (rounded to nearest even), d_initial_state
  * float32 [B][heads][d_k][d_v] or NULL (not wanted).  Pointers 16-byte
- * aligned; no output may overlap an input or another output.  The call uses
- * a workspace of B*heads*(2*n_spans + 1)*(d_k*d_v + d_k) floats, n_spans =
- * ceil(ceil(H*W/64) / 2).  Domain as gla_chunk_fwd, plus
- * d_out . v and its kin within float16 range.  Errors as gla_chunk_fwd
+ * aligned; no output may overlap an input or another output.  A head wider
+ * than 64 runs as a grid of 64 x 64 blocks (key dims x value dims): the key
+ * rows and value columns of the state evolve independently, so each block is
+ * the 64-dim problem on its dims, dv adds up over the key blocks and dq, dk,
+ * dlog_alpha over the value blocks (each addition of a float16 partial
+ * rounds once more), and d_initial_state is the blocks side by side.  The
+ * call uses a workspace of B*heads*(2*n_spans + 1)*(64*64 + 64) floats,
+ * n_spans = ceil(ceil(H*W/64) / 2), reused by the blocks in turn.  Domain: log_alpha finite and <= 0 with the
+ * decay summed over any 16 consecutive scan steps of one key dim >= -10
+ * (natural log: the backward's scaled float16 tiles use factors up to e^10;
+ * unlike the forward it has no exact fallback), plus d_out . v and its kin
+ * within float16 range.  Errors as gla_chunk_fwd
  * (GLA_ERR_UNSUPPORTED for any other d_k, d_v or chunk).  With the
  * measurement hook armed, event pairs bracket the kernel that forms both
  * summaries of every span (events 0, 1), the kernel that scans both (2, 3)
- * and the chunk kernel (4, 5).
+ * and the chunk kernel (4, 5), of the last block when there are several.
  */
 int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* log_alpha,
                   const void* d_out, const float* d_final_state, const float* initial_state,

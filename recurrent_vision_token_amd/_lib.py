@@ -306,7 +306,7 @@ def raw_call_bwd(q, k, v, la, d_out, d_final, init, scan_dir, B, heads, H, W, d_
 
 def gla_chunk_bwd(q, k, v, log_alpha, d_out, scan_dir, d_final_state=None, initial_state=None,
                   want_d_initial_state=False, chunk=64, stream=None):
-    """Chunkwise backward pass (float16, d_k = d_v = 64).
+    """Chunkwise backward pass (float16, d_k and d_v in {64, 128}).
 
     Gradients of sum(d_out * out) + sum(d_final_state * final_state) for the
     forward call gla_chunk_fwd / gla_chunk_fwd_ex(q, k, v, log_alpha, scan_dir,

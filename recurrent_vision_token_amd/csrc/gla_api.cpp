@@ -555,7 +555,8 @@ int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* log_a
     if (T > (1LL << 30) || BH > (1LL << 30)) return GLA_ERR_SHAPE;
     const long long dmax = d_k > d_v ? d_k : d_v;
     if (T * dmax * 2 >= (1LL << 31)) return GLA_ERR_SHAPE;
-    if (chunk != kChunk || d_k != 64 || d_v != 64) return GLA_ERR_UNSUPPORTED;
+    if (chunk != kChunk || (d_k != 64 && d_k != 128) || (d_v != 64 && d_v != 128))
+      return GLA_ERR_UNSUPPORTED;
     const void* half_t[9] = {q, k, v, log_alpha, d_out, dq, dk, dv, dlog_alpha};
     for (const void* t : half_t)
       if (reinterpret_cast<uintptr_t>(t) % 16 != 0) return GLA_ERR_ALIGN;
@@ -586,13 +587,14 @@ int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* log_a
 
     const int n_chunks = (int)((T + kChunk - 1) / kChunk);
     if (BH * n_chunks > (1LL << 31) - 1) return GLA_ERR_SHAPE;
+    // The recurrence's key rows and value columns evolve independently (the
+    // decay is a diagonal on the key side), so a wider head is a grid of
+    // 64 x 64 blocks: block (kb, vb) is the 64-dim problem on key dims
+    // 64 kb .. and value dims 64 vb .., its gradients add up along the other
+    // axis (dv over key blocks; dq, dk and dlog-alpha over value blocks), and
+    // d_initial_state is the blocks side by side.  The blocks run in order on
+    // the stream, the later ones adding to what the earlier ones stored.
     gla::FwdParams f{};
-    f.q = q;
-    f.k = k;
-    f.v = v;
-    f.la = log_alpha;
-    f.out = dq;  // not touched by the state kernels
-    f.initial_state = initial_state;
     f.inv_tau = 1.f;
     f.B = B;
     f.heads = heads;
@@ -605,12 +607,16 @@ int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* log_a
     f.n_chunks = n_chunks;
     f.span_chunks = 2;  // the chunk kernel forms the other chunk's state of a pair
     f.n_spans = (n_chunks + 1) / 2;
+    f.ldk = (unsigned)d_k;
+    f.ldv = (unsigned)d_v;
+    f.st_row = (unsigned)d_v;
+    f.st_bh = (unsigned)(d_k * d_v);
     const int n_spans = f.n_spans;
 
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const size_t map = (size_t)d_k * d_v;
-    const size_t fwd_floats = (size_t)BH * n_spans * (map + d_k);
-    const size_t adj_floats = (size_t)BH * (n_spans + 1) * (map + d_k);
+    constexpr size_t map = 64 * 64;   // one block's state
+    const size_t fwd_floats = (size_t)BH * n_spans * (map + 64);
+    const size_t adj_floats = (size_t)BH * (n_spans + 1) * (map + 64);
     // the summaries kernel keeps two workgroups per CU (80 KB of LDS each);
     // each streams enough spans for one round over the chip
     int dev = 0;
@@ -628,25 +634,13 @@ int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* log_a
     float* w = static_cast<float*>(ws.ptr());
     f.span_state = w;
     f.span_gate = w + (size_t)BH * n_spans * map;
-    f.dout = d_out;
-    f.adj_initial = d_final_state;
     f.adj_state = w + fwd_floats;
     f.adj_gate = f.adj_state + (size_t)BH * (n_spans + 1) * map;
     f.adj_slots = n_spans + 1;
 
     gla::BwdParams pb{};
-    pb.q = q;
-    pb.k = k;
-    pb.v = v;
-    pb.la = log_alpha;
-    pb.dout = d_out;
-    pb.dq = dq;
-    pb.dk = dk;
-    pb.dv = dv;
-    pb.dla = dlog_alpha;
     pb.fwd_state = f.span_state;
     pb.adj_state = f.adj_state;
-    pb.d_initial_state = d_initial_state;
     pb.B = B;
     pb.heads = heads;
     pb.H = H;
@@ -659,12 +653,48 @@ int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* log_a
     pb.scan_dir = scan_dir;
     pb.n_chunks = n_chunks;
     pb.n_spans = n_spans;
+    pb.ldk = f.ldk;
+    pb.ldv = f.ldv;
+    pb.st_row = f.st_row;
+    pb.st_bh = f.st_bh;
 
+    // with the measurement hook armed, every block's kernels record into the
+    // same event pairs, so they end up bracketing the last block's kernels
     const hipEvent_t* ev = t_events_set ? t_events : nullptr;
     t_events_set = false;
-    hipError_t e = gla::launch_bwd_states(d_k, d_v, f, st, ev);
-    if (e == hipSuccess)
-      e = gla::launch_bwd_chunks(d_k, d_v, pb, st, ev ? ev[4] : nullptr, ev ? ev[5] : nullptr);
+    auto at = [](const void* base, size_t elems, size_t esize) {
+      return base ? static_cast<const void*>(static_cast<const char*>(base) + elems * esize) : nullptr;
+    };
+    hipError_t e = hipSuccess;
+    for (int kb = 0; kb < d_k / 64 && e == hipSuccess; ++kb) {
+      for (int vb = 0; vb < d_v / 64 && e == hipSuccess; ++vb) {
+        const size_t ko = (size_t)64 * kb, vo = (size_t)64 * vb;
+        const size_t so = (size_t)64 * kb * d_v + vo;   // block offset in a [d_k][d_v] state
+        f.q = at(q, ko, 2);
+        f.k = at(k, ko, 2);
+        f.la = at(log_alpha, ko, 2);
+        f.v = at(v, vo, 2);
+        f.dout = at(d_out, vo, 2);
+        f.out = const_cast<void*>(at(dq, ko, 2));  // not touched by the state kernels
+        f.initial_state = static_cast<const float*>(at(initial_state, so, 4));
+        f.adj_initial = static_cast<const float*>(at(d_final_state, so, 4));
+        pb.q = f.q;
+        pb.k = f.k;
+        pb.la = f.la;
+        pb.v = f.v;
+        pb.dout = f.dout;
+        pb.dq = const_cast<void*>(at(dq, ko, 2));
+        pb.dk = const_cast<void*>(at(dk, ko, 2));
+        pb.dla = const_cast<void*>(at(dlog_alpha, ko, 2));
+        pb.dv = const_cast<void*>(at(dv, vo, 2));
+        pb.d_initial_state = const_cast<float*>(static_cast<const float*>(at(d_initial_state, so, 4)));
+        pb.acc_dv = kb > 0;
+        pb.acc_dqk = vb > 0;
+        e = gla::launch_bwd_states(64, 64, f, st, ev);
+        if (e == hipSuccess)
+          e = gla::launch_bwd_chunks(64, 64, pb, st, ev ? ev[4] : nullptr, ev ? ev[5] : nullptr);
+      }
+    }
     if (ws.finish() != hipSuccess) return GLA_ERR_HIP;
     return e == hipSuccess ? GLA_OK : GLA_ERR_HIP;
   } catch (...) {

@@ -106,17 +106,20 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
   gm.sw = p.div_w_s;
   gm.sh = p.div_h_s;
 
-  const uint32_t seq_bytes = (uint32_t)p.T * RB;
-  const size_t so = (size_t)bh * p.T * DK;
-  const rsrc_t rq = seq_rsrc(static_cast<const f16*>(p.q) + so, seq_bytes);
-  const rsrc_t rk = seq_rsrc(static_cast<const f16*>(p.k) + so, seq_bytes);
-  const rsrc_t rla = seq_rsrc(static_cast<const f16*>(p.la) + so, seq_bytes);
-  const rsrc_t rv = seq_rsrc(static_cast<const f16*>(p.v) + so, seq_bytes);
-  const rsrc_t rdo = seq_rsrc(static_cast<const f16*>(p.dout) + so, seq_bytes);
-  const rsrc_t wdq = seq_rsrc(static_cast<f16*>(p.dq) + so, seq_bytes);
-  const rsrc_t wdk = seq_rsrc(static_cast<f16*>(p.dk) + so, seq_bytes);
-  const rsrc_t wdv = seq_rsrc(static_cast<f16*>(p.dv) + so, seq_bytes);
-  const rsrc_t wdla = seq_rsrc(static_cast<f16*>(p.dla) + so, seq_bytes);
+  // rows of ldk (q, k, log-alpha and their gradients) or ldv (v, d_out, dv)
+  // elements: this block's 64 dims of a wider head, or the whole row
+  const uint32_t gsk = p.ldk * 2u, gsv = p.ldv * 2u;  // row strides in bytes
+  const uint32_t kbytes = (uint32_t)p.T * gsk, vbytes = (uint32_t)p.T * gsv;
+  const size_t sok = (size_t)bh * p.T * p.ldk, sov = (size_t)bh * p.T * p.ldv;
+  const rsrc_t rq = seq_rsrc(static_cast<const f16*>(p.q) + sok, kbytes);
+  const rsrc_t rk = seq_rsrc(static_cast<const f16*>(p.k) + sok, kbytes);
+  const rsrc_t rla = seq_rsrc(static_cast<const f16*>(p.la) + sok, kbytes);
+  const rsrc_t rv = seq_rsrc(static_cast<const f16*>(p.v) + sov, vbytes);
+  const rsrc_t rdo = seq_rsrc(static_cast<const f16*>(p.dout) + sov, vbytes);
+  const rsrc_t wdq = seq_rsrc(static_cast<f16*>(p.dq) + sok, kbytes);
+  const rsrc_t wdk = seq_rsrc(static_cast<f16*>(p.dk) + sok, kbytes);
+  const rsrc_t wdv = seq_rsrc(static_cast<f16*>(p.dv) + sov, vbytes);
+  const rsrc_t wdla = seq_rsrc(static_cast<f16*>(p.dla) + sok, kbytes);
   // Chunk c is position pos of span sp (two chunks per span).  The span
   // states give the forward state entering the span's first chunk and the
   // adjoint entering its last chunk from the right; the other chunk of a
@@ -187,13 +190,14 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
     const int blk = wave * 2 + i;
     uint32_t cf;
     bool first;
-    const uint32_t off = dma_offset_cell<RB>(blk, t0, valid, gm, &cf, &first);
+    const uint32_t off = dma_offset_cell_s<RB>(blk, t0, valid, gm, gsk, &cf, &first);
+    const uint32_t offv = dma_offset_s<RB>(blk, t0, valid, gm, gsv);
     if (first) srow[(blk * 1024 + 16 * lane) / RB] = cf;
     dma16(rq, tq + blk * 512, off);
     dma16(rk, tk + blk * 512, off);
-    dma16(rv, tv + blk * 512, off);
+    dma16(rv, tv + blk * 512, offv);
     dma16(rla, tla + blk * 512, off);
-    dma16(rdo, tdo + blk * 512, off);
+    dma16(rdo, tdo + blk * 512, offv);
   }
   if (e_from_partner || r_from_partner) {
     const int tp = e_from_partner ? t0 - kChunk : t0 + kChunk;
@@ -201,10 +205,11 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int blk = wave * 2 + i;
-      const uint32_t off = dma_offset<RB>(blk, tp, vp, gm);
+      const uint32_t off = dma_offset_s<RB>(blk, tp, vp, gm, gsk);
+      const uint32_t offv = dma_offset_s<RB>(blk, tp, vp, gm, gsv);
       dma16(e_from_partner ? rk : rq, tqs + blk * 512, off);
       dma16(rla, tkd + blk * 512, off);
-      dma16(e_from_partner ? rv : rdo, pv + blk * 512, off);
+      dma16(e_from_partner ? rv : rdo, pv + blk * 512, offv);
     }
   }
   wait_barrier<vmcnt_lgkm0_imm(0)>();  // tiles landed, row table written
@@ -401,14 +406,20 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
   }
   __syncthreads();
 
-  auto row_off = [&](int t, int col) -> uint32_t {
+  // a block after the first adds its part of a gradient to what the
+  // earlier blocks stored (the calls of one backward pass run in order)
+  auto store4 = [&](rsrc_t dst, uint32_t gs, bool acc, int t, int col, f32x4 x) {
     const uint32_t cf = srow[t];
-    return ((cf & 0x7fffffffu) * RB + (uint32_t)col * 2) | (cf & 0x80000000u);
+    const uint32_t off = ((cf & 0x7fffffffu) * gs + (uint32_t)col * 2) | (cf & 0x80000000u);
+    if (acc) {
+      const f16x4 old =
+          __builtin_bit_cast(f16x4, __builtin_amdgcn_raw_buffer_load_b64(dst, off, 0, 0));
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[u] += (float)old[u];
+    }
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, to_f16(x)), dst, off, 0, 0);
   };
-  auto store4 = [&](rsrc_t dst, int t, int col, f32x4 x) {
-    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, to_f16(x)), dst, row_off(t, col),
-                                          0, 0);
-  };
+  const bool acc_k = p.acc_dqk != 0, acc_v = p.acc_dv != 0;
 
   // ---- 3a. dq (rows: key dims of this wave, columns: tokens of sub-block I)
   f32x4 dqv[4];
@@ -443,7 +454,7 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) dq[u] = ec[u] * (acc[u] + (float)fb[u] * ed[u]);
     dqv[I] = dq;
-    store4(wdq, t, ki, dq);
+    store4(wdq, gsk, acc_k, t, ki, dq);
   }
 
   // ---- 3b. dk (rows: key dims of this wave, columns: tokens of sub-block J)
@@ -479,7 +490,7 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
     for (int u = 0; u < 4; ++u)
       dk[u] = __builtin_amdgcn_rcpf(ec[u]) * (acc[u] + (float)fe[u] * rv[u]);
     dkv[J] = dk;
-    store4(wdk, t, ki, dk);
+    store4(wdk, gsk, acc_k, t, ki, dk);
   }
 
   // ---- 3c. dv (rows: value dims of this wave, columns: tokens of sub-block J)
@@ -520,7 +531,7 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
     // inter-chunk: (R^T Ke^T)[value dim][token]
     f32x4 rk = mma32(rta[0], ld128(tke + swz<RB>(16 * J + n16, 8 * g)), f32x4{0.f, 0.f, 0.f, 0.f});
     rk = mma32(rta[1], ld128(tke + swz<RB>(16 * J + n16, 32 + 8 * g)), rk);
-    store4(wdv, 16 * J + n16, vj, acc + rk);
+    store4(wdv, gsv, acc_v, 16 * J + n16, vj, acc + rk);
   }
 
   // ---- 4. next state, carry, dlog_alpha
@@ -574,15 +585,16 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
         dla[u] = x[u] + running[u];
         running[u] += dpp_f<kRowBcast + 0>(x[u]);   // the row's total (lane 0)
       }
-      store4(wdla, t, ki, dla);
+      store4(wdla, gsk, acc_k, t, ki, dla);
     }
   }
 
   if (c == 0 && p.d_initial_state != nullptr) {
     const float* src = p.adj_state + ((size_t)bh * (p.n_spans + 1) + p.n_spans) * DK * DV;
-    float* dst = p.d_initial_state + (size_t)bh * DK * DV;
+    float* dst = p.d_initial_state + (size_t)bh * p.st_bh;
     for (int e = tid * 4; e < DK * DV; e += kThreads * 4)
-      *reinterpret_cast<f32x4*>(dst + e) = *reinterpret_cast<const f32x4*>(src + e);
+      *reinterpret_cast<f32x4*>(dst + (size_t)(e / DV) * p.st_row + e % DV) =
+          *reinterpret_cast<const f32x4*>(src + e);
   }
 }
 

@@ -37,6 +37,12 @@ struct FwdParams {
   float* adj_gate;      // [BH][adj_slots][d_k]
   const float* adj_initial;  // the final-state gradient (scan start), may be null
   int spans_per_wg;     // spans streamed by one workgroup of the summaries kernel
+  // the backward pass runs on 64 x 64 blocks of a larger head: row strides of
+  // the [T][d_k]-side tensors (q, k, log-alpha) and the [T][d_v]-side ones
+  // (v, d_out), in elements, and the layout of the caller's [BH][d_k][d_v]
+  // float32 states (adj_initial, initial_state): element (i, j) of sequence
+  // bh at bh * st_bh + i * st_row + j
+  unsigned int ldk, ldv, st_row, st_bh;
   // single-pass forward: hand-off words and span aggregates
   unsigned int* sync;   // [0] ticket, [1] finished workgroups, [2] epoch, [3] error bits,
                         // then one ready flag per (batch*head, span) from word kSyncFlags on
@@ -138,6 +144,14 @@ struct BwdParams {
   int scan_dir;
   int n_chunks;
   int n_spans;              // ceil(n_chunks / 2)
+  // one 64 x 64 block of a larger head: row strides of the [T][d_k]-side
+  // tensors (q, k, log-alpha, dq, dk, dlog-alpha) and the [T][d_v]-side ones
+  // (v, d_out, dv), in elements; d_initial_state's layout as FwdParams'
+  // st_row / st_bh; and which gradients add to what the outputs already hold
+  // (a block after the first along the key dims adds dv, along the value
+  // dims dq, dk and dlog-alpha)
+  unsigned int ldk, ldv, st_row, st_bh;
+  int acc_dv, acc_dqk;
 };
 
 hipError_t launch_bwd_chunks(int d_k, int d_v, const BwdParams& p, hipStream_t stream,

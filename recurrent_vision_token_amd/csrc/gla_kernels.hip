@@ -356,11 +356,13 @@ constexpr int kScanElems = kThreads / kScanSeg;   // state elements per workgrou
 
 // One workgroup scans the state elements yb * kScanElems .. of sequence bh
 // over n_spans summaries (state [BH][n_spans][DK][DV], gate [BH][n_spans][DK]),
-// in place.
+// in place.  The initial state's element (i, j) of sequence bh is at
+// bh * st_bh + i * st_row + j (dense: DK * DV, DV).
 template <int DK, int DV>
 __device__ __forceinline__ void span_scan_body(float* span_state, const float* span_gate,
                                                const float* initial_state, int n_spans, int bh,
-                                               int yb) {
+                                               int yb, size_t st_bh = (size_t)DK * DV,
+                                               unsigned int st_row = DV) {
   __shared__ float seg_l[kScanSeg][kScanElems];
   __shared__ float seg_g[kScanSeg][kScanElems];
   const int seg = threadIdx.x / kScanElems;
@@ -372,7 +374,8 @@ __device__ __forceinline__ void span_scan_body(float* span_state, const float* s
 
   // state entering the current round; the first round starts from the
   // initial state, which the scan also writes as span 0's entry state
-  float carry = initial_state ? initial_state[(size_t)bh * DK * DV + e] : 0.f;
+  float carry =
+      initial_state ? initial_state[(size_t)bh * st_bh + (size_t)dim * st_row + (e - dim * DV)] : 0.f;
   for (int r0 = 0; r0 < n_spans; r0 += kScanSeg * kScanU) {
     const int s0 = r0 + seg * kScanU;
     float l[kScanU], gg[kScanU];
@@ -425,10 +428,10 @@ __global__ __launch_bounds__(kThreads) void bwd_state_scans_kernel(FwdParams p) 
   constexpr int kBlocks = DK * DV / kScanElems;
   if ((int)blockIdx.y < kBlocks) {
     span_scan_body<DK, DV>(p.span_state, p.span_gate, p.initial_state, p.n_spans, blockIdx.x,
-                           blockIdx.y);
+                           blockIdx.y, p.st_bh, p.st_row);
   } else {
     span_scan_body<DK, DV>(p.adj_state, p.adj_gate, p.adj_initial, p.adj_slots, blockIdx.x,
-                           blockIdx.y - kBlocks);
+                           blockIdx.y - kBlocks, p.st_bh, p.st_row);
   }
 }
 
@@ -1372,20 +1375,27 @@ __global__ __launch_bounds__(kThreads) void bwd_state_summaries_kernel(FwdParams
     const Item it = item(i < n_items ? i : 0);
     const bool live = i < n_items && it.live;
     const GridMap gm = grid_map(p, it.bh / p.heads);
-    const SeqBufs sb = seq_bufs<DK, DV>(p, it.bh);
-    const rsrc_t rdo = seq_rsrc(static_cast<const f16*>(p.dout) + (size_t)it.bh * p.T * DV,
-                                (uint32_t)p.T * RBV);
+    // rows of ldk / ldv elements (a 64-dim block of a wider head)
+    typedef _Float16 h;
+    const size_t ok = (size_t)it.bh * p.T * p.ldk, ov = (size_t)it.bh * p.T * p.ldv;
+    const uint32_t kbytes = (uint32_t)p.T * p.ldk * 2u, vbytes = (uint32_t)p.T * p.ldv * 2u;
+    const rsrc_t rk = seq_rsrc(static_cast<const h*>(p.k) + ok, kbytes);
+    const rsrc_t rla = seq_rsrc(static_cast<const h*>(p.la) + ok, kbytes);
+    const rsrc_t rq = seq_rsrc(static_cast<const h*>(p.q) + ok, kbytes);
+    const rsrc_t rv = seq_rsrc(static_cast<const h*>(p.v) + ov, vbytes);
+    const rsrc_t rdo = seq_rsrc(static_cast<const h*>(p.dout) + ov, vbytes);
     const int t0 = it.c * kChunk;
     const int valid = live ? min(kChunk, p.T - t0) : 0;
 #pragma unroll
     for (int j = 0; j < NBK; ++j) {
       const int blk = wave * NBK + j;
-      const uint32_t off = dma_offset<RBK>(blk, t0, valid, gm);
-      dma16(sb.k, f.k + blk * 512, off);
-      dma16(sb.la, f.la + blk * 512, off);
-      dma16(sb.v, f.v + blk * 512, off);
-      dma16(sb.q, a.k + blk * 512, off);
-      dma16(rdo, a.v + blk * 512, off);
+      const uint32_t offk = dma_offset_s<RBK>(blk, t0, valid, gm, p.ldk * 2u);
+      const uint32_t offv = dma_offset_s<RBV>(blk, t0, valid, gm, p.ldv * 2u);
+      dma16(rk, f.k + blk * 512, offk);
+      dma16(rla, f.la + blk * 512, offk);
+      dma16(rv, f.v + blk * 512, offv);
+      dma16(rq, a.k + blk * 512, offk);
+      dma16(rdo, a.v + blk * 512, offv);
     }
   };
 

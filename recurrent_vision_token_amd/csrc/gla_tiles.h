@@ -98,6 +98,32 @@ __device__ __forceinline__ uint32_t dma_offset_cell(int blk, int t0, int valid, 
 }
 
 
+// The same pair for rows of `gs` bytes in memory (a block of a wider row):
+// the tile still holds RB bytes per row, the source row r starts at cell * gs.
+template <int RB>
+__device__ __forceinline__ uint32_t dma_offset_s(int blk, int t0, int valid, const GridMap& gm,
+                                                 uint32_t gs) {
+  const int lane = threadIdx.x & 63;
+  const int byte = blk * 1024 + 16 * lane;
+  const int r = byte / RB, pp = (byte % RB) / 16;
+  const uint32_t off = (uint32_t)gm.cell(t0 + r) * gs + (uint32_t)((pp ^ (r & 7)) * 16);
+  return off | ((uint32_t)(r >= valid) << 31);
+}
+template <int RB>
+__device__ __forceinline__ uint32_t dma_offset_cell_s(int blk, int t0, int valid, const GridMap& gm,
+                                                      uint32_t gs, uint32_t* cell_flag,
+                                                      bool* first_piece) {
+  const int lane = threadIdx.x & 63;
+  const int byte = blk * 1024 + 16 * lane;
+  const int r = byte / RB, pp = (byte % RB) / 16;
+  const uint32_t flag = (uint32_t)(r >= valid) << 31;
+  const uint32_t cell = (uint32_t)gm.cell(t0 + r);
+  *cell_flag = cell | flag;
+  *first_piece = pp == 0;
+  return (cell * gs + (uint32_t)((pp ^ (r & 7)) * 16)) | flag;
+}
+
+
 // ---------------------------------------------------------------------------
 // Per-chunk decay helpers shared by the forward kernels.
 

@@ -40,9 +40,9 @@ def check(got, ref, label, tol=5e-3, mtol=2e-2):
         assert rel <= tol and mx <= mtol, "%s %s: rel %.3g max %.3g" % (label, name, rel, mx)
 
 
-def case(B, heads, H, W, d, seed, gate_std=1.0, states=True):
-    q, k, v, la = make_inputs(B, heads, H, W, 64, 64, "fp16", gate_std, seed)
-    do, dfin, init = make_bwd_inputs(B, heads, H, W, 64, seed=seed + 1)
+def case(B, heads, H, W, d, seed, gate_std=1.0, states=True, dk=64, dv=64):
+    q, k, v, la = make_inputs(B, heads, H, W, dk, dv, "fp16", gate_std, seed)
+    do, dfin, init = make_bwd_inputs(B, heads, H, W, dv, d_k=dk, seed=seed + 1)
     if not states:
         dfin = init = None
     print("bwd case", B, heads, H, W, d, seed, flush=True)
@@ -80,9 +80,38 @@ def test_deterministic():
 
 
 def test_binding_rejects_unbuilt_dims():
-    x = torch.zeros((1, 1, 4, 4, 128), dtype=torch.float16, device=dev())
+    x = torch.zeros((1, 1, 4, 4, 96), dtype=torch.float16, device=dev())
     with pytest.raises(GlaError):
         gla_chunk_bwd(x, x, x, x, x.clone(), 0)
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 64), (64, 128), (128, 128)])
+@pytest.mark.parametrize("d", [0, 3, 4])
+def test_head_dims(dk, dv, d):
+    # wider heads run as 64 x 64 blocks whose gradients add up
+    B = 4 if d == 4 else 1
+    case(B, 2, 21, 19, d, seed=370 + dk + dv + d, dk=dk, dv=dv)
+
+
+def test_batched_shape_sampled():
+    # the batched configuration (32 x 16 sequences of 64 x 64 tokens,
+    # d_k = 128, d_v = 64, directions rotating over the batch): the whole
+    # call on the GPU, a sample of sequences against the oracle
+    wl = WORKLOADS["batched"]
+    B, heads, H, W = wl.B, wl.heads, wl.H, wl.W
+    q, k, v, la = make_inputs(B, heads, H, W, wl.d_k, wl.d_v, "fp16", wl.gate_std, 380)
+    do, dfin, init = make_bwd_inputs(B, heads, H, W, wl.d_v, d_k=wl.d_k, seed=381)
+    print("bwd batched shape", flush=True)
+    got = run(q, k, v, la, do, 4, dfin, init)
+    for x in got:
+        assert np.all(np.isfinite(x))
+    rng = np.random.default_rng(382)
+    for bh in rng.choice(B * heads, 3, replace=False):
+        b, h = divmod(int(bh), heads)
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        ref = gla_backward(q[sl], k[sl], v[sl], la[sl], do[sl], b % 4, d_final_state=dfin[sl],
+                           initial_state=init[sl])
+        check([x[sl] for x in got], ref, "batched b %d h %d" % (b, h))
 
 
 def test_full_size_16k():
