@@ -172,7 +172,9 @@ int gla_set_forward_mode(int mode);
  * takes the work split gla_chunk_fwd would take (gla_plan_forward), except
  * that the single-pass mode is not used: its hand-off words would need an
  * allocation, so under that mode the call takes the automatic choice.  The
- * span states take B*heads*n_spans*(d_k*d_v + d_k) floats; an automatic split
+ * span states take B*heads*n_spans*(d_k*d_v + d_k) floats, plus
+ * B*heads*n_spans*d_k*d_v float16 entry states on the three-pass path (the
+ * workspace of gla_plan_forward's split); an automatic split
  * has at most one span per resident output workgroup, which on an MI355X
  * stays within the array for every supported d_k, d_v.  A split that does not
  * fit (a forced one: gla_set_forward_mode with two or three passes, or
@@ -233,7 +235,8 @@ int gla_chunk_fwd_f32(const float* q, const float* k, const float* v, const floa
  * last may be shorter), one output workgroup per (batch, head, span).  When
  * n_spans > 1 the call also runs the span-summary kernel, and the span-scan
  * kernel on the three-pass path, and uses a workspace of
- * B*heads*n_spans*(d_k*d_v + d_k) floats.  gla_plan_forward also gives the
+ * B*heads*n_spans*(d_k*d_v + d_k) floats, plus B*heads*n_spans*d_k*d_v
+ * float16 entry states on the float16 three-pass path.  gla_plan_forward also gives the
  * number of kernels the call runs: 1 (no split), 2 (two-pass path) or 3
  * (three-pass path; see gla_set_forward_mode).  use_f32 selects the float32
  * entry.  Reads device attributes (a HIP call); returns the same argument

@@ -357,8 +357,12 @@ int forward(gla::Dtype dt, size_t esize, const void* q, const void* k, const voi
   }
   const int n_spans = (n_chunks + span_chunks - 1) / span_chunks;
   if (BH * n_spans > (1LL << 31) - 1 - gla::kSyncFlags) return GLA_ERR_SHAPE;
-  if (no_alloc && n_spans > 1 &&
-      (size_t)(BH * n_spans) * (size_t)(d_k * d_v + d_k) * sizeof(float) > ex.scratch_bytes)
+  // span states: summaries (float32) and, on the float16 three-pass path,
+  // the scan's float16 entry states
+  const bool entry16 = !fused && !two_pass && n_spans > 1 && dt == gla::Dtype::kF16;
+  const size_t span_bytes =
+      (size_t)(d_k * d_v + d_k) * sizeof(float) + (entry16 ? (size_t)d_k * d_v * 2 : 0);
+  if (no_alloc && n_spans > 1 && (size_t)(BH * n_spans) * span_bytes > ex.scratch_bytes)
     return GLA_ERR_SCRATCH;
   if (plan_only != nullptr) {
     plan_only[0] = span_chunks;
@@ -390,12 +394,15 @@ int forward(gla::Dtype dt, size_t esize, const void* q, const void* k, const voi
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   WsLease ws;
+  const size_t state_elems = (size_t)BH * n_spans * d_k * d_v;
+  const size_t gate_elems = (size_t)BH * n_spans * d_k;
   if (no_alloc) {
     if (n_spans > 1) {
       float* base = static_cast<float*>(ex.scratch_of(dev));
       if (base == nullptr) return GLA_ERR_HIP;
       p.span_state = base;
-      p.span_gate = base + (size_t)BH * n_spans * d_k * d_v;
+      p.span_gate = base + state_elems;
+      if (entry16) p.span_entry16 = p.span_gate + gate_elems;
     }
   } else if (fused) {
     // span summaries (gate product + state) and one hand-off word per span
@@ -406,11 +413,10 @@ int forward(gla::Dtype dt, size_t esize, const void* q, const void* k, const voi
     p.agg = static_cast<float*>(ws.ptr());
     p.sync = ws.sync();
   } else if (n_spans > 1) {
-    const size_t state_elems = (size_t)BH * n_spans * d_k * d_v;
-    const size_t gate_elems = (size_t)BH * n_spans * d_k;
-    if (ws.acquire(st, (state_elems + gate_elems) * sizeof(float)) != hipSuccess) return GLA_ERR_HIP;
+    if (ws.acquire(st, (size_t)BH * n_spans * span_bytes) != hipSuccess) return GLA_ERR_HIP;
     p.span_state = static_cast<float*>(ws.ptr());
     p.span_gate = p.span_state + state_elems;
+    if (entry16) p.span_entry16 = p.span_gate + gate_elems;   // 4-byte aligned, 2-byte elements
   }
   const hipEvent_t* ev = t_events_set ? t_events : nullptr;
   t_events_set = false;

@@ -22,6 +22,7 @@ struct FwdParams {
   float* span_state;    // [BH][n_spans][d_k][d_v] span summaries, then entry states (three
                         // passes), or summaries in the output kernel's layout (two passes)
   float* span_gate;     // [BH][n_spans][d_k] product of the span's gates
+  void* span_entry16;   // [BH][n_spans][d_k][d_v] float16 entry states (float16 three passes)
   int B, heads, H, W, T;
   // t / W and t / H as (umulhi(t, m) + t) >> s, exact for t < 2^31
   unsigned int div_w_m, div_h_m;

@@ -358,11 +358,13 @@ constexpr int kScanElems = kThreads / kScanSeg;   // state elements per workgrou
 // over n_spans summaries (state [BH][n_spans][DK][DV], gate [BH][n_spans][DK]),
 // in place.  The initial state's element (i, j) of sequence bh is at
 // bh * st_bh + i * st_row + j (dense: DK * DV, DV).
+// With entry16 set, the entry states go there as float16 [BH][n_spans][DK][DV]
+// instead of over the summaries.
 template <int DK, int DV>
 __device__ __forceinline__ void span_scan_body(float* span_state, const float* span_gate,
                                                const float* initial_state, int n_spans, int bh,
                                                int yb, size_t st_bh = (size_t)DK * DV,
-                                               unsigned int st_row = DV) {
+                                               unsigned int st_row = DV, f16* entry16 = nullptr) {
   __shared__ float seg_l[kScanSeg][kScanElems];
   __shared__ float seg_g[kScanSeg][kScanElems];
   const int seg = threadIdx.x / kScanElems;
@@ -370,6 +372,7 @@ __device__ __forceinline__ void span_scan_body(float* span_state, const float* s
   const int e = yb * kScanElems + le;
   const int dim = e / DV;
   float* const L = span_state + (size_t)bh * n_spans * DK * DV + e;
+  f16* const Lh = entry16 ? entry16 + (size_t)bh * n_spans * DK * DV + e : nullptr;
   const float* const G = span_gate + (size_t)bh * n_spans * DK + dim;
 
   // state entering the current round; the first round starts from the
@@ -406,7 +409,12 @@ __device__ __forceinline__ void span_scan_body(float* span_state, const float* s
     }
 #pragma unroll
     for (int u = 0; u < kScanU; ++u) {
-      if (s0 + u < n_spans) L[(size_t)(s0 + u) * DK * DV] = run;
+      if (s0 + u < n_spans) {
+        if (Lh)
+          Lh[(size_t)(s0 + u) * DK * DV] = (f16)run;
+        else
+          L[(size_t)(s0 + u) * DK * DV] = run;
+      }
       run = gg[u] * run + l[u];
     }
     carry = next;
@@ -414,10 +422,11 @@ __device__ __forceinline__ void span_scan_body(float* span_state, const float* s
   }
 }
 
-template <int DK, int DV>
+template <int DK, int DV, bool E16 = false>
 __global__ __launch_bounds__(kThreads) void span_scan_kernel(FwdParams p) {
   span_scan_body<DK, DV>(p.span_state, p.span_gate, p.initial_state, p.n_spans, blockIdx.x,
-                         blockIdx.y);
+                         blockIdx.y, (size_t)DK * DV, DV,
+                         E16 ? static_cast<f16*>(p.span_entry16) : nullptr);
 }
 
 // The backward pass's two scans in one launch: blockIdx.y below half the grid
@@ -718,6 +727,20 @@ __device__ __forceinline__ void load_state_tiles(const float* src, int wave, int
     for (int r = 0; r < DK / 16; ++r)
 #pragma unroll
       for (int u = 0; u < 4; ++u) st[r][j][u] = src ? src[(16 * r + 4 * g + u) * DV + col] : 0.f;
+  }
+}
+
+// The same from a float16 state (the three-pass scan's entry states).
+template <int DK, int DV>
+__device__ __forceinline__ void load_state_tiles16(const f16* src, int wave, int n16, int g,
+                                                   f32x4 (&st)[DK / 16][DV / 64]) {
+#pragma unroll
+  for (int j = 0; j < DV / 64; ++j) {
+    const int col = 16 * (wave + 4 * j) + n16;
+#pragma unroll
+    for (int r = 0; r < DK / 16; ++r)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) st[r][j][u] = (float)src[(16 * r + 4 * g + u) * DV + col];
   }
 }
 
@@ -1025,10 +1048,15 @@ __global__ __launch_bounds__(kThreads, LOOKBACK ? 2 : (DK == 64 && DV == 64) ? 4
   f32x4 st[DK / 16][DV / 64];
   const StepTiles<DK, DV> slot0{q0, k0, la0, v0}, slot1{q1, k1, la1, v1};
   if constexpr (!LOOKBACK) {
-    load_state_tiles<DK, DV>(
-        (p.n_spans > 1) ? p.span_state + ((size_t)bh * p.n_spans + span) * DK * DV
-        : p.initial_state ? p.initial_state + (size_t)bh * DK * DV : nullptr,
-        wave, lane & 15, lane >> 4, st);
+    // the scan's entry states come as float16 (they enter the products as
+    // float16 operands anyway; the state update runs on from them in float32)
+    if (p.n_spans > 1)
+      load_state_tiles16<DK, DV>(
+          static_cast<const f16*>(p.span_entry16) + ((size_t)bh * p.n_spans + span) * DK * DV,
+          wave, lane & 15, lane >> 4, st);
+    else
+      load_state_tiles<DK, DV>(p.initial_state ? p.initial_state + (size_t)bh * DK * DV : nullptr,
+                               wave, lane & 15, lane >> 4, st);
     output_span<DK, DV, GATE>(p, bh, span, slot0, slot1, sqt, sgd, srow, sxf, st, [](auto&) {});
   } else {
     const int g = lane >> 4;
@@ -1503,12 +1531,14 @@ hipError_t skip_one(hipStream_t stream, hipEvent_t const* ev, int slot) {
 template <class T, int DK, int DV, bool GATE>
 hipError_t launch_variant(const FwdParams& p, hipStream_t stream, hipEvent_t const* ev) {
   using F = Family<T, DK, DV, GATE>;
+  constexpr bool kE16 = std::is_same<T, f16>::value;  // float16 entry states
   const int BH = p.B * p.heads;
   hipError_t e;
   if (p.n_spans > 1) {
+    if (kE16 && p.span_entry16 == nullptr) return hipErrorInvalidValue;
     if ((e = launch_one(F::summary, dim3(BH * p.n_spans), stream, p, ev, 0)) != hipSuccess) return e;
-    if ((e = launch_one(span_scan_kernel<DK, DV>, dim3(BH, DK * DV / kScanElems), stream, p, ev,
-                        1)) != hipSuccess)
+    if ((e = launch_one(span_scan_kernel<DK, DV, kE16>, dim3(BH, DK * DV / kScanElems), stream, p,
+                        ev, 1)) != hipSuccess)
       return e;
   } else {
     if ((e = skip_one(stream, ev, 0)) != hipSuccess) return e;
