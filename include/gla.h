@@ -275,8 +275,9 @@ int gla_plan_spans(int use_f32, int B, int heads, int H, int W, int d_k, int d_v
  * the 64-dim problem on its dims, dv adds up over the key blocks and dq, dk,
  * dlog_alpha over the value blocks (each addition of a float16 partial
  * rounds once more), and d_initial_state is the blocks side by side.  The
- * call uses a workspace of B*heads*(2*n_spans + 1)*(64*64 + 64) floats,
- * n_spans = ceil(ceil(H*W/64) / 2), reused by the blocks in turn.  Domain: log_alpha finite and <= 0 with the
+ * call uses a workspace of B*heads*(2*n_spans + 1)*(64*64 + 64) floats plus
+ * B*heads*(2*n_spans + 1)*64*64 float16 span states, n_spans =
+ * ceil(ceil(H*W/64) / 2), reused by the blocks in turn.  Domain: log_alpha finite and <= 0 with the
  * decay summed over any 16 consecutive scan steps of one key dim >= -10
  * (natural log: the backward's scaled float16 tiles use factors up to e^10;
  * unlike the forward it has no exact fallback), plus d_out . v and its kin

@@ -635,18 +635,26 @@ int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* log_a
     const long long total_spans = BH * n_spans;
     const long long wg_slots = 2LL * cu_count(dev);
     f.spans_per_wg = spw_override ? spw_override : (int)((total_spans + wg_slots - 1) / wg_slots);
+    // float32 summaries and gates of both recurrences, then the scans'
+    // float16 entry states (the chunk kernel's operands)
+    const size_t fwd16 = (size_t)BH * n_spans * map, adj16 = (size_t)BH * (n_spans + 1) * map;
     WsLease ws;
-    if (ws.acquire(st, (fwd_floats + adj_floats) * sizeof(float)) != hipSuccess) return GLA_ERR_HIP;
+    if (ws.acquire(st, (fwd_floats + adj_floats) * sizeof(float) + (fwd16 + adj16) * 2) !=
+        hipSuccess)
+      return GLA_ERR_HIP;
     float* w = static_cast<float*>(ws.ptr());
     f.span_state = w;
     f.span_gate = w + (size_t)BH * n_spans * map;
     f.adj_state = w + fwd_floats;
     f.adj_gate = f.adj_state + (size_t)BH * (n_spans + 1) * map;
     f.adj_slots = n_spans + 1;
+    f.span_entry16 = w + fwd_floats + adj_floats;
+    f.adj_entry16 = static_cast<char*>(f.span_entry16) + fwd16 * 2;
 
     gla::BwdParams pb{};
-    pb.fwd_state = f.span_state;
-    pb.adj_state = f.adj_state;
+    pb.fwd_state = f.span_entry16;
+    pb.adj_state = f.adj_entry16;
+    pb.adj_last = f.adj_state;
     pb.B = B;
     pb.heads = heads;
     pb.H = H;

@@ -130,9 +130,10 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
   const int span_len = min(2, p.n_chunks - 2 * sp);
   const bool e_from_partner = pos == 1;
   const bool r_from_partner = pos == 0 && span_len == 2;
-  const float* E_span = p.fwd_state + ((size_t)bh * p.n_spans + sp) * DK * DV;
-  const float* R_span =
-      p.adj_state + ((size_t)bh * (p.n_spans + 1) + (p.n_spans - 1 - sp)) * DK * DV;
+  // the span states come from the scans as float16
+  const f16* E_span = static_cast<const f16*>(p.fwd_state) + ((size_t)bh * p.n_spans + sp) * DK * DV;
+  const f16* R_span = static_cast<const f16*>(p.adj_state) +
+                      ((size_t)bh * (p.n_spans + 1) + (p.n_spans - 1 - sp)) * DK * DV;
   float* const stage = sEc;  // the partner-formed state, before sEc is needed
   const int kb = wave;          // key dims 16 kb .. owned by this wave (dq, dk, dla)
   const int vb = wave;          // value dims 16 vb .. (dv, next state rows)
@@ -146,37 +147,38 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
   // is, the MFMA operand layouts below (raw float32 until the tiles landed)
   // (32-bit byte offsets from the workgroup's span-state bases, so each load
   // is one uniform base plus one lane offset)
-  f32x4 e4s[4], r4s[4], ea_raw[4], ra_raw[4];
-  float rta_raw[16];
-  auto ld4 = [](const float* base, uint32_t byte_off) {
-    return *reinterpret_cast<const f32x4*>(reinterpret_cast<const char*>(base) + byte_off);
+  // (raw float16 bits until the tiles landed)
+  u32x2 e4h[4], r4h[4], eah[4], rah[4];
+  unsigned short rtah[16];
+  auto ld4 = [](const f16* base, uint32_t byte_off) {
+    return *reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(base) + byte_off);
   };
-  auto ld1 = [](const float* base, uint32_t byte_off) {
-    return *reinterpret_cast<const float*>(reinterpret_cast<const char*>(base) + byte_off);
+  auto ld1 = [](const f16* base, uint32_t byte_off) {
+    return *reinterpret_cast<const unsigned short*>(reinterpret_cast<const char*>(base) + byte_off);
   };
-  const uint32_t o_acc = 4u * (uint32_t)(n16 * DV + vj);            // row n, columns vj ..
-  const uint32_t o_op = 4u * (uint32_t)((16 * kb + n16) * DV + 8 * g);  // row 16 kb + n, cols 8g ..
-  const uint32_t o_t = 4u * (uint32_t)(8 * g * DV + 16 * vb + n16);   // R[8g][16 vb + n]
+  const uint32_t o_acc = 2u * (uint32_t)(n16 * DV + vj);            // row n, columns vj ..
+  const uint32_t o_op = 2u * (uint32_t)((16 * kb + n16) * DV + 8 * g);  // row 16 kb + n, cols 8g ..
+  const uint32_t o_t = 2u * (uint32_t)(8 * g * DV + 16 * vb + n16);   // R[8g][16 vb + n]
 #pragma unroll
   for (int kc = 0; kc < 4; ++kc) {
-    e4s[kc] = ld4(E_span, o_acc + 4u * 16 * kc * DV);
-    r4s[kc] = ld4(R_span, o_acc + 4u * 16 * kc * DV);
+    e4h[kc] = ld4(E_span, o_acc + 2u * 16 * kc * DV);
+    r4h[kc] = ld4(R_span, o_acc + 2u * 16 * kc * DV);
   }
   if (!e_from_partner) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      ea_raw[2 * h] = ld4(E_span, o_op + 4u * 32 * h);
-      ea_raw[2 * h + 1] = ld4(E_span, o_op + 4u * (32 * h + 4));
+      eah[2 * h] = ld4(E_span, o_op + 2u * 32 * h);
+      eah[2 * h + 1] = ld4(E_span, o_op + 2u * (32 * h + 4));
     }
   }
   if (!r_from_partner) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      ra_raw[2 * h] = ld4(R_span, o_op + 4u * 32 * h);
-      ra_raw[2 * h + 1] = ld4(R_span, o_op + 4u * (32 * h + 4));
+      rah[2 * h] = ld4(R_span, o_op + 2u * 32 * h);
+      rah[2 * h + 1] = ld4(R_span, o_op + 2u * (32 * h + 4));
       // R^T rows 16 vb + n: R[32 h + 8g + e][16 vb + n]
 #pragma unroll
-      for (int e = 0; e < 8; ++e) rta_raw[8 * h + e] = ld1(R_span, o_t + 4u * (32 * h + e) * DV);
+      for (int e = 0; e < 8; ++e) rtah[8 * h + e] = ld1(R_span, o_t + 2u * (32 * h + e) * DV);
     }
   }
 
@@ -217,11 +219,21 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
   // conversions (and so the compiler's waits for them) after the wait above
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    asm volatile("" : "+v"(ea_raw[j]), "+v"(ra_raw[j]));
-    asm volatile("" : "+v"(e4s[j]), "+v"(r4s[j]));
+    asm volatile("" : "+v"(eah[j]), "+v"(rah[j]));
+    asm volatile("" : "+v"(e4h[j]), "+v"(r4h[j]));
   }
 #pragma unroll
-  for (int j = 0; j < 16; ++j) asm volatile("" : "+v"(rta_raw[j]));
+  for (int j = 0; j < 16; ++j) asm volatile("" : "+v"(rtah[j]));
+  auto wide = [](u32x2 x) {
+    const f16x4 h = __builtin_bit_cast(f16x4, x);
+    return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+  };
+  f32x4 e4s[4], r4s[4];
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc) {
+    e4s[kc] = wide(e4h[kc]);
+    r4s[kc] = wide(r4h[kc]);
+  }
 
   if (e_from_partner || r_from_partner) {
     // partner decay profile per key dim: keys decayed to the partner's end
@@ -316,7 +328,7 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
     if (e_from_partner) {
       ea[h] = ld8f(stage + (16 * kb + n16) * ES + 32 * h + 8 * g);
     } else {
-      ea[h] = cat8(to_f16(ea_raw[2 * h]), to_f16(ea_raw[2 * h + 1]));
+      ea[h] = cat8(__builtin_bit_cast(f16x4, eah[2 * h]), __builtin_bit_cast(f16x4, eah[2 * h + 1]));
     }
     f16x8 x;
     if (r_from_partner) {
@@ -324,9 +336,9 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = (f16)stage[(32 * h + 8 * g + e) * ES + 16 * vb + n16];
     } else {
-      ra[h] = cat8(to_f16(ra_raw[2 * h]), to_f16(ra_raw[2 * h + 1]));
+      ra[h] = cat8(__builtin_bit_cast(f16x4, rah[2 * h]), __builtin_bit_cast(f16x4, rah[2 * h + 1]));
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = (f16)rta_raw[8 * h + e];
+      for (int e = 0; e < 8; ++e) x[e] = __builtin_bit_cast(f16, rtah[8 * h + e]);
     }
     rta[h] = x;
   }
@@ -590,7 +602,7 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
   }
 
   if (c == 0 && p.d_initial_state != nullptr) {
-    const float* src = p.adj_state + ((size_t)bh * (p.n_spans + 1) + p.n_spans) * DK * DV;
+    const float* src = p.adj_last + ((size_t)bh * (p.n_spans + 1) + p.n_spans) * DK * DV;
     float* dst = p.d_initial_state + (size_t)bh * p.st_bh;
     for (int e = tid * 4; e < DK * DV; e += kThreads * 4)
       *reinterpret_cast<f32x4*>(dst + (size_t)(e / DV) * p.st_row + e % DV) =

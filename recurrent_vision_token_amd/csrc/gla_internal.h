@@ -36,6 +36,8 @@ struct FwdParams {
   const void* dout;     // the output gradient, in place of v
   float* adj_state;     // [BH][adj_slots][d_k][d_v]
   float* adj_gate;      // [BH][adj_slots][d_k]
+  void* adj_entry16;    // [BH][adj_slots][d_k][d_v] float16 adjoint entry states (all slots but
+                        // the last, which stays float32 in adj_state)
   const float* adj_initial;  // the final-state gradient (scan start), may be null
   int spans_per_wg;     // spans streamed by one workgroup of the summaries kernel
   // the backward pass runs on 64 x 64 blocks of a larger head: row strides of
@@ -135,9 +137,11 @@ struct BwdParams {
   void* dk;
   void* dv;                 // [B][heads][H][W][d_v]
   void* dla;                // [B][heads][H][W][d_k]
-  const float* fwd_state;   // [BH][n_spans][d_k][d_v] state entering each span of two chunks
-  const float* adj_state;   // [BH][n_spans + 1][d_k][d_v]: slot n_spans - 1 - s enters span s's
-                            // last chunk from the right; slot n_spans is dL/dS_{-1}
+  const void* fwd_state;    // [BH][n_spans][d_k][d_v] float16: state entering each span of two chunks
+  const void* adj_state;    // [BH][n_spans + 1][d_k][d_v] float16: slot n_spans - 1 - s enters
+                            // span s's last chunk from the right
+  const float* adj_last;    // [BH][n_spans + 1][d_k][d_v] float32, of which slot n_spans
+                            // (dL/dS_{-1}) is read
   float* d_initial_state;   // [BH][d_k][d_v], or null
   int B, heads, H, W, T;
   unsigned int div_w_m, div_h_m;

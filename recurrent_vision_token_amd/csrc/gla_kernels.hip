@@ -358,13 +358,15 @@ constexpr int kScanElems = kThreads / kScanSeg;   // state elements per workgrou
 // over n_spans summaries (state [BH][n_spans][DK][DV], gate [BH][n_spans][DK]),
 // in place.  The initial state's element (i, j) of sequence bh is at
 // bh * st_bh + i * st_row + j (dense: DK * DV, DV).
-// With entry16 set, the entry states go there as float16 [BH][n_spans][DK][DV]
-// instead of over the summaries.
+// With entry16 set, the entry states of spans below f32_from go there as
+// float16 [BH][n_spans][DK][DV] instead of over the summaries (the others
+// still over the summaries, in float32).
 template <int DK, int DV>
 __device__ __forceinline__ void span_scan_body(float* span_state, const float* span_gate,
                                                const float* initial_state, int n_spans, int bh,
                                                int yb, size_t st_bh = (size_t)DK * DV,
-                                               unsigned int st_row = DV, f16* entry16 = nullptr) {
+                                               unsigned int st_row = DV, f16* entry16 = nullptr,
+                                               int f32_from = 1 << 30) {
   __shared__ float seg_l[kScanSeg][kScanElems];
   __shared__ float seg_g[kScanSeg][kScanElems];
   const int seg = threadIdx.x / kScanElems;
@@ -410,7 +412,7 @@ __device__ __forceinline__ void span_scan_body(float* span_state, const float* s
 #pragma unroll
     for (int u = 0; u < kScanU; ++u) {
       if (s0 + u < n_spans) {
-        if (Lh)
+        if (Lh && s0 + u < f32_from)
           Lh[(size_t)(s0 + u) * DK * DV] = (f16)run;
         else
           L[(size_t)(s0 + u) * DK * DV] = run;
@@ -437,10 +439,13 @@ __global__ __launch_bounds__(kThreads) void bwd_state_scans_kernel(FwdParams p) 
   constexpr int kBlocks = DK * DV / kScanElems;
   if ((int)blockIdx.y < kBlocks) {
     span_scan_body<DK, DV>(p.span_state, p.span_gate, p.initial_state, p.n_spans, blockIdx.x,
-                           blockIdx.y, p.st_bh, p.st_row);
+                           blockIdx.y, p.st_bh, p.st_row, static_cast<f16*>(p.span_entry16));
   } else {
+    // the last slot (the gradient of the state before the first step, copied
+    // out as d_initial_state) stays float32
     span_scan_body<DK, DV>(p.adj_state, p.adj_gate, p.adj_initial, p.adj_slots, blockIdx.x,
-                           blockIdx.y - kBlocks, p.st_bh, p.st_row);
+                           blockIdx.y - kBlocks, p.st_bh, p.st_row,
+                           static_cast<f16*>(p.adj_entry16), p.adj_slots - 1);
   }
 }
 
