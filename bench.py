@@ -100,15 +100,17 @@ def kernel_bytes(wl, n_spans, kernels=3):
     th = wl.B * wl.heads * wl.T
     bh = wl.B * wl.heads
     st = wl.d_k * wl.d_v * 4
+    # entry states of the three-pass path: float16 on the float16 path
+    st_entry = wl.d_k * wl.d_v * es
     if kernels == 2:
         entry = bh * n_spans * (n_spans - 1) // 2 * (st + 4 * wl.d_k)
     else:
-        entry = bh * n_spans * st if n_spans > 1 else 0
+        entry = bh * n_spans * st_entry if n_spans > 1 else 0
     out = {"chunk_output": th * es * (3 * wl.d_k + 2 * wl.d_v) + bh * st + entry}
     if n_spans > 1:
         out["span_summary"] = th * es * (2 * wl.d_k + wl.d_v) + bh * n_spans * (st + 4 * wl.d_k)
         if kernels == 3:
-            out["span_scan"] = bh * n_spans * (2 * st + 4 * wl.d_k)
+            out["span_scan"] = bh * n_spans * (st + 4 * wl.d_k + st_entry)
     return out
 
 
@@ -439,7 +441,8 @@ def bwd_bytes(wl):
     st = wl.d_k * wl.d_v * 4
     n = -(-wl.T // wl.chunk)
     tensors = th * 2 * (3 * wl.d_k + 2 * wl.d_v) + th * 2 * (3 * wl.d_k + wl.d_v)
-    return {"call": tensors + 3 * bh * st, "chunk_bwd": tensors + 2 * bh * n * st + bh * st}
+    # every chunk reads its span's forward and adjoint entry states (float16)
+    return {"call": tensors + 3 * bh * st, "chunk_bwd": tensors + 2 * bh * n * (st // 2) + bh * st}
 
 
 def time_bwd(wl, torch, steps, warmup):

@@ -106,10 +106,12 @@ def test_kernel_bytes_of_both_forward_paths():
     from recurrent_vision_token_amd.workloads import WORKLOADS
     wl = WORKLOADS["gtr1.6k"]
     bh, st, gate = wl.B * wl.heads, 64 * 64 * 4, 64 * 4
+    st16 = 64 * 64 * 2      # float16 entry states of the three-pass path
     io = wl.B * wl.heads * wl.T * 2 * (3 * 64 + 2 * 64)
     three = bench.kernel_bytes(wl, 13, 3)
     two = bench.kernel_bytes(wl, 13, 2)
-    assert three["chunk_output"] == io + bh * st + bh * 13 * st
+    assert three["chunk_output"] == io + bh * st + bh * 13 * st16
+    assert three["span_scan"] == bh * 13 * (st + gate + st16)
     assert two["chunk_output"] == io + bh * st + bh * (13 * 12 // 2) * (st + gate)
     assert "span_scan" in three and "span_scan" not in two
     assert two["span_summary"] == three["span_summary"]
