@@ -435,14 +435,14 @@ def bwd_bytes(wl):
     """Algorithmic bytes of one backward call: read q, k, v, log_alpha, d_out,
     write dq, dk, dv, dlog_alpha (fp16), the states in and out (fp32); and the
     chunk kernel's own traffic, which adds the forward and adjoint state of
-    every chunk (fp32) to the tensors."""
+    every chunk (fp16) to the tensors."""
     th = wl.B * wl.heads * wl.T
     bh = wl.B * wl.heads
     st = wl.d_k * wl.d_v * 4
     n = -(-wl.T // wl.chunk)
     tensors = th * 2 * (3 * wl.d_k + 2 * wl.d_v) + th * 2 * (3 * wl.d_k + wl.d_v)
-    # every chunk reads its span's forward and adjoint entry states (float16)
-    return {"call": tensors + 3 * bh * st, "chunk_bwd": tensors + 2 * bh * n * (st // 2) + bh * st}
+    # every chunk reads its forward and adjoint entry states (float16)
+    return {"call": tensors + 3 * bh * st, "chunk_bwd": tensors + 2 * bh * n * (st // 2)}
 
 
 def time_bwd(wl, torch, steps, warmup):

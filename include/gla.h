@@ -259,10 +259,12 @@ int gla_plan_spans(int use_f32, int B, int heads, int H, int W, int d_k, int d_v
  * dv_t = k_t G_t, dlog_alpha_t = alpha_t * rowsum(G_t * S_{t-1}) and
  * d_initial_state = diag(alpha_0) G_0; the pass is chunkwise like the
  * forward one (GTR news write-up, sections "What linear attention saves" and
- * "Where the speed comes from"): forward entry states and the adjoint states
- * entering each chunk from its right come from the span-summary / span-scan
- * kernels (the adjoint recurrence is the forward one read from the end), then
- * every chunk computes its gradients independently.
+ * "Where the speed comes from"): the forward state entering each chunk and
+ * the adjoint state entering it from its right come from a summary kernel and
+ * a scan kernel over chunks (the adjoint recurrence is the forward one read
+ * from the end; per-chunk summaries and states are kept as float16, the scans
+ * accumulate in float32), then every chunk computes its gradients
+ * independently.
  *
  * Layout as gla_chunk_fwd; d_out is [B][heads][H][W][d_v] float16;
  * d_final_state and initial_state are float32 [B][heads][d_k][d_v] or NULL
@@ -275,16 +277,16 @@ int gla_plan_spans(int use_f32, int B, int heads, int H, int W, int d_k, int d_v
  * the 64-dim problem on its dims, dv adds up over the key blocks and dq, dk,
  * dlog_alpha over the value blocks (each addition of a float16 partial
  * rounds once more), and d_initial_state is the blocks side by side.  The
- * call uses a workspace of B*heads*(2*n_spans + 1)*(64*64 + 64) floats plus
- * B*heads*(2*n_spans + 1)*64*64 float16 span states, n_spans =
- * ceil(ceil(H*W/64) / 2), reused by the blocks in turn.  Domain: log_alpha finite and <= 0 with the
+ * call uses a workspace of B*heads*2*n_chunks*64 floats plus
+ * B*heads*2*n_chunks*64*64 float16 chunk states, n_chunks =
+ * ceil(H*W/64), reused by the blocks in turn.  Domain: log_alpha finite and <= 0 with the
  * decay summed over any 16 consecutive scan steps of one key dim >= -10
  * (natural log: the backward's scaled float16 tiles use factors up to e^10;
- * unlike the forward it has no exact fallback), plus d_out . v and its kin
- * within float16 range.  Errors as gla_chunk_fwd
+ * unlike the forward it has no exact fallback), plus d_out . v, both states
+ * and their per-chunk summaries within float16 range.  Errors as gla_chunk_fwd
  * (GLA_ERR_UNSUPPORTED for any other d_k, d_v or chunk).  With the
  * measurement hook armed, event pairs bracket the kernel that forms both
- * summaries of every span (events 0, 1), the kernel that scans both (2, 3)
+ * summaries of every chunk (events 0, 1), the kernel that scans both (2, 3)
  * and the chunk kernel (4, 5), of the last block when there are several.
  */
 int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* log_alpha,

@@ -611,8 +611,9 @@ int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* log_a
     gla::fast_div_constants((unsigned)H, &f.div_h_m, &f.div_h_s);
     f.scan_dir = scan_dir;
     f.n_chunks = n_chunks;
-    f.span_chunks = 2;  // the chunk kernel forms the other chunk's state of a pair
-    f.n_spans = (n_chunks + 1) / 2;
+    // spans of one chunk: the scans give every chunk both of its states
+    f.span_chunks = 1;
+    f.n_spans = n_chunks;
     f.ldk = (unsigned)d_k;
     f.ldv = (unsigned)d_v;
     f.st_row = (unsigned)d_v;
@@ -621,8 +622,6 @@ int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* log_a
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     constexpr size_t map = 64 * 64;   // one block's state
-    const size_t fwd_floats = (size_t)BH * n_spans * (map + 64);
-    const size_t adj_floats = (size_t)BH * (n_spans + 1) * (map + 64);
     // the summaries kernel keeps two workgroups per CU (80 KB of LDS each);
     // each streams enough spans for one round over the chip
     int dev = 0;
@@ -635,26 +634,23 @@ int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* log_a
     const long long total_spans = BH * n_spans;
     const long long wg_slots = 2LL * cu_count(dev);
     f.spans_per_wg = spw_override ? spw_override : (int)((total_spans + wg_slots - 1) / wg_slots);
-    // float32 summaries and gates of both recurrences, then the scans'
-    // float16 entry states (the chunk kernel's operands)
-    const size_t fwd16 = (size_t)BH * n_spans * map, adj16 = (size_t)BH * (n_spans + 1) * map;
+    // float32 gate products of both recurrences, then their float16
+    // summaries, which the scans overwrite with the entry states (the chunk
+    // kernel's operands)
+    const size_t slots = (size_t)BH * n_spans;   // of each recurrence
     WsLease ws;
-    if (ws.acquire(st, (fwd_floats + adj_floats) * sizeof(float) + (fwd16 + adj16) * 2) !=
-        hipSuccess)
+    if (ws.acquire(st, 2 * slots * (64 * sizeof(float) + map * 2)) != hipSuccess)
       return GLA_ERR_HIP;
     float* w = static_cast<float*>(ws.ptr());
-    f.span_state = w;
-    f.span_gate = w + (size_t)BH * n_spans * map;
-    f.adj_state = w + fwd_floats;
-    f.adj_gate = f.adj_state + (size_t)BH * (n_spans + 1) * map;
-    f.adj_slots = n_spans + 1;
-    f.span_entry16 = w + fwd_floats + adj_floats;
-    f.adj_entry16 = static_cast<char*>(f.span_entry16) + fwd16 * 2;
+    f.span_gate = w;
+    f.adj_gate = w + slots * 64;
+    f.adj_slots = n_spans;
+    f.span_entry16 = w + 2 * slots * 64;
+    f.adj_entry16 = static_cast<char*>(f.span_entry16) + slots * map * 2;
 
     gla::BwdParams pb{};
     pb.fwd_state = f.span_entry16;
     pb.adj_state = f.adj_entry16;
-    pb.adj_last = f.adj_state;
     pb.B = B;
     pb.heads = heads;
     pb.H = H;
@@ -666,11 +662,8 @@ int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* log_a
     pb.div_h_s = f.div_h_s;
     pb.scan_dir = scan_dir;
     pb.n_chunks = n_chunks;
-    pb.n_spans = n_spans;
     pb.ldk = f.ldk;
     pb.ldv = f.ldv;
-    pb.st_row = f.st_row;
-    pb.st_bh = f.st_bh;
 
     // with the measurement hook armed, every block's kernels record into the
     // same event pairs, so they end up bracketing the last block's kernels
@@ -701,7 +694,7 @@ int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* log_a
         pb.dk = const_cast<void*>(at(dk, ko, 2));
         pb.dla = const_cast<void*>(at(dlog_alpha, ko, 2));
         pb.dv = const_cast<void*>(at(dv, vo, 2));
-        pb.d_initial_state = const_cast<float*>(static_cast<const float*>(at(d_initial_state, so, 4)));
+        f.adj_final = const_cast<float*>(static_cast<const float*>(at(d_initial_state, so, 4)));
         pb.acc_dv = kb > 0;
         pb.acc_dqk = vb > 0;
         e = gla::launch_bwd_states(64, 64, f, st, ev);

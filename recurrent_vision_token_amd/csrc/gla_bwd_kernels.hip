@@ -20,8 +20,9 @@
 // (the last term is the same sum over every later token, by the adjoint
 // identity dlog_alpha_t = alpha_t * rowsum(G_t * S_{t-1}) at the chunk's end).
 //
-// The chunk kernel (one workgroup per (batch*head, chunk), wave w owning key
-// dims and value dims 16w..16w+15):
+// The state kernels work on spans of one chunk, so every chunk finds both of
+// its states (float16) in memory.  The chunk kernel (one workgroup per
+// (batch*head, chunk), wave w owning key dims and value dims 16w..16w+15):
 //   1. q, k, v, log-alpha and dO land in LDS (LDS-writing loads, swizzled
 //      rows); B is summed per key dim in float32;
 //   2. float16 operand tiles with every decay factor bounded: Qs = q e^{c}
@@ -63,21 +64,14 @@ __device__ __forceinline__ float dpp_f(float x) {
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
 
-__device__ __forceinline__ f16x8 ld8f(const float* a) {
-  const f32x4 lo = *reinterpret_cast<const f32x4*>(a);
-  const f32x4 hi = *reinterpret_cast<const f32x4*>(a + 4);
-  return cat8(to_f16(lo), to_f16(hi));
-}
-
 template <int DK, int DV>
 __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
   static_assert(DK == 64 && DV == 64, "built for 64 key and value dims");
   constexpr int RB = 128;  // bytes per tile row
-  // row stride (floats) of sEc and of a state staged there: 4 floats of
-  // padding move consecutive rows 4 banks apart, so 16 lanes reading 16 bytes
-  // each from 16 rows hit 64 different banks
+  // row stride (floats) of sEc: 4 floats of padding move consecutive rows 4
+  // banks apart, so 16 lanes reading 16 bytes each from 16 rows hit 64
+  // different banks
   constexpr int ES = DK + 4;
-  static_assert(DK == DV, "the staged state shares sEc's row stride");
   __shared__ __attribute__((aligned(16))) f16 tq[kChunk * DK], tk[kChunk * DK], tv[kChunk * DV];
   __shared__ __attribute__((aligned(16))) f16 tla[kChunk * DK], tdo[kChunk * DV];
   __shared__ __attribute__((aligned(16))) f16 tqs[kChunk * DK], tkd[kChunk * DK];
@@ -120,34 +114,22 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
   const rsrc_t wdk = seq_rsrc(static_cast<f16*>(p.dk) + sok, kbytes);
   const rsrc_t wdv = seq_rsrc(static_cast<f16*>(p.dv) + sov, vbytes);
   const rsrc_t wdla = seq_rsrc(static_cast<f16*>(p.dla) + sok, kbytes);
-  // Chunk c is position pos of span sp (two chunks per span).  The span
-  // states give the forward state entering the span's first chunk and the
-  // adjoint entering its last chunk from the right; the other chunk of a
-  // two-chunk span forms the missing one from its partner's tiles:
-  //   second chunk: E_c = diag(g_{c-1}) E_span + (Ke_{c-1})^T V_{c-1}
-  //   first chunk:  R_c = diag(g_{c+1}) R_span + (Q_{c+1} e^{B})^T dO_{c+1}
-  const int sp = c >> 1, pos = c & 1;
-  const int span_len = min(2, p.n_chunks - 2 * sp);
-  const bool e_from_partner = pos == 1;
-  const bool r_from_partner = pos == 0 && span_len == 2;
-  // the span states come from the scans as float16
-  const f16* E_span = static_cast<const f16*>(p.fwd_state) + ((size_t)bh * p.n_spans + sp) * DK * DV;
-  const f16* R_span = static_cast<const f16*>(p.adj_state) +
-                      ((size_t)bh * (p.n_spans + 1) + (p.n_spans - 1 - sp)) * DK * DV;
-  float* const stage = sEc;  // the partner-formed state, before sEc is needed
+  // the states of this chunk, float16 from the scans: the forward state
+  // entering it and the adjoint entering it from the right
+  const f16* E_c = static_cast<const f16*>(p.fwd_state) + ((size_t)bh * p.n_chunks + c) * DK * DV;
+  const f16* R_c = static_cast<const f16*>(p.adj_state) +
+                   ((size_t)bh * p.n_chunks + (p.n_chunks - 1 - c)) * DK * DV;
   const int kb = wave;          // key dims 16 kb .. owned by this wave (dq, dk, dla)
   const int vb = wave;          // value dims 16 vb .. (dv, next state rows)
   const int ki = 16 * kb + 4 * g;  // first of the lane's 4 key dims in a dq / dk tile
   const int vj = 16 * vb + 4 * g;
 
-  // ---- 0. the span states, read from memory before the tiles so that their
+  // ---- 0. the states, read from memory before the tiles so that their
   // latency hides behind the tiles': E and R in the accumulator layout of the
-  // next-state update (rows 16 kc + n, columns 16 w + 4g ..; for the state a
-  // partner completes, the span's part of it), and, for a state taken as it
-  // is, the MFMA operand layouts below (raw float32 until the tiles landed)
-  // (32-bit byte offsets from the workgroup's span-state bases, so each load
-  // is one uniform base plus one lane offset)
-  // (raw float16 bits until the tiles landed)
+  // next-state update (rows 16 kc + n, columns 16 w + 4g ..) and in the MFMA
+  // operand layouts below (raw float16 bits until the tiles landed; 32-bit
+  // byte offsets from the state bases, so each load is one uniform base plus
+  // one lane offset)
   u32x2 e4h[4], r4h[4], eah[4], rah[4];
   unsigned short rtah[16];
   auto ld4 = [](const f16* base, uint32_t byte_off) {
@@ -161,32 +143,23 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
   const uint32_t o_t = 2u * (uint32_t)(8 * g * DV + 16 * vb + n16);   // R[8g][16 vb + n]
 #pragma unroll
   for (int kc = 0; kc < 4; ++kc) {
-    e4h[kc] = ld4(E_span, o_acc + 2u * 16 * kc * DV);
-    r4h[kc] = ld4(R_span, o_acc + 2u * 16 * kc * DV);
+    e4h[kc] = ld4(E_c, o_acc + 2u * 16 * kc * DV);
+    r4h[kc] = ld4(R_c, o_acc + 2u * 16 * kc * DV);
   }
-  if (!e_from_partner) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      eah[2 * h] = ld4(E_span, o_op + 2u * 32 * h);
-      eah[2 * h + 1] = ld4(E_span, o_op + 2u * (32 * h + 4));
-    }
-  }
-  if (!r_from_partner) {
+  for (int h = 0; h < 2; ++h) {
+    eah[2 * h] = ld4(E_c, o_op + 2u * 32 * h);
+    eah[2 * h + 1] = ld4(E_c, o_op + 2u * (32 * h + 4));
+    rah[2 * h] = ld4(R_c, o_op + 2u * 32 * h);
+    rah[2 * h + 1] = ld4(R_c, o_op + 2u * (32 * h + 4));
+    // R^T rows 16 vb + n: R[32 h + 8g + e][16 vb + n]
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      rah[2 * h] = ld4(R_span, o_op + 2u * 32 * h);
-      rah[2 * h + 1] = ld4(R_span, o_op + 2u * (32 * h + 4));
-      // R^T rows 16 vb + n: R[32 h + 8g + e][16 vb + n]
-#pragma unroll
-      for (int e = 0; e < 8; ++e) rtah[8 * h + e] = ld1(R_span, o_t + 2u * (32 * h + e) * DV);
-    }
+    for (int e = 0; e < 8; ++e) rtah[8 * h + e] = ld1(R_c, o_t + 2u * (32 * h + e) * DV);
   }
 
-  // ---- 1. tiles (and the partner's: keys or queries, log-alpha, values or
-  // output gradients into the operand-tile and sEc areas), cumulative decay
+  // ---- 1. tiles, cumulative decay
   const int t0 = c * kChunk;
   const int valid = min(kChunk, p.T - t0);
-  f16* const pv = reinterpret_cast<f16*>(sEc);  // partner value tile (8 KB of sEc)
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int blk = wave * 2 + i;
@@ -200,19 +173,6 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
     dma16(rv, tv + blk * 512, offv);
     dma16(rla, tla + blk * 512, off);
     dma16(rdo, tdo + blk * 512, offv);
-  }
-  if (e_from_partner || r_from_partner) {
-    const int tp = e_from_partner ? t0 - kChunk : t0 + kChunk;
-    const int vp = min(kChunk, p.T - tp);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int blk = wave * 2 + i;
-      const uint32_t off = dma_offset_s<RB>(blk, tp, vp, gm, gsk);
-      const uint32_t offv = dma_offset_s<RB>(blk, tp, vp, gm, gsv);
-      dma16(e_from_partner ? rk : rq, tqs + blk * 512, off);
-      dma16(rla, tkd + blk * 512, off);
-      dma16(e_from_partner ? rv : rdo, pv + blk * 512, offv);
-    }
   }
   wait_barrier<vmcnt_lgkm0_imm(0)>();  // tiles landed, row table written
   // the raw state values are used from here on only: the empty asm keeps their
@@ -234,115 +194,19 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
     e4s[kc] = wide(e4h[kc]);
     r4s[kc] = wide(r4h[kc]);
   }
-
-  if (e_from_partner || r_from_partner) {
-    // partner decay profile per key dim: keys decayed to the partner's end
-    // (exclusive of the token), or queries decayed from its start (inclusive);
-    // thread (key-dim pair, half of a 16-token sub-block)
-    const int i2 = tid & 31, h = (tid >> 5) & 1, J = tid >> 6;
-    const int i = 2 * i2;
-    float al0[8], al1[8], tot0 = 0.f, tot1 = 0.f;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const f16x2 la2 = *reinterpret_cast<const f16x2*>(&tkd[swz<RB>(16 * J + 8 * h + u, i)]);
-      const float l0 = (float)la2[0], l1 = (float)la2[1];
-      al0[u] = ex(l0);
-      al1[u] = ex(l1);
-      tot0 += l0;
-      tot1 += l1;
-    }
-    const float ot0 = __shfl_xor(tot0, 32), ot1 = __shfl_xor(tot1, 32);
-    if (h == 0) *reinterpret_cast<f32x2*>(&sTot[J][i]) = f32x2{tot0 + ot0, tot1 + ot1};
-    __syncthreads();
-    float before0 = 0.f, before1 = 0.f, after0 = 0.f, after1 = 0.f, all0 = 0.f, all1 = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x2 t2 = *reinterpret_cast<const f32x2*>(&sTot[j][i]);
-      before0 += j < J ? t2[0] : 0.f;
-      before1 += j < J ? t2[1] : 0.f;
-      after0 += j > J ? t2[0] : 0.f;
-      after1 += j > J ? t2[1] : 0.f;
-      all0 += t2[0];
-      all1 += t2[1];
-    }
-    if (J == 0 && h == 0) *reinterpret_cast<f32x2*>(&sCarry[0][i]) = f32x2{ex(all0), ex(all1)};
-    if (e_from_partner) {
-      // the second half's tokens come after the first's
-      float sfx0 = ex(h ? after0 : after0 + ot0), sfx1 = ex(h ? after1 : after1 + ot1);
-#pragma unroll
-      for (int u = 7; u >= 0; --u) {
-        const int e = swz<RB>(16 * J + 8 * h + u, i);
-        const f16x2 x2 = *reinterpret_cast<const f16x2*>(&tqs[e]);
-        *reinterpret_cast<f16x2*>(&tkd[e]) = f16x2{(f16)((float)x2[0] * sfx0), (f16)((float)x2[1] * sfx1)};
-        sfx0 *= al0[u];
-        sfx1 *= al1[u];
-      }
-    } else {
-      float pre0 = ex(h ? before0 + ot0 : before0), pre1 = ex(h ? before1 + ot1 : before1);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int e = swz<RB>(16 * J + 8 * h + u, i);
-        pre0 *= al0[u];
-        pre1 *= al1[u];
-        const f16x2 x2 = *reinterpret_cast<const f16x2*>(&tqs[e]);
-        *reinterpret_cast<f16x2*>(&tkd[e]) = f16x2{(f16)((float)x2[0] * pre0), (f16)((float)x2[1] * pre1)};
-      }
-    }
-    __syncthreads();
-    // wave w: columns 16 w .. of the state, all rows: the partner's
-    // contribution as (values)^T (decayed keys or queries) over its tokens
-    f32x4 st[4];
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int P = 0; P < 2; ++P) {
-        const f16x8 av = cat8(tr_read<RB>(pv, 32 * P, 16 * wave), tr_read<RB>(pv, 32 * P + 16, 16 * wave));
-        const f16x8 bk = cat8(tr_read<RB>(tkd, 32 * P, 16 * kc), tr_read<RB>(tkd, 32 * P + 16, 16 * kc));
-        acc = mma32(av, bk, acc);
-      }
-      st[kc] = acc;
-    }
-    f32x4 x[4];
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      const int row = 16 * kc + n16;
-      x[kc] = sCarry[0][row] * (e_from_partner ? e4s[kc] : r4s[kc]) + st[kc];
-      if (e_from_partner) e4s[kc] = x[kc];
-      else r4s[kc] = x[kc];
-    }
-    __syncthreads();  // every wave is done with the partner tiles in sEc
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc)
-      *reinterpret_cast<f32x4*>(stage + (16 * kc + n16) * ES + vj) = x[kc];
-    __syncthreads();
-  }
-
-  // This chunk's states as float16 MFMA A operands: E and R rows of the
+  // this chunk's states as float16 MFMA A operands: E and R rows of the
   // wave's key dims (lane (n, g): row 16 kb + n, columns 32 h + 8g .. + 7) and
-  // R^T rows of its value dims; a partner-formed state is read from the stage
-  // while it is still in place.
+  // R^T rows of its value dims
   f16x8 ea[2], ra[2], rta[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    if (e_from_partner) {
-      ea[h] = ld8f(stage + (16 * kb + n16) * ES + 32 * h + 8 * g);
-    } else {
-      ea[h] = cat8(__builtin_bit_cast(f16x4, eah[2 * h]), __builtin_bit_cast(f16x4, eah[2 * h + 1]));
-    }
+    ea[h] = cat8(__builtin_bit_cast(f16x4, eah[2 * h]), __builtin_bit_cast(f16x4, eah[2 * h + 1]));
+    ra[h] = cat8(__builtin_bit_cast(f16x4, rah[2 * h]), __builtin_bit_cast(f16x4, rah[2 * h + 1]));
     f16x8 x;
-    if (r_from_partner) {
-      ra[h] = ld8f(stage + (16 * kb + n16) * ES + 32 * h + 8 * g);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = (f16)stage[(32 * h + 8 * g + e) * ES + 16 * vb + n16];
-    } else {
-      ra[h] = cat8(__builtin_bit_cast(f16x4, rah[2 * h]), __builtin_bit_cast(f16x4, rah[2 * h + 1]));
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = __builtin_bit_cast(f16, rtah[8 * h + e]);
-    }
+    for (int e = 0; e < 8; ++e) x[e] = __builtin_bit_cast(f16, rtah[8 * h + e]);
     rta[h] = x;
   }
-  __syncthreads();  // the staging area becomes sEc
 
   // Thread (key dims 2 i2, 2 i2 + 1; tokens 8h .. 8h + 7 of sub-block J, its
   // wave) walks its tokens: alpha_t = e^{la_t}, e^{c_t} as a running product
@@ -599,14 +463,6 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
       }
       store4(wdla, gsk, acc_k, t, ki, dla);
     }
-  }
-
-  if (c == 0 && p.d_initial_state != nullptr) {
-    const float* src = p.adj_last + ((size_t)bh * (p.n_spans + 1) + p.n_spans) * DK * DV;
-    float* dst = p.d_initial_state + (size_t)bh * p.st_bh;
-    for (int e = tid * 4; e < DK * DV; e += kThreads * 4)
-      *reinterpret_cast<f32x4*>(dst + (size_t)(e / DV) * p.st_row + e % DV) =
-          *reinterpret_cast<const f32x4*>(src + e);
   }
 }
 

@@ -31,20 +31,21 @@ struct FwdParams {
   int n_chunks;         // ceil(T / 64)
   int span_chunks;      // chunks handled by one workgroup of the output kernel
   int n_spans;          // ceil(n_chunks / span_chunks)
-  // backward pass: the adjoint recurrence's inputs and summaries
-  int adj_slots;        // summary slots per sequence of the adjoint scan (n_spans + 1)
+  // backward pass (spans of one chunk): span_entry16 holds the float16 forward
+  // summaries, then the entry states; the adjoint recurrence likewise
+  int adj_slots;        // summary slots per sequence of the adjoint scan (n_spans)
   const void* dout;     // the output gradient, in place of v
-  float* adj_state;     // [BH][adj_slots][d_k][d_v]
   float* adj_gate;      // [BH][adj_slots][d_k]
-  void* adj_entry16;    // [BH][adj_slots][d_k][d_v] float16 adjoint entry states (all slots but
-                        // the last, which stays float32 in adj_state)
+  void* adj_entry16;    // [BH][adj_slots][d_k][d_v] float16 adjoint summaries, then entry states
   const float* adj_initial;  // the final-state gradient (scan start), may be null
+  float* adj_final;     // the adjoint state after its last slot (the gradient of the state
+                        // before the first step), float32 in the initial state's layout, or null
   int spans_per_wg;     // spans streamed by one workgroup of the summaries kernel
   // the backward pass runs on 64 x 64 blocks of a larger head: row strides of
   // the [T][d_k]-side tensors (q, k, log-alpha) and the [T][d_v]-side ones
   // (v, d_out), in elements, and the layout of the caller's [BH][d_k][d_v]
-  // float32 states (adj_initial, initial_state): element (i, j) of sequence
-  // bh at bh * st_bh + i * st_row + j
+  // float32 states (adj_initial, initial_state, adj_final): element (i, j) of
+  // sequence bh at bh * st_bh + i * st_row + j
   unsigned int ldk, ldv, st_row, st_bh;
   // single-pass forward: hand-off words and span aggregates
   unsigned int* sync;   // [0] ticket, [1] finished workgroups, [2] epoch, [3] error bits,
@@ -115,12 +116,12 @@ hipError_t launch_forward_two_pass(bool gate_logits, const FwdParams& p, hipStre
                                    hipEvent_t const* events);
 
 // Backward pass, float16, d_k = d_v = 64.  `p` describes the forward
-// tensors (q, k, v, la; spans of span_chunks chunks, n_spans of them) with
-// the forward-state workspace (span_state, span_gate, initial_state) and the
-// adjoint recurrence: dout, adj_state, adj_gate, adj_initial (the final-state
-// gradient) and adj_slots = n_spans + 1.  Runs the fused summaries kernel
-// and the fused scans kernel; events: null, or at least four hipEvent_t, the
-// start / stop of each.
+// tensors (q, k, v, la; spans of one chunk, n_spans = n_chunks of them) with
+// the forward-state workspace (span_entry16, span_gate, initial_state) and
+// the adjoint recurrence: dout, adj_entry16, adj_gate, adj_initial (the
+// final-state gradient), adj_slots = n_spans and adj_final.  Runs the
+// fused summaries kernel and the fused scans kernel; events: null, or at
+// least four hipEvent_t, the start / stop of each.
 hipError_t launch_bwd_states(int d_k, int d_v, const FwdParams& p, hipStream_t stream,
                              hipEvent_t const* events);
 
@@ -137,25 +138,20 @@ struct BwdParams {
   void* dk;
   void* dv;                 // [B][heads][H][W][d_v]
   void* dla;                // [B][heads][H][W][d_k]
-  const void* fwd_state;    // [BH][n_spans][d_k][d_v] float16: state entering each span of two chunks
-  const void* adj_state;    // [BH][n_spans + 1][d_k][d_v] float16: slot n_spans - 1 - s enters
-                            // span s's last chunk from the right
-  const float* adj_last;    // [BH][n_spans + 1][d_k][d_v] float32, of which slot n_spans
-                            // (dL/dS_{-1}) is read
-  float* d_initial_state;   // [BH][d_k][d_v], or null
+  const void* fwd_state;    // [BH][n_chunks][d_k][d_v] float16: the state entering chunk c
+  const void* adj_state;    // [BH][n_chunks][d_k][d_v] float16: slot n_chunks - 1 - c is the
+                            // state gradient entering chunk c from the right
   int B, heads, H, W, T;
   unsigned int div_w_m, div_h_m;
   int div_w_s, div_h_s;
   int scan_dir;
   int n_chunks;
-  int n_spans;              // ceil(n_chunks / 2)
   // one 64 x 64 block of a larger head: row strides of the [T][d_k]-side
   // tensors (q, k, log-alpha, dq, dk, dlog-alpha) and the [T][d_v]-side ones
-  // (v, d_out, dv), in elements; d_initial_state's layout as FwdParams'
-  // st_row / st_bh; and which gradients add to what the outputs already hold
-  // (a block after the first along the key dims adds dv, along the value
-  // dims dq, dk and dlog-alpha)
-  unsigned int ldk, ldv, st_row, st_bh;
+  // (v, d_out, dv), in elements; and which gradients add to what the outputs
+  // already hold (a block after the first along the key dims adds dv, along
+  // the value dims dq, dk and dlog-alpha)
+  unsigned int ldk, ldv;
   int acc_dv, acc_dqk;
 };
 

@@ -355,18 +355,14 @@ constexpr int kScanU = 32;
 constexpr int kScanElems = kThreads / kScanSeg;   // state elements per workgroup
 
 // One workgroup scans the state elements yb * kScanElems .. of sequence bh
-// over n_spans summaries (state [BH][n_spans][DK][DV], gate [BH][n_spans][DK]),
-// in place.  The initial state's element (i, j) of sequence bh is at
-// bh * st_bh + i * st_row + j (dense: DK * DV, DV).
-// With entry16 set, the entry states of spans below f32_from go there as
-// float16 [BH][n_spans][DK][DV] instead of over the summaries (the others
-// still over the summaries, in float32).
+// over n_spans summaries (state [BH][n_spans][DK][DV], gate [BH][n_spans][DK],
+// initial state [BH][DK][DV] or null), in place; with entry16 set, the entry
+// states go there as float16 [BH][n_spans][DK][DV] instead of over the
+// summaries.
 template <int DK, int DV>
 __device__ __forceinline__ void span_scan_body(float* span_state, const float* span_gate,
                                                const float* initial_state, int n_spans, int bh,
-                                               int yb, size_t st_bh = (size_t)DK * DV,
-                                               unsigned int st_row = DV, f16* entry16 = nullptr,
-                                               int f32_from = 1 << 30) {
+                                               int yb, f16* entry16) {
   __shared__ float seg_l[kScanSeg][kScanElems];
   __shared__ float seg_g[kScanSeg][kScanElems];
   const int seg = threadIdx.x / kScanElems;
@@ -379,8 +375,7 @@ __device__ __forceinline__ void span_scan_body(float* span_state, const float* s
 
   // state entering the current round; the first round starts from the
   // initial state, which the scan also writes as span 0's entry state
-  float carry =
-      initial_state ? initial_state[(size_t)bh * st_bh + (size_t)dim * st_row + (e - dim * DV)] : 0.f;
+  float carry = initial_state ? initial_state[(size_t)bh * DK * DV + e] : 0.f;
   for (int r0 = 0; r0 < n_spans; r0 += kScanSeg * kScanU) {
     const int s0 = r0 + seg * kScanU;
     float l[kScanU], gg[kScanU];
@@ -412,7 +407,7 @@ __device__ __forceinline__ void span_scan_body(float* span_state, const float* s
 #pragma unroll
     for (int u = 0; u < kScanU; ++u) {
       if (s0 + u < n_spans) {
-        if (Lh && s0 + u < f32_from)
+        if (Lh)
           Lh[(size_t)(s0 + u) * DK * DV] = (f16)run;
         else
           L[(size_t)(s0 + u) * DK * DV] = run;
@@ -427,26 +422,97 @@ __device__ __forceinline__ void span_scan_body(float* span_state, const float* s
 template <int DK, int DV, bool E16 = false>
 __global__ __launch_bounds__(kThreads) void span_scan_kernel(FwdParams p) {
   span_scan_body<DK, DV>(p.span_state, p.span_gate, p.initial_state, p.n_spans, blockIdx.x,
-                         blockIdx.y, (size_t)DK * DV, DV,
-                         E16 ? static_cast<f16*>(p.span_entry16) : nullptr);
+                         blockIdx.y, E16 ? static_cast<f16*>(p.span_entry16) : nullptr);
+}
+
+// The backward pass's scans run over float16 chunk summaries (one chunk per
+// span), in place: each slot's summary is replaced by the float16 state
+// entering that slot.  The slots of a round are cut into kBScanSeg segments
+// of kBScanU, one row of 16 lanes per segment, each lane taking 4 adjacent
+// elements (a row reads 128 contiguous bytes per slot), so a round spans 256
+// slots; the segments' folds meet through LDS as in span_scan_body.  The
+// caller's float32 states sit at bh * st_bh + i * st_row + j: `init` the
+// state before the first slot (or null: zero), `final_out` (or null) receives
+// the state after the last slot.
+constexpr int kBScanSeg = 16;
+constexpr int kBScanU = 16;
+constexpr int kBScanElems = 4 * kThreads / kBScanSeg;  // state elements per workgroup
+template <int DK, int DV>
+__device__ __forceinline__ void bwd_scan_body(f16* sum16, const float* gate, const float* init,
+                                              int n_slots, int bh, int yb, size_t st_bh,
+                                              unsigned int st_row, float* final_out) {
+  static_assert(DV % 4 == 0 && kBScanElems <= DV, "a workgroup's elements share one state row");
+  __shared__ f32x4 seg_l[kBScanSeg][kBScanElems / 4];
+  __shared__ float seg_g[kBScanSeg][kBScanElems / 4];
+  const int lg = threadIdx.x & 15;   // the lane's elements: 4 lg .. of the workgroup's
+  const int seg = threadIdx.x >> 4;
+  const int e = yb * kBScanElems + 4 * lg;
+  const int dim = e / DV, col = e - dim * DV;
+  // one sequence's slots as buffers (the host keeps them under 2^31 bytes):
+  // slots at or past n_slots read as zero and their stores are dropped, so
+  // every load is issued unconditionally
+  const rsrc_t rl = seq_rsrc(sum16 + (size_t)bh * n_slots * DK * DV, (uint32_t)n_slots * DK * DV * 2);
+  const rsrc_t rg = seq_rsrc(gate + (size_t)bh * n_slots * DK, (uint32_t)n_slots * DK * 4);
+  const size_t io = (size_t)bh * st_bh + (size_t)dim * st_row + col;
+
+  f32x4 carry = init ? *reinterpret_cast<const f32x4*>(init + io) : f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int r0 = 0; r0 < n_slots; r0 += kBScanSeg * kBScanU) {
+    const int s0 = r0 + seg * kBScanU;
+    f32x4 l[kBScanU];
+    float gg[kBScanU];
+#pragma unroll
+    for (int u = 0; u < kBScanU; ++u) {
+      const uint32_t sl = (uint32_t)(s0 + u);
+      const f16x4 lv = __builtin_bit_cast(
+          f16x4, __builtin_amdgcn_raw_buffer_load_b64(rl, (sl * DK * DV + e) * 2u, 0, 0));
+      const float gv = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(rg, (sl * DK + dim) * 4u, 0, 0));
+      l[u] = f32x4{(float)lv[0], (float)lv[1], (float)lv[2], (float)lv[3]};
+      gg[u] = gv + (sl < (uint32_t)n_slots ? 0.f : 1.f);  // a slot past the end: gate 1
+    }
+    f32x4 fl = f32x4{0.f, 0.f, 0.f, 0.f};
+    float fg = 1.f;
+#pragma unroll
+    for (int u = 0; u < kBScanU; ++u) {
+      fl = gg[u] * fl + l[u];
+      fg *= gg[u];
+    }
+    seg_l[seg][lg] = fl;
+    seg_g[seg][lg] = fg;
+    __syncthreads();
+    f32x4 run = carry, next = carry;
+    for (int j = 0; j < kBScanSeg; ++j) {
+      const f32x4 lj = seg_l[j][lg];
+      const float gj = seg_g[j][lg];
+      if (j < seg) run = gj * run + lj;
+      next = gj * next + lj;
+    }
+#pragma unroll
+    for (int u = 0; u < kBScanU; ++u) {
+      const uint32_t sl = (uint32_t)(s0 + u);
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, to_f16(run)), rl,
+                                            (sl * DK * DV + e) * 2u, 0, 0);
+      run = gg[u] * run + l[u];
+    }
+    carry = next;
+    __syncthreads();  // the LDS folds are reused by the next round
+  }
+  if (final_out && seg == 0) *reinterpret_cast<f32x4*>(final_out + io) = carry;
 }
 
 // The backward pass's two scans in one launch: blockIdx.y below half the grid
 // scans the forward summaries (from the initial state), the rest the adjoint
-// summaries (from the final-state gradient; adj_slots slots).
+// summaries (from the final-state gradient; the state after its last slot is
+// the gradient of the state before the first step).
 template <int DK, int DV>
 __global__ __launch_bounds__(kThreads) void bwd_state_scans_kernel(FwdParams p) {
-  constexpr int kBlocks = DK * DV / kScanElems;
-  if ((int)blockIdx.y < kBlocks) {
-    span_scan_body<DK, DV>(p.span_state, p.span_gate, p.initial_state, p.n_spans, blockIdx.x,
-                           blockIdx.y, p.st_bh, p.st_row, static_cast<f16*>(p.span_entry16));
-  } else {
-    // the last slot (the gradient of the state before the first step, copied
-    // out as d_initial_state) stays float32
-    span_scan_body<DK, DV>(p.adj_state, p.adj_gate, p.adj_initial, p.adj_slots, blockIdx.x,
-                           blockIdx.y - kBlocks, p.st_bh, p.st_row,
-                           static_cast<f16*>(p.adj_entry16), p.adj_slots - 1);
-  }
+  constexpr int kBlocks = DK * DV / kBScanElems;
+  const bool adj = (int)blockIdx.y >= kBlocks;
+  bwd_scan_body<DK, DV>(static_cast<f16*>(adj ? p.adj_entry16 : p.span_entry16),
+                        adj ? p.adj_gate : p.span_gate, adj ? p.adj_initial : p.initial_state,
+                        adj ? p.adj_slots : p.n_spans, blockIdx.x,
+                        adj ? blockIdx.y - kBlocks : blockIdx.y, p.st_bh, p.st_row,
+                        adj ? p.adj_final : nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -1218,6 +1284,24 @@ __device__ __forceinline__ void store_summary(float* span_state, float* span_gat
   }
 }
 
+// store_summary with the state rounded to float16 (the gate stays float32).
+template <int DK, int DV>
+__device__ __forceinline__ void store_summary16(f16* state16, float* span_gate, int bh,
+                                                size_t slots, size_t slot, int wave, int n16, int g,
+                                                const f32x4 (&st)[DK / 64][DV / 16],
+                                                const f32x4 (&gdec)[DK / 64]) {
+  f16* dst = state16 + ((size_t)bh * slots + slot) * DK * DV;
+#pragma unroll
+  for (int d = 0; d < DK / 64; ++d) {
+    const int dim = 16 * (wave + 4 * d) + n16;
+#pragma unroll
+    for (int cb = 0; cb < DV / 16; ++cb)
+      *reinterpret_cast<f16x4*>(dst + dim * DV + 16 * cb + 4 * g) = to_f16(st[d][cb]);
+    if (g == 0)
+      span_gate[((size_t)bh * slots + slot) * DK + dim] = exp2_fast(gdec[d][0] * 1.4426950408889634f);
+  }
+}
+
 // The span's summary (st, gdec as in fold_chunk, from zero) through the two
 // tile buffers; returns with every load landed, the buffers still being read
 // by other waves (a barrier must come before they are refilled).
@@ -1355,11 +1439,10 @@ __global__ __launch_bounds__(kThreads) void span_summary_f16_kernel(FwdParams p)
 // The backward pass's two summaries of a span: the forward one (k, v; the
 // state entering each span) and the adjoint one (q and the output gradient
 // d_out; the state gradient entering each span from its right), sharing the
-// log-alpha tile.  Span s's adjoint summary goes to slot adj_slots - 2 - s,
-// so that the adjoint scan runs from the end of the sequence to its start;
-// span 0 also writes the neutral summary (gate 1, state 0) into the last
-// slot, whose entry state is then the gradient of the state before the first
-// step.  float16, no fused gate activation.
+// log-alpha tile, stored as float16 (span_entry16, adj_entry16) with float32
+// gate products.  Span s's adjoint summary goes to slot adj_slots - 1 - s, so
+// that the adjoint scan runs from the end of the sequence to its start.
+// float16, no fused gate activation.
 //
 // A workgroup takes spans_per_wg consecutive spans (of the flattened
 // (batch*head, span) order) and streams their chunks through two tile
@@ -1459,22 +1542,10 @@ __global__ __launch_bounds__(kThreads) void bwd_state_summaries_kernel(FwdParams
       fold_chunk<DK, DV, false, true>(a, valid, 1.f, m_lower, m_ones, wave, sa, gadj);
     }
     if (i % sc == sc - 1) {
-      store_summary<DK, DV>(p.span_state, p.span_gate, it.bh, p.n_spans, it.span, wave, n16, g,
-                            st, gdec);
-      store_summary<DK, DV>(p.adj_state, p.adj_gate, it.bh, slots, slots - 2 - it.span, wave, n16,
-                            g, sa, gadj);
-      if (it.span == 0) {
-        float* last = p.adj_state + ((size_t)it.bh * slots + slots - 1) * DK * DV;
-#pragma unroll
-        for (int d = 0; d < NDB; ++d) {
-          const int dim = 16 * (wave + 4 * d) + n16;
-#pragma unroll
-          for (int cb = 0; cb < NCB; ++cb)
-            *reinterpret_cast<f32x4*>(last + dim * DV + 16 * cb + 4 * g) =
-                f32x4{0.f, 0.f, 0.f, 0.f};
-          if (g == 0) p.adj_gate[((size_t)it.bh * slots + slots - 1) * DK + dim] = 1.f;
-        }
-      }
+      store_summary16<DK, DV>(static_cast<f16*>(p.span_entry16), p.span_gate, it.bh, p.n_spans,
+                              it.span, wave, n16, g, st, gdec);
+      store_summary16<DK, DV>(static_cast<f16*>(p.adj_entry16), p.adj_gate, it.bh, slots,
+                              slots - 1 - it.span, wave, n16, g, sa, gadj);
       reset();
     }
   };
@@ -1675,7 +1746,7 @@ hipError_t launch_bwd_states_variant(const FwdParams& p, hipStream_t stream, hip
   if ((e = launch_marked(bwd_state_summaries_kernel<DK, DV>, sum_grid, stream, p,
                          ev ? ev[0] : nullptr, ev ? ev[1] : nullptr)) != hipSuccess)
     return e;
-  return launch_marked(bwd_state_scans_kernel<DK, DV>, dim3(BH, 2 * DK * DV / kScanElems), stream,
+  return launch_marked(bwd_state_scans_kernel<DK, DV>, dim3(BH, 2 * DK * DV / kBScanElems), stream,
                        p, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr);
 }
 
