@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
@@ -664,6 +665,9 @@ int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* log_a
     pb.n_chunks = n_chunks;
     pb.ldk = f.ldk;
     pb.ldv = f.ldv;
+    // the chunk kernel is persistent, two workgroups per CU (74 KB of LDS
+    // each)
+    pb.n_wg = (int)std::min<long long>(BH * n_chunks, 2LL * cu_count(dev));
 
     // with the measurement hook armed, every block's kernels record into the
     // same event pairs, so they end up bracketing the last block's kernels

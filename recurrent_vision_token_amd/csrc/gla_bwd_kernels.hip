@@ -21,23 +21,27 @@
 // identity dlog_alpha_t = alpha_t * rowsum(G_t * S_{t-1}) at the chunk's end).
 //
 // The state kernels work on spans of one chunk, so every chunk finds both of
-// its states (float16) in memory.  The chunk kernel (one workgroup per
-// (batch*head, chunk), wave w owning key dims and value dims 16w..16w+15):
-//   1. q, k, v, log-alpha and dO land in LDS (LDS-writing loads, swizzled
-//      rows); B is summed per key dim in float32;
+// its states (float16) in memory.  The chunk kernel is persistent: two
+// 8-wave workgroups per CU take the (batch*head, chunk) pairs in turn.  Per
+// chunk (wave w owning key dims and value dims 16 (w % 4) .. + 15 and the
+// 16-token sub-blocks {0, 3} or {1, 2}):
+//   1. q, k, v, log-alpha, dO and both states are in LDS (LDS-writing loads,
+//      swizzled rows, issued during the previous chunk); B is summed per key
+//      dim in float32;
 //   2. float16 operand tiles with every decay factor bounded: Qs = q e^{c}
 //      (c = B - B at the 16-token sub-block start, in [-10, 0]), Kd = k decayed
 //      to its sub-block's end, Ke = k decayed to the chunk's end; the diagonal
 //      sub-blocks use Kd times the sub-block decay back (<= e^10), and the
-//      factors between sub-blocks (<= 1) scale 16x16 accumulators in float32;
-//   3. the score tiles dO V^T, V dO^T and (Q e^B)(K e^-B)^T are formed per
-//      sub-block pair on the matrix cores (every wave forms the ones it needs;
-//      the accumulator of one is the next MFMA's operand, no LDS round trip),
-//      then dq, dk, dv as 16x16 MFMA tiles, outputs rounded to float16 and
-//      stored to their grid cells (scan-order remap as in the forward pass);
-//   4. E_{c+1} = diag(e^{B_end}) E_c + Ke^T V, its row sums against R_c give
-//      the carry, and dlog_alpha is a suffix sum across the 16 lanes of each
-//      tile row plus the later sub-blocks' totals.
+//      factors between sub-blocks scale the operands of the other pairs;
+//   3. E_{c+1} = diag(e^{B_end}) E_c + Ke^T V and its row sums against R_c
+//      (the carry);
+//   4. the 20 score tiles dO V^T and (Q e^B)(K e^-B)^T of the sub-block pairs
+//      are formed once on the matrix cores and kept in LDS, from which dv, dq
+//      and dk are 16x16 MFMA tiles, rounded to float16 and stored to their
+//      grid cells (scan-order remap as in the forward pass); as soon as a tile
+//      is done with, the next chunk's data is loaded into it;
+//   5. dlog_alpha is a suffix sum across the 16 lanes of each tile row plus
+//      the later sub-blocks' totals and the carry.
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -50,418 +54,559 @@
 namespace gla {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;  // 8 waves
 constexpr int kChunk = 64;
 
 __device__ __forceinline__ float ex(float x) { return exp2_fast(x * 1.4426950408889634f); }
 
-// DPP moves within the 16-lane rows of a wave: lane n of a row reads lane
-// n + k of the same row (zero past the row's end), or every lane reads lane k.
-constexpr int kRowShl = 0x100, kRowBcast = 0x150;
+// DPP move within the 16-lane rows of a wave: lane n of a row reads lane
+// n + k of the same row (zero past the row's end).
+constexpr int kRowShl = 0x100;
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
   return __builtin_bit_cast(
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
 
-template <int DK, int DV>
-__global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
+// 16 x 16 float16 score tiles in LDS: row-major, 32-byte rows, the four
+// 8-byte column groups of rows 8..15 stored in the order 2 3 0 1, so that the
+// 16 lanes writing (or reading) one column group of rows 0..15 hit distinct
+// banks.  Offset (elements) of row r, columns 4 c .. 4 c + 3:
+__device__ __forceinline__ int st_tile_off(int r, int c) { return r * 16 + 4 * (c ^ ((r >> 2) & 2)); }
+
+// Transposed read of such a tile (ds_read_b64_tr_b16): lane (n, g) receives
+// rows 4g .. 4g + 3 of column n, the MFMA operand that reduces over rows.
+// Lane j of each 16-lane group addresses row 4g + j / 4, columns 4 (j % 4) ...
+__device__ __forceinline__ f16x4 tr_tile(const f16* tile, int lane) {
+  const int j = lane & 15, g = lane >> 4;
+  const f16* a = tile + st_tile_off(4 * g + (j >> 2), j & 3);
+  const lds_h4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+      (__attribute__((address_space(3))) lds_h4_t*)(lds_void_t*)a);
+  return __builtin_bit_cast(f16x4, x);
+}
+
+// tr_read of a swizzled tile with 128-byte rows (see gla_device.h), for the
+// lane index given
+__device__ __forceinline__ f16x4 tr_read_l(const f16* tile, int row0, int col0, int lane) {
+  const int j = lane & 15, g = lane >> 4;
+  const int row = row0 + 4 * g + (j >> 2);
+  const int col = col0 + 4 * (j & 3);
+  const f16* a = tile + row * 64 + (((col >> 3) ^ (row & 7)) << 3) + (col & 4);
+  const lds_h4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+      (__attribute__((address_space(3))) lds_h4_t*)(lds_void_t*)a);
+  return __builtin_bit_cast(f16x4, x);
+}
+
+// Over the four 16-lane groups of a wave (group q = lane / 16): the
+// product of x over the groups before this lane's (*before) and after it
+// (*after).
+__device__ __forceinline__ void group_products(float x, int q, float* before, float* after) {
+  const float x1 = __shfl_xor(x, 16), x2 = __shfl_xor(x, 32), x3 = __shfl_xor(x1, 32);
+  // x1, x2, x3: groups q ^ 1, q ^ 2, q ^ 3
+  const float y23 = x2 * x3, y123 = x1 * y23;
+  *before = q == 0 ? 1.f : q == 1 ? x1 : q == 2 ? y23 : y123;
+  *after = q == 0 ? y123 : q == 1 ? y23 : q == 2 ? x1 : 1.f;
+}
+__device__ __forceinline__ float group_sum(float x) {
+  const float x1 = __shfl_xor(x, 16);
+  const float y = x + x1;
+  return y + __shfl_xor(y, 32);
+}
+
+// Four gradient values of one token to float16 at `off` of `dst`; with ACC
+// (a block after the first of a wider head) added to what the earlier blocks
+// stored there (the calls of one backward pass run in order).  A template
+// flag, so that the plain store carries no load of the old value.
+template <bool ACC>
+__device__ __forceinline__ void store_grad4(rsrc_t dst, uint32_t off, f32x4 x) {
+  if constexpr (ACC) {
+    const f16x4 old = __builtin_bit_cast(f16x4, __builtin_amdgcn_raw_buffer_load_b64(dst, off, 0, 0));
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x[u] += (float)old[u];
+  }
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, to_f16(x)), dst, off, 0, 0);
+}
+
+// VMEM operations one wave issues per chunk after its last prefetch: the
+// two dlog-alpha stores, and the loads of the stored values they add to.
+template <bool ACC_K>
+constexpr int kVmemAfterPrefetch = ACC_K ? 4 : 2;
+
+// Persistent: workgroup w takes the chunks w, w + gridDim.x, .. of the
+// flattened (batch*head, chunk) order, one at a time.  Each input tile is
+// refilled with the next chunk's data as soon as the current chunk is done
+// with it (log-alpha, k and d_out after dq; q, v and both states after dk),
+// so that the loads run under the rest of the chunk's work, and a chunk's
+// stores drain under the next one's.  ACC_V: dv adds to the stored values;
+// ACC_K: dq, dk and dlog-alpha do.
+template <int DK, int DV, bool ACC_V, bool ACC_K>
+__global__ __launch_bounds__(kThreads, 4) void chunk_bwd_f16_kernel(BwdParams p) {
   static_assert(DK == 64 && DV == 64, "built for 64 key and value dims");
   constexpr int RB = 128;  // bytes per tile row
   // row stride (floats) of sEc: 4 floats of padding move consecutive rows 4
   // banks apart, so 16 lanes reading 16 bytes each from 16 rows hit 64
   // different banks
   constexpr int ES = DK + 4;
+  // the chunk's q, k, v, log-alpha and d_out; after the decay pass q's tile
+  // holds Qs, k's Kd and log-alpha's Ke (each wave keeps the exact q and k of
+  // its dlog-alpha tiles in registers)
   __shared__ __attribute__((aligned(16))) f16 tq[kChunk * DK], tk[kChunk * DK], tv[kChunk * DV];
   __shared__ __attribute__((aligned(16))) f16 tla[kChunk * DK], tdo[kChunk * DV];
-  __shared__ __attribute__((aligned(16))) f16 tqs[kChunk * DK], tkd[kChunk * DK];
+  // grid cell of each token row of the current and the next chunk (bit 31:
+  // past the sequence)
+  __shared__ uint32_t srow[2][kChunk];
   __shared__ __attribute__((aligned(16))) float sEc[kChunk * ES];  // e^{c_t}, c = decay since the sub-block start
+  // score tiles of the sub-block pairs J <= I (pair index I (I + 1) / 2 + J),
+  // 16 x 16 row-major (st_tile layout): sM row s of J, column t of I holds
+  // v_s . dO_t; sP row s of I, column t of J holds
+  // sum_i q_si k_ti e^{B_si - B_ti}; diagonal tiles keep only s <= t (sM) or
+  // s >= t (sP)
+  __shared__ __attribute__((aligned(16))) f16 sM[10][256], sP[10][256];
   __shared__ __attribute__((aligned(16))) f16 sF[5][5][DK];  // e^{Bst_a - Bst_b} per key dim
+  // per sub-block and key dim: the log-decay total (decay pass), later the
+  // total of q dq - k dk (dlog-alpha)
   __shared__ float sTot[4][DK];
   __shared__ float sBst[5][DK];   // B before sub-block I (I = 0..3), [4] = chunk total
   __shared__ float sCarry[4][DK];
-  __shared__ uint32_t srow[kChunk];
-  f16* const tke = tla;           // k decayed to the chunk end, in place of log-alpha
+  f16* const tqs = tq;            // q e^{c}
+  f16* const tkd = tk;            // k decayed to its sub-block's end
+  f16* const tke = tla;           // k decayed to the chunk end
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n16 = lane & 15, g = lane >> 4;
-
-  const int bh = blockIdx.x / p.n_chunks;
-  const int c = blockIdx.x - bh * p.n_chunks;
-  const int b = bh / p.heads;
-  GridMap gm;
-  gm.H = p.H;
-  gm.W = p.W;
-  gm.dir = (p.scan_dir == 4) ? (b & 3) : p.scan_dir;
-  gm.mw = p.div_w_m;
-  gm.mh = p.div_h_m;
-  gm.sw = p.div_w_s;
-  gm.sh = p.div_h_s;
-
-  // rows of ldk (q, k, log-alpha and their gradients) or ldv (v, d_out, dv)
-  // elements: this block's 64 dims of a wider head, or the whole row
+  // wave w: key dims and value dims 16 kb .. 16 kb + 15 and two of the four
+  // 16-token sub-blocks, {0, 3} or {1, 2} (five sub-block pairs either way);
+  // lane (n, g) = (lane % 16, lane / 16) of its 16 x 16 tiles holds key dims
+  // ki = 16 kb + 4g .. of a dq / dk tile, value dims vj = 16 vb + 4g .. of a
+  // dv tile
+  const int kb = wave & 3, vb = kb;
+  const int hf = wave >> 2;
+  const int sub[2] = {hf, 3 - hf};
   const uint32_t gsk = p.ldk * 2u, gsv = p.ldv * 2u;  // row strides in bytes
   const uint32_t kbytes = (uint32_t)p.T * gsk, vbytes = (uint32_t)p.T * gsv;
-  const size_t sok = (size_t)bh * p.T * p.ldk, sov = (size_t)bh * p.T * p.ldv;
-  const rsrc_t rq = seq_rsrc(static_cast<const f16*>(p.q) + sok, kbytes);
-  const rsrc_t rk = seq_rsrc(static_cast<const f16*>(p.k) + sok, kbytes);
-  const rsrc_t rla = seq_rsrc(static_cast<const f16*>(p.la) + sok, kbytes);
-  const rsrc_t rv = seq_rsrc(static_cast<const f16*>(p.v) + sov, vbytes);
-  const rsrc_t rdo = seq_rsrc(static_cast<const f16*>(p.dout) + sov, vbytes);
-  const rsrc_t wdq = seq_rsrc(static_cast<f16*>(p.dq) + sok, kbytes);
-  const rsrc_t wdk = seq_rsrc(static_cast<f16*>(p.dk) + sok, kbytes);
-  const rsrc_t wdv = seq_rsrc(static_cast<f16*>(p.dv) + sov, vbytes);
-  const rsrc_t wdla = seq_rsrc(static_cast<f16*>(p.dla) + sok, kbytes);
-  // the states of this chunk, float16 from the scans: the forward state
-  // entering it and the adjoint entering it from the right
-  const f16* E_c = static_cast<const f16*>(p.fwd_state) + ((size_t)bh * p.n_chunks + c) * DK * DV;
-  const f16* R_c = static_cast<const f16*>(p.adj_state) +
+  const int total = p.B * p.heads * p.n_chunks;
+
+  // Loads of chunk `item`: this wave fills block `wave` (tokens 8 wave .. + 7;
+  // lane l: 16 bytes of row 8 wave + l / 8, swizzled pieces) of each tile.  A
+  // token row's grid cell serves both row widths; rows past the sequence get
+  // an offset past the buffer and read as zero.  plan() also records the
+  // rows' cells in srow[sel].
+  struct Plan {
+    uint32_t off, offv;
+    size_t sok, sov;
+  };
+  auto plan = [&](int item, int sel, int lane) {
+    const int bh = item / p.n_chunks, c = item - bh * p.n_chunks;
+    GridMap gm;
+    gm.H = p.H;
+    gm.W = p.W;
+    gm.dir = (p.scan_dir == 4) ? ((bh / p.heads) & 3) : p.scan_dir;
+    gm.mw = p.div_w_m;
+    gm.mh = p.div_h_m;
+    gm.sw = p.div_w_s;
+    gm.sh = p.div_h_s;
+    const int t0 = c * kChunk, valid = min(kChunk, p.T - t0);
+    const int r = 8 * wave + (lane >> 3);
+    const uint32_t sw = (uint32_t)(((lane & 7) ^ (r & 7)) * 16);
+    const uint32_t flag = (uint32_t)(r >= valid) << 31;
+    const uint32_t cell = (uint32_t)gm.cell(t0 + r);
+    if ((lane & 7) == 0) srow[sel][r] = cell | flag;
+    Plan pl;
+    pl.off = (cell * gsk + sw) | flag;
+    pl.offv = (cell * gsv + sw) | flag;
+    pl.sok = (size_t)bh * p.T * p.ldk;
+    pl.sov = (size_t)bh * p.T * p.ldv;
+    return pl;
+  };
+  auto load_k_side = [&](const Plan& pl, const void* src, f16* tile) {
+    dma16_asm<false>(seq_rsrc(static_cast<const f16*>(src) + pl.sok, kbytes), tile + wave * 512, pl.off);
+  };
+  auto load_v_side = [&](const Plan& pl, const void* src, f16* tile) {
+    dma16_asm<false>(seq_rsrc(static_cast<const f16*>(src) + pl.sov, vbytes), tile + wave * 512, pl.offv);
+  };
+  // The states of chunk `item`, float16 from the scans: the forward state
+  // entering it and the adjoint entering it from the right, each a 64 x 64
+  // tile swizzled like the input tiles, loaded into the area of sEc (free
+  // from the end of one chunk's dk to the next chunk's decay pass).
+  f16* const sE = reinterpret_cast<f16*>(sEc);
+  f16* const sR = sE + DK * DV;
+  static_assert(2 * DK * DV * 2 <= kChunk * ES * 4, "both states fit in sEc");
+  auto load_states = [&](int item, int lane) {
+    const int bh = item / p.n_chunks, c = item - bh * p.n_chunks;
+    const f16* E = static_cast<const f16*>(p.fwd_state) + ((size_t)bh * p.n_chunks + c) * DK * DV;
+    const f16* R = static_cast<const f16*>(p.adj_state) +
                    ((size_t)bh * p.n_chunks + (p.n_chunks - 1 - c)) * DK * DV;
-  const int kb = wave;          // key dims 16 kb .. owned by this wave (dq, dk, dla)
-  const int vb = wave;          // value dims 16 vb .. (dv, next state rows)
-  const int ki = 16 * kb + 4 * g;  // first of the lane's 4 key dims in a dq / dk tile
-  const int vj = 16 * vb + 4 * g;
-
-  // ---- 0. the states, read from memory before the tiles so that their
-  // latency hides behind the tiles': E and R in the accumulator layout of the
-  // next-state update (rows 16 kc + n, columns 16 w + 4g ..) and in the MFMA
-  // operand layouts below (raw float16 bits until the tiles landed; 32-bit
-  // byte offsets from the state bases, so each load is one uniform base plus
-  // one lane offset)
-  u32x2 e4h[4], r4h[4], eah[4], rah[4];
-  unsigned short rtah[16];
-  auto ld4 = [](const f16* base, uint32_t byte_off) {
-    return *reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(base) + byte_off);
+    const int r = 8 * wave + (lane >> 3);
+    const uint32_t off = (uint32_t)r * RB + (uint32_t)(((lane & 7) ^ (r & 7)) * 16);
+    dma16_asm<false>(seq_rsrc(E, DK * DV * 2), sE + wave * 512, off);
+    dma16_asm<false>(seq_rsrc(R, DK * DV * 2), sR + wave * 512, off);
   };
-  auto ld1 = [](const f16* base, uint32_t byte_off) {
-    return *reinterpret_cast<const unsigned short*>(reinterpret_cast<const char*>(base) + byte_off);
-  };
-  const uint32_t o_acc = 2u * (uint32_t)(n16 * DV + vj);            // row n, columns vj ..
-  const uint32_t o_op = 2u * (uint32_t)((16 * kb + n16) * DV + 8 * g);  // row 16 kb + n, cols 8g ..
-  const uint32_t o_t = 2u * (uint32_t)(8 * g * DV + 16 * vb + n16);   // R[8g][16 vb + n]
-#pragma unroll
-  for (int kc = 0; kc < 4; ++kc) {
-    e4h[kc] = ld4(E_c, o_acc + 2u * 16 * kc * DV);
-    r4h[kc] = ld4(R_c, o_acc + 2u * 16 * kc * DV);
-  }
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    eah[2 * h] = ld4(E_c, o_op + 2u * 32 * h);
-    eah[2 * h + 1] = ld4(E_c, o_op + 2u * (32 * h + 4));
-    rah[2 * h] = ld4(R_c, o_op + 2u * 32 * h);
-    rah[2 * h + 1] = ld4(R_c, o_op + 2u * (32 * h + 4));
-    // R^T rows 16 vb + n: R[32 h + 8g + e][16 vb + n]
-#pragma unroll
-    for (int e = 0; e < 8; ++e) rtah[8 * h + e] = ld1(R_c, o_t + 2u * (32 * h + e) * DV);
-  }
 
-  // ---- 1. tiles, cumulative decay
-  const int t0 = c * kChunk;
-  const int valid = min(kChunk, p.T - t0);
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int blk = wave * 2 + i;
-    uint32_t cf;
-    bool first;
-    const uint32_t off = dma_offset_cell_s<RB>(blk, t0, valid, gm, gsk, &cf, &first);
-    const uint32_t offv = dma_offset_s<RB>(blk, t0, valid, gm, gsv);
-    if (first) srow[(blk * 1024 + 16 * lane) / RB] = cf;
-    dma16(rq, tq + blk * 512, off);
-    dma16(rk, tk + blk * 512, off);
-    dma16(rv, tv + blk * 512, offv);
-    dma16(rla, tla + blk * 512, off);
-    dma16(rdo, tdo + blk * 512, offv);
-  }
-  wait_barrier<vmcnt_lgkm0_imm(0)>();  // tiles landed, row table written
-  // the raw state values are used from here on only: the empty asm keeps their
-  // conversions (and so the compiler's waits for them) after the wait above
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    asm volatile("" : "+v"(eah[j]), "+v"(rah[j]));
-    asm volatile("" : "+v"(e4h[j]), "+v"(r4h[j]));
-  }
-#pragma unroll
-  for (int j = 0; j < 16; ++j) asm volatile("" : "+v"(rtah[j]));
-  auto wide = [](u32x2 x) {
-    const f16x4 h = __builtin_bit_cast(f16x4, x);
-    return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
-  };
-  f32x4 e4s[4], r4s[4];
-#pragma unroll
-  for (int kc = 0; kc < 4; ++kc) {
-    e4s[kc] = wide(e4h[kc]);
-    r4s[kc] = wide(r4h[kc]);
-  }
-  // this chunk's states as float16 MFMA A operands: E and R rows of the
-  // wave's key dims (lane (n, g): row 16 kb + n, columns 32 h + 8g .. + 7) and
-  // R^T rows of its value dims
-  f16x8 ea[2], ra[2], rta[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    ea[h] = cat8(__builtin_bit_cast(f16x4, eah[2 * h]), __builtin_bit_cast(f16x4, eah[2 * h + 1]));
-    ra[h] = cat8(__builtin_bit_cast(f16x4, rah[2 * h]), __builtin_bit_cast(f16x4, rah[2 * h + 1]));
-    f16x8 x;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = __builtin_bit_cast(f16, rtah[8 * h + e]);
-    rta[h] = x;
-  }
-
-  // Thread (key dims 2 i2, 2 i2 + 1; tokens 8h .. 8h + 7 of sub-block J, its
-  // wave) walks its tokens: alpha_t = e^{la_t}, e^{c_t} as a running product
-  // from the sub-block start and the decay to the sub-block end as a running
-  // product from its end, one exponential per token; the two halves of a
-  // sub-block (lanes l and l ^ 32) hand each other their decay products.
+  int item = blockIdx.x;
+  if (item >= total) return;
   {
-    const int i2 = tid & 31, h = (tid >> 5) & 1, J = tid >> 6;
-    const int i = 2 * i2;
-    float al0[8], al1[8];
-    float tot0 = 0.f, tot1 = 0.f, p0 = 1.f, p1 = 1.f;
+    const Plan pl = plan(item, 0, lane);
+    load_k_side(pl, p.q, tq);
+    load_k_side(pl, p.k, tk);
+    load_v_side(pl, p.v, tv);
+    load_k_side(pl, p.la, tla);
+    load_v_side(pl, p.dout, tdo);
+    load_states(item, lane);
+    wait_barrier<vmcnt_lgkm0_imm(0)>();
+  }
+  for (int sel = 0; item < total; item += gridDim.x, sel ^= 1) {
+    const int next = item + (int)gridDim.x;
+    const bool more = next < total;
+    // this chunk's inputs landed (what this wave issued after the last of
+    // them are the previous chunk's dlog-alpha stores)
+    wait_barrier<vmcnt_lgkm0_imm(kVmemAfterPrefetch<ACC_K>)>();
+    // the lane's indices, re-derived each chunk from a value the compiler
+    // cannot see through: the many LDS addresses built from them are then
+    // formed where they are used instead of held across the loop
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int n16 = ln & 15, g = ln >> 4;
+    const int ki = 16 * kb + 4 * g, vj = 16 * vb + 4 * g;
+    // the states in this wave's layouts, read before the decay pass reuses
+    // their area: E and R rows 16 kc + n, columns vj .. (the accumulator
+    // layout of the next-state update, kc = 2 hf, 2 hf + 1); E and R rows of
+    // the wave's key dims as MFMA A operands (lane (n, g): row 16 kb + n,
+    // columns 32 h + 8g .. + 7); R^T rows of its value dims (lane (n, g):
+    // R[32 h + 4g + u][16 vb + n] and R[32 h + 16 + 4g + u][16 vb + n], the
+    // order in which the matching Ke operand takes the key dims)
+    f16x4 e4h[2], r4h[2];
+    f16x8 ea[2], ra[2], rta[2];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const f16x2 la2 = *reinterpret_cast<const f16x2*>(&tla[swz<RB>(16 * J + 8 * h + u, i)]);
-      const float l0 = (float)la2[0], l1 = (float)la2[1];
-      al0[u] = ex(l0);
-      al1[u] = ex(l1);
-      tot0 += l0;
-      tot1 += l1;
-      p0 *= al0[u];
-      p1 *= al1[u];
+    for (int x = 0; x < 2; ++x) {
+      e4h[x] = ld64(sE + swz<RB>(16 * (2 * hf + x) + n16, vj));
+      r4h[x] = ld64(sR + swz<RB>(16 * (2 * hf + x) + n16, vj));
     }
-    const float o0 = __shfl_xor(p0, 32), o1 = __shfl_xor(p1, 32);
-    const float ot0 = __shfl_xor(tot0, 32), ot1 = __shfl_xor(tot1, 32);
-    float ec0 = h ? o0 : 1.f, ec1 = h ? o1 : 1.f;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int t = 16 * J + 8 * h + u;
-      const int e = swz<RB>(t, i);
-      ec0 *= al0[u];
-      ec1 *= al1[u];
-      *reinterpret_cast<f32x2*>(&sEc[t * ES + i]) = f32x2{ec0, ec1};
-      const f16x2 q2 = *reinterpret_cast<const f16x2*>(&tq[e]);
-      *reinterpret_cast<f16x2*>(&tqs[e]) = f16x2{(f16)((float)q2[0] * ec0), (f16)((float)q2[1] * ec1)};
+    for (int h = 0; h < 2; ++h) {
+      ea[h] = ld128(sE + swz<RB>(16 * kb + n16, 32 * h + 8 * g));
+      ra[h] = ld128(sR + swz<RB>(16 * kb + n16, 32 * h + 8 * g));
+      rta[h] = cat8(tr_read_l(sR, 32 * h, 16 * vb, ln), tr_read_l(sR, 32 * h + 16, 16 * vb, ln));
     }
-    float sfx0 = h ? 1.f : o0, sfx1 = h ? 1.f : o1, kf0[8], kf1[8];
+
+    const int bh = item / p.n_chunks;
+    const size_t sok = (size_t)bh * p.T * p.ldk, sov = (size_t)bh * p.T * p.ldv;
+    const rsrc_t wdq = seq_rsrc(static_cast<f16*>(p.dq) + sok, kbytes);
+    const rsrc_t wdk = seq_rsrc(static_cast<f16*>(p.dk) + sok, kbytes);
+    const rsrc_t wdv = seq_rsrc(static_cast<f16*>(p.dv) + sov, vbytes);
+    const rsrc_t wdla = seq_rsrc(static_cast<f16*>(p.dla) + sok, kbytes);
+    // byte offset of token t's columns col .. in a gradient row of gs bytes
+    auto grad_off = [&](uint32_t gs, int t, int col) {
+      const uint32_t cf = srow[sel][t];
+      return ((cf & 0x7fffffffu) * gs + (uint32_t)col * 2) | (cf & 0x80000000u);
+    };
+
+    // the exact q and k of this wave's dlog-alpha tiles (token 16 I + n of
+    // its two sub-blocks, key dims ki ..), read before the decay pass
+    // overwrites their tiles
+    f16x4 q4r[2], k4r[2];
 #pragma unroll
-    for (int u = 7; u >= 0; --u) {
-      const int e = swz<RB>(16 * J + 8 * h + u, i);
-      const f16x2 k2 = *reinterpret_cast<const f16x2*>(&tk[e]);
-      kf0[u] = (float)k2[0] * sfx0;   // k decayed to the sub-block end
-      kf1[u] = (float)k2[1] * sfx1;
-      *reinterpret_cast<f16x2*>(&tkd[e]) = f16x2{(f16)kf0[u], (f16)kf1[u]};
-      sfx0 *= al0[u];
-      sfx1 *= al1[u];
+    for (int x = 0; x < 2; ++x) {
+      q4r[x] = ld64(tq + swz<RB>(16 * sub[x] + n16, ki));
+      k4r[x] = ld64(tk + swz<RB>(16 * sub[x] + n16, ki));
     }
-    if (h == 0) *reinterpret_cast<f32x2*>(&sTot[J][i]) = f32x2{tot0 + ot0, tot1 + ot1};
-    __syncthreads();
-    if (tid < DK) {
-      float acc = 0.f;
-      sBst[0][tid] = 0.f;
+
+    // ---- decay pass.  Wave w takes sub-block J = w % 4 and key dims
+    // 32 (w / 4) ..; lane (i2, q) = (lane % 16, lane / 16) walks key dims
+    // i, i + 1 (i = 32 (w / 4) + 2 i2) over the sub-block's tokens 4q .. 4q + 3:
+    // alpha_t = e^{la_t}, e^{c_t} as a running product from the sub-block
+    // start, the decay to the sub-block end as a running product from its end
+    // (one exponential per token); the four lane groups hand each other their
+    // decay products.  Qs, Kd and e^c stay in registers until every wave has
+    // its q, k and states.
+    {
+      const int J = wave & 3;
+      const int q = g;
+      const int i = 32 * (wave >> 2) + 2 * n16;
+      const int tb = 16 * J + 4 * q;
+      float al0[4], al1[4];
+      float tot0 = 0.f, tot1 = 0.f, p0 = 1.f, p1 = 1.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc += sTot[j][tid];
-        sBst[j + 1][tid] = acc;
+      for (int u = 0; u < 4; ++u) {
+        const f16x2 la2 = *reinterpret_cast<const f16x2*>(&tla[swz<RB>(tb + u, i)]);
+        const float l0 = (float)la2[0], l1 = (float)la2[1];
+        al0[u] = ex(l0);
+        al1[u] = ex(l1);
+        tot0 += l0;
+        tot1 += l1;
+        p0 *= al0[u];
+        p1 *= al1[u];
+      }
+      float pre0, pre1, suf0, suf1;
+      group_products(p0, q, &pre0, &suf0);
+      group_products(p1, q, &pre1, &suf1);
+      tot0 = group_sum(tot0);
+      tot1 = group_sum(tot1);
+      float ec0 = pre0, ec1 = pre1;
+      f16x2 qs2[4], kd2[4];
+      f32x2 ecs[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int t = tb + u;
+        ec0 *= al0[u];
+        ec1 *= al1[u];
+        ecs[u] = f32x2{ec0, ec1};
+        const f16x2 q2 = *reinterpret_cast<const f16x2*>(&tq[swz<RB>(t, i)]);
+        qs2[u] = f16x2{(f16)((float)q2[0] * ec0), (f16)((float)q2[1] * ec1)};
+      }
+      float sfx0 = suf0, sfx1 = suf1, kf0[4], kf1[4];
+#pragma unroll
+      for (int u = 3; u >= 0; --u) {
+        const f16x2 k2 = *reinterpret_cast<const f16x2*>(&tk[swz<RB>(tb + u, i)]);
+        kf0[u] = (float)k2[0] * sfx0;   // k decayed to the sub-block end
+        kf1[u] = (float)k2[1] * sfx1;
+        kd2[u] = f16x2{(f16)kf0[u], (f16)kf1[u]};
+        sfx0 *= al0[u];
+        sfx1 *= al1[u];
+      }
+      if (q == 0) *reinterpret_cast<f32x2*>(&sTot[J][i]) = f32x2{tot0, tot1};
+      // every wave holds its q, k and states; the sub-block totals are in
+      wait_barrier<kLgkmZero>();
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = swz<RB>(tb + u, i);
+        *reinterpret_cast<f16x2*>(&tqs[e]) = qs2[u];
+        *reinterpret_cast<f16x2*>(&tkd[e]) = kd2[u];
+        *reinterpret_cast<f32x2*>(&sEc[(tb + u) * ES + i]) = ecs[u];
+      }
+      if (wave == 0) {
+        float acc = 0.f;
+        sBst[0][ln] = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc += sTot[j][ln];
+          sBst[j + 1][ln] = acc;
+        }
+      }
+      wait_barrier<kLgkmZero>();
+      // k decayed to the chunk end = k decayed to its sub-block end times the
+      // decay of the later sub-blocks (log-alpha's tile is free now)
+      const float te0 = ex(sBst[4][i] - sBst[J + 1][i]), te1 = ex(sBst[4][i + 1] - sBst[J + 1][i + 1]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = swz<RB>(tb + u, i);
+        *reinterpret_cast<f16x2*>(&tke[e]) = f16x2{(f16)(kf0[u] * te0), (f16)(kf1[u] * te1)};
+      }
+      // factors between sub-block boundaries, thread (key dim, eighth)
+      for (int ab = wave; ab < 25; ab += kThreads / 64) {
+        const int a = ab / 5, bb = ab % 5;
+        sF[a][bb][ln] = (f16)ex(sBst[a][ln] - sBst[bb][ln]);
       }
     }
-    __syncthreads();
-    // k decayed to the chunk end = k decayed to its sub-block end times the
-    // decay of the later sub-blocks (log-alpha's tile is free now)
-    const float te0 = ex(sBst[4][i] - sBst[J + 1][i]), te1 = ex(sBst[4][i + 1] - sBst[J + 1][i + 1]);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int e = swz<RB>(16 * J + 8 * h + u, i);
-      *reinterpret_cast<f16x2*>(&tke[e]) = f16x2{(f16)(kf0[u] * te0), (f16)(kf1[u] * te1)};
-    }
-    // factors between sub-block boundaries, thread (key dim, quarter)
-    const int d = tid & 63;
-    for (int ab = tid >> 6; ab < 25; ab += 4) {
-      const int a = ab / 5, bb = ab % 5;
-      sF[a][bb][d] = (f16)ex(sBst[a][d] - sBst[bb][d]);
-    }
-  }
-  __syncthreads();
+    wait_barrier<kLgkmZero>();
 
-  // a block after the first adds its part of a gradient to what the
-  // earlier blocks stored (the calls of one backward pass run in order)
-  auto store4 = [&](rsrc_t dst, uint32_t gs, bool acc, int t, int col, f32x4 x) {
-    const uint32_t cf = srow[t];
-    const uint32_t off = ((cf & 0x7fffffffu) * gs + (uint32_t)col * 2) | (cf & 0x80000000u);
-    if (acc) {
-      const f16x4 old =
-          __builtin_bit_cast(f16x4, __builtin_amdgcn_raw_buffer_load_b64(dst, off, 0, 0));
+    // ---- next state rows 16 kc + n (kc = 2 hf, 2 hf + 1), columns vj ..:
+    // E_{c+1} = diag(e^{B_end}) E_c + Ke^T V; its row sums against R_c over
+    // the wave's 16 value columns are its part of the carry (read after the
+    // barrier before dlog-alpha)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) x[u] += (float)old[u];
-    }
-    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, to_f16(x)), dst, off, 0, 0);
-  };
-  const bool acc_k = p.acc_dqk != 0, acc_v = p.acc_dv != 0;
-
-  // ---- 3a. dq (rows: key dims of this wave, columns: tokens of sub-block I)
-  f32x4 dqv[4];
+    for (int x = 0; x < 2; ++x) {
+      const int kc = 2 * hf + x;
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int I = 0; I < 4; ++I) {
-    const f16x8 dob0 = ld128(tdo + swz<RB>(16 * I + n16, 8 * g));
-    const f16x8 dob1 = ld128(tdo + swz<RB>(16 * I + n16, 32 + 8 * g));
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int J = 0; J <= I; ++J) {
-      // (V dO^T)[s in J][t in I]: lane (n, g) holds s = 16J + 4g + u, t = 16I + n
-      f32x4 sc = mma32(ld128(tv + swz<RB>(16 * J + n16, 8 * g)), dob0, f32x4{0.f, 0.f, 0.f, 0.f});
-      sc = mma32(ld128(tv + swz<RB>(16 * J + n16, 32 + 8 * g)), dob1, sc);
-      if (J == I) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) sc[u] = (4 * g + u <= n16) ? sc[u] : 0.f;
+      for (int P = 0; P < 2; ++P) {
+        const f16x8 av = cat8(tr_read_l(tv, 32 * P, 16 * vb, ln), tr_read_l(tv, 32 * P + 16, 16 * vb, ln));
+        const f16x8 bk = cat8(tr_read_l(tke, 32 * P, 16 * kc, ln), tr_read_l(tke, 32 * P + 16, 16 * kc, ln));
+        acc = mma32(av, bk, acc);
       }
-      // Kd^T: key dim 16 kb + n, tokens 16J + 4g..; the row's factor is the
-      // decay back to the sub-block start, k e^{-c} = Kd e^{Bst_J - Bst_{J+1}}
-      // (>= 1) for J = I, or between the boundaries, e^{Bst_I - Bst_{J+1}}
-      // (<= 1) for J < I
-      const f16 fk = sF[J == I ? J : I][J + 1][16 * kb + n16];
-      acc = mma16(tr_read<RB>(tkd, 16 * J, 16 * kb) * fk, to_f16(sc), acc);
+      // lane (n, g): E_next[i = 16 kc + n][j = 16 vb + 4g + u]
+      const int i = 16 * kc + n16;
+      const float ebe = ex(sBst[4][i]);
+      const f16x4 e4 = e4h[x], r4 = r4h[x];
+      float part = 0.f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) part += (ebe * (float)e4[u] + acc[u]) * (float)r4[u];
+      part += __shfl_xor(part, 16);
+      part += __shfl_xor(part, 32);
+      if (g == 0) sCarry[vb][i] = part;
     }
-    // inter-chunk: (E dO^T)[key dim][token]
-    f32x4 ed = mma32(ea[0], dob0, f32x4{0.f, 0.f, 0.f, 0.f});
-    ed = mma32(ea[1], dob1, ed);
-    const int t = 16 * I + n16;
-    const f32x4 ec = *reinterpret_cast<const f32x4*>(&sEc[t * ES + ki]);
-    const f16x4 fb = ld64(&sF[I][0][ki]);
-    f32x4 dq;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) dq[u] = ec[u] * (acc[u] + (float)fb[u] * ed[u]);
-    dqv[I] = dq;
-    store4(wdq, gsk, acc_k, t, ki, dq);
-  }
 
-  // ---- 3b. dk (rows: key dims of this wave, columns: tokens of sub-block J)
-  f32x4 dkv[4];
+    // ---- the score tiles (the ten sM tiles, then the ten sP tiles; wave w
+    // forms tiles w, w + 8, w + 16), each once for all waves.  Lane (n, g) of
+    // a 16 x 16 accumulator holds row n, columns 4g .. 4g + 3 when the first
+    // operand supplies the columns and the second the rows.
+    const int soff = st_tile_off(n16, g);
 #pragma unroll
-  for (int J = 0; J < 4; ++J) {
-    const f16x8 vb0 = ld128(tv + swz<RB>(16 * J + n16, 8 * g));
-    const f16x8 vb1 = ld128(tv + swz<RB>(16 * J + n16, 32 + 8 * g));
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < 3; ++m) {
+      const int tau = wave + 8 * m;
+      if (tau < 20) {
+        const int pr = tau < 10 ? tau : tau - 10;
+        const int I = pr >= 6 ? 3 : pr >= 3 ? 2 : pr >= 1 ? 1 : 0;
+        const int J = pr - I * (I + 1) / 2;
+        if (tau < 10) {
+          // rows s of J (values), columns t of I (output gradients)
+          f32x4 sc = mma32(ld128(tdo + swz<RB>(16 * I + n16, 8 * g)),
+                           ld128(tv + swz<RB>(16 * J + n16, 8 * g)), f32x4{0.f, 0.f, 0.f, 0.f});
+          sc = mma32(ld128(tdo + swz<RB>(16 * I + n16, 32 + 8 * g)),
+                     ld128(tv + swz<RB>(16 * J + n16, 32 + 8 * g)), sc);
+          if (I == J) {
 #pragma unroll
-    for (int I = J; I < 4; ++I) {
-      // (dO V^T)[s in I][t in J]: lane (n, g) holds s = 16I + 4g + u, t = 16J + n
-      f32x4 sc = mma32(ld128(tdo + swz<RB>(16 * I + n16, 8 * g)), vb0, f32x4{0.f, 0.f, 0.f, 0.f});
-      sc = mma32(ld128(tdo + swz<RB>(16 * I + n16, 32 + 8 * g)), vb1, sc);
-      if (I == J) {
+            for (int u = 0; u < 4; ++u) sc[u] = (n16 <= 4 * g + u) ? sc[u] : 0.f;
+          }
+          st64(sM[pr] + soff, to_f16(sc));
+        } else {
+          // rows s of I (Qs), columns t of J (Kd); the decay between the
+          // rows' sub-block start and the columns' sub-block end sits on the
+          // key dims: e^{Bst_I - Bst_{J+1}} (<= 1) on Qs for I > J, or
+          // e^{Bst_J - Bst_{J+1}} (>= 1, back to the sub-block start) on Kd
+          // for I = J (Qs stays <= |q|)
+          f16x8 qa0 = ld128(tqs + swz<RB>(16 * I + n16, 8 * g));
+          f16x8 qa1 = ld128(tqs + swz<RB>(16 * I + n16, 32 + 8 * g));
+          f16x8 kx0 = ld128(tkd + swz<RB>(16 * J + n16, 8 * g));
+          f16x8 kx1 = ld128(tkd + swz<RB>(16 * J + n16, 32 + 8 * g));
+          const f16x8 f0 = ld128(&sF[I][J + 1][8 * g]);
+          const f16x8 f1 = ld128(&sF[I][J + 1][32 + 8 * g]);
+          if (I == J) {
+            kx0 = kx0 * f0;
+            kx1 = kx1 * f1;
+          } else {
+            qa0 = qa0 * f0;
+            qa1 = qa1 * f1;
+          }
+          f32x4 sc = mma32(kx0, qa0, f32x4{0.f, 0.f, 0.f, 0.f});
+          sc = mma32(kx1, qa1, sc);
+          if (I == J) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) sc[u] = (4 * g + u >= n16) ? sc[u] : 0.f;
+            for (int u = 0; u < 4; ++u) sc[u] = (n16 >= 4 * g + u) ? sc[u] : 0.f;
+          }
+          st64(sP[pr] + soff, to_f16(sc));
+        }
       }
-      // Qs^T: key dim 16 kb + n, tokens 16I + 4g..; for I > J its row takes
-      // the decay between the boundaries, e^{Bst_I - Bst_J} (<= 1)
-      f16x4 aop = tr_read<RB>(tqs, 16 * I, 16 * kb);
-      if (I > J) aop = aop * sF[I][J][16 * kb + n16];
-      acc = mma16(aop, to_f16(sc), acc);
     }
-    // inter-chunk: (R V^T)[key dim][token]
-    f32x4 rv = mma32(ra[0], vb0, f32x4{0.f, 0.f, 0.f, 0.f});
-    rv = mma32(ra[1], vb1, rv);
-    const int t = 16 * J + n16;
-    const f32x4 ec = *reinterpret_cast<const f32x4*>(&sEc[t * ES + ki]);
-    const f16x4 fe = ld64(&sF[4][J][ki]);
-    f32x4 dk;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      dk[u] = __builtin_amdgcn_rcpf(ec[u]) * (acc[u] + (float)fe[u] * rv[u]);
-    dkv[J] = dk;
-    store4(wdk, gsk, acc_k, t, ki, dk);
-  }
+    wait_barrier<kLgkmZero>();
 
-  // ---- 3c. dv (rows: value dims of this wave, columns: tokens of sub-block J)
+    // ---- dv (rows: value dims of this wave, columns: tokens of sub-block J)
 #pragma unroll
-  for (int J = 0; J < 4; ++J) {
-    f16x8 kx0 = ld128(tkd + swz<RB>(16 * J + n16, 8 * g));
-    f16x8 kx1 = ld128(tkd + swz<RB>(16 * J + n16, 32 + 8 * g));
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int x = 0; x < 2; ++x) {
+      const int J = sub[x];
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int I = J; I < 4; ++I)
+        acc = mma16(tr_read_l(tdo, 16 * I, 16 * vb, ln), tr_tile(sP[I * (I + 1) / 2 + J], ln), acc);
+      // inter-chunk: (R^T Ke^T)[value dim][token], key dims in rta's order
+      const int row = 16 * J + n16;
+      f32x4 rk = mma32(rta[0], cat8(ld64(tke + swz<RB>(row, 4 * g)), ld64(tke + swz<RB>(row, 16 + 4 * g))),
+                       f32x4{0.f, 0.f, 0.f, 0.f});
+      rk = mma32(rta[1], cat8(ld64(tke + swz<RB>(row, 32 + 4 * g)), ld64(tke + swz<RB>(row, 48 + 4 * g))),
+                 rk);
+      store_grad4<ACC_V>(wdv, grad_off(gsv, row, vj), acc + rk);
+    }
+
+    // ---- dq (rows: key dims of this wave, columns: tokens of sub-block I)
+    f32x4 dqv[2];
 #pragma unroll
-    for (int I = J; I < 4; ++I) {
-      // ((Q e^B)(K e^-B)^T)[s in I][t in J], bounded operands: Qs rows of I,
-      // and Kd rows of J scaled by e^{B(I) - B(J+1)} (<= 1) for I > J, or by
-      // e^{B(J) - B(J+1)} (>= 1, back to the sub-block start) for I = J;
-      // the factor sits on the contraction index and is applied to Qs here
-      f16x8 qa0 = ld128(tqs + swz<RB>(16 * I + n16, 8 * g));
-      f16x8 qa1 = ld128(tqs + swz<RB>(16 * I + n16, 32 + 8 * g));
-      const int top = (I == J) ? J : I;
-      const f16x8 f0 = ld128(&sF[top][J + 1][8 * g]);
-      const f16x8 f1 = ld128(&sF[top][J + 1][32 + 8 * g]);
-      if (I == J) {
-        // the >= 1 factor goes on the keys (Qs stays <= |q|)
-        kx0 = kx0 * f0;
-        kx1 = kx1 * f1;
-      } else {
-        qa0 = qa0 * f0;
-        qa1 = qa1 * f1;
+    for (int x = 0; x < 2; ++x) {
+      const int I = sub[x];
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int J = 0; J <= I; ++J) {
+        // Kd^T: key dim 16 kb + n, tokens 16J + 4g..; the row's factor is the
+        // decay back to the sub-block start, k e^{-c} = Kd e^{Bst_J - Bst_{J+1}}
+        // (>= 1) for J = I, or between the boundaries, e^{Bst_I - Bst_{J+1}}
+        // (<= 1) for J < I; times (V dO^T)[s in J][t in I]
+        const f16 fk = sF[I][J + 1][16 * kb + n16];
+        acc = mma16(tr_read_l(tkd, 16 * J, 16 * kb, ln) * fk, tr_tile(sM[I * (I + 1) / 2 + J], ln), acc);
       }
-      f32x4 sc = mma32(qa0, kx0, f32x4{0.f, 0.f, 0.f, 0.f});
-      sc = mma32(qa1, kx1, sc);
-      if (I == J) {
-        kx0 = ld128(tkd + swz<RB>(16 * J + n16, 8 * g));
-        kx1 = ld128(tkd + swz<RB>(16 * J + n16, 32 + 8 * g));
-#pragma unroll
-        for (int u = 0; u < 4; ++u) sc[u] = (4 * g + u >= n16) ? sc[u] : 0.f;
-      }
-      acc = mma16(tr_read<RB>(tdo, 16 * I, 16 * vb), to_f16(sc), acc);
-    }
-    // inter-chunk: (R^T Ke^T)[value dim][token]
-    f32x4 rk = mma32(rta[0], ld128(tke + swz<RB>(16 * J + n16, 8 * g)), f32x4{0.f, 0.f, 0.f, 0.f});
-    rk = mma32(rta[1], ld128(tke + swz<RB>(16 * J + n16, 32 + 8 * g)), rk);
-    store4(wdv, gsv, acc_v, 16 * J + n16, vj, acc + rk);
-  }
-
-  // ---- 4. next state, carry, dlog_alpha
-#pragma unroll
-  for (int kc = 0; kc < 4; ++kc) {
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int P = 0; P < 2; ++P) {
-      const f16x8 av = cat8(tr_read<RB>(tv, 32 * P, 16 * vb), tr_read<RB>(tv, 32 * P + 16, 16 * vb));
-      const f16x8 bk = cat8(tr_read<RB>(tke, 32 * P, 16 * kc), tr_read<RB>(tke, 32 * P + 16, 16 * kc));
-      acc = mma32(av, bk, acc);
-    }
-    // lane (n, g): E_next[i = 16 kc + n][j = 16 vb + 4g + u]
-    const int i = 16 * kc + n16;
-    const float ebe = ex(sBst[4][i]);
-    const f32x4 e4 = e4s[kc];
-    const f32x4 r4 = r4s[kc];
-    float part = 0.f;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) part += (ebe * e4[u] + acc[u]) * r4[u];
-    part += __shfl_xor(part, 16);
-    part += __shfl_xor(part, 32);
-    if (g == 0) sCarry[vb][i] = part;
-  }
-  __syncthreads();
-
-  {
-    f32x4 running;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      running[u] = ((sCarry[0][ki + u] + sCarry[1][ki + u]) + sCarry[2][ki + u]) + sCarry[3][ki + u];
-#pragma unroll
-    for (int I = 3; I >= 0; --I) {
+      // inter-chunk: (E dO^T)[key dim][token]
+      f32x4 ed = mma32(ea[0], ld128(tdo + swz<RB>(16 * I + n16, 8 * g)), f32x4{0.f, 0.f, 0.f, 0.f});
+      ed = mma32(ea[1], ld128(tdo + swz<RB>(16 * I + n16, 32 + 8 * g)), ed);
       const int t = 16 * I + n16;
-      const f16x4 q4 = ld64(tq + swz<RB>(t, ki));
-      const f16x4 k4 = ld64(tk + swz<RB>(t, ki));
-      f32x4 x;
+      const f32x4 ec = *reinterpret_cast<const f32x4*>(&sEc[t * ES + ki]);
+      const f16x4 fb = ld64(&sF[I][0][ki]);
+      f32x4 dq;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) x[u] = (float)q4[u] * dqv[I][u] - (float)k4[u] * dkv[I][u];
-      // suffix sums over the 16 tokens of the tile row (lanes n .. 15)
+      for (int u = 0; u < 4; ++u) dq[u] = ec[u] * (acc[u] + (float)fb[u] * ed[u]);
+      dqv[x] = dq;
+      store_grad4<ACC_K>(wdq, grad_off(gsk, t, ki), dq);
+    }
+
+    // log-alpha (Ke), k (Kd) and d_out are done with: the next chunk's go in
+    Plan pn;
+    if (more) {
+      wait_barrier<kLgkmZero>();
+      pn = plan(next, sel ^ 1, ln);
+      load_k_side(pn, p.la, tla);
+      load_k_side(pn, p.k, tk);
+      load_v_side(pn, p.dout, tdo);
+    }
+
+    // ---- dk (rows: key dims of this wave, columns: tokens of sub-block J)
+    f32x4 dkv[2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int J = sub[x];
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int I = J; I < 4; ++I) {
+        // Qs^T: key dim 16 kb + n, tokens 16I + 4g..; for I > J its row takes
+        // the decay between the boundaries, e^{Bst_I - Bst_J} (<= 1); times
+        // (dO V^T)[s in I][t in J], the transpose of an sM tile
+        f16x4 aop = tr_read_l(tqs, 16 * I, 16 * kb, ln);
+        if (I > J) aop = aop * sF[I][J][16 * kb + n16];
+        acc = mma16(aop, ld64(sM[I * (I + 1) / 2 + J] + soff), acc);
+      }
+      // inter-chunk: (R V^T)[key dim][token]
+      f32x4 rv = mma32(ra[0], ld128(tv + swz<RB>(16 * J + n16, 8 * g)), f32x4{0.f, 0.f, 0.f, 0.f});
+      rv = mma32(ra[1], ld128(tv + swz<RB>(16 * J + n16, 32 + 8 * g)), rv);
+      const int t = 16 * J + n16;
+      const f32x4 ec = *reinterpret_cast<const f32x4*>(&sEc[t * ES + ki]);
+      const f16x4 fe = ld64(&sF[4][J][ki]);
+      f32x4 dk;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        dk[u] = __builtin_amdgcn_rcpf(ec[u]) * (acc[u] + (float)fe[u] * rv[u]);
+      dkv[x] = dk;
+      store_grad4<ACC_K>(wdk, grad_off(gsk, t, ki), dk);
+    }
+
+    // dlog_alpha terms of the wave's two sub-blocks, q dq - k dk per token
+    // and key dim, summed over the tokens from each to its sub-block's end
+    // (the 16 lanes of a tile row, lanes n .. 15); the sub-block totals go to
+    // sTot
+    f32x4 xs[2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      f32x4 y;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) y[u] = (float)q4r[x][u] * dqv[x][u] - (float)k4r[x][u] * dkv[x][u];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        x[u] += dpp_f<kRowShl + 1>(x[u]);
-        x[u] += dpp_f<kRowShl + 2>(x[u]);
-        x[u] += dpp_f<kRowShl + 4>(x[u]);
-        x[u] += dpp_f<kRowShl + 8>(x[u]);
+        y[u] += dpp_f<kRowShl + 1>(y[u]);
+        y[u] += dpp_f<kRowShl + 2>(y[u]);
+        y[u] += dpp_f<kRowShl + 4>(y[u]);
+        y[u] += dpp_f<kRowShl + 8>(y[u]);
       }
-      f32x4 dla;
+      xs[x] = y;
+      if (n16 == 0) *reinterpret_cast<f32x4*>(&sTot[sub[x]][ki]) = y;   // the row's total
+    }
+    // q (Qs), v and the states are done with as well: the next chunk's go in
+    // (the barrier also makes the sub-block totals and the carry visible)
+    wait_barrier<kLgkmZero>();
+    if (more) {
+      load_k_side(pn, p.q, tq);
+      load_v_side(pn, p.v, tv);
+      load_states(next, ln);
+    }
+
+    // dlog_alpha = the in-sub-block suffix sum + the later sub-blocks' totals
+    // + the carry (the four value blocks' row sums)
+    const f32x4 carry = ((*reinterpret_cast<const f32x4*>(&sCarry[0][ki]) +
+                          *reinterpret_cast<const f32x4*>(&sCarry[1][ki])) +
+                         *reinterpret_cast<const f32x4*>(&sCarry[2][ki])) +
+                        *reinterpret_cast<const f32x4*>(&sCarry[3][ki]);
+    f32x4 tot[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        dla[u] = x[u] + running[u];
-        running[u] += dpp_f<kRowBcast + 0>(x[u]);   // the row's total (lane 0)
-      }
-      store4(wdla, gsk, acc_k, t, ki, dla);
+    for (int I2 = 1; I2 < 4; ++I2) tot[I2] = *reinterpret_cast<const f32x4*>(&sTot[I2][ki]);
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int I = sub[x];
+      f32x4 run = carry;
+#pragma unroll
+      for (int I2 = 3; I2 > 0; --I2)
+        if (I2 > I) run += tot[I2];
+      store_grad4<ACC_K>(wdla, grad_off(gsk, 16 * I + n16, ki), xs[x] + run);
     }
   }
 }
@@ -471,8 +616,11 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_f16_kernel(BwdParams p) {
 hipError_t launch_bwd_chunks(int d_k, int d_v, const BwdParams& p, hipStream_t stream,
                              hipEvent_t start, hipEvent_t stop) {
   if (d_k != 64 || d_v != 64) return hipErrorInvalidValue;
-  const dim3 grid(p.B * p.heads * p.n_chunks), block(kThreads);
-  const auto kernel = chunk_bwd_f16_kernel<64, 64>;
+  const dim3 grid(p.n_wg), block(kThreads);
+  const auto kernel = p.acc_dv ? (p.acc_dqk ? chunk_bwd_f16_kernel<64, 64, true, true>
+                                            : chunk_bwd_f16_kernel<64, 64, true, false>)
+                               : (p.acc_dqk ? chunk_bwd_f16_kernel<64, 64, false, true>
+                                            : chunk_bwd_f16_kernel<64, 64, false, false>);
   if (start != nullptr || stop != nullptr) {
     hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, start, stop, 0, p);
   } else {

@@ -80,6 +80,29 @@ __host__ __device__ constexpr int vmcnt_lgkm0_imm(int n) {
 __device__ __forceinline__ void dma16(rsrc_t src, f16* block, uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void_t*)block, 16, off, 0, 0, 0);
 }
+// The same written as assembly, so that the compiler adds no waits of its
+// own for it (it cannot tell the LDS this load fills from the LDS that later
+// reads touch, and would wait for the load before them): every wait on these
+// loads must be explicit (s_waitcnt vmcnt), and the LDS they fill read only
+// after such a wait and a barrier.  The block address goes to m0, which the
+// calling kernel must use for nothing else; one wait state separates the m0
+// write from the load that reads it.  NT marks the data non-temporal.
+template <bool NT>
+__device__ __forceinline__ void dma16_asm(rsrc_t src, const f16* block, uint32_t off) {
+  const uint32_t lds =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)const_cast<f16*>(block));
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+                 :
+                 : "s"(lds), "v"(off), "s"(src)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds), "v"(off), "s"(src)
+                 : "memory", "m0");
+}
+
 // The same with a cache policy: AUX bit 1 marks the data non-temporal (read
 // for the last time; the caches need not keep it).
 constexpr int kAuxNT = 2;

@@ -101,28 +101,6 @@ __device__ __forceinline__ f16x4 tr32(const f16* tile, int r0, int c0) {
   return __builtin_bit_cast(f16x4, x);
 }
 
-// LDS-writing load of 16 bytes per lane into a 1 KB block (lane l's bytes
-// land at byte 16 l of the block; an offset past the buffer writes zeros),
-// written as assembly so that the compiler adds no waits of its own for it:
-// every wait on these loads is explicit (s_waitcnt vmcnt), and the LDS they
-// fill is read only after such a wait and a barrier.  The block address goes
-// to m0, which nothing else in the kernel uses.
-template <bool NT>
-__device__ __forceinline__ void dma16a(rsrc_t src, const f16* block, uint32_t off) {
-  const uint32_t lds =
-      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)const_cast<f16*>(block));
-  if constexpr (NT)
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
-                 :
-                 : "s"(lds), "v"(off), "s"(src)
-                 : "memory", "m0");
-  else
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :
-                 : "s"(lds), "v"(off), "s"(src)
-                 : "memory", "m0");
-}
-
 // Per-stream context of a workgroup.
 struct Ctx {
   int bh, span;
@@ -152,10 +130,10 @@ __device__ __forceinline__ void issue_step(const Ctx& c, const FB& B, int j, int
     bool first;
     const uint32_t off = dma_offset_cell<128>(blk, t0, valid, c.gm, &cf, &first);
     if (OUT && first) B.rows[8 * blk + (lane >> 3)] = cf;
-    if (OUT) dma16a<OUT>(c.sb.q, B.q + blk * 512, off);
-    dma16a<OUT>(c.sb.k, B.k + blk * 512, off);
-    dma16a<OUT>(c.sb.la, B.l + blk * 512, off);
-    dma16a<OUT>(c.sb.v, B.v + blk * 512, off);
+    if (OUT) dma16_asm<OUT>(c.sb.q, B.q + blk * 512, off);
+    dma16_asm<OUT>(c.sb.k, B.k + blk * 512, off);
+    dma16_asm<OUT>(c.sb.la, B.l + blk * 512, off);
+    dma16_asm<OUT>(c.sb.v, B.v + blk * 512, off);
   }
 }
 

@@ -125,9 +125,10 @@ hipError_t launch_forward_two_pass(bool gate_logits, const FwdParams& p, hipStre
 hipError_t launch_bwd_states(int d_k, int d_v, const FwdParams& p, hipStream_t stream,
                              hipEvent_t const* events);
 
-// The chunk kernel of the backward pass: one workgroup per (batch*head,
-// chunk) turns the chunk's tiles, its forward entry state and the adjoint
-// state entering it from the right into dq, dk, dv and dlog_alpha.
+// The chunk kernel of the backward pass: n_wg persistent workgroups take the
+// (batch*head, chunk) pairs in turn and turn each chunk's tiles, its forward
+// entry state and the adjoint state entering it from the right into dq, dk,
+// dv and dlog_alpha.
 struct BwdParams {
   const void* q;
   const void* k;
@@ -153,6 +154,7 @@ struct BwdParams {
   // the value dims dq, dk and dlog-alpha)
   unsigned int ldk, ldv;
   int acc_dv, acc_dqk;
+  int n_wg;                 // persistent workgroups (at most two per CU)
 };
 
 hipError_t launch_bwd_chunks(int d_k, int d_v, const BwdParams& p, hipStream_t stream,
