@@ -47,6 +47,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "gla_device.h"
 #include "gla_internal.h"
 #include "gla_tiles.h"
@@ -97,20 +99,36 @@ __device__ __forceinline__ f16x4 tr_read_l(const f16* tile, int row0, int col0, 
   return __builtin_bit_cast(f16x4, x);
 }
 
+// x of the lane whose index differs in bit 4 (xor16) or bit 5 (xor32), by a
+// row swap in the VALU: with both operands x, v_permlane16_swap leaves row
+// q ^ 1's values in its first result for odd rows q and in its second for
+// even rows, v_permlane32_swap rows q ^ 2's in its first result for rows 2, 3
+// and in its second for rows 0, 1.
+__device__ __forceinline__ float xor16(float x, int lane) {
+  const unsigned b = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  return __builtin_bit_cast(float, (lane & 16) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float xor32(float x, int lane) {
+  const unsigned b = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  return __builtin_bit_cast(float, (lane & 32) ? r[0] : r[1]);
+}
+
 // Over the four 16-lane groups of a wave (group q = lane / 16): the
 // product of x over the groups before this lane's (*before) and after it
 // (*after).
-__device__ __forceinline__ void group_products(float x, int q, float* before, float* after) {
-  const float x1 = __shfl_xor(x, 16), x2 = __shfl_xor(x, 32), x3 = __shfl_xor(x1, 32);
+__device__ __forceinline__ void group_products(float x, int lane, float* before, float* after) {
+  const int q = lane >> 4;
+  const float x1 = xor16(x, lane), x2 = xor32(x, lane), x3 = xor32(x1, lane);
   // x1, x2, x3: groups q ^ 1, q ^ 2, q ^ 3
   const float y23 = x2 * x3, y123 = x1 * y23;
   *before = q == 0 ? 1.f : q == 1 ? x1 : q == 2 ? y23 : y123;
   *after = q == 0 ? y123 : q == 1 ? y23 : q == 2 ? x1 : 1.f;
 }
-__device__ __forceinline__ float group_sum(float x) {
-  const float x1 = __shfl_xor(x, 16);
-  const float y = x + x1;
-  return y + __shfl_xor(y, 32);
+__device__ __forceinline__ float group_sum(float x, int lane) {
+  const float y = x + xor16(x, lane);
+  return y + xor32(y, lane);
 }
 
 // Four gradient values of one token to float16 at `off` of `dst`; with ACC
@@ -338,10 +356,10 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_bwd_f16_kernel(BwdParams p)
         p1 *= al1[u];
       }
       float pre0, pre1, suf0, suf1;
-      group_products(p0, q, &pre0, &suf0);
-      group_products(p1, q, &pre1, &suf1);
-      tot0 = group_sum(tot0);
-      tot1 = group_sum(tot1);
+      group_products(p0, ln, &pre0, &suf0);
+      group_products(p1, ln, &pre1, &suf1);
+      tot0 = group_sum(tot0, ln);
+      tot1 = group_sum(tot1, ln);
       float ec0 = pre0, ec1 = pre1;
       f16x2 qs2[4], kd2[4];
       f32x2 ecs[4];
@@ -392,222 +410,278 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_bwd_f16_kernel(BwdParams p)
         const int e = swz<RB>(tb + u, i);
         *reinterpret_cast<f16x2*>(&tke[e]) = f16x2{(f16)(kf0[u] * te0), (f16)(kf1[u] * te1)};
       }
-      // factors between sub-block boundaries, thread (key dim, eighth)
-      for (int ab = wave; ab < 25; ab += kThreads / 64) {
-        const int a = ab / 5, bb = ab % 5;
-        sF[a][bb][ln] = (f16)ex(sBst[a][ln] - sBst[bb][ln]);
+      // factors between sub-block boundaries, thread (key dim, eighth): wave
+      // w forms the pairs w, w + 8, .. (pair ab: a = ab / 5, b = ab % 5), each
+      // as code of its own
+      float bs[5];
+#pragma unroll
+      for (int j = 0; j < 5; ++j) bs[j] = sBst[j][ln];
+      auto factor = [&](auto ab_c) __attribute__((always_inline)) {
+        constexpr int ab = decltype(ab_c)::value;
+        if constexpr (ab < 25) sF[ab / 5][ab % 5][ln] = (f16)ex(bs[ab / 5] - bs[ab % 5]);
+      };
+      auto factors = [&](auto w_c) __attribute__((always_inline)) {
+        constexpr int w = decltype(w_c)::value;
+        factor(std::integral_constant<int, w>{});
+        factor(std::integral_constant<int, w + 8>{});
+        factor(std::integral_constant<int, w + 16>{});
+        factor(std::integral_constant<int, w + 24>{});
+      };
+      switch (wave) {
+        case 0: factors(std::integral_constant<int, 0>{}); break;
+        case 1: factors(std::integral_constant<int, 1>{}); break;
+        case 2: factors(std::integral_constant<int, 2>{}); break;
+        case 3: factors(std::integral_constant<int, 3>{}); break;
+        case 4: factors(std::integral_constant<int, 4>{}); break;
+        case 5: factors(std::integral_constant<int, 5>{}); break;
+        case 6: factors(std::integral_constant<int, 6>{}); break;
+        default: factors(std::integral_constant<int, 7>{}); break;
       }
     }
     wait_barrier<kLgkmZero>();
 
-    // ---- next state rows 16 kc + n (kc = 2 hf, 2 hf + 1), columns vj ..:
-    // E_{c+1} = diag(e^{B_end}) E_c + Ke^T V; its row sums against R_c over
-    // the wave's 16 value columns are its part of the carry (read after the
-    // barrier before dlog-alpha)
+    // The next state: instantiated for each half of the waves, so that their
+    // sub-blocks are constants and the loops over sub-block pairs unroll
+    auto next_state = [&](auto half) __attribute__((always_inline)) {
+      constexpr int HF = decltype(half)::value;
+      // ---- next state rows 16 kc + n (kc = 2 hf, 2 hf + 1), columns vj ..:
+      // E_{c+1} = diag(e^{B_end}) E_c + Ke^T V; its row sums against R_c over
+      // the wave's 16 value columns are its part of the carry (read after the
+      // barrier before dlog-alpha)
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int kc = 2 * hf + x;
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int x = 0; x < 2; ++x) {
+        const int kc = 2 * HF + x;
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int P = 0; P < 2; ++P) {
-        const f16x8 av = cat8(tr_read_l(tv, 32 * P, 16 * vb, ln), tr_read_l(tv, 32 * P + 16, 16 * vb, ln));
-        const f16x8 bk = cat8(tr_read_l(tke, 32 * P, 16 * kc, ln), tr_read_l(tke, 32 * P + 16, 16 * kc, ln));
-        acc = mma32(av, bk, acc);
+        for (int P = 0; P < 2; ++P) {
+          const f16x8 av = cat8(tr_read_l(tv, 32 * P, 16 * vb, ln), tr_read_l(tv, 32 * P + 16, 16 * vb, ln));
+          const f16x8 bk = cat8(tr_read_l(tke, 32 * P, 16 * kc, ln), tr_read_l(tke, 32 * P + 16, 16 * kc, ln));
+          acc = mma32(av, bk, acc);
+        }
+        // lane (n, g): E_next[i = 16 kc + n][j = 16 vb + 4g + u]
+        const int i = 16 * kc + n16;
+        const float ebe = ex(sBst[4][i]);
+        const f16x4 e4 = e4h[x], r4 = r4h[x];
+        float part = 0.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) part += (ebe * (float)e4[u] + acc[u]) * (float)r4[u];
+        part += xor16(part, ln);
+        part += xor32(part, ln);
+        if (g == 0) sCarry[vb][i] = part;
       }
-      // lane (n, g): E_next[i = 16 kc + n][j = 16 vb + 4g + u]
-      const int i = 16 * kc + n16;
-      const float ebe = ex(sBst[4][i]);
-      const f16x4 e4 = e4h[x], r4 = r4h[x];
-      float part = 0.f;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) part += (ebe * (float)e4[u] + acc[u]) * (float)r4[u];
-      part += __shfl_xor(part, 16);
-      part += __shfl_xor(part, 32);
-      if (g == 0) sCarry[vb][i] = part;
-    }
+    };
+    if (hf == 0)
+      next_state(std::integral_constant<int, 0>{});
+    else
+      next_state(std::integral_constant<int, 1>{});
 
     // ---- the score tiles (the ten sM tiles, then the ten sP tiles; wave w
-    // forms tiles w, w + 8, w + 16), each once for all waves.  Lane (n, g) of
-    // a 16 x 16 accumulator holds row n, columns 4g .. 4g + 3 when the first
-    // operand supplies the columns and the second the rows.
+    // forms tiles w, w + 8, w + 16), each once for all waves, each as code of
+    // its own (its sub-blocks constants).  Lane (n, g) of a 16 x 16
+    // accumulator holds row n, columns 4g .. 4g + 3 when the first operand
+    // supplies the columns and the second the rows.
     const int soff = st_tile_off(n16, g);
+    auto score_tile = [&](auto tau_c) __attribute__((always_inline)) {
+      constexpr int tau = decltype(tau_c)::value;
+      constexpr int pr = tau < 10 ? tau : tau - 10;
+      constexpr int I = pr >= 6 ? 3 : pr >= 3 ? 2 : pr >= 1 ? 1 : 0;
+      constexpr int J = pr - I * (I + 1) / 2;
+      if constexpr (tau < 10) {
+        // rows s of J (values), columns t of I (output gradients)
+        f32x4 sc = mma32(ld128(tdo + swz<RB>(16 * I + n16, 8 * g)),
+                         ld128(tv + swz<RB>(16 * J + n16, 8 * g)), f32x4{0.f, 0.f, 0.f, 0.f});
+        sc = mma32(ld128(tdo + swz<RB>(16 * I + n16, 32 + 8 * g)),
+                   ld128(tv + swz<RB>(16 * J + n16, 32 + 8 * g)), sc);
+        if constexpr (I == J) {
 #pragma unroll
-    for (int m = 0; m < 3; ++m) {
-      const int tau = wave + 8 * m;
-      if (tau < 20) {
-        const int pr = tau < 10 ? tau : tau - 10;
-        const int I = pr >= 6 ? 3 : pr >= 3 ? 2 : pr >= 1 ? 1 : 0;
-        const int J = pr - I * (I + 1) / 2;
-        if (tau < 10) {
-          // rows s of J (values), columns t of I (output gradients)
-          f32x4 sc = mma32(ld128(tdo + swz<RB>(16 * I + n16, 8 * g)),
-                           ld128(tv + swz<RB>(16 * J + n16, 8 * g)), f32x4{0.f, 0.f, 0.f, 0.f});
-          sc = mma32(ld128(tdo + swz<RB>(16 * I + n16, 32 + 8 * g)),
-                     ld128(tv + swz<RB>(16 * J + n16, 32 + 8 * g)), sc);
-          if (I == J) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) sc[u] = (n16 <= 4 * g + u) ? sc[u] : 0.f;
-          }
-          st64(sM[pr] + soff, to_f16(sc));
-        } else {
-          // rows s of I (Qs), columns t of J (Kd); the decay between the
-          // rows' sub-block start and the columns' sub-block end sits on the
-          // key dims: e^{Bst_I - Bst_{J+1}} (<= 1) on Qs for I > J, or
-          // e^{Bst_J - Bst_{J+1}} (>= 1, back to the sub-block start) on Kd
-          // for I = J (Qs stays <= |q|)
-          f16x8 qa0 = ld128(tqs + swz<RB>(16 * I + n16, 8 * g));
-          f16x8 qa1 = ld128(tqs + swz<RB>(16 * I + n16, 32 + 8 * g));
-          f16x8 kx0 = ld128(tkd + swz<RB>(16 * J + n16, 8 * g));
-          f16x8 kx1 = ld128(tkd + swz<RB>(16 * J + n16, 32 + 8 * g));
-          const f16x8 f0 = ld128(&sF[I][J + 1][8 * g]);
-          const f16x8 f1 = ld128(&sF[I][J + 1][32 + 8 * g]);
-          if (I == J) {
-            kx0 = kx0 * f0;
-            kx1 = kx1 * f1;
-          } else {
-            qa0 = qa0 * f0;
-            qa1 = qa1 * f1;
-          }
-          f32x4 sc = mma32(kx0, qa0, f32x4{0.f, 0.f, 0.f, 0.f});
-          sc = mma32(kx1, qa1, sc);
-          if (I == J) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) sc[u] = (n16 >= 4 * g + u) ? sc[u] : 0.f;
-          }
-          st64(sP[pr] + soff, to_f16(sc));
+          for (int u = 0; u < 4; ++u) sc[u] = (n16 <= 4 * g + u) ? sc[u] : 0.f;
         }
+        st64(sM[pr] + soff, to_f16(sc));
+      } else {
+        // rows s of I (Qs), columns t of J (Kd); the decay between the rows'
+        // sub-block start and the columns' sub-block end sits on the key
+        // dims: e^{Bst_I - Bst_{J+1}} (<= 1) on Qs for I > J, or
+        // e^{Bst_J - Bst_{J+1}} (>= 1, back to the sub-block start) on Kd for
+        // I = J (Qs stays <= |q|)
+        f16x8 qa0 = ld128(tqs + swz<RB>(16 * I + n16, 8 * g));
+        f16x8 qa1 = ld128(tqs + swz<RB>(16 * I + n16, 32 + 8 * g));
+        f16x8 kx0 = ld128(tkd + swz<RB>(16 * J + n16, 8 * g));
+        f16x8 kx1 = ld128(tkd + swz<RB>(16 * J + n16, 32 + 8 * g));
+        const f16x8 f0 = ld128(&sF[I][J + 1][8 * g]);
+        const f16x8 f1 = ld128(&sF[I][J + 1][32 + 8 * g]);
+        if constexpr (I == J) {
+          kx0 = kx0 * f0;
+          kx1 = kx1 * f1;
+        } else {
+          qa0 = qa0 * f0;
+          qa1 = qa1 * f1;
+        }
+        f32x4 sc = mma32(kx0, qa0, f32x4{0.f, 0.f, 0.f, 0.f});
+        sc = mma32(kx1, qa1, sc);
+        if constexpr (I == J) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) sc[u] = (n16 >= 4 * g + u) ? sc[u] : 0.f;
+        }
+        st64(sP[pr] + soff, to_f16(sc));
       }
+    };
+    using std::integral_constant;
+    switch (wave) {
+      case 0: score_tile(integral_constant<int, 0>{}); score_tile(integral_constant<int, 8>{});
+              score_tile(integral_constant<int, 16>{}); break;
+      case 1: score_tile(integral_constant<int, 1>{}); score_tile(integral_constant<int, 9>{});
+              score_tile(integral_constant<int, 17>{}); break;
+      case 2: score_tile(integral_constant<int, 2>{}); score_tile(integral_constant<int, 10>{});
+              score_tile(integral_constant<int, 18>{}); break;
+      case 3: score_tile(integral_constant<int, 3>{}); score_tile(integral_constant<int, 11>{});
+              score_tile(integral_constant<int, 19>{}); break;
+      case 4: score_tile(integral_constant<int, 4>{}); score_tile(integral_constant<int, 12>{}); break;
+      case 5: score_tile(integral_constant<int, 5>{}); score_tile(integral_constant<int, 13>{}); break;
+      case 6: score_tile(integral_constant<int, 6>{}); score_tile(integral_constant<int, 14>{}); break;
+      default: score_tile(integral_constant<int, 7>{}); score_tile(integral_constant<int, 15>{}); break;
     }
     wait_barrier<kLgkmZero>();
 
-    // ---- dv (rows: value dims of this wave, columns: tokens of sub-block J)
+    // dv, dq, dk and dlog-alpha: instantiated for each half of the waves, so that their
+    // sub-blocks are constants and the loops over sub-block pairs unroll
+    auto gradients = [&](auto half) __attribute__((always_inline)) {
+      constexpr int HF = decltype(half)::value;
+      // ---- dv (rows: value dims of this wave, columns: tokens of sub-block J)
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int J = sub[x];
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int I = J; I < 4; ++I)
-        acc = mma16(tr_read_l(tdo, 16 * I, 16 * vb, ln), tr_tile(sP[I * (I + 1) / 2 + J], ln), acc);
-      // inter-chunk: (R^T Ke^T)[value dim][token], key dims in rta's order
-      const int row = 16 * J + n16;
-      f32x4 rk = mma32(rta[0], cat8(ld64(tke + swz<RB>(row, 4 * g)), ld64(tke + swz<RB>(row, 16 + 4 * g))),
-                       f32x4{0.f, 0.f, 0.f, 0.f});
-      rk = mma32(rta[1], cat8(ld64(tke + swz<RB>(row, 32 + 4 * g)), ld64(tke + swz<RB>(row, 48 + 4 * g))),
-                 rk);
-      store_grad4<ACC_V>(wdv, grad_off(gsv, row, vj), acc + rk);
-    }
-
-    // ---- dq (rows: key dims of this wave, columns: tokens of sub-block I)
-    f32x4 dqv[2];
+      for (int x = 0; x < 2; ++x) {
+        const int J = (x == 0 ? HF : 3 - HF);
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int I = sub[x];
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int J = 0; J <= I; ++J) {
-        // Kd^T: key dim 16 kb + n, tokens 16J + 4g..; the row's factor is the
-        // decay back to the sub-block start, k e^{-c} = Kd e^{Bst_J - Bst_{J+1}}
-        // (>= 1) for J = I, or between the boundaries, e^{Bst_I - Bst_{J+1}}
-        // (<= 1) for J < I; times (V dO^T)[s in J][t in I]
-        const f16 fk = sF[I][J + 1][16 * kb + n16];
-        acc = mma16(tr_read_l(tkd, 16 * J, 16 * kb, ln) * fk, tr_tile(sM[I * (I + 1) / 2 + J], ln), acc);
+        for (int I = J; I < 4; ++I)
+          acc = mma16(tr_read_l(tdo, 16 * I, 16 * vb, ln), tr_tile(sP[I * (I + 1) / 2 + J], ln), acc);
+        // inter-chunk: (R^T Ke^T)[value dim][token], key dims in rta's order
+        const int row = 16 * J + n16;
+        f32x4 rk = mma32(rta[0], cat8(ld64(tke + swz<RB>(row, 4 * g)), ld64(tke + swz<RB>(row, 16 + 4 * g))),
+                         f32x4{0.f, 0.f, 0.f, 0.f});
+        rk = mma32(rta[1], cat8(ld64(tke + swz<RB>(row, 32 + 4 * g)), ld64(tke + swz<RB>(row, 48 + 4 * g))),
+                   rk);
+        store_grad4<ACC_V>(wdv, grad_off(gsv, row, vj), acc + rk);
       }
-      // inter-chunk: (E dO^T)[key dim][token]
-      f32x4 ed = mma32(ea[0], ld128(tdo + swz<RB>(16 * I + n16, 8 * g)), f32x4{0.f, 0.f, 0.f, 0.f});
-      ed = mma32(ea[1], ld128(tdo + swz<RB>(16 * I + n16, 32 + 8 * g)), ed);
-      const int t = 16 * I + n16;
-      const f32x4 ec = *reinterpret_cast<const f32x4*>(&sEc[t * ES + ki]);
-      const f16x4 fb = ld64(&sF[I][0][ki]);
-      f32x4 dq;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) dq[u] = ec[u] * (acc[u] + (float)fb[u] * ed[u]);
-      dqv[x] = dq;
-      store_grad4<ACC_K>(wdq, grad_off(gsk, t, ki), dq);
-    }
 
-    // log-alpha (Ke), k (Kd) and d_out are done with: the next chunk's go in
-    Plan pn;
-    if (more) {
+      // ---- dq (rows: key dims of this wave, columns: tokens of sub-block I)
+      f32x4 dqv[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int I = (x == 0 ? HF : 3 - HF);
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int J = 0; J <= I; ++J) {
+          // Kd^T: key dim 16 kb + n, tokens 16J + 4g..; the row's factor is the
+          // decay back to the sub-block start, k e^{-c} = Kd e^{Bst_J - Bst_{J+1}}
+          // (>= 1) for J = I, or between the boundaries, e^{Bst_I - Bst_{J+1}}
+          // (<= 1) for J < I; times (V dO^T)[s in J][t in I]
+          const f16 fk = sF[I][J + 1][16 * kb + n16];
+          acc = mma16(tr_read_l(tkd, 16 * J, 16 * kb, ln) * fk, tr_tile(sM[I * (I + 1) / 2 + J], ln), acc);
+        }
+        // inter-chunk: (E dO^T)[key dim][token]
+        f32x4 ed = mma32(ea[0], ld128(tdo + swz<RB>(16 * I + n16, 8 * g)), f32x4{0.f, 0.f, 0.f, 0.f});
+        ed = mma32(ea[1], ld128(tdo + swz<RB>(16 * I + n16, 32 + 8 * g)), ed);
+        const int t = 16 * I + n16;
+        const f32x4 ec = *reinterpret_cast<const f32x4*>(&sEc[t * ES + ki]);
+        const f16x4 fb = ld64(&sF[I][0][ki]);
+        f32x4 dq;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) dq[u] = ec[u] * (acc[u] + (float)fb[u] * ed[u]);
+        dqv[x] = dq;
+        store_grad4<ACC_K>(wdq, grad_off(gsk, t, ki), dq);
+      }
+
+      // log-alpha (Ke), k (Kd) and d_out are done with: the next chunk's go in
+      Plan pn;
+      if (more) {
+        wait_barrier<kLgkmZero>();
+        pn = plan(next, sel ^ 1, ln);
+        load_k_side(pn, p.la, tla);
+        load_k_side(pn, p.k, tk);
+        load_v_side(pn, p.dout, tdo);
+      }
+
+      // ---- dk (rows: key dims of this wave, columns: tokens of sub-block J)
+      f32x4 dkv[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int J = (x == 0 ? HF : 3 - HF);
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int I = J; I < 4; ++I) {
+          // Qs^T: key dim 16 kb + n, tokens 16I + 4g..; for I > J its row takes
+          // the decay between the boundaries, e^{Bst_I - Bst_J} (<= 1); times
+          // (dO V^T)[s in I][t in J], the transpose of an sM tile
+          f16x4 aop = tr_read_l(tqs, 16 * I, 16 * kb, ln);
+          if (I > J) aop = aop * sF[I][J][16 * kb + n16];
+          acc = mma16(aop, ld64(sM[I * (I + 1) / 2 + J] + soff), acc);
+        }
+        // inter-chunk: (R V^T)[key dim][token]
+        f32x4 rv = mma32(ra[0], ld128(tv + swz<RB>(16 * J + n16, 8 * g)), f32x4{0.f, 0.f, 0.f, 0.f});
+        rv = mma32(ra[1], ld128(tv + swz<RB>(16 * J + n16, 32 + 8 * g)), rv);
+        const int t = 16 * J + n16;
+        const f32x4 ec = *reinterpret_cast<const f32x4*>(&sEc[t * ES + ki]);
+        const f16x4 fe = ld64(&sF[4][J][ki]);
+        f32x4 dk;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          dk[u] = __builtin_amdgcn_rcpf(ec[u]) * (acc[u] + (float)fe[u] * rv[u]);
+        dkv[x] = dk;
+        store_grad4<ACC_K>(wdk, grad_off(gsk, t, ki), dk);
+      }
+
+      // dlog_alpha terms of the wave's two sub-blocks, q dq - k dk per token
+      // and key dim, summed over the tokens from each to its sub-block's end
+      // (the 16 lanes of a tile row, lanes n .. 15); the sub-block totals go to
+      // sTot
+      f32x4 xs[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        f32x4 y;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) y[u] = (float)q4r[x][u] * dqv[x][u] - (float)k4r[x][u] * dkv[x][u];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          y[u] += dpp_f<kRowShl + 1>(y[u]);
+          y[u] += dpp_f<kRowShl + 2>(y[u]);
+          y[u] += dpp_f<kRowShl + 4>(y[u]);
+          y[u] += dpp_f<kRowShl + 8>(y[u]);
+        }
+        xs[x] = y;
+        if (n16 == 0) *reinterpret_cast<f32x4*>(&sTot[(x == 0 ? HF : 3 - HF)][ki]) = y;   // the row's total
+      }
+      // q (Qs), v and the states are done with as well: the next chunk's go in
+      // (the barrier also makes the sub-block totals and the carry visible)
       wait_barrier<kLgkmZero>();
-      pn = plan(next, sel ^ 1, ln);
-      load_k_side(pn, p.la, tla);
-      load_k_side(pn, p.k, tk);
-      load_v_side(pn, p.dout, tdo);
-    }
-
-    // ---- dk (rows: key dims of this wave, columns: tokens of sub-block J)
-    f32x4 dkv[2];
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int J = sub[x];
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int I = J; I < 4; ++I) {
-        // Qs^T: key dim 16 kb + n, tokens 16I + 4g..; for I > J its row takes
-        // the decay between the boundaries, e^{Bst_I - Bst_J} (<= 1); times
-        // (dO V^T)[s in I][t in J], the transpose of an sM tile
-        f16x4 aop = tr_read_l(tqs, 16 * I, 16 * kb, ln);
-        if (I > J) aop = aop * sF[I][J][16 * kb + n16];
-        acc = mma16(aop, ld64(sM[I * (I + 1) / 2 + J] + soff), acc);
+      if (more) {
+        load_k_side(pn, p.q, tq);
+        load_v_side(pn, p.v, tv);
+        load_states(next, ln);
       }
-      // inter-chunk: (R V^T)[key dim][token]
-      f32x4 rv = mma32(ra[0], ld128(tv + swz<RB>(16 * J + n16, 8 * g)), f32x4{0.f, 0.f, 0.f, 0.f});
-      rv = mma32(ra[1], ld128(tv + swz<RB>(16 * J + n16, 32 + 8 * g)), rv);
-      const int t = 16 * J + n16;
-      const f32x4 ec = *reinterpret_cast<const f32x4*>(&sEc[t * ES + ki]);
-      const f16x4 fe = ld64(&sF[4][J][ki]);
-      f32x4 dk;
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        dk[u] = __builtin_amdgcn_rcpf(ec[u]) * (acc[u] + (float)fe[u] * rv[u]);
-      dkv[x] = dk;
-      store_grad4<ACC_K>(wdk, grad_off(gsk, t, ki), dk);
-    }
 
-    // dlog_alpha terms of the wave's two sub-blocks, q dq - k dk per token
-    // and key dim, summed over the tokens from each to its sub-block's end
-    // (the 16 lanes of a tile row, lanes n .. 15); the sub-block totals go to
-    // sTot
-    f32x4 xs[2];
+      // dlog_alpha = the in-sub-block suffix sum + the later sub-blocks' totals
+      // + the carry (the four value blocks' row sums)
+      const f32x4 carry = ((*reinterpret_cast<const f32x4*>(&sCarry[0][ki]) +
+                            *reinterpret_cast<const f32x4*>(&sCarry[1][ki])) +
+                           *reinterpret_cast<const f32x4*>(&sCarry[2][ki])) +
+                          *reinterpret_cast<const f32x4*>(&sCarry[3][ki]);
+      f32x4 tot[4];
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      f32x4 y;
+      for (int I2 = 1; I2 < 4; ++I2) tot[I2] = *reinterpret_cast<const f32x4*>(&sTot[I2][ki]);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) y[u] = (float)q4r[x][u] * dqv[x][u] - (float)k4r[x][u] * dkv[x][u];
+      for (int x = 0; x < 2; ++x) {
+        const int I = (x == 0 ? HF : 3 - HF);
+        f32x4 run = carry;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        y[u] += dpp_f<kRowShl + 1>(y[u]);
-        y[u] += dpp_f<kRowShl + 2>(y[u]);
-        y[u] += dpp_f<kRowShl + 4>(y[u]);
-        y[u] += dpp_f<kRowShl + 8>(y[u]);
+        for (int I2 = 3; I2 > 0; --I2)
+          if (I2 > I) run += tot[I2];
+        store_grad4<ACC_K>(wdla, grad_off(gsk, 16 * I + n16, ki), xs[x] + run);
       }
-      xs[x] = y;
-      if (n16 == 0) *reinterpret_cast<f32x4*>(&sTot[sub[x]][ki]) = y;   // the row's total
-    }
-    // q (Qs), v and the states are done with as well: the next chunk's go in
-    // (the barrier also makes the sub-block totals and the carry visible)
-    wait_barrier<kLgkmZero>();
-    if (more) {
-      load_k_side(pn, p.q, tq);
-      load_v_side(pn, p.v, tv);
-      load_states(next, ln);
-    }
-
-    // dlog_alpha = the in-sub-block suffix sum + the later sub-blocks' totals
-    // + the carry (the four value blocks' row sums)
-    const f32x4 carry = ((*reinterpret_cast<const f32x4*>(&sCarry[0][ki]) +
-                          *reinterpret_cast<const f32x4*>(&sCarry[1][ki])) +
-                         *reinterpret_cast<const f32x4*>(&sCarry[2][ki])) +
-                        *reinterpret_cast<const f32x4*>(&sCarry[3][ki]);
-    f32x4 tot[4];
-#pragma unroll
-    for (int I2 = 1; I2 < 4; ++I2) tot[I2] = *reinterpret_cast<const f32x4*>(&sTot[I2][ki]);
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int I = sub[x];
-      f32x4 run = carry;
-#pragma unroll
-      for (int I2 = 3; I2 > 0; --I2)
-        if (I2 > I) run += tot[I2];
-      store_grad4<ACC_K>(wdla, grad_off(gsk, 16 * I + n16, ki), xs[x] + run);
-    }
+    };
+    if (hf == 0)
+      gradients(std::integral_constant<int, 0>{});
+    else
+      gradients(std::integral_constant<int, 1>{});
   }
 }
 
