@@ -184,7 +184,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_bwd_f16_kernel(BwdParams p)
   // per sub-block and key dim: the log-decay total (decay pass), later the
   // total of q dq - k dk (dlog-alpha)
   __shared__ float sTot[4][DK];
-  __shared__ float sBst[5][DK];   // B before sub-block I (I = 0..3), [4] = chunk total
+  __shared__ float sBst[DK];      // B at the chunk end (the chunk's log-decay total)
   __shared__ float sCarry[4][DK];
   f16* const tqs = tq;            // q e^{c}
   f16* const tkd = tk;            // k decayed to its sub-block's end
@@ -392,19 +392,26 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_bwd_f16_kernel(BwdParams p)
         *reinterpret_cast<f16x2*>(&tkd[e]) = kd2[u];
         *reinterpret_cast<f32x2*>(&sEc[(tb + u) * ES + i]) = ecs[u];
       }
-      if (wave == 0) {
-        float acc = 0.f;
-        sBst[0][ln] = 0.f;
+      // B before each sub-block boundary for key dim ln (the boundary
+      // factors), summed from the sub-block totals; the chunk total goes to
+      // sBst for the next-state update
+      float bs[5];
+      bs[0] = 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          acc += sTot[j][ln];
-          sBst[j + 1][ln] = acc;
-        }
-      }
-      wait_barrier<kLgkmZero>();
+      for (int j = 0; j < 4; ++j) bs[j + 1] = bs[j] + sTot[j][ln];
+      if (wave == 0) sBst[ln] = bs[4];
       // k decayed to the chunk end = k decayed to its sub-block end times the
       // decay of the later sub-blocks (log-alpha's tile is free now)
-      const float te0 = ex(sBst[4][i] - sBst[J + 1][i]), te1 = ex(sBst[4][i + 1] - sBst[J + 1][i + 1]);
+      float lt0 = 0.f, lt1 = 0.f;
+#pragma unroll
+      for (int j = 1; j < 4; ++j) {
+        if (j > J) {
+          const f32x2 t2 = *reinterpret_cast<const f32x2*>(&sTot[j][i]);
+          lt0 += t2[0];
+          lt1 += t2[1];
+        }
+      }
+      const float te0 = ex(lt0), te1 = ex(lt1);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int e = swz<RB>(tb + u, i);
@@ -413,9 +420,6 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_bwd_f16_kernel(BwdParams p)
       // factors between sub-block boundaries, thread (key dim, eighth): wave
       // w forms the pairs w, w + 8, .. (pair ab: a = ab / 5, b = ab % 5), each
       // as code of its own
-      float bs[5];
-#pragma unroll
-      for (int j = 0; j < 5; ++j) bs[j] = sBst[j][ln];
       auto factor = [&](auto ab_c) __attribute__((always_inline)) {
         constexpr int ab = decltype(ab_c)::value;
         if constexpr (ab < 25) sF[ab / 5][ab % 5][ln] = (f16)ex(bs[ab / 5] - bs[ab % 5]);
@@ -460,7 +464,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_bwd_f16_kernel(BwdParams p)
         }
         // lane (n, g): E_next[i = 16 kc + n][j = 16 vb + 4g + u]
         const int i = 16 * kc + n16;
-        const float ebe = ex(sBst[4][i]);
+        const float ebe = ex(sBst[i]);
         const f16x4 e4 = e4h[x], r4 = r4h[x];
         float part = 0.f;
 #pragma unroll
