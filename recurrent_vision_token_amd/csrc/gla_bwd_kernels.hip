@@ -567,8 +567,9 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_bwd_f16_kernel(BwdParams p)
         store_grad4<ACC_V>(wdv, grad_off(gsv, row, vj), acc + rk);
       }
 
-      // ---- dq (rows: key dims of this wave, columns: tokens of sub-block I)
-      f32x4 dqv[2];
+      // ---- dq (rows: key dims of this wave, columns: tokens of sub-block I):
+      // the products first, which are the last reads of Kd and d_out
+      f32x4 qacc[2], qed[2];
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
         const int I = (x == 0 ? HF : 3 - HF);
@@ -582,20 +583,21 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_bwd_f16_kernel(BwdParams p)
           const f16 fk = sF[I][J + 1][16 * kb + n16];
           acc = mma16(tr_read_l(tkd, 16 * J, 16 * kb, ln) * fk, tr_tile(sM[I * (I + 1) / 2 + J], ln), acc);
         }
+        qacc[x] = acc;
         // inter-chunk: (E dO^T)[key dim][token]
         f32x4 ed = mma32(ea[0], ld128(tdo + swz<RB>(16 * I + n16, 8 * g)), f32x4{0.f, 0.f, 0.f, 0.f});
-        ed = mma32(ea[1], ld128(tdo + swz<RB>(16 * I + n16, 32 + 8 * g)), ed);
-        const int t = 16 * I + n16;
-        const f32x4 ec = *reinterpret_cast<const f32x4*>(&sEc[t * ES + ki]);
-        const f16x4 fb = ld64(&sF[I][0][ki]);
-        f32x4 dq;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) dq[u] = ec[u] * (acc[u] + (float)fb[u] * ed[u]);
-        dqv[x] = dq;
-        store_grad4<ACC_K>(wdq, grad_off(gsk, t, ki), dq);
+        qed[x] = mma32(ea[1], ld128(tdo + swz<RB>(16 * I + n16, 32 + 8 * g)), ed);
       }
 
-      // log-alpha (Ke), k (Kd) and d_out are done with: the next chunk's go in
+      // e^c of this wave's dq / dk tiles (the same tokens and key dims), taken
+      // out of the area the next chunk's states go into
+      f32x4 ecr[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+        ecr[x] = *reinterpret_cast<const f32x4*>(&sEc[(16 * (x == 0 ? HF : 3 - HF) + n16) * ES + ki]);
+
+      // log-alpha (Ke), k (Kd), d_out and the states are done with: the next
+      // chunk's go in
       Plan pn;
       if (more) {
         wait_barrier<kLgkmZero>();
@@ -603,6 +605,22 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_bwd_f16_kernel(BwdParams p)
         load_k_side(pn, p.la, tla);
         load_k_side(pn, p.k, tk);
         load_v_side(pn, p.dout, tdo);
+        load_states(next, ln);
+      }
+
+      // dq's scaling and stores
+      f32x4 dqv[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int I = (x == 0 ? HF : 3 - HF);
+        const int t = 16 * I + n16;
+        const f32x4 ec = ecr[x];
+        const f16x4 fb = ld64(&sF[I][0][ki]);
+        f32x4 dq;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) dq[u] = ec[u] * (qacc[x][u] + (float)fb[u] * qed[x][u]);
+        dqv[x] = dq;
+        store_grad4<ACC_K>(wdq, grad_off(gsk, t, ki), dq);
       }
 
       // ---- dk (rows: key dims of this wave, columns: tokens of sub-block J)
@@ -624,7 +642,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_bwd_f16_kernel(BwdParams p)
         f32x4 rv = mma32(ra[0], ld128(tv + swz<RB>(16 * J + n16, 8 * g)), f32x4{0.f, 0.f, 0.f, 0.f});
         rv = mma32(ra[1], ld128(tv + swz<RB>(16 * J + n16, 32 + 8 * g)), rv);
         const int t = 16 * J + n16;
-        const f32x4 ec = *reinterpret_cast<const f32x4*>(&sEc[t * ES + ki]);
+        const f32x4 ec = ecr[x];
         const f16x4 fe = ld64(&sF[4][J][ki]);
         f32x4 dk;
 #pragma unroll
@@ -654,13 +672,12 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_bwd_f16_kernel(BwdParams p)
         xs[x] = y;
         if (n16 == 0) *reinterpret_cast<f32x4*>(&sTot[(x == 0 ? HF : 3 - HF)][ki]) = y;   // the row's total
       }
-      // q (Qs), v and the states are done with as well: the next chunk's go in
-      // (the barrier also makes the sub-block totals and the carry visible)
+      // q (Qs) and v are done with as well: the next chunk's go in (the
+      // barrier also makes the sub-block totals and the carry visible)
       wait_barrier<kLgkmZero>();
       if (more) {
         load_k_side(pn, p.q, tq);
         load_v_side(pn, p.v, tv);
-        load_states(next, ln);
       }
 
       // dlog_alpha = the in-sub-block suffix sum + the later sub-blocks' totals
