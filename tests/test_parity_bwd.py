@@ -126,8 +126,8 @@ def test_full_size_16k():
 
 
 def test_many_spans_per_summary_workgroup():
-    # 8 x 16 sequences of 64 chunks: 4096 spans of two chunks, so every
-    # workgroup of the summaries kernel streams eight spans (crossing
+    # 8 x 16 sequences of 64 chunks: 8192 spans of one chunk, so every
+    # workgroup of the summaries kernel streams sixteen spans (crossing
     # sequence boundaries) on a 256-CU device; the rotation gives every
     # sequence group its own direction.  A sample of sequences is held to the
     # oracle, and the whole output to finiteness.
@@ -146,3 +146,24 @@ def test_many_spans_per_summary_workgroup():
         ref = gla_backward(q[sl], k[sl], v[sl], la[sl], do[sl], b % 4, d_final_state=dfin[sl],
                            initial_state=init[sl])
         check([x[sl] for x in got], ref, "many spans b %d h %d" % (b, h))
+
+
+def test_uneven_chunks_per_persistent_workgroup():
+    # 2 x 5 sequences of 63 x 65 tokens: 64 chunks each (the last one
+    # ragged), 640 in all, against the chunk kernel's 512 persistent
+    # workgroups on a 256-CU device: the first 128 workgroups take a second
+    # chunk (sequences 8 and 9), the others stop after one, so the refill of
+    # a next chunk is taken on some workgroups and skipped on others
+    B, heads, H, W = 2, 5, 63, 65
+    q, k, v, la = make_inputs(B, heads, H, W, 64, 64, "fp16", 1.0, 390)
+    do, dfin, init = make_bwd_inputs(B, heads, H, W, 64, seed=391)
+    print("bwd uneven persistent", flush=True)
+    got = run(q, k, v, la, do, 4, dfin, init)
+    for x in got:
+        assert np.all(np.isfinite(x))
+    for bh in (0, 4, 8, 9):
+        b, h = divmod(bh, heads)
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        ref = gla_backward(q[sl], k[sl], v[sl], la[sl], do[sl], b % 4, d_final_state=dfin[sl],
+                           initial_state=init[sl])
+        check([x[sl] for x in got], ref, "uneven b %d h %d" % (b, h))
