@@ -345,13 +345,13 @@ __global__ __launch_bounds__(kThreads) void span_summary_kernel(FwdParams p) {
 // span summary (G_s, L_s) into the state entering span s:
 //   E_0 = 0,  E_{s+1} = diag(G_s) E_s + L_s.
 // The combine (G, L) o (G', L') = (G G', diag(G') L + L') is associative, so
-// spans are taken in rounds of kScanSeg segments of kScanU spans, one wave per
+// spans are taken in rounds of kScanSeg segments of U spans, one wave per
 // segment: each lane loads its segment's summaries at once (one memory round
 // trip), folds them from zero, the folds are exchanged through LDS to give
 // every segment its carry-in, and the same registers then yield the entry
-// states.
+// states.  U is 16 when one round of 16 covers the sequence's spans (no lane
+// then loads past them), else 32.
 constexpr int kScanSeg = 4;
-constexpr int kScanU = 32;
 constexpr int kScanElems = kThreads / kScanSeg;   // state elements per workgroup
 
 // One workgroup scans the state elements yb * kScanElems .. of sequence bh
@@ -359,7 +359,7 @@ constexpr int kScanElems = kThreads / kScanSeg;   // state elements per workgrou
 // initial state [BH][DK][DV] or null), in place; with entry16 set, the entry
 // states go there as float16 [BH][n_spans][DK][DV] instead of over the
 // summaries.
-template <int DK, int DV>
+template <int DK, int DV, int U>
 __device__ __forceinline__ void span_scan_body(float* span_state, const float* span_gate,
                                                const float* initial_state, int n_spans, int bh,
                                                int yb, f16* entry16) {
@@ -376,11 +376,11 @@ __device__ __forceinline__ void span_scan_body(float* span_state, const float* s
   // state entering the current round; the first round starts from the
   // initial state, which the scan also writes as span 0's entry state
   float carry = initial_state ? initial_state[(size_t)bh * DK * DV + e] : 0.f;
-  for (int r0 = 0; r0 < n_spans; r0 += kScanSeg * kScanU) {
-    const int s0 = r0 + seg * kScanU;
-    float l[kScanU], gg[kScanU];
+  for (int r0 = 0; r0 < n_spans; r0 += kScanSeg * U) {
+    const int s0 = r0 + seg * U;
+    float l[U], gg[U];
 #pragma unroll
-    for (int u = 0; u < kScanU; ++u) {
+    for (int u = 0; u < U; ++u) {
       // slots past the last span re-read span 0 and are neutralised (no
       // branches around the loads, so all of them are in flight together)
       const bool in = s0 + u < n_spans;
@@ -392,7 +392,7 @@ __device__ __forceinline__ void span_scan_body(float* span_state, const float* s
     }
     float fl = 0.f, fg = 1.f;
 #pragma unroll
-    for (int u = 0; u < kScanU; ++u) {
+    for (int u = 0; u < U; ++u) {
       fl = gg[u] * fl + l[u];
       fg *= gg[u];
     }
@@ -405,7 +405,7 @@ __device__ __forceinline__ void span_scan_body(float* span_state, const float* s
       next = seg_g[j][le] * next + seg_l[j][le];
     }
 #pragma unroll
-    for (int u = 0; u < kScanU; ++u) {
+    for (int u = 0; u < U; ++u) {
       if (s0 + u < n_spans) {
         if (Lh)
           Lh[(size_t)(s0 + u) * DK * DV] = (f16)run;
@@ -419,10 +419,10 @@ __device__ __forceinline__ void span_scan_body(float* span_state, const float* s
   }
 }
 
-template <int DK, int DV, bool E16 = false>
+template <int DK, int DV, bool E16, int U>
 __global__ __launch_bounds__(kThreads) void span_scan_kernel(FwdParams p) {
-  span_scan_body<DK, DV>(p.span_state, p.span_gate, p.initial_state, p.n_spans, blockIdx.x,
-                         blockIdx.y, E16 ? static_cast<f16*>(p.span_entry16) : nullptr);
+  span_scan_body<DK, DV, U>(p.span_state, p.span_gate, p.initial_state, p.n_spans, blockIdx.x,
+                            blockIdx.y, E16 ? static_cast<f16*>(p.span_entry16) : nullptr);
 }
 
 // The backward pass's scans run over float16 chunk summaries (one chunk per
@@ -1613,9 +1613,11 @@ hipError_t launch_variant(const FwdParams& p, hipStream_t stream, hipEvent_t con
   if (p.n_spans > 1) {
     if (kE16 && p.span_entry16 == nullptr) return hipErrorInvalidValue;
     if ((e = launch_one(F::summary, dim3(BH * p.n_spans), stream, p, ev, 0)) != hipSuccess) return e;
-    if ((e = launch_one(span_scan_kernel<DK, DV, kE16>, dim3(BH, DK * DV / kScanElems), stream, p,
-                        ev, 1)) != hipSuccess)
-      return e;
+    const dim3 scan_grid(BH, DK * DV / kScanElems);
+    e = p.n_spans <= kScanSeg * 16
+            ? launch_one(span_scan_kernel<DK, DV, kE16, 16>, scan_grid, stream, p, ev, 1)
+            : launch_one(span_scan_kernel<DK, DV, kE16, 32>, scan_grid, stream, p, ev, 1);
+    if (e != hipSuccess) return e;
   } else {
     if ((e = skip_one(stream, ev, 0)) != hipSuccess) return e;
     if ((e = skip_one(stream, ev, 1)) != hipSuccess) return e;
