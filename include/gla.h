@@ -278,8 +278,8 @@ int gla_plan_spans(int use_f32, int B, int heads, int H, int W, int d_k, int d_v
  * dlog_alpha over the value blocks (each addition of a float16 partial
  * rounds once more), and d_initial_state is the blocks side by side.  The
  * call uses a workspace of B*heads*2*n_chunks*64 floats plus
- * B*heads*2*n_chunks*64*64 float16 chunk states, n_chunks =
- * ceil(H*W/64), reused by the blocks in turn.  Domain: log_alpha finite and <= 0 with the
+ * B*heads*2*n_chunks*64*64 float16 chunk states and 256 bytes (a
+ * work counter), n_chunks = ceil(H*W/64), reused by the blocks in turn.  Domain: log_alpha finite and <= 0 with the
  * decay summed over any 16 consecutive scan steps of one key dim >= -10
  * (natural log: the backward's scaled float16 tiles use factors up to e^10;
  * unlike the forward it has no exact fallback), plus d_out . v, both states

@@ -643,9 +643,11 @@ int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* log_a
     // kernel's operands)
     const size_t slots = (size_t)BH * n_spans;   // of each recurrence
     WsLease ws;
-    if (ws.acquire(st, 2 * slots * (64 * sizeof(float) + map * 2)) != hipSuccess)
-      return GLA_ERR_HIP;
+    // ... and the chunk kernel's ticket counter after them
+    const size_t state_bytes = 2 * slots * (64 * sizeof(float) + map * 2);
+    if (ws.acquire(st, state_bytes + 256) != hipSuccess) return GLA_ERR_HIP;
     float* w = static_cast<float*>(ws.ptr());
+    f.bwd_ticket = reinterpret_cast<unsigned int*>(static_cast<char*>(ws.ptr()) + state_bytes);
     f.span_gate = w;
     f.adj_gate = w + slots * 64;
     f.adj_slots = n_spans;
@@ -671,6 +673,7 @@ int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* log_a
     // the chunk kernel is persistent, two workgroups per CU (74 KB of LDS
     // each)
     pb.n_wg = (int)std::min<long long>(BH * n_chunks, 2LL * cu_count(dev));
+    pb.ticket = f.bwd_ticket;
 
     // with the measurement hook armed, every block's kernels record into the
     // same event pairs, so they end up bracketing the last block's kernels

@@ -150,13 +150,18 @@ __device__ __forceinline__ void store_grad4(rsrc_t dst, uint32_t off, f32x4 x) {
 template <bool ACC_K>
 constexpr int kVmemAfterPrefetch = ACC_K ? 4 : 2;
 
-// Persistent: workgroup w takes the chunks w, w + gridDim.x, .. of the
-// flattened (batch*head, chunk) order, one at a time.  Each input tile is
+// Persistent: workgroup w starts with chunk w of the flattened
+// (batch*head, chunk) order and then takes chunk gridDim.x + t, t a ticket
+// from a counter, until the tickets run past the last chunk.  Two workgroups
+// share a CU, and the one dispatched first issues ahead of the other (older
+// waves win the arbitration); handing chunks out in ticket order lets the
+// faster one take more of them, so both end together instead of the second
+// running alone at half occupancy for the last chunks.  Each input tile is
 // refilled with the next chunk's data as soon as the current chunk is done
-// with it (log-alpha, k and d_out after dq; q, v and both states after dk),
-// so that the loads run under the rest of the chunk's work, and a chunk's
-// stores drain under the next one's.  ACC_V: dv adds to the stored values;
-// ACC_K: dq, dk and dlog-alpha do.
+// with it (log-alpha, k, d_out and both states after dq's products; q and v
+// after dk), so that the loads run under the rest of the chunk's work, and a
+// chunk's stores drain under the next one's.  ACC_V: dv adds to the stored
+// values; ACC_K: dq, dk and dlog-alpha do.
 template <int DK, int DV, bool ACC_V, bool ACC_K>
 __global__ __launch_bounds__(kThreads, 4) void chunk_bwd_f16_kernel(BwdParams p) {
   static_assert(DK == 64 && DV == 64, "built for 64 key and value dims");
@@ -186,6 +191,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_bwd_f16_kernel(BwdParams p)
   __shared__ float sTot[4][DK];
   __shared__ float sBst[DK];      // B at the chunk end (the chunk's log-decay total)
   __shared__ float sCarry[4][DK];
+  __shared__ int sNext;            // the workgroup's next chunk (ticket)
   f16* const tqs = tq;            // q e^{c}
   f16* const tkd = tk;            // k decayed to its sub-block's end
   f16* const tke = tla;           // k decayed to the chunk end
@@ -273,12 +279,23 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_bwd_f16_kernel(BwdParams p)
     load_states(item, lane);
     wait_barrier<vmcnt_lgkm0_imm(0)>();
   }
-  for (int sel = 0; item < total; item += gridDim.x, sel ^= 1) {
-    const int next = item + (int)gridDim.x;
-    const bool more = next < total;
+  for (int sel = 0; item < total; sel ^= 1) {
     // this chunk's inputs landed (what this wave issued after the last of
     // them are the previous chunk's dlog-alpha stores)
     wait_barrier<vmcnt_lgkm0_imm(kVmemAfterPrefetch<ACC_K>)>();
+    // the next chunk: a ticket taken now, read after the decay pass (the
+    // atomic's latency hides under it).  The counter's address goes through
+    // a vector register, so the compiler treats it as per-lane and leaves the
+    // atomic alone instead of combining it over the wave, which would wait
+    // for the result right here.
+    unsigned int ticket = 0;
+    if (threadIdx.x == 0) {
+      // (a global, not a flat, atomic: a flat one would also count against
+      // the LDS waits of the decay pass)
+      auto* ctr = (__attribute__((address_space(1))) unsigned int*)p.ticket;
+      asm volatile("" : "+v"(ctr));
+      ticket = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     // the lane's indices, re-derived each chunk from a value the compiler
     // cannot see through: the many LDS addresses built from them are then
     // formed where they are used instead of held across the loop
@@ -441,8 +458,11 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_bwd_f16_kernel(BwdParams p)
         case 6: factors(std::integral_constant<int, 6>{}); break;
         default: factors(std::integral_constant<int, 7>{}); break;
       }
+      if (threadIdx.x == 0) sNext = (int)gridDim.x + (int)ticket;
     }
     wait_barrier<kLgkmZero>();
+    const int next = __builtin_amdgcn_readfirstlane(sNext);
+    const bool more = next < total;
 
     // The next state: instantiated for each half of the waves, so that their
     // sub-blocks are constants and the loops over sub-block pairs unroll
@@ -703,6 +723,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_bwd_f16_kernel(BwdParams p)
       gradients(std::integral_constant<int, 0>{});
     else
       gradients(std::integral_constant<int, 1>{});
+    item = next;
   }
 }
 

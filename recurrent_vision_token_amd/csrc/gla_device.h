@@ -76,6 +76,24 @@ __host__ __device__ constexpr int vmcnt_lgkm0_imm(int n) {
   return (n & 15) | (7 << 4) | ((n >> 4) << 14);
 }
 
+// Wave priority that falls as the workgroup gets through its work (`done`
+// of `total` units, both uniform): 3 in the first quarter, then 2, 1, 0.
+// The issue arbiter of a SIMD picks the oldest ready wave among those of the
+// highest priority, so workgroups of equal work sharing a CU would otherwise
+// finish in dispatch order, the last one running alone at the end; falling
+// priorities let the ones behind catch up.
+__device__ __forceinline__ void prio_by_progress(int done, int total) {
+  const int level = (4 * done) / total;
+  if (level <= 0)
+    __builtin_amdgcn_s_setprio(3);
+  else if (level == 1)
+    __builtin_amdgcn_s_setprio(2);
+  else if (level == 2)
+    __builtin_amdgcn_s_setprio(1);
+  else
+    __builtin_amdgcn_s_setprio(0);
+}
+
 // LDS-writing load of 16 bytes per lane into a 1 KB block of a tile.
 __device__ __forceinline__ void dma16(rsrc_t src, f16* block, uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void_t*)block, 16, off, 0, 0, 0);

@@ -41,6 +41,7 @@ struct FwdParams {
   float* adj_final;     // the adjoint state after its last slot (the gradient of the state
                         // before the first step), float32 in the initial state's layout, or null
   int spans_per_wg;     // spans streamed by one workgroup of the summaries kernel
+  unsigned int* bwd_ticket;  // the backward chunk kernel's ticket counter, cleared by the scans
   // the backward pass runs on 64 x 64 blocks of a larger head: row strides of
   // the [T][d_k]-side tensors (q, k, log-alpha) and the [T][d_v]-side ones
   // (v, d_out), in elements, and the layout of the caller's [BH][d_k][d_v]
@@ -126,7 +127,8 @@ hipError_t launch_bwd_states(int d_k, int d_v, const FwdParams& p, hipStream_t s
                              hipEvent_t const* events);
 
 // The chunk kernel of the backward pass: n_wg persistent workgroups take the
-// (batch*head, chunk) pairs in turn and turn each chunk's tiles, its forward
+// (batch*head, chunk) pairs (the first n_wg one each, the rest by ticket from
+// p.ticket, which must be zero at launch) and turn each chunk's tiles, its forward
 // entry state and the adjoint state entering it from the right into dq, dk,
 // dv and dlog_alpha.
 struct BwdParams {
@@ -155,6 +157,10 @@ struct BwdParams {
   unsigned int ldk, ldv;
   int acc_dv, acc_dqk;
   int n_wg;                 // persistent workgroups (at most two per CU)
+  // the chunks after each workgroup's first are handed out in ticket
+  // order; the counter is zero when the kernel starts (the state scans
+  // before it clear it)
+  unsigned int* ticket;
 };
 
 hipError_t launch_bwd_chunks(int d_k, int d_v, const BwdParams& p, hipStream_t stream,

@@ -508,6 +508,9 @@ template <int DK, int DV>
 __global__ __launch_bounds__(kThreads) void bwd_state_scans_kernel(FwdParams p) {
   constexpr int kBlocks = DK * DV / kBScanElems;
   const bool adj = (int)blockIdx.y >= kBlocks;
+  // the chunk kernel that follows hands out its chunks from this counter
+  if (p.bwd_ticket != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
+    __hip_atomic_store(p.bwd_ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   bwd_scan_body<DK, DV>(static_cast<f16*>(adj ? p.adj_entry16 : p.span_entry16),
                         adj ? p.adj_gate : p.span_gate, adj ? p.adj_initial : p.initial_state,
                         adj ? p.adj_slots : p.n_spans, blockIdx.x,
@@ -1045,6 +1048,7 @@ __device__ __forceinline__ void output_span(const FwdParams& p, int bh, int span
   // steps alternate between the two buffers; a step's exactness mark is its
   // index + 1 in its buffer's word (0 when the kernel starts)
   auto run_step = [&](const StepTiles<DK, DV>& s, const uint32_t* rows, int step) {
+    prio_by_progress(step, n_steps);
     uint32_t* xf = sxf + (step & 1);
     phase_p(s, valid_rows(step), xf, (uint32_t)step + 1u);
     wait_barrier<kLgkmZero>();
@@ -1365,6 +1369,7 @@ __device__ __forceinline__ void summarize_span(const FwdParams& p, int bh, int s
   issue(slot0, c_end - 1);
   issue(slot1, c_end - 2);
   for (int c = c_end - 1; c >= c_begin; c -= 2) {
+    prio_by_progress(c_end - 1 - c, c_end - c_begin);
     wait_barrier<vmcnt_imm(NDMA)>();  // every wave's part of slot0 has landed
     fold(slot0, c);
     wait_barrier<kLgkmZero>();        // every wave's reads of slot0 are done
