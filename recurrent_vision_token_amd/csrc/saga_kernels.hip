@@ -140,6 +140,7 @@ __global__ __launch_bounds__(kThreads) void saga_kv_partial_kernel(SagaParams p)
   issue(slot0, c_begin);
   issue(slot1, c_begin + 1);
   for (int c = c_begin; c < c_end; c += 2) {
+    prio_by_progress(c - c_begin, c_end - c_begin);
     wait_barrier<vmcnt_imm(NDMA)>();  // every wave's part of slot0 has landed
     fold(slot0);
     wait_barrier<kLgkmZero>();        // every wave's reads of slot0 are done
