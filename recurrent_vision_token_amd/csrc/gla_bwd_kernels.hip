@@ -99,36 +99,49 @@ __device__ __forceinline__ f16x4 tr_read_l(const f16* tile, int row0, int col0, 
   return __builtin_bit_cast(f16x4, x);
 }
 
-// x of the lane whose index differs in bit 4 (xor16) or bit 5 (xor32), by a
-// row swap in the VALU: with both operands x, v_permlane16_swap leaves row
-// q ^ 1's values in its first result for odd rows q and in its second for
-// even rows, v_permlane32_swap rows q ^ 2's in its first result for rows 2, 3
-// and in its second for rows 0, 1.
-__device__ __forceinline__ float xor16(float x, int lane) {
-  const unsigned b = __builtin_bit_cast(unsigned, x);
-  const auto r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
-  return __builtin_bit_cast(float, (lane & 16) ? r[0] : r[1]);
+// Row swaps in the VALU: with both operands x, v_permlane16_swap returns x
+// of this lane's 16-lane row and of its partner row q ^ 1, in .a and .b: the
+// partner's in .a for odd rows (own in .b), in .b for even rows (own in .a).
+// v_permlane32_swap likewise with partner row q ^ 2: the partner's in .a for
+// rows 2, 3, in .b for rows 0, 1.  Sums and products over a row pair use
+// both halves as they come, with no select.
+struct SwapPair {
+  float a, b;
+};
+// (The halves are copied out as values before the bit casts: a bit cast of
+// the vector element r[1] itself was compiled as a read of element 0.)
+__device__ __forceinline__ SwapPair swap16(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const unsigned a = r[0], b = r[1];
+  return {__builtin_bit_cast(float, a), __builtin_bit_cast(float, b)};
 }
-__device__ __forceinline__ float xor32(float x, int lane) {
-  const unsigned b = __builtin_bit_cast(unsigned, x);
-  const auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
-  return __builtin_bit_cast(float, (lane & 32) ? r[0] : r[1]);
+__device__ __forceinline__ SwapPair swap32(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const unsigned a = r[0], b = r[1];
+  return {__builtin_bit_cast(float, a), __builtin_bit_cast(float, b)};
 }
 
 // Over the four 16-lane groups of a wave (group q = lane / 16): the
 // product of x over the groups before this lane's (*before) and after it
 // (*after).
 __device__ __forceinline__ void group_products(float x, int lane, float* before, float* after) {
-  const int q = lane >> 4;
-  const float x1 = xor16(x, lane), x2 = xor32(x, lane), x3 = xor32(x1, lane);
-  // x1, x2, x3: groups q ^ 1, q ^ 2, q ^ 3
-  const float y23 = x2 * x3, y123 = x1 * y23;
-  *before = q == 0 ? 1.f : q == 1 ? x1 : q == 2 ? y23 : y123;
-  *after = q == 0 ? y123 : q == 1 ? y23 : q == 2 ? x1 : 1.f;
+  const bool odd = lane & 16, upper = lane & 32;
+  const SwapPair s = swap16(x);
+  const float bip = odd ? s.a : 1.f;   // group q - 1 of the pair (odd q)
+  const float aip = odd ? 1.f : s.b;   // group q + 1 of the pair (even q)
+  // the other pair's product: in groups 2 and 3, .a is the product over
+  // groups 0 and 1; in groups 0 and 1, .b is that over groups 2 and 3
+  const SwapPair t = swap32(s.a * s.b);
+  *before = upper ? bip * t.a : bip;
+  *after = upper ? aip : aip * t.b;
 }
-__device__ __forceinline__ float group_sum(float x, int lane) {
-  const float y = x + xor16(x, lane);
-  return y + xor32(y, lane);
+// The sum of x over the four 16-lane groups, the same in every lane.
+__device__ __forceinline__ float group_sum(float x) {
+  const SwapPair s = swap16(x);
+  const SwapPair t = swap32(s.a + s.b);
+  return t.a + t.b;
 }
 
 // Four gradient values of one token to float16 at `off` of `dst`; with ACC
@@ -375,8 +388,10 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_bwd_f16_kernel(BwdParams p)
       float pre0, pre1, suf0, suf1;
       group_products(p0, ln, &pre0, &suf0);
       group_products(p1, ln, &pre1, &suf1);
-      tot0 = group_sum(tot0, ln);
-      tot1 = group_sum(tot1, ln);
+      tot0 = group_sum(tot0);
+      tot1 = group_sum(tot1);
+      // (the scaled operands are packed float16 products: the factors, all
+      // <= 1, rounded to float16 first)
       float ec0 = pre0, ec1 = pre1;
       f16x2 qs2[4], kd2[4];
       f32x2 ecs[4];
@@ -387,15 +402,14 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_bwd_f16_kernel(BwdParams p)
         ec1 *= al1[u];
         ecs[u] = f32x2{ec0, ec1};
         const f16x2 q2 = *reinterpret_cast<const f16x2*>(&tq[swz<RB>(t, i)]);
-        qs2[u] = f16x2{(f16)((float)q2[0] * ec0), (f16)((float)q2[1] * ec1)};
+        qs2[u] = q2 * __builtin_convertvector(ecs[u], f16x2);
       }
-      float sfx0 = suf0, sfx1 = suf1, kf0[4], kf1[4];
+      float sfx0 = suf0, sfx1 = suf1;
 #pragma unroll
       for (int u = 3; u >= 0; --u) {
         const f16x2 k2 = *reinterpret_cast<const f16x2*>(&tk[swz<RB>(tb + u, i)]);
-        kf0[u] = (float)k2[0] * sfx0;   // k decayed to the sub-block end
-        kf1[u] = (float)k2[1] * sfx1;
-        kd2[u] = f16x2{(f16)kf0[u], (f16)kf1[u]};
+        // k decayed to the sub-block end
+        kd2[u] = k2 * __builtin_convertvector(f32x2{sfx0, sfx1}, f16x2);
         sfx0 *= al0[u];
         sfx1 *= al1[u];
       }
@@ -428,11 +442,11 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_bwd_f16_kernel(BwdParams p)
           lt1 += t2[1];
         }
       }
-      const float te0 = ex(lt0), te1 = ex(lt1);
+      const f16x2 te2 = __builtin_convertvector(f32x2{ex(lt0), ex(lt1)}, f16x2);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int e = swz<RB>(tb + u, i);
-        *reinterpret_cast<f16x2*>(&tke[e]) = f16x2{(f16)(kf0[u] * te0), (f16)(kf1[u] * te1)};
+        *reinterpret_cast<f16x2*>(&tke[e]) = kd2[u] * te2;
       }
       // factors between sub-block boundaries, thread (key dim, eighth): wave
       // w forms the pairs w, w + 8, .. (pair ab: a = ab / 5, b = ab % 5), each
@@ -489,8 +503,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_bwd_f16_kernel(BwdParams p)
         float part = 0.f;
 #pragma unroll
         for (int u = 0; u < 4; ++u) part += (ebe * (float)e4[u] + acc[u]) * (float)r4[u];
-        part += xor16(part, ln);
-        part += xor32(part, ln);
+        part = group_sum(part);
         if (g == 0) sCarry[vb][i] = part;
       }
     };
