@@ -108,9 +108,12 @@ def kernel_bytes(wl, n_spans, kernels=3):
         entry = bh * n_spans * st_entry if n_spans > 1 else 0
     out = {"chunk_output": th * es * (3 * wl.d_k + 2 * wl.d_v) + bh * st + entry}
     if n_spans > 1:
-        out["span_summary"] = th * es * (2 * wl.d_k + wl.d_v) + bh * n_spans * (st + 4 * wl.d_k)
+        # three passes: summaries in the entry states' precision (float16 on
+        # the float16 path), scanned in place; two passes: float32 summaries
+        st_sum = st_entry if kernels == 3 else st
+        out["span_summary"] = th * es * (2 * wl.d_k + wl.d_v) + bh * n_spans * (st_sum + 4 * wl.d_k)
         if kernels == 3:
-            out["span_scan"] = bh * n_spans * (st + 4 * wl.d_k + st_entry)
+            out["span_scan"] = bh * n_spans * (st_sum + 4 * wl.d_k + st_entry)
     return out
 
 

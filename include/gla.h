@@ -112,8 +112,9 @@ enum {
  * above) is computed exactly, token by token in float32, on every path
  * (strong forgetting: log-alpha of -2 per step, alpha -> 0).  Otherwise the
  * within-step attention scores q_t . k_s e^{b_t - b_s}, the state entries
- * and the outputs must lie in the float16 range (they pass through float16
- * MFMA operands or are stored as float16).
+ * (also a span's summary: the state its tokens alone reach) and the outputs
+ * must lie in the float16 range (they pass through float16 MFMA operands or
+ * are stored as float16).
  */
 int gla_chunk_fwd(const void* q, const void* k, const void* v, const void* log_alpha,
                   int scan_dir, int B, int heads, int H, int W, int d_k, int d_v, int chunk,
@@ -172,8 +173,9 @@ int gla_set_forward_mode(int mode);
  * takes the work split gla_chunk_fwd would take (gla_plan_forward), except
  * that the single-pass mode is not used: its hand-off words would need an
  * allocation, so under that mode the call takes the automatic choice.  The
- * span states take B*heads*n_spans*(d_k*d_v + d_k) floats, plus
- * B*heads*n_spans*d_k*d_v float16 entry states on the three-pass path (the
+ * span states take B*heads*n_spans*d_k floats (gate products) and
+ * B*heads*n_spans*d_k*d_v float16 states on the three-pass path, and
+ * B*heads*n_spans*(d_k*d_v + d_k) floats on the two-pass path (the
  * workspace of gla_plan_forward's split); an automatic split
  * has at most one span per resident output workgroup, which on an MI355X
  * stays within the array for every supported d_k, d_v.  A split that does not
@@ -234,9 +236,12 @@ int gla_chunk_fwd_f32(const float* q, const float* k, const float* v, const floa
  * of ceil(H*W/64) chunks is cut into n_spans spans of span_chunks chunks (the
  * last may be shorter), one output workgroup per (batch, head, span).  When
  * n_spans > 1 the call also runs the span-summary kernel, and the span-scan
- * kernel on the three-pass path, and uses a workspace of
- * B*heads*n_spans*(d_k*d_v + d_k) floats, plus B*heads*n_spans*d_k*d_v
- * float16 entry states on the float16 three-pass path.  gla_plan_forward also gives the
+ * kernel on the three-pass path, and uses a workspace of B*heads*n_spans*d_k
+ * floats (gate products) plus B*heads*n_spans*d_k*d_v float16 span states
+ * (summaries, which the scan turns into entry states in place) on the float16
+ * three-pass path, or B*heads*n_spans*(d_k*d_v + d_k) floats otherwise; a
+ * forced float16 three-pass split whose span states of one sequence reach
+ * 2 GiB returns GLA_ERR_SHAPE.  gla_plan_forward also gives the
  * number of kernels the call runs: 1 (no split), 2 (two-pass path) or 3
  * (three-pass path; see gla_set_forward_mode).  use_f32 selects the float32
  * entry.  Reads device attributes (a HIP call); returns the same argument

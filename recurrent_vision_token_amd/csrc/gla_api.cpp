@@ -358,11 +358,15 @@ int forward(gla::Dtype dt, size_t esize, const void* q, const void* k, const voi
   }
   const int n_spans = (n_chunks + span_chunks - 1) / span_chunks;
   if (BH * n_spans > (1LL << 31) - 1 - gla::kSyncFlags) return GLA_ERR_SHAPE;
-  // span states: summaries (float32) and, on the float16 three-pass path,
-  // the scan's float16 entry states
+  // span states: on the float16 three-pass path float16 summaries, which the
+  // scan turns into the entry states in place, and float32 gate products;
+  // otherwise float32 summaries and gate products
   const bool entry16 = !fused && !two_pass && n_spans > 1 && dt == gla::Dtype::kF16;
-  const size_t span_bytes =
-      (size_t)(d_k * d_v + d_k) * sizeof(float) + (entry16 ? (size_t)d_k * d_v * 2 : 0);
+  const size_t span_bytes = entry16 ? (size_t)d_k * sizeof(float) + (size_t)d_k * d_v * 2
+                                    : (size_t)(d_k * d_v + d_k) * sizeof(float);
+  // the in-place scan addresses one sequence's float16 states with 32-bit
+  // byte offsets (only a forced split of a very long sequence comes near)
+  if (entry16 && (long long)n_spans * d_k * d_v * 2 > (1LL << 31) - 1) return GLA_ERR_SHAPE;
   if (no_alloc && n_spans > 1 && (size_t)(BH * n_spans) * span_bytes > ex.scratch_bytes)
     return GLA_ERR_SCRATCH;
   if (plan_only != nullptr) {
@@ -401,9 +405,13 @@ int forward(gla::Dtype dt, size_t esize, const void* q, const void* k, const voi
     if (n_spans > 1) {
       float* base = static_cast<float*>(ex.scratch_of(dev));
       if (base == nullptr) return GLA_ERR_HIP;
-      p.span_state = base;
-      p.span_gate = base + state_elems;
-      if (entry16) p.span_entry16 = p.span_gate + gate_elems;
+      if (entry16) {
+        p.span_gate = base;
+        p.span_entry16 = base + gate_elems;
+      } else {
+        p.span_state = base;
+        p.span_gate = base + state_elems;
+      }
     }
   } else if (fused) {
     // span summaries (gate product + state) and one hand-off word per span
@@ -415,9 +423,14 @@ int forward(gla::Dtype dt, size_t esize, const void* q, const void* k, const voi
     p.sync = ws.sync();
   } else if (n_spans > 1) {
     if (ws.acquire(st, (size_t)BH * n_spans * span_bytes) != hipSuccess) return GLA_ERR_HIP;
-    p.span_state = static_cast<float*>(ws.ptr());
-    p.span_gate = p.span_state + state_elems;
-    if (entry16) p.span_entry16 = p.span_gate + gate_elems;   // 4-byte aligned, 2-byte elements
+    float* base = static_cast<float*>(ws.ptr());
+    if (entry16) {
+      p.span_gate = base;
+      p.span_entry16 = base + gate_elems;   // 256-byte aligned: the gates are whole 64-float rows
+    } else {
+      p.span_state = base;
+      p.span_gate = base + state_elems;
+    }
   }
   const hipEvent_t* ev = t_events_set ? t_events : nullptr;
   t_events_set = false;

@@ -19,10 +19,12 @@ struct FwdParams {
   float* final_state;   // may be null
   const float* initial_state;  // [B][heads][d_k][d_v], may be null (zero state)
   float inv_tau;        // 1 / tau when `la` holds gate logits (fused activation)
-  float* span_state;    // [BH][n_spans][d_k][d_v] span summaries, then entry states (three
-                        // passes), or summaries in the output kernel's layout (two passes)
+  float* span_state;    // [BH][n_spans][d_k][d_v] span summaries, then entry states (float32
+                        // three passes), or summaries in the output kernel's layout (two
+                        // passes); unused on the float16 three-pass path
   float* span_gate;     // [BH][n_spans][d_k] product of the span's gates
-  void* span_entry16;   // [BH][n_spans][d_k][d_v] float16 entry states (float16 three passes)
+  void* span_entry16;   // [BH][n_spans][d_k][d_v] float16 span summaries, then (in place)
+                        // the entry states (float16 three passes)
   int B, heads, H, W, T;
   // t / W and t / H as (umulhi(t, m) + t) >> s, exact for t < 2^31
   unsigned int div_w_m, div_h_m;

@@ -341,8 +341,9 @@ __global__ __launch_bounds__(kThreads) void span_summary_kernel(FwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 2: scan over spans, elementwise over the d_k x d_v state, turning each
-// span summary (G_s, L_s) into the state entering span s:
+// Kernel 2 (float32 path; the float16 path runs scan16_body below): scan over
+// spans, elementwise over the d_k x d_v state, turning each span summary
+// (G_s, L_s) into the state entering span s:
 //   E_0 = 0,  E_{s+1} = diag(G_s) E_s + L_s.
 // The combine (G, L) o (G', L') = (G G', diag(G') L + L') is associative, so
 // spans are taken in rounds of kScanSeg segments of U spans, one wave per
@@ -356,13 +357,11 @@ constexpr int kScanElems = kThreads / kScanSeg;   // state elements per workgrou
 
 // One workgroup scans the state elements yb * kScanElems .. of sequence bh
 // over n_spans summaries (state [BH][n_spans][DK][DV], gate [BH][n_spans][DK],
-// initial state [BH][DK][DV] or null), in place; with entry16 set, the entry
-// states go there as float16 [BH][n_spans][DK][DV] instead of over the
-// summaries.
+// initial state [BH][DK][DV] or null), in place.
 template <int DK, int DV, int U>
 __device__ __forceinline__ void span_scan_body(float* span_state, const float* span_gate,
                                                const float* initial_state, int n_spans, int bh,
-                                               int yb, f16* entry16) {
+                                               int yb) {
   __shared__ float seg_l[kScanSeg][kScanElems];
   __shared__ float seg_g[kScanSeg][kScanElems];
   const int seg = threadIdx.x / kScanElems;
@@ -370,7 +369,6 @@ __device__ __forceinline__ void span_scan_body(float* span_state, const float* s
   const int e = yb * kScanElems + le;
   const int dim = e / DV;
   float* const L = span_state + (size_t)bh * n_spans * DK * DV + e;
-  f16* const Lh = entry16 ? entry16 + (size_t)bh * n_spans * DK * DV + e : nullptr;
   const float* const G = span_gate + (size_t)bh * n_spans * DK + dim;
 
   // state entering the current round; the first round starts from the
@@ -406,12 +404,7 @@ __device__ __forceinline__ void span_scan_body(float* span_state, const float* s
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (s0 + u < n_spans) {
-        if (Lh)
-          Lh[(size_t)(s0 + u) * DK * DV] = (f16)run;
-        else
-          L[(size_t)(s0 + u) * DK * DV] = run;
-      }
+      if (s0 + u < n_spans) L[(size_t)(s0 + u) * DK * DV] = run;
       run = gg[u] * run + l[u];
     }
     carry = next;
@@ -419,28 +412,29 @@ __device__ __forceinline__ void span_scan_body(float* span_state, const float* s
   }
 }
 
-template <int DK, int DV, bool E16, int U>
+template <int DK, int DV, int U>
 __global__ __launch_bounds__(kThreads) void span_scan_kernel(FwdParams p) {
   span_scan_body<DK, DV, U>(p.span_state, p.span_gate, p.initial_state, p.n_spans, blockIdx.x,
-                            blockIdx.y, E16 ? static_cast<f16*>(p.span_entry16) : nullptr);
+                            blockIdx.y);
 }
 
-// The backward pass's scans run over float16 chunk summaries (one chunk per
-// span), in place: each slot's summary is replaced by the float16 state
-// entering that slot.  The slots of a round are cut into kBScanSeg segments
-// of kBScanU, one row of 16 lanes per segment, each lane taking 4 adjacent
-// elements (a row reads 128 contiguous bytes per slot), so a round spans 256
-// slots; the segments' folds meet through LDS as in span_scan_body.  The
-// caller's float32 states sit at bh * st_bh + i * st_row + j: `init` the
-// state before the first slot (or null: zero), `final_out` (or null) receives
-// the state after the last slot.
+// Scan over float16 summaries, in place: each slot's summary (the state
+// reached from zero over the slot, with its float32 gate product) is replaced
+// by the float16 state entering that slot.  The float16 forward's span scan
+// and both scans of the backward pass (one chunk per slot) run on it.  The
+// slots of a round are cut into kBScanSeg segments of U, one row of 16 lanes
+// per segment, each lane taking 4 adjacent elements (a row reads 128
+// contiguous bytes per slot), so a round spans 16 U slots; the segments'
+// folds meet through LDS as in span_scan_body.  The caller's float32 states
+// sit at bh * st_bh + i * st_row + j: `init` the state before the first slot
+// (or null: zero), `final_out` (or null) receives the state after the last
+// slot.
 constexpr int kBScanSeg = 16;
-constexpr int kBScanU = 16;
 constexpr int kBScanElems = 4 * kThreads / kBScanSeg;  // state elements per workgroup
-template <int DK, int DV>
-__device__ __forceinline__ void bwd_scan_body(f16* sum16, const float* gate, const float* init,
-                                              int n_slots, int bh, int yb, size_t st_bh,
-                                              unsigned int st_row, float* final_out) {
+template <int DK, int DV, int U>
+__device__ __forceinline__ void scan16_body(f16* sum16, const float* gate, const float* init,
+                                            int n_slots, int bh, int yb, size_t st_bh,
+                                            unsigned int st_row, float* final_out) {
   static_assert(DV % 4 == 0 && kBScanElems <= DV, "a workgroup's elements share one state row");
   __shared__ f32x4 seg_l[kBScanSeg][kBScanElems / 4];
   __shared__ float seg_g[kBScanSeg][kBScanElems / 4];
@@ -455,13 +449,16 @@ __device__ __forceinline__ void bwd_scan_body(f16* sum16, const float* gate, con
   const rsrc_t rg = seq_rsrc(gate + (size_t)bh * n_slots * DK, (uint32_t)n_slots * DK * 4);
   const size_t io = (size_t)bh * st_bh + (size_t)dim * st_row + col;
 
-  f32x4 carry = init ? *reinterpret_cast<const f32x4*>(init + io) : f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int r0 = 0; r0 < n_slots; r0 += kBScanSeg * kBScanU) {
-    const int s0 = r0 + seg * kBScanU;
-    f32x4 l[kBScanU];
-    float gg[kBScanU];
+  // (element by element: the forward's initial state need only be 4-byte
+  // aligned)
+  f32x4 carry = init ? f32x4{init[io], init[io + 1], init[io + 2], init[io + 3]}
+                     : f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int r0 = 0; r0 < n_slots; r0 += kBScanSeg * U) {
+    const int s0 = r0 + seg * U;
+    f32x4 l[U];
+    float gg[U];
 #pragma unroll
-    for (int u = 0; u < kBScanU; ++u) {
+    for (int u = 0; u < U; ++u) {
       const uint32_t sl = (uint32_t)(s0 + u);
       const f16x4 lv = __builtin_bit_cast(
           f16x4, __builtin_amdgcn_raw_buffer_load_b64(rl, (sl * DK * DV + e) * 2u, 0, 0));
@@ -473,7 +470,7 @@ __device__ __forceinline__ void bwd_scan_body(f16* sum16, const float* gate, con
     f32x4 fl = f32x4{0.f, 0.f, 0.f, 0.f};
     float fg = 1.f;
 #pragma unroll
-    for (int u = 0; u < kBScanU; ++u) {
+    for (int u = 0; u < U; ++u) {
       fl = gg[u] * fl + l[u];
       fg *= gg[u];
     }
@@ -488,7 +485,7 @@ __device__ __forceinline__ void bwd_scan_body(f16* sum16, const float* gate, con
       next = gj * next + lj;
     }
 #pragma unroll
-    for (int u = 0; u < kBScanU; ++u) {
+    for (int u = 0; u < U; ++u) {
       const uint32_t sl = (uint32_t)(s0 + u);
       __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, to_f16(run)), rl,
                                             (sl * DK * DV + e) * 2u, 0, 0);
@@ -511,11 +508,19 @@ __global__ __launch_bounds__(kThreads) void bwd_state_scans_kernel(FwdParams p) 
   // the chunk kernel that follows hands out its chunks from this counter
   if (p.bwd_ticket != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
     __hip_atomic_store(p.bwd_ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  bwd_scan_body<DK, DV>(static_cast<f16*>(adj ? p.adj_entry16 : p.span_entry16),
-                        adj ? p.adj_gate : p.span_gate, adj ? p.adj_initial : p.initial_state,
-                        adj ? p.adj_slots : p.n_spans, blockIdx.x,
-                        adj ? blockIdx.y - kBlocks : blockIdx.y, p.st_bh, p.st_row,
-                        adj ? p.adj_final : nullptr);
+  scan16_body<DK, DV, 16>(static_cast<f16*>(adj ? p.adj_entry16 : p.span_entry16),
+                          adj ? p.adj_gate : p.span_gate, adj ? p.adj_initial : p.initial_state,
+                          adj ? p.adj_slots : p.n_spans, blockIdx.x,
+                          adj ? blockIdx.y - kBlocks : blockIdx.y, p.st_bh, p.st_row,
+                          adj ? p.adj_final : nullptr);
+}
+
+// The float16 forward's span scan: the summaries in span_entry16 become the
+// entry states, from the initial state ([B*heads][d_k][d_v] float32).
+template <int DK, int DV, int U>
+__global__ __launch_bounds__(kThreads) void span_scan16_kernel(FwdParams p) {
+  scan16_body<DK, DV, U>(static_cast<f16*>(p.span_entry16), p.span_gate, p.initial_state,
+                         p.n_spans, blockIdx.x, blockIdx.y, (size_t)DK * DV, DV, nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -1269,26 +1274,8 @@ __device__ __forceinline__ f16x4 tri_operand(int n16, int g) {
   return m;
 }
 
-// Writes one summary (state rows of the wave's key blocks, gate) to `slot`
-// of the sequence's `slots`.
-template <int DK, int DV>
-__device__ __forceinline__ void store_summary(float* span_state, float* span_gate, int bh,
-                                              size_t slots, size_t slot, int wave, int n16, int g,
-                                              const f32x4 (&st)[DK / 64][DV / 16],
-                                              const f32x4 (&gdec)[DK / 64]) {
-  float* dst = span_state + ((size_t)bh * slots + slot) * DK * DV;
-#pragma unroll
-  for (int d = 0; d < DK / 64; ++d) {
-    const int dim = 16 * (wave + 4 * d) + n16;
-#pragma unroll
-    for (int cb = 0; cb < DV / 16; ++cb)
-      *reinterpret_cast<f32x4*>(dst + dim * DV + 16 * cb + 4 * g) = st[d][cb];
-    if (g == 0)
-      span_gate[((size_t)bh * slots + slot) * DK + dim] = exp2_fast(gdec[d][0] * 1.4426950408889634f);
-  }
-}
-
-// store_summary with the state rounded to float16 (the gate stays float32).
+// Writes one summary to `slot` of the sequence's `slots`: the state rows of
+// the wave's key blocks rounded to float16, the gate product in float32.
 template <int DK, int DV>
 __device__ __forceinline__ void store_summary16(f16* state16, float* span_gate, int bh,
                                                 size_t slots, size_t slot, int wave, int n16, int g,
@@ -1437,8 +1424,8 @@ __global__ __launch_bounds__(kThreads) void span_summary_f16_kernel(FwdParams p)
                                      reinterpret_cast<float*>(wave < 2 ? k0 : la0) + (wave & 1) * 1024,
                                      st, gdec);
   } else
-    store_summary<DK, DV>(p.span_state, p.span_gate, bh, p.n_spans, span, wave, lane & 15,
-                          lane >> 4, st, gdec);
+    store_summary16<DK, DV>(static_cast<f16*>(p.span_entry16), p.span_gate, bh, p.n_spans, span,
+                            wave, lane & 15, lane >> 4, st, gdec);
 }
 
 // The backward pass's two summaries of a span: the forward one (k, v; the
@@ -1618,10 +1605,21 @@ hipError_t launch_variant(const FwdParams& p, hipStream_t stream, hipEvent_t con
   if (p.n_spans > 1) {
     if (kE16 && p.span_entry16 == nullptr) return hipErrorInvalidValue;
     if ((e = launch_one(F::summary, dim3(BH * p.n_spans), stream, p, ev, 0)) != hipSuccess) return e;
-    const dim3 scan_grid(BH, DK * DV / kScanElems);
-    e = p.n_spans <= kScanSeg * 16
-            ? launch_one(span_scan_kernel<DK, DV, kE16, 16>, scan_grid, stream, p, ev, 1)
-            : launch_one(span_scan_kernel<DK, DV, kE16, 32>, scan_grid, stream, p, ev, 1);
+    if constexpr (kE16) {
+      // float16 summaries scanned in place; segments of 4, 8 or 16 spans so
+      // that one round of 16 segments covers the sequence when it can
+      const dim3 scan_grid(BH, DK * DV / kBScanElems);
+      e = p.n_spans <= kBScanSeg * 4
+              ? launch_one(span_scan16_kernel<DK, DV, 4>, scan_grid, stream, p, ev, 1)
+          : p.n_spans <= kBScanSeg * 8
+              ? launch_one(span_scan16_kernel<DK, DV, 8>, scan_grid, stream, p, ev, 1)
+              : launch_one(span_scan16_kernel<DK, DV, 16>, scan_grid, stream, p, ev, 1);
+    } else {
+      const dim3 scan_grid(BH, DK * DV / kScanElems);
+      e = p.n_spans <= kScanSeg * 16
+              ? launch_one(span_scan_kernel<DK, DV, 16>, scan_grid, stream, p, ev, 1)
+              : launch_one(span_scan_kernel<DK, DV, 32>, scan_grid, stream, p, ev, 1);
+    }
     if (e != hipSuccess) return e;
   } else {
     if ((e = skip_one(stream, ev, 0)) != hipSuccess) return e;

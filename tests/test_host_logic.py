@@ -100,19 +100,23 @@ def test_all_cores_oracle_pool_matches_the_oracle():
 
 
 def test_kernel_bytes_of_both_forward_paths():
-    # the two-pass output kernel reads every earlier span's summary (state and
-    # gate); the three-pass one reads one entry state per span
+    # the two-pass output kernel reads every earlier span's summary (float32
+    # state and gate); on the three-pass path the summaries are float16, the
+    # scan turns them into float16 entry states in place, and the output
+    # kernel reads one entry state per span
     import bench
     from recurrent_vision_token_amd.workloads import WORKLOADS
     wl = WORKLOADS["gtr1.6k"]
     bh, st, gate = wl.B * wl.heads, 64 * 64 * 4, 64 * 4
-    st16 = 64 * 64 * 2      # float16 entry states of the three-pass path
+    st16 = 64 * 64 * 2      # float16 summaries and entry states of the three-pass path
+    kv = wl.B * wl.heads * wl.T * 2 * (2 * 64 + 64)       # k, log-alpha, v
     io = wl.B * wl.heads * wl.T * 2 * (3 * 64 + 2 * 64)
     three = bench.kernel_bytes(wl, 13, 3)
     two = bench.kernel_bytes(wl, 13, 2)
     assert three["chunk_output"] == io + bh * st + bh * 13 * st16
-    assert three["span_scan"] == bh * 13 * (st + gate + st16)
+    assert three["span_summary"] == kv + bh * 13 * (st16 + gate)
+    assert three["span_scan"] == bh * 13 * (st16 + gate + st16)
     assert two["chunk_output"] == io + bh * st + bh * (13 * 12 // 2) * (st + gate)
+    assert two["span_summary"] == kv + bh * 13 * (st + gate)
     assert "span_scan" in three and "span_scan" not in two
-    assert two["span_summary"] == three["span_summary"]
     assert bench.kernel_bytes(wl, 1, 1) == {"chunk_output": io + bh * st}

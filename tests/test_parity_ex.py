@@ -64,6 +64,32 @@ def test_initial_state(H, W, d):
     parity_ex(q, k, v, la, d, "log_alpha", rand_state(rng, 1, 3, 64, 64), "init %dx%d" % (H, W))
 
 
+def test_initial_state_4_byte_aligned():
+    # the entry promises 4-byte alignment for the initial state; the
+    # three-pass scan reads it there: a state one float into a buffer
+    torch = _torch()
+    from recurrent_vision_token_amd import _lib, gla_chunk_fwd_ex
+    rng = np.random.default_rng(5)
+    q, k, v, la = make_inputs(1, 3, 40, 40, 64, 64, "fp16", 1.0, seed=17)
+    init = rand_state(rng, 1, 3, 64, 64)
+    dev = torch.device("cuda:0")
+    buf = torch.zeros(1 + init.size, dtype=torch.float32, device=dev)
+    ti = buf[1:].view(init.shape)
+    ti.copy_(torch.from_numpy(init).to(dev))
+    assert ti.data_ptr() % 16 == 4
+    tq, tk, tv, tg = (torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in (q, k, v, la))
+    try:
+        _lib.set_forward_mode("three_pass")
+        assert _lib.plan_forward("fp16", 1, 3, 40, 40, 64, 64)[2] == 3
+        out, fs = gla_chunk_fwd_ex(tq, tk, tv, tg, 1, gate_mode="log_alpha", tau=TAU, initial_state=ti)
+        torch.cuda.synchronize()
+    finally:
+        _lib.set_forward_mode("auto")
+    ro, rs = gla_forward(q, k, v, la, 1, initial_state=init)
+    check(out.float().cpu().numpy().astype(np.float64), ro, True, "4-byte aligned init out")
+    check(fs.cpu().numpy().astype(np.float64), rs, True, "4-byte aligned init final_state")
+
+
 @pytest.mark.parametrize("d", [0, 1, 2, 3])
 @pytest.mark.parametrize("H,W", [(1, 1), (7, 9), (37, 53), (129, 7)])
 def test_fused_gate(H, W, d):

@@ -58,10 +58,11 @@ def _both(B, heads, H, W, scan_dir, seed, d_k=64, d_v=64, exact=True):
 
 
 def _uses_scratch(B, heads, H, W, d_k=64, d_v=64):
-    # span summaries in float32, and on the three-pass path the float16 entry states
+    # float32 gate products with float16 span states on the three-pass path,
+    # float32 summaries and gate products on the two-pass path
     from recurrent_vision_token_amd import _lib
     _, n_spans, kernels = _lib.plan_forward("fp16", B, heads, H, W, d_k, d_v)
-    per_span = (d_k * d_v + d_k) * 4 + (d_k * d_v * 2 if kernels == 3 else 0)
+    per_span = d_k * 4 + d_k * d_v * 2 if kernels == 3 else (d_k * d_v + d_k) * 4
     return n_spans > 1, B * heads * n_spans * per_span
 
 
