@@ -1440,9 +1440,12 @@ __global__ __launch_bounds__(kThreads) void span_summary_f16_kernel(FwdParams p)
 // (batch*head, span) order) and streams their chunks through two tile
 // buffers, so that the loads of one chunk overlap the folds of the previous
 // one; a span's summaries are stored when its first chunk (folded last) is
-// done.
+// done.  Eight waves: four fold the forward summary and four the adjoint one
+// from the same tiles, so a SIMD has two waves to switch between even at one
+// workgroup per CU.
+constexpr int kSumThreads = 512;  // 8 waves: 4 fold the forward summary, 4 the adjoint
 template <int DK, int DV>
-__global__ __launch_bounds__(kThreads) void bwd_state_summaries_kernel(FwdParams p) {
+__global__ __launch_bounds__(kSumThreads) void bwd_state_summaries_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(16))) f16 k0[kChunk * DK], la0[kChunk * DK], v0[kChunk * DV];
   __shared__ __attribute__((aligned(16))) f16 q0[kChunk * DK], do0[kChunk * DV];
   __shared__ __attribute__((aligned(16))) f16 k1[kChunk * DK], la1[kChunk * DK], v1[kChunk * DV];
@@ -1452,11 +1455,13 @@ __global__ __launch_bounds__(kThreads) void bwd_state_summaries_kernel(FwdParams
   constexpr int NDB = DK / 64, NCB = DV / 16;
   constexpr int RBK = 2 * DK, RBV = 2 * DV;
   static_assert(RBK == 128 && RBV == 128, "built for 64 key and value dims");
-  constexpr int NBK = RBK / 64;       // 1 KB blocks per wave and tile
-  constexpr int NDMA = 5 * NBK;       // LDS-writing loads per wave and chunk (k, la, v, q, d_out)
+  constexpr int NDMA = 5;  // LDS-writing loads per wave and chunk: one 1 KB block of each tile
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n16 = lane & 15, g = lane >> 4;
+  // waves 0..3 fold the forward summary, 4..7 the adjoint one, each over key
+  // block wq; all eight load the tiles
+  const int fam = wave >> 2, wq = wave & 3;
 
   const int sc = p.span_chunks;
   const long long total = (long long)p.B * p.heads * p.n_spans;
@@ -1494,32 +1499,25 @@ __global__ __launch_bounds__(kThreads) void bwd_state_summaries_kernel(FwdParams
     const rsrc_t rdo = seq_rsrc(static_cast<const h*>(p.dout) + ov, vbytes);
     const int t0 = it.c * kChunk;
     const int valid = live ? min(kChunk, p.T - t0) : 0;
-#pragma unroll
-    for (int j = 0; j < NBK; ++j) {
-      const int blk = wave * NBK + j;
-      const uint32_t offk = dma_offset_s<RBK>(blk, t0, valid, gm, p.ldk * 2u);
-      const uint32_t offv = dma_offset_s<RBV>(blk, t0, valid, gm, p.ldv * 2u);
-      dma16(rk, f.k + blk * 512, offk);
-      dma16(rla, f.la + blk * 512, offk);
-      dma16(rv, f.v + blk * 512, offv);
-      dma16(rq, a.k + blk * 512, offk);
-      dma16(rdo, a.v + blk * 512, offv);
-    }
+    const int blk = wave;
+    const uint32_t offk = dma_offset_s<RBK>(blk, t0, valid, gm, p.ldk * 2u);
+    const uint32_t offv = dma_offset_s<RBV>(blk, t0, valid, gm, p.ldv * 2u);
+    dma16(rk, f.k + blk * 512, offk);
+    dma16(rla, f.la + blk * 512, offk);
+    dma16(rv, f.v + blk * 512, offv);
+    dma16(rq, a.k + blk * 512, offk);
+    dma16(rdo, a.v + blk * 512, offv);
   };
 
-  const f16x4 m_upper = tri_operand<false>(n16, g), m_lower = tri_operand<true>(n16, g);
+  const f16x4 m_tri = fam == 0 ? tri_operand<false>(n16, g) : tri_operand<true>(n16, g);
   const f16x4 m_ones = f16x4{(f16)1.f, (f16)1.f, (f16)1.f, (f16)1.f};
-  f32x4 st[NDB][NCB], gdec[NDB], sa[NDB][NCB], gadj[NDB];
+  f32x4 st[NDB][NCB], gdec[NDB];   // this wave's summary (forward or adjoint)
   auto reset = [&]() {
 #pragma unroll
     for (int d = 0; d < NDB; ++d) {
       gdec[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-      gadj[d] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        st[d][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        sa[d][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+      for (int cb = 0; cb < NCB; ++cb) st[d][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   };
   reset();
@@ -1530,14 +1528,18 @@ __global__ __launch_bounds__(kThreads) void bwd_state_summaries_kernel(FwdParams
     const Item it = item(i);
     if (it.live) {
       const int valid = min(kChunk, p.T - it.c * kChunk);
-      fold_chunk<DK, DV, false, false>(f, valid, 1.f, m_upper, m_ones, wave, st, gdec);
-      fold_chunk<DK, DV, false, true>(a, valid, 1.f, m_lower, m_ones, wave, sa, gadj);
+      if (fam == 0)
+        fold_chunk<DK, DV, false, false>(f, valid, 1.f, m_tri, m_ones, wq, st, gdec);
+      else
+        fold_chunk<DK, DV, false, true>(a, valid, 1.f, m_tri, m_ones, wq, st, gdec);
     }
     if (i % sc == sc - 1) {
-      store_summary16<DK, DV>(static_cast<f16*>(p.span_entry16), p.span_gate, it.bh, p.n_spans,
-                              it.span, wave, n16, g, st, gdec);
-      store_summary16<DK, DV>(static_cast<f16*>(p.adj_entry16), p.adj_gate, it.bh, slots,
-                              slots - 1 - it.span, wave, n16, g, sa, gadj);
+      if (fam == 0)
+        store_summary16<DK, DV>(static_cast<f16*>(p.span_entry16), p.span_gate, it.bh, p.n_spans,
+                                it.span, wq, n16, g, st, gdec);
+      else
+        store_summary16<DK, DV>(static_cast<f16*>(p.adj_entry16), p.adj_gate, it.bh, slots,
+                                slots - 1 - it.span, wq, n16, g, st, gdec);
       reset();
     }
   };
@@ -1730,11 +1732,11 @@ namespace {
 // be null), so one event pair can bracket several kernels.
 template <class K>
 hipError_t launch_marked(K kernel, dim3 grid, hipStream_t stream, const FwdParams& p,
-                         hipEvent_t start, hipEvent_t stop) {
+                         hipEvent_t start, hipEvent_t stop, int threads = kThreads) {
   if (start != nullptr || stop != nullptr) {
-    hipExtLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, start, stop, 0, p);
+    hipExtLaunchKernelGGL(kernel, grid, dim3(threads), 0, stream, start, stop, 0, p);
   } else {
-    hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(kernel, grid, dim3(threads), 0, stream, p);
   }
   return hipGetLastError();
 }
@@ -1749,7 +1751,7 @@ hipError_t launch_bwd_states_variant(const FwdParams& p, hipStream_t stream, hip
   const long long total = (long long)BH * p.n_spans;
   const dim3 sum_grid((unsigned)((total + p.spans_per_wg - 1) / p.spans_per_wg));
   if ((e = launch_marked(bwd_state_summaries_kernel<DK, DV>, sum_grid, stream, p,
-                         ev ? ev[0] : nullptr, ev ? ev[1] : nullptr)) != hipSuccess)
+                         ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, kSumThreads)) != hipSuccess)
     return e;
   return launch_marked(bwd_state_scans_kernel<DK, DV>, dim3(BH, 2 * DK * DV / kBScanElems), stream,
                        p, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr);
