@@ -772,6 +772,12 @@ __global__ __launch_bounds__(kThreads) void chunk_output_kernel(FwdParams p) {
 // 8g+4..8g+7 the same tokens of sub-block 1, which is what two transposed
 // 16x16 reads (or two 16x16 accumulator tiles) deliver.
 constexpr int kStep = 32;
+// Cache policies of the output kernel's tile loads and output stores: both
+// non-temporal.  The loads are the inputs' last use in the call; the outputs
+// leave in whole 128-byte rows during the kernel, instead of lingering as
+// dirty lines that drain while the next kernel streams its own inputs.
+constexpr int kOutLoadAux = kAuxNT;
+constexpr int kOutStoreAux = kAuxNT;
 // log2 of the largest key factor exp(-c) the fast step path forms
 constexpr float kKeyFactorLog2 = 10.f;
 typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
@@ -831,13 +837,11 @@ template <int DK, int DV, bool GATE, class Entry>
 __device__ __forceinline__ void output_span(const FwdParams& p, int bh, int span,
                                             const StepTiles<DK, DV>& slot0,
                                             const StepTiles<DK, DV>& slot1, f16* sqt, float* sgd,
-                                            uint32_t (*srow)[kStep], uint32_t* sxf,
+                                            uint32_t* sxf,
                                             f32x4 (&st)[DK / 16][DV / 64], Entry&& entry) {
   constexpr int RBK = 2 * DK, RBV = 2 * DV;
   constexpr int NR = DK / 16, NC = DV / 64, NRHO = DK / 32;
   constexpr int NBK = RBK / 128, NBV = RBV / 128;  // 1 KB blocks per wave and tile of one step
-  constexpr int NSTORE = 2 * NC;                    // output stores per wave and step
-  static_assert(NSTORE < 64, "vmcnt range");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n16 = lane & 15, g = lane >> 4;
@@ -849,28 +853,45 @@ __device__ __forceinline__ void output_span(const FwdParams& p, int bh, int span
   const int t_end = min(t_begin + p.span_chunks * kChunk, p.T);
   const int n_steps = (t_end - t_begin + kStep - 1) / kStep;
 
-  auto issue = [&](const StepTiles<DK, DV>& s, uint32_t* rows, int step) {
+  auto issue = [&](const StepTiles<DK, DV>& s, int step) {
     const int t0 = t_begin + kStep * step;
     const int valid = max(0, min(kStep, t_end - t0));
 #pragma unroll
     for (int i = 0; i < NBK; ++i) {
       const int blk = wave * NBK + i;
-      uint32_t cf;
-      bool first;
-      const uint32_t off = dma_offset_cell<RBK>(blk, t0, valid, gm, &cf, &first);
-      if (first) rows[(blk * 1024 + 16 * lane) / RBK] = cf;
-      dma16(sb.q, s.q + blk * 512, off);
-      dma16(sb.k, s.k + blk * 512, off);
-      dma16(sb.la, s.la + blk * 512, off);
-      if (RBV == RBK) dma16(sb.v, s.v + blk * 512, off);
+      const uint32_t off = dma_offset<RBK>(blk, t0, valid, gm);
+      dma16p<kOutLoadAux>(sb.q, s.q + blk * 512, off);
+      dma16p<kOutLoadAux>(sb.k, s.k + blk * 512, off);
+      dma16p<kOutLoadAux>(sb.la, s.la + blk * 512, off);
+      if (RBV == RBK) dma16p<kOutLoadAux>(sb.v, s.v + blk * 512, off);
     }
     if (RBV != RBK) {
 #pragma unroll
       for (int i = 0; i < NBV; ++i) {
         const int blk = wave * NBV + i;
-        dma16(sb.v, s.v + blk * 512, dma_offset<RBV>(blk, t0, valid, gm));
+        dma16p<kOutLoadAux>(sb.v, s.v + blk * 512, dma_offset<RBV>(blk, t0, valid, gm));
       }
     }
+  };
+  // The outputs of step `step`, staged in place of its v tile (same swizzle),
+  // out to their grid cells: each lane writes the 16 bytes at its own
+  // position of the tile, i.e. the piece the swizzle put there, so 8 lanes
+  // write one whole output row.  Rows past the span are dropped by the
+  // buffer range check.  Returns once the tile has been read, so that the
+  // buffer can take the next loads.
+  auto flush = [&](const StepTiles<DK, DV>& s, int step) {
+    const int t0 = t_begin + kStep * step;
+    const int valid = max(0, min(kStep, t_end - t0));
+#pragma unroll
+    for (int i = 0; i < NBV; ++i) {
+      const int blk = wave * NBV + i;
+      const f16x8 x = ld128(s.v + blk * 512 + 8 * lane);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), sb.out,
+                                             dma_offset<RBV>(blk, t0, valid, gm), 0, kOutStoreAux);
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kLgkmZero);
+    asm volatile("" ::: "memory");
   };
 
   const f16x4 u_hi = upper_incl(kLog2eHi), u_lo = upper_incl(kLog2eLo);
@@ -932,7 +953,7 @@ __device__ __forceinline__ void output_span(const FwdParams& p, int bh, int span
   // ---- exact step: the recurrence token by token in float32, on this
   // wave's state columns, from the raw q, k and log-alpha (loaded again: the
   // P phase overwrote them; v is untouched)
-  auto phase_x = [&](const StepTiles<DK, DV>& s, const uint32_t* rows, int step) {
+  auto phase_x = [&](const StepTiles<DK, DV>& s, int step) {
     const int t0 = t_begin + kStep * step;
     const int valid = max(0, min(kStep, t_end - t0));
 #pragma unroll
@@ -967,24 +988,19 @@ __device__ __forceinline__ void output_span(const FwdParams& p, int bh, int span
           }
         }
       }
-      const uint32_t orow_t = (rows[t] & 0x7fffffffu) * RBV;
 #pragma unroll
       for (int j = 0; j < NC; ++j) {
         float o = part[j] + __shfl_xor(part[j], 16);
         o += __shfl_xor(o, 32);
-        if (g == 0)
-          __builtin_amdgcn_raw_buffer_store_b16(
-              __builtin_bit_cast(unsigned short, (f16)o), sb.out,
-              orow_t + (uint32_t)((16 * (wave + 4 * j) + n16) * 2), 0, 0);
+        if (g == 0) s.v[swz<RBV>(t, 16 * (wave + 4 * j) + n16)] = (f16)o;
       }
     }
   };
 
   // ---- O: scores, outputs, state update
-  auto phase_o = [&](const StepTiles<DK, DV>& s, const uint32_t* rows, const uint32_t* xf,
-                     uint32_t tag, int step) {
+  auto phase_o = [&](const StepTiles<DK, DV>& s, const uint32_t* xf, uint32_t tag, int step) {
     if (__builtin_amdgcn_readfirstlane(*xf) == tag) {
-      phase_x(s, rows, step);
+      phase_x(s, step);
       return;
     }
     // A^T tiles: lane (t, g) holds A[t][s = 4g + u] of the tile
@@ -1015,12 +1031,6 @@ __device__ __forceinline__ void output_span(const FwdParams& p, int bh, int span
     f16x8 sbt[2];
     sbt[0] = cat8(to_f16(d00), z4);
     sbt[1] = cat8(to_f16(d01), to_f16(d11));
-    uint32_t orow[2];
-#pragma unroll
-    for (int T = 0; T < 2; ++T) {
-      const uint32_t cf = rows[16 * T + n16];
-      orow[T] = (cf & 0x7fffffffu) * RBV | (cf & 0x80000000u);
-    }
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
       const int col0 = 16 * (wave + 4 * j);
@@ -1035,9 +1045,7 @@ __device__ __forceinline__ void output_span(const FwdParams& p, int bh, int span
 #pragma unroll
         for (int rho = 0; rho < NRHO; ++rho)
           acc = mma32(sh[rho], ld128(sqt + swz<RBK>(row, 32 * rho + 8 * g)), acc);
-        const f16x4 o = to_f16(acc);
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o), sb.out,
-                                              orow[T] + (uint32_t)((col0 + 4 * g) * 2), 0, 0);
+        st64(s.v + swz<RBV>(row, col0 + 4 * g), to_f16(acc));
       }
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
@@ -1052,27 +1060,37 @@ __device__ __forceinline__ void output_span(const FwdParams& p, int bh, int span
   auto valid_rows = [&](int step) { return max(0, min(kStep, t_end - t_begin - kStep * step)); };
   // steps alternate between the two buffers; a step's exactness mark is its
   // index + 1 in its buffer's word (0 when the kernel starts)
-  auto run_step = [&](const StepTiles<DK, DV>& s, const uint32_t* rows, int step) {
+  // A step's outputs replace its v tile (each wave's value columns of v are
+  // in its registers by then, and no other wave reads them); they go out
+  // after the barrier that ends the step, before the buffer is refilled.
+  auto run_step = [&](const StepTiles<DK, DV>& s, int step) {
     prio_by_progress(step, n_steps);
     uint32_t* xf = sxf + (step & 1);
     phase_p(s, valid_rows(step), xf, (uint32_t)step + 1u);
     wait_barrier<kLgkmZero>();
-    phase_o(s, rows, xf, (uint32_t)step + 1u, step);
+    phase_o(s, xf, (uint32_t)step + 1u, step);
   };
-  // Before step s the loads in flight are step s and the stores of s - 1.
-  issue(slot0, srow[0], 0);
+  // Before step s the vector-memory operations in flight are the output
+  // stores of step s - 2 and then the loads of step s; after it, those of
+  // step s + 1 are the youngest, so the wait for them takes all.
+  issue(slot0, 0);
   entry(st);                     // completes the entry state while step 0 loads
   wait_barrier<vmcnt_imm(0)>();  // the entry state and step 0 have landed
   for (int step = 0; step < n_steps; step += 2) {
-    issue(slot1, srow[1], step + 1);
-    run_step(slot0, srow[0], step);
+    issue(slot1, step + 1);
+    run_step(slot0, step);
     if (step + 1 >= n_steps) break;
-    wait_barrier<vmcnt_lgkm0_imm(NSTORE)>();  // step + 1 landed; slot0 free
-    issue(slot0, srow[0], step + 2);
-    run_step(slot1, srow[1], step + 1);
+    wait_barrier<vmcnt_lgkm0_imm(0)>();  // step + 1 landed; step's outputs staged
+    flush(slot0, step);
+    issue(slot0, step + 2);
+    run_step(slot1, step + 1);
     if (step + 2 >= n_steps) break;
-    wait_barrier<vmcnt_lgkm0_imm(NSTORE)>();
+    wait_barrier<vmcnt_lgkm0_imm(0)>();
+    flush(slot1, step + 1);
   }
+  // the last step's outputs, staged by every wave
+  wait_barrier<kLgkmZero>();
+  flush((n_steps - 1) & 1 ? slot1 : slot0, n_steps - 1);
   // loads past the span's end (zero fills) must land before the workgroup's
   // LDS can be handed on
   asm volatile("" ::: "memory");
@@ -1114,8 +1132,6 @@ __global__ __launch_bounds__(kThreads, LOOKBACK ? 2 : (DK == 64 && DV == 64) ? 4
   // q decayed from the step start, columns in token-slot order (see qt_slot)
   __shared__ __attribute__((aligned(16))) f16 sqt[kStep * DK];
   __shared__ __attribute__((aligned(16))) float sgd[DK];  // exp(decay over the step)
-  // grid cell of each step row (bit 31: past the span), per step buffer
-  __shared__ uint32_t srow[2][kStep];
   // exactness mark of the step in each buffer (see output_span)
   __shared__ uint32_t sxf[2];
   if (threadIdx.x < 2) sxf[threadIdx.x] = 0u;
@@ -1137,7 +1153,7 @@ __global__ __launch_bounds__(kThreads, LOOKBACK ? 2 : (DK == 64 && DV == 64) ? 4
     else
       load_state_tiles<DK, DV>(p.initial_state ? p.initial_state + (size_t)bh * DK * DV : nullptr,
                                wave, lane & 15, lane >> 4, st);
-    output_span<DK, DV, GATE>(p, bh, span, slot0, slot1, sqt, sgd, srow, sxf, st, [](auto&) {});
+    output_span<DK, DV, GATE>(p, bh, span, slot0, slot1, sqt, sgd, sxf, st, [](auto&) {});
   } else {
     const int g = lane >> 4;
     load_state_tiles<DK, DV>(p.initial_state ? p.initial_state + (size_t)bh * DK * DV : nullptr,
@@ -1165,7 +1181,7 @@ __global__ __launch_bounds__(kThreads, LOOKBACK ? 2 : (DK == 64 && DV == 64) ? 4
             for (int r = 0; r < DK / 16; ++r) s[r][0] = gv[i][r] * s[r][0] + av[i][r];
       }
     };
-    output_span<DK, DV, GATE>(p, bh, span, slot0, slot1, sqt, sgd, srow, sxf, st, fold_earlier);
+    output_span<DK, DV, GATE>(p, bh, span, slot0, slot1, sqt, sgd, sxf, st, fold_earlier);
   }
 }
 
