@@ -117,6 +117,20 @@ def kernel_bytes(wl, n_spans, kernels=3):
     return out
 
 
+_HOST_INPUTS = {}
+
+
+def host_inputs(wl, seed):
+    """A workload's seeded host inputs, generated once per (workload, seed): the
+    batched configuration's 2 GB take tens of seconds to draw, and its forward
+    and backward lines share them."""
+    from recurrent_vision_token_amd.workloads import workload_inputs
+    key = (wl.name, seed)
+    if key not in _HOST_INPUTS:
+        _HOST_INPUTS[key] = tuple(workload_inputs(wl, seed))
+    return _HOST_INPUTS[key]
+
+
 class Runner:
     """Device copies of a workload's inputs, cycled across calls.
 
@@ -125,7 +139,6 @@ class Runner:
     stored initial state."""
 
     def __init__(self, wl, torch, min_sets_bytes=2 * LLC_BYTES, ext=False):
-        from recurrent_vision_token_amd.workloads import workload_inputs
         self.torch = torch
         self.wl = wl
         self.dev = torch.device("cuda:0")
@@ -133,7 +146,7 @@ class Runner:
         host = {}
         for seed, _ in calls:
             if seed not in host:
-                host[seed] = workload_inputs(wl, seed)
+                host[seed] = host_inputs(wl, seed)
         self.host = host
         per_call = algorithmic(wl)["bytes"]
         reps = max(1, math.ceil(min_sets_bytes / (per_call * len(calls))))
@@ -394,14 +407,14 @@ class BwdRunner:
 
     def __init__(self, wl, torch, min_sets_bytes=2 * LLC_BYTES):
         from recurrent_vision_token_amd import _lib
-        from recurrent_vision_token_amd.workloads import make_bwd_inputs, workload_inputs
+        from recurrent_vision_token_amd.workloads import make_bwd_inputs
         self.wl = wl
         dev = torch.device("cuda:0")
         self.host = {}
         for seed, _ in wl.calls:
             if seed not in self.host:
-                self.host[seed] = workload_inputs(wl, seed) + make_bwd_inputs(
-                    wl.B, wl.heads, wl.H, wl.W, wl.d_v, wl.d_k, seed=seed + 1000)
+                self.host[seed] = list(host_inputs(wl, seed)) + list(make_bwd_inputs(
+                    wl.B, wl.heads, wl.H, wl.W, wl.d_v, wl.d_k, seed=seed + 1000))
         per_call = bwd_bytes(wl)["call"]
         reps = max(1, math.ceil(min_sets_bytes / (per_call * len(wl.calls))))
         self.sets = []
@@ -497,10 +510,16 @@ def bwd_cpu_baseline(wl, host):
 
 def bwd_summary(wl, ms_step, k_ms, cpu):
     nb = bwd_bytes(wl)
-    # the call's method bytes over the dominant kernel's launch; its own bytes
-    # (state reads included) separately
-    ach = nb["call"] / (k_ms["chunk_bwd"] * 1e-3) / 1e9
-    own = nb["chunk_bwd"] / (k_ms["chunk_bwd"] * 1e-3) / 1e9
+    # A wider head runs as a grid of 64 x 64 blocks, each with the three
+    # kernels, in order on the stream; the kernel events then bracket the
+    # last block's kernels, and the call's chunk kernels take `blocks` times
+    # that (the last block also adds its partial gradients to the earlier
+    # ones', so this slightly overstates them).
+    blocks = (wl.d_k // 64) * (wl.d_v // 64)
+    # the call's method bytes over the dominant kernel's launches; its own
+    # bytes (state reads included; one block only) separately
+    ach = nb["call"] / (blocks * k_ms["chunk_bwd"] * 1e-3) / 1e9
+    own = nb["chunk_bwd"] / (k_ms["chunk_bwd"] * 1e-3) / 1e9 if blocks == 1 else None
     wall_call_ms = ms_step / len(wl.calls)
     path = nb["call"] / (wall_call_ms * 1e-3) / 1e9
     tokens = len(wl.calls) * wl.B * wl.T
@@ -514,15 +533,18 @@ def bwd_summary(wl, ms_step, k_ms, cpu):
                      "frac": round(ach / HBM_PEAK_GBPS, 4),
                      "traffic": traffic_from_profiles(wl.name, "chunk_bwd"),
                      "traffic_counts": TRAFFIC_NOTE,
-                     "kernel": "chunk_bwd", "algorithmic_bytes_per_launch": nb["call"],
+                     "kernel": "chunk_bwd" if blocks == 1 else
+                               "chunk_bwd (%d launches per call, one per 64 x 64 block)" % blocks,
+                     "algorithmic_bytes_per_launch": nb["call"] // blocks,
                      "avg_launch_us": round(k_ms["chunk_bwd"] * 1e3, 2),
-                     "kernel_bytes_per_launch": nb["chunk_bwd"],
-                     "dominant_kernel_frac": round(own / HBM_PEAK_GBPS, 4)},
+                     "kernel_bytes_per_launch": nb["chunk_bwd"] if blocks == 1 else None,
+                     "dominant_kernel_frac": round(own / HBM_PEAK_GBPS, 4) if own else None},
         "path": {"wall_us_per_call": round(wall_call_ms * 1e3, 2),
                  "event_us_per_call": round(k_ms["call"] * 1e3, 2),
                  "algorithmic_bytes_per_call": nb["call"],
                  "achieved_GBps": round(path, 1), "hbm_frac": round(path / HBM_PEAK_GBPS, 4),
-                 "kernel_us": {k: round(v * 1e3, 2) for k, v in k_ms.items() if k != "call"}},
+                 "kernel_us": {k: round(v * 1e3, 2) for k, v in k_ms.items() if k != "call"},
+                 "kernel_us_of": "the call" if blocks == 1 else "its last 64 x 64 block"},
         "cpu_baseline": cpu,
     }
 
@@ -1063,6 +1085,16 @@ def main():
             (wl.name, ms_b, bwd["value"], bwd["path"]["kernel_us"]))
         del brun
 
+    # the backward pass on the batched configuration (d_k = 128: two key blocks)
+    bwd_batched = None
+    if args.batched and not args.no_bwd:
+        wl5 = WORKLOADS["batched"]
+        brun, ms_b, k_b = time_bwd(wl5, torch, 10, 3)
+        bwd_batched = bwd_summary(wl5, ms_b, k_b, None)
+        log("[bench] %s backward: %.3f ms/call, %.3e tokens/s, kernels of its last block %s" %
+            (wl5.name, ms_b, bwd_batched["value"], bwd_batched["path"]["kernel_us"]))
+        del brun
+
     swiglu = None
     if args.swiglu:
         from recurrent_vision_token_amd.workloads import SWIGLU_WORKLOADS
@@ -1129,6 +1161,7 @@ def main():
         "time_vs_tokens": sweep,
         "fused_gate_initial_state": ext,
         "backward": bwd,
+        "backward_batched": bwd_batched,
         "spatial_swiglu": swiglu,
         "saga": saga,
     }

@@ -501,14 +501,14 @@ __device__ __forceinline__ void scan16_body(f16* sum16, const float* gate, const
 // scans the forward summaries (from the initial state), the rest the adjoint
 // summaries (from the final-state gradient; the state after its last slot is
 // the gradient of the state before the first step).
-template <int DK, int DV>
+template <int DK, int DV, int U>
 __global__ __launch_bounds__(kThreads) void bwd_state_scans_kernel(FwdParams p) {
   constexpr int kBlocks = DK * DV / kBScanElems;
   const bool adj = (int)blockIdx.y >= kBlocks;
   // the chunk kernel that follows hands out its chunks from this counter
   if (p.bwd_ticket != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
     __hip_atomic_store(p.bwd_ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  scan16_body<DK, DV, 16>(static_cast<f16*>(adj ? p.adj_entry16 : p.span_entry16),
+  scan16_body<DK, DV, U>(static_cast<f16*>(adj ? p.adj_entry16 : p.span_entry16),
                           adj ? p.adj_gate : p.span_gate, adj ? p.adj_initial : p.initial_state,
                           adj ? p.adj_slots : p.n_spans, blockIdx.x,
                           adj ? blockIdx.y - kBlocks : blockIdx.y, p.st_bh, p.st_row,
@@ -1769,8 +1769,14 @@ hipError_t launch_bwd_states_variant(const FwdParams& p, hipStream_t stream, hip
   if ((e = launch_marked(bwd_state_summaries_kernel<DK, DV>, sum_grid, stream, p,
                          ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, kSumThreads)) != hipSuccess)
     return e;
-  return launch_marked(bwd_state_scans_kernel<DK, DV>, dim3(BH, 2 * DK * DV / kBScanElems), stream,
-                       p, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr);
+  // segments of 4, 8 or 16 slots, so that one round of 16 segments covers
+  // the sequence when it can (a 64-chunk sequence in segments of 16 would
+  // leave three quarters of every workgroup idle)
+  const dim3 scan_grid(BH, 2 * DK * DV / kBScanElems);
+  auto* scans = p.n_spans <= kBScanSeg * 4   ? bwd_state_scans_kernel<DK, DV, 4>
+                : p.n_spans <= kBScanSeg * 8 ? bwd_state_scans_kernel<DK, DV, 8>
+                                             : bwd_state_scans_kernel<DK, DV, 16>;
+  return launch_marked(scans, scan_grid, stream, p, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr);
 }
 
 }  // namespace
