@@ -158,6 +158,15 @@ __device__ __forceinline__ float logsigmoid_scaled(float z, float inv_tau) {
   const float l = t < 0.015625f ? series : __builtin_amdgcn_logf(1.f + t) * 0.6931471805599453f;
   return (fminf(z, 0.f) - l) * inv_tau;
 }
+// The same for a result that is rounded to float16 next: ln(1 + t) as
+// log2(1 + t) ln 2 throughout.  Where 1 + t drops t's low bits (small t) the
+// absolute error stays below 2^-24 / tau, under one spacing of float16 at any
+// value (2^-24 is its smallest) when tau >= 1, so the rounded log-decay moves
+// by at most one unit in its last place.
+__device__ __forceinline__ float logsigmoid_scaled_f16(float z, float inv_tau) {
+  const float t = exp2_fast(-fabsf(z) * 1.4426950408889634f);
+  return fminf(z, 0.f) * inv_tau - __builtin_amdgcn_logf(1.f + t) * (0.6931471805599453f * inv_tau);
+}
 // Log-alpha of a transposed 16 x 16 read (lane (i, g): rows row0 + 4g + u):
 // the tile value itself, or with GATE the activation of the logits there.
 // Rows at or past `valid` (zero fills) must not decay, so they get 0 rather
@@ -167,11 +176,15 @@ __device__ __forceinline__ f16x4 log_alpha_of(f16x4 x, float inv_tau, int row0, 
   if constexpr (!GATE) {
     return x;
   } else {
-    const int g = (threadIdx.x & 63) >> 4;
     f32x4 r;
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      r[u] = (row0 + 4 * g + u < valid) ? logsigmoid_scaled((float)x[u], inv_tau) : 0.f;
+    for (int u = 0; u < 4; ++u) r[u] = logsigmoid_scaled_f16((float)x[u], inv_tau);
+    if (row0 + 16 > valid) {  // a tile with zero-filled rows (workgroup-uniform)
+      const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (row0 + 4 * g + u >= valid) r[u] = 0.f;
+    }
     return to_f16(r);
   }
 }
