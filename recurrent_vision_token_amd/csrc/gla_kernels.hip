@@ -1117,9 +1117,9 @@ __device__ __forceinline__ void output_span(const FwdParams& p, int bh, int span
 // LOOKBACK (d_k = d_v = 64): the entry state is not read from span_state but
 // formed here from the initial state and the summaries of the earlier spans
 // of the sequence, stored by span_summary_f16_kernel<..., true> in this
-// kernel's register layout: S_entry = g_{s-1} (... (g_0 S_init + A_0) ...) +
-// A_{s-1}, the scan's recurrence, with four summaries' loads in flight at a
-// time, overlapping the first step's tile loads.
+// kernel's register layout as float16: S_entry = g_{s-1} (... (g_0 S_init +
+// A_0) ...) + A_{s-1}, the scan's recurrence in float32, with four summaries'
+// loads in flight at a time, overlapping the first step's tile loads.
 template <int DK, int DV, bool GATE, bool LOOKBACK = false>
 __global__ __launch_bounds__(kThreads, LOOKBACK ? 2 : (DK == 64 && DV == 64) ? 4 : (DK == 128 && DV == 128) ? 1 : 2) void chunk_output_f16_kernel(
     FwdParams p) {
@@ -1159,8 +1159,8 @@ __global__ __launch_bounds__(kThreads, LOOKBACK ? 2 : (DK == 64 && DV == 64) ? 4
     load_state_tiles<DK, DV>(p.initial_state ? p.initial_state + (size_t)bh * DK * DV : nullptr,
                              wave, lane & 15, g, st);
     auto fold_earlier = [&](f32x4 (&s)[DK / 16][DV / 64]) {
-      const float* A =
-          p.span_state + (size_t)bh * p.n_spans * DK * DV + ((size_t)wave * 4 * 64 + lane) * 4;
+      const f16* A = reinterpret_cast<const f16*>(p.span_state) + (size_t)bh * p.n_spans * DK * DV +
+                     ((size_t)wave * 4 * 64 + lane) * 4;
       const float* G = p.span_gate + (size_t)bh * p.n_spans * DK + 4 * g;
       constexpr int NB = 4;  // summaries in flight
       for (int j0 = 0; j0 < span; j0 += NB) {
@@ -1170,7 +1170,7 @@ __global__ __launch_bounds__(kThreads, LOOKBACK ? 2 : (DK == 64 && DV == 64) ? 4
           const int j = min(j0 + i, span - 1);
 #pragma unroll
           for (int r = 0; r < DK / 16; ++r) {
-            av[i][r] = *reinterpret_cast<const f32x4*>(A + (size_t)j * DK * DV + r * 256);
+            av[i][r] = __builtin_convertvector(ld64(A + (size_t)j * DK * DV + r * 256), f32x4);
             gv[i][r] = *reinterpret_cast<const f32x4*>(G + (size_t)j * DK + 16 * r);
           }
         }
@@ -1392,10 +1392,11 @@ __device__ __forceinline__ void summarize_span(const FwdParams& p, int bh, int s
 // (d_k = d_v = 64): lane (n, g) of wave w holds S[16 w + n][16 cb + 4g + u];
 // in the output kernel's layout that element belongs to wave cb, row block
 // r = w, lane (4g + u) + 16 (n / 4), component n % 4, and the summary is
-// [wave][r][lane][4] floats, so each reader lane loads 16-byte pieces.  Each
-// wave's four 1 KB blocks go through its own 4 KB of LDS (`stage`, free once
-// the workgroup is past the barrier before this call) and out as 16-byte
-// stores.
+// [wave][r][lane][4] float16 values, so each reader lane loads 8-byte pieces
+// (float16 halves the look-back's reads; the fold itself runs in float32).
+// Each wave's four 1 KB blocks of floats go through its own 4 KB of LDS
+// (`stage`, free once the workgroup is past the barrier before this call)
+// and out as 8-byte stores.
 template <int DK, int DV>
 __device__ __forceinline__ void store_summary_out_layout(const FwdParams& p, int bh, int span,
                                                          int wave, int lane, float* stage,
@@ -1408,11 +1409,11 @@ __device__ __forceinline__ void store_summary_out_layout(const FwdParams& p, int
 #pragma unroll
     for (int u = 0; u < 4; ++u)
       stage[cb * 256 + (4 * g + u + 16 * (n16 >> 2)) * 4 + (n16 & 3)] = st[0][cb][u];
-  float* dst = p.span_state + ((size_t)bh * p.n_spans + span) * DK * DV;
+  f16* dst = reinterpret_cast<f16*>(p.span_state) + ((size_t)bh * p.n_spans + span) * DK * DV;
 #pragma unroll
   for (int cb = 0; cb < DV / 16; ++cb)
-    *reinterpret_cast<f32x4*>(dst + (cb * 4 + wave) * 256 + 4 * lane) =
-        *reinterpret_cast<const f32x4*>(stage + cb * 256 + 4 * lane);
+    st64(dst + (cb * 4 + wave) * 256 + 4 * lane,
+         to_f16(*reinterpret_cast<const f32x4*>(stage + cb * 256 + 4 * lane)));
   if (g == 0)
     p.span_gate[((size_t)bh * p.n_spans + span) * DK + 16 * wave + n16] =
         exp2_fast(gdec[0][0] * 1.4426950408889634f);
