@@ -625,14 +625,31 @@ int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* log_a
     gla::fast_div_constants((unsigned)H, &f.div_h_m, &f.div_h_s);
     f.scan_dir = scan_dir;
     f.n_chunks = n_chunks;
-    // spans of one chunk: the scans give every chunk both of its states
-    f.span_chunks = 1;
-    f.n_spans = n_chunks;
+    // The adjoint recurrence in spans of one chunk, the forward one in spans
+    // of `fwd_span`: with 2 the chunk kernel takes a pair of chunks at a time
+    // and carries the forward state from the first into the second itself,
+    // so the scans give each pair its forward state (half the forward state
+    // traffic) and each chunk its adjoint.  Pairs make the chunk kernel's
+    // work units twice as long, which costs more than it saves at the end of
+    // the kernel unless each persistent workgroup has many chunks: pairs
+    // from 16 chunks per workgroup (batched configuration: 2.69 -> 2.53 ms
+    // per call; at 16.4K, 6 chunks each, the chunk kernel ran 5 us slower).
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return GLA_ERR_HIP;
+    const long long cus = cu_count(dev);
+    // (GLA_BWD_PAIRS=1 or 0 forces either form: a test and tuning override,
+    // read on every call)
+    const char* pairs_env = std::getenv("GLA_BWD_PAIRS");
+    const int fwd_span = pairs_env && pairs_env[0] == '1' ? 2
+                         : pairs_env && pairs_env[0] == '0' ? 1
+                         : BH * n_chunks >= 16 * 2 * cus ? 2 : 1;
+    const int n_units = (n_chunks + fwd_span - 1) / fwd_span;
+    f.span_chunks = fwd_span;
+    f.n_spans = n_units;
     f.ldk = (unsigned)d_k;
     f.ldv = (unsigned)d_v;
     f.st_row = (unsigned)d_v;
     f.st_bh = (unsigned)(d_k * d_v);
-    const int n_spans = f.n_spans;
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     constexpr size_t map = 64 * 64;   // one block's state
@@ -640,21 +657,18 @@ int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* log_a
     // of LDS per workgroup): one round over the chip, one workgroup per CU
     // once each then streams at least 8 chunks (16.4K: 12 chunks each, 40 us
     // against 42 us at two per CU), else two per CU
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return GLA_ERR_HIP;
     static const int spw_override = [] {
       const char* e = std::getenv("GLA_BWD_SPANS_PER_WG");  // tuning override
       const int v = e ? std::atoi(e) : 0;
       return (v >= 1 && v <= 64) ? v : 0;
     }();
-    const long long total_spans = BH * n_spans;
-    const long long cus = cu_count(dev);
-    const long long wg_slots = total_spans >= 8 * cus ? cus : 2 * cus;
+    const long long total_spans = BH * n_units;
+    const long long wg_slots = BH * n_chunks >= 8 * cus ? cus : 2 * cus;
     f.spans_per_wg = spw_override ? spw_override : (int)((total_spans + wg_slots - 1) / wg_slots);
     // float32 gate products of both recurrences, then their float16
     // summaries, which the scans overwrite with the entry states (the chunk
     // kernel's operands)
-    const size_t slots = (size_t)BH * n_spans;   // of each recurrence
+    const size_t slots = (size_t)BH * n_chunks;   // of each recurrence (the forward uses half)
     WsLease ws;
     // ... and the chunk kernel's ticket counter after them
     const size_t state_bytes = 2 * slots * (64 * sizeof(float) + map * 2);
@@ -663,7 +677,7 @@ int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* log_a
     f.bwd_ticket = reinterpret_cast<unsigned int*>(static_cast<char*>(ws.ptr()) + state_bytes);
     f.span_gate = w;
     f.adj_gate = w + slots * 64;
-    f.adj_slots = n_spans;
+    f.adj_slots = n_chunks;
     f.span_entry16 = w + 2 * slots * 64;
     f.adj_entry16 = static_cast<char*>(f.span_entry16) + slots * map * 2;
 
@@ -685,7 +699,8 @@ int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* log_a
     pb.ldv = f.ldv;
     // the chunk kernel is persistent, two workgroups per CU (74 KB of LDS
     // each)
-    pb.n_wg = (int)std::min<long long>(BH * n_chunks, 2LL * cu_count(dev));
+    pb.n_wg = (int)std::min<long long>(BH * n_units, 2LL * cus);
+    pb.fwd_span = fwd_span;
     pb.ticket = f.bwd_ticket;
 
     // with the measurement hook armed, every block's kernels record into the

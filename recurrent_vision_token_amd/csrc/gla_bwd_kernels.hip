@@ -20,11 +20,14 @@
 // (the last term is the same sum over every later token, by the adjoint
 // identity dlog_alpha_t = alpha_t * rowsum(G_t * S_{t-1}) at the chunk's end).
 //
-// The state kernels work on spans of one chunk, so every chunk finds both of
-// its states (float16) in memory.  The chunk kernel is persistent: two
-// 8-wave workgroups per CU take the (batch*head, chunk) pairs in turn.  Per
-// chunk (wave w owning key dims and value dims 16 (w % 4) .. + 15 and the
-// 16-token sub-blocks {0, 3} or {1, 2}):
+// The state kernels give every chunk its adjoint state and every pair of
+// consecutive chunks its forward state (float16, in memory).  The chunk
+// kernel is persistent: two 8-wave workgroups per CU take the pairs of
+// chunks of each (batch*head) sequence in turn, the first chunk of a pair and
+// then the second, which enters with the first one's next state (step 3
+// below), written into LDS by the workgroup instead of loaded.  Per chunk
+// (wave w owning key dims and value dims 16 (w % 4) .. + 15 and the 16-token
+// sub-blocks {0, 3} or {1, 2}):
 //   1. q, k, v, log-alpha, dO and both states are in LDS (LDS-writing loads,
 //      swizzled rows, issued during the previous chunk); B is summed per key
 //      dim in float32;
@@ -174,8 +177,10 @@ constexpr int kVmemAfterPrefetch = ACC_K ? 4 : 2;
 // with it (log-alpha, k, d_out and both states after dq's products; q and v
 // after dk), so that the loads run under the rest of the chunk's work, and a
 // chunk's stores drain under the next one's.  ACC_V: dv adds to the stored
-// values; ACC_K: dq, dk and dlog-alpha do.
-template <int DK, int DV, bool ACC_V, bool ACC_K>
+// values; ACC_K: dq, dk and dlog-alpha do.  PAIRS: the work units are pairs
+// of chunks, the second entering with the first one's next state (else
+// single chunks, each with its forward state from memory).
+template <int DK, int DV, bool ACC_V, bool ACC_K, bool PAIRS>
 __global__ __launch_bounds__(kThreads, 4) void chunk_bwd_f16_kernel(BwdParams p) {
   static_assert(DK == 64 && DV == 64, "built for 64 key and value dims");
   constexpr int RB = 128;  // bytes per tile row
@@ -223,6 +228,12 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_bwd_f16_kernel(BwdParams p)
   const uint32_t gsk = p.ldk * 2u, gsv = p.ldv * 2u;  // row strides in bytes
   const uint32_t kbytes = (uint32_t)p.T * gsk, vbytes = (uint32_t)p.T * gsv;
   const int total = p.B * p.heads * p.n_chunks;
+  // work units: pairs of consecutive chunks of one sequence (the last one of
+  // an odd sequence alone), taken whole by one workgroup in order; or single
+  // chunks.  The forward states in memory are one per unit.
+  constexpr int kSpan = PAIRS ? 2 : 1;
+  const int n_units = PAIRS ? (p.n_chunks + 1) >> 1 : p.n_chunks;
+  const int total_units = p.B * p.heads * n_units;
 
   // Loads of chunk `item`: this wave fills block `wave` (tokens 8 wave .. + 7;
   // lane l: 16 bytes of row 8 wave + l / 8, swizzled pieces) of each tile.  A
@@ -269,19 +280,29 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_bwd_f16_kernel(BwdParams p)
   f16* const sE = reinterpret_cast<f16*>(sEc);
   f16* const sR = sE + DK * DV;
   static_assert(2 * DK * DV * 2 <= kChunk * ES * 4, "both states fit in sEc");
-  auto load_states = [&](int item, int lane) {
+  // The forward state comes from memory only for the first chunk of a unit
+  // (slot c / kSpan); a pair's second chunk's is the first one's next state,
+  // which the workgroup writes into sE itself (with_e false).
+  auto load_states = [&](int item, int lane, bool with_e) {
     const int bh = item / p.n_chunks, c = item - bh * p.n_chunks;
-    const f16* E = static_cast<const f16*>(p.fwd_state) + ((size_t)bh * p.n_chunks + c) * DK * DV;
+    const f16* E = static_cast<const f16*>(p.fwd_state) + ((size_t)bh * n_units + c / kSpan) * DK * DV;
     const f16* R = static_cast<const f16*>(p.adj_state) +
                    ((size_t)bh * p.n_chunks + (p.n_chunks - 1 - c)) * DK * DV;
     const int r = 8 * wave + (lane >> 3);
     const uint32_t off = (uint32_t)r * RB + (uint32_t)(((lane & 7) ^ (r & 7)) * 16);
-    dma16_asm<false>(seq_rsrc(E, DK * DV * 2), sE + wave * 512, off);
+    if (with_e) dma16_asm<false>(seq_rsrc(E, DK * DV * 2), sE + wave * 512, off);
     dma16_asm<false>(seq_rsrc(R, DK * DV * 2), sR + wave * 512, off);
   };
+  // first chunk of work unit u, or `total` past the last unit
+  auto unit_chunk = [&](int u) {
+    if (u >= total_units) return total;
+    if constexpr (!PAIRS) return u;
+    const int bh = u / n_units;
+    return bh * p.n_chunks + kSpan * (u - bh * n_units);
+  };
 
-  int item = blockIdx.x;
-  if (item >= total) return;
+  if ((int)blockIdx.x >= total_units) return;
+  int item = unit_chunk(blockIdx.x);
   {
     const Plan pl = plan(item, 0, lane);
     load_k_side(pl, p.q, tq);
@@ -289,7 +310,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_bwd_f16_kernel(BwdParams p)
     load_v_side(pl, p.v, tv);
     load_k_side(pl, p.la, tla);
     load_v_side(pl, p.dout, tdo);
-    load_states(item, lane);
+    load_states(item, lane, true);
     wait_barrier<vmcnt_lgkm0_imm(0)>();
   }
   for (int sel = 0; item < total; sel ^= 1) {
@@ -301,8 +322,14 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_bwd_f16_kernel(BwdParams p)
     // a vector register, so the compiler treats it as per-lane and leaves the
     // atomic alone instead of combining it over the wave, which would wait
     // for the result right here.
+    // the next chunk is this pair's second (workgroup-uniform)
+    bool to_second = false;
+    if constexpr (PAIRS) {
+      const int c_cur = item - (item / p.n_chunks) * p.n_chunks;
+      to_second = (c_cur & 1) == 0 && c_cur + 1 < p.n_chunks;
+    }
     unsigned int ticket = 0;
-    if (threadIdx.x == 0) {
+    if (threadIdx.x == 0 && !to_second) {
       // (a global, not a flat, atomic: a flat one would also count against
       // the LDS waits of the decay pass)
       auto* ctr = (__attribute__((address_space(1))) unsigned int*)p.ticket;
@@ -472,14 +499,17 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_bwd_f16_kernel(BwdParams p)
         case 6: factors(std::integral_constant<int, 6>{}); break;
         default: factors(std::integral_constant<int, 7>{}); break;
       }
-      if (threadIdx.x == 0) sNext = (int)gridDim.x + (int)ticket;
+      if (threadIdx.x == 0) sNext = to_second ? item + 1 : unit_chunk((int)gridDim.x + (int)ticket);
     }
     wait_barrier<kLgkmZero>();
     const int next = __builtin_amdgcn_readfirstlane(sNext);
     const bool more = next < total;
 
     // The next state: instantiated for each half of the waves, so that their
-    // sub-blocks are constants and the loops over sub-block pairs unroll
+    // sub-blocks are constants and the loops over sub-block pairs unroll.
+    // With PAIRS the lane's entries are also kept (float16), for a pair's
+    // second chunk.
+    f16x4 enext[2];
     auto next_state = [&](auto half) __attribute__((always_inline)) {
       constexpr int HF = decltype(half)::value;
       // ---- next state rows 16 kc + n (kc = 2 hf, 2 hf + 1), columns vj ..:
@@ -501,8 +531,13 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_bwd_f16_kernel(BwdParams p)
         const float ebe = ex(sBst[i]);
         const f16x4 e4 = e4h[x], r4 = r4h[x];
         float part = 0.f;
+        f32x4 en;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) part += (ebe * (float)e4[u] + acc[u]) * (float)r4[u];
+        for (int u = 0; u < 4; ++u) {
+          en[u] = ebe * (float)e4[u] + acc[u];
+          part += en[u] * (float)r4[u];
+        }
+        if constexpr (PAIRS) enext[x] = to_f16(en);
         part = group_sum(part);
         if (g == 0) sCarry[vb][i] = part;
       }
@@ -638,7 +673,12 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_bwd_f16_kernel(BwdParams p)
         load_k_side(pn, p.la, tla);
         load_k_side(pn, p.k, tk);
         load_v_side(pn, p.dout, tdo);
-        load_states(next, ln);
+        load_states(next, ln, !to_second);
+        if (PAIRS && to_second) {
+          // the next chunk enters with this one's next state
+#pragma unroll
+          for (int x = 0; x < 2; ++x) st64(sE + swz<RB>(16 * (2 * HF + x) + n16, vj), enext[x]);
+        }
       }
 
       // dq's scaling and stores
@@ -746,10 +786,14 @@ hipError_t launch_bwd_chunks(int d_k, int d_v, const BwdParams& p, hipStream_t s
                              hipEvent_t start, hipEvent_t stop) {
   if (d_k != 64 || d_v != 64) return hipErrorInvalidValue;
   const dim3 grid(p.n_wg), block(kThreads);
-  const auto kernel = p.acc_dv ? (p.acc_dqk ? chunk_bwd_f16_kernel<64, 64, true, true>
-                                            : chunk_bwd_f16_kernel<64, 64, true, false>)
-                               : (p.acc_dqk ? chunk_bwd_f16_kernel<64, 64, false, true>
-                                            : chunk_bwd_f16_kernel<64, 64, false, false>);
+  auto pick = [&](auto pairs) {
+    constexpr bool PR = decltype(pairs)::value;
+    return p.acc_dv ? (p.acc_dqk ? chunk_bwd_f16_kernel<64, 64, true, true, PR>
+                                 : chunk_bwd_f16_kernel<64, 64, true, false, PR>)
+                    : (p.acc_dqk ? chunk_bwd_f16_kernel<64, 64, false, true, PR>
+                                 : chunk_bwd_f16_kernel<64, 64, false, false, PR>);
+  };
+  const auto kernel = p.fwd_span == 2 ? pick(std::true_type{}) : pick(std::false_type{});
   if (start != nullptr || stop != nullptr) {
     hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, start, stop, 0, p);
   } else {

@@ -143,7 +143,9 @@ struct BwdParams {
   void* dk;
   void* dv;                 // [B][heads][H][W][d_v]
   void* dla;                // [B][heads][H][W][d_k]
-  const void* fwd_state;    // [BH][n_chunks][d_k][d_v] float16: the state entering chunk c
+  const void* fwd_state;    // [BH][ceil(n_chunks / fwd_span)][d_k][d_v] float16: slot
+                            // c / fwd_span is the state entering chunk c, the
+                            // first of its unit
   const void* adj_state;    // [BH][n_chunks][d_k][d_v] float16: slot n_chunks - 1 - c is the
                             // state gradient entering chunk c from the right
   int B, heads, H, W, T;
@@ -159,6 +161,8 @@ struct BwdParams {
   unsigned int ldk, ldv;
   int acc_dv, acc_dqk;
   int n_wg;                 // persistent workgroups (at most two per CU)
+  int fwd_span;             // chunks per work unit: 2 (pairs, the second entering with
+                            // the first one's next state) or 1
   // the chunks after each workgroup's first are handed out in ticket
   // order; the counter is zero when the kernel starts (the state scans
   // before it clear it)

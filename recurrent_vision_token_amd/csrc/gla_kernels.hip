@@ -1445,19 +1445,20 @@ __global__ __launch_bounds__(kThreads) void span_summary_f16_kernel(FwdParams p)
                             wave, lane & 15, lane >> 4, st, gdec);
 }
 
-// The backward pass's two summaries of a span: the forward one (k, v; the
-// state entering each span) and the adjoint one (q and the output gradient
-// d_out; the state gradient entering each span from its right), sharing the
-// log-alpha tile, stored as float16 (span_entry16, adj_entry16) with float32
-// gate products.  Span s's adjoint summary goes to slot adj_slots - 1 - s, so
-// that the adjoint scan runs from the end of the sequence to its start.
-// float16, no fused gate activation.
+// The backward pass's two kinds of summary: the forward one (k, v; the state
+// entering each span, a span being a pair of chunks) and the adjoint one (q
+// and the output gradient d_out; the state gradient entering each chunk from
+// its right), sharing the log-alpha tile, stored as float16 (span_entry16,
+// adj_entry16) with float32 gate products.  Chunk c's adjoint summary goes to
+// slot adj_slots - 1 - c, so that the adjoint scan runs from the end of the
+// sequence to its start.  float16, no fused gate activation.
 //
 // A workgroup takes spans_per_wg consecutive spans (of the flattened
 // (batch*head, span) order) and streams their chunks through two tile
 // buffers, so that the loads of one chunk overlap the folds of the previous
-// one; a span's summaries are stored when its first chunk (folded last) is
-// done.  Eight waves: four fold the forward summary and four the adjoint one
+// one; a span's chunks are taken last to first, its forward summary stored
+// when its first chunk (folded last) is done, each chunk's adjoint summary
+// when that chunk is.  Eight waves: four fold the forward summary and four the adjoint one
 // from the same tiles, so a SIMD has two waves to switch between even at one
 // workgroup per CU.
 constexpr int kSumThreads = 512;  // 8 waves: 4 fold the forward summary, 4 the adjoint
@@ -1550,13 +1551,15 @@ __global__ __launch_bounds__(kSumThreads) void bwd_state_summaries_kernel(FwdPar
       else
         fold_chunk<DK, DV, false, true>(a, valid, 1.f, m_tri, m_ones, wq, st, gdec);
     }
-    if (i % sc == sc - 1) {
-      if (fam == 0)
+    if (fam == 0) {
+      if (i % sc == sc - 1) {
         store_summary16<DK, DV>(static_cast<f16*>(p.span_entry16), p.span_gate, it.bh, p.n_spans,
                                 it.span, wq, n16, g, st, gdec);
-      else
-        store_summary16<DK, DV>(static_cast<f16*>(p.adj_entry16), p.adj_gate, it.bh, slots,
-                                slots - 1 - it.span, wq, n16, g, st, gdec);
+        reset();
+      }
+    } else if (it.live) {
+      store_summary16<DK, DV>(static_cast<f16*>(p.adj_entry16), p.adj_gate, it.bh, slots,
+                              slots - 1 - it.c, wq, n16, g, st, gdec);
       reset();
     }
   };
@@ -1774,9 +1777,10 @@ hipError_t launch_bwd_states_variant(const FwdParams& p, hipStream_t stream, hip
   // the sequence when it can (a 64-chunk sequence in segments of 16 would
   // leave three quarters of every workgroup idle)
   const dim3 scan_grid(BH, 2 * DK * DV / kBScanElems);
-  auto* scans = p.n_spans <= kBScanSeg * 4   ? bwd_state_scans_kernel<DK, DV, 4>
-                : p.n_spans <= kBScanSeg * 8 ? bwd_state_scans_kernel<DK, DV, 8>
-                                             : bwd_state_scans_kernel<DK, DV, 16>;
+  const int slots = p.n_spans > p.adj_slots ? p.n_spans : p.adj_slots;
+  auto* scans = slots <= kBScanSeg * 4   ? bwd_state_scans_kernel<DK, DV, 4>
+                : slots <= kBScanSeg * 8 ? bwd_state_scans_kernel<DK, DV, 8>
+                                         : bwd_state_scans_kernel<DK, DV, 16>;
   return launch_marked(scans, scan_grid, stream, p, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr);
 }
 

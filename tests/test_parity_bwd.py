@@ -167,3 +167,20 @@ def test_uneven_chunks_per_persistent_workgroup():
         ref = gla_backward(q[sl], k[sl], v[sl], la[sl], do[sl], b % 4, d_final_state=dfin[sl],
                            initial_state=init[sl])
         check([x[sl] for x in got], ref, "uneven b %d h %d" % (b, h))
+
+
+@pytest.mark.parametrize("pairs", ["1", "0"])
+def test_chunk_pairs_and_single_chunks(pairs, monkeypatch):
+    # The chunk kernel takes pairs of chunks (the second entering with the
+    # first one's next state, the scans giving the forward state per pair)
+    # when every persistent workgroup has many chunks, else single chunks;
+    # GLA_BWD_PAIRS forces either.  Odd chunk counts leave a pair of one
+    # chunk at each sequence's end; wide heads run the accumulating variants;
+    # the rotation mixes directions within a call.
+    monkeypatch.setenv("GLA_BWD_PAIRS", pairs)
+    case(1, 2, 13, 11, 1, seed=400)                 # 3 chunks: one pair and a ragged one
+    case(1, 2, 1, 37, 0, seed=401)                  # a single chunk
+    case(2, 3, 16, 24, 4, seed=402)                 # 6 chunks, rotation, 6 sequences
+    case(4, 2, 21, 19, 4, seed=403, dk=128, dv=64)  # 7 chunks, dv accumulated over key blocks
+    case(1, 2, 21, 19, 2, seed=404, dk=64, dv=128)  # dq, dk, dlog-alpha accumulated
+    case(1, 3, 20, 20, 3, seed=405, gate_std=2.0)   # strong decay
