@@ -269,7 +269,11 @@ int gla_plan_spans(int use_f32, int B, int heads, int H, int W, int d_k, int d_v
  * a scan kernel over chunks (the adjoint recurrence is the forward one read
  * from the end; per-chunk summaries and states are kept as float16, the scans
  * accumulate in float32), then every chunk computes its gradients
- * independently.
+ * independently.  When every persistent workgroup of the chunk kernel gets at
+ * least 16 chunks, the forward states are kept per pair of chunks instead, and
+ * the second chunk of a pair starts from the state the first one reaches;
+ * the environment variable GLA_BWD_PAIRS (1 or 0, read on every call) forces
+ * the paired or the per-chunk form.
  *
  * Layout as gla_chunk_fwd; d_out is [B][heads][H][W][d_v] float16;
  * d_final_state and initial_state are float32 [B][heads][d_k][d_v] or NULL
