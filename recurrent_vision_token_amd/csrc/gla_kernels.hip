@@ -765,8 +765,10 @@ __global__ __launch_bounds__(kThreads) void chunk_output_kernel(FwdParams p) {
 //   O : wave w owns value columns 16w.. : the three causal score tiles in
 //       transposed orientation (A^T, computed by every wave: cheaper than a
 //       barrier), O^T = V^T A^T + S^T Qt^T with the score tiles used straight
-//       from the accumulators, outputs stored from registers to their grid
-//       cells, then S <- diag(exp(b_end)) S + KL^T V.
+//       from the accumulators, the outputs written over the wave's own value
+//       columns of the step's v tile (out to their grid cells as whole rows
+//       after the step's closing barrier), then S <- diag(exp(b_end)) S +
+//       KL^T V.
 // The x32 MFMAs that reduce over tokens use one token-slot order for both
 // operands: slots 8g..8g+3 hold tokens 4g..4g+3 of sub-block 0 and slots
 // 8g+4..8g+7 the same tokens of sub-block 1, which is what two transposed
